@@ -1,0 +1,414 @@
+"""Pins for the fp64 oracle: each test checks it against something other than
+itself -- a closed form, a library routine, an independent formulation of the
+same method from the pages, an exact worked example, or brute force.
+
+Sources (pages, by title and section):
+  [KO]  Mamba-3 summary on b-lab.team (Korean): section 1 "Exponential-
+        Trapezoidal Discretization" (recurrence, alpha/beta/gamma, lam limits,
+        two-band mask), section 2 "Complex-Valued SSM" (complex SSM, real
+        block-rotation form = Proposition 2, RoPE trick = Proposition 3),
+        section 3 "MIMO".
+  [TAI] Towards AI explainer of Mamba-3: section II (trapezoid error orders,
+        "decay mask times a size-two convolutional mask"), section III (parity
+        tracking with data-dependent RoPE).
+  [OSC] Summary of "Understanding Mamba-3 Through Oscillatory Dynamics":
+        section 3 (each decay-rotation step is the exact flow of a fixed
+        generator), appendix on accumulation under persistent forcing, and the
+        learned phase increments of about 180 deg (parity) and 120 deg (mod 3).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.signal
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_inputs(rng, Bt, L, H, R, P, N, lam=None, theta_scale=1.0):
+    x = rng.standard_normal((Bt, L, H, R, P))
+    Bm = rng.standard_normal((Bt, L, H, R, N))
+    Cm = rng.standard_normal((Bt, L, H, R, N))
+    dt = np.log1p(np.exp(rng.standard_normal((Bt, L, H))))
+    A = -np.exp(rng.uniform(-1, 1, size=H))
+    theta = rng.uniform(-math.pi, math.pi, size=(Bt, L, H, N // 2)) * theta_scale
+    if lam is None:
+        lam = 1.0 / (1.0 + np.exp(-rng.standard_normal((Bt, L, H))))
+    else:
+        lam = np.full((Bt, L, H), float(lam))
+    return x, Bm, Cm, dt, A, theta, lam
+
+
+def rel_err(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------------------
+# [KO] s1: lam = 1 is Mamba-2's exponential-Euler rule.  With theta = 0 and
+# constant B, C, dt the system is LTI, and the output is a first-order IIR
+# filter of x: y = lfilter([dt * C.B], [1, -alpha], x).
+def test_lambda_one_is_euler_lti_lfilter():
+    rng = np.random.default_rng(1)
+    L, P, N = 200, 3, 6
+    b = rng.standard_normal(N)
+    c = rng.standard_normal(N)
+    d, A = 0.37, -0.8
+    x = rng.standard_normal((1, L, 1, 1, P))
+    Bm = np.broadcast_to(b, (1, L, 1, 1, N))
+    Cm = np.broadcast_to(c, (1, L, 1, 1, N))
+    dt = np.full((1, L, 1), d)
+    lam = np.ones((1, L, 1))
+    theta = np.zeros((1, L, 1, N // 2))
+    y, h, _, _ = oracle.scan(x, Bm, Cm, dt, np.array([A]), theta, lam)
+    alpha = math.exp(d * A)
+    for p in range(P):
+        ref = scipy.signal.lfilter([d * float(c @ b)], [1.0, -alpha], x[0, :, 0, 0, p])
+        np.testing.assert_allclose(y[0, :, 0, 0, p], ref, rtol=1e-12, atol=1e-12)
+
+
+# [KO] s1: lam = 1, theta = 0 with time-varying inputs is the Mamba-2 recurrence
+# h_t = exp(dt_t A) h_{t-1} + dt_t B_t x_t^T (no previous-endpoint term, no
+# rotation), including MIMO input summation and per-rank readout.
+def test_lambda_one_theta_zero_is_mamba2_time_varying():
+    rng = np.random.default_rng(2)
+    Bt, L, H, R, P, N = 2, 37, 3, 2, 4, 8
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N, lam=1.0)
+    theta[:] = 0.0
+    h0 = rng.standard_normal((Bt, H, N, P))
+    y, hL, _, _ = oracle.scan(x, Bm, Cm, dt, A, theta, lam, h0=h0,
+                              Bprev=rng.standard_normal((Bt, H, R, N)),
+                              xprev=rng.standard_normal((Bt, H, R, P)))
+    for b in range(Bt):
+        for hh in range(H):
+            h = h0[b, hh].copy()
+            for t in range(L):
+                h = math.exp(dt[b, t, hh] * A[hh]) * h + dt[b, t, hh] * (Bm[b, t, hh].T @ x[b, t, hh])
+                np.testing.assert_allclose(y[b, t, hh], Cm[b, t, hh] @ h, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(hL[b, hh], h, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# [KO] s1 / [TAI] s.II: the trapezoid (lam = 1/2) has global error O(dt^2), the
+# Euler rule (lam = 1) and the left-endpoint rule (lam = 0) O(dt).  Pinned
+# against the closed-form solution of the continuous complex SSM
+# z' = (a + i w) z + b u(t), u = cos(nu t), over [0, T]:
+#   z(T) = b/2 [ (e^{i nu T} - e^{sT})/(i nu - s) + (e^{-i nu T} - e^{sT})/(-i nu - s) ],
+# s = a + i w.  The sample u(0) enters through the state record (B_prev, x_prev).
+def _trapezoid_error(n, lam_value, a=-0.7, w=2.3, nu=1.7, T=3.0, b=(0.8, -0.5)):
+    d = T / n
+    t = d * np.arange(1, n + 1)
+    x = np.cos(nu * t).reshape(1, n, 1, 1, 1)
+    Bm = np.broadcast_to(np.array(b), (1, n, 1, 1, 2))
+    Cm = np.zeros((1, n, 1, 1, 2))
+    dt = np.full((1, n, 1), d)
+    theta = np.full((1, n, 1, 1), w)
+    lam = np.full((1, n, 1), lam_value)
+    _, hL, _, _ = oracle.scan(x, Bm, Cm, dt, np.array([a]), theta, lam,
+                              h0=np.zeros((1, 1, 2, 1)),
+                              Bprev=np.array(b).reshape(1, 1, 1, 2),
+                              xprev=np.ones((1, 1, 1, 1)))
+    s = complex(a, w)
+    bc = complex(*b)
+    e = complex(0, nu)
+    zT = bc * 0.5 * ((np.exp(e * T) - np.exp(s * T)) / (e - s)
+                     + (np.exp(-e * T) - np.exp(s * T)) / (-e - s))
+    return abs(complex(hL[0, 0, 0, 0], hL[0, 0, 1, 0]) - zT)
+
+
+@pytest.mark.parametrize("lam_value,order", [(0.5, 2.0), (1.0, 1.0), (0.0, 1.0)])
+def test_discretization_order(lam_value, order):
+    ns = [100, 200, 400, 800]
+    errs = [_trapezoid_error(n, lam_value) for n in ns]
+    slope = -np.polyfit(np.log(ns), np.log(errs), 1)[0]
+    assert abs(slope - order) < 0.05, (lam_value, slope, errs)
+
+
+# ---------------------------------------------------------------------------
+# [KO] s2, Proposition 2: the complex SSM with h in C^{N/2},
+#   h' = Diag(A + i theta) h + (B + i B^) x,   y = Re((C + i C^)^T h),
+# discretised with the exponential-trapezoidal rule of s1 (each step's flow is
+# exp(dt (A + i theta)), applied to the state and to the previous endpoint),
+# equals the real N-state SSM with block rotations.  Real rows (2i, 2i+1) stack
+# (Re, Im) of B, and (Re, -Im) of (C + i C^) because the readout is a plain
+# transpose.  Native complex128 arithmetic here.
+def complex_form(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev):
+    Bt, L, H, R, P = x.shape
+    N = Bm.shape[-1]
+    y = np.zeros((Bt, L, H, R, P))
+    hL = np.zeros((Bt, H, N, P))
+    for b in range(Bt):
+        for hh in range(H):
+            z = h0[b, hh, 0::2] + 1j * h0[b, hh, 1::2]                  # [N/2, P]
+            Bc = Bprev[b, hh, :, 0::2] + 1j * Bprev[b, hh, :, 1::2]     # [R, N/2]
+            Uprev = Bc.T @ xprev[b, hh]                                 # [N/2, P]
+            for t in range(L):
+                E = np.exp(dt[b, t, hh] * (A[hh] + 1j * theta[b, t, hh]))[:, None]
+                Bc = Bm[b, t, hh, :, 0::2] + 1j * Bm[b, t, hh, :, 1::2]
+                U = Bc.T @ x[b, t, hh]
+                z = (E * z + (1 - lam[b, t, hh]) * dt[b, t, hh] * E * Uprev
+                     + lam[b, t, hh] * dt[b, t, hh] * U)
+                Cc = Cm[b, t, hh, :, 0::2] - 1j * Cm[b, t, hh, :, 1::2]
+                y[b, t, hh] = np.real(Cc @ z)
+                Uprev = U
+            hL[b, hh, 0::2] = z.real
+            hL[b, hh, 1::2] = z.imag
+    return y, hL
+
+
+def test_complex_real_equivalence_mimo():
+    rng = np.random.default_rng(3)
+    Bt, L, H, R, P, N = 2, 23, 2, 3, 5, 6
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N)
+    h0 = rng.standard_normal((Bt, H, N, P))
+    Bp = rng.standard_normal((Bt, H, R, N))
+    xp = rng.standard_normal((Bt, H, R, P))
+    y, hL, BL, xL = oracle.scan(x, Bm, Cm, dt, A, theta, lam, h0=h0, Bprev=Bp, xprev=xp)
+    yc, hc = complex_form(x, Bm, Cm, dt, A, theta, lam, h0, Bp, xp)
+    assert rel_err(y, yc) < 1e-12
+    assert rel_err(hL, hc) < 1e-12
+    np.testing.assert_array_equal(BL, Bm[:, -1])
+    np.testing.assert_array_equal(xL, x[:, -1])
+
+
+# ---------------------------------------------------------------------------
+# [KO] s2, Proposition 3 ("RoPE trick"): rotating B and C by the cumulative
+# phase Phi_t = sum_{s<=t} dt_s theta_s turns the scan into a rotation-free
+# scalar-decay scan: Bbar_t = R(Phi_t)^T B_t, Cbar_t = R(Phi_t)^T C_t,
+#   hbar_t = alpha_t hbar_{t-1} + beta_t Bbar_{t-1} X_{t-1} + gamma_t Bbar_t X_t,
+#   y_t = Cbar_t^T hbar_t,  and the true state is h_L = R(Phi_L) hbar_L.
+def rot_pairs(v, ang, transpose):
+    """Apply R(ang) (or its transpose) to adjacent pairs of the last axis of v."""
+    c, s = np.cos(ang), np.sin(ang)
+    if transpose:
+        s = -s
+    out = np.empty_like(v)
+    out[..., 0::2] = c * v[..., 0::2] - s * v[..., 1::2]
+    out[..., 1::2] = s * v[..., 0::2] + c * v[..., 1::2]
+    return out
+
+
+def rope_form(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev):
+    Bt, L, H, R, P = x.shape
+    N = Bm.shape[-1]
+    y = np.zeros((Bt, L, H, R, P))
+    hL = np.zeros((Bt, H, N, P))
+    for b in range(Bt):
+        for hh in range(H):
+            Phi = np.cumsum(dt[b, :, hh, None] * theta[b, :, hh], axis=0)   # [L, N/2]
+            Bbar = rot_pairs(Bm[b, :, hh], Phi[:, None, :], True)            # [L, R, N]
+            Cbar = rot_pairs(Cm[b, :, hh], Phi[:, None, :], True)
+            hb = h0[b, hh].copy()
+            Uprev = Bprev[b, hh].T @ xprev[b, hh]
+            for t in range(L):
+                alpha = math.exp(dt[b, t, hh] * A[hh])
+                U = Bbar[t].T @ x[b, t, hh]
+                hb = (alpha * hb + (1 - lam[b, t, hh]) * dt[b, t, hh] * alpha * Uprev
+                      + lam[b, t, hh] * dt[b, t, hh] * U)
+                y[b, t, hh] = Cbar[t] @ hb
+                Uprev = U
+            hL[b, hh] = rot_pairs(hb.T, Phi[-1], False).T
+    return y, hL
+
+
+def test_rope_rewrite():
+    rng = np.random.default_rng(4)
+    Bt, L, H, R, P, N = 2, 31, 2, 2, 3, 8
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N)
+    h0 = rng.standard_normal((Bt, H, N, P))
+    Bp = rng.standard_normal((Bt, H, R, N))
+    xp = rng.standard_normal((Bt, H, R, P))
+    y, hL, _, _ = oracle.scan(x, Bm, Cm, dt, A, theta, lam, h0=h0, Bprev=Bp, xprev=xp)
+    yr, hr = rope_form(x, Bm, Cm, dt, A, theta, lam, h0, Bp, xp)
+    assert rel_err(y, yr) < 1e-12
+    assert rel_err(hL, hr) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# [KO] s1 and [TAI] s.II: the trapezoid makes the SSD mask a product of the
+# 1-semiseparable decay mask and a size-two (lower bidiagonal) convolution
+# mask.  Brute force for a zero initial state:
+#   Ldec[t, s] = prod_{k=s+1..t} alpha_k  (s <= t),  0 otherwise
+#   D2[s, s] = gamma_s,  D2[s+1, s] = beta_{s+1}
+#   y_t = sum_s (Ldec @ D2)[t, s] * Cbar_t^T Bbar_s X_s
+def test_two_band_quadratic_form():
+    rng = np.random.default_rng(5)
+    Bt, L, H, R, P, N = 1, 16, 2, 3, 4, 6
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N)
+    y, _, _, _ = oracle.scan(x, Bm, Cm, dt, A, theta, lam)
+    for hh in range(H):
+        d, lm = dt[0, :, hh], lam[0, :, hh]
+        alpha = np.exp(d * A[hh])
+        Ldec = np.zeros((L, L))
+        for t in range(L):
+            for s in range(t + 1):
+                Ldec[t, s] = np.prod(alpha[s + 1:t + 1])
+        D2 = np.diag(lm * d) + np.diag(((1 - lm) * d * alpha)[1:], k=-1)
+        M = Ldec @ D2
+        Phi = np.cumsum(d[:, None] * theta[0, :, hh], axis=0)
+        Bbar = rot_pairs(Bm[0, :, hh], Phi[:, None, :], True).reshape(L * R, N)
+        Cbar = rot_pairs(Cm[0, :, hh], Phi[:, None, :], True).reshape(L * R, N)
+        G = Cbar @ Bbar.T                                      # [(t,r1), (s,r2)]
+        Mx = np.kron(M, np.ones((R, R)))                       # mask per token pair
+        Y = (Mx * G) @ x[0, :, hh].reshape(L * R, P)
+        assert rel_err(y[0, :, hh].reshape(L * R, P), Y) < 1e-12
+        # the mask is exactly two-band-structured: zero above the diagonal
+        assert np.all(np.triu(M, 1) == 0)
+
+
+# ---------------------------------------------------------------------------
+# [OSC] s3: one homogeneous step (no input) is the exact flow of the generator
+# blockdiag([[A, -theta_i], [theta_i, A]]) over dt: exp(dt A) R(dt theta_i).
+def test_step_is_generator_exponential():
+    rng = np.random.default_rng(6)
+    N = 10
+    A = np.array([-0.43])
+    dt = np.array([[[0.71]]])
+    theta = rng.uniform(-3, 3, size=(1, 1, 1, N // 2))
+    h0 = np.eye(N).reshape(1, 1, N, N)                        # P = N identity columns
+    _, hL, _, _ = oracle.scan(np.zeros((1, 1, 1, 1, N)), np.zeros((1, 1, 1, 1, N)),
+                              np.zeros((1, 1, 1, 1, N)), dt, A, theta,
+                              np.full((1, 1, 1), 0.5), h0=h0)
+    G = np.zeros((N, N))
+    for i in range(N // 2):
+        G[2 * i:2 * i + 2, 2 * i:2 * i + 2] = [[A[0], -theta[0, 0, 0, i]],
+                                               [theta[0, 0, 0, i], A[0]]]
+    np.testing.assert_allclose(hL[0, 0], scipy.linalg.expm(dt[0, 0, 0] * G), atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# [TAI] s.III and [OSC] (learned increments near 180 deg for parity, 120 deg for
+# mod 3): a hand-set data-dependent rotation tracks parity exactly.  A = 0,
+# dt = 1, lam = 1, B = 0, h_0 = e_1, C = e_1, theta_t = pi b_t
+#   => y_t = cos(pi sum_{s<=t} b_s) = (-1)^{parity}.
+@pytest.mark.parametrize("modulus", [2, 3])
+def test_hand_set_rotation_tracks_parity_and_mod3(modulus):
+    rng = np.random.default_rng(7 + modulus)
+    L = 4096
+    bits = rng.integers(0, 2, size=L)
+    theta = (2 * math.pi / modulus * bits).reshape(1, L, 1, 1)
+    y, _, _, _ = oracle.scan(np.zeros((1, L, 1, 1, 1)), np.zeros((1, L, 1, 1, 2)),
+                             np.broadcast_to(np.array([1.0, 0.0]), (1, L, 1, 1, 2)),
+                             np.ones((1, L, 1)), np.zeros(1), theta, np.ones((1, L, 1)),
+                             h0=np.array([1.0, 0.0]).reshape(1, 1, 2, 1))
+    count = np.cumsum(bits) % modulus
+    expect = np.cos(2 * math.pi / modulus * count)
+    np.testing.assert_allclose(y[0, :, 0, 0, 0], expect, atol=1e-9)
+    if modulus == 2:
+        assert np.array_equal(np.sign(y[0, :, 0, 0, 0]), np.where(count == 0, 1.0, -1.0))
+
+
+# ---------------------------------------------------------------------------
+# [OSC] appendix (accumulation under persistent forcing): with constant U,
+# alpha, phase phi and lam, the state converges to the fixed point of
+# h = alpha R h + beta R U + gamma U, i.e. per pair in complex form
+#   h_inf = (beta e^{i phi} + gamma) U / (1 - alpha e^{i phi}).
+def test_persistent_forcing_steady_state():
+    N, P, L = 6, 2, 3000
+    rng = np.random.default_rng(8)
+    b = rng.standard_normal(N)
+    xv = rng.standard_normal(P)
+    d, A, lm = 0.3, -0.35, 0.6
+    th = rng.uniform(-2, 2, size=N // 2)
+    _, hL, _, _ = oracle.scan(np.broadcast_to(xv, (1, L, 1, 1, P)),
+                              np.broadcast_to(b, (1, L, 1, 1, N)),
+                              np.zeros((1, L, 1, 1, N)), np.full((1, L, 1), d),
+                              np.array([A]), np.broadcast_to(th, (1, L, 1, N // 2)),
+                              np.full((1, L, 1), lm))
+    alpha = math.exp(d * A)
+    beta, gamma = (1 - lm) * d * alpha, lm * d
+    for i in range(N // 2):
+        e = np.exp(1j * d * th[i])
+        U = (b[2 * i] + 1j * b[2 * i + 1]) * xv
+        hinf = (beta * e + gamma) * U / (1 - alpha * e)
+        np.testing.assert_allclose(hL[0, 0, 2 * i], hinf.real, atol=1e-12)
+        np.testing.assert_allclose(hL[0, 0, 2 * i + 1], hinf.imag, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# [KO] s3 (MIMO): the input term B_t X_t sums the R ranks and the readout gives
+# one output per rank, so by linearity a rank-R scan is the sum of R x R
+# single-rank scans (input rank r, readout rank r').
+def test_mimo_is_superposition_of_siso():
+    rng = np.random.default_rng(9)
+    Bt, L, H, R, P, N = 1, 19, 2, 3, 4, 6
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N)
+    y, hL, _, _ = oracle.scan(x, Bm, Cm, dt, A, theta, lam)
+    ysum = np.zeros_like(y)
+    hsum = np.zeros_like(hL)
+    for r in range(R):
+        for r2 in range(R):
+            yy, hh, _, _ = oracle.scan(x[..., r:r + 1, :], Bm[..., r:r + 1, :],
+                                       Cm[..., r2:r2 + 1, :], dt, A, theta, lam)
+            ysum[..., r2, :] += yy[..., 0, :]
+            if r2 == 0:
+                hsum += hh
+    assert rel_err(y, ysum) < 1e-12
+    assert rel_err(hL, hsum) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# The state record (h, B_prev, x_prev) is a checkpoint: a scan split in two,
+# or a scan followed by single decode steps, equals one scan.
+def test_split_scan_and_decode_equal_one_scan():
+    rng = np.random.default_rng(10)
+    Bt, L, H, R, P, N = 2, 40, 2, 2, 3, 8
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N)
+    h0 = rng.standard_normal((Bt, H, N, P))
+    Bp = rng.standard_normal((Bt, H, R, N))
+    xp = rng.standard_normal((Bt, H, R, P))
+    args = lambda sl: (x[:, sl], Bm[:, sl], Cm[:, sl], dt[:, sl], A, theta[:, sl], lam[:, sl])
+    y, hL, BL, xL = oracle.scan(*args(slice(0, L)), h0=h0, Bprev=Bp, xprev=xp)
+    L1 = 17
+    y1, h1, B1, x1 = oracle.scan(*args(slice(0, L1)), h0=h0, Bprev=Bp, xprev=xp)
+    y2, h2, B2, x2 = oracle.scan(*args(slice(L1, L)), h0=h1, Bprev=B1, xprev=x1)
+    np.testing.assert_array_equal(np.concatenate([y1, y2], axis=1), y)
+    np.testing.assert_array_equal(h2, hL)
+    h, Bs, xs = h1, B1, x1
+    for t in range(L1, L):
+        yt, h, Bs, xs = oracle.decode_step(x[:, t], Bm[:, t], Cm[:, t], dt[:, t], A,
+                                           theta[:, t], lam[:, t], h, Bs, xs)
+        np.testing.assert_array_equal(yt, y[:, t])
+    np.testing.assert_array_equal(h, hL)
+    np.testing.assert_array_equal(Bs, BL)
+    np.testing.assert_array_equal(xs, xL)
+
+
+def test_empty_sequence_passes_state_through():
+    rng = np.random.default_rng(11)
+    Bt, H, R, P, N = 2, 3, 2, 4, 6
+    z = lambda *s: np.zeros(s)
+    h0 = rng.standard_normal((Bt, H, N, P))
+    Bp = rng.standard_normal((Bt, H, R, N))
+    xp = rng.standard_normal((Bt, H, R, P))
+    y, hL, BL, xL = oracle.scan(z(Bt, 0, H, R, P), z(Bt, 0, H, R, N), z(Bt, 0, H, R, N),
+                                z(Bt, 0, H), -np.ones(H), z(Bt, 0, H, N // 2), z(Bt, 0, H),
+                                h0=h0, Bprev=Bp, xprev=xp)
+    assert y.shape == (Bt, 0, H, R, P)
+    np.testing.assert_array_equal(hL, h0)
+    np.testing.assert_array_equal(BL, Bp)
+    np.testing.assert_array_equal(xL, xp)
+
+
+# ---------------------------------------------------------------------------
+# A worked example derived by hand (tests/golden/worked_example.json holds the
+# inputs, the derivation and the exact expected values).
+def test_hand_worked_example():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        g = json.load(f)
+    L = len(g["x"])
+    y, hL, BL, xL = oracle.scan(np.array(g["x"], float).reshape(1, L, 1, 1, 1),
+                                np.array(g["B"], float).reshape(1, L, 1, 1, 2),
+                                np.array(g["C"], float).reshape(1, L, 1, 1, 2),
+                                np.array(g["dt"], float).reshape(1, L, 1),
+                                np.array([g["A"]], float),
+                                np.array(g["theta"], float).reshape(1, L, 1, 1),
+                                np.array(g["lam"], float).reshape(1, L, 1))
+    np.testing.assert_allclose(y.ravel(), g["expect_y"], atol=1e-12)
+    np.testing.assert_allclose(hL.ravel(), g["expect_h"], atol=1e-12)
+    np.testing.assert_array_equal(BL.ravel(), g["B"][-1])
+    np.testing.assert_array_equal(xL.ravel(), [g["x"][-1]])
