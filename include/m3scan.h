@@ -1,0 +1,181 @@
+/*
+ * m3scan.h -- C ABI of libm3scan, the MI355X (gfx950) implementation of the
+ * Mamba-3 sequence mixer: chunked prefill (m3_scan_fwd) and one autoregressive
+ * step (m3_decode_step).
+ *
+ * The operation (per batch row b and head h, t = 1..L):
+ *
+ *   h_t = alpha_t R_t h_{t-1} + beta_t R_t B_{t-1} X_{t-1} + gamma_t B_t X_t
+ *   y_t = C_t^T h_t
+ *   alpha_t = exp(dt_t A_h),  beta_t = (1 - lam_t) dt_t alpha_t,  gamma_t = lam_t dt_t
+ *
+ *   - Exponential-trapezoidal discretization: Mamba-3 summary on b-lab.team,
+ *     section 1 "Exponential-Trapezoidal Discretization" (recurrence and the
+ *     alpha/beta/gamma shorthand; lam = 1 is Mamba-2's Euler rule, lam = 1/2
+ *     the classic trapezoid).
+ *   - R_t: block-diagonal rotation with N/2 blocks R(dt_t theta_t[i]) =
+ *     [[cos, -sin], [sin, cos]] on adjacent state rows (2i, 2i+1): same page,
+ *     section 2 "Complex-Valued SSM" (real form of the complex SSM,
+ *     Proposition 2).  The library applies it as data-dependent RoPE on B and
+ *     C (Proposition 3, the "RoPE trick").  R_t also carries the previous
+ *     endpoint B_{t-1} X_{t-1} across the step (the trapezoid's left endpoint
+ *     is propagated by the same flow as the state).
+ *   - MIMO: B_t, C_t are N x R, X_t is R x P; the input term B_t X_t sums the
+ *     R ranks and the readout C_t^T h_t gives R outputs of length P: same
+ *     page, section 3 "MIMO".
+ *
+ * Data layout.  Every tensor is dense, row-major, contiguous:
+ *   x, y            [batch, seqlen, nheads, rank, headdim]     io dtype
+ *   B, C            [batch, seqlen, nheads, rank, dstate]      io dtype
+ *   dt, lam         [batch, seqlen, nheads]                    float32
+ *   theta           [batch, seqlen, nheads, dstate/2]          float32
+ *   A               [nheads]                                   float32
+ *   state record:
+ *     h             [batch, nheads, dstate, headdim]           float32
+ *     B_prev        [batch, nheads, rank, dstate]              io dtype
+ *     x_prev        [batch, nheads, rank, headdim]             io dtype
+ * The state record (h_t, B_t, X_t) is everything needed to continue: a scan
+ * split into several calls, or a scan followed by decode steps, equals one
+ * scan.  h is the true state after the last token; the record's (B, X) pair is
+ * the last token's input, which the next token's trapezoid term needs.
+ *
+ * io dtype is M3_F32 (float) or M3_BF16 (bfloat16).  Arithmetic is float32
+ * (bf16 products on matrix cores accumulate in float32 for M3_BF16).
+ *
+ * Ownership and execution.  All pointers are device pointers owned by the
+ * caller; the library keeps none of them after a call returns.  m3_scan_fwd
+ * and m3_decode_step allocate nothing, never synchronise, and enqueue their
+ * kernels on the caller's stream (a hipStream_t passed as void*, NULL = the
+ * default stream); the results are ready when that stream reaches them.
+ * Calls are reentrant; the library holds no global mutable state besides a
+ * thread-local record of the last HIP error.
+ *
+ * Errors.  Every entry point validates all arguments before making any HIP
+ * call and returns M3_OK or one of the negative m3_status codes below.  On an
+ * error nothing has been enqueued.  NaN or Inf inputs are not errors: they
+ * propagate into the outputs (within the dense chunk form a non-finite input
+ * may reach outputs of earlier tokens of the same chunk).
+ */
+#ifndef M3SCAN_H
+#define M3SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define M3_ABI_VERSION 1
+
+typedef enum {
+    M3_F32 = 0,
+    M3_BF16 = 1
+} m3_dtype;
+
+typedef enum {
+    M3_OK = 0,
+    M3_ERR_NULL = -1,        /* a required pointer is NULL, or the state record is partial */
+    M3_ERR_SHAPE = -2,       /* a negative dimension, zero headdim/dstate/rank, odd dstate */
+    M3_ERR_UNSUPPORTED = -3, /* dstate, headdim, rank or chunk outside the compiled set */
+    M3_ERR_DTYPE = -4,       /* io_dtype is not an m3_dtype */
+    M3_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+    M3_ERR_WORKSPACE = -6,   /* workspace missing or smaller than m3_scan_workspace_bytes */
+    M3_ERR_ALIAS = -7,       /* an output overlaps an input it must not overlap */
+    M3_ERR_HIP = -8          /* a HIP call failed; see m3_last_hip_error() */
+} m3_status;
+
+/*
+ * Arguments of m3_scan_fwd.
+ *
+ * Sizes: batch >= 0, seqlen >= 0, nheads >= 0 (a zero batch or head count is a
+ * no-op); headdim P, dstate N (even), rank R >= 1.  Supported sets are listed
+ * by m3_scan_supported().
+ *
+ * chunk: chunk length Q of the chunked (SSD) form, or 0 for the library's
+ * choice.  Results do not depend on Q beyond float32 rounding.
+ * p_split, segments: work decomposition (0 = library's choice).  p_split
+ * divides headdim into independent column slices; segments > 1 splits the
+ * sequence into that many pieces whose boundary states are combined through a
+ * workspace.  Neither changes the result beyond float32 rounding.
+ *
+ * State record in (h_in, B_prev_in, x_prev_in): all three NULL means a zero
+ * state and no previous token; otherwise all three must be given.
+ * State record out (h_out, B_prev_out, x_prev_out): all three NULL, or all
+ * three given; they must not overlap any input of the call.  With seqlen = 0
+ * the record is copied through (or zeroed when no input record is given).
+ * y may be NULL only when seqlen * batch * nheads == 0.
+ * workspace: device memory of at least m3_scan_workspace_bytes(args) bytes,
+ * 256-byte aligned (may be NULL when that size is 0).
+ */
+typedef struct {
+    int64_t batch, seqlen, nheads, headdim, dstate, rank;
+    int32_t chunk;
+    int32_t io_dtype;                 /* m3_dtype */
+    int32_t p_split;                  /* 0 = auto */
+    int32_t segments;                 /* 0 = auto */
+    const void *x, *B, *C;            /* io dtype */
+    const float *dt, *A, *theta, *lam;
+    const float *h_in;                /* optional state record in */
+    const void *B_prev_in, *x_prev_in;
+    void *y;                          /* io dtype */
+    float *h_out;                     /* optional state record out */
+    void *B_prev_out, *x_prev_out;
+    void *workspace;
+    size_t workspace_bytes;
+} m3_scan_args;
+
+/*
+ * Arguments of m3_decode_step: one token for every (batch, head).
+ *   x [batch, nheads, rank, headdim], B, C [batch, nheads, rank, dstate] (io dtype)
+ *   dt, lam [batch, nheads], theta [batch, nheads, dstate/2], A [nheads] (float32)
+ *   h [batch, nheads, dstate, headdim] float32, B_prev, x_prev: the state
+ *   record, read and then overwritten in place with (h_t, B_t, X_t).
+ *   y [batch, nheads, rank, headdim] (io dtype) receives C_t^T h_t.
+ * y must not overlap the state record or the step inputs.
+ */
+typedef struct {
+    int64_t batch, nheads, headdim, dstate, rank;
+    int32_t io_dtype;
+    int32_t reserved;
+    const void *x, *B, *C;
+    const float *dt, *A, *theta, *lam;
+    float *h;
+    void *B_prev, *x_prev;
+    void *y;
+} m3_decode_args;
+
+/* Chunked prefill: y and (optionally) the state record after the last token.
+ * Enqueued on `stream`; returns before the work completes. */
+m3_status m3_scan_fwd(const m3_scan_args *args, void *stream);
+
+/* Workspace bytes that m3_scan_fwd needs for these arguments (0 when the call
+ * runs in a single pass).  Depends only on sizes, dtype, chunk, p_split and
+ * segments.  Returns 0 for arguments that m3_scan_fwd would reject. */
+size_t m3_scan_workspace_bytes(const m3_scan_args *args);
+
+/* One decode step, state record updated in place.  Enqueued on `stream`. */
+m3_status m3_decode_step(const m3_decode_args *args, void *stream);
+
+/* 1 when (dstate, headdim, rank, chunk, io_dtype) is in the compiled set of
+ * m3_scan_fwd (chunk 0 = the default chunk), else 0. */
+int m3_scan_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t chunk,
+                      int32_t io_dtype);
+
+/* 1 when (dstate, headdim, rank, io_dtype) is supported by m3_decode_step. */
+int m3_decode_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t io_dtype);
+
+/* Static description of a status code.  Never NULL. */
+const char *m3_status_string(m3_status status);
+
+/* hipError_t value of the last failed HIP call on this thread (0 if none). */
+int m3_last_hip_error(void);
+
+/* M3_ABI_VERSION of the built library. */
+int m3_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M3SCAN_H */

@@ -1,0 +1,240 @@
+"""Thin Python binding of libm3scan (ctypes).  Argument marshalling only:
+every step of the mixer runs in the HIP library; torch provides device memory
+and the current stream.  There is no fallback: if the library is missing the
+calls raise.
+
+Names follow the C ABI (include/m3scan.h): m3_scan_fwd, m3_decode_step,
+m3_scan_workspace_bytes, m3_scan_supported, m3_decode_supported,
+m3_status_string, m3_abi_version.
+
+Layouts (contiguous):
+    x, y [Bt, L, H, R, P]   B, C [Bt, L, H, R, N]   dt, lam [Bt, L, H]
+    theta [Bt, L, H, N/2]   A [H]
+    state: h [Bt, H, N, P] float32, B_prev [Bt, H, R, N], x_prev [Bt, H, R, P]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libm3scan.so")
+
+M3_F32, M3_BF16 = 0, 1
+_STATUS = {0: "M3_OK", -1: "M3_ERR_NULL", -2: "M3_ERR_SHAPE", -3: "M3_ERR_UNSUPPORTED",
+           -4: "M3_ERR_DTYPE", -5: "M3_ERR_ALIGN", -6: "M3_ERR_WORKSPACE", -7: "M3_ERR_ALIAS",
+           -8: "M3_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+
+
+class ScanArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("rank", ctypes.c_int64),
+                ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("p_split", ctypes.c_int32), ("segments", ctypes.c_int32),
+                ("x", _vp), ("B", _vp), ("C", _vp),
+                ("dt", _vp), ("A", _vp), ("theta", _vp), ("lam", _vp),
+                ("h_in", _vp), ("B_prev_in", _vp), ("x_prev_in", _vp),
+                ("y", _vp), ("h_out", _vp), ("B_prev_out", _vp), ("x_prev_out", _vp),
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("rank", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
+                ("x", _vp), ("B", _vp), ("C", _vp),
+                ("dt", _vp), ("A", _vp), ("theta", _vp), ("lam", _vp),
+                ("h", _vp), ("B_prev", _vp), ("x_prev", _vp), ("y", _vp)]
+
+
+class M3Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (what, _STATUS.get(status, status),
+                                                  m3_status_string(status)))
+
+
+_lib = None
+
+
+def load_library():
+    """Load libm3scan.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libm3scan.so is not built (%s); run "
+                               "`python -m mamba_selective_ssm_amd.build`" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+        lib.m3_scan_fwd.restype = ctypes.c_int
+        lib.m3_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp]
+        lib.m3_decode_step.restype = ctypes.c_int
+        lib.m3_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+        lib.m3_scan_workspace_bytes.restype = ctypes.c_size_t
+        lib.m3_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanArgs)]
+        lib.m3_scan_supported.restype = ctypes.c_int
+        lib.m3_scan_supported.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int32, ctypes.c_int32]
+        lib.m3_decode_supported.restype = ctypes.c_int
+        lib.m3_decode_supported.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int32]
+        lib.m3_status_string.restype = ctypes.c_char_p
+        lib.m3_status_string.argtypes = [ctypes.c_int]
+        lib.m3_last_hip_error.restype = ctypes.c_int
+        lib.m3_last_hip_error.argtypes = []
+        lib.m3_abi_version.restype = ctypes.c_int
+        lib.m3_abi_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def m3_status_string(status: int) -> str:
+    return load_library().m3_status_string(int(status)).decode()
+
+
+def m3_abi_version() -> int:
+    return load_library().m3_abi_version()
+
+
+def m3_scan_supported(dstate: int, headdim: int, rank: int, chunk: int, io_dtype: int) -> bool:
+    return bool(load_library().m3_scan_supported(dstate, headdim, rank, chunk, io_dtype))
+
+
+def m3_decode_supported(dstate: int, headdim: int, rank: int, io_dtype: int) -> bool:
+    return bool(load_library().m3_decode_supported(dstate, headdim, rank, io_dtype))
+
+
+class State(NamedTuple):
+    """State record: true state h plus the last token's (B, X)."""
+    h: torch.Tensor        # [Bt, H, N, P] float32
+    B_prev: torch.Tensor   # [Bt, H, R, N] io dtype
+    x_prev: torch.Tensor   # [Bt, H, R, P] io dtype
+
+
+def zero_state(batch, nheads, headdim, dstate, rank, dtype, device) -> State:
+    return State(torch.zeros(batch, nheads, dstate, headdim, dtype=torch.float32, device=device),
+                 torch.zeros(batch, nheads, rank, dstate, dtype=dtype, device=device),
+                 torch.zeros(batch, nheads, rank, headdim, dtype=dtype, device=device))
+
+
+def _io_code(dtype) -> int:
+    if dtype == torch.float32:
+        return M3_F32
+    if dtype == torch.bfloat16:
+        return M3_BF16
+    raise TypeError("io dtype must be float32 or bfloat16, got %s" % dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def m3_scan_fwd(x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
+                chunk: int = 0, p_split: int = 0, segments: int = 0,
+                return_state: bool = True, y: Optional[torch.Tensor] = None,
+                state_out: Optional[State] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None):
+    """Chunked prefill.  Returns (y, State after the last token or None)."""
+    lib = load_library()
+    Bt, L, H, R, P = x.shape
+    N = B.shape[-1]
+    io = _io_code(x.dtype)
+    _check(x, "x", (Bt, L, H, R, P), x.dtype)
+    _check(B, "B", (Bt, L, H, R, N), x.dtype)
+    _check(C, "C", (Bt, L, H, R, N), x.dtype)
+    _check(dt, "dt", (Bt, L, H), torch.float32)
+    _check(lam, "lam", (Bt, L, H), torch.float32)
+    _check(theta, "theta", (Bt, L, H, N // 2), torch.float32)
+    _check(A, "A", (H,), torch.float32)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (Bt, L, H, R, P), x.dtype)
+    if state is not None:
+        _check(state.h, "state.h", (Bt, H, N, P), torch.float32)
+        _check(state.B_prev, "state.B_prev", (Bt, H, R, N), x.dtype)
+        _check(state.x_prev, "state.x_prev", (Bt, H, R, P), x.dtype)
+    if return_state and state_out is None:
+        state_out = State(torch.empty(Bt, H, N, P, dtype=torch.float32, device=x.device),
+                          torch.empty(Bt, H, R, N, dtype=x.dtype, device=x.device),
+                          torch.empty(Bt, H, R, P, dtype=x.dtype, device=x.device))
+    a = ScanArgs(batch=Bt, seqlen=L, nheads=H, headdim=P, dstate=N, rank=R,
+                 chunk=chunk, io_dtype=io, p_split=p_split, segments=segments,
+                 x=_ptr(x), B=_ptr(B), C=_ptr(C), dt=_ptr(dt), A=_ptr(A),
+                 theta=_ptr(theta), lam=_ptr(lam),
+                 h_in=_ptr(state.h) if state else None,
+                 B_prev_in=_ptr(state.B_prev) if state else None,
+                 x_prev_in=_ptr(state.x_prev) if state else None,
+                 y=_ptr(y),
+                 h_out=_ptr(state_out.h) if state_out else None,
+                 B_prev_out=_ptr(state_out.B_prev) if state_out else None,
+                 x_prev_out=_ptr(state_out.x_prev) if state_out else None,
+                 workspace=None, workspace_bytes=0)
+    need = lib.m3_scan_workspace_bytes(ctypes.byref(a))
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(int(need), dtype=torch.uint8, device=x.device)
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib.m3_scan_fwd(ctypes.byref(a), _stream_handle(stream))
+    if st != 0:
+        raise M3Error(st, "m3_scan_fwd")
+    return y, state_out
+
+
+def m3_scan_workspace_bytes(x, B, *, chunk=0, p_split=0, segments=0) -> int:
+    Bt, L, H, R, P = x.shape
+    a = ScanArgs(batch=Bt, seqlen=L, nheads=H, headdim=P, dstate=B.shape[-1], rank=R,
+                 chunk=chunk, io_dtype=_io_code(x.dtype), p_split=p_split, segments=segments)
+    return int(load_library().m3_scan_workspace_bytes(ctypes.byref(a)))
+
+
+def m3_decode_step(x, B, C, dt, A, theta, lam, state: State, *,
+                   y: Optional[torch.Tensor] = None, stream=None):
+    """One token for every (batch, head); ``state`` is updated in place.  Returns y_t."""
+    lib = load_library()
+    Bt, H, R, P = x.shape
+    N = B.shape[-1]
+    io = _io_code(x.dtype)
+    _check(x, "x", (Bt, H, R, P), x.dtype)
+    _check(B, "B", (Bt, H, R, N), x.dtype)
+    _check(C, "C", (Bt, H, R, N), x.dtype)
+    _check(dt, "dt", (Bt, H), torch.float32)
+    _check(lam, "lam", (Bt, H), torch.float32)
+    _check(theta, "theta", (Bt, H, N // 2), torch.float32)
+    _check(A, "A", (H,), torch.float32)
+    _check(state.h, "state.h", (Bt, H, N, P), torch.float32)
+    _check(state.B_prev, "state.B_prev", (Bt, H, R, N), x.dtype)
+    _check(state.x_prev, "state.x_prev", (Bt, H, R, P), x.dtype)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (Bt, H, R, P), x.dtype)
+    a = DecodeArgs(batch=Bt, nheads=H, headdim=P, dstate=N, rank=R, io_dtype=io,
+                   x=_ptr(x), B=_ptr(B), C=_ptr(C), dt=_ptr(dt), A=_ptr(A),
+                   theta=_ptr(theta), lam=_ptr(lam), h=_ptr(state.h),
+                   B_prev=_ptr(state.B_prev), x_prev=_ptr(state.x_prev), y=_ptr(y))
+    st = lib.m3_decode_step(ctypes.byref(a), _stream_handle(stream))
+    if st != 0:
+        raise M3Error(st, "m3_decode_step")
+    return y

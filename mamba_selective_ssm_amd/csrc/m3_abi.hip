@@ -1,0 +1,229 @@
+// C ABI of libm3scan: argument validation (complete before any HIP call),
+// variant selection and launch.  See include/m3scan.h for the contract.
+#include "m3scan.h"
+
+#include <stdint.h>
+#include <string.h>
+
+#include "m3_internal.hpp"
+#include "m3_scan_kernel.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + static_cast<uintptr_t>(bytes > 0 ? bytes : 0)};
+}
+
+bool overlaps(const Range& a, const Range& b)
+{
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int io_size(int dt) { return dt == M3_F32 ? 4 : 2; }
+
+int default_chunk(int64_t R) { return R == 1 ? 64 : (R == 2 ? 32 : 16); }
+
+template <typename F>
+void for_each_variant(F&& f)
+{
+    using table_fn = const m3::ScanVariant* (*)(int*);
+    const table_fn tables[] = {m3::scan_variants_f32, m3::scan_variants_bf16a,
+                               m3::scan_variants_bf16b};
+    for (table_fn t : tables) {
+        int n = 0;
+        const m3::ScanVariant* v = t(&n);
+        for (int i = 0; i < n; ++i) f(v[i]);
+    }
+}
+
+// The compiled variant for these sizes.  chunk / p_split 0 = library choice:
+// the widest headdim slice that still gives at least 256 workgroups (one per
+// compute unit), else the narrowest slice.
+const m3::ScanVariant* pick_scan(int io, int64_t N, int64_t R, int64_t P, int chunk,
+                                 int p_split, int64_t nbh)
+{
+    const int Q = chunk ? chunk : default_chunk(R);
+    const m3::ScanVariant* best = nullptr;
+    const m3::ScanVariant* narrowest = nullptr;
+    for_each_variant([&](const m3::ScanVariant& v) {
+        if (v.io != io || v.N != N || v.R != R || v.Q != Q) return;
+        if (P % v.PS != 0) return;
+        if (p_split != 0 && P / v.PS != p_split) return;
+        if (narrowest == nullptr || v.PS < narrowest->PS) narrowest = &v;
+        if (nbh * (P / v.PS) >= 256 && (best == nullptr || v.PS > best->PS)) best = &v;
+    });
+    return best ? best : narrowest;
+}
+
+m3_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return M3_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return M3_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int m3_abi_version(void) { return M3_ABI_VERSION; }
+
+int m3_last_hip_error(void) { return g_last_hip_error; }
+
+const char* m3_status_string(m3_status s)
+{
+    switch (s) {
+    case M3_OK: return "ok";
+    case M3_ERR_NULL: return "required pointer is NULL or state record incomplete";
+    case M3_ERR_SHAPE: return "invalid shape (negative or zero size, odd dstate)";
+    case M3_ERR_UNSUPPORTED: return "dstate/headdim/rank/chunk outside the compiled set";
+    case M3_ERR_DTYPE: return "unknown io dtype";
+    case M3_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case M3_ERR_WORKSPACE: return "workspace missing or too small";
+    case M3_ERR_ALIAS: return "output overlaps an input";
+    case M3_ERR_HIP: return "HIP call failed";
+    }
+    return "unknown status";
+}
+
+int m3_scan_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t chunk,
+                      int32_t io_dtype)
+{
+    if (io_dtype != M3_F32 && io_dtype != M3_BF16) return 0;
+    if (dstate < 2 || headdim < 1 || rank < 1 || chunk < 0) return 0;
+    return pick_scan(io_dtype, dstate, rank, headdim, chunk, 0, 1 << 20) != nullptr;
+}
+
+int m3_decode_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t io_dtype)
+{
+    return m3::decode_supported(dstate, headdim, rank, io_dtype) ? 1 : 0;
+}
+
+size_t m3_scan_workspace_bytes(const m3_scan_args* a)
+{
+    (void)a;
+    return 0;
+}
+
+m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
+{
+    if (a == nullptr) return M3_ERR_NULL;
+    const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
+    const int64_t P = a->headdim, N = a->dstate, R = a->rank;
+    if (Bt < 0 || L < 0 || H < 0 || P < 1 || N < 1 || R < 1 || (N % 2) != 0) return M3_ERR_SHAPE;
+    if (a->chunk < 0 || a->p_split < 0 || a->segments < 0) return M3_ERR_SHAPE;
+    if (a->io_dtype != M3_F32 && a->io_dtype != M3_BF16) return M3_ERR_DTYPE;
+    const int64_t nbh = Bt * H;
+    if (nbh > (int64_t)1 << 28) return M3_ERR_UNSUPPORTED;
+    const m3::ScanVariant* v = pick_scan(a->io_dtype, N, R, P, a->chunk, a->p_split,
+                                         nbh > 0 ? nbh : 1);
+    if (v == nullptr) return M3_ERR_UNSUPPORTED;
+    if (a->segments > 1) return M3_ERR_UNSUPPORTED;
+    if (nbh == 0) return M3_OK;
+
+    const bool st_in = a->h_in || a->B_prev_in || a->x_prev_in;
+    const bool st_out = a->h_out || a->B_prev_out || a->x_prev_out;
+    if (st_in && !(a->h_in && a->B_prev_in && a->x_prev_in)) return M3_ERR_NULL;
+    if (st_out && !(a->h_out && a->B_prev_out && a->x_prev_out)) return M3_ERR_NULL;
+    if (a->A == nullptr) return M3_ERR_NULL;
+    if (L > 0 && (!a->x || !a->B || !a->C || !a->dt || !a->theta || !a->lam || !a->y))
+        return M3_ERR_NULL;
+
+    const void* ptrs[] = {a->x, a->B, a->C, a->dt, a->A, a->theta, a->lam, a->h_in,
+                          a->B_prev_in, a->x_prev_in, a->y, a->h_out, a->B_prev_out,
+                          a->x_prev_out};
+    for (const void* q : ptrs)
+        if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
+
+    const int e = io_size(a->io_dtype);
+    const int64_t tok = Bt * L * H;
+    const Range in[] = {
+        range_of(a->x, tok * R * P * e),         range_of(a->B, tok * R * N * e),
+        range_of(a->C, tok * R * N * e),         range_of(a->dt, tok * 4),
+        range_of(a->A, H * 4),                   range_of(a->theta, tok * (N / 2) * 4),
+        range_of(a->lam, tok * 4),               range_of(a->h_in, nbh * N * P * 4),
+        range_of(a->B_prev_in, nbh * R * N * e), range_of(a->x_prev_in, nbh * R * P * e),
+    };
+    const Range out[] = {
+        range_of(a->y, tok * R * P * e),         range_of(a->h_out, nbh * N * P * 4),
+        range_of(a->B_prev_out, nbh * R * N * e), range_of(a->x_prev_out, nbh * R * P * e),
+    };
+    for (const Range& o : out) {
+        for (const Range& i : in)
+            if (overlaps(o, i)) return M3_ERR_ALIAS;
+    }
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(out[i], out[j])) return M3_ERR_ALIAS;
+    if (a->workspace_bytes < m3_scan_workspace_bytes(a)) return M3_ERR_WORKSPACE;
+
+    m3::ScanParams p;
+    memset(&p, 0, sizeof(p));
+    p.x = a->x; p.B = a->B; p.C = a->C;
+    p.dt = a->dt; p.A = a->A; p.theta = a->theta; p.lam = a->lam;
+    p.h_in = a->h_in; p.Bp_in = a->B_prev_in; p.xp_in = a->x_prev_in;
+    p.y = a->y; p.h_out = a->h_out; p.Bp_out = a->B_prev_out; p.xp_out = a->x_prev_out;
+    p.batch = Bt; p.L = L; p.H = H; p.P = P;
+    p.p_split = (int)(P / v->PS);
+    p.nbh = (int)nbh;
+    return hip_status(v->fn(p, static_cast<hipStream_t>(stream)));
+}
+
+m3_status m3_decode_step(const m3_decode_args* a, void* stream)
+{
+    if (a == nullptr) return M3_ERR_NULL;
+    const int64_t Bt = a->batch, H = a->nheads, P = a->headdim, N = a->dstate, R = a->rank;
+    if (Bt < 0 || H < 0 || P < 1 || N < 1 || R < 1 || (N % 2) != 0) return M3_ERR_SHAPE;
+    if (a->io_dtype != M3_F32 && a->io_dtype != M3_BF16) return M3_ERR_DTYPE;
+    if (!m3::decode_supported(N, P, R, a->io_dtype)) return M3_ERR_UNSUPPORTED;
+    const int64_t nbh = Bt * H;
+    if (nbh > (int64_t)1 << 30) return M3_ERR_UNSUPPORTED;
+    if (nbh == 0) return M3_OK;
+    const void* ptrs[] = {a->x, a->B, a->C, a->dt, a->A, a->theta, a->lam,
+                          a->h, a->B_prev, a->x_prev, a->y};
+    for (const void* q : ptrs)
+        if (q == nullptr) return M3_ERR_NULL;
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return M3_ERR_ALIGN;
+    const int e = io_size(a->io_dtype);
+    const Range in[] = {
+        range_of(a->x, nbh * R * P * e), range_of(a->B, nbh * R * N * e),
+        range_of(a->C, nbh * R * N * e), range_of(a->dt, nbh * 4), range_of(a->A, H * 4),
+        range_of(a->theta, nbh * (N / 2) * 4), range_of(a->lam, nbh * 4),
+    };
+    const Range rec[] = {
+        range_of(a->h, nbh * N * P * 4), range_of(a->B_prev, nbh * R * N * e),
+        range_of(a->x_prev, nbh * R * P * e),
+    };
+    const Range y = range_of(a->y, nbh * R * P * e);
+    for (const Range& r : rec) {
+        if (overlaps(y, r)) return M3_ERR_ALIAS;
+        for (const Range& i : in)
+            if (overlaps(r, i)) return M3_ERR_ALIAS;
+    }
+    for (const Range& i : in)
+        if (overlaps(y, i)) return M3_ERR_ALIAS;
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(rec[i], rec[j])) return M3_ERR_ALIAS;
+
+    m3::DecodeParams p;
+    p.x = a->x; p.B = a->B; p.C = a->C;
+    p.dt = a->dt; p.A = a->A; p.theta = a->theta; p.lam = a->lam;
+    p.h = a->h; p.Bp = a->B_prev; p.xp = a->x_prev; p.y = a->y;
+    p.H = H; p.N = (int)N; p.P = (int)P; p.R = (int)R; p.nbh = nbh;
+    return hip_status(m3::launch_decode(p, a->io_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

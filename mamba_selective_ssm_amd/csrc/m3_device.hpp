@@ -1,0 +1,135 @@
+// Device-side helpers for libm3scan (gfx950 only): operand fragments for the
+// 16x16 matrix-core tiles, element conversions, vector loads.
+//
+// Matrix-core tile conventions used throughout (wave64, 16x16 output tile):
+//   A operand (16 x K): lane l supplies row (l % 16), K-slots g*8 + e (g = l/16,
+//                       e = 0..7) -- 8 values per lane per 32-wide K block.
+//   B operand (K x 16): lane l supplies column (l % 16), the same K-slots.
+//   D (16 x 16 fp32):   lane l holds column (l % 16), rows g*4 + i, i = 0..3.
+// Which physical K index a slot carries is up to the caller, as long as A and
+// B use the same assignment; the kernels exploit that to avoid transposes.
+// bf16 operands use one v_mfma_f32_16x16x32_bf16 per 32-wide K block; fp32
+// operands use eight v_mfma_f32_16x16x4_f32 (slot e of every lane group forms
+// the 4-wide K block of the e-th instruction).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m3 {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+// 8 K-slots of one lane.
+template <typename OP> struct Frag;
+template <> struct Frag<bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void set(int e, float x) { v[e] = (bf16)x; }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)0.0f;
+    }
+};
+template <> struct Frag<float> {
+    float v[8];
+    __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+    }
+};
+
+__device__ __forceinline__ void mma(const Frag<bf16>& a, const Frag<bf16>& b, f32x4& c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(const Frag<float>& a, const Frag<float>& b, f32x4& c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+}
+
+// 8 contiguous operand elements from LDS (16-byte aligned for bf16, 32 for fp32).
+__device__ __forceinline__ void lds_frag8(Frag<bf16>& f, const bf16* p) {
+    f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void lds_frag8(Frag<float>& f, const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+}
+// Two runs of 4 contiguous elements: slots 0..3 from p0, slots 4..7 from p1.
+__device__ __forceinline__ void lds_frag4x2(Frag<bf16>& f, const bf16* p0, const bf16* p1) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+}
+__device__ __forceinline__ void lds_frag4x2(Frag<float>& f, const float* p0, const float* p1) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p0);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+}
+__device__ __forceinline__ void lds_frag4(Frag<bf16>& f, const bf16* p0) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = (bf16)0.0f; }
+}
+__device__ __forceinline__ void lds_frag4(Frag<float>& f, const float* p0) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = 0.0f; }
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// 8 contiguous io elements from global memory as floats.
+__device__ __forceinline__ void gload8(float (&d)[8], const bf16* p) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = (float)v[e];
+}
+__device__ __forceinline__ void gload8(float (&d)[8], const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { d[e] = a[e]; d[4 + e] = b[e]; }
+}
+// A pair of adjacent io elements (one rotation pair) from global memory.
+__device__ __forceinline__ void gload2(float& a, float& b, const bf16* p) {
+    const bf16x2 v = *reinterpret_cast<const bf16x2*>(p);
+    a = (float)v[0]; b = (float)v[1];
+}
+__device__ __forceinline__ void gload2(float& a, float& b, const float* p) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    a = v.x; b = v.y;
+}
+__device__ __forceinline__ void sstore2(bf16* p, float a, float b) {
+    bf16x2 v; v[0] = (bf16)a; v[1] = (bf16)b;
+    *reinterpret_cast<bf16x2*>(p) = v;
+}
+__device__ __forceinline__ void sstore2(float* p, float a, float b) {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+// 4 contiguous io elements to global memory.
+__device__ __forceinline__ void gstore4(bf16* p, const f32x4& v) {
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x4*>(p) = o;
+}
+__device__ __forceinline__ void gstore4(float* p, const f32x4& v) {
+    *reinterpret_cast<f32x4*>(p) = v;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace m3

@@ -1,0 +1,42 @@
+// Internal (non-ABI) declarations shared by the libm3scan translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace m3 {
+
+struct ScanParams;
+
+struct DecodeParams {
+    const void *x, *B, *C;
+    const float *dt, *A, *theta, *lam;
+    float *h;
+    void *Bp, *xp;
+    void *y;
+    int64_t H;
+    int N, P, R;
+    int64_t nbh;
+};
+
+bool decode_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
+hipError_t launch_decode(const DecodeParams& p, int io_dtype, hipStream_t stream);
+
+typedef hipError_t (*scan_launcher)(const ScanParams&, hipStream_t);
+
+// One compiled instantiation of the fused scan kernel.
+struct ScanVariant {
+    int io;        // m3_dtype
+    int N, R, Q, PS, NW;
+    size_t lds_bytes;
+    scan_launcher fn;
+};
+
+// Tables defined by the instantiation units (host functions, so that the
+// device pass never sees host function pointers).
+const ScanVariant* scan_variants_f32(int* count);
+const ScanVariant* scan_variants_bf16a(int* count);
+const ScanVariant* scan_variants_bf16b(int* count);
+
+}  // namespace m3

@@ -1,0 +1,24 @@
+// bf16 variants for the measured workload shapes: other chunk lengths and
+// wider headdim slices.
+#include "m3_scan_inst.hpp"
+
+namespace m3 {
+
+const ScanVariant* scan_variants_bf16b(int* count)
+{
+    static const ScanVariant table[] = {
+    M3_SCAN_VARIANT(bf16, 1, 64, 1, 32, 16, 4),
+    M3_SCAN_VARIANT(bf16, 1, 64, 1, 128, 16, 4),
+    M3_SCAN_VARIANT(bf16, 1, 128, 1, 32, 16, 4),
+    M3_SCAN_VARIANT(bf16, 1, 128, 1, 128, 16, 4),
+    M3_SCAN_VARIANT(bf16, 1, 64, 1, 64, 64, 4),
+    M3_SCAN_VARIANT(bf16, 1, 128, 1, 64, 64, 4),
+    M3_SCAN_VARIANT(bf16, 1, 128, 4, 16, 64, 4),
+    M3_SCAN_VARIANT(bf16, 1, 128, 4, 32, 64, 4),
+    M3_SCAN_VARIANT(bf16, 1, 128, 4, 32, 16, 4),
+    };
+    *count = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+}  // namespace m3

@@ -1,0 +1,155 @@
+"""C ABI contract, checked without a GPU: the library loads, exports every
+function that include/m3scan.h declares, the ctypes structures match the C
+layout, and argument validation returns its status codes before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m3scan.h")
+
+from mamba_selective_ssm_amd import binding  # noqa: E402
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(m3_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(re.findall(r" T (m3_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """Compile a tiny C program against the header and compare offsets."""
+    fields_s = [f[0] for f in binding.ScanArgs._fields_]
+    fields_d = [f[0] for f in binding.DecodeArgs._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "m3scan.h"', "int main(void){"]
+    src.append('printf("%zu\\n", sizeof(m3_scan_args));')
+    for f in fields_s:
+        src.append('printf("%%zu\\n", offsetof(m3_scan_args, %s));' % f)
+    src.append('printf("%zu\\n", sizeof(m3_decode_args));')
+    for f in fields_d:
+        src.append('printf("%%zu\\n", offsetof(m3_decode_args, %s));' % f)
+    src.append("return 0;}")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(c)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], stdout=subprocess.PIPE, text=True,
+                                           check=True).stdout.split()]
+    expect = [ctypes.sizeof(binding.ScanArgs)]
+    expect += [getattr(binding.ScanArgs, f).offset for f in fields_s]
+    expect += [ctypes.sizeof(binding.DecodeArgs)]
+    expect += [getattr(binding.DecodeArgs, f).offset for f in fields_d]
+    assert vals == expect
+
+
+def test_version_and_status_strings(lib):
+    assert lib.m3_abi_version() == 1
+    for code in range(-8, 1):
+        s = lib.m3_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.m3_status_string(-99) == b"unknown status"
+    assert lib.m3_last_hip_error() == 0
+
+
+FAKE = 0x7F0000000000   # never dereferenced: validation fails before any device access
+
+
+def scan_args(**kw):
+    base = dict(batch=2, seqlen=10, nheads=3, headdim=32, dstate=64, rank=1, chunk=0,
+                io_dtype=1, p_split=0, segments=0)
+    ptrs = ["x", "B", "C", "dt", "A", "theta", "lam", "y"]
+    a = binding.ScanArgs(**base)
+    for i, p in enumerate(ptrs):
+        setattr(a, p, FAKE + i * (1 << 32))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def run_scan(lib, a):
+    return lib.m3_scan_fwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dstate=63), -2), (dict(headdim=0), -2), (dict(rank=0), -2), (dict(batch=-1), -2),
+    (dict(seqlen=-5), -2), (dict(chunk=-1), -2),
+    (dict(io_dtype=7), -4),
+    (dict(dstate=48), -3), (dict(rank=3), -3), (dict(chunk=24), -3), (dict(headdim=40), -3),
+    (dict(p_split=3), -3), (dict(segments=4), -3),
+    (dict(x=None), -1), (dict(y=None), -1), (dict(theta=None), -1), (dict(A=None), -1),
+    (dict(h_in=FAKE + (20 << 32)), -1),                      # partial state record
+    (dict(h_out=FAKE + (21 << 32), B_prev_out=FAKE + (22 << 32)), -1),
+    (dict(x=FAKE + 8), -5), (dict(dt=FAKE + 4), -5),
+    (dict(y=FAKE), -7),                                      # y aliases x
+    (dict(y=FAKE + (1 << 32) + 64), -7),                     # y overlaps B
+])
+def test_scan_validation_codes(lib, kw, code):
+    assert run_scan(lib, scan_args(**kw)) == code
+
+
+def test_scan_zero_work_is_ok_without_pointers(lib):
+    a = binding.ScanArgs(batch=0, seqlen=100, nheads=4, headdim=64, dstate=64, rank=1,
+                         io_dtype=1)
+    assert run_scan(lib, a) == 0
+    a = binding.ScanArgs(batch=3, seqlen=100, nheads=0, headdim=64, dstate=64, rank=1,
+                         io_dtype=0)
+    assert run_scan(lib, a) == 0
+
+
+def test_scan_null_args(lib):
+    assert lib.m3_scan_fwd(None, None) == -1
+    assert lib.m3_decode_step(None, None) == -1
+
+
+def decode_args(**kw):
+    a = binding.DecodeArgs(batch=4, nheads=2, headdim=64, dstate=128, rank=4, io_dtype=1)
+    for i, p in enumerate(["x", "B", "C", "dt", "A", "theta", "lam", "h", "B_prev", "x_prev", "y"]):
+        setattr(a, p, FAKE + i * (1 << 32))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dstate=5), -2), (dict(rank=0), -2), (dict(io_dtype=2), -4),
+    (dict(rank=3), -3), (dict(headdim=6), -3),
+    (dict(h=None), -1), (dict(y=None), -1),
+    (dict(h=FAKE + (7 << 32) + 4), -5),
+    (dict(y=FAKE + (7 << 32)), -7),          # y aliases the state
+    (dict(B_prev=FAKE + (1 << 32)), -7),     # state record aliases a step input
+])
+def test_decode_validation_codes(lib, kw, code):
+    assert lib.m3_decode_step(ctypes.byref(decode_args(**kw)), None) == code
+
+
+def test_supported_sets(lib):
+    for io in (0, 1):
+        for N in (16, 32, 64, 128):
+            for R in (1, 2, 4):
+                assert lib.m3_scan_supported(N, 64, R, 0, io) == 1
+                assert lib.m3_decode_supported(N, 64, R, io) == 1
+    assert lib.m3_scan_supported(64, 64, 1, 32, 1) == 1
+    assert lib.m3_scan_supported(64, 64, 1, 128, 1) == 1
+    assert lib.m3_scan_supported(96, 64, 1, 0, 1) == 0
+    assert lib.m3_scan_supported(64, 24, 1, 0, 1) == 0
+    assert lib.m3_scan_workspace_bytes(ctypes.byref(scan_args())) == 0
