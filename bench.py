@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of libm3scan on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+A step is one m3_scan_fwd call (the whole chunked prefill: prefix scans,
+data-RoPE, intra-chunk tiles, state passing, outputs and final state) over one
+batch of the prefill_bf16 workload (batch 4, 16 heads, L = 2048, P = 64,
+N = 64, R = 1, bf16 I/O, fp32 state), inputs resident in HBM.  Prints one
+JSON line: whole-job tokens/s, the roofline of the scan kernel (algorithmic
+bytes per launch / its average launch time from HIP events on the launch
+stream, against 8 TB/s), the fp64 oracle's rate on this host's cores, and
+secondary lines for the MIMO, long-context and decode workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Mamba-3 scan tokens/s (chunked prefill) + decode step/s; % MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def io_bytes(w):
+    return 4 if w.io_dtype == "f32" else 2
+
+
+def scan_algorithmic_bytes(w, L=None):
+    """Minimum HBM bytes of one m3_scan_fwd: every input read once, y and the
+    final state record written once."""
+    L = w.seqlen if L is None else L
+    e = io_bytes(w)
+    R, P, N = w.rank, w.headdim, w.dstate
+    per_tok = e * (2 * R * P + 2 * R * N) + 4 * (N // 2 + 2)
+    per_bh = 4 * N * P + e * (R * N + R * P)
+    return w.batch * w.heads * (L * per_tok + per_bh) + 4 * w.heads
+
+
+def decode_algorithmic_bytes(w):
+    """One m3_decode_step: state h read and written, record (B, X) read and
+    written, step inputs read, y written."""
+    e = io_bytes(w)
+    R, P, N = w.rank, w.headdim, w.dstate
+    per_bh = 8 * N * P + 2 * e * (R * N + R * P) + e * (2 * R * N + R * P) + 4 * (N // 2 + 2) \
+        + e * R * P
+    return w.batch * w.heads * per_bh + 4 * w.heads
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mamba_selective_ssm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILE_DIR, "%s_traffic.json" % name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Run fn() warmup + steps times; returns (total seconds, mean kernel ms)
+    with HIP events recorded on the current stream around every launch."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    kms = sum(a.elapsed_time(b) for a, b in ev) / max(steps, 1)
+    return total, kms
+
+
+def bench_prefill(w, steps, warmup, torch, m3, synth, seed=1001):
+    inp = synth.make_scan_inputs(w, seed, "cuda")
+    st_out = m3.zero_state(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.torch_dtype, "cuda")
+    y = torch.empty_like(inp["x"])
+
+    def step():
+        m3.m3_scan_fwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
+                       inp["lam"], chunk=w.chunk, y=y, state_out=st_out)
+
+    total, kms = time_launches(step, steps, warmup, torch)
+    tokens = w.batch * w.seqlen
+    nbytes = scan_algorithmic_bytes(w)
+    return dict(tokens_per_s=tokens * steps / total, ms_per_step=1e3 * total / steps,
+                kernel_ms=kms, bytes=nbytes, gbs=nbytes / (kms * 1e-3) / 1e9, inputs=inp)
+
+
+def bench_decode(w, steps, warmup, torch, m3, synth, seed=1004):
+    """Decode workload: a 1024-token prefill builds the resident state, then
+    `steps` single-token steps with fresh inputs, one launch each."""
+    pre = synth.make_scan_inputs(w, seed, "cuda")
+    _, st = m3.m3_scan_fwd(pre["x"], pre["B"], pre["C"], pre["dt"], pre["A"], pre["theta"],
+                           pre["lam"], chunk=w.chunk)
+    A = pre["A"]
+    del pre
+    nsteps = warmup + steps
+    ins = [synth.make_decode_inputs(w, seed, s, A, "cuda") for s in range(nsteps)]
+    y = torch.empty(w.batch, w.heads, w.rank, w.headdim, dtype=w.torch_dtype, device="cuda")
+    it = iter(ins)
+
+    def step():
+        s = next(it)
+        m3.m3_decode_step(s["x"], s["B"], s["C"], s["dt"], s["A"], s["theta"], s["lam"], st, y=y)
+
+    total, kms = time_launches(step, steps, warmup, torch)
+    nbytes = decode_algorithmic_bytes(w)
+    return dict(steps_per_s=steps / total, tokens_per_s=w.batch * steps / total,
+                ms_per_step=1e3 * total / steps, kernel_ms=kms, bytes=nbytes,
+                gbs=nbytes / (kms * 1e-3) / 1e9)
+
+
+def cpu_baseline(w, inp, budget_s, torch):
+    """fp64 oracle on this host's cores over the same inputs (whole workload,
+    repeated until about budget_s seconds have been spent)."""
+    import oracle
+    from mamba_selective_ssm_amd.synth import to_f64_numpy
+    args = [to_f64_numpy(inp[k]) for k in ("x", "B", "C", "dt", "A", "theta", "lam")]
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.scan(*args, threads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s or reps >= 50:
+            break
+    el = time.perf_counter() - t0
+    return {"value": w.batch * w.seqlen * reps / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "whole %s workload (%d x %d tokens, %d heads) x %d repetitions, %.1f s"
+                      % (w.name, w.batch, w.seqlen, w.heads, reps, el)}
+
+
+def progress(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_bf16")
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the mixer needs no exchange "
+              "between GPUs; batch and heads shard without communication).", file=sys.stderr)
+        return 2
+
+    import torch
+    import mamba_selective_ssm_amd as m3
+    from mamba_selective_ssm_amd import synth
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}))
+        return 0
+
+    w = synth.WORKLOADS[args.workload]
+    if args.chunk:
+        w = w.with_(chunk=args.chunk)
+    progress("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
+    r = bench_prefill(w, args.steps, args.warmup, torch, m3, synth)
+    traffic = load_traffic("scan_%s" % w.name)
+    roof = {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "m3::scan_kernel", "kernel_ms": round(r["kernel_ms"], 5),
+            "algorithmic_bytes_per_launch": r["bytes"]}
+    out = {"metric": METRIC, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": w.io_dtype, "data": "synthetic",
+           "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
+                      "seqlen": w.seqlen, "headdim": w.headdim, "dstate": w.dstate,
+                      "rank": w.rank, "chunk": w.chunk, "state": "fp32",
+                      "accumulate": "fp32"},
+           "roofline": roof}
+    inp = r.pop("inputs")
+
+    if not args.no_secondary:
+        sec = {}
+        for name in ("mimo_prefill_bf16", "long_prefill_bf16"):
+            ws = synth.WORKLOADS[name]
+            progress("timing %s" % name)
+            rs = bench_prefill(ws, 5, 2, torch, m3, synth)
+            rs.pop("inputs")
+            sec[name] = {"tokens_per_s": round(rs["tokens_per_s"], 1),
+                         "kernel_ms": round(rs["kernel_ms"], 4),
+                         "hbm_gbs": round(rs["gbs"], 1),
+                         "hbm_frac": round(rs["gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": load_traffic("scan_%s" % name)}
+            torch.cuda.empty_cache()
+        wd = synth.WORKLOADS["decode"]
+        progress("timing decode: prefill + %d steps" % args.decode_steps)
+        rd = bench_decode(wd, args.decode_steps, 8, torch, m3, synth)
+        sec["decode"] = {"steps_per_s": round(rd["steps_per_s"], 1),
+                         "tokens_per_s": round(rd["tokens_per_s"], 1),
+                         "kernel_ms": round(rd["kernel_ms"], 5),
+                         "hbm_gbs": round(rd["gbs"], 1),
+                         "hbm_frac": round(rd["gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": load_traffic("decode")}
+        out["secondary"] = sec
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        progress("timing the fp64 oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, torch)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

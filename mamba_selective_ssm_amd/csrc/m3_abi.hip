@@ -19,6 +19,7 @@ struct Range {
 Range range_of(const void* p, int64_t bytes)
 {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if (p == nullptr) return Range{0, 0};   // absent pointers overlap nothing
     return Range{a, a + static_cast<uintptr_t>(bytes > 0 ? bytes : 0)};
 }
 
@@ -48,22 +49,21 @@ void for_each_variant(F&& f)
 }
 
 // The compiled variant for these sizes.  chunk / p_split 0 = library choice:
-// the widest headdim slice that still gives at least 256 workgroups (one per
-// compute unit), else the narrowest slice.
+// the widest headdim slice (no work repeated across slices); sequence
+// segments then supply the parallelism.
 const m3::ScanVariant* pick_scan(int io, int64_t N, int64_t R, int64_t P, int chunk,
                                  int p_split, int64_t nbh)
 {
     const int Q = chunk ? chunk : default_chunk(R);
     const m3::ScanVariant* best = nullptr;
-    const m3::ScanVariant* narrowest = nullptr;
     for_each_variant([&](const m3::ScanVariant& v) {
         if (v.io != io || v.N != N || v.R != R || v.Q != Q) return;
         if (P % v.PS != 0) return;
         if (p_split != 0 && P / v.PS != p_split) return;
-        if (narrowest == nullptr || v.PS < narrowest->PS) narrowest = &v;
-        if (nbh * (P / v.PS) >= 256 && (best == nullptr || v.PS > best->PS)) best = &v;
+        (void)nbh;
+        if (best == nullptr || v.PS > best->PS) best = &v;
     });
-    return best ? best : narrowest;
+    return best;
 }
 
 m3_status hip_status(hipError_t e)
@@ -71,6 +71,54 @@ m3_status hip_status(hipError_t e)
     if (e == hipSuccess) return M3_OK;
     g_last_hip_error = static_cast<int>(e);
     return M3_ERR_HIP;
+}
+
+struct ScanPlan {
+    const m3::ScanVariant* v;
+    int p_split, nseg, seg_chunks;
+    size_t ws;
+};
+
+// Everything about a call that depends only on sizes: the compiled variant,
+// the headdim split, the sequence segments and the workspace they need.
+m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
+{
+    if (a == nullptr) return M3_ERR_NULL;
+    const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
+    const int64_t P = a->headdim, N = a->dstate, R = a->rank;
+    if (Bt < 0 || L < 0 || H < 0 || P < 1 || N < 1 || R < 1 || (N % 2) != 0) return M3_ERR_SHAPE;
+    if (a->chunk < 0 || a->p_split < 0 || a->segments < 0) return M3_ERR_SHAPE;
+    if (a->io_dtype != M3_F32 && a->io_dtype != M3_BF16) return M3_ERR_DTYPE;
+    const int64_t nbh = Bt * H;
+    if (nbh > (int64_t)1 << 28) return M3_ERR_UNSUPPORTED;
+    const m3::ScanVariant* v = pick_scan(a->io_dtype, N, R, P, a->chunk, a->p_split,
+                                         nbh > 0 ? nbh : 1);
+    if (v == nullptr) return M3_ERR_UNSUPPORTED;
+    // In-chunk offsets are 32-bit: a chunk's span of every tensor must fit.
+    const int64_t wide = (N > P ? N : P) * R;
+    if ((int64_t)v->Q * H * wide >= ((int64_t)1 << 31)) return M3_ERR_UNSUPPORTED;
+    const int p_split = (int)(P / v->PS);
+    const int64_t nchunks = (L + v->Q - 1) / v->Q;
+    int64_t nseg = a->segments;
+    if (nseg == 0) {
+        // Aim for about two workgroups per compute unit, with at least four
+        // chunks per segment.
+        const int64_t per_seg = (nbh > 0 ? (nbh + 7) / 8 * 8 : 8) * p_split;
+        nseg = (512 + per_seg - 1) / per_seg;
+        if (nseg > nchunks / 4) nseg = nchunks / 4;
+        if (nseg > 64) nseg = 64;
+    }
+    if (nseg > nchunks) nseg = nchunks;
+    if (nseg < 1) nseg = 1;
+    int64_t seg_chunks = nchunks > 0 ? (nchunks + nseg - 1) / nseg : 1;
+    nseg = nchunks > 0 ? (nchunks + seg_chunks - 1) / seg_chunks : 1;
+    if (nseg * ((nbh + 7) / 8 * 8) * p_split >= ((int64_t)1 << 31)) return M3_ERR_UNSUPPORTED;
+    out->v = v;
+    out->p_split = p_split;
+    out->nseg = (int)nseg;
+    out->seg_chunks = (int)seg_chunks;
+    out->ws = v->ws_bytes(nbh, P, (int)nseg);
+    return M3_OK;
 }
 
 }  // namespace
@@ -112,24 +160,19 @@ int m3_decode_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t i
 
 size_t m3_scan_workspace_bytes(const m3_scan_args* a)
 {
-    (void)a;
-    return 0;
+    ScanPlan plan;
+    if (plan_scan(a, &plan) != M3_OK) return 0;
+    return plan.ws;
 }
 
 m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
 {
-    if (a == nullptr) return M3_ERR_NULL;
+    ScanPlan plan;
+    const m3_status ps = plan_scan(a, &plan);
+    if (ps != M3_OK) return ps;
     const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
     const int64_t P = a->headdim, N = a->dstate, R = a->rank;
-    if (Bt < 0 || L < 0 || H < 0 || P < 1 || N < 1 || R < 1 || (N % 2) != 0) return M3_ERR_SHAPE;
-    if (a->chunk < 0 || a->p_split < 0 || a->segments < 0) return M3_ERR_SHAPE;
-    if (a->io_dtype != M3_F32 && a->io_dtype != M3_BF16) return M3_ERR_DTYPE;
     const int64_t nbh = Bt * H;
-    if (nbh > (int64_t)1 << 28) return M3_ERR_UNSUPPORTED;
-    const m3::ScanVariant* v = pick_scan(a->io_dtype, N, R, P, a->chunk, a->p_split,
-                                         nbh > 0 ? nbh : 1);
-    if (v == nullptr) return M3_ERR_UNSUPPORTED;
-    if (a->segments > 1) return M3_ERR_UNSUPPORTED;
     if (nbh == 0) return M3_OK;
 
     const bool st_in = a->h_in || a->B_prev_in || a->x_prev_in;
@@ -158,15 +201,20 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     const Range out[] = {
         range_of(a->y, tok * R * P * e),         range_of(a->h_out, nbh * N * P * 4),
         range_of(a->B_prev_out, nbh * R * N * e), range_of(a->x_prev_out, nbh * R * P * e),
+        range_of(a->workspace, (int64_t)plan.ws),
     };
+    const int nout = sizeof(out) / sizeof(out[0]);
     for (const Range& o : out) {
         for (const Range& i : in)
             if (overlaps(o, i)) return M3_ERR_ALIAS;
     }
-    for (int i = 0; i < 4; ++i)
-        for (int j = i + 1; j < 4; ++j)
+    for (int i = 0; i < nout; ++i)
+        for (int j = i + 1; j < nout; ++j)
             if (overlaps(out[i], out[j])) return M3_ERR_ALIAS;
-    if (a->workspace_bytes < m3_scan_workspace_bytes(a)) return M3_ERR_WORKSPACE;
+    if (plan.ws > 0) {
+        if (a->workspace == nullptr || a->workspace_bytes < plan.ws) return M3_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0) return M3_ERR_ALIGN;
+    }
 
     m3::ScanParams p;
     memset(&p, 0, sizeof(p));
@@ -174,10 +222,13 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     p.dt = a->dt; p.A = a->A; p.theta = a->theta; p.lam = a->lam;
     p.h_in = a->h_in; p.Bp_in = a->B_prev_in; p.xp_in = a->x_prev_in;
     p.y = a->y; p.h_out = a->h_out; p.Bp_out = a->B_prev_out; p.xp_out = a->x_prev_out;
+    p.ws = static_cast<float*>(a->workspace);
     p.batch = Bt; p.L = L; p.H = H; p.P = P;
-    p.p_split = (int)(P / v->PS);
+    p.p_split = plan.p_split;
     p.nbh = (int)nbh;
-    return hip_status(v->fn(p, static_cast<hipStream_t>(stream)));
+    p.nseg = plan.nseg;
+    p.seg_chunks = plan.seg_chunks;
+    return hip_status(plan.v->fn(p, static_cast<hipStream_t>(stream)));
 }
 
 m3_status m3_decode_step(const m3_decode_args* a, void* stream)

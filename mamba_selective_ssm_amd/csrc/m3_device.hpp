@@ -133,3 +133,47 @@ __device__ __forceinline__ void gstore4(float* p, const f32x4& v) {
 constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace m3
+
+namespace m3 {
+
+// A rotation pair (two adjacent io elements) held in registers.
+template <typename T> struct IoPair;
+template <> struct IoPair<bf16> {
+    bf16x2 v;
+    __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x2*>(p); }
+    __device__ __forceinline__ float lo() const { return (float)v[0]; }
+    __device__ __forceinline__ float hi() const { return (float)v[1]; }
+};
+template <> struct IoPair<float> {
+    float2 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float2*>(p); }
+    __device__ __forceinline__ float lo() const { return v.x; }
+    __device__ __forceinline__ float hi() const { return v.y; }
+};
+
+// 8 contiguous io elements held in registers.
+template <typename T> struct IoRow8;
+template <> struct IoRow8<bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+    __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
+};
+template <> struct IoRow8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const f32x4*>(p);
+        b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
+// Four operand elements to LDS in one store.
+__device__ __forceinline__ void lds_store4(bf16* p, float a, float b, float c, float d) {
+    bf16x4 v; v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+    *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void lds_store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+}  // namespace m3

@@ -24,6 +24,7 @@ bool decode_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
 hipError_t launch_decode(const DecodeParams& p, int io_dtype, hipStream_t stream);
 
 typedef hipError_t (*scan_launcher)(const ScanParams&, hipStream_t);
+typedef size_t (*scan_ws_fn)(int64_t nbh, int64_t P, int nseg);
 
 // One compiled instantiation of the fused scan kernel.
 struct ScanVariant {
@@ -31,6 +32,7 @@ struct ScanVariant {
     int N, R, Q, PS, NW;
     size_t lds_bytes;
     scan_launcher fn;
+    scan_ws_fn ws_bytes;   // workspace bytes for a segmented call
 };
 
 // Tables defined by the instantiation units (host functions, so that the

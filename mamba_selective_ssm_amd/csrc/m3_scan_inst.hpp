@@ -5,4 +5,5 @@
 
 #define M3_SCAN_VARIANT(IO, IOCODE, N, R, Q, PS, NW)                                   \
     {IOCODE, N, R, Q, PS, NW, ::m3::ScanCfg<IO, N, PS, R, Q, NW>::lds_bytes,            \
-     &::m3::launch_scan<::m3::ScanCfg<IO, N, PS, R, Q, NW>>}
+     &::m3::launch_scan<::m3::ScanCfg<IO, N, PS, R, Q, NW>>,                          \
+     &::m3::scan_workspace_bytes<::m3::ScanCfg<IO, N, PS, R, Q, NW>>}

@@ -28,7 +28,10 @@
 // Work decomposition: one workgroup per (b, h, headdim slice of PS columns)
 // walks the chunks in order.  The fp32 state G (N x PS) stays in matrix-core
 // accumulator registers for the whole sequence, so the only HBM traffic is the
-// inputs read once and y written once.  Per chunk (Q tokens, T = Q*R rows):
+// inputs read once and y written once.  Each thread loads its share of chunk
+// c+1's raw inputs (dt, lam, theta, B/C pairs, X rows) into registers as soon
+// as chunk c's have been moved to LDS, so those loads are in flight while
+// chunk c's matrix-core phases run.  Per chunk (Q tokens, T = Q*R rows):
 //   A0  one wave: inclusive wavefront prefix scan of dt*A, weights w, gamma,
 //       and d_k = w_k e^{Lam_tot-Lam_k}.
 //   A1  all threads: angle prefix sums per (pair, token block), sincos, and
@@ -40,7 +43,17 @@
 //       e^{Lam_j} G^T Cbar^T; y written straight from the accumulators.
 //   D   each wave owns state tiles: G <- R(Phi_tot)(e^{Lam_tot} G + Bbar_d^T X)
 //       on matrix cores; the new state is staged in LDS (bf16 hi + lo split
-//       for the bf16 path) as the next chunk's state-term operand.
+//       for the bf16 path) as the next chunk's state-term operand.  The stage
+//       is double-buffered, so C and D of one chunk need no barrier between
+//       them.
+//
+// Sequence segments (more workgroups when batch*heads*slices is small): a
+// state pass walks segments 0..S-2 without outputs and records each one's end
+// state (segment 0 from the true initial state, the others from zero) with
+// its total decay and angle; the output pass then starts segment s from
+//   G = R(Phi_{s-1})(e^{Lam_{s-1}} ... ) + G_{s-1}
+// (the chunk-summary operator (a2,Phi2,S2)o(a1,Phi1,S1) =
+// (a1+a2, Phi1+Phi2, e^{a2} R(Phi2) S1 + S2) applied across segments).
 #pragma once
 
 #include "m3_device.hpp"
@@ -56,9 +69,12 @@ struct ScanParams {
     void *y;
     float *h_out;
     void *Bp_out, *xp_out;
+    float *ws;          // segment records: written by the state pass, read by the output pass
     int64_t batch, L, H, P;
     int p_split;
     int nbh;
+    int nseg;           // sequence segments (1 = single pass)
+    int seg_chunks;     // chunks per segment
 };
 
 template <typename IO, int N_, int PS_, int R_, int Q_, int NW_>
@@ -79,7 +95,7 @@ struct ScanCfg {
     static constexpr int NHT = HILO ? 2 : 1;
     static constexpr int TB0 = NT / NPR;
     static constexpr int TB = TB0 < Q ? TB0 : Q;     // token blocks of the angle scan
-    static constexpr int TPB = Q / TB;
+    static constexpr int TPB = Q / TB;               // tokens per block
     static constexpr int QT = T / 16;                // 16-row query/key tiles
     static constexpr int KB = T / 32;                // 32-row key blocks
     static constexpr int PT = PS / 16;
@@ -88,16 +104,24 @@ struct ScanCfg {
     static constexpr int TPW = (NTILES + NW - 1) / NW;
     static constexpr int QPW = (QT + NW - 1) / NW;
     static constexpr int QPL = (Q + 63) / 64;        // tokens per lane in A0
+    static constexpr int XITEMS = T * (PS / 8);      // 8-element X row pieces
+    static constexpr int XI = (XITEMS + NT - 1) / NT;
     static constexpr size_t sz_B = (size_t)T * LDB * E;
     static constexpr size_t off_B = 0;
     static constexpr size_t off_C = off_B + sz_B;
     static constexpr size_t off_X = off_C + sz_B;
     static constexpr size_t sz_X = (size_t)PS * LDX * E;
     static constexpr size_t off_H = off_X + sz_X;
-    static constexpr size_t sz_H = (size_t)NHT * PS * LDH * E;
-    static constexpr size_t off_F = off_H + sz_H;
+    static constexpr size_t sz_H1 = (size_t)NHT * PS * LDH * E;   // one state stage
+    static constexpr size_t off_F = off_H + 2 * sz_H1;
     static constexpr size_t nF = 4 * (size_t)Q + (size_t)TB * NPR + 2 * (size_t)NPR + 4;
     static constexpr size_t lds_bytes = off_F + nF * 4;
+    // The state-only pass needs no Cbar and no state stage.
+    static constexpr size_t off_X1 = off_C;
+    static constexpr size_t off_F1 = off_X1 + sz_X;
+    static constexpr size_t lds_bytes_state = off_F1 + nF * 4;
+    // Segment record: G [N][P] fp32, then Lam_seg*log2(e), then Phi_seg[N/2].
+    __host__ __device__ static int64_t rec_floats(int64_t P) { return ((int64_t)N * P + 1 + NPR + 3) / 4 * 4; }
     static_assert(T % 32 == 0, "Q*R must be a multiple of 32");
     static_assert(PS % 16 == 0, "headdim slice must be a multiple of 16");
     static_assert(N % 2 == 0 && NPR <= NT && NT % NPR == 0, "bad dstate");
@@ -105,7 +129,34 @@ struct ScanCfg {
     static_assert(lds_bytes <= 160 * 1024, "LDS budget");
 };
 
-template <class Cf>
+// One thread's share of a chunk's raw inputs, loaded a chunk ahead.
+template <class Cf> struct ChunkStage {
+    using io_t = typename Cf::io_t;
+    float a_dt[Cf::QPL], a_lm[Cf::QPL], a_dn[Cf::QPL], a_ln[Cf::QPL];  // dt, lam at t, t+1
+    float dtv[Cf::TPB], thv[Cf::TPB];                                   // angle block
+    IoPair<io_t> bq[Cf::TPB][Cf::R], cq[Cf::TPB][Cf::R];                // B, C pairs
+    IoRow8<io_t> xq[Cf::XI];                                            // X row pieces
+};
+
+template <typename OP> __device__ __forceinline__ void rope_sincos(float a, float* s, float* c);
+// bf16 operands carry 8 mantissa bits: the hardware sine/cosine suffices.
+template <> __device__ __forceinline__ void rope_sincos<bf16>(float a, float* s, float* c)
+{
+    __sincosf(a, s, c);
+}
+template <> __device__ __forceinline__ void rope_sincos<float>(float a, float* s, float* c)
+{
+    sincosf(a, s, c);
+}
+
+// 2^x with the hardware exp (results below 2^-126 flush to zero; every
+// argument here is <= 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// FULL: outputs y (and the state record when this is the last segment).
+// !FULL: state pass -- each segment except the last writes its end state
+// (from a zero start, except segment 0 which starts from the true state).
+template <class Cf, bool FULL>
 __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
 {
     using io_t = typename Cf::io_t;
@@ -115,15 +166,17 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
     constexpr int LDB = Cf::LDB, LDX = Cf::LDX, LDH = Cf::LDH;
     constexpr int TB = Cf::TB, TPB = Cf::TPB, QT = Cf::QT, KB = Cf::KB, PT = Cf::PT;
     constexpr int NTILES = Cf::NTILES, TPW = Cf::TPW, QPW = Cf::QPW, QPL = Cf::QPL;
+    constexpr int XI = Cf::XI, XITEMS = Cf::XITEMS;
+    constexpr int HSTAGE = Cf::NHT * PS * LDH;   // elements of one state stage
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     op_t* sB = reinterpret_cast<op_t*>(smem + Cf::off_B);   // [T][LDB]   Bbar rows
     op_t* sC = reinterpret_cast<op_t*>(smem + Cf::off_C);   // [T][LDB]   Cbar rows
-    op_t* sX = reinterpret_cast<op_t*>(smem + Cf::off_X);   // [PS][LDX]  X^T slice
-    op_t* sH = reinterpret_cast<op_t*>(smem + Cf::off_H);   // [NHT][PS][LDH] G^T
-    float* sL2 = reinterpret_cast<float*>(smem + Cf::off_F); // [Q] Lam_j * log2(e)
-    float* sW = sL2 + Q;                                     // [Q] w_j
-    float* sG = sW + Q;                                      // [Q] gamma_j
+    op_t* sX = reinterpret_cast<op_t*>(smem + (FULL ? Cf::off_X : Cf::off_X1));  // [PS][LDX]
+    op_t* sH = reinterpret_cast<op_t*>(smem + Cf::off_H);   // [2][NHT][PS][LDH] G^T
+    float* sLW = reinterpret_cast<float*>(smem + (FULL ? Cf::off_F : Cf::off_F1));
+    //   sLW: [Q][2] = (Lam_j * log2(e), w_j)
+    float* sG = sLW + 2 * Q;                                 // [Q] gamma_j
     float* sD = sG + Q;                                      // [Q] w_j e^{Lam_tot-Lam_j}
     float* sTot = sD + Q;                                    // [TB][NPR] angle block sums
     float* sCSt = sTot + TB * NPR;                           // [NPR][2] cos/sin Phi_tot
@@ -133,10 +186,12 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
     const int lane = tid & 63, wv = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
 
-    // Workgroup -> (b, h, headdim slice).  Consecutive workgroup ids go to
-    // different XCDs (round robin over 8), so the slices of one (b, h) are
-    // given ids 8 apart: they share an XCD and its L2 for the B/C/theta reads.
-    const int bid = blockIdx.x;
+    // Workgroup -> (segment, b, h, headdim slice).  Consecutive workgroup ids
+    // go to different XCDs (round robin over 8), so the slices of one (b, h)
+    // are given ids 8 apart: they share an XCD and its L2 for B/C/theta.
+    const int per_seg = (p.nbh + 7) / 8 * 8 * p.p_split;
+    const int seg = blockIdx.x / per_seg;
+    const int bid = blockIdx.x % per_seg;
     const int bh = (bid >> 3) / p.p_split * 8 + (bid & 7);
     const int ps = (bid >> 3) % p.p_split;
     if (bh >= p.nbh) return;
@@ -145,100 +200,235 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
     const int p0 = ps * PS;
     const float Ah = p.A[h];
 
-    const io_t* __restrict__ X = reinterpret_cast<const io_t*>(p.x);
-    const io_t* __restrict__ Bm = reinterpret_cast<const io_t*>(p.B);
-    const io_t* __restrict__ Cm = reinterpret_cast<const io_t*>(p.C);
-    const float* __restrict__ dt = p.dt;
-    const float* __restrict__ lam = p.lam;
-    const float* __restrict__ theta = p.theta;
-    io_t* __restrict__ Y = reinterpret_cast<io_t*>(p.y);
-    auto tok = [&](int64_t t) -> int64_t { return (b * L + t) * H + h; };
+    const int64_t nchunks_all = (L + Q - 1) / Q;
+    const int64_t c_begin = (int64_t)seg * p.seg_chunks;
+    const int64_t c_end = c_begin + p.seg_chunks < nchunks_all ? c_begin + p.seg_chunks : nchunks_all;
+    const bool last_seg = seg == p.nseg - 1;
+
+    // Per-(b, h) base pointers at the segment's first token; advanced by one
+    // chunk per iteration.  Offsets inside a chunk are 32-bit.
+    const int sDT = (int)H, sTH = (int)(H * NPR), sBN = (int)(H * R * N), sXP = (int)(H * R * P);
+    const int64_t tok0 = (b * L + c_begin * Q) * H + h;
+    const float* __restrict__ dtc = p.dt + tok0;
+    const float* __restrict__ lamc = p.lam + tok0;
+    const float* __restrict__ thc = p.theta + tok0 * NPR;
+    const io_t* __restrict__ Bc = reinterpret_cast<const io_t*>(p.B) + tok0 * R * N;
+    const io_t* __restrict__ Cc = reinterpret_cast<const io_t*>(p.C) + tok0 * R * N;
+    const io_t* __restrict__ Xc = reinterpret_cast<const io_t*>(p.x) + tok0 * R * P + p0;
+    io_t* __restrict__ Yc = reinterpret_cast<io_t*>(p.y) + tok0 * R * P + p0;
+
+    // Angle-scan role: pair ai, token block ablk.  Threads beyond the TB
+    // blocks repeat the last block and store identical values.
+    const int ai = tid % NPR;
+    const int ablk = tid / NPR < TB ? tid / NPR : TB - 1;
 
     // Padded state columns (N < NP) are constant zeros.
     if constexpr (NP > N) {
         for (int idx = tid; idx < T * (NP - N); idx += NT) {
             const int row = idx / (NP - N), col = N + idx % (NP - N);
             sB[row * LDB + col] = from_f32<op_t>(0.f);
-            sC[row * LDB + col] = from_f32<op_t>(0.f);
+            if constexpr (FULL) sC[row * LDB + col] = from_f32<op_t>(0.f);
         }
     }
 
-    // Initial augmented state G_0 = h_0 + bhat_1 B_prev X_prev, in the tile
-    // layout of the state-update accumulators: tile tau = wv + NW*k covers
-    // rows 16*nt + 4*g + i, column p0 + 16*pt + l16.
+    // ---- chunk input loads -------------------------------------------------
+    // Token indices are clamped to the last valid token (values past it are
+    // masked on use).  Loads are issued in the order the next iteration
+    // consumes them, every one unconditional, so the in-order load counter
+    // lets each phase wait only for its own data.
+    ChunkStage<Cf> st;
+    auto issue_loads = [&](int64_t c) {
+        const int64_t t0 = c * Q;
+        const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));  // last valid j
+        const int jn = (int)((L - 1 - t0) < Q ? (L - 1 - t0) : Q);              // last valid j+1
+#pragma unroll
+        for (int kk = 0; kk < QPL; ++kk) {
+            const int j = lane * QPL + kk;
+            const int jc = j < jl ? j : jl;
+            const int jnc = j + 1 < jn ? j + 1 : jn;
+            st.a_dt[kk] = dtc[jc * sDT];
+            st.a_lm[kk] = lamc[jc * sDT];
+            st.a_dn[kk] = dtc[jnc * sDT];
+            st.a_ln[kk] = lamc[jnc * sDT];
+        }
+#pragma unroll
+        for (int k = 0; k < XI; ++k) {
+            int it = tid + k * NT;
+            if (XITEMS % NT != 0 && it >= XITEMS) it = XITEMS - 1;   // duplicate, not stored
+            const int rho = it % T, cg = it / T;
+            const int j = rho / R < jl ? rho / R : jl;
+            st.xq[k].load(Xc + j * sXP + (rho % R) * (int)P + 8 * cg);
+        }
+#pragma unroll
+        for (int kk = 0; kk < TPB; ++kk) {
+            const int j = ablk * TPB + kk < jl ? ablk * TPB + kk : jl;
+            st.dtv[kk] = dtc[j * sDT];
+            st.thv[kk] = thc[j * sTH + ai];
+        }
+#pragma unroll
+        for (int kk = 0; kk < TPB; ++kk) {
+            const int j = ablk * TPB + kk < jl ? ablk * TPB + kk : jl;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int off = j * sBN + r * N + 2 * ai;
+                st.bq[kk][r].load(Bc + off);
+                if constexpr (FULL) st.cq[kk][r].load(Cc + off);
+            }
+        }
+    };
+
+    // ---- initial state ------------------------------------------------------
+    // Wave wv owns state tiles tau = wv*TPW + k: rows 16*nt + 4*g + i, column
+    // p0 + 16*pt + l16 of the N x P state.
     f32x4 hacc[TPW];
-    {
-        const float bhat1 = (L > 0) ? (1.f - lam[tok(0)]) * dt[tok(0)] : 0.f;
+    const int64_t rec_sz = Cf::rec_floats(P);
+    float* recs = p.ws + (int64_t)bh * (p.nseg - 1) * rec_sz;   // this (b, h)'s records
+    if (seg == 0) {
+        // G_0 = h_0 + bhat_1 B_prev X_prev.  All loads first, then arithmetic.
+        float hv[TPW][4], bv[TPW][4][R], xv[TPW][R];
         const io_t* Bp = reinterpret_cast<const io_t*>(p.Bp_in);
         const io_t* xp = reinterpret_cast<const io_t*>(p.xp_in);
+        const float* hsrc = p.h_in;
+        float bhat1 = 0.f;
+        if (hsrc != nullptr) {
 #pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-            const int tau = wv + NW * k;
-            hacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (tau < NTILES) {
+            for (int k = 0; k < TPW; ++k) {
+                const int tau = wv * TPW + k < NTILES ? wv * TPW + k : NTILES - 1;
                 const int nt = tau / PT, pt = tau % PT;
                 const int64_t col = p0 + 16 * pt + l16;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int n = 16 * nt + 4 * g + i;
-                    if (n < N) {
-                        float v = p.h_in ? p.h_in[((int64_t)bh * N + n) * P + col] : 0.f;
-                        if (Bp != nullptr) {
-                            float u = 0.f;
+                for (int r = 0; r < R; ++r) xv[k][r] = to_f32(xp[((int64_t)bh * R + r) * P + col]);
 #pragma unroll
-                            for (int r = 0; r < R; ++r)
-                                u += to_f32(Bp[((int64_t)bh * R + r) * N + n]) *
-                                     to_f32(xp[((int64_t)bh * R + r) * P + col]);
-                            v += bhat1 * u;
-                        }
-                        hacc[k][i] = v;
+                for (int i = 0; i < 4; ++i) {
+                    const int n = 16 * nt + 4 * g + i < N ? 16 * nt + 4 * g + i : N - 1;
+                    hv[k][i] = hsrc[((int64_t)bh * N + n) * P + col];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) bv[k][i][r] = to_f32(Bp[((int64_t)bh * R + r) * N + n]);
+                }
+            }
+            if (L > 0) bhat1 = (1.f - p.lam[(b * L) * H + h]) * p.dt[(b * L) * H + h];
+        } else {
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) xv[k][r] = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    hv[k][i] = 0.f;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) bv[k][i][r] = 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int tau = wv * TPW + k;
+            const int nt = tau / PT;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float u = 0.f;
+#pragma unroll
+                for (int r = 0; r < R; ++r) u += bv[k][i][r] * xv[k][r];
+                const bool ok = tau < NTILES && 16 * nt + 4 * g + i < N;
+                hacc[k][i] = ok ? hv[k][i] + bhat1 * u : 0.f;
+            }
+        }
+    } else if constexpr (FULL) {
+        // Combine the end states of the earlier segments (associative
+        // operator of the chunk summaries): G = R(Phi_s)(2^{l2_s} G) + G_s.
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int tau = wv * TPW + k < NTILES ? wv * TPW + k : NTILES - 1;
+            const int nt = tau / PT, pt = tau % PT;
+            const int64_t col = p0 + 16 * pt + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = 16 * nt + 4 * g + i < N ? 16 * nt + 4 * g + i : N - 1;
+                hacc[k][i] = recs[(int64_t)n * P + col];
+            }
+        }
+        for (int s = 1; s < seg; ++s) {
+            const float* rec = recs + (int64_t)s * rec_sz;
+            const float sc = fast_exp2(rec[(int64_t)N * P]);
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+                const int tau = wv * TPW + k < NTILES ? wv * TPW + k : NTILES - 1;
+                const int nt = tau / PT, pt = tau % PT;
+                const int64_t col = p0 + 16 * pt + l16;
+#pragma unroll
+                for (int ip = 0; ip < 2; ++ip) {
+                    const int n = 16 * nt + 4 * g + 2 * ip;
+                    if (n < N) {
+                        float sn, cs;
+                        sincosf(rec[(int64_t)N * P + 1 + n / 2], &sn, &cs);
+                        const float a0 = sc * hacc[k][2 * ip], a1 = sc * hacc[k][2 * ip + 1];
+                        hacc[k][2 * ip] = cs * a0 - sn * a1 + rec[(int64_t)n * P + col];
+                        hacc[k][2 * ip + 1] = sn * a0 + cs * a1 + rec[(int64_t)(n + 1) * P + col];
                     }
                 }
             }
         }
-    }
-
-    // Stage G^T (operand type; bf16 as hi + lo) for the state term.
-    auto stage_state = [&]() {
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
-            const int tau = wv + NW * k;
+            const int tau = wv * TPW + k;
+            const int nt = tau / PT;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!(tau < NTILES && 16 * nt + 4 * g + i < N)) hacc[k][i] = 0.f;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) hacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Stage G^T (operand type; bf16 as hi + lo) into state buffer `buf`.
+    auto stage_state = [&](int buf) {
+        op_t* base = sH + buf * HSTAGE;
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int tau = wv * TPW + k;
             if (tau < NTILES) {
                 const int nt = tau / PT, pt = tau % PT;
-                op_t* dst = sH + (16 * pt + l16) * LDH + 16 * nt + 4 * g;
+                op_t* dst = base + (16 * pt + l16) * LDH + 16 * nt + 4 * g;
+                const f32x4 v = hacc[k];
+                lds_store4(dst, v[0], v[1], v[2], v[3]);
+                if constexpr (Cf::HILO) {
+                    float lo[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const op_t hi = from_f32<op_t>(hacc[k][i]);
-                    dst[i] = hi;
-                    if constexpr (Cf::HILO) dst[PS * LDH + i] = from_f32<op_t>(hacc[k][i] - to_f32(hi));
+                    for (int i = 0; i < 4; ++i) lo[i] = v[i] - to_f32(from_f32<op_t>(v[i]));
+                    lds_store4(dst + PS * LDH, lo[0], lo[1], lo[2], lo[3]);
                 }
             }
         }
     };
-    stage_state();
+    int hbuf = 0;
+    if constexpr (FULL) stage_state(hbuf);
 
-    const int64_t nchunks = (L + Q - 1) / Q;
-    for (int64_t c = 0; c < nchunks; ++c) {
+    double l2seg = 0.0, phiseg = 0.0;   // segment totals (state pass)
+
+    if (c_begin < c_end) issue_loads(c_begin);
+    for (int64_t c = c_begin; c < c_end; ++c) {
         const int64_t t0 = c * Q;
+        const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
 
-        // ---- A0: decay prefix scan and trapezoid weights (wave 0) ----------
-        if (wv == 0) {
+        // ---- A0: decay prefix scan and trapezoid weights --------------------
+        // Every wave evaluates it (uniform load/consume pattern); wave 0 stores.
+        {
             float a[QPL], wt[QPL], gm[QPL];
             float run = 0.f;
 #pragma unroll
             for (int kk = 0; kk < QPL; ++kk) {
                 const int j = lane * QPL + kk;
-                a[kk] = 0.f; wt[kk] = 0.f; gm[kk] = 0.f;
-                if (j < Q) {
-                    const int64_t t = t0 + j;
-                    float d = 0.f, lm = 0.f, dn = 0.f, ln = 0.f;
-                    if (t < L) { d = dt[tok(t)]; lm = lam[tok(t)]; }
-                    if (t + 1 < L) { dn = dt[tok(t + 1)]; ln = lam[tok(t + 1)]; }
-                    gm[kk] = lm * d;
-                    wt[kk] = gm[kk] + (1.f - ln) * dn;
-                    run += d * Ah;
-                    a[kk] = run;
-                }
+                const bool ok = j < Q && j <= jl;
+                const bool okn = j < Q && t0 + j + 1 < L;
+                const float d = ok ? st.a_dt[kk] : 0.f;
+                const float lm = ok ? st.a_lm[kk] : 0.f;
+                const float dn = okn ? st.a_dn[kk] : 0.f;
+                const float ln = okn ? st.a_ln[kk] : 0.f;
+                gm[kk] = lm * d;
+                wt[kk] = gm[kk] + (1.f - ln) * dn;
+                run += d * Ah;
+                a[kk] = run;
             }
             float incl = run;
 #pragma unroll
@@ -251,180 +441,190 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
 #pragma unroll
             for (int kk = 0; kk < QPL; ++kk) {
                 const int j = lane * QPL + kk;
-                if (j < Q) {
+                if (wv == 0 && j < Q) {
                     const float l2 = (excl + a[kk]) * kLog2e;
-                    sL2[j] = l2;
-                    sW[j] = wt[kk];
+                    *reinterpret_cast<float2*>(sLW + 2 * j) = make_float2(l2, wt[kk]);
                     sG[j] = gm[kk];
-                    sD[j] = wt[kk] * exp2f(l2tot - l2);
+                    sD[j] = wt[kk] * fast_exp2(l2tot - l2);
                 }
             }
-            if (lane == 0) sMisc[0] = l2tot;
+            if (wv == 0 && lane == 0) sMisc[0] = l2tot;
+            if constexpr (!FULL) l2seg += (double)l2tot;
         }
 
-        // ---- A2: X^T slice ------------------------------------------------
-        for (int it = tid; it < T * (PS / 8); it += NT) {
-            const int rho = it / (PS / 8), cg = it % (PS / 8);
-            const int j = rho / R, r = rho % R;
-            const int64_t t = t0 + j;
-            float v[8];
-            if (t < L) {
-                gload8(v, X + (tok(t) * R + r) * P + p0 + 8 * cg);
-            } else {
+        // ---- A2: X^T slice (consecutive lanes take consecutive rows) -------
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = 0.f;
-            }
+        for (int k = 0; k < XI; ++k) {
+            int it = tid + k * NT;
+            if (XITEMS % NT != 0 && it >= XITEMS) it = XITEMS - 1;   // identical duplicate
+            const int rho = it % T, cg = it / T;
+            const bool ok = rho / R <= jl;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sX[(8 * cg + e) * LDX + rho] = from_f32<op_t>(v[e]);
+            for (int e = 0; e < 8; ++e)
+                sX[(8 * cg + e) * LDX + rho] = from_f32<op_t>(ok ? st.xq[k].get(e) : 0.f);
         }
 
         // ---- A1: angle prefix per (pair, token block), rotate B and C ------
-        const int ai = tid % NPR, ablk = tid / NPR;
-        const bool aact = ablk < TB;
         float loc[TPB];
-        if (aact) {
+        {
             float s = 0.f;
 #pragma unroll
             for (int kk = 0; kk < TPB; ++kk) {
-                const int64_t t = t0 + ablk * TPB + kk;
-                if (t < L) s += dt[tok(t)] * theta[tok(t) * NPR + ai];
+                if (ablk * TPB + kk <= jl) s += st.dtv[kk] * st.thv[kk];
                 loc[kk] = s;
             }
             sTot[ablk * NPR + ai] = s;
         }
         __syncthreads();
-        if (aact) {
+        {
             float off = 0.f;
             for (int bb = 0; bb < ablk; ++bb) off += sTot[bb * NPR + ai];
 #pragma unroll
             for (int kk = 0; kk < TPB; ++kk) {
                 const int j = ablk * TPB + kk;
-                const int64_t t = t0 + j;
+                const bool ok = j <= jl;
                 float sn, cs;
-                sincosf(off + loc[kk], &sn, &cs);
+                rope_sincos<op_t>(off + loc[kk], &sn, &cs);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const int rho = j * R + r;
-                    float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
-                    if (t < L) {
-                        const int64_t row = (tok(t) * R + r) * N + 2 * ai;
-                        gload2(b0, b1, Bm + row);
-                        gload2(c0, c1, Cm + row);
-                    }
+                    const float b0 = ok ? st.bq[kk][r].lo() : 0.f, b1 = ok ? st.bq[kk][r].hi() : 0.f;
                     // R(Phi)^T applied to the pair
                     sstore2(sB + rho * LDB + 2 * ai, cs * b0 + sn * b1, cs * b1 - sn * b0);
-                    sstore2(sC + rho * LDB + 2 * ai, cs * c0 + sn * c1, cs * c1 - sn * c0);
+                    if constexpr (FULL) {
+                        const float c0 = ok ? st.cq[kk][r].lo() : 0.f;
+                        const float c1 = ok ? st.cq[kk][r].hi() : 0.f;
+                        sstore2(sC + rho * LDB + 2 * ai, cs * c0 + sn * c1, cs * c1 - sn * c0);
+                    }
                 }
             }
             if (ablk == TB - 1) {
+                const float phi = off + loc[TPB - 1];
                 float sn, cs;
-                sincosf(off + loc[TPB - 1], &sn, &cs);
+                sincosf(phi, &sn, &cs);
                 sCSt[2 * ai] = cs;
                 sCSt[2 * ai + 1] = sn;
+                if constexpr (!FULL) phiseg += (double)phi;
             }
         }
+        // This chunk's raw inputs now live in LDS: fetch the next chunk's.
+        dtc += Q * sDT; lamc += Q * sDT; thc += Q * sTH;
+        Bc += Q * sBN; Cc += Q * sBN; Xc += Q * sXP;
+        if (c + 1 < c_end) issue_loads(c + 1);
         __syncthreads();
 
         // ---- C: outputs of this chunk --------------------------------------
+        if constexpr (FULL) {
+            const op_t* sHc = sH + hbuf * HSTAGE;
 #pragma unroll 1
-        for (int qi = 0; qi < QPW; ++qi) {
-            const int qt = (qi & 1) ? qi * NW + (NW - 1 - wv) : qi * NW + wv;
-            if (qt >= QT) continue;
-            const int rq = 16 * qt + l16;
-            const int jq = rq / R;
-            const float l2q = sL2[jq];
-            const float gq = sG[jq];
+            for (int qi = 0; qi < QPW; ++qi) {
+                const int qt = (qi & 1) ? qi * NW + (NW - 1 - wv) : qi * NW + wv;
+                if (qt >= QT) continue;
+                const int rq = 16 * qt + l16;
+                const int jq = rq / R;
+                const float2 lwq = *reinterpret_cast<const float2*>(sLW + 2 * jq);
+                const float l2q = lwq.x;
+                const float gq = sG[jq];
 
-            Frag<op_t> cf[NP / 32];
+                Frag<op_t> cf[NP / 32];
 #pragma unroll
-            for (int s = 0; s < NP / 32; ++s) lds_frag8(cf[s], sC + rq * LDB + 32 * s + 8 * g);
+                for (int s = 0; s < NP / 32; ++s) lds_frag8(cf[s], sC + rq * LDB + 32 * s + 8 * g);
 
-            f32x4 yacc[PT];
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                yacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < NP / 32; ++s) {
-                    Frag<op_t> a;
-                    lds_frag8(a, sH + (16 * pt + l16) * LDH + 32 * s + 8 * g);
-                    mma(a, cf[s], yacc[pt]);
-                    if constexpr (Cf::HILO) {
-                        lds_frag8(a, sH + PS * LDH + (16 * pt + l16) * LDH + 32 * s + 8 * g);
-                        mma(a, cf[s], yacc[pt]);
-                    }
-                }
-                const float sq = exp2f(l2q);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) yacc[pt][i] *= sq;
-            }
-
-#pragma unroll 1
-            for (int kp = 0; kp <= qt; kp += 2) {
-                Frag<op_t> pf;
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int kt = kp + half;
-                    if (kt <= qt) {
-                        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s = 0; s < NP / 32; ++s) {
-                            Frag<op_t> a;
-                            lds_frag8(a, sB + (16 * kt + l16) * LDB + 32 * s + 8 * g);
-                            mma(a, cf[s], sacc);
-                        }
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int jk = (16 * kt + 4 * g) / R + i / R;
-                            float v = 0.f;
-                            if (jk < jq) v = sacc[i] * (sW[jk] * exp2f(l2q - sL2[jk]));
-                            else if (jk == jq) v = sacc[i] * gq;
-                            pf.set(4 * half + i, v);
-                        }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) pf.set(4 * half + i, 0.f);
-                    }
-                }
+                f32x4 yacc[PT];
+                const float sq = fast_exp2(l2q);
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
-                    Frag<op_t> xa;
-                    const op_t* xr = sX + (16 * pt + l16) * LDX;
-                    if (kp + 1 <= qt) lds_frag4x2(xa, xr + 16 * kp + 4 * g, xr + 16 * (kp + 1) + 4 * g);
-                    else lds_frag4(xa, xr + 16 * kp + 4 * g);
-                    mma(xa, pf, yacc[pt]);
+                    yacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < NP / 32; ++s) {
+                        Frag<op_t> a;
+                        lds_frag8(a, sHc + (16 * pt + l16) * LDH + 32 * s + 8 * g);
+                        mma(a, cf[s], yacc[pt]);
+                        if constexpr (Cf::HILO) {
+                            lds_frag8(a, sHc + PS * LDH + (16 * pt + l16) * LDH + 32 * s + 8 * g);
+                            mma(a, cf[s], yacc[pt]);
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) yacc[pt][i] *= sq;
+                }
+
+#pragma unroll 1
+                for (int kp = 0; kp <= qt; kp += 2) {
+                    Frag<op_t> pf;
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int kt = kp + half;
+                        if (kt <= qt) {
+                            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int s = 0; s < NP / 32; ++s) {
+                                Frag<op_t> a;
+                                lds_frag8(a, sB + (16 * kt + l16) * LDB + 32 * s + 8 * g);
+                                mma(a, cf[s], sacc);
+                            }
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int jk = (16 * kt + 4 * g) / R + i / R;
+                                const float2 lw = *reinterpret_cast<const float2*>(sLW + 2 * jk);
+                                const float m = jk < jq ? lw.y * fast_exp2(l2q - lw.x)
+                                                        : (jk == jq ? gq : 0.f);
+                                pf.set(4 * half + i, jk <= jq ? sacc[i] * m : 0.f);
+                            }
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) pf.set(4 * half + i, 0.f);
+                        }
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        Frag<op_t> xa;
+                        const op_t* xr = sX + (16 * pt + l16) * LDX;
+                        if (kp + 1 <= qt) lds_frag4x2(xa, xr + 16 * kp + 4 * g, xr + 16 * (kp + 1) + 4 * g);
+                        else lds_frag4(xa, xr + 16 * kp + 4 * g);
+                        mma(xa, pf, yacc[pt]);
+                    }
+                }
+
+                if (jq <= jl) {
+                    io_t* yrow = Yc + jq * sXP + (rq % R) * (int)P;
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) gstore4(yrow + 16 * pt + 4 * g, yacc[pt]);
                 }
             }
-
-            const int64_t tq = t0 + jq;
-            if (tq < L) {
-                io_t* yrow = Y + (tok(tq) * R + rq % R) * P + p0;
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) gstore4(yrow + 16 * pt + 4 * g, yacc[pt]);
-            }
+            Yc += Q * sXP;
         }
-        __syncthreads();
 
         // ---- D: state update  G <- R(Phi_tot)(e^{Lam_tot} G + Bbar_d^T X) --
         {
-            const float aT = exp2f(sMisc[0]);
+            const float aT = fast_exp2(sMisc[0]);
+            Frag<op_t> bfr[KB];
+            int cur_nt = -1;
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
-                const int tau = wv + NW * k;
+                const int tau = wv * TPW + k;
                 if (tau < NTILES) {
                     const int nt = tau / PT, pt = tau % PT;
+                    if (nt != cur_nt) {
+                        // Bbar_d^T operand rows n = 16*nt + l16: a strided gather
+                        // down the keys of Bbar (stored key-major for C).
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const int rho = 32 * kb + 8 * g + e;
+                                bfr[kb].set(e, to_f32(sB[rho * LDB + 16 * nt + l16]) * sD[rho / R]);
+                            }
+                        cur_nt = nt;
+                    }
                     f32x4 acc = hacc[k];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[i] *= aT;
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
-                        Frag<op_t> bfr, xfr;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int rho = 32 * kb + 8 * g + e;
-                            bfr.set(e, to_f32(sB[rho * LDB + 16 * nt + l16]) * sD[rho / R]);
-                        }
+                        Frag<op_t> xfr;
                         lds_frag8(xfr, sX + (16 * pt + l16) * LDX + 32 * kb + 8 * g);
-                        mma(bfr, xfr, acc);
+                        mma(bfr[kb], xfr, acc);
                     }
 #pragma unroll
                     for (int ip = 0; ip < 2; ++ip) {
@@ -439,16 +639,45 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
                     hacc[k] = acc;
                 }
             }
-            stage_state();
+            if constexpr (FULL) {
+                hbuf ^= 1;
+                stage_state(hbuf);
+            }
         }
         __syncthreads();
     }
 
-    // ---- final state record ------------------------------------------------
-    if (p.h_out != nullptr) {
+    if constexpr (!FULL) {
+        // End state of this segment and its decay / angle totals.
+        float* rec = recs + (int64_t)seg * rec_sz;
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
-            const int tau = wv + NW * k;
+            const int tau = wv * TPW + k;
+            if (tau < NTILES) {
+                const int nt = tau / PT, pt = tau % PT;
+                const int64_t col = p0 + 16 * pt + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int n = 16 * nt + 4 * g + i;
+                    if (n < N) rec[(int64_t)n * P + col] = hacc[k][i];
+                }
+            }
+        }
+        if (ps == 0) {
+            if (tid == 0) rec[(int64_t)N * P] = (float)l2seg;
+            if (ablk == TB - 1 && tid / NPR == TB - 1) {
+                const double twopi = 6.283185307179586;
+                rec[(int64_t)N * P + 1 + ai] = (float)(phiseg - twopi * floor(phiseg / twopi));
+            }
+        }
+        return;
+    }
+
+    // ---- final state record (last segment) ----------------------------------
+    if (FULL && last_seg && p.h_out != nullptr) {
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int tau = wv * TPW + k;
             if (tau < NTILES) {
                 const int nt = tau / PT, pt = tau % PT;
                 const int64_t col = p0 + 16 * pt + l16;
@@ -460,19 +689,22 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
             }
         }
         if (ps == 0) {
+            const io_t* Bm = reinterpret_cast<const io_t*>(p.B);
+            const io_t* X = reinterpret_cast<const io_t*>(p.x);
             io_t* Bo = reinterpret_cast<io_t*>(p.Bp_out) + (int64_t)bh * R * N;
             io_t* xo = reinterpret_cast<io_t*>(p.xp_out) + (int64_t)bh * R * P;
             const io_t* Bi = reinterpret_cast<const io_t*>(p.Bp_in);
             const io_t* xi = reinterpret_cast<const io_t*>(p.xp_in);
+            const int64_t tl = (b * L + (L - 1)) * H + h;
             for (int idx = tid; idx < R * N; idx += NT) {
                 io_t v = from_f32<io_t>(0.f);
-                if (L > 0) v = Bm[tok(L - 1) * R * N + idx];
+                if (L > 0) v = Bm[tl * R * N + idx];
                 else if (Bi != nullptr) v = Bi[(int64_t)bh * R * N + idx];
                 Bo[idx] = v;
             }
             for (int64_t idx = tid; idx < R * P; idx += NT) {
                 io_t v = from_f32<io_t>(0.f);
-                if (L > 0) v = X[tok(L - 1) * R * P + idx];
+                if (L > 0) v = X[tl * R * P + idx];
                 else if (xi != nullptr) v = xi[(int64_t)bh * R * P + idx];
                 xo[idx] = v;
             }
@@ -481,16 +713,32 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
 }
 
 template <class Cf>
+size_t scan_workspace_bytes(int64_t nbh, int64_t P, int nseg)
+{
+    return nseg > 1 ? (size_t)nbh * (size_t)(nseg - 1) * (size_t)Cf::rec_floats(P) * 4 : 0;
+}
+
+template <class Cf>
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream)
 {
-    const void* fn = reinterpret_cast<const void*>(&scan_kernel<Cf>);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)Cf::lds_bytes);
-    if (e != hipSuccess) return e;
-    const int64_t groups = (int64_t)((p.nbh + 7) / 8) * 8 * p.p_split;
+    const int64_t per_seg = (int64_t)((p.nbh + 7) / 8) * 8 * p.p_split;
+    hipError_t e;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(scan_kernel<Cf>, dim3((unsigned)groups), dim3(Cf::NT), Cf::lds_bytes,
-                       stream, p);
+    if (p.nseg > 1) {
+        const void* f1 = reinterpret_cast<const void*>(&scan_kernel<Cf, false>);
+        e = hipFuncSetAttribute(f1, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)Cf::lds_bytes_state);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((scan_kernel<Cf, false>), dim3((unsigned)(per_seg * (p.nseg - 1))),
+                           dim3(Cf::NT), Cf::lds_bytes_state, stream, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const void* f2 = reinterpret_cast<const void*>(&scan_kernel<Cf, true>);
+    e = hipFuncSetAttribute(f2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::lds_bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((scan_kernel<Cf, true>), dim3((unsigned)(per_seg * p.nseg)), dim3(Cf::NT),
+                       Cf::lds_bytes, stream, p);
     return hipGetLastError();
 }
 

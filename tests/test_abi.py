@@ -95,7 +95,9 @@ def run_scan(lib, a):
     (dict(seqlen=-5), -2), (dict(chunk=-1), -2),
     (dict(io_dtype=7), -4),
     (dict(dstate=48), -3), (dict(rank=3), -3), (dict(chunk=24), -3), (dict(headdim=40), -3),
-    (dict(p_split=3), -3), (dict(segments=4), -3),
+    (dict(p_split=3), -3),
+    (dict(seqlen=1000, segments=4), -6),                    # needs a workspace
+    (dict(seqlen=1000, segments=4, workspace=FAKE + (30 << 32) + 16, workspace_bytes=1 << 40), -5),
     (dict(x=None), -1), (dict(y=None), -1), (dict(theta=None), -1), (dict(A=None), -1),
     (dict(h_in=FAKE + (20 << 32)), -1),                      # partial state record
     (dict(h_out=FAKE + (21 << 32), B_prev_out=FAKE + (22 << 32)), -1),
@@ -153,3 +155,7 @@ def test_supported_sets(lib):
     assert lib.m3_scan_supported(96, 64, 1, 0, 1) == 0
     assert lib.m3_scan_supported(64, 24, 1, 0, 1) == 0
     assert lib.m3_scan_workspace_bytes(ctypes.byref(scan_args())) == 0
+    # segmented calls need one record (N*P state + totals) per (b, h, segment boundary)
+    ws = lib.m3_scan_workspace_bytes(ctypes.byref(scan_args(seqlen=1000, segments=4)))
+    assert ws >= 2 * 3 * 3 * 64 * 32 * 4
+    assert lib.m3_scan_workspace_bytes(ctypes.byref(scan_args(dstate=63))) == 0

@@ -17,14 +17,15 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def check_scan(w, seed, with_state=False, chunk=0, p_split=0, label=""):
-    say("case %s: B%d L%d H%d R%d P%d N%d %s chunk=%d p_split=%d state=%s seed=%d" % (
+def check_scan(w, seed, with_state=False, chunk=0, p_split=0, segments=0, label=""):
+    say("case %s: B%d L%d H%d R%d P%d N%d %s chunk=%d p_split=%d seg=%d state=%s seed=%d" % (
         label, w.batch, w.seqlen, w.heads, w.rank, w.headdim, w.dstate, w.io_dtype, chunk,
-        p_split, with_state, seed))
+        p_split, segments, with_state, seed))
     inp = synth.make_scan_inputs(w, seed, DEV)
     st = random_state(w, seed + 7, DEV) if with_state else None
     y, so = m3_scan_fwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
-                        inp["lam"], State(*st) if st else None, chunk=chunk, p_split=p_split)
+                        inp["lam"], State(*st) if st else None, chunk=chunk, p_split=p_split,
+                        segments=segments)
     torch.cuda.synchronize()
     yr, hr, br, xr = oracle_scan(inp, st)
     tol = TOL[w.io_dtype]
@@ -66,6 +67,20 @@ def test_chunk_invariance_bf16(chunk):
 def test_headdim_split_invariance(p_split):
     w = workload(2, 300, 2, 1, 64, 64, io="bf16")
     check_scan(w, 6, with_state=True, p_split=p_split, label="psplit")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("segments", [2, 3, 5])
+def test_sequence_segments(io, segments):
+    """Segmented scans (state pass + output pass) with ragged chunk counts."""
+    w = workload(2, 1000, 3, 2, 32, 64, io=io, dt_mu=-1.0)
+    check_scan(w, 50 + segments, with_state=True, segments=segments, label="segments")
+
+
+def test_sequence_segments_fast_rotation_slow_decay():
+    """Large angles and slow decay carry the state across many segments."""
+    w = workload(1, 2000, 2, 1, 16, 32, io="f32", dt_mu=-4.0, theta="uniform_pi")
+    check_scan(w, 61, with_state=True, segments=7, label="segments-slow")
 
 
 def test_split_scan_equals_one_scan():
