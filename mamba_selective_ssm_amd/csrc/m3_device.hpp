@@ -177,3 +177,34 @@ __device__ __forceinline__ void lds_store4(float* p, float a, float b, float c, 
 }
 
 }  // namespace m3
+
+namespace m3 {
+
+// Inclusive prefix sum across the 64 lanes of a wavefront with DPP moves:
+// row shifts by 1, 2, 4, 8 scan each row of 16 lanes, then the row
+// broadcasts of lanes 15 and 31 carry row totals upward.  Lanes with no DPP
+// source add the old value 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_moved(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                 ROW_MASK, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_inclusive_sum(float v)
+{
+    v += dpp_moved<0x111, 0xf>(v);   // row_shr:1
+    v += dpp_moved<0x112, 0xf>(v);   // row_shr:2
+    v += dpp_moved<0x114, 0xf>(v);   // row_shr:4
+    v += dpp_moved<0x118, 0xf>(v);   // row_shr:8
+    v += dpp_moved<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_moved<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+__device__ __forceinline__ float wave_read_lane(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+}  // namespace m3

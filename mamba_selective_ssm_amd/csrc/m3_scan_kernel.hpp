@@ -430,14 +430,9 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
                 run += d * Ah;
                 a[kk] = run;
             }
-            float incl = run;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += o;
-            }
+            const float incl = wave_inclusive_sum(run);
             const float excl = incl - run;
-            const float l2tot = __shfl(incl, (Q - 1) / QPL, 64) * kLog2e;
+            const float l2tot = wave_read_lane(incl, (Q - 1) / QPL) * kLog2e;
 #pragma unroll
             for (int kk = 0; kk < QPL; ++kk) {
                 const int j = lane * QPL + kk;
@@ -478,7 +473,11 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
         __syncthreads();
         {
             float off = 0.f;
-            for (int bb = 0; bb < ablk; ++bb) off += sTot[bb * NPR + ai];
+#pragma unroll
+            for (int bb = 0; bb < TB - 1; ++bb) {
+                const float v = sTot[bb * NPR + ai];
+                off += bb < ablk ? v : 0.f;
+            }
 #pragma unroll
             for (int kk = 0; kk < TPB; ++kk) {
                 const int j = ablk * TPB + kk;
