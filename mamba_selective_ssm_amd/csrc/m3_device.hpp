@@ -208,3 +208,39 @@ __device__ __forceinline__ float wave_read_lane(float v, int lane)
 }
 
 }  // namespace m3
+
+namespace m3 {
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j supplies the address of 4 consecutive bf16 values; lane i then
+// receives element (i % 4) of the values supplied by lanes (i / 4), 4 + (i / 4),
+// 8 + (i / 4) and 12 + (i / 4).  With lane j pointing at row k0 + j / 4,
+// columns c0 + 4 * (j % 4) .. + 3 of a row-major bf16 block, lane i gets rows
+// k0 .. k0 + 3 of column c0 + i: four consecutive keys of one column, the
+// K-slots of a matrix-core operand read from a key-major array.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+}  // namespace m3
+
+namespace m3 {
+
+// Eight operand elements to LDS (16 B for bf16, 32 B for fp32).
+__device__ __forceinline__ void lds_store8(bf16* p, const float (&v)[8])
+{
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x8*>(p) = o;
+}
+__device__ __forceinline__ void lds_store8(float* p, const float (&v)[8])
+{
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+}  // namespace m3

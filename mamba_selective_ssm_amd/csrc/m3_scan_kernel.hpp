@@ -34,9 +34,12 @@
 // chunk c's matrix-core phases run.  Per chunk (Q tokens, T = Q*R rows):
 //   A0  one wave: inclusive wavefront prefix scan of dt*A, weights w, gamma,
 //       and d_k = w_k e^{Lam_tot-Lam_k}.
-//   A1  all threads: angle prefix sums per (pair, token block), sincos, and
-//       rotation of B and C rows into LDS (Bbar, Cbar as matrix-core operands).
-//   A2  X^T slice into LDS.
+//   A1  all threads: angle prefix sums per (pair quad, token block) -- in
+//       registers, across a wave's blocks with shuffles, across waves through
+//       LDS -- sine/cosine, and rotation of B and C rows (16 bytes per lane)
+//       into LDS (Bbar, Cbar as matrix-core operand rows).
+//   A2  X slice into LDS: bf16 as rows, read transposed (ds_read_tr16_b64)
+//       by both matrix-core products that contract over keys; fp32 as X^T.
 //   C   each wave takes 16-row query tiles: S^T = Bbar Cbar^T on matrix
 //       cores, two-band decay mask in fp32 registers, (S o M)^T cast to the
 //       operand type, Y^T += X^T (S o M)^T, plus the state term
@@ -84,18 +87,21 @@ struct ScanCfg {
     static constexpr int N = N_, PS = PS_, R = R_, Q = Q_, NW = NW_;
     static constexpr int NP = N < 32 ? 32 : N;      // state rows padded to the K block
     static constexpr int NPR = N / 2;                // rotation pairs
+    static constexpr int NPR4 = NPR / 4;             // pair quads (8 state rows, 16 B of bf16)
     static constexpr int T = Q * R;                  // operand rows per chunk
     static constexpr int NT = 64 * NW;
     static constexpr int E = (int)sizeof(op_t);
+    static constexpr bool BF = (E == 2);
     static constexpr int PADE = 16 / E;              // 16-byte row padding
     static constexpr int LDB = NP + PADE;
-    static constexpr int LDX = T + PADE;
+    static constexpr int LDX = T + PADE;             // fp32: X^T rows
+    static constexpr int LDXR = PS + PADE;           // bf16: X rows
     static constexpr int LDH = NP + PADE;
-    static constexpr bool HILO = (E == 2);
+    static constexpr bool HILO = BF;
     static constexpr int NHT = HILO ? 2 : 1;
-    static constexpr int TB0 = NT / NPR;
-    static constexpr int TB = TB0 < Q ? TB0 : Q;     // token blocks of the angle scan
-    static constexpr int TPB = Q / TB;               // tokens per block
+    static constexpr int TBA = NT / NPR4 < Q ? NT / NPR4 : Q;   // angle-scan token blocks
+    static constexpr int TPB = Q / TBA;              // tokens per block
+    static constexpr int BW = 64 / NPR4;             // angle blocks per wave
     static constexpr int QT = T / 16;                // 16-row query/key tiles
     static constexpr int KB = T / 32;                // 32-row key blocks
     static constexpr int PT = PS / 16;
@@ -107,14 +113,14 @@ struct ScanCfg {
     static constexpr int XITEMS = T * (PS / 8);      // 8-element X row pieces
     static constexpr int XI = (XITEMS + NT - 1) / NT;
     static constexpr size_t sz_B = (size_t)T * LDB * E;
+    static constexpr size_t sz_X = BF ? (size_t)T * LDXR * E : (size_t)PS * LDX * E;
     static constexpr size_t off_B = 0;
     static constexpr size_t off_C = off_B + sz_B;
     static constexpr size_t off_X = off_C + sz_B;
-    static constexpr size_t sz_X = (size_t)PS * LDX * E;
     static constexpr size_t off_H = off_X + sz_X;
     static constexpr size_t sz_H1 = (size_t)NHT * PS * LDH * E;   // one state stage
     static constexpr size_t off_F = off_H + 2 * sz_H1;
-    static constexpr size_t nF = 4 * (size_t)Q + (size_t)TB * NPR + 2 * (size_t)NPR + 4;
+    static constexpr size_t nF = 4 * (size_t)Q + (size_t)NW * NPR + 2 * (size_t)NPR + 4;
     static constexpr size_t lds_bytes = off_F + nF * 4;
     // The state-only pass needs no Cbar and no state stage.
     static constexpr size_t off_X1 = off_C;
@@ -124,8 +130,8 @@ struct ScanCfg {
     __host__ __device__ static int64_t rec_floats(int64_t P) { return ((int64_t)N * P + 1 + NPR + 3) / 4 * 4; }
     static_assert(T % 32 == 0, "Q*R must be a multiple of 32");
     static_assert(PS % 16 == 0, "headdim slice must be a multiple of 16");
-    static_assert(N % 2 == 0 && NPR <= NT && NT % NPR == 0, "bad dstate");
-    static_assert(Q % TB == 0, "");
+    static_assert(N % 8 == 0 && NPR4 <= 64 && NT % NPR4 == 0, "bad dstate");
+    static_assert(Q % TBA == 0, "");
     static_assert(lds_bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -133,8 +139,9 @@ struct ScanCfg {
 template <class Cf> struct ChunkStage {
     using io_t = typename Cf::io_t;
     float a_dt[Cf::QPL], a_lm[Cf::QPL], a_dn[Cf::QPL], a_ln[Cf::QPL];  // dt, lam at t, t+1
-    float dtv[Cf::TPB], thv[Cf::TPB];                                   // angle block
-    IoPair<io_t> bq[Cf::TPB][Cf::R], cq[Cf::TPB][Cf::R];                // B, C pairs
+    float dtv[Cf::TPB];                                                 // angle block: dt
+    f32x4 thv[Cf::TPB];                                                 //   theta, 4 pairs
+    IoRow8<io_t> bq[Cf::TPB][Cf::R], cq[Cf::TPB][Cf::R];                //   B, C: 4 pairs
     IoRow8<io_t> xq[Cf::XI];                                            // X row pieces
 };
 
@@ -161,25 +168,28 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
 {
     using io_t = typename Cf::io_t;
     using op_t = typename Cf::op_t;
-    constexpr int N = Cf::N, NP = Cf::NP, NPR = Cf::NPR, PS = Cf::PS, R = Cf::R;
+    constexpr int N = Cf::N, NP = Cf::NP, NPR = Cf::NPR, NPR4 = Cf::NPR4, PS = Cf::PS, R = Cf::R;
     constexpr int Q = Cf::Q, T = Cf::T, NW = Cf::NW, NT = Cf::NT;
-    constexpr int LDB = Cf::LDB, LDX = Cf::LDX, LDH = Cf::LDH;
-    constexpr int TB = Cf::TB, TPB = Cf::TPB, QT = Cf::QT, KB = Cf::KB, PT = Cf::PT;
+    constexpr int LDB = Cf::LDB, LDX = Cf::LDX, LDXR = Cf::LDXR, LDH = Cf::LDH;
+    constexpr int TBA = Cf::TBA, TPB = Cf::TPB, BW = Cf::BW, QT = Cf::QT, KB = Cf::KB, PT = Cf::PT;
     constexpr int NTILES = Cf::NTILES, TPW = Cf::TPW, QPW = Cf::QPW, QPL = Cf::QPL;
+    constexpr int NTL = Cf::NTL;
     constexpr int XI = Cf::XI, XITEMS = Cf::XITEMS;
+    constexpr bool BF = Cf::BF;
     constexpr int HSTAGE = Cf::NHT * PS * LDH;   // elements of one state stage
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     op_t* sB = reinterpret_cast<op_t*>(smem + Cf::off_B);   // [T][LDB]   Bbar rows
     op_t* sC = reinterpret_cast<op_t*>(smem + Cf::off_C);   // [T][LDB]   Cbar rows
-    op_t* sX = reinterpret_cast<op_t*>(smem + (FULL ? Cf::off_X : Cf::off_X1));  // [PS][LDX]
+    // X slice: bf16 rows [T][LDXR] (read transposed), fp32 X^T [PS][LDX]
+    op_t* sX = reinterpret_cast<op_t*>(smem + (FULL ? Cf::off_X : Cf::off_X1));
     op_t* sH = reinterpret_cast<op_t*>(smem + Cf::off_H);   // [2][NHT][PS][LDH] G^T
     float* sLW = reinterpret_cast<float*>(smem + (FULL ? Cf::off_F : Cf::off_F1));
     //   sLW: [Q][2] = (Lam_j * log2(e), w_j)
     float* sG = sLW + 2 * Q;                                 // [Q] gamma_j
     float* sD = sG + Q;                                      // [Q] w_j e^{Lam_tot-Lam_j}
-    float* sTot = sD + Q;                                    // [TB][NPR] angle block sums
-    float* sCSt = sTot + TB * NPR;                           // [NPR][2] cos/sin Phi_tot
+    float* sWt = sD + Q;                                     // [NW][NPR] per-wave angle sums
+    float* sCSt = sWt + NW * NPR;                            // [NPR][2] cos/sin Phi_tot
     float* sMisc = sCSt + 2 * NPR;                           // [0] = Lam_tot * log2(e)
 
     const int tid = threadIdx.x;
@@ -217,10 +227,20 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
     const io_t* __restrict__ Xc = reinterpret_cast<const io_t*>(p.x) + tok0 * R * P + p0;
     io_t* __restrict__ Yc = reinterpret_cast<io_t*>(p.y) + tok0 * R * P + p0;
 
-    // Angle-scan role: pair ai, token block ablk.  Threads beyond the TB
-    // blocks repeat the last block and store identical values.
-    const int ai = tid % NPR;
-    const int ablk = tid / NPR < TB ? tid / NPR : TB - 1;
+    // Angle / rotation role: pair quad aq (pairs 4aq .. 4aq+3, state rows
+    // 8aq .. 8aq+7) of the tokens of block ablk.  Consecutive lanes take
+    // consecutive quads of one row, so theta, B and C load 16 bytes per lane,
+    // coalesced.  Threads beyond the TBA blocks repeat the last block and
+    // neither contribute to the scan nor store.
+    const int aq = tid % NPR4;
+    const bool aact = tid / NPR4 < TBA;
+    const int ablk = aact ? tid / NPR4 : TBA - 1;
+
+    // X piece of item `it`: (row rho, 8-column group cg).
+    auto xmap = [](int it, int& rho, int& cg) {
+        if constexpr (BF) { rho = it / (PS / 8); cg = it % (PS / 8); }   // rows: coalesced
+        else { rho = it % T; cg = it / T; }                               // X^T: conflict-free
+    };
 
     // Padded state columns (N < NP) are constant zeros.
     if constexpr (NP > N) {
@@ -254,8 +274,9 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
 #pragma unroll
         for (int k = 0; k < XI; ++k) {
             int it = tid + k * NT;
-            if (XITEMS % NT != 0 && it >= XITEMS) it = XITEMS - 1;   // duplicate, not stored
-            const int rho = it % T, cg = it / T;
+            if (XITEMS % NT != 0 && it >= XITEMS) it = XITEMS - 1;   // duplicate
+            int rho, cg;
+            xmap(it, rho, cg);
             const int j = rho / R < jl ? rho / R : jl;
             st.xq[k].load(Xc + j * sXP + (rho % R) * (int)P + 8 * cg);
         }
@@ -263,23 +284,27 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
         for (int kk = 0; kk < TPB; ++kk) {
             const int j = ablk * TPB + kk < jl ? ablk * TPB + kk : jl;
             st.dtv[kk] = dtc[j * sDT];
-            st.thv[kk] = thc[j * sTH + ai];
+            st.thv[kk] = *reinterpret_cast<const f32x4*>(thc + j * sTH + 4 * aq);
         }
 #pragma unroll
         for (int kk = 0; kk < TPB; ++kk) {
             const int j = ablk * TPB + kk < jl ? ablk * TPB + kk : jl;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int off = j * sBN + r * N + 2 * ai;
+                const int off = j * sBN + r * N + 8 * aq;
                 st.bq[kk][r].load(Bc + off);
                 if constexpr (FULL) st.cq[kk][r].load(Cc + off);
             }
         }
     };
 
+    // The first chunk's loads go out before the initial state is formed.
+    if (c_begin < c_end) issue_loads(c_begin);
+
     // ---- initial state ------------------------------------------------------
-    // Wave wv owns state tiles tau = wv*TPW + k: rows 16*nt + 4*g + i, column
-    // p0 + 16*pt + l16 of the N x P state.
+    // Wave wv owns state tiles tau = wv*TPW + k, p-tile major (pt = tau / NTL,
+    // nt = tau % NTL): rows 16*nt + 4*g + i, column p0 + 16*pt + l16 of the
+    // N x P state.  A wave's tiles then share one d-scaled X operand in D.
     f32x4 hacc[TPW];
     const int64_t rec_sz = Cf::rec_floats(P);
     float* recs = p.ws + (int64_t)bh * (p.nseg - 1) * rec_sz;   // this (b, h)'s records
@@ -294,7 +319,7 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
                 const int tau = wv * TPW + k < NTILES ? wv * TPW + k : NTILES - 1;
-                const int nt = tau / PT, pt = tau % PT;
+                const int pt = tau / NTL, nt = tau % NTL;
                 const int64_t col = p0 + 16 * pt + l16;
 #pragma unroll
                 for (int r = 0; r < R; ++r) xv[k][r] = to_f32(xp[((int64_t)bh * R + r) * P + col]);
@@ -323,7 +348,7 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
             const int tau = wv * TPW + k;
-            const int nt = tau / PT;
+            const int nt = tau % NTL;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float u = 0.f;
@@ -339,7 +364,7 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
             const int tau = wv * TPW + k < NTILES ? wv * TPW + k : NTILES - 1;
-            const int nt = tau / PT, pt = tau % PT;
+            const int pt = tau / NTL, nt = tau % NTL;
             const int64_t col = p0 + 16 * pt + l16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -347,31 +372,58 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
                 hacc[k][i] = recs[(int64_t)n * P + col];
             }
         }
-        for (int s = 1; s < seg; ++s) {
+        // Records are folded in order; the next record's values are loaded
+        // while the current one is applied (one round trip per record would
+        // otherwise serialise the prologue).
+        float nv[TPW][4], nphi[TPW][2], nl2 = 0.f;
+        auto load_rec = [&](int s) {
             const float* rec = recs + (int64_t)s * rec_sz;
-            const float sc = fast_exp2(rec[(int64_t)N * P]);
+            nl2 = rec[(int64_t)N * P];
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
                 const int tau = wv * TPW + k < NTILES ? wv * TPW + k : NTILES - 1;
-                const int nt = tau / PT, pt = tau % PT;
+                const int pt = tau / NTL, nt = tau % NTL;
                 const int64_t col = p0 + 16 * pt + l16;
 #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int n = 16 * nt + 4 * g + i < N ? 16 * nt + 4 * g + i : N - 2 + (i & 1);
+                    nv[k][i] = rec[(int64_t)n * P + col];
+                }
+#pragma unroll
                 for (int ip = 0; ip < 2; ++ip) {
-                    const int n = 16 * nt + 4 * g + 2 * ip;
-                    if (n < N) {
-                        float sn, cs;
-                        sincosf(rec[(int64_t)N * P + 1 + n / 2], &sn, &cs);
-                        const float a0 = sc * hacc[k][2 * ip], a1 = sc * hacc[k][2 * ip + 1];
-                        hacc[k][2 * ip] = cs * a0 - sn * a1 + rec[(int64_t)n * P + col];
-                        hacc[k][2 * ip + 1] = sn * a0 + cs * a1 + rec[(int64_t)(n + 1) * P + col];
-                    }
+                    const int n = 16 * nt + 4 * g + 2 * ip < N ? 16 * nt + 4 * g + 2 * ip : N - 2;
+                    nphi[k][ip] = rec[(int64_t)N * P + 1 + n / 2];
+                }
+            }
+        };
+        if (seg > 1) load_rec(1);
+        for (int s = 1; s < seg; ++s) {
+            float cv[TPW][4], cphi[TPW][2];
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cv[k][i] = nv[k][i];
+                cphi[k][0] = nphi[k][0];
+                cphi[k][1] = nphi[k][1];
+            }
+            const float sc = fast_exp2(nl2);
+            if (s + 1 < seg) load_rec(s + 1);
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+#pragma unroll
+                for (int ip = 0; ip < 2; ++ip) {
+                    float sn, cs;
+                    sincosf(cphi[k][ip], &sn, &cs);
+                    const float a0 = sc * hacc[k][2 * ip], a1 = sc * hacc[k][2 * ip + 1];
+                    hacc[k][2 * ip] = cs * a0 - sn * a1 + cv[k][2 * ip];
+                    hacc[k][2 * ip + 1] = sn * a0 + cs * a1 + cv[k][2 * ip + 1];
                 }
             }
         }
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
             const int tau = wv * TPW + k;
-            const int nt = tau / PT;
+            const int nt = tau % NTL;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (!(tau < NTILES && 16 * nt + 4 * g + i < N)) hacc[k][i] = 0.f;
@@ -388,7 +440,7 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
         for (int k = 0; k < TPW; ++k) {
             const int tau = wv * TPW + k;
             if (tau < NTILES) {
-                const int nt = tau / PT, pt = tau % PT;
+                const int pt = tau / NTL, nt = tau % NTL;
                 op_t* dst = base + (16 * pt + l16) * LDH + 16 * nt + 4 * g;
                 const f32x4 v = hacc[k];
                 lds_store4(dst, v[0], v[1], v[2], v[3]);
@@ -404,9 +456,8 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
     int hbuf = 0;
     if constexpr (FULL) stage_state(hbuf);
 
-    double l2seg = 0.0, phiseg = 0.0;   // segment totals (state pass)
+    double l2seg = 0.0, phiseg[4] = {0.0, 0.0, 0.0, 0.0};   // segment totals (state pass)
 
-    if (c_begin < c_end) issue_loads(c_begin);
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int64_t t0 = c * Q;
         const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
@@ -447,63 +498,100 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
             if constexpr (!FULL) l2seg += (double)l2tot;
         }
 
-        // ---- A2: X^T slice (consecutive lanes take consecutive rows) -------
+        // ---- A2: X slice into LDS ----------------------------------------------
 #pragma unroll
         for (int k = 0; k < XI; ++k) {
             int it = tid + k * NT;
             if (XITEMS % NT != 0 && it >= XITEMS) it = XITEMS - 1;   // identical duplicate
-            const int rho = it % T, cg = it / T;
+            int rho, cg;
+            xmap(it, rho, cg);
             const bool ok = rho / R <= jl;
+            float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sX[(8 * cg + e) * LDX + rho] = from_f32<op_t>(ok ? st.xq[k].get(e) : 0.f);
+            for (int e = 0; e < 8; ++e) v[e] = ok ? st.xq[k].get(e) : 0.f;
+            if constexpr (BF) {
+                lds_store8(sX + rho * LDXR + 8 * cg, v);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sX[(8 * cg + e) * LDX + rho] = v[e];
+            }
         }
 
-        // ---- A1: angle prefix per (pair, token block), rotate B and C ------
-        float loc[TPB];
+        // ---- A1: angle prefix per (pair quad, token block), rotate B and C --
+        f32x4 loc[TPB], aoff;
         {
-            float s = 0.f;
+            f32x4 run = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < TPB; ++kk) {
-                if (ablk * TPB + kk <= jl) s += st.dtv[kk] * st.thv[kk];
-                loc[kk] = s;
+                const bool ok = ablk * TPB + kk <= jl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) run[e] += ok ? st.dtv[kk] * st.thv[kk][e] : 0.f;
+                loc[kk] = run;
             }
-            sTot[ablk * NPR + ai] = s;
+            // Exclusive scan of the block sums over the blocks of this wave
+            // (lanes aq, aq + NPR4, ...), then across waves through LDS.
+            const f32x4 tot = aact ? run : f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 inc = tot;
+#pragma unroll
+            for (int d = 1; d < BW; d <<= 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = __shfl_up(inc[e], d * NPR4, 64);
+                    if (lane >= d * NPR4) inc[e] += v;
+                }
+            }
+            aoff = inc - tot;
+            if (lane / NPR4 == BW - 1) *reinterpret_cast<f32x4*>(sWt + wv * NPR + 4 * aq) = inc;
         }
         __syncthreads();
         {
-            float off = 0.f;
 #pragma unroll
-            for (int bb = 0; bb < TB - 1; ++bb) {
-                const float v = sTot[bb * NPR + ai];
-                off += bb < ablk ? v : 0.f;
+            for (int w2 = 0; w2 < NW - 1; ++w2) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(sWt + w2 * NPR + 4 * aq);
+                if (w2 < wv) aoff += v;
             }
 #pragma unroll
             for (int kk = 0; kk < TPB; ++kk) {
                 const int j = ablk * TPB + kk;
                 const bool ok = j <= jl;
-                float sn, cs;
-                rope_sincos<op_t>(off + loc[kk], &sn, &cs);
+                float cs[4], sn[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rope_sincos<op_t>(aoff[e] + loc[kk][e], &sn[e], &cs[e]);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const int rho = j * R + r;
-                    const float b0 = ok ? st.bq[kk][r].lo() : 0.f, b1 = ok ? st.bq[kk][r].hi() : 0.f;
-                    // R(Phi)^T applied to the pair
-                    sstore2(sB + rho * LDB + 2 * ai, cs * b0 + sn * b1, cs * b1 - sn * b0);
+                    // R(Phi)^T applied to each pair
+                    float o[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float b0 = ok ? st.bq[kk][r].get(2 * e) : 0.f;
+                        const float b1 = ok ? st.bq[kk][r].get(2 * e + 1) : 0.f;
+                        o[2 * e] = cs[e] * b0 + sn[e] * b1;
+                        o[2 * e + 1] = cs[e] * b1 - sn[e] * b0;
+                    }
+                    if (aact) lds_store8(sB + rho * LDB + 8 * aq, o);
                     if constexpr (FULL) {
-                        const float c0 = ok ? st.cq[kk][r].lo() : 0.f;
-                        const float c1 = ok ? st.cq[kk][r].hi() : 0.f;
-                        sstore2(sC + rho * LDB + 2 * ai, cs * c0 + sn * c1, cs * c1 - sn * c0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float c0 = ok ? st.cq[kk][r].get(2 * e) : 0.f;
+                            const float c1 = ok ? st.cq[kk][r].get(2 * e + 1) : 0.f;
+                            o[2 * e] = cs[e] * c0 + sn[e] * c1;
+                            o[2 * e + 1] = cs[e] * c1 - sn[e] * c0;
+                        }
+                        if (aact) lds_store8(sC + rho * LDB + 8 * aq, o);
                     }
                 }
             }
-            if (ablk == TB - 1) {
-                const float phi = off + loc[TPB - 1];
-                float sn, cs;
-                sincosf(phi, &sn, &cs);
-                sCSt[2 * ai] = cs;
-                sCSt[2 * ai + 1] = sn;
-                if constexpr (!FULL) phiseg += (double)phi;
+            if (aact && ablk == TBA - 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float phi = aoff[e] + loc[TPB - 1][e];
+                    float sn, cs;
+                    sincosf(phi, &sn, &cs);
+                    sCSt[2 * (4 * aq + e)] = cs;
+                    sCSt[2 * (4 * aq + e) + 1] = sn;
+                    if constexpr (!FULL) phiseg[e] += (double)phi;
+                }
             }
         }
         // This chunk's raw inputs now live in LDS: fetch the next chunk's.
@@ -551,6 +639,7 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
 #pragma unroll 1
                 for (int kp = 0; kp <= qt; kp += 2) {
                     Frag<op_t> pf;
+                    const bool second = kp + 1 <= qt;   // wave-uniform
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         const int kt = kp + half;
@@ -578,9 +667,21 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) {
                         Frag<op_t> xa;
-                        const op_t* xr = sX + (16 * pt + l16) * LDX;
-                        if (kp + 1 <= qt) lds_frag4x2(xa, xr + 16 * kp + 4 * g, xr + 16 * (kp + 1) + 4 * g);
-                        else lds_frag4(xa, xr + 16 * kp + 4 * g);
+                        if constexpr (BF) {
+                            // X^T[p][keys]: keys 16*kp + 4*g + 0..3 (slots 0..3) and
+                            // 16*(kp+1) + 4*g + 0..3 (slots 4..7), column p = 16*pt + l16.
+                            const bf16* xr = sX + (16 * kp + 4 * g + (l16 >> 2)) * LDXR + 16 * pt
+                                             + 4 * (l16 & 3);
+                            const bf16x4 lo = lds_read_tr4(xr);
+                            bf16x4 hi = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+                            if (second) hi = lds_read_tr4(xr + 16 * LDXR);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) { xa.v[e] = lo[e]; xa.v[4 + e] = hi[e]; }
+                        } else {
+                            const op_t* xr = sX + (16 * pt + l16) * LDX;
+                            if (second) lds_frag4x2(xa, xr + 16 * kp + 4 * g, xr + 16 * (kp + 1) + 4 * g);
+                            else lds_frag4(xa, xr + 16 * kp + 4 * g);
+                        }
                         mma(xa, pf, yacc[pt]);
                     }
                 }
@@ -597,34 +698,61 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
         // ---- D: state update  G <- R(Phi_tot)(e^{Lam_tot} G + Bbar_d^T X) --
         {
             const float aT = fast_exp2(sMisc[0]);
-            Frag<op_t> bfr[KB];
-            int cur_nt = -1;
+            // Tiles of a wave: tau = wv*TPW + k -> (nt, pt).  The d-scaled X
+            // operand depends only on (pt, kb) and the Bbar^T operand only on
+            // (nt, kb); each is rebuilt only when its index changes.
+            Frag<op_t> bfr[KB], xfr[KB];
+            int cur_nt = -1, cur_pt = -1;
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
                 const int tau = wv * TPW + k;
                 if (tau < NTILES) {
-                    const int nt = tau / PT, pt = tau % PT;
+                    const int pt = tau / NTL, nt = tau % NTL;
                     if (nt != cur_nt) {
-                        // Bbar_d^T operand rows n = 16*nt + l16: a strided gather
-                        // down the keys of Bbar (stored key-major for C).
+                        // A operand Bbar^T: rows n = 16*nt + l16, K-slots keys 32*kb + 8*g + e.
 #pragma unroll
-                        for (int kb = 0; kb < KB; ++kb)
+                        for (int kb = 0; kb < KB; ++kb) {
+                            if constexpr (BF) {
+                                const bf16* br = sB + (32 * kb + 8 * g + (l16 >> 2)) * LDB + 16 * nt
+                                                 + 4 * (l16 & 3);
+                                const bf16x4 lo = lds_read_tr4(br);
+                                const bf16x4 hi = lds_read_tr4(br + 4 * LDB);
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const int rho = 32 * kb + 8 * g + e;
-                                bfr[kb].set(e, to_f32(sB[rho * LDB + 16 * nt + l16]) * sD[rho / R]);
+                                for (int e = 0; e < 4; ++e) { bfr[kb].v[e] = lo[e]; bfr[kb].v[4 + e] = hi[e]; }
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 8; ++e)
+                                    bfr[kb].set(e, sB[(32 * kb + 8 * g + e) * LDB + 16 * nt + l16]);
                             }
+                        }
                         cur_nt = nt;
+                    }
+                    if (pt != cur_pt) {
+                        // B operand X_d[keys][p] = d_key X[key][p]: column p = 16*pt + l16.
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb) {
+                            float xv[8];
+                            if constexpr (BF) {
+                                const bf16* xr = sX + (32 * kb + 8 * g + (l16 >> 2)) * LDXR + 16 * pt
+                                                 + 4 * (l16 & 3);
+                                const bf16x4 lo = lds_read_tr4(xr);
+                                const bf16x4 hi = lds_read_tr4(xr + 4 * LDXR);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) { xv[e] = (float)lo[e]; xv[4 + e] = (float)hi[e]; }
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) xv[e] = sX[(16 * pt + l16) * LDX + 32 * kb + 8 * g + e];
+                            }
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) xfr[kb].set(e, xv[e] * sD[(32 * kb + 8 * g + e) / R]);
+                        }
+                        cur_pt = pt;
                     }
                     f32x4 acc = hacc[k];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[i] *= aT;
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        Frag<op_t> xfr;
-                        lds_frag8(xfr, sX + (16 * pt + l16) * LDX + 32 * kb + 8 * g);
-                        mma(bfr[kb], xfr, acc);
-                    }
+                    for (int kb = 0; kb < KB; ++kb) mma(bfr[kb], xfr[kb], acc);
 #pragma unroll
                     for (int ip = 0; ip < 2; ++ip) {
                         const int n = 16 * nt + 4 * g + 2 * ip;
@@ -653,7 +781,7 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
         for (int k = 0; k < TPW; ++k) {
             const int tau = wv * TPW + k;
             if (tau < NTILES) {
-                const int nt = tau / PT, pt = tau % PT;
+                const int pt = tau / NTL, nt = tau % NTL;
                 const int64_t col = p0 + 16 * pt + l16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -664,9 +792,12 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
         }
         if (ps == 0) {
             if (tid == 0) rec[(int64_t)N * P] = (float)l2seg;
-            if (ablk == TB - 1 && tid / NPR == TB - 1) {
+            if (aact && ablk == TBA - 1) {
                 const double twopi = 6.283185307179586;
-                rec[(int64_t)N * P + 1 + ai] = (float)(phiseg - twopi * floor(phiseg / twopi));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    rec[(int64_t)N * P + 1 + 4 * aq + e] =
+                        (float)(phiseg[e] - twopi * floor(phiseg[e] / twopi));
             }
         }
         return;
@@ -678,7 +809,7 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
         for (int k = 0; k < TPW; ++k) {
             const int tau = wv * TPW + k;
             if (tau < NTILES) {
-                const int nt = tau / PT, pt = tau % PT;
+                const int pt = tau / NTL, nt = tau % NTL;
                 const int64_t col = p0 + 16 * pt + l16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
