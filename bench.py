@@ -55,6 +55,55 @@ def decode_algorithmic_bytes(w):
     return w.batch * w.heads * per_bh + 4 * w.heads
 
 
+def _counter_rows(path, kernel_regex=None):
+    import csv
+    import re
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel_regex and not re.search(kernel_regex, r["Kernel_Name"]):
+                continue
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_summary(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib,
+                    kernel_regex, call_regex):
+    """HBM bytes per call of the library entry point from rocprofv3 FETCH_SIZE
+    and WRITE_SIZE runs (KiB per dispatch, summed over the dispatches a call
+    makes), each scaled by copy_bytes / counter reading of a plain device copy
+    of `copy_mib` MiB.  Writes profiles/<name>_traffic.json."""
+    import collections
+    copy_bytes = copy_mib * (1 << 20)
+
+    def per_dispatch(path, regex):
+        d = collections.defaultdict(float)
+        for did, k, v in _counter_rows(path, regex):
+            d[did] += v
+        return d
+
+    cf = per_dispatch(copy_fetch_csv, "copyBuffer|copy")
+    cw = per_dispatch(copy_write_csv, "copyBuffer|copy")
+    big_f = [v for v in cf.values() if v > copy_bytes / 1024 / 8]
+    big_w = [v for v in cw.values() if v > copy_bytes / 1024 / 8]
+    ffac = copy_bytes / (sum(big_f) / len(big_f) * 1024)
+    wfac = copy_bytes / (sum(big_w) / len(big_w) * 1024)
+    f = per_dispatch(fetch_csv, kernel_regex)
+    w = per_dispatch(write_csv, kernel_regex)
+    ncalls_f = len({d for d, k, v in _counter_rows(fetch_csv, call_regex)})
+    ncalls_w = len({d for d, k, v in _counter_rows(write_csv, call_regex)})
+    fetch = sum(f.values()) * 1024 * ffac / ncalls_f
+    write = sum(w.values()) * 1024 * wfac / ncalls_w
+    out = {"workload": name, "bytes_per_launch": round(fetch + write),
+           "fetch_bytes": round(fetch), "write_bytes": round(write),
+           "fetch_scale": round(ffac, 4), "write_scale": round(wfac, 4),
+           "calls": ncalls_f, "source_hash": kernel_source_hash()}
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    with open(os.path.join(PROFILE_DIR, "%s_traffic.json" % name), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mamba_selective_ssm_amd", "csrc")
@@ -100,13 +149,10 @@ def time_launches(fn, steps, warmup, torch):
 
 def bench_prefill(w, steps, warmup, torch, m3, synth, seed=1001):
     inp = synth.make_scan_inputs(w, seed, "cuda")
-    st_out = m3.zero_state(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.torch_dtype, "cuda")
-    y = torch.empty_like(inp["x"])
-
-    def step():
-        m3.m3_scan_fwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
-                       inp["lam"], chunk=w.chunk, y=y, state_out=st_out)
-
+    # Arguments, outputs and workspace are prepared once; each step is one
+    # m3_scan_fwd call on the same resident inputs.
+    step = m3.ScanCall(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
+                       inp["lam"], chunk=w.chunk)
     total, kms = time_launches(step, steps, warmup, torch)
     tokens = w.batch * w.seqlen
     nbytes = scan_algorithmic_bytes(w)
@@ -125,11 +171,11 @@ def bench_decode(w, steps, warmup, torch, m3, synth, seed=1004):
     nsteps = warmup + steps
     ins = [synth.make_decode_inputs(w, seed, s, A, "cuda") for s in range(nsteps)]
     y = torch.empty(w.batch, w.heads, w.rank, w.headdim, dtype=w.torch_dtype, device="cuda")
-    it = iter(ins)
+    calls = iter([m3.DecodeCall(s["x"], s["B"], s["C"], s["dt"], s["A"], s["theta"], s["lam"],
+                                st, y=y) for s in ins])
 
     def step():
-        s = next(it)
-        m3.m3_decode_step(s["x"], s["B"], s["C"], s["dt"], s["A"], s["theta"], s["lam"], st, y=y)
+        next(calls)()
 
     total, kms = time_launches(step, steps, warmup, torch)
     nbytes = decode_algorithmic_bytes(w)
@@ -150,7 +196,7 @@ def cpu_baseline(w, inp, budget_s, torch):
     while True:
         oracle.scan(*args, threads=threads)
         reps += 1
-        if time.perf_counter() - t0 >= budget_s or reps >= 50:
+        if time.perf_counter() - t0 >= budget_s or reps >= 1000:
             break
     el = time.perf_counter() - t0
     return {"value": w.batch * w.seqlen * reps / el, "unit": "tokens/s", "cores": threads,
@@ -176,7 +222,21 @@ def main(argv=None):
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time the decode workload (for per-kernel counter runs)")
+    ap.add_argument("--traffic-summary", nargs=5,
+                    metavar=("NAME", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE csv files into "
+                         "profiles/NAME_traffic.json (no GPU needed)")
+    ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args(argv)
+
+    if args.traffic_summary:
+        name = args.traffic_summary[0]
+        regex, call = (("decode_kernel", "decode_kernel") if name == "decode"
+                       else ("scan_kernel", "scan_kernel.*Lb1E"))
+        traffic_summary(name, *args.traffic_summary[1:], args.copy_mib, regex, call)
+        return 0
 
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the mixer needs no exchange "
@@ -195,6 +255,15 @@ def main(argv=None):
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}))
+        return 0
+
+    if args.decode_only:
+        wd = synth.WORKLOADS["decode"]
+        progress("timing decode only: prefill + %d steps" % args.decode_steps)
+        rd = bench_decode(wd, args.decode_steps, 2, torch, m3, synth)
+        print(json.dumps({"workload": "decode", "steps_per_s": round(rd["steps_per_s"], 1),
+                          "kernel_ms": round(rd["kernel_ms"], 5),
+                          "hbm_gbs": round(rd["gbs"], 1)}), flush=True)
         return 0
 
     w = synth.WORKLOADS[args.workload]

@@ -151,12 +151,8 @@ def _stream_handle(stream) -> int:
     return s.cuda_stream
 
 
-def m3_scan_fwd(x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
-                chunk: int = 0, p_split: int = 0, segments: int = 0,
-                return_state: bool = True, y: Optional[torch.Tensor] = None,
-                state_out: Optional[State] = None, workspace: Optional[torch.Tensor] = None,
-                stream=None):
-    """Chunked prefill.  Returns (y, State after the last token or None)."""
+def _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, return_state,
+                  y, state_out, workspace):
     lib = load_library()
     Bt, L, H, R, P = x.shape
     N = B.shape[-1]
@@ -197,10 +193,44 @@ def m3_scan_fwd(x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
             workspace = torch.empty(int(need), dtype=torch.uint8, device=x.device)
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
-    st = lib.m3_scan_fwd(ctypes.byref(a), _stream_handle(stream))
+    return a, y, state_out, workspace
+
+
+def m3_scan_fwd(x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
+                chunk: int = 0, p_split: int = 0, segments: int = 0,
+                return_state: bool = True, y: Optional[torch.Tensor] = None,
+                state_out: Optional[State] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None):
+    """Chunked prefill.  Returns (y, State after the last token or None)."""
+    a, y, state_out, _ = _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split,
+                                       segments, return_state, y, state_out, workspace)
+    st = load_library().m3_scan_fwd(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_fwd")
     return y, state_out
+
+
+class ScanCall:
+    """An m3_scan_fwd call marshalled once: calling it re-issues the same scan
+    (same tensors, outputs and workspace) on the current stream.  Repeated
+    scans then cost one C call each."""
+
+    def __init__(self, x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
+                 chunk: int = 0, p_split: int = 0, segments: int = 0, return_state: bool = True,
+                 y: Optional[torch.Tensor] = None, state_out: Optional[State] = None,
+                 workspace: Optional[torch.Tensor] = None):
+        self._keep = (x, B, C, dt, A, theta, lam, state)
+        self.args, self.y, self.state_out, self.workspace = _prepare_scan(
+            x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, return_state, y,
+            state_out, workspace)
+        self._ref = ctypes.byref(self.args)
+        self._fn = load_library().m3_scan_fwd
+
+    def __call__(self, stream=None):
+        st = self._fn(self._ref, _stream_handle(stream))
+        if st != 0:
+            raise M3Error(st, "m3_scan_fwd")
+        return self.y, self.state_out
 
 
 def m3_scan_workspace_bytes(x, B, *, chunk=0, p_split=0, segments=0) -> int:
@@ -210,10 +240,7 @@ def m3_scan_workspace_bytes(x, B, *, chunk=0, p_split=0, segments=0) -> int:
     return int(load_library().m3_scan_workspace_bytes(ctypes.byref(a)))
 
 
-def m3_decode_step(x, B, C, dt, A, theta, lam, state: State, *,
-                   y: Optional[torch.Tensor] = None, stream=None):
-    """One token for every (batch, head); ``state`` is updated in place.  Returns y_t."""
-    lib = load_library()
+def _prepare_decode(x, B, C, dt, A, theta, lam, state, y):
     Bt, H, R, P = x.shape
     N = B.shape[-1]
     io = _io_code(x.dtype)
@@ -234,7 +261,32 @@ def m3_decode_step(x, B, C, dt, A, theta, lam, state: State, *,
                    x=_ptr(x), B=_ptr(B), C=_ptr(C), dt=_ptr(dt), A=_ptr(A),
                    theta=_ptr(theta), lam=_ptr(lam), h=_ptr(state.h),
                    B_prev=_ptr(state.B_prev), x_prev=_ptr(state.x_prev), y=_ptr(y))
-    st = lib.m3_decode_step(ctypes.byref(a), _stream_handle(stream))
+    return a, y
+
+
+def m3_decode_step(x, B, C, dt, A, theta, lam, state: State, *,
+                   y: Optional[torch.Tensor] = None, stream=None):
+    """One token for every (batch, head); ``state`` is updated in place.  Returns y_t."""
+    a, y = _prepare_decode(x, B, C, dt, A, theta, lam, state, y)
+    st = load_library().m3_decode_step(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_decode_step")
     return y
+
+
+class DecodeCall:
+    """An m3_decode_step call marshalled once (fixed step inputs, state record
+    and y); calling it issues that step on the current stream."""
+
+    def __init__(self, x, B, C, dt, A, theta, lam, state: State, *,
+                 y: Optional[torch.Tensor] = None):
+        self._keep = (x, B, C, dt, A, theta, lam, state)
+        self.args, self.y = _prepare_decode(x, B, C, dt, A, theta, lam, state, y)
+        self._ref = ctypes.byref(self.args)
+        self._fn = load_library().m3_decode_step
+
+    def __call__(self, stream=None):
+        st = self._fn(self._ref, _stream_handle(stream))
+        if st != 0:
+            raise M3Error(st, "m3_decode_step")
+        return self.y

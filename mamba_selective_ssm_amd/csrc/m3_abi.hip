@@ -33,7 +33,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int io_size(int dt) { return dt == M3_F32 ? 4 : 2; }
 
-int default_chunk(int64_t R) { return R == 1 ? 64 : (R == 2 ? 32 : 16); }
+// Default chunk length: 64 tokens, or 32 for rank >= 2 (16 for fp32 rank 4,
+// whose tiles would not fit LDS at 32).
+int default_chunk(int64_t R, int io) { return R == 1 ? 64 : (R == 2 || io == M3_BF16 ? 32 : 16); }
 
 template <typename F>
 void for_each_variant(F&& f)
@@ -54,14 +56,14 @@ void for_each_variant(F&& f)
 const m3::ScanVariant* pick_scan(int io, int64_t N, int64_t R, int64_t P, int chunk,
                                  int p_split, int64_t nbh)
 {
-    const int Q = chunk ? chunk : default_chunk(R);
+    const int Q = chunk ? chunk : default_chunk(R, io);
     const m3::ScanVariant* best = nullptr;
     for_each_variant([&](const m3::ScanVariant& v) {
         if (v.io != io || v.N != N || v.R != R || v.Q != Q) return;
         if (P % v.PS != 0) return;
         if (p_split != 0 && P / v.PS != p_split) return;
         (void)nbh;
-        if (best == nullptr || v.PS > best->PS) best = &v;
+        if (best == nullptr || v.PS > best->PS) best = &v;   // first of the widest
     });
     return best;
 }
@@ -101,10 +103,11 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
     const int64_t nchunks = (L + v->Q - 1) / v->Q;
     int64_t nseg = a->segments;
     if (nseg == 0) {
-        // Aim for about two workgroups per compute unit, with at least four
-        // chunks per segment.
+        // Aim for about 8 waves per compute unit (2048 / NW workgroups on 256
+        // CUs), with at least four chunks per segment.
         const int64_t per_seg = (nbh > 0 ? (nbh + 7) / 8 * 8 : 8) * p_split;
-        nseg = (512 + per_seg - 1) / per_seg;
+        const int64_t target = 2048 / v->NW;
+        nseg = (target + per_seg - 1) / per_seg;
         if (nseg > nchunks / 4) nseg = nchunks / 4;
         if (nseg > 64) nseg = 64;
     }

@@ -48,10 +48,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
     IO* xp = reinterpret_cast<IO*>(p.xp) + bh * R * P;
     float* hs = p.h + bh * (int64_t)N * P;
 
-    // State loads first: they are the bulk of the traffic.
+    // State loads first (the bulk of the traffic): the first round of a
+    // thread's rows is in flight while the small operands go to LDS.
     const int items = NPR * P4;
     float4 hv[kDecBatch][2];
     const int nrounds = (items + kDecThreads * kDecBatch - 1) / (kDecThreads * kDecBatch);
+    const int cg = tid % P4;   // fixed per thread: kDecThreads is a multiple of P4
+    auto load_round = [&](int rd) {
+        const int base = rd * kDecThreads * kDecBatch;
+#pragma unroll
+        for (int k = 0; k < kDecBatch; ++k) {
+            const int it = base + k * kDecThreads + tid;
+            if (it < items) {
+                const int i = it / P4;
+                const float4* src = reinterpret_cast<const float4*>(hs + (int64_t)(2 * i) * P) + cg;
+                hv[k][0] = src[0];
+                hv[k][1] = src[P4];
+            }
+        }
+    };
+    if (nrounds > 0) load_round(0);
 
     for (int idx = tid; idx < R * N; idx += kDecThreads) {
         sBp[idx] = to_f32(Bp[idx]);
@@ -85,21 +101,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
 #pragma unroll
         for (int q = 0; q < 4; ++q) yp[r][q] = 0.f;
 
-    // Threads sharing a column group: tid % P4 is fixed for a thread because
-    // kDecThreads is a multiple of P4 (P4 divides 64).
-    const int cg = tid % P4;
     for (int rd = 0; rd < nrounds; ++rd) {
         const int base = rd * kDecThreads * kDecBatch;
-#pragma unroll
-        for (int k = 0; k < kDecBatch; ++k) {
-            const int it = base + k * kDecThreads + tid;
-            if (it < items) {
-                const int i = it / P4;
-                const float4* src = reinterpret_cast<const float4*>(hs + (int64_t)(2 * i) * P) + cg;
-                hv[k][0] = src[0];
-                hv[k][1] = src[P4];
-            }
-        }
+        if (rd > 0) load_round(rd);
 #pragma unroll
         for (int k = 0; k < kDecBatch; ++k) {
             const int it = base + k * kDecThreads + tid;
@@ -156,9 +160,12 @@ template <typename IO, int R>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream)
 {
     const size_t lds = sizeof(float) * (3 * R * p.N + 2 * R * p.P + p.N + kDecThreads * R * 4);
-    const void* fn = reinterpret_cast<const void*>(&decode_kernel<IO, R>);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    // The largest supported shape (N = 1024, P = 256, R = 4) needs 76 KiB;
+    // raise the limit once.
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_kernel<IO, R>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    if (attr != hipSuccess) return attr;
     (void)hipGetLastError();
     hipLaunchKernelGGL((decode_kernel<IO, R>), dim3((unsigned)p.nbh), dim3(kDecThreads), lds,
                        stream, p);

@@ -10,7 +10,7 @@ const ScanVariant* scan_variants_bf16a(int* count)
     static const ScanVariant table[] = {
     V(16, 1, 64),  V(32, 1, 64),  V(64, 1, 64),  V(128, 1, 64),
     V(16, 2, 32),  V(32, 2, 32),  V(64, 2, 32),  V(128, 2, 32),
-    V(16, 4, 16),  V(32, 4, 16),  V(64, 4, 16),  V(128, 4, 16),
+    V(16, 4, 32),  V(32, 4, 32),  V(64, 4, 32),  V(128, 4, 32),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -6,7 +6,12 @@ namespace m3 {
 
 const ScanVariant* scan_variants_bf16b(int* count)
 {
+    // Order matters: among variants with the same (N, R, chunk) and the widest
+    // headdim slice, the first listed is the one the library picks.
     static const ScanVariant table[] = {
+    M3_SCAN_VARIANT(bf16, 1, 128, 1, 64, 64, 8),
+    M3_SCAN_VARIANT(bf16, 1, 128, 4, 32, 64, 8),
+    M3_SCAN_VARIANT(bf16, 1, 64, 1, 128, 64, 8),
     M3_SCAN_VARIANT(bf16, 1, 64, 1, 32, 16, 4),
     M3_SCAN_VARIANT(bf16, 1, 64, 1, 128, 16, 4),
     M3_SCAN_VARIANT(bf16, 1, 128, 1, 32, 16, 4),

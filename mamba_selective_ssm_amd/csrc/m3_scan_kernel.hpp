@@ -45,8 +45,8 @@
 //       operand type, Y^T += X^T (S o M)^T, plus the state term
 //       e^{Lam_j} G^T Cbar^T; y written straight from the accumulators.
 //   D   each wave owns state tiles: G <- R(Phi_tot)(e^{Lam_tot} G + Bbar_d^T X)
-//       on matrix cores; the new state is staged in LDS (bf16 hi + lo split
-//       for the bf16 path) as the next chunk's state-term operand.  The stage
+//       on matrix cores; the new state is staged in LDS (in the operand type)
+//       as the next chunk's state-term operand.  The stage
 //       is double-buffered, so C and D of one chunk need no barrier between
 //       them.
 //
@@ -97,7 +97,10 @@ struct ScanCfg {
     static constexpr int LDX = T + PADE;             // fp32: X^T rows
     static constexpr int LDXR = PS + PADE;           // bf16: X rows
     static constexpr int LDH = NP + PADE;
-    static constexpr bool HILO = BF;
+    // The state-term operand is the state rounded once to the operand type
+    // (bf16 relative error 2^-9 on that term).  A hi + lo split halves the
+    // error at twice the state-term matrix-core work; it is off.
+    static constexpr bool HILO = false;
     static constexpr int NHT = HILO ? 2 : 1;
     static constexpr int TBA = NT / NPR4 < Q ? NT / NPR4 : Q;   // angle-scan token blocks
     static constexpr int TPB = Q / TBA;              // tokens per block
@@ -433,7 +436,7 @@ __global__ __launch_bounds__(Cf::NT) void scan_kernel(const ScanParams p)
         for (int k = 0; k < TPW; ++k) hacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Stage G^T (operand type; bf16 as hi + lo) into state buffer `buf`.
+    // Stage G^T (operand type; optionally hi + lo) into state buffer `buf`.
     auto stage_state = [&](int buf) {
         op_t* base = sH + buf * HSTAGE;
 #pragma unroll
@@ -848,6 +851,18 @@ size_t scan_workspace_bytes(int64_t nbh, int64_t P, int nseg)
     return nseg > 1 ? (size_t)nbh * (size_t)(nseg - 1) * (size_t)Cf::rec_floats(P) * 4 : 0;
 }
 
+// Raise the dynamic-LDS limit of one kernel once per process.
+template <class Cf, bool FULL>
+hipError_t scan_set_lds_limit()
+{
+    static hipError_t status = [] {
+        const void* f = reinterpret_cast<const void*>(&scan_kernel<Cf, FULL>);
+        return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)(FULL ? Cf::lds_bytes : Cf::lds_bytes_state));
+    }();
+    return status;
+}
+
 template <class Cf>
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream)
 {
@@ -855,17 +870,14 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t stream)
     hipError_t e;
     (void)hipGetLastError();
     if (p.nseg > 1) {
-        const void* f1 = reinterpret_cast<const void*>(&scan_kernel<Cf, false>);
-        e = hipFuncSetAttribute(f1, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)Cf::lds_bytes_state);
+        e = scan_set_lds_limit<Cf, false>();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((scan_kernel<Cf, false>), dim3((unsigned)(per_seg * (p.nseg - 1))),
                            dim3(Cf::NT), Cf::lds_bytes_state, stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const void* f2 = reinterpret_cast<const void*>(&scan_kernel<Cf, true>);
-    e = hipFuncSetAttribute(f2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::lds_bytes);
+    e = scan_set_lds_limit<Cf, true>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((scan_kernel<Cf, true>), dim3((unsigned)(per_seg * p.nseg)), dim3(Cf::NT),
                        Cf::lds_bytes, stream, p);

@@ -55,13 +55,13 @@ WORKLOADS = {
     "prefill_bf16": Workload("prefill_bf16", 4, 16, 2048, 64, 64, 1, "bf16", 64, -2.0,
                              "normal_0.5"),
     # MIMO prefill, rank 4.
-    "mimo_prefill_bf16": Workload("mimo_prefill_bf16", 8, 32, 4096, 64, 128, 4, "bf16", 16,
+    "mimo_prefill_bf16": Workload("mimo_prefill_bf16", 8, 32, 4096, 64, 128, 4, "bf16", 32,
                                   -2.0, "normal_0.5"),
     # Long-context prefill with slow decay.
     "long_prefill_bf16": Workload("long_prefill_bf16", 1, 32, 65536, 64, 128, 1, "bf16", 64,
                                   -3.0, "normal_0.5"),
     # Decode: 1024-token MIMO prefill at batch 256, then 1024 single-token steps.
-    "decode": Workload("decode", 256, 32, 1024, 64, 128, 4, "bf16", 16, -2.0, "normal_0.5",
+    "decode": Workload("decode", 256, 32, 1024, 64, 128, 4, "bf16", 32, -2.0, "normal_0.5",
                        decode_steps=1024),
 }
 
