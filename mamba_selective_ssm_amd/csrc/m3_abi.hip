@@ -33,9 +33,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int io_size(int dt) { return dt == M3_F32 ? 4 : 2; }
 
-// Default chunk length: 64 tokens, or 32 for rank >= 2 (16 for fp32 rank 4,
-// whose tiles would not fit LDS at 32).
-int default_chunk(int64_t R, int io) { return R == 1 ? 64 : (R == 2 || io == M3_BF16 ? 32 : 16); }
+// Default chunk length: 64 operand rows (tokens x rank) for bf16, 32 for fp32
+// (whose double-buffered tiles take twice the LDS).
+int default_chunk(int64_t R, int io) { return io == M3_BF16 ? (int)(64 / R) : (int)(32 / R); }
 
 template <typename F>
 void for_each_variant(F&& f)
@@ -103,12 +103,12 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
     const int64_t nchunks = (L + v->Q - 1) / v->Q;
     int64_t nseg = a->segments;
     if (nseg == 0) {
-        // Aim for about 8 waves per compute unit (2048 / NW workgroups on 256
-        // CUs), with at least four chunks per segment.
+        // Fill the chip: about `occ` workgroups per compute unit (256 CUs),
+        // with at least three chunks per segment.
         const int64_t per_seg = (nbh > 0 ? (nbh + 7) / 8 * 8 : 8) * p_split;
-        const int64_t target = 2048 / v->NW;
+        const int64_t target = 256 * (int64_t)v->occ;
         nseg = (target + per_seg - 1) / per_seg;
-        if (nseg > nchunks / 4) nseg = nchunks / 4;
+        if (nseg > nchunks / 3) nseg = nchunks / 3;
         if (nseg > 64) nseg = 64;
     }
     if (nseg > nchunks) nseg = nchunks;

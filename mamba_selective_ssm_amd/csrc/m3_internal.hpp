@@ -30,6 +30,7 @@ typedef size_t (*scan_ws_fn)(int64_t nbh, int64_t P, int nseg);
 struct ScanVariant {
     int io;        // m3_dtype
     int N, R, Q, PS, NW;
+    int occ;       // workgroups per compute unit the launch bounds aim for
     size_t lds_bytes;
     scan_launcher fn;
     scan_ws_fn ws_bytes;   // workspace bytes for a segmented call

@@ -3,7 +3,8 @@
 
 #include "m3_scan_kernel.hpp"
 
-#define M3_SCAN_VARIANT(IO, IOCODE, N, R, Q, PS, NW)                                   \
-    {IOCODE, N, R, Q, PS, NW, ::m3::ScanCfg<IO, N, PS, R, Q, NW>::lds_bytes,            \
-     &::m3::launch_scan<::m3::ScanCfg<IO, N, PS, R, Q, NW>>,                          \
-     &::m3::scan_workspace_bytes<::m3::ScanCfg<IO, N, PS, R, Q, NW>>}
+#define M3_SCAN_VARIANT(IO, IOCODE, N, R, Q, PS, NWM, NWP, OCC)                              \
+    {IOCODE, N, R, Q, PS, NWM + NWP, OCC,                                                    \
+     ::m3::ScanCfg<IO, N, PS, R, Q, NWM, NWP, OCC>::lds_bytes,                               \
+     &::m3::launch_scan<::m3::ScanCfg<IO, N, PS, R, Q, NWM, NWP, OCC>>,                      \
+     &::m3::scan_workspace_bytes<::m3::ScanCfg<IO, N, PS, R, Q, NWM, NWP, OCC>>}

@@ -50,18 +50,18 @@ class Workload:
 
 WORKLOADS = {
     # Tiny fp32 single-head scan (oracle finishes instantly).
-    "tiny_f32": Workload("tiny_f32", 1, 1, 64, 16, 16, 1, "f32", 64, 0.0, "uniform_pi"),
+    "tiny_f32": Workload("tiny_f32", 1, 1, 64, 16, 16, 1, "f32", 32, 0.0, "uniform_pi"),
     # Single-layer prefill, bf16 I/O, fp32 state and accumulation.
     "prefill_bf16": Workload("prefill_bf16", 4, 16, 2048, 64, 64, 1, "bf16", 64, -2.0,
                              "normal_0.5"),
     # MIMO prefill, rank 4.
-    "mimo_prefill_bf16": Workload("mimo_prefill_bf16", 8, 32, 4096, 64, 128, 4, "bf16", 32,
+    "mimo_prefill_bf16": Workload("mimo_prefill_bf16", 8, 32, 4096, 64, 128, 4, "bf16", 16,
                                   -2.0, "normal_0.5"),
     # Long-context prefill with slow decay.
     "long_prefill_bf16": Workload("long_prefill_bf16", 1, 32, 65536, 64, 128, 1, "bf16", 64,
                                   -3.0, "normal_0.5"),
     # Decode: 1024-token MIMO prefill at batch 256, then 1024 single-token steps.
-    "decode": Workload("decode", 256, 32, 1024, 64, 128, 4, "bf16", 32, -2.0, "normal_0.5",
+    "decode": Workload("decode", 256, 32, 1024, 64, 128, 4, "bf16", 16, -2.0, "normal_0.5",
                        decode_steps=1024),
 }
 
