@@ -54,11 +54,16 @@
 // Sequence segments (more workgroups when batch*heads*slices is small): a
 // state pass walks segments 0..S-2 without outputs and records each one's end
 // state (segment 0 from the true initial state, the others from zero) with
-// its total decay and the cosine/sine of its total angle; a fold kernel makes
-// the records inclusive under the chunk-summary operator
-// (a2,Phi2,S2)o(a1,Phi1,S1) = (a1+a2, Phi1+Phi2, e^{a2} R(Phi2) S1 + S2), and
-// the output pass starts segment s from inclusive record s-1.
+// its total decay and the cosine/sine of its total angle; the output pass
+// starts segment s from the fold of records 0..s-1 under the chunk-summary
+// operator (a2,Phi2,S2)o(a1,Phi1,S1) = (a1+a2, Phi1+Phi2, e^{a2} R(Phi2) S1 + S2),
+// computed by its math waves while the prep waves wait for the first chunk.
+// (The kernel boundary orders the two passes; any hand-off between
+// workgroups of one pass would need device-scope fences, which write back
+// and invalidate the L2 under every workgroup still streaming.)
 #pragma once
+
+#include <type_traits>
 
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
@@ -124,6 +129,9 @@ struct ScanCfg {
     // When every math wave reads in C only the state rows it writes itself in
     // D, one state stage suffices (LDS operations of a wave stay in order).
     static constexpr bool SH1 = (QG == 1) && (NTILES % NWM == 0);
+    // Segment records folded per round trip in the output pass prologue
+    // (8*TPW + 1 registers each).
+    static constexpr int FB = TPW <= 2 ? 4 : (TPW <= 4 || OCC == 1 ? 2 : 1);
     // LDS: two chunk buffers {Bbar, Cbar, X, scalars} and the state stage(s).
     static constexpr size_t sz_B = (size_t)T * LDB * E;
     static constexpr size_t sz_X = BF ? (size_t)T * LDXR * E : (size_t)PS * LDX * E;
@@ -140,10 +148,11 @@ struct ScanCfg {
     };
     static constexpr size_t lds_bytes = Lay<true>::bytes;
     static constexpr size_t lds_bytes_state = Lay<false>::bytes;
-    // Segment record: G [N][P] fp32, Lam_seg*log2(e), then (cos, sin) of the
-    // segment's total angle per pair.
-    __host__ __device__ static int64_t rec_floats(int64_t P) { return ((int64_t)N * P + 1 + 2 * NPR + 3) / 4 * 4; }
+    // Segment record: G [N][P] fp32, Lam_seg*log2(e) (padded to 4 floats),
+    // then (cos, sin) of the segment's total angle per pair.
+    __host__ __device__ static int64_t rec_floats(int64_t P) { return (int64_t)N * P + 4 + 2 * NPR; }
     static_assert(T % 32 == 0, "Q*R must be a multiple of 32");
+    static_assert(R == 1 || R == 2 || R == 4, "rank must be 1, 2 or 4");
     static_assert(PS % 16 == 0, "headdim slice must be a multiple of 16");
     static_assert(N % 8 == 0 && LQ >= 16 && LQ <= 64, "unsupported dstate");
     static_assert(NPR4 < NWP || NPR4 % NWP == 0, "pair quads must split evenly over prep waves");
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     constexpr int QPWV = Cf::QPWV, WA = Cf::WA, LQ = Cf::LQ, TPL = Cf::TPL, QPL = Cf::QPL;
     constexpr int XI = Cf::XI, XITEMS = Cf::XITEMS;
     constexpr int QT = Cf::QT, KB = Cf::KB, NTL = Cf::NTL, NTILES = Cf::NTILES, TPW = Cf::TPW;
-    constexpr int PG = Cf::PG, QG = Cf::QG, PPW = Cf::PPW, QPW = Cf::QPW;
+    constexpr int PG = Cf::PG, QG = Cf::QG, PPW = Cf::PPW, QPW = Cf::QPW, FB = Cf::FB;
     constexpr bool BF = Cf::BF;
     constexpr int HSTAGE = PS * LDH;   // elements of one state stage
 
@@ -396,64 +405,86 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
 
         // ---- A1: angle prefix per pair quad, rotate B and C ----------------
         if (arole) {
-            f32x4 loc[TPL];
-            f32x4 run = {0.f, 0.f, 0.f, 0.f};
+            // FULLC: every token of the chunk is valid (no masking needed)
+            auto rotate_all = [&](auto fullc) {
+                constexpr bool FULLC = decltype(fullc)::value;
+                f32x4 loc[TPL];
+                f32x4 run = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < TPL; ++kk) {
-                const bool ok = li * TPL + kk <= jl;
+                for (int kk = 0; kk < TPL; ++kk) {
+                    // lanes past the chunk (LQ * TPL > Q) never contribute
+                    const int j = li * TPL + kk;
+                    const bool ok = FULLC ? (LQ * TPL == Q || j < Q) : j <= jl;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) run[e] += ok ? st.dtv[kk] * st.thv[kk][e] : 0.f;
-                loc[kk] = run;
-            }
-            f32x4 inc;
+                    for (int e = 0; e < 4; ++e) run[e] += ok ? st.dtv[kk] * st.thv[kk][e] : 0.f;
+                    loc[kk] = run;
+                }
+                f32x4 inc;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) inc[e] = group_inclusive_sum<LQ>(run[e]);
-            const f32x4 ex = inc - run;
+                for (int e = 0; e < 4; ++e) inc[e] = group_inclusive_sum<LQ>(run[e]);
+                const f32x4 ex = inc - run;
 #pragma unroll
-            for (int kk = 0; kk < TPL; ++kk) {
-                const int j = li * TPL + kk;
-                const bool ok = j <= jl;
-                if (j < Q) {
-                    float cs[4], sn[4];
+                for (int kk = 0; kk < TPL; ++kk) {
+                    const int j = li * TPL + kk;
+                    const bool ok = FULLC || j <= jl;
+                    if (LQ * TPL == Q || j < Q) {
+                        float cs[4], sn[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) rope_sincos<op_t>(ex[e] + loc[kk][e], &sn[e], &cs[e]);
+                        for (int e = 0; e < 4; ++e) rope_sincos<op_t>(ex[e] + loc[kk][e], &sn[e], &cs[e]);
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const int rho = j * R + r;
-                        // R(Phi)^T applied to each pair
-                        float o[8];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float b0 = ok ? st.bq[kk][r].get(2 * e) : 0.f;
-                            const float b1 = ok ? st.bq[kk][r].get(2 * e + 1) : 0.f;
-                            o[2 * e] = cs[e] * b0 + sn[e] * b1;
-                            o[2 * e + 1] = cs[e] * b1 - sn[e] * b0;
-                        }
-                        lds_store8(sB + rho * LDB + 8 * qd, o);
-                        if constexpr (FULL) {
+                        for (int r = 0; r < R; ++r) {
+                            const int rho = j * R + r;
+                            // R(Phi)^T applied to each pair
+                            float o[8];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const float c0 = ok ? st.cq[kk][r].get(2 * e) : 0.f;
-                                const float c1 = ok ? st.cq[kk][r].get(2 * e + 1) : 0.f;
-                                o[2 * e] = cs[e] * c0 + sn[e] * c1;
-                                o[2 * e + 1] = cs[e] * c1 - sn[e] * c0;
+                                const float b0 = ok ? st.bq[kk][r].get(2 * e) : 0.f;
+                                const float b1 = ok ? st.bq[kk][r].get(2 * e + 1) : 0.f;
+                                o[2 * e] = cs[e] * b0 + sn[e] * b1;
+                                o[2 * e + 1] = cs[e] * b1 - sn[e] * b0;
                             }
-                            lds_store8(sC + rho * LDB + 8 * qd, o);
+                            lds_store8(sB + rho * LDB + 8 * qd, o);
+                            if constexpr (FULL) {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const float c0 = ok ? st.cq[kk][r].get(2 * e) : 0.f;
+                                    const float c1 = ok ? st.cq[kk][r].get(2 * e + 1) : 0.f;
+                                    o[2 * e] = cs[e] * c0 + sn[e] * c1;
+                                    o[2 * e + 1] = cs[e] * c1 - sn[e] * c0;
+                                }
+                                lds_store8(sC + rho * LDB + 8 * qd, o);
+                            }
                         }
                     }
                 }
-            }
-            // The group's last lane holds the chunk's total angle per pair.
-            if (li == LQ - 1) {
+                // The group's last lane holds the chunk's total angle per pair.
+                if constexpr (BF) {
+                    // hardware sine/cosine in every lane (no divergent branch)
+                    float cs[4], sn[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float sn, cs;
-                    sincosf(inc[e], &sn, &cs);
-                    sCSt[2 * (4 * qd + e)] = cs;
-                    sCSt[2 * (4 * qd + e) + 1] = sn;
-                    if constexpr (!FULL) phiseg[e] += (double)inc[e];
+                    for (int e = 0; e < 4; ++e) __sincosf(inc[e], &sn[e], &cs[e]);
+                    if (li == LQ - 1) {
+                        *reinterpret_cast<f32x4*>(sCSt + 8 * qd) = f32x4{cs[0], sn[0], cs[1], sn[1]};
+                        *reinterpret_cast<f32x4*>(sCSt + 8 * qd + 4) = f32x4{cs[2], sn[2], cs[3], sn[3]};
+                    }
+                } else if (li == LQ - 1) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float sn, cs;
+                        sincosf(inc[e], &sn, &cs);
+                        sCSt[2 * (4 * qd + e)] = cs;
+                        sCSt[2 * (4 * qd + e) + 1] = sn;
+                    }
                 }
-            }
+                if constexpr (!FULL) {
+                    if (li == LQ - 1) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) phiseg[e] += (double)inc[e];
+                    }
+                }
+            };
+            if (jl == Q - 1) rotate_all(std::true_type{});
+            else rotate_all(std::false_type{});
         }
     };
 
@@ -520,18 +551,55 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 }
             }
         } else if constexpr (FULL) {
-            // The state entering segment seg: record seg-1, made inclusive of
-            // all earlier segments by the fold kernel.
-            const float* rec = recs + (int64_t)(seg - 1) * rec_sz;
+            // The state entering segment seg: fold of records 0..seg-1 under
+            // the chunk-summary operator, G <- R(Phi_s)(2^{l2_s} G) + G_s.
+            // FB records per round trip; this overlaps the prep waves' wait
+            // for the first chunk's inputs.
+#pragma unroll 1
+            for (int s0 = 0; s0 < seg; s0 += FB) {
+                float gv[FB][TPW][4], cz[FB][TPW][4], l2v[FB];
 #pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-                int pt, nt;
-                tile_of(k, pt, nt);
-                const int64_t col = p0 + 16 * pt + l16;
+                for (int f = 0; f < FB; ++f) {
+                    const float* rec = recs + (int64_t)(s0 + f < seg ? s0 + f : seg - 1) * rec_sz;
+                    l2v[f] = rec[(int64_t)N * P];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int n = 16 * nt + 4 * g + i < N ? 16 * nt + 4 * g + i : N - 1;
-                    hacc[k][i] = rec[(int64_t)n * P + col];
+                    for (int k = 0; k < TPW; ++k) {
+                        int pt, nt;
+                        tile_of(k, pt, nt);
+                        const int64_t col = p0 + 16 * pt + l16;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int n = 16 * nt + 4 * g + i < N ? 16 * nt + 4 * g + i : N - 2 + (i & 1);
+                            gv[f][k][i] = rec[(int64_t)n * P + col];
+                        }
+                        // (cos, sin) of pairs n0/2 and n0/2 + 1
+                        const int n0 = 16 * nt + 4 * g < N ? 16 * nt + 4 * g : N - 4;
+                        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rec + (int64_t)N * P + 4 + n0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) cz[f][k][i] = c4[i];
+                    }
+                }
+#pragma unroll
+                for (int f = 0; f < FB; ++f) {
+                    const int s = s0 + f;
+                    if (s == 0) {
+#pragma unroll
+                        for (int k = 0; k < TPW; ++k)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) hacc[k][i] = gv[f][k][i];
+                    } else if (s < seg) {
+                        const float sc = fast_exp2(l2v[f]);
+#pragma unroll
+                        for (int k = 0; k < TPW; ++k) {
+#pragma unroll
+                            for (int ip = 0; ip < 2; ++ip) {
+                                const float cs = cz[f][k][2 * ip], sn = cz[f][k][2 * ip + 1];
+                                const float a0 = sc * hacc[k][2 * ip], a1 = sc * hacc[k][2 * ip + 1];
+                                hacc[k][2 * ip] = cs * a0 - sn * a1 + gv[f][k][2 * ip];
+                                hacc[k][2 * ip + 1] = sn * a0 + cs * a1 + gv[f][k][2 * ip + 1];
+                            }
+                        }
+                    }
                 }
             }
         } else {
@@ -690,77 +758,115 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     };
 
     // ---- D: state update  G <- R(Phi_tot)(e^{Lam_tot} G + Bbar_d^T X) ------
+    // A operand Bbar^T (rows n = 16*nt + l16, K-slots keys 32*kb + 8*g + e)
+    // and B operand X_d[keys][p] = d_key X[key][p] (column p = 16*pt + l16).
+    auto load_bt = [&](const op_t* sB, int nt, int kb, Frag<op_t>& f) {
+        if constexpr (BF) {
+            const bf16* br = sB + (32 * kb + 8 * g + (l16 >> 2)) * LDB + 16 * nt + 4 * (l16 & 3);
+            const bf16x4 lo = lds_read_tr4(br);
+            const bf16x4 hi = lds_read_tr4(br + 4 * LDB);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { f.v[e] = lo[e]; f.v[4 + e] = hi[e]; }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f.set(e, sB[(32 * kb + 8 * g + e) * LDB + 16 * nt + l16]);
+        }
+    };
+    auto load_xd = [&](const op_t* sX, const float* sD, int pt, int kb, Frag<op_t>& f) {
+        float xv[8];
+        if constexpr (BF) {
+            const bf16* xr = sX + (32 * kb + 8 * g + (l16 >> 2)) * LDXR + 16 * pt + 4 * (l16 & 3);
+            const bf16x4 lo = lds_read_tr4(xr);
+            const bf16x4 hi = lds_read_tr4(xr + 4 * LDXR);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { xv[e] = (float)lo[e]; xv[4 + e] = (float)hi[e]; }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[e] = sX[(16 * pt + l16) * LDX + 32 * kb + 8 * g + e];
+        }
+        // d of the 8 / R tokens behind the 8 K-slots (naturally aligned loads)
+        float dv[8 / R];
+        if constexpr (R == 1) {
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(sD + 32 * kb + 8 * g);
+            const f32x4 d1 = *reinterpret_cast<const f32x4*>(sD + 32 * kb + 8 * g + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { dv[e] = d0[e]; dv[4 + e] = d1[e]; }
+        } else if constexpr (R == 2) {
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(sD + 16 * kb + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dv[e] = d0[e];
+        } else {
+            const float2 d0 = *reinterpret_cast<const float2*>(sD + 8 * kb + 2 * g);
+            dv[0] = d0.x;
+            dv[1] = d0.y;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.set(e, xv[e] * dv[e / R]);
+    };
+    auto update_tile = [&](f32x4& hk, int nt, const Frag<op_t>* bfr, const Frag<op_t>* xfr,
+                           float aT, const float* sCSt) {
+        f32x4 acc = hk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] *= aT;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) mma(bfr[kb], xfr[kb], acc);
+        const f32x4 csn = *reinterpret_cast<const f32x4*>(sCSt + 16 * nt + 4 * g);
+#pragma unroll
+        for (int ip = 0; ip < 2; ++ip) {
+            if (16 * nt + 4 * g + 2 * ip < N) {
+                const float cs = csn[2 * ip], sn = csn[2 * ip + 1];
+                const float a0 = acc[2 * ip], a1 = acc[2 * ip + 1];
+                acc[2 * ip] = cs * a0 - sn * a1;
+                acc[2 * ip + 1] = sn * a0 + cs * a1;
+            }
+        }
+        hk = acc;
+    };
     auto phase_D = [&](int s) {
         const op_t* sB = buf_B(s);
         const op_t* sX = buf_X(s);
         const float* sD = buf_F(s) + 3 * Q;
         const float* sCSt = sD + Q;
         const float aT = fast_exp2(sCSt[2 * NPR]);
-        // The d-scaled X operand depends only on (pt, kb) and the Bbar^T
-        // operand only on (nt, kb); each is rebuilt only when its index changes.
-        Frag<op_t> bfr[KB], xfr[KB];
-        int cur_nt = -1, cur_pt = -1;
+        if constexpr (TPW % NTL == 0 && NTILES % NWM == 0) {
+            // A wave owns whole columns of tiles: every Bbar^T operand is
+            // loaded once, up front, and reused for each of its p tiles.
+            constexpr int PPD = TPW / NTL;
+            Frag<op_t> bfr[NTL][KB];
 #pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-            const int tau = wv * TPW + k;
-            if (tau < NTILES) {
-                const int pt = tau / NTL, nt = tau % NTL;
-                if (nt != cur_nt) {
-                    // A operand Bbar^T: rows n = 16*nt + l16, K-slots keys 32*kb + 8*g + e.
+            for (int nt = 0; nt < NTL; ++nt)
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        if constexpr (BF) {
-                            const bf16* br = sB + (32 * kb + 8 * g + (l16 >> 2)) * LDB + 16 * nt
-                                             + 4 * (l16 & 3);
-                            const bf16x4 lo = lds_read_tr4(br);
-                            const bf16x4 hi = lds_read_tr4(br + 4 * LDB);
+                for (int kb = 0; kb < KB; ++kb) load_bt(sB, nt, kb, bfr[nt][kb]);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) { bfr[kb].v[e] = lo[e]; bfr[kb].v[4 + e] = hi[e]; }
-                        } else {
+            for (int pp = 0; pp < PPD; ++pp) {
+                const int pt = wv * PPD + pp;
+                Frag<op_t> xfr[KB];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                bfr[kb].set(e, sB[(32 * kb + 8 * g + e) * LDB + 16 * nt + l16]);
-                        }
+                for (int kb = 0; kb < KB; ++kb) load_xd(sX, sD, pt, kb, xfr[kb]);
+#pragma unroll
+                for (int nt = 0; nt < NTL; ++nt) update_tile(hacc[pp * NTL + nt], nt, bfr[nt], xfr, aT, sCSt);
+            }
+        } else {
+            // Generic layout: operands rebuilt only when their tile index changes.
+            Frag<op_t> bfr[KB], xfr[KB];
+            int cur_nt = -1, cur_pt = -1;
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+                const int tau = wv * TPW + k;
+                if (tau < NTILES) {
+                    const int pt = tau / NTL, nt = tau % NTL;
+                    if (nt != cur_nt) {
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb) load_bt(sB, nt, kb, bfr[kb]);
+                        cur_nt = nt;
                     }
-                    cur_nt = nt;
-                }
-                if (pt != cur_pt) {
-                    // B operand X_d[keys][p] = d_key X[key][p]: column p = 16*pt + l16.
+                    if (pt != cur_pt) {
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        float xv[8];
-                        if constexpr (BF) {
-                            const bf16* xr = sX + (32 * kb + 8 * g + (l16 >> 2)) * LDXR + 16 * pt
-                                             + 4 * (l16 & 3);
-                            const bf16x4 lo = lds_read_tr4(xr);
-                            const bf16x4 hi = lds_read_tr4(xr + 4 * LDXR);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) { xv[e] = (float)lo[e]; xv[4 + e] = (float)hi[e]; }
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) xv[e] = sX[(16 * pt + l16) * LDX + 32 * kb + 8 * g + e];
-                        }
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) xfr[kb].set(e, xv[e] * sD[(32 * kb + 8 * g + e) / R]);
+                        for (int kb = 0; kb < KB; ++kb) load_xd(sX, sD, pt, kb, xfr[kb]);
+                        cur_pt = pt;
                     }
-                    cur_pt = pt;
+                    update_tile(hacc[k], nt, bfr, xfr, aT, sCSt);
                 }
-                f32x4 acc = hacc[k];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= aT;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) mma(bfr[kb], xfr[kb], acc);
-#pragma unroll
-                for (int ip = 0; ip < 2; ++ip) {
-                    const int n = 16 * nt + 4 * g + 2 * ip;
-                    if (n < N) {
-                        const float cs = sCSt[n], sn = sCSt[n + 1];
-                        const float a0 = acc[2 * ip], a1 = acc[2 * ip + 1];
-                        acc[2 * ip] = cs * a0 - sn * a1;
-                        acc[2 * ip + 1] = sn * a0 + cs * a1;
-                    }
-                }
-                hacc[k] = acc;
             }
         }
     };
@@ -797,8 +903,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                         const float phi = (float)(phiseg[e] - twopi * floor(phiseg[e] / twopi));
                         float sn, cs;
                         sincosf(phi, &sn, &cs);
-                        rec[(int64_t)N * P + 1 + 2 * (4 * qd + e)] = cs;
-                        rec[(int64_t)N * P + 2 + 2 * (4 * qd + e)] = sn;
+                        rec[(int64_t)N * P + 4 + 2 * (4 * qd + e)] = cs;
+                        rec[(int64_t)N * P + 5 + 2 * (4 * qd + e)] = sn;
                     }
                 }
             }
@@ -880,52 +986,6 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     }
 }
 
-// Segment records 1..S-2 made inclusive: I_s = R(Phi_s)(2^{l2_s} I_{s-1}) + G_s,
-// I_0 = G_0.  One thread per (b, h, rotation pair, column); its loads for up
-// to 16 records go out together.
-template <class Cf>
-__global__ __launch_bounds__(256) void fold_kernel(const ScanParams p)
-{
-    constexpr int N = Cf::N, NPR = Cf::NPR, FK = 16;
-    const int64_t P = p.P;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)p.nbh * NPR * P) return;
-    const int64_t bh = idx / (NPR * P), rem = idx % (NPR * P);
-    const int m = (int)(rem / P);
-    const int64_t col = rem % P;
-    const int64_t rec_sz = Cf::rec_floats(P);
-    const int nrec = p.nseg - 1;
-    float* recs = p.ws + bh * nrec * rec_sz;
-    const int64_t o0 = (int64_t)(2 * m) * P + col, o1 = o0 + P;
-    float g0 = recs[o0], g1 = recs[o1];
-    for (int s0 = 1; s0 < nrec; s0 += FK) {
-        float a0[FK], a1[FK], l2[FK], cs[FK], sn[FK];
-#pragma unroll
-        for (int f = 0; f < FK; ++f) {
-            const int s = s0 + f < nrec ? s0 + f : nrec - 1;
-            const float* rec = recs + (int64_t)s * rec_sz;
-            a0[f] = rec[o0];
-            a1[f] = rec[o1];
-            l2[f] = rec[(int64_t)N * P];
-            cs[f] = rec[(int64_t)N * P + 1 + 2 * m];
-            sn[f] = rec[(int64_t)N * P + 2 + 2 * m];
-        }
-#pragma unroll
-        for (int f = 0; f < FK; ++f) {
-            const int s = s0 + f;
-            if (s < nrec) {
-                const float sc = fast_exp2(l2[f]);
-                const float x0 = sc * g0, x1 = sc * g1;
-                g0 = cs[f] * x0 - sn[f] * x1 + a0[f];
-                g1 = sn[f] * x0 + cs[f] * x1 + a1[f];
-                float* rec = recs + (int64_t)s * rec_sz;
-                rec[o0] = g0;
-                rec[o1] = g1;
-            }
-        }
-    }
-}
-
 template <class Cf>
 size_t scan_workspace_bytes(int64_t nbh, int64_t P, int nseg)
 {
@@ -955,13 +1015,6 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t stream)
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((scan_kernel<Cf, false>), dim3((unsigned)(per_seg * (p.nseg - 1))),
                            dim3(Cf::NT), Cf::lds_bytes_state, stream, p);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (p.nseg > 2) {
-        const int64_t threads = (int64_t)p.nbh * Cf::NPR * p.P;
-        hipLaunchKernelGGL((fold_kernel<Cf>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                           stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from mamba_selective_ssm_amd import State, m3_scan_fwd, synth
+from mamba_selective_ssm_amd import State, m3_scan_fwd, m3_scan_workspace_bytes, synth
 from helpers import TOL, f64, oracle_scan, random_state, rel_err, say, workload
 
 pytestmark = pytest.mark.gpu
@@ -124,3 +124,24 @@ def test_hand_set_parity_tracking_exact_sign():
     got = y[0, :, 0, 0, :].double().cpu()
     assert torch.all(torch.sign(got) == expect[:, None])
     assert float((got - expect[:, None]).abs().max()) < 1e-3
+
+
+def test_segment_workspace_reused_and_uncleared():
+    """The workspace of a segmented call holds only that call's records: one
+    filled with arbitrary bytes and reused across calls gives the same result
+    every time."""
+    w = workload(2, 1500, 3, 1, 64, 64, io="bf16", dt_mu=-1.0)
+    say("case workspace reuse: %s segments=6" % (w,))
+    inp = synth.make_scan_inputs(w, 71, DEV)
+    args = [inp[k] for k in ("x", "B", "C", "dt", "A", "theta", "lam")]
+    need = m3_scan_workspace_bytes(inp["x"], inp["B"], segments=6)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(3):
+        y, so = m3_scan_fwd(*args, segments=6, workspace=ws)
+        outs.append((y.clone(), so.h.clone()))
+    torch.cuda.synchronize()
+    yr, hr, _, _ = oracle_scan(inp, None)
+    for y, h in outs:
+        assert rel_err(f64(y), yr) <= TOL["bf16"] and rel_err(f64(h), hr) <= TOL["bf16"]
+        assert torch.equal(y, outs[0][0]) and torch.equal(h, outs[0][1])
