@@ -8,13 +8,18 @@
 // endpoint U_{t-1} = B_prev X_prev comes from the state record, which the step
 // then overwrites with (h_t, B_t, X_t).
 //
-// The update is memory-bound: per (b, h) it streams the N x P fp32 state in
-// and out once (2*4*N*P bytes) against about (4R + 10) N P flops.  One
-// workgroup of 256 threads per (b, h); each thread owns rotation-pair rows
-// (2i, 2i+1) x 4 consecutive columns, read and written as float4 so that a
-// wave moves whole 256-byte rows.  All state loads of a thread are issued
-// before any arithmetic.  The rank-R readout is reduced across the threads
-// that share a column group through LDS.
+// The update streams the N x P fp32 state in and out once (8 N P bytes per
+// (b, h)) against about (3R + 5) N P flops: memory-bound.  One wavefront per
+// (b, h), no workgroup barriers:
+//   * lane l owns columns 4*(l % P4) .. +3 (P4 = P/4) of the rotation pairs
+//     i = l / P4 + RG * k (RG = 64 / P4 row groups), so one load instruction
+//     moves 2*RG consecutive state rows -- contiguous, 16 bytes per lane;
+//   * pairs are streamed in batches of PB with the next batch's loads in
+//     flight while the current one is updated and stored;
+//   * B_prev, B and C go to the wave's own LDS slice as [n][r] rows (read as
+//     broadcasts by the lanes of a row group); X_prev, X stay in registers;
+//   * the rank-R readout of each column is reduced across the row groups
+//     with lane shuffles.
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
 
@@ -22,25 +27,67 @@ namespace m3 {
 
 namespace {
 
-constexpr int kDecThreads = 256;
-constexpr int kDecBatch = 4;   // pair-row items per thread held in flight
+constexpr int kDecWaves = 4;   // wavefronts (one (b, h) each) per workgroup, at most
+constexpr int kPB = 1;         // rotation pairs per batch and lane
+
+template <int R> struct RVec;
+template <> struct RVec<1> {
+    float v[1];
+    __device__ __forceinline__ void load(const float* p) { v[0] = p[0]; }
+};
+template <> struct RVec<2> {
+    float v[2];
+    __device__ __forceinline__ void load(const float* p) {
+        const float2 a = *reinterpret_cast<const float2*>(p);
+        v[0] = a.x; v[1] = a.y;
+    }
+};
+template <> struct RVec<4> {
+    float v[4];
+    __device__ __forceinline__ void load(const float* p) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    }
+};
+
+// 8 consecutive io elements copied (16 or 32 bytes).
+__device__ __forceinline__ void copy8(bf16* d, const bf16* s) {
+    *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
+}
+__device__ __forceinline__ void copy8(float* d, const float* s) {
+    reinterpret_cast<uint4*>(d)[0] = reinterpret_cast<const uint4*>(s)[0];
+    reinterpret_cast<uint4*>(d)[1] = reinterpret_cast<const uint4*>(s)[1];
+}
+
+// 4 consecutive io elements as floats.
+__device__ __forceinline__ void load4(float (&d)[4], const bf16* p) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = (float)v[e];
+}
+__device__ __forceinline__ void load4(float (&d)[4], const float* p) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = v[e];
+}
 
 template <typename IO, int R>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams p)
+__global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodeParams p)
 {
     extern __shared__ __attribute__((aligned(16))) float dsm[];
-    const int N = p.N, P = p.P, NPR = N / 2, P4 = P / 4;
-    float* sBp = dsm;                 // [R][N]
-    float* sB = sBp + R * N;          // [R][N]
-    float* sC = sB + R * N;           // [R][N]
-    float* sXp = sC + R * N;          // [R][P]
-    float* sX = sXp + R * P;          // [R][P]
-    float* sCS = sX + R * P;          // [NPR][2]
-    float* sY = sCS + 2 * NPR;        // [kDecThreads][R][4] partial readouts
-
-    const int tid = threadIdx.x;
-    const int64_t bh = blockIdx.x;
+    const int N = p.N, P = p.P, NPR = N / 2;
+    const int P4 = P / 4, RG = 64 / P4;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t bh = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
+    if (bh >= p.nbh) return;   // whole wavefront
     const int64_t h = bh % p.H;
+
+    float* sBp = dsm + (int64_t)wv * (3 * R * N + N);   // this wave's slice: [N][R]
+    float* sB = sBp + R * N;                            // [N][R]
+    float* sC = sB + R * N;                             // [N][R]
+    float* sCS = sC + R * N;                            // [NPR][2] cos, sin
+
     const IO* x = reinterpret_cast<const IO*>(p.x) + bh * R * P;
     const IO* Bt = reinterpret_cast<const IO*>(p.B) + bh * R * N;
     const IO* Ct = reinterpret_cast<const IO*>(p.C) + bh * R * N;
@@ -48,127 +95,167 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
     IO* xp = reinterpret_cast<IO*>(p.xp) + bh * R * P;
     float* hs = p.h + bh * (int64_t)N * P;
 
-    // State loads first (the bulk of the traffic): the first round of a
-    // thread's rows is in flight while the small operands go to LDS.
-    const int items = NPR * P4;
-    float4 hv[kDecBatch][2];
-    const int nrounds = (items + kDecThreads * kDecBatch - 1) / (kDecThreads * kDecBatch);
-    const int cg = tid % P4;   // fixed per thread: kDecThreads is a multiple of P4
-    auto load_round = [&](int rd) {
-        const int base = rd * kDecThreads * kDecBatch;
+    const int cg = lane % P4, rg = lane / P4;
+    const int npl = (NPR - rg + RG - 1) / RG;   // pairs of this lane
+    const int nbat = (NPR / RG + (NPR % RG ? 1 : 0) + kPB - 1) / kPB;   // wave-uniform
+
+    // State batches: rows 2i and 2i+1 of pair i = rg + RG*(kPB*bt + k).
+    f32x4 ha[kPB][2], hb[kPB][2];
+    auto load_batch = [&](f32x4 (&hv)[kPB][2], int bt) {
 #pragma unroll
-        for (int k = 0; k < kDecBatch; ++k) {
-            const int it = base + k * kDecThreads + tid;
-            if (it < items) {
-                const int i = it / P4;
-                const float4* src = reinterpret_cast<const float4*>(hs + (int64_t)(2 * i) * P) + cg;
-                hv[k][0] = src[0];
-                hv[k][1] = src[P4];
-            }
+        for (int k = 0; k < kPB; ++k) {
+            int j = kPB * bt + k;
+            if (j >= npl) j = npl - 1;   // clamped duplicate (never stored)
+            const int i = j >= 0 ? rg + RG * j : 0;
+            const f32x4* src = reinterpret_cast<const f32x4*>(hs + (int64_t)(2 * i) * P) + cg;
+            hv[k][0] = src[0];
+            hv[k][1] = src[P4];
         }
     };
-    if (nrounds > 0) load_round(0);
+    if (npl > 0) load_batch(ha, 0);
 
-    for (int idx = tid; idx < R * N; idx += kDecThreads) {
-        sBp[idx] = to_f32(Bp[idx]);
-        sB[idx] = to_f32(Bt[idx]);
-        sC[idx] = to_f32(Ct[idx]);
+    // Small operands: B_prev, B, C transposed into the wave's LDS slice, the
+    // pair rotations, this lane's columns of X_prev and X.
+    // 8 consecutive elements (one rank row) per lane and load when N % 8 == 0.
+    const int n8 = (N % 8 == 0) ? R * N : 0;
+    for (int idx = 8 * lane; idx < n8; idx += 512) {
+        const int r = idx / N, n = idx % N;
+        float vbp[8], vb[8], vc[8];
+        gload8(vbp, Bp + idx);
+        gload8(vb, Bt + idx);
+        gload8(vc, Ct + idx);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sBp[(n + e) * R + r] = vbp[e];
+            sB[(n + e) * R + r] = vb[e];
+            sC[(n + e) * R + r] = vc[e];
+        }
     }
-    for (int idx = tid; idx < R * P; idx += kDecThreads) {
-        sXp[idx] = to_f32(xp[idx]);
-        sX[idx] = to_f32(x[idx]);
+    for (int idx = n8 + lane; idx < R * N; idx += 64) {
+        const int r = idx / N, n = idx % N;
+        sBp[n * R + r] = to_f32(Bp[idx]);
+        sB[n * R + r] = to_f32(Bt[idx]);
+        sC[n * R + r] = to_f32(Ct[idx]);
     }
     const float d = p.dt[bh], lm = p.lam[bh];
-    for (int i = tid; i < NPR; i += kDecThreads) {
+    for (int i = lane; i < NPR; i += 64) {
         float sn, cs;
         sincosf(d * p.theta[bh * NPR + i], &sn, &cs);
-        sCS[2 * i] = cs;
-        sCS[2 * i + 1] = sn;
+        *reinterpret_cast<float2*>(sCS + 2 * i) = make_float2(cs, sn);
     }
-    __syncthreads();
-
-    // The record's (B, X) has been read into LDS by every thread: overwrite it.
-    for (int idx = tid; idx < R * N; idx += kDecThreads) Bp[idx] = Bt[idx];
-    for (int idx = tid; idx < R * P; idx += kDecThreads) xp[idx] = x[idx];
-
+    float xv[R][4], xpv[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        load4(xv[r], x + r * P + 4 * cg);
+        load4(xpv[r], xp + r * P + 4 * cg);
+    }
     const float alpha = expf(d * p.A[h]);
     const float beta = (1.f - lm) * d * alpha;
     const float gamma = lm * d;
+    // The record's (B, X) are in LDS / registers: overwrite it with this
+    // step's (every element is rewritten by an instruction of this wave that
+    // follows the one that read it).
+    for (int idx = 8 * lane; idx < n8; idx += 512) copy8(Bp + idx, Bt + idx);
+    for (int idx = n8 + lane; idx < R * N; idx += 64) Bp[idx] = Bt[idx];
+    if (rg == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) gstore4(xp + r * P + 4 * cg, f32x4{xv[r][0], xv[r][1], xv[r][2], xv[r][3]});
+    }
+    // The LDS slice is written and read by this wavefront only.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    float yp[R][4];
+    float yacc[R][4];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) yp[r][q] = 0.f;
+        for (int q = 0; q < 4; ++q) yacc[r][q] = 0.f;
 
-    for (int rd = 0; rd < nrounds; ++rd) {
-        const int base = rd * kDecThreads * kDecBatch;
-        if (rd > 0) load_round(rd);
+    auto update_batch = [&](f32x4 (&hv)[kPB][2], int bt) {
 #pragma unroll
-        for (int k = 0; k < kDecBatch; ++k) {
-            const int it = base + k * kDecThreads + tid;
-            if (it < items) {
-                const int i = it / P4;
-                const float cs = sCS[2 * i], sn = sCS[2 * i + 1];
-                float h0[4] = {hv[k][0].x, hv[k][0].y, hv[k][0].z, hv[k][0].w};
-                float h1[4] = {hv[k][1].x, hv[k][1].y, hv[k][1].z, hv[k][1].w};
+        for (int k = 0; k < kPB; ++k) {
+            const int j = kPB * bt + k;
+            if (j < npl) {
+                const int i = rg + RG * j;
+                const float2 csn = *reinterpret_cast<const float2*>(sCS + 2 * i);
+                RVec<R> bp0, bp1, b0, b1, c0, c1;
+                bp0.load(sBp + (2 * i) * R); bp1.load(sBp + (2 * i + 1) * R);
+                b0.load(sB + (2 * i) * R);   b1.load(sB + (2 * i + 1) * R);
+                c0.load(sC + (2 * i) * R);   c1.load(sC + (2 * i + 1) * R);
+                f32x4 n0v, n1v;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int col = 4 * cg + q;
                     float up0 = 0.f, up1 = 0.f, u0 = 0.f, u1 = 0.f;
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        const float xpv = sXp[r * P + col], xv = sX[r * P + col];
-                        up0 += sBp[r * N + 2 * i] * xpv;
-                        up1 += sBp[r * N + 2 * i + 1] * xpv;
-                        u0 += sB[r * N + 2 * i] * xv;
-                        u1 += sB[r * N + 2 * i + 1] * xv;
+                        up0 += bp0.v[r] * xpv[r][q];
+                        up1 += bp1.v[r] * xpv[r][q];
+                        u0 += b0.v[r] * xv[r][q];
+                        u1 += b1.v[r] * xv[r][q];
                     }
                     // alpha R h + beta R U_prev = R (alpha h + beta U_prev)
-                    const float a0 = alpha * h0[q] + beta * up0;
-                    const float a1 = alpha * h1[q] + beta * up1;
-                    const float n0 = cs * a0 - sn * a1 + gamma * u0;
-                    const float n1 = sn * a0 + cs * a1 + gamma * u1;
-                    h0[q] = n0;
-                    h1[q] = n1;
+                    const float a0 = alpha * hv[k][0][q] + beta * up0;
+                    const float a1 = alpha * hv[k][1][q] + beta * up1;
+                    const float n0 = csn.x * a0 - csn.y * a1 + gamma * u0;
+                    const float n1 = csn.y * a0 + csn.x * a1 + gamma * u1;
+                    n0v[q] = n0;
+                    n1v[q] = n1;
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        yp[r][q] += sC[r * N + 2 * i] * n0 + sC[r * N + 2 * i + 1] * n1;
+                    for (int r = 0; r < R; ++r) yacc[r][q] += c0.v[r] * n0 + c1.v[r] * n1;
                 }
-                float4* dst = reinterpret_cast<float4*>(hs + (int64_t)(2 * i) * P) + cg;
-                dst[0] = make_float4(h0[0], h0[1], h0[2], h0[3]);
-                dst[P4] = make_float4(h1[0], h1[1], h1[2], h1[3]);
+                f32x4* dst = reinterpret_cast<f32x4*>(hs + (int64_t)(2 * i) * P) + cg;
+                dst[0] = n0v;
+                dst[P4] = n1v;
             }
+        }
+    };
+
+    // Batches alternate between two register sets; the next one's loads are
+    // in flight while the current one is updated.
+    for (int bt = 0; bt < nbat; bt += 2) {
+        if (bt + 1 < nbat) load_batch(hb, bt + 1);
+        update_batch(ha, bt);
+        if (bt + 1 < nbat) {
+            if (bt + 2 < nbat) load_batch(ha, bt + 2);
+            update_batch(hb, bt + 1);
         }
     }
 
+    // Readout: sum the row groups' partial products of each column.
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int off = P4; off < 64; off <<= 1)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sY[(tid * R + r) * 4 + q] = yp[r][q];
-    __syncthreads();
-    IO* y = reinterpret_cast<IO*>(p.y) + bh * R * P;
-    for (int o = tid; o < R * P; o += kDecThreads) {
-        const int r = o / P, col = o % P, c4 = col / 4, q = col % 4;
-        float s = 0.f;
-        for (int t = c4; t < kDecThreads; t += P4) s += sY[(t * R + r) * 4 + q];
-        y[o] = from_f32<IO>(s);
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) yacc[r][q] += __shfl_xor(yacc[r][q], off, 64);
+    if (rg == 0) {
+        IO* y = reinterpret_cast<IO*>(p.y) + bh * R * P;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            gstore4(y + r * P + 4 * cg, f32x4{yacc[r][0], yacc[r][1], yacc[r][2], yacc[r][3]});
     }
 }
+
+// LDS slice of one wavefront: B_prev, B, C as [N][R] and the pair rotations.
+size_t decode_wave_lds(int N, int R) { return sizeof(float) * (size_t)(3 * R * N + N); }
 
 template <typename IO, int R>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream)
 {
-    const size_t lds = sizeof(float) * (3 * R * p.N + 2 * R * p.P + p.N + kDecThreads * R * 4);
-    // The largest supported shape (N = 1024, P = 256, R = 4) needs 76 KiB;
-    // raise the limit once.
+    // Up to kDecWaves wavefronts per workgroup, as many as fit in LDS (the
+    // largest supported shape, N = 1024 and R = 4, takes 52 KiB per wave).
+    const size_t per_wave = decode_wave_lds(p.N, R);
+    int waves = (int)((160 * 1024) / per_wave);
+    if (waves > kDecWaves) waves = kDecWaves;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&decode_kernel<IO, R>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((decode_kernel<IO, R>), dim3((unsigned)p.nbh), dim3(kDecThreads), lds,
-                       stream, p);
+    const int64_t blocks = (p.nbh + waves - 1) / waves;
+    hipLaunchKernelGGL((decode_kernel<IO, R>), dim3((unsigned)blocks), dim3(64 * waves),
+                       per_wave * waves, stream, p);
     return hipGetLastError();
 }
 
