@@ -96,9 +96,11 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
     const m3::ScanVariant* v = pick_scan(a->io_dtype, N, R, P, a->chunk, a->p_split,
                                          nbh > 0 ? nbh : 1);
     if (v == nullptr) return M3_ERR_UNSUPPORTED;
-    // In-chunk offsets are 32-bit: a chunk's span of every tensor must fit.
+    // In-chunk offsets are 32-bit: a chunk's span of every tensor must fit,
+    // and a token's byte stride must fit the 24-bit multiplier.
     const int64_t wide = (N > P ? N : P) * R;
     if ((int64_t)v->Q * H * wide >= ((int64_t)1 << 31)) return M3_ERR_UNSUPPORTED;
+    if (H * wide * 4 >= ((int64_t)1 << 24)) return M3_ERR_UNSUPPORTED;
     const int p_split = (int)(P / v->PS);
     const int64_t nchunks = (L + v->Q - 1) / v->Q;
     int64_t nseg = a->segments;

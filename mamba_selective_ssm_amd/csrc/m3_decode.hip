@@ -59,6 +59,19 @@ __device__ __forceinline__ void copy8(float* d, const float* s) {
     reinterpret_cast<uint4*>(d)[1] = reinterpret_cast<const uint4*>(s)[1];
 }
 
+// 8 consecutive io elements as floats, streamed (read once).
+__device__ __forceinline__ void gload8_nt(float (&d)[8], const bf16* p) {
+    const bf16x8 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = (float)v[e];
+}
+__device__ __forceinline__ void gload8_nt(float (&d)[8], const float* p) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { d[e] = a[e]; d[4 + e] = b[e]; }
+}
+
 // 4 consecutive io elements as floats.
 __device__ __forceinline__ void load4(float (&d)[4], const bf16* p) {
     const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
@@ -122,8 +135,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
         const int r = idx / N, n = idx % N;
         float vbp[8], vb[8], vc[8];
         gload8(vbp, Bp + idx);
-        gload8(vb, Bt + idx);
-        gload8(vc, Ct + idx);
+        gload8_nt(vb, Bt + idx);
+        gload8_nt(vc, Ct + idx);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             sBp[(n + e) * R + r] = vbp[e];

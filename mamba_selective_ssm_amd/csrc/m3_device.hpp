@@ -157,6 +157,7 @@ template <> struct IoRow8<bf16> {
     bf16x8 v;
     __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
     __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
+    __device__ __forceinline__ void store_raw(bf16* p) const { *reinterpret_cast<bf16x8*>(p) = v; }
 };
 template <> struct IoRow8<float> {
     f32x4 a, b;
@@ -165,6 +166,10 @@ template <> struct IoRow8<float> {
         b = *reinterpret_cast<const f32x4*>(p + 4);
     }
     __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+    __device__ __forceinline__ void store_raw(float* p) const {
+        *reinterpret_cast<f32x4*>(p) = a;
+        *reinterpret_cast<f32x4*>(p + 4) = b;
+    }
 };
 
 // Four operand elements to LDS in one store.

@@ -135,7 +135,9 @@ struct ScanCfg {
     // LDS: two chunk buffers {Bbar, Cbar, X, scalars} and the state stage(s).
     static constexpr size_t sz_B = (size_t)T * LDB * E;
     static constexpr size_t sz_X = BF ? (size_t)T * LDXR * E : (size_t)PS * LDX * E;
-    static constexpr size_t nF = 4 * (size_t)Q + 2 * (size_t)NPR + 4;
+    // chunk scalars: (l2, w)[Q], gamma[Q], d[Q], (cos, sin) of Phi_tot [NPR],
+    // misc[4], u[Q] (w_k relative to its key tile's last token)
+    static constexpr size_t nF = 5 * (size_t)Q + 2 * (size_t)NPR + 4;
     static constexpr size_t sz_H1 = (size_t)PS * LDH * E;
     template <bool FULL> struct Lay {
         static constexpr size_t oB = 0;
@@ -148,9 +150,11 @@ struct ScanCfg {
     };
     static constexpr size_t lds_bytes = Lay<true>::bytes;
     static constexpr size_t lds_bytes_state = Lay<false>::bytes;
-    // Segment record: G [N][P] fp32, Lam_seg*log2(e) (padded to 4 floats),
-    // then (cos, sin) of the segment's total angle per pair.
-    __host__ __device__ static int64_t rec_floats(int64_t P) { return (int64_t)N * P + 4 + 2 * NPR; }
+    // Segment record: G (fp32, NP x P) in the math waves' tile order -- tile
+    // slot (slice, tau) holds 64 lanes x 4 rows, one 16-byte access per lane
+    // -- then Lam_seg*log2(e) (padded to 4 floats), then (cos, sin) of the
+    // segment's total angle per pair.
+    __host__ __device__ static int64_t rec_floats(int64_t P) { return (int64_t)NP * P + 4 + N; }
     static_assert(T % 32 == 0, "Q*R must be a multiple of 32");
     static_assert(R == 1 || R == 2 || R == 4, "rank must be 1, 2 or 4");
     static_assert(PS % 16 == 0, "headdim slice must be a multiple of 16");
@@ -292,6 +296,16 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // masked on use).  Every load is unconditional and issued in the order
     // prep consumes it, so the in-order load counter lets each step wait only
     // for its own data.
+    // Offsets inside a chunk are 32-bit byte offsets (token index times the
+    // per-token byte stride, < 2^24, via the 24-bit multiplier) added to the
+    // wave-uniform chunk base: no 64-bit vector address arithmetic.
+    const unsigned bDT = 4u * (unsigned)sDT, bTH = 4u * (unsigned)sTH;
+    const unsigned bBN = (unsigned)sizeof(io_t) * (unsigned)sBN, bXP = (unsigned)sizeof(io_t) * (unsigned)sXP;
+    const unsigned thq = 16u * (unsigned)qd;                                // theta quad
+    const unsigned bcq = (unsigned)sizeof(io_t) * 8u * (unsigned)qd;       // B/C quad
+    auto at = [](const auto* base, unsigned off) {
+        return reinterpret_cast<decltype(base)>(reinterpret_cast<const char*>(base) + off);
+    };
     PrepStage<Cf> st;
     auto issue_loads = [&](int64_t c) {
         const int64_t t0 = c * Q;
@@ -300,12 +314,12 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
 #pragma unroll
         for (int kk = 0; kk < QPL; ++kk) {
             const int j = lane * QPL + kk;
-            const int jc = j < jl ? j : jl;
-            const int jnc = j + 1 < jn ? j + 1 : jn;
-            st.a_dt[kk] = ldt[jc * sDT];
-            st.a_lm[kk] = llam[jc * sDT];
-            st.a_dn[kk] = ldt[jnc * sDT];
-            st.a_ln[kk] = llam[jnc * sDT];
+            const unsigned jc = (unsigned)(j < jl ? j : jl);
+            const unsigned jnc = (unsigned)(j + 1 < jn ? j + 1 : jn);
+            st.a_dt[kk] = *at(ldt, __umul24(jc, bDT));
+            st.a_lm[kk] = *at(llam, __umul24(jc, bDT));
+            st.a_dn[kk] = *at(ldt, __umul24(jnc, bDT));
+            st.a_ln[kk] = *at(llam, __umul24(jnc, bDT));
         }
 #pragma unroll
         for (int k = 0; k < XI; ++k) {
@@ -313,23 +327,24 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             if (XITEMS % (64 * NWP) != 0 && it >= XITEMS) it = XITEMS - 1;   // duplicate
             int rho, cg;
             xmap(it, rho, cg);
-            const int j = rho / R < jl ? rho / R : jl;
-            st.xq[k].load(lX + j * sXP + (rho % R) * (int)P + 8 * cg);
+            const unsigned j = (unsigned)(rho / R < jl ? rho / R : jl);
+            const unsigned lo = (unsigned)sizeof(io_t) * ((unsigned)(rho % R) * (unsigned)P + 8u * (unsigned)cg);
+            st.xq[k].load(at(lX, __umul24(j, bXP) + lo));
         }
 #pragma unroll
         for (int kk = 0; kk < TPL; ++kk) {
-            const int j = li * TPL + kk < jl ? li * TPL + kk : jl;
-            st.dtv[kk] = ldt[j * sDT];
-            st.thv[kk] = *reinterpret_cast<const f32x4*>(lth + j * sTH + 4 * qd);
+            const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
+            st.dtv[kk] = *at(ldt, __umul24(j, bDT));
+            st.thv[kk] = *reinterpret_cast<const f32x4*>(at(lth, __umul24(j, bTH) + thq));
         }
 #pragma unroll
         for (int kk = 0; kk < TPL; ++kk) {
-            const int j = li * TPL + kk < jl ? li * TPL + kk : jl;
+            const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int off = j * sBN + r * N + 8 * qd;
-                st.bq[kk][r].load(lB + off);
-                if constexpr (FULL) st.cq[kk][r].load(lC + off);
+                const unsigned off = __umul24(j, bBN) + (unsigned)sizeof(io_t) * (unsigned)(r * N) + bcq;
+                st.bq[kk][r].load(at(lB, off));
+                if constexpr (FULL) st.cq[kk][r].load(at(lC, off));
             }
         }
         ldt += Q * sDT; llam += Q * sDT; lth += Q * sTH;
@@ -346,6 +361,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         float* sD = sG + Q;
         float* sCSt = sD + Q;
         float* sMisc = sCSt + 2 * NPR;
+        float* sU = sMisc + 4;
         const int64_t t0 = c * Q;
         const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
 
@@ -370,14 +386,21 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             const float incl = wave_inclusive_sum(run);
             const float excl = incl - run;
             const float l2tot = wave_read_lane(incl, (Q - 1) / QPL) * kLog2e;
+            float l2v[QPL];
+#pragma unroll
+            for (int kk = 0; kk < QPL; ++kk) l2v[kk] = (excl + a[kk]) * kLog2e;
+            // l2 at the last token of each token's 16-row key tile
+            constexpr int TM = 16 / R - 1;
+            const float l2te = __shfl(l2v[QPL - 1], ((lane * QPL) | TM) / QPL, 64);
 #pragma unroll
             for (int kk = 0; kk < QPL; ++kk) {
                 const int j = lane * QPL + kk;
                 if (j < Q) {
-                    const float l2 = (excl + a[kk]) * kLog2e;
+                    const float l2 = l2v[kk];
                     *reinterpret_cast<float2*>(sLW + 2 * j) = make_float2(l2, wt[kk]);
                     sG[j] = gm[kk];
                     sD[j] = wt[kk] * fast_exp2(l2tot - l2);
+                    sU[j] = wt[kk] * fast_exp2(l2te - l2);
                 }
             }
             if (lane == 0) sMisc[0] = l2tot;
@@ -385,6 +408,17 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         }
 
         // ---- A2: X slice into LDS ------------------------------------------
+        if (BF && jl == Q - 1) {
+            // full chunk: the raw bf16 rows go to LDS as loaded
+#pragma unroll
+            for (int k = 0; k < XI; ++k) {
+                int it = ptid + k * 64 * NWP;
+                if (XITEMS % (64 * NWP) != 0 && it >= XITEMS) it = XITEMS - 1;
+                int rho, cg;
+                xmap(it, rho, cg);
+                st.xq[k].store_raw(sX + rho * LDXR + 8 * cg);
+            }
+        } else
 #pragma unroll
         for (int k = 0; k < XI; ++k) {
             int it = ptid + k * 64 * NWP;
@@ -495,6 +529,12 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     f32x4 hacc[TPW];
     io_t* __restrict__ Y0 = reinterpret_cast<io_t*>(p.y) + tok0 * R * P + p0;
 
+    // Float offset of this lane's 4 rows of tile k in a segment record.
+    auto rec_slot = [&](int k) -> int64_t {
+        int tau = wv * TPW + k;
+        if (tau >= NTILES) tau = NTILES - 1;
+        return ((int64_t)(ps * NTILES + tau) * 64 + lane) * 4;
+    };
     auto tile_of = [&](int k, int& pt, int& nt) {
         int tau = wv * TPW + k;
         if (tau >= NTILES) tau = NTILES - 1;
@@ -561,20 +601,17 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
 #pragma unroll
                 for (int f = 0; f < FB; ++f) {
                     const float* rec = recs + (int64_t)(s0 + f < seg ? s0 + f : seg - 1) * rec_sz;
-                    l2v[f] = rec[(int64_t)N * P];
+                    l2v[f] = rec[(int64_t)NP * P];
 #pragma unroll
                     for (int k = 0; k < TPW; ++k) {
                         int pt, nt;
                         tile_of(k, pt, nt);
-                        const int64_t col = p0 + 16 * pt + l16;
+                        const f32x4 g4 = *reinterpret_cast<const f32x4*>(rec + rec_slot(k));
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int n = 16 * nt + 4 * g + i < N ? 16 * nt + 4 * g + i : N - 2 + (i & 1);
-                            gv[f][k][i] = rec[(int64_t)n * P + col];
-                        }
+                        for (int i = 0; i < 4; ++i) gv[f][k][i] = g4[i];
                         // (cos, sin) of pairs n0/2 and n0/2 + 1
                         const int n0 = 16 * nt + 4 * g < N ? 16 * nt + 4 * g : N - 4;
-                        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rec + (int64_t)N * P + 4 + n0);
+                        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rec + (int64_t)NP * P + 4 + n0);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) cz[f][k][i] = c4[i];
                     }
@@ -638,6 +675,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         const op_t* sX = buf_X(s);
         const float* sLW = buf_F(s);
         const float* sG = sLW + 2 * Q;
+        const float* sU = sLW + 4 * Q + 2 * NPR + 4;
         const int64_t t0 = c * Q;
         const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
         io_t* __restrict__ Yc = Y0 + (c - c_begin) * Q * (int64_t)sXP;
@@ -684,9 +722,37 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
 #pragma unroll
                         for (int half = 0; half < 2; ++half) {
                             const int kt = kp + half;
-                            if (kt <= qt) {
-                                // (Lam_k log2 e, w_k) of this lane's 4 / R distinct keys,
-                                // loaded before the products that they scale
+                            if (kt < qt) {
+                                // Key tile wholly before the query token: the mask
+                                // factors as u_k * 2^{l2_q - l2_te} (te = the tile's
+                                // last token, both factors <= 1).
+                                const int jk0 = (16 * kt + 4 * g) / R;
+                                float uk[4 / R];
+                                if constexpr (R == 1) {
+                                    const f32x4 u4 = *reinterpret_cast<const f32x4*>(sU + jk0);
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) uk[e] = u4[e];
+                                } else if constexpr (R == 2) {
+                                    const float2 u2 = *reinterpret_cast<const float2*>(sU + jk0);
+                                    uk[0] = u2.x; uk[1] = u2.y;
+                                } else {
+                                    uk[0] = sU[jk0];
+                                }
+                                const float l2te = sLW[2 * ((16 * kt + 15) / R)];
+                                f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                                for (int s2 = 0; s2 < NP / 32; ++s2) {
+                                    Frag<op_t> a;
+                                    lds_frag8(a, sB + (16 * kt + l16) * LDB + 32 * s2 + 8 * g);
+                                    mma(a, cf[s2], sacc);
+                                }
+                                const float vq = fast_exp2(l2q - l2te);
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) pf.set(4 * half + i, sacc[i] * (uk[i / R] * vq));
+                            } else if (kt == qt) {
+                                // diagonal tile: exact two-band mask per element
+                                // ((Lam_k log2 e, w_k) of this lane's 4 / R distinct keys,
+                                // loaded before the products that they scale)
                                 const int jk0 = (16 * kt + 4 * g) / R;
                                 float kl[8];
                                 if constexpr (R == 1) {
@@ -875,6 +941,10 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // Each role runs its own loop with the same number of barriers: one after
     // the prologue and one per chunk.  (The role test is a scalar branch, so a
     // wave only ever executes its own loop.)
+    // A workgroup in its prologue (first chunk's inputs, state fold) issues
+    // ahead of other workgroups' steady-state loops on the same CU, so that
+    // workgroups that start together also reach their loops together.
+    __builtin_amdgcn_s_setprio(1);
     if (!is_math) {
         // prologue: chunk c_begin into buffer 0, chunk c_begin+1's loads out
         if (c_begin < c_end) {
@@ -883,6 +953,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             if (c_begin + 1 < c_end) issue_loads(c_begin + 1);
         }
         __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
         for (int64_t c = c_begin; c < c_end; ++c) {
             const int s = (int)((c - c_begin) & 1);
             if (c + 1 < c_end) {
@@ -895,7 +966,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             // decay and angle totals of this segment
             float* rec = recs + (int64_t)seg * rec_sz;
             if (ps == 0) {
-                if (pw == 0 && lane == 0) rec[(int64_t)N * P] = (float)l2seg;
+                if (pw == 0 && lane == 0) rec[(int64_t)NP * P] = (float)l2seg;
                 if (arole && li == LQ - 1) {
                     const double twopi = 6.283185307179586;
 #pragma unroll
@@ -903,8 +974,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                         const float phi = (float)(phiseg[e] - twopi * floor(phiseg[e] / twopi));
                         float sn, cs;
                         sincosf(phi, &sn, &cs);
-                        rec[(int64_t)N * P + 4 + 2 * (4 * qd + e)] = cs;
-                        rec[(int64_t)N * P + 5 + 2 * (4 * qd + e)] = sn;
+                        rec[(int64_t)NP * P + 4 + 2 * (4 * qd + e)] = cs;
+                        rec[(int64_t)NP * P + 5 + 2 * (4 * qd + e)] = sn;
                     }
                 }
             }
@@ -914,6 +985,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         initial_state();
         if constexpr (FULL) stage_state(0);
         __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
         for (int64_t c = c_begin; c < c_end; ++c) {
             const int s = (int)((c - c_begin) & 1);
             if constexpr (FULL) {
@@ -930,18 +1002,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             // end state of this segment
             float* rec = recs + (int64_t)seg * rec_sz;
 #pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-                const int tau = wv * TPW + k;
-                if (tau < NTILES) {
-                    const int pt = tau / NTL, nt = tau % NTL;
-                    const int64_t col = p0 + 16 * pt + l16;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int n = 16 * nt + 4 * g + i;
-                        if (n < N) rec[(int64_t)n * P + col] = hacc[k][i];
-                    }
-                }
-            }
+            for (int k = 0; k < TPW; ++k)
+                if (wv * TPW + k < NTILES) *reinterpret_cast<f32x4*>(rec + rec_slot(k)) = hacc[k];
         } else if (last_seg && p.h_out != nullptr) {
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
