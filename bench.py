@@ -127,23 +127,24 @@ def load_traffic(name):
 
 
 def time_launches(fn, steps, warmup, torch):
-    """Run fn() warmup + steps times; returns (total seconds, mean kernel ms)
-    with HIP events recorded on the current stream around every launch."""
+    """Run fn() warmup + steps times; returns (total seconds, mean kernel ms).
+    One HIP event is recorded on the launch stream at every step boundary of
+    the timed region, so each step's duration is the span between the events
+    around it (the step's kernels and the gaps between them)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-        b.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
-    kms = sum(a.elapsed_time(b) for a, b in ev) / max(steps, 1)
+    kms = ev[0].elapsed_time(ev[steps]) / max(steps, 1)
     return total, kms
 
 
@@ -271,7 +272,7 @@ def main(argv=None):
         w = w.with_(chunk=args.chunk)
     progress("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
     r = bench_prefill(w, args.steps, args.warmup, torch, m3, synth)
-    traffic = load_traffic("scan_%s" % w.name)
+    traffic = load_traffic(w.name)
     roof = {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "m3::scan_kernel", "kernel_ms": round(r["kernel_ms"], 5),
@@ -298,7 +299,7 @@ def main(argv=None):
                          "kernel_ms": round(rs["kernel_ms"], 4),
                          "hbm_gbs": round(rs["gbs"], 1),
                          "hbm_frac": round(rs["gbs"] / HBM_PEAK_GBS, 4),
-                         "traffic": load_traffic("scan_%s" % name)}
+                         "traffic": load_traffic(name)}
             torch.cuda.empty_cache()
         wd = synth.WORKLOADS["decode"]
         progress("timing decode: prefill + %d steps" % args.decode_steps)

@@ -311,15 +311,19 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         const int64_t t0 = c * Q;
         const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));  // last valid j
         const int jn = (int)((L - 1 - t0) < Q ? (L - 1 - t0) : Q);              // last valid j+1
+        // per-token dt / lam (at t and t+1) for A0: only the wave that runs A0
+        // (each lane reads its own token's cache line)
+        if (pw == 0) {
 #pragma unroll
-        for (int kk = 0; kk < QPL; ++kk) {
-            const int j = lane * QPL + kk;
-            const unsigned jc = (unsigned)(j < jl ? j : jl);
-            const unsigned jnc = (unsigned)(j + 1 < jn ? j + 1 : jn);
-            st.a_dt[kk] = *at(ldt, __umul24(jc, bDT));
-            st.a_lm[kk] = *at(llam, __umul24(jc, bDT));
-            st.a_dn[kk] = *at(ldt, __umul24(jnc, bDT));
-            st.a_ln[kk] = *at(llam, __umul24(jnc, bDT));
+            for (int kk = 0; kk < QPL; ++kk) {
+                const int j = lane * QPL + kk;
+                const unsigned jc = (unsigned)(j < jl ? j : jl);
+                const unsigned jnc = (unsigned)(j + 1 < jn ? j + 1 : jn);
+                st.a_dt[kk] = *at(ldt, __umul24(jc, bDT));
+                st.a_lm[kk] = *at(llam, __umul24(jc, bDT));
+                st.a_dn[kk] = *at(ldt, __umul24(jnc, bDT));
+                st.a_ln[kk] = *at(llam, __umul24(jnc, bDT));
+            }
         }
 #pragma unroll
         for (int k = 0; k < XI; ++k) {
