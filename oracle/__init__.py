@@ -9,6 +9,16 @@ units); this module only builds it with gcc and marshals numpy arrays.
 Every function takes and returns float64 numpy arrays in the library's layouts:
     x [Bt,L,H,R,P]   Bm, Cm [Bt,L,H,R,N]   dt, lam [Bt,L,H]   theta [Bt,L,H,N/2]
     A [H]            h [Bt,H,N,P]          Bprev [Bt,H,R,N]   xprev [Bt,H,R,P]
+
+Options of ``scan`` and ``decode_step`` (each one a plain transform of the
+inputs, applied before the recurrence, written out below):
+    A per token      A of shape [Bt,L,H] (scan) or [Bt,H] (decode) instead of [H]
+    ngroups=G        Bm, Cm given per head group, [Bt,L,G,R,N]; head h reads
+                     group h // (H/G)
+    phase            "native", "zero", "reverse" or "shuffle" (with ``perm``)
+    premix           dict of pre-mixer parameters: dt and lam are then the raw
+                     projections, and B, C are RMS-normalised with gains and
+                     biases
 """
 from __future__ import annotations
 
@@ -69,22 +79,116 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
-def scan(x, Bm, Cm, dt, A, theta, lam, h0=None, Bprev=None, xprev=None, threads=None):
+# ---------------------------------------------------------------------------
+# Input transforms.  Each returns new float64 arrays; the recurrence itself is
+# the C code's.
+
+def expand_groups(M, H):
+    """B or C given per head group, [..., G, R, N], to per head, [..., H, R, N].
+
+    Head h reads group h // (H // G): contiguous blocks of H/G heads share one
+    B and one C (the grouping of the pages' predecessor Mamba-2, whose heads
+    share parameters in groups; the Mamba-3 pages are silent on grouping)."""
+    M = np.asarray(M, dtype=np.float64)
+    G = M.shape[-3]
+    if G <= 0 or H % G != 0:
+        raise ValueError("oracle: %d heads cannot be split into %d groups" % (H, G))
+    return np.repeat(M, H // G, axis=-3)
+
+
+def phase_transform(theta, mode, perm=None):
+    """Phase interventions of "Understanding Mamba-3 Through Oscillatory
+    Dynamics" (section 5.3 and appendix D.4): the per-pair phase increments are
+    zeroed, reversed in sign, or shuffled across the rotary pairs (the same
+    permutation at every step, so each step keeps its set of increments); the
+    decay is left alone.  ``shuffle``: pair i takes the increment of pair
+    perm[i]."""
+    theta = np.asarray(theta, dtype=np.float64)
+    if mode in (None, "native"):
+        return theta
+    if mode == "zero":
+        return np.zeros_like(theta)
+    if mode == "reverse":
+        return -theta
+    if mode == "shuffle":
+        perm = np.asarray(perm)
+        if sorted(perm.tolist()) != list(range(theta.shape[-1])):
+            raise ValueError("oracle: perm must be a permutation of the pairs")
+        return theta[..., perm]
+    raise ValueError("oracle: unknown phase mode %r" % (mode,))
+
+
+def softplus(z):
+    """log(1 + e^z), evaluated without overflow."""
+    return np.logaddexp(0.0, np.asarray(z, dtype=np.float64))
+
+
+def sigmoid(z):
+    """1 / (1 + e^-z)."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.exp(-np.logaddexp(0.0, -z))
+
+
+def rms_norm(v, weight, eps):
+    """v / sqrt(mean(v^2) + eps) * weight over the last axis (dstate)."""
+    v = np.asarray(v, dtype=np.float64)
+    return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps) * np.asarray(weight, np.float64)
+
+
+def premix_bc(M, weight, bias, eps):
+    """Pre-mixer of B or C: RMS normalisation over dstate with a gain per
+    state channel, then a bias per (head, rank, state channel).  The Towards AI
+    explainer of Mamba-3 (section II) pairs the mixer with QKNorm-style RMSNorm
+    and learnable channel-wise biases on the B and C projections; the pages
+    give no formula, so the plain RMSNorm-then-bias reading is taken.
+    ``M`` is per head, [..., H, R, N]; ``bias`` is [H, R, N]; ``weight`` [N]."""
+    return rms_norm(M, weight, eps) + np.asarray(bias, dtype=np.float64)
+
+
+def premix_dt_lam(dt_raw, lam_raw, dt_bias):
+    """dt = softplus(dt_raw + dt_bias[h]) and lam = sigmoid(lam_raw): the
+    positive step and the trapezoid weight in [0, 1] from raw projections
+    (the workload recipes draw dt and lam through the same two maps)."""
+    return softplus(np.asarray(dt_raw, np.float64) + np.asarray(dt_bias, np.float64)), sigmoid(lam_raw)
+
+
+def _apply_options(Bm, Cm, dt, A, theta, lam, H, ngroups, phase, perm, premix, per_token_shape):
+    if ngroups:
+        Bm = expand_groups(Bm, H)
+        Cm = expand_groups(Cm, H)
+    theta = phase_transform(theta, phase, perm)
+    if premix is not None:
+        eps = float(premix.get("eps", 1e-6))
+        Bm = premix_bc(Bm, premix["B_norm_w"], premix["B_bias"], eps)
+        Cm = premix_bc(Cm, premix["C_norm_w"], premix["C_bias"], eps)
+        dt, lam = premix_dt_lam(dt, lam, premix["dt_bias"])
+    A = np.asarray(A, dtype=np.float64)
+    if A.shape == (H,):
+        A = np.broadcast_to(A, per_token_shape)
+    return Bm, Cm, dt, A, theta, lam
+
+
+def scan(x, Bm, Cm, dt, A, theta, lam, h0=None, Bprev=None, xprev=None, threads=None, *,
+         ngroups=None, phase="native", perm=None, premix=None):
     """Run the recurrence over all L steps.
 
     Returns (y [Bt,L,H,R,P], h_L [Bt,H,N,P], B_L [Bt,H,R,N], x_L [Bt,H,R,P]).
     ``h0``/``Bprev``/``xprev`` may be None (zero state, zero previous endpoint).
+    B_L is the last token's B as the recurrence used it (after the group
+    expansion and the pre-mixer): the previous endpoint a later call needs.
     """
     x = np.asarray(x)
     Bt, L, H, R, P = x.shape
     N = np.asarray(Bm).shape[-1]
+    Bm, Cm, dt, A, theta, lam = _apply_options(Bm, Cm, dt, A, theta, lam, H, ngroups, phase,
+                                               perm, premix, (Bt, L, H))
     x = _arr(x, (Bt, L, H, R, P))
     Bm = _arr(Bm, (Bt, L, H, R, N))
     Cm = _arr(Cm, (Bt, L, H, R, N))
     dt = _arr(dt, (Bt, L, H))
     lam = _arr(lam, (Bt, L, H))
     theta = _arr(theta, (Bt, L, H, N // 2))
-    A = _arr(A, (H,))
+    A = _arr(A, (Bt, L, H))
     h0 = None if h0 is None else _arr(h0, (Bt, H, N, P))
     if (Bprev is None) != (xprev is None):
         raise ValueError("oracle: Bprev and xprev must be given together")
@@ -104,18 +208,24 @@ def scan(x, Bm, Cm, dt, A, theta, lam, h0=None, Bprev=None, xprev=None, threads=
     return y, h_out, Bp_out, xp_out
 
 
-def decode_step(x, Bm, Cm, dt, A, theta, lam, h, Bprev, xprev):
-    """One step on a state record; returns (y_t, h', Bprev', xprev') as new arrays."""
+def decode_step(x, Bm, Cm, dt, A, theta, lam, h, Bprev, xprev, *, ngroups=None,
+                phase="native", perm=None, premix=None):
+    """One step on a state record; returns (y_t, h', Bprev', xprev') as new arrays.
+
+    The record's Bprev is taken as the recurrence uses it (already through the
+    pre-mixer); Bprev' is this step's B after group expansion and pre-mixer."""
     x = np.asarray(x)
     Bt, H, R, P = x.shape
     N = np.asarray(Bm).shape[-1]
+    Bm, Cm, dt, A, theta, lam = _apply_options(Bm, Cm, dt, A, theta, lam, H, ngroups, phase,
+                                               perm, premix, (Bt, H))
     x = _arr(x, (Bt, H, R, P))
     Bm = _arr(Bm, (Bt, H, R, N))
     Cm = _arr(Cm, (Bt, H, R, N))
     dt = _arr(dt, (Bt, H))
     lam = _arr(lam, (Bt, H))
     theta = _arr(theta, (Bt, H, N // 2))
-    A = _arr(A, (H,))
+    A = _arr(A, (Bt, H))
     h = _arr(h, (Bt, H, N, P)).copy()
     Bprev = _arr(Bprev, (Bt, H, R, N)).copy()
     xprev = _arr(xprev, (Bt, H, R, P)).copy()

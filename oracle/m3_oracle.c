@@ -35,9 +35,13 @@
  *     step L+1 is not folded in.  Instead (B_L, X_L) are returned so that a
  *     later scan or decode step can supply it.
  *
+ * The decay rate is taken per token, A_t, as section 1 of the same page
+ * writes it (exp(dt_t A_t)); a rate constant per head is the special case
+ * A_t = A_h, which the Python wrapper passes broadcast.
+ *
  * Layouts (row-major, contiguous, all double):
  *   x      [Bt, L, H, R, P]      Bm, Cm [Bt, L, H, R, N]
- *   dt,lam [Bt, L, H]            theta  [Bt, L, H, N/2]     A [H]
+ *   dt,lam [Bt, L, H]            theta  [Bt, L, H, N/2]     A [Bt, L, H]
  *   h      [Bt, H, N, P]         Bprev  [Bt, H, R, N]       xprev [Bt, H, R, P]
  *   y      [Bt, L, H, R, P]
  */
@@ -124,7 +128,7 @@ static void scan_unit(const scan_job *j, int64_t b, int64_t hh, double *h,
         const double *Bt = j->Bm + bth * R * N;
         const double *Xt = j->x + bth * R * P;
         input_term(Bt, Xt, N, P, R, U);
-        step(h, Uprev, U, j->Cm + bth * R * N, j->dt[bth], j->A[hh],
+        step(h, Uprev, U, j->Cm + bth * R * N, j->dt[bth], j->A[bth],
              j->theta + bth * (N / 2), j->lam[bth], N, P, R, j->y + bth * R * P);
         double *tmp = Uprev; Uprev = U; U = tmp;
     }
@@ -197,7 +201,7 @@ int m3o_scan(int64_t Bt, int64_t L, int64_t H, int64_t P, int64_t N, int64_t R,
 /*
  * One autoregressive step on a resident state record, for every (b, h):
  *   inputs  x_t [Bt,H,R,P], Bm_t, Cm_t [Bt,H,R,N], dt_t, lam_t [Bt,H],
- *           theta_t [Bt,H,N/2], A [H]
+ *           theta_t [Bt,H,N/2], A_t [Bt,H]
  *   in/out  h [Bt,H,N,P], Bprev [Bt,H,R,N], xprev [Bt,H,R,P]
  *   out     y_t [Bt,H,R,P]
  * This is the scan's step applied once, with the previous endpoint taken from
@@ -215,10 +219,9 @@ int m3o_decode_step(int64_t Bt, int64_t H, int64_t P, int64_t N, int64_t R,
     if (!Uprev) return -2;
     double *U = Uprev + N * P;
     for (int64_t u = 0; u < Bt * H; ++u) {
-        const int64_t hh = u % H;
         input_term(Bprev + u * R * N, xprev + u * R * P, N, P, R, Uprev);
         input_term(Bm + u * R * N, x + u * R * P, N, P, R, U);
-        step(h + u * N * P, Uprev, U, Cm + u * R * N, dt[u], A[hh],
+        step(h + u * N * P, Uprev, U, Cm + u * R * N, dt[u], A[u],
              theta + u * (N / 2), lam[u], N, P, R, y + u * R * P);
         memcpy(Bprev + u * R * N, Bm + u * R * N, sizeof(double) * R * N);
         memcpy(xprev + u * R * P, x + u * R * P, sizeof(double) * R * P);

@@ -412,3 +412,179 @@ def test_hand_worked_example():
     np.testing.assert_allclose(hL.ravel(), g["expect_h"], atol=1e-12)
     np.testing.assert_array_equal(BL.ravel(), g["B"][-1])
     np.testing.assert_array_equal(xL.ravel(), [g["x"][-1]])
+
+
+# ===========================================================================
+# Oracle options: per-token decay, head groups, phase interventions and the
+# pre-mixer.  Each is pinned to an independent formulation or a library routine.
+
+# [KO] s1 writes the decay as exp(dt_t A_t).  With lam = 1 and theta = 0 the
+# recurrence is Mamba-2's with a time-varying rate, stepped here directly.
+# B and C come per head group (head h reads group h // (H/G)) to pin the group
+# indexing in the same loop.
+def test_per_token_decay_and_groups_are_mamba2_time_varying():
+    rng = np.random.default_rng(21)
+    Bt, L, H, G, R, P, N = 2, 23, 4, 2, 2, 3, 6
+    x = rng.standard_normal((Bt, L, H, R, P))
+    Bg = rng.standard_normal((Bt, L, G, R, N))
+    Cg = rng.standard_normal((Bt, L, G, R, N))
+    dt = np.log1p(np.exp(rng.standard_normal((Bt, L, H))))
+    At = -np.exp(rng.uniform(-1, 1, size=(Bt, L, H)))
+    theta = rng.uniform(-3, 3, size=(Bt, L, H, N // 2))
+    lam = np.ones((Bt, L, H))
+    y, hL, BL, _ = oracle.scan(x, Bg, Cg, dt, At, theta, lam, ngroups=G, phase="zero")
+    for b in range(Bt):
+        for hh in range(H):
+            g = hh // (H // G)
+            h = np.zeros((N, P))
+            for t in range(L):
+                h = math.exp(dt[b, t, hh] * At[b, t, hh]) * h + dt[b, t, hh] * (Bg[b, t, g].T @ x[b, t, hh])
+                np.testing.assert_allclose(y[b, t, hh], Cg[b, t, g] @ h, rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(hL[b, hh], h, rtol=1e-11, atol=1e-12)
+            np.testing.assert_array_equal(BL[b, hh], Bg[b, L - 1, g])
+
+
+def test_per_token_decay_decode_matches_scan():
+    rng = np.random.default_rng(22)
+    Bt, L, H, G, R, P, N = 2, 9, 4, 2, 2, 3, 6
+    x = rng.standard_normal((Bt, L, H, R, P))
+    Bg = rng.standard_normal((Bt, L, G, R, N))
+    Cg = rng.standard_normal((Bt, L, G, R, N))
+    dt = np.log1p(np.exp(rng.standard_normal((Bt, L, H))))
+    At = -np.exp(rng.uniform(-1, 1, size=(Bt, L, H)))
+    theta = rng.uniform(-3, 3, size=(Bt, L, H, N // 2))
+    lam = rng.uniform(0, 1, size=(Bt, L, H))
+    y, hL, BL, xL = oracle.scan(x, Bg, Cg, dt, At, theta, lam, ngroups=G)
+    z = np.zeros
+    h, Bs, xs = z((Bt, H, N, P)), z((Bt, H, R, N)), z((Bt, H, R, P))
+    for t in range(L):
+        yt, h, Bs, xs = oracle.decode_step(x[:, t], Bg[:, t], Cg[:, t], dt[:, t], At[:, t],
+                                           theta[:, t], lam[:, t], h, Bs, xs, ngroups=G)
+        np.testing.assert_array_equal(yt, y[:, t])
+    np.testing.assert_array_equal(h, hL)
+    np.testing.assert_array_equal(Bs, BL)
+
+
+# [OSC] s5.3: reversing the phase increments.  R(-phi) = D R(phi) D with
+# D = diag(1, -1) on every pair, so the reversed system is the native one
+# conjugated by D: y_rev(B, C) = y(DB, DC) and h_rev = D h(DB, DC).
+def test_reverse_phase_is_reflection_conjugate():
+    rng = np.random.default_rng(23)
+    Bt, L, H, R, P, N = 2, 31, 2, 2, 3, 8
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N)
+    h0 = rng.standard_normal((Bt, H, N, P))
+    Bp = rng.standard_normal((Bt, H, R, N))
+    xp = rng.standard_normal((Bt, H, R, P))
+    d = np.tile([1.0, -1.0], N // 2)
+    y_rev, h_rev, _, _ = oracle.scan(x, Bm, Cm, dt, A, theta, lam, h0=h0, Bprev=Bp, xprev=xp,
+                                     phase="reverse")
+    y_ref, h_ref, _, _ = oracle.scan(x, Bm * d, Cm * d, dt, A, theta, lam, h0=h0 * d[:, None],
+                                     Bprev=Bp * d, xprev=xp)
+    assert rel_err(y_rev, y_ref) < 1e-12
+    assert rel_err(h_rev, h_ref * d[:, None]) < 1e-12
+    # and reversal is not the identity on these inputs
+    y_nat, _, _, _ = oracle.scan(x, Bm, Cm, dt, A, theta, lam, h0=h0, Bprev=Bp, xprev=xp)
+    assert rel_err(y_rev, y_nat) > 1e-2
+
+
+# [OSC] App. D.4: shuffling the increments across rotary pairs.  Relabelling
+# the pairs is a change of basis: pair i driven by theta[perm[i]] is pair
+# perm[i] of a native system whose B, C pairs are moved to position perm[i].
+def test_shuffled_phase_is_pair_relabelling():
+    rng = np.random.default_rng(24)
+    Bt, L, H, R, P, N = 1, 29, 3, 2, 3, 10
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N)
+    perm = rng.permutation(N // 2)
+    y_sh, h_sh, _, _ = oracle.scan(x, Bm, Cm, dt, A, theta, lam, phase="shuffle", perm=perm)
+
+    def move(M):   # pair i of M goes to pair perm[i]
+        out = np.empty_like(M)
+        for i in range(N // 2):
+            out[..., 2 * perm[i]:2 * perm[i] + 2] = M[..., 2 * i:2 * i + 2]
+        return out
+    y_ref, h_ref, _, _ = oracle.scan(x, move(Bm), move(Cm), dt, A, theta, lam)
+    assert rel_err(y_sh, y_ref) < 1e-12
+    h_back = np.empty_like(h_sh)
+    for i in range(N // 2):
+        h_back[:, :, 2 * i:2 * i + 2] = h_ref[:, :, 2 * perm[i]:2 * perm[i] + 2]
+    assert rel_err(h_sh, h_back) < 1e-12
+
+
+# [OSC] s5.3: zeroing the phase leaves a rotation-free trapezoid; the output no
+# longer depends on theta, and equals the complex SSM with theta = 0.
+def test_zero_phase_ignores_theta():
+    rng = np.random.default_rng(25)
+    Bt, L, H, R, P, N = 1, 17, 2, 1, 3, 6
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N)
+    y0, _, _, _ = oracle.scan(x, Bm, Cm, dt, A, theta, lam, phase="zero")
+    y1, _, _, _ = oracle.scan(x, Bm, Cm, dt, A, rng.standard_normal(theta.shape), lam, phase="zero")
+    z = np.zeros
+    yc, _ = complex_form(x, Bm, Cm, dt, A, np.zeros_like(theta), lam, z((Bt, H, N, P)),
+                         z((Bt, H, R, N)), z((Bt, H, R, P)))
+    np.testing.assert_array_equal(y0, y1)
+    assert rel_err(y0, yc) < 1e-12
+
+
+# Pre-mixer ([TAI] s.II: QKNorm-style RMSNorm and channel-wise biases on B and
+# C; dt and lam through softplus and sigmoid).  Each map against torch's own.
+def test_premix_maps_match_torch():
+    import torch
+    rng = np.random.default_rng(26)
+    v = rng.standard_normal((5, 3, 2, 16)) * 3.0
+    w = rng.standard_normal(16)
+    for eps in (1e-6, 0.5):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(v), (16,), torch.from_numpy(w), eps)
+        np.testing.assert_allclose(oracle.rms_norm(v, w, eps), ref.numpy(), rtol=1e-13, atol=1e-14)
+    z = np.concatenate([rng.standard_normal(100) * 10.0, [-800.0, -50.0, 0.0, 50.0, 800.0]])
+    small = z <= 20.0   # torch returns z itself above its threshold of 20
+    np.testing.assert_allclose(oracle.softplus(z[small]),
+                               torch.nn.functional.softplus(torch.from_numpy(z[small])).numpy(),
+                               rtol=1e-13, atol=1e-300)
+    big = z[~small]     # log(1 + e^z) = z + log(1 + e^-z), within e^-z of z
+    assert np.all(np.abs(oracle.softplus(big) - big) <= np.exp(-big) + 1e-15 * big)
+    np.testing.assert_allclose(oracle.sigmoid(z), torch.sigmoid(torch.from_numpy(z)).numpy(),
+                               rtol=1e-13, atol=1e-300)
+
+
+def _premix_params(rng, H, R, N, eps=1e-5):
+    return dict(B_norm_w=rng.uniform(0.5, 1.5, N), C_norm_w=rng.uniform(0.5, 1.5, N),
+                B_bias=0.3 * rng.standard_normal((H, R, N)),
+                C_bias=0.3 * rng.standard_normal((H, R, N)),
+                dt_bias=rng.uniform(-2.0, 0.0, H), eps=eps)
+
+
+# With the pre-mixer the scan consumes RMSNorm(B)*w + b (torch's rms_norm),
+# softplus(dt + dt_bias) and sigmoid(lam).  RMS normalisation also makes the
+# output invariant to a positive rescaling of each B or C row.
+def test_premix_scan_consumes_torch_maps():
+    import torch
+    rng = np.random.default_rng(27)
+    Bt, L, H, G, R, P, N = 2, 13, 4, 2, 2, 3, 8
+    x = rng.standard_normal((Bt, L, H, R, P))
+    Bg = rng.standard_normal((Bt, L, G, R, N))
+    Cg = rng.standard_normal((Bt, L, G, R, N))
+    dt_raw = rng.standard_normal((Bt, L, H))
+    lam_raw = rng.standard_normal((Bt, L, H))
+    A = -np.exp(rng.uniform(-1, 1, size=H))
+    theta = rng.uniform(-3, 3, size=(Bt, L, H, N // 2))
+    pm = _premix_params(rng, H, R, N)
+    y, hL, BL, _ = oracle.scan(x, Bg, Cg, dt_raw, A, theta, lam_raw, ngroups=G, premix=pm)
+
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    Bh = np.repeat(Bg, H // G, axis=2)
+    Ch = np.repeat(Cg, H // G, axis=2)
+    Bn = (torch.nn.functional.rms_norm(T(Bh), (N,), T(pm["B_norm_w"]), pm["eps"]) + T(pm["B_bias"])).numpy()
+    Cn = (torch.nn.functional.rms_norm(T(Ch), (N,), T(pm["C_norm_w"]), pm["eps"]) + T(pm["C_bias"])).numpy()
+    dt = torch.nn.functional.softplus(T(dt_raw) + T(pm["dt_bias"])).numpy()
+    lam = torch.sigmoid(T(lam_raw)).numpy()
+    y_ref, h_ref, B_ref, _ = oracle.scan(x, Bn, Cn, dt, A, theta, lam)
+    assert rel_err(y, y_ref) < 1e-12
+    assert rel_err(hL, h_ref) < 1e-12
+    assert rel_err(BL, B_ref) < 1e-13
+
+    scale = rng.uniform(0.2, 5.0, size=(Bt, L, G, R, 1))
+    pm0 = dict(pm, eps=0.0)
+    ya, _, _, _ = oracle.scan(x, Bg, Cg, dt_raw, A, theta, lam_raw, ngroups=G, premix=pm0)
+    yb, _, _, _ = oracle.scan(x, Bg * scale, Cg / scale, dt_raw, A, theta, lam_raw, ngroups=G,
+                              premix=pm0)
+    assert rel_err(yb, ya) < 1e-12
