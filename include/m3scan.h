@@ -50,6 +50,26 @@
  * Calls are reentrant; the library holds no global mutable state besides a
  * thread-local record of the last HIP error.
  *
+ * Options (m3_options, zero-initialised = none of them; both entry points):
+ *   - per-token decay rate A_t: the Mamba-3 summary on b-lab.team, section 1,
+ *     writes the decay as exp(dt_t A_t); A is then [batch, seqlen, nheads]
+ *     (decode: [batch, nheads]) instead of one value per head;
+ *   - head groups: B and C given once per group of nheads/ngroups consecutive
+ *     heads, [batch, seqlen, ngroups, rank, dstate] (decode: [batch, ngroups,
+ *     rank, dstate]); head h reads group h / (nheads / ngroups);
+ *   - phase interventions of "Understanding Mamba-3 Through Oscillatory
+ *     Dynamics" (section 5.3, appendix D.4): the phase increments dt_t theta_t
+ *     are zeroed, negated, or shuffled across the rotary pairs (pair i uses
+ *     theta[..., perm[i]] at every step); the decay is untouched;
+ *   - pre-mixer: the Towards AI explainer of Mamba-3 (section II) pairs the
+ *     mixer with QKNorm-style RMSNorm and channel-wise biases on B and C.
+ *     With premix set, dt and lam are raw projections and the mixer uses
+ *         dt  = softplus(dt_raw + dt_bias[h]),   lam = sigmoid(lam_raw),
+ *         B'  = B / sqrt(mean_n(B^2) + eps) * B_norm_w[n] + B_bias[h, r, n]
+ *     (and C' alike), the mean over the dstate entries of one (token, head,
+ *     rank) row.  The state record's B_prev holds B' (what the recurrence
+ *     consumed), so a record can be continued with or without the pre-mixer.
+ *
  * Errors.  Every entry point validates all arguments before making any HIP
  * call and returns M3_OK or one of the negative m3_status codes below.  On an
  * error nothing has been enqueued.  NaN or Inf inputs are not errors: they
@@ -66,12 +86,19 @@
 extern "C" {
 #endif
 
-#define M3_ABI_VERSION 1
+#define M3_ABI_VERSION 2
 
 typedef enum {
     M3_F32 = 0,
     M3_BF16 = 1
 } m3_dtype;
+
+typedef enum {
+    M3_PHASE_NATIVE = 0,   /* theta as given */
+    M3_PHASE_ZERO = 1,     /* no rotation; theta is not read and may be NULL */
+    M3_PHASE_REVERSE = 2,  /* theta negated */
+    M3_PHASE_SHUFFLE = 3   /* pair i uses theta[..., phase_perm[i]] */
+} m3_phase_mode;
 
 typedef enum {
     M3_OK = 0,
@@ -82,8 +109,34 @@ typedef enum {
     M3_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
     M3_ERR_WORKSPACE = -6,   /* workspace missing or smaller than m3_scan_workspace_bytes */
     M3_ERR_ALIAS = -7,       /* an output overlaps an input it must not overlap */
-    M3_ERR_HIP = -8          /* a HIP call failed; see m3_last_hip_error() */
+    M3_ERR_HIP = -8,         /* a HIP call failed; see m3_last_hip_error() */
+    M3_ERR_OPTION = -9       /* an m3_options field is out of range */
 } m3_status;
+
+/*
+ * Options shared by m3_scan_fwd and m3_decode_step (all zero = the plain
+ * mixer).  Pointers are device pointers owned by the caller.
+ *   ngroups      0 = one B and C per head; else a divisor of nheads
+ *   A_per_token  0: A is [nheads]; 1: A is [batch, seqlen, nheads] in a scan,
+ *                [batch, nheads] in a decode step
+ *   phase_mode   an m3_phase_mode; phase_perm ([dstate/2] int32) is required
+ *                for M3_PHASE_SHUFFLE and must hold each of 0 .. dstate/2-1
+ *                once (entries are clamped into that range, never checked)
+ *   premix       1 = apply the pre-mixer; B_norm_w, C_norm_w [dstate] (NULL =
+ *                all ones), B_bias, C_bias [nheads, rank, dstate] and dt_bias
+ *                [nheads] (NULL = zeros), norm_eps >= 0
+ */
+typedef struct {
+    int64_t ngroups;
+    int32_t A_per_token;
+    int32_t phase_mode;
+    const int32_t *phase_perm;
+    int32_t premix;
+    float norm_eps;
+    const float *B_norm_w, *C_norm_w;
+    const float *B_bias, *C_bias;
+    const float *dt_bias;
+} m3_options;
 
 /*
  * Arguments of m3_scan_fwd.
@@ -123,6 +176,7 @@ typedef struct {
     void *B_prev_out, *x_prev_out;
     void *workspace;
     size_t workspace_bytes;
+    m3_options opt;
 } m3_scan_args;
 
 /*
@@ -143,6 +197,7 @@ typedef struct {
     float *h;
     void *B_prev, *x_prev;
     void *y;
+    m3_options opt;
 } m3_decode_args;
 
 /* Chunked prefill: y and (optionally) the state record after the last token.

@@ -11,6 +11,13 @@ Layouts (contiguous):
     x, y [Bt, L, H, R, P]   B, C [Bt, L, H, R, N]   dt, lam [Bt, L, H]
     theta [Bt, L, H, N/2]   A [H]
     state: h [Bt, H, N, P] float32, B_prev [Bt, H, R, N], x_prev [Bt, H, R, P]
+
+Options (the m3_options of the C ABI), keyword arguments of the scan and
+decode calls:
+    A of shape [Bt, L, H] (decode: [Bt, H])  per-token decay rate
+    ngroups=G      B, C given per head group: [Bt, L, G, R, N] (decode [Bt, G, R, N])
+    phase          "native" | "zero" | "reverse" | "shuffle"; perm: int32 [N/2]
+    premix         a Premix: dt and lam are raw, B and C RMS-normalised
 """
 from __future__ import annotations
 
@@ -26,9 +33,30 @@ LIB_PATH = os.path.join(_HERE, "libm3scan.so")
 M3_F32, M3_BF16 = 0, 1
 _STATUS = {0: "M3_OK", -1: "M3_ERR_NULL", -2: "M3_ERR_SHAPE", -3: "M3_ERR_UNSUPPORTED",
            -4: "M3_ERR_DTYPE", -5: "M3_ERR_ALIGN", -6: "M3_ERR_WORKSPACE", -7: "M3_ERR_ALIAS",
-           -8: "M3_ERR_HIP"}
+           -8: "M3_ERR_HIP", -9: "M3_ERR_OPTION"}
+PHASE_MODES = {"native": 0, "zero": 1, "reverse": 2, "shuffle": 3}
 
 _vp = ctypes.c_void_p
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("ngroups", ctypes.c_int64), ("A_per_token", ctypes.c_int32),
+                ("phase_mode", ctypes.c_int32), ("phase_perm", _vp),
+                ("premix", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("B_norm_w", _vp), ("C_norm_w", _vp), ("B_bias", _vp), ("C_bias", _vp),
+                ("dt_bias", _vp)]
+
+
+class Premix(NamedTuple):
+    """Pre-mixer parameters (float32 device tensors; None = ones / zeros).
+    dt = softplus(dt_raw + dt_bias[h]), lam = sigmoid(lam_raw),
+    B' = B / sqrt(mean_n B^2 + eps) * B_norm_w[n] + B_bias[h, r, n] (C alike)."""
+    B_norm_w: Optional[torch.Tensor] = None   # [N]
+    C_norm_w: Optional[torch.Tensor] = None   # [N]
+    B_bias: Optional[torch.Tensor] = None     # [H, R, N]
+    C_bias: Optional[torch.Tensor] = None     # [H, R, N]
+    dt_bias: Optional[torch.Tensor] = None    # [H]
+    eps: float = 1e-5
 
 
 class ScanArgs(ctypes.Structure):
@@ -41,7 +69,8 @@ class ScanArgs(ctypes.Structure):
                 ("dt", _vp), ("A", _vp), ("theta", _vp), ("lam", _vp),
                 ("h_in", _vp), ("B_prev_in", _vp), ("x_prev_in", _vp),
                 ("y", _vp), ("h_out", _vp), ("B_prev_out", _vp), ("x_prev_out", _vp),
-                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("opt", Options)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -51,7 +80,8 @@ class DecodeArgs(ctypes.Structure):
                 ("reserved", ctypes.c_int32),
                 ("x", _vp), ("B", _vp), ("C", _vp),
                 ("dt", _vp), ("A", _vp), ("theta", _vp), ("lam", _vp),
-                ("h", _vp), ("B_prev", _vp), ("x_prev", _vp), ("y", _vp)]
+                ("h", _vp), ("B_prev", _vp), ("x_prev", _vp), ("y", _vp),
+                ("opt", Options)]
 
 
 class M3Error(RuntimeError):
@@ -146,24 +176,52 @@ def _check(t: torch.Tensor, name: str, shape, dtype):
         raise ValueError("%s must be a device tensor" % name)
 
 
+def _options(H, N, R, A_per_token, ngroups, phase, perm, premix, device):
+    """m3_options from the keyword arguments (plus the tensors to keep alive)."""
+    mode = PHASE_MODES[phase] if isinstance(phase, str) else int(phase)
+    o = Options(ngroups=int(ngroups or 0), A_per_token=int(bool(A_per_token)), phase_mode=mode)
+    keep = []
+    if mode == PHASE_MODES["shuffle"]:
+        if perm is None:
+            raise ValueError("phase='shuffle' needs perm")
+        _check(perm, "perm", (N // 2,), torch.int32)
+        o.phase_perm = perm.data_ptr()
+        keep.append(perm)
+    if premix is not None:
+        o.premix = 1
+        o.norm_eps = float(premix.eps)
+        for name, shape in (("B_norm_w", (N,)), ("C_norm_w", (N,)), ("B_bias", (H, R, N)),
+                            ("C_bias", (H, R, N)), ("dt_bias", (H,))):
+            t = getattr(premix, name)
+            if t is not None:
+                _check(t, "premix." + name, shape, torch.float32)
+                setattr(o, name, t.data_ptr())
+                keep.append(t)
+    return o, keep
+
+
 def _stream_handle(stream) -> int:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
 
 
 def _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, return_state,
-                  y, state_out, workspace):
+                  y, state_out, workspace, ngroups=0, phase="native", perm=None, premix=None):
     lib = load_library()
     Bt, L, H, R, P = x.shape
     N = B.shape[-1]
+    G = int(ngroups) if ngroups else H
     io = _io_code(x.dtype)
     _check(x, "x", (Bt, L, H, R, P), x.dtype)
-    _check(B, "B", (Bt, L, H, R, N), x.dtype)
-    _check(C, "C", (Bt, L, H, R, N), x.dtype)
+    _check(B, "B", (Bt, L, G, R, N), x.dtype)
+    _check(C, "C", (Bt, L, G, R, N), x.dtype)
     _check(dt, "dt", (Bt, L, H), torch.float32)
     _check(lam, "lam", (Bt, L, H), torch.float32)
-    _check(theta, "theta", (Bt, L, H, N // 2), torch.float32)
-    _check(A, "A", (H,), torch.float32)
+    if theta is not None or phase != "zero":
+        _check(theta, "theta", (Bt, L, H, N // 2), torch.float32)
+    a_tok = A.dim() == 3
+    _check(A, "A", (Bt, L, H) if a_tok else (H,), torch.float32)
+    opt, keep = _options(H, N, R, a_tok, ngroups, phase, perm, premix, x.device)
     if y is None:
         y = torch.empty_like(x)
     _check(y, "y", (Bt, L, H, R, P), x.dtype)
@@ -186,7 +244,8 @@ def _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, r
                  h_out=_ptr(state_out.h) if state_out else None,
                  B_prev_out=_ptr(state_out.B_prev) if state_out else None,
                  x_prev_out=_ptr(state_out.x_prev) if state_out else None,
-                 workspace=None, workspace_bytes=0)
+                 workspace=None, workspace_bytes=0, opt=opt)
+    a._keep = keep
     need = lib.m3_scan_workspace_bytes(ctypes.byref(a))
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -200,10 +259,12 @@ def m3_scan_fwd(x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
                 chunk: int = 0, p_split: int = 0, segments: int = 0,
                 return_state: bool = True, y: Optional[torch.Tensor] = None,
                 state_out: Optional[State] = None, workspace: Optional[torch.Tensor] = None,
-                stream=None):
+                ngroups: int = 0, phase="native", perm: Optional[torch.Tensor] = None,
+                premix: Optional[Premix] = None, stream=None):
     """Chunked prefill.  Returns (y, State after the last token or None)."""
     a, y, state_out, _ = _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split,
-                                       segments, return_state, y, state_out, workspace)
+                                       segments, return_state, y, state_out, workspace,
+                                       ngroups, phase, perm, premix)
     st = load_library().m3_scan_fwd(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_fwd")
@@ -218,11 +279,12 @@ class ScanCall:
     def __init__(self, x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
                  chunk: int = 0, p_split: int = 0, segments: int = 0, return_state: bool = True,
                  y: Optional[torch.Tensor] = None, state_out: Optional[State] = None,
-                 workspace: Optional[torch.Tensor] = None):
+                 workspace: Optional[torch.Tensor] = None, ngroups: int = 0, phase="native",
+                 perm: Optional[torch.Tensor] = None, premix: Optional[Premix] = None):
         self._keep = (x, B, C, dt, A, theta, lam, state)
         self.args, self.y, self.state_out, self.workspace = _prepare_scan(
             x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, return_state, y,
-            state_out, workspace)
+            state_out, workspace, ngroups, phase, perm, premix)
         self._ref = ctypes.byref(self.args)
         self._fn = load_library().m3_scan_fwd
 
@@ -240,17 +302,22 @@ def m3_scan_workspace_bytes(x, B, *, chunk=0, p_split=0, segments=0) -> int:
     return int(load_library().m3_scan_workspace_bytes(ctypes.byref(a)))
 
 
-def _prepare_decode(x, B, C, dt, A, theta, lam, state, y):
+def _prepare_decode(x, B, C, dt, A, theta, lam, state, y, ngroups=0, phase="native", perm=None,
+                    premix=None):
     Bt, H, R, P = x.shape
     N = B.shape[-1]
+    G = int(ngroups) if ngroups else H
     io = _io_code(x.dtype)
     _check(x, "x", (Bt, H, R, P), x.dtype)
-    _check(B, "B", (Bt, H, R, N), x.dtype)
-    _check(C, "C", (Bt, H, R, N), x.dtype)
+    _check(B, "B", (Bt, G, R, N), x.dtype)
+    _check(C, "C", (Bt, G, R, N), x.dtype)
     _check(dt, "dt", (Bt, H), torch.float32)
     _check(lam, "lam", (Bt, H), torch.float32)
-    _check(theta, "theta", (Bt, H, N // 2), torch.float32)
-    _check(A, "A", (H,), torch.float32)
+    if theta is not None or phase != "zero":
+        _check(theta, "theta", (Bt, H, N // 2), torch.float32)
+    a_tok = A.dim() == 2
+    _check(A, "A", (Bt, H) if a_tok else (H,), torch.float32)
+    opt, keep = _options(H, N, R, a_tok, ngroups, phase, perm, premix, x.device)
     _check(state.h, "state.h", (Bt, H, N, P), torch.float32)
     _check(state.B_prev, "state.B_prev", (Bt, H, R, N), x.dtype)
     _check(state.x_prev, "state.x_prev", (Bt, H, R, P), x.dtype)
@@ -260,14 +327,17 @@ def _prepare_decode(x, B, C, dt, A, theta, lam, state, y):
     a = DecodeArgs(batch=Bt, nheads=H, headdim=P, dstate=N, rank=R, io_dtype=io,
                    x=_ptr(x), B=_ptr(B), C=_ptr(C), dt=_ptr(dt), A=_ptr(A),
                    theta=_ptr(theta), lam=_ptr(lam), h=_ptr(state.h),
-                   B_prev=_ptr(state.B_prev), x_prev=_ptr(state.x_prev), y=_ptr(y))
+                   B_prev=_ptr(state.B_prev), x_prev=_ptr(state.x_prev), y=_ptr(y), opt=opt)
+    a._keep = keep
     return a, y
 
 
 def m3_decode_step(x, B, C, dt, A, theta, lam, state: State, *,
-                   y: Optional[torch.Tensor] = None, stream=None):
+                   y: Optional[torch.Tensor] = None, ngroups: int = 0, phase="native",
+                   perm: Optional[torch.Tensor] = None, premix: Optional[Premix] = None,
+                   stream=None):
     """One token for every (batch, head); ``state`` is updated in place.  Returns y_t."""
-    a, y = _prepare_decode(x, B, C, dt, A, theta, lam, state, y)
+    a, y = _prepare_decode(x, B, C, dt, A, theta, lam, state, y, ngroups, phase, perm, premix)
     st = load_library().m3_decode_step(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_decode_step")
@@ -279,9 +349,11 @@ class DecodeCall:
     and y); calling it issues that step on the current stream."""
 
     def __init__(self, x, B, C, dt, A, theta, lam, state: State, *,
-                 y: Optional[torch.Tensor] = None):
+                 y: Optional[torch.Tensor] = None, ngroups: int = 0, phase="native",
+                 perm: Optional[torch.Tensor] = None, premix: Optional[Premix] = None):
         self._keep = (x, B, C, dt, A, theta, lam, state)
-        self.args, self.y = _prepare_decode(x, B, C, dt, A, theta, lam, state, y)
+        self.args, self.y = _prepare_decode(x, B, C, dt, A, theta, lam, state, y, ngroups, phase,
+                                            perm, premix)
         self._ref = ctypes.byref(self.args)
         self._fn = load_library().m3_decode_step
 

@@ -75,6 +75,47 @@ m3_status hip_status(hipError_t e)
     return M3_ERR_HIP;
 }
 
+// Options common to both entry points: ranges, required pointers, alignment.
+// Fills the kernel-side fields; `ntok` is the number of (batch, token) rows
+// the per-token decay covers (batch * seqlen, or batch for a decode step).
+m3_status check_options(const m3_options& o, int64_t H, int64_t N, int64_t R, int64_t ntok,
+                        m3::OptParams* k)
+{
+    if (o.ngroups < 0 || (o.ngroups > 0 && H > 0 && H % o.ngroups != 0)) return M3_ERR_OPTION;
+    if (o.A_per_token != 0 && o.A_per_token != 1) return M3_ERR_OPTION;
+    if (o.phase_mode < M3_PHASE_NATIVE || o.phase_mode > M3_PHASE_SHUFFLE) return M3_ERR_OPTION;
+    if (o.premix != 0 && o.premix != 1) return M3_ERR_OPTION;
+    if (o.premix && !(o.norm_eps >= 0.f && o.norm_eps < 3.0e38f)) return M3_ERR_OPTION;
+    if (o.phase_mode == M3_PHASE_SHUFFLE && o.phase_perm == nullptr) return M3_ERR_NULL;
+    const void* ptrs[] = {o.phase_perm, o.B_norm_w, o.C_norm_w, o.B_bias, o.C_bias, o.dt_bias};
+    for (const void* q : ptrs)
+        if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
+    (void)N; (void)R; (void)ntok;
+    k->groups = o.ngroups > 0 ? o.ngroups : H;
+    k->a_tok = o.A_per_token;
+    k->phase = o.phase_mode;
+    k->perm = o.phase_mode == M3_PHASE_SHUFFLE ? o.phase_perm : nullptr;
+    k->premix = o.premix;
+    k->eps = o.norm_eps;
+    k->Bw = o.premix ? o.B_norm_w : nullptr;
+    k->Cw = o.premix ? o.C_norm_w : nullptr;
+    k->Bb = o.premix ? o.B_bias : nullptr;
+    k->Cb = o.premix ? o.C_bias : nullptr;
+    k->dtb = o.premix ? o.dt_bias : nullptr;
+    return M3_OK;
+}
+
+// Byte ranges of the option arrays (inputs of the call).
+void option_ranges(const m3_options& o, int64_t H, int64_t N, int64_t R, Range* out)
+{
+    out[0] = range_of(o.phase_mode == M3_PHASE_SHUFFLE ? o.phase_perm : nullptr, (N / 2) * 4);
+    out[1] = range_of(o.premix ? o.B_norm_w : nullptr, N * 4);
+    out[2] = range_of(o.premix ? o.C_norm_w : nullptr, N * 4);
+    out[3] = range_of(o.premix ? o.B_bias : nullptr, H * R * N * 4);
+    out[4] = range_of(o.premix ? o.C_bias : nullptr, H * R * N * 4);
+    out[5] = range_of(o.premix ? o.dt_bias : nullptr, H * 4);
+}
+
 struct ScanPlan {
     const m3::ScanVariant* v;
     int p_split, nseg, seg_chunks;
@@ -146,6 +187,7 @@ const char* m3_status_string(m3_status s)
     case M3_ERR_WORKSPACE: return "workspace missing or too small";
     case M3_ERR_ALIAS: return "output overlaps an input";
     case M3_ERR_HIP: return "HIP call failed";
+    case M3_ERR_OPTION: return "option out of range (groups, phase mode, premix, eps)";
     }
     return "unknown status";
 }
@@ -180,15 +222,20 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     const int64_t nbh = Bt * H;
     if (nbh == 0) return M3_OK;
 
+    m3::OptParams op;
+    const m3_status os = check_options(a->opt, H, N, R, Bt * L, &op);
+    if (os != M3_OK) return os;
     const bool st_in = a->h_in || a->B_prev_in || a->x_prev_in;
     const bool st_out = a->h_out || a->B_prev_out || a->x_prev_out;
     if (st_in && !(a->h_in && a->B_prev_in && a->x_prev_in)) return M3_ERR_NULL;
     if (st_out && !(a->h_out && a->B_prev_out && a->x_prev_out)) return M3_ERR_NULL;
-    if (a->A == nullptr) return M3_ERR_NULL;
-    if (L > 0 && (!a->x || !a->B || !a->C || !a->dt || !a->theta || !a->lam || !a->y))
+    if (a->A == nullptr && !(a->opt.A_per_token && L == 0)) return M3_ERR_NULL;
+    const bool need_theta = a->opt.phase_mode != M3_PHASE_ZERO;
+    if (L > 0 && (!a->x || !a->B || !a->C || !a->dt || (need_theta && !a->theta) || !a->lam || !a->y))
         return M3_ERR_NULL;
+    const void* theta = need_theta ? a->theta : nullptr;
 
-    const void* ptrs[] = {a->x, a->B, a->C, a->dt, a->A, a->theta, a->lam, a->h_in,
+    const void* ptrs[] = {a->x, a->B, a->C, a->dt, a->A, theta, a->lam, a->h_in,
                           a->B_prev_in, a->x_prev_in, a->y, a->h_out, a->B_prev_out,
                           a->x_prev_out};
     for (const void* q : ptrs)
@@ -196,13 +243,16 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
 
     const int e = io_size(a->io_dtype);
     const int64_t tok = Bt * L * H;
-    const Range in[] = {
-        range_of(a->x, tok * R * P * e),         range_of(a->B, tok * R * N * e),
-        range_of(a->C, tok * R * N * e),         range_of(a->dt, tok * 4),
-        range_of(a->A, H * 4),                   range_of(a->theta, tok * (N / 2) * 4),
+    const int64_t tokg = Bt * L * op.groups;
+    Range in[16] = {
+        range_of(a->x, tok * R * P * e),         range_of(a->B, tokg * R * N * e),
+        range_of(a->C, tokg * R * N * e),        range_of(a->dt, tok * 4),
+        range_of(a->A, (a->opt.A_per_token ? tok : H) * 4),
+        range_of(theta, tok * (N / 2) * 4),
         range_of(a->lam, tok * 4),               range_of(a->h_in, nbh * N * P * 4),
         range_of(a->B_prev_in, nbh * R * N * e), range_of(a->x_prev_in, nbh * R * P * e),
     };
+    option_ranges(a->opt, H, N, R, in + 10);
     const Range out[] = {
         range_of(a->y, tok * R * P * e),         range_of(a->h_out, nbh * N * P * 4),
         range_of(a->B_prev_out, nbh * R * N * e), range_of(a->x_prev_out, nbh * R * P * e),
@@ -228,6 +278,8 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     p.h_in = a->h_in; p.Bp_in = a->B_prev_in; p.xp_in = a->x_prev_in;
     p.y = a->y; p.h_out = a->h_out; p.Bp_out = a->B_prev_out; p.xp_out = a->x_prev_out;
     p.ws = static_cast<float*>(a->workspace);
+    p.opt = op;
+    p.theta = static_cast<const float*>(theta);
     p.batch = Bt; p.L = L; p.H = H; p.P = P;
     p.p_split = plan.p_split;
     p.nbh = (int)nbh;
@@ -245,19 +297,26 @@ m3_status m3_decode_step(const m3_decode_args* a, void* stream)
     if (!m3::decode_supported(N, P, R, a->io_dtype)) return M3_ERR_UNSUPPORTED;
     const int64_t nbh = Bt * H;
     if (nbh > (int64_t)1 << 30) return M3_ERR_UNSUPPORTED;
+    m3::OptParams op;
+    const m3_status os = check_options(a->opt, H, N, R, Bt, &op);
+    if (os != M3_OK) return os;
     if (nbh == 0) return M3_OK;
-    const void* ptrs[] = {a->x, a->B, a->C, a->dt, a->A, a->theta, a->lam,
+    const void* theta = a->opt.phase_mode != M3_PHASE_ZERO ? a->theta : nullptr;
+    const void* ptrs[] = {a->x, a->B, a->C, a->dt, a->A, theta, a->lam,
                           a->h, a->B_prev, a->x_prev, a->y};
+    for (int i = 0; i < 11; ++i)
+        if (ptrs[i] == nullptr && !(i == 5 && a->opt.phase_mode == M3_PHASE_ZERO)) return M3_ERR_NULL;
     for (const void* q : ptrs)
-        if (q == nullptr) return M3_ERR_NULL;
-    for (const void* q : ptrs)
-        if (!aligned16(q)) return M3_ERR_ALIGN;
+        if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
     const int e = io_size(a->io_dtype);
-    const Range in[] = {
-        range_of(a->x, nbh * R * P * e), range_of(a->B, nbh * R * N * e),
-        range_of(a->C, nbh * R * N * e), range_of(a->dt, nbh * 4), range_of(a->A, H * 4),
-        range_of(a->theta, nbh * (N / 2) * 4), range_of(a->lam, nbh * 4),
+    const int64_t nbg = Bt * op.groups;
+    Range in[13] = {
+        range_of(a->x, nbh * R * P * e), range_of(a->B, nbg * R * N * e),
+        range_of(a->C, nbg * R * N * e), range_of(a->dt, nbh * 4),
+        range_of(a->A, (a->opt.A_per_token ? nbh : H) * 4),
+        range_of(theta, nbh * (N / 2) * 4), range_of(a->lam, nbh * 4),
     };
+    option_ranges(a->opt, H, N, R, in + 7);
     const Range rec[] = {
         range_of(a->h, nbh * N * P * 4), range_of(a->B_prev, nbh * R * N * e),
         range_of(a->x_prev, nbh * R * P * e),
@@ -276,7 +335,8 @@ m3_status m3_decode_step(const m3_decode_args* a, void* stream)
 
     m3::DecodeParams p;
     p.x = a->x; p.B = a->B; p.C = a->C;
-    p.dt = a->dt; p.A = a->A; p.theta = a->theta; p.lam = a->lam;
+    p.dt = a->dt; p.A = a->A; p.theta = static_cast<const float*>(theta); p.lam = a->lam;
+    p.opt = op;
     p.h = a->h; p.Bp = a->B_prev; p.xp = a->x_prev; p.y = a->y;
     p.H = H; p.N = (int)N; p.P = (int)P; p.R = (int)R; p.nbh = nbh;
     return hip_status(m3::launch_decode(p, a->io_dtype, static_cast<hipStream_t>(stream)));

@@ -20,6 +20,10 @@
 //     broadcasts by the lanes of a row group); X_prev, X stay in registers;
 //   * the rank-R readout of each column is reduced across the row groups
 //     with lane shuffles.
+// Options: per-token decay A_t, B/C shared by head groups, phase
+// interventions (zero / reverse / shuffled increments) and the pre-mixer
+// (softplus / sigmoid of the raw dt / lam, RMSNorm with gains and biases on
+// B and C, applied to the wave's LDS copy; the record keeps the normalised B).
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
 
@@ -84,7 +88,10 @@ __device__ __forceinline__ void load4(float (&d)[4], const float* p) {
     for (int e = 0; e < 4; ++e) d[e] = v[e];
 }
 
-template <typename IO, int R>
+__device__ __forceinline__ float softplus_d(float z) { return z > 20.f ? z : log1pf(expf(z)); }
+__device__ __forceinline__ float sigmoid_d(float z) { return 1.f / (1.f + expf(-z)); }
+
+template <typename IO, int R, bool PM>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodeParams p)
 {
     extern __shared__ __attribute__((aligned(16))) float dsm[];
@@ -95,6 +102,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
     const int64_t bh = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
     if (bh >= p.nbh) return;   // whole wavefront
     const int64_t h = bh % p.H;
+    const int64_t G = p.opt.groups;
+    const int64_t bg = (bh / p.H) * G + h / (p.H / G);   // B/C row of this head's group
 
     float* sBp = dsm + (int64_t)wv * (3 * R * N + N);   // this wave's slice: [N][R]
     float* sB = sBp + R * N;                            // [N][R]
@@ -102,8 +111,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
     float* sCS = sC + R * N;                            // [NPR][2] cos, sin
 
     const IO* x = reinterpret_cast<const IO*>(p.x) + bh * R * P;
-    const IO* Bt = reinterpret_cast<const IO*>(p.B) + bh * R * N;
-    const IO* Ct = reinterpret_cast<const IO*>(p.C) + bh * R * N;
+    const IO* Bt = reinterpret_cast<const IO*>(p.B) + bg * R * N;
+    const IO* Ct = reinterpret_cast<const IO*>(p.C) + bg * R * N;
     IO* Bp = reinterpret_cast<IO*>(p.Bp) + bh * R * N;
     IO* xp = reinterpret_cast<IO*>(p.xp) + bh * R * P;
     float* hs = p.h + bh * (int64_t)N * P;
@@ -150,10 +159,22 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
         sB[n * R + r] = to_f32(Bt[idx]);
         sC[n * R + r] = to_f32(Ct[idx]);
     }
-    const float d = p.dt[bh], lm = p.lam[bh];
+    float d = p.dt[bh], lm = p.lam[bh];
+    if constexpr (PM) {
+        d = softplus_d(d + (p.opt.dtb != nullptr ? p.opt.dtb[h] : 0.f));
+        lm = sigmoid_d(lm);
+    }
     for (int i = lane; i < NPR; i += 64) {
+        float th = 0.f;                                        // zero: theta not read
+        if (p.opt.phase == 0) th = p.theta[bh * NPR + i];
+        else if (p.opt.phase == 2) th = -p.theta[bh * NPR + i];
+        else if (p.opt.phase == 3) {
+            int src = p.opt.perm[i];
+            src = src < 0 ? 0 : (src >= NPR ? NPR - 1 : src);
+            th = p.theta[bh * NPR + src];
+        }
         float sn, cs;
-        sincosf(d * p.theta[bh * NPR + i], &sn, &cs);
+        sincosf(d * th, &sn, &cs);
         *reinterpret_cast<float2*>(sCS + 2 * i) = make_float2(cs, sn);
     }
     float xv[R][4], xpv[R][4];
@@ -162,14 +183,50 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
         load4(xv[r], x + r * P + 4 * cg);
         load4(xpv[r], xp + r * P + 4 * cg);
     }
-    const float alpha = expf(d * p.A[h]);
+    const float alpha = expf(d * p.A[p.opt.a_tok ? bh : h]);
     const float beta = (1.f - lm) * d * alpha;
     const float gamma = lm * d;
     // The record's (B, X) are in LDS / registers: overwrite it with this
     // step's (every element is rewritten by an instruction of this wave that
     // follows the one that read it).
-    for (int idx = 8 * lane; idx < n8; idx += 512) copy8(Bp + idx, Bt + idx);
-    for (int idx = n8 + lane; idx < R * N; idx += 64) Bp[idx] = Bt[idx];
+    if constexpr (PM) {
+        // Pre-mixer on the LDS copies of B and C: each (matrix, rank) row is
+        // scaled by 1/rms over its N entries, times the gain, plus the bias.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float sc[2][R];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float* row = m == 0 ? sB : sC;
+                float ss = 0.f;
+                for (int n = lane; n < N; n += 64) ss += row[n * R + r] * row[n * R + r];
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                sc[m][r] = rsqrtf(ss / (float)N + p.opt.eps);
+            }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int n = lane; n < N; n += 64) {
+            const float wb = p.opt.Bw != nullptr ? p.opt.Bw[n] : 1.f;
+            const float wc = p.opt.Cw != nullptr ? p.opt.Cw[n] : 1.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int64_t bi = (h * R + r) * (int64_t)N + n;
+                const float vb = sB[n * R + r] * sc[0][r] * wb + (p.opt.Bb != nullptr ? p.opt.Bb[bi] : 0.f);
+                const float vc = sC[n * R + r] * sc[1][r] * wc + (p.opt.Cb != nullptr ? p.opt.Cb[bi] : 0.f);
+                sB[n * R + r] = vb;
+                sC[n * R + r] = vc;
+                Bp[r * N + n] = from_f32<IO>(vb);
+            }
+        }
+    } else {
+        for (int idx = 8 * lane; idx < n8; idx += 512) copy8(Bp + idx, Bt + idx);
+        for (int idx = n8 + lane; idx < R * N; idx += 64) Bp[idx] = Bt[idx];
+    }
     if (rg == 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) gstore4(xp + r * P + 4 * cg, f32x4{xv[r][0], xv[r][1], xv[r][2], xv[r][3]});
@@ -253,7 +310,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
 // LDS slice of one wavefront: B_prev, B, C as [N][R] and the pair rotations.
 size_t decode_wave_lds(int N, int R) { return sizeof(float) * (size_t)(3 * R * N + N); }
 
-template <typename IO, int R>
+template <typename IO, int R, bool PM>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream)
 {
     // Up to kDecWaves wavefronts per workgroup, as many as fit in LDS (the
@@ -261,15 +318,20 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream)
     const size_t per_wave = decode_wave_lds(p.N, R);
     int waves = (int)((160 * 1024) / per_wave);
     if (waves > kDecWaves) waves = kDecWaves;
+    auto* const kern = &decode_kernel<IO, R, PM>;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_kernel<IO, R>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
     (void)hipGetLastError();
     const int64_t blocks = (p.nbh + waves - 1) / waves;
-    hipLaunchKernelGGL((decode_kernel<IO, R>), dim3((unsigned)blocks), dim3(64 * waves),
-                       per_wave * waves, stream, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * waves), per_wave * waves, stream, p);
     return hipGetLastError();
+}
+
+template <typename IO, int R>
+hipError_t launch_decode_r(const DecodeParams& p, hipStream_t stream)
+{
+    return p.opt.premix ? launch_decode_t<IO, R, true>(p, stream) : launch_decode_t<IO, R, false>(p, stream);
 }
 
 }  // namespace
@@ -287,15 +349,15 @@ hipError_t launch_decode(const DecodeParams& p, int io_dtype, hipStream_t stream
 {
     if (io_dtype == 0) {
         switch (p.R) {
-        case 1: return launch_decode_t<float, 1>(p, stream);
-        case 2: return launch_decode_t<float, 2>(p, stream);
-        default: return launch_decode_t<float, 4>(p, stream);
+        case 1: return launch_decode_r<float, 1>(p, stream);
+        case 2: return launch_decode_r<float, 2>(p, stream);
+        default: return launch_decode_r<float, 4>(p, stream);
         }
     }
     switch (p.R) {
-    case 1: return launch_decode_t<bf16, 1>(p, stream);
-    case 2: return launch_decode_t<bf16, 2>(p, stream);
-    default: return launch_decode_t<bf16, 4>(p, stream);
+    case 1: return launch_decode_r<bf16, 1>(p, stream);
+    case 2: return launch_decode_r<bf16, 2>(p, stream);
+    default: return launch_decode_r<bf16, 4>(p, stream);
     }
 }
 

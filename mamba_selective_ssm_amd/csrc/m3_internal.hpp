@@ -9,6 +9,19 @@ namespace m3 {
 
 struct ScanParams;
 
+// Options of both entry points, resolved for the kernels.
+struct OptParams {
+    int64_t groups;        // B/C head groups (nheads when not grouped)
+    int a_tok;             // A per (batch, token, head) instead of per head
+    int phase;             // m3_phase_mode
+    const int* perm;       // [N/2] pair permutation (shuffle only)
+    int premix;            // dt/lam raw, B/C RMS-normalised with gains and biases
+    float eps;
+    const float *Bw, *Cw;  // [N] or NULL (ones)
+    const float *Bb, *Cb;  // [H, R, N] or NULL (zeros)
+    const float *dtb;      // [H] or NULL (zeros)
+};
+
 struct DecodeParams {
     const void *x, *B, *C;
     const float *dt, *A, *theta, *lam;
@@ -18,6 +31,7 @@ struct DecodeParams {
     int64_t H;
     int N, P, R;
     int64_t nbh;
+    OptParams opt;
 };
 
 bool decode_supported(int64_t N, int64_t P, int64_t R, int io_dtype);

@@ -79,6 +79,7 @@ struct ScanParams {
     float *h_out;
     void *Bp_out, *xp_out;
     float *ws;          // segment records: written by the state pass, read by the output pass
+    OptParams opt;      // head groups, per-token decay, phase mode, pre-mixer
     int64_t batch, L, H, P;
     int p_split;
     int nbh;
@@ -139,17 +140,27 @@ struct ScanCfg {
     // misc[4], u[Q] (w_k relative to its key tile's last token)
     static constexpr size_t nF = 5 * (size_t)Q + 2 * (size_t)NPR + 4;
     static constexpr size_t sz_H1 = (size_t)PS * LDH * E;
-    template <bool FULL> struct Lay {
+    // Pre-mixer (PM): gains [2][N] and biases [2][R][N] (each prep wave stages
+    // the entries of its own pair quads), partial row sums of squares
+    // [WA][2][T] exchanged between the prep waves, and their counter.
+    static constexpr size_t sz_PMW = 2 * (size_t)(R + 1) * N * 4;
+    static constexpr size_t sz_SS = (size_t)WA * 2 * T * 4;
+    template <bool FULL, bool PM = false> struct Lay {
         static constexpr size_t oB = 0;
         static constexpr size_t oC = sz_B;
         static constexpr size_t oX = oC + (FULL ? sz_B : 0);
         static constexpr size_t oF = oX + sz_X;
         static constexpr size_t BUF = (oF + nF * 4 + 15) / 16 * 16;
         static constexpr size_t oH = 2 * BUF;
-        static constexpr size_t bytes = oH + (FULL ? (SH1 ? 1 : 2) * sz_H1 : 0);
+        static constexpr size_t oPW = oH + (FULL ? (SH1 ? 1 : 2) * sz_H1 : 0);
+        static constexpr size_t oSS = oPW + (PM ? sz_PMW : 0);
+        static constexpr size_t oCNT = oSS + (PM ? sz_SS : 0);
+        static constexpr size_t bytes = oCNT + (PM ? 16 : 0);
     };
     static constexpr size_t lds_bytes = Lay<true>::bytes;
     static constexpr size_t lds_bytes_state = Lay<false>::bytes;
+    static constexpr size_t lds_bytes_pm = Lay<true, true>::bytes;
+    static constexpr size_t lds_bytes_state_pm = Lay<false, true>::bytes;
     // Segment record: G (fp32, NP x P) in the math waves' tile order -- tile
     // slot (slice, tau) holds 64 lanes x 4 rows, one 16-byte access per lane
     // -- then Lam_seg*log2(e) (padded to 4 floats), then (cos, sin) of the
@@ -161,13 +172,14 @@ struct ScanCfg {
     static_assert(N % 8 == 0 && LQ >= 16 && LQ <= 64, "unsupported dstate");
     static_assert(NPR4 < NWP || NPR4 % NWP == 0, "pair quads must split evenly over prep waves");
     static_assert(PT % PG == 0 && NWM % PG == 0, "headdim tiles must split evenly over math waves");
-    static_assert(lds_bytes <= 160 * 1024, "LDS budget");
+    static_assert(lds_bytes <= 160 * 1024 && lds_bytes_pm <= 160 * 1024, "LDS budget");
 };
 
 // One prep thread's share of a chunk's raw inputs, loaded a chunk ahead.
 template <class Cf> struct PrepStage {
     using io_t = typename Cf::io_t;
     float a_dt[Cf::QPL], a_lm[Cf::QPL], a_dn[Cf::QPL], a_ln[Cf::QPL];  // dt, lam at t, t+1
+    float a_A[Cf::QPL];                                                 // decay rate at t
     float dtv[Cf::TPL];                                                 // dt of the lane's tokens
     f32x4 thv[Cf::TPL];                                                 // theta, 4 pairs
     IoRow8<io_t> bq[Cf::TPL][Cf::R], cq[Cf::TPL][Cf::R];                // B, C: 4 pairs
@@ -205,12 +217,19 @@ __device__ __forceinline__ float group_inclusive_sum(float v)
 // FULL: outputs y (and the state record when this is the last segment).
 // !FULL: state pass -- each segment except the last writes its end state
 // (from a zero start, except segment 0 which starts from the true state).
-template <class Cf, bool FULL>
+// softplus(z) = log(1 + e^z) (z itself above 20, where the difference is
+// below float32 resolution) and sigmoid(z) = 1 / (1 + e^-z): the pre-mixer's
+// maps of the raw dt and lam projections.
+__device__ __forceinline__ float softplus_f(float z) { return z > 20.f ? z : log1pf(expf(z)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + expf(-z)); }
+
+// PM: pre-mixer on (the raw dt, lam, B and C are normalised in the prep waves).
+template <class Cf, bool FULL, bool PM>
 __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(const ScanParams p)
 {
     using io_t = typename Cf::io_t;
     using op_t = typename Cf::op_t;
-    using Lay = typename Cf::template Lay<FULL>;
+    using Lay = typename Cf::template Lay<FULL, PM>;
     constexpr int N = Cf::N, NP = Cf::NP, NPR = Cf::NPR, PS = Cf::PS, R = Cf::R;
     constexpr int Q = Cf::Q, T = Cf::T, NWM = Cf::NWM, NWP = Cf::NWP, NT = Cf::NT;
     constexpr int LDB = Cf::LDB, LDX = Cf::LDX, LDXR = Cf::LDXR, LDH = Cf::LDH;
@@ -255,8 +274,11 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     const int64_t c_end = c_begin + p.seg_chunks < nchunks_all ? c_begin + p.seg_chunks : nchunks_all;
     const bool last_seg = seg == p.nseg - 1;
 
-    const int sDT = (int)H, sTH = (int)(H * NPR), sBN = (int)(H * R * N), sXP = (int)(H * R * P);
+    const int64_t G = p.opt.groups;                 // B/C head groups
+    const int64_t hg = h / (H / G);                  // this head's group
+    const int sDT = (int)H, sTH = (int)(H * NPR), sBN = (int)(G * R * N), sXP = (int)(H * R * P);
     const int64_t tok0 = (b * L + c_begin * Q) * H + h;
+    const int64_t tok0g = (b * L + c_begin * Q) * G + hg;   // B, C rows
     const int64_t rec_sz = Cf::rec_floats(P);
     float* recs = p.ws + (int64_t)bh * (p.nseg - 1) * rec_sz;   // this (b, h)'s records
 
@@ -276,15 +298,43 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     const bool arole = !is_math && pw < WA;
     const int qd = (arole ? pw : 0) * QPWV + lane / LQ;   // pair quad: rows 8qd .. 8qd+7
     const int li = lane % LQ;                              // lane within the quad's group
-    const float Ah = p.A[h];
+
+    // Pre-mixer state: gains and biases of this lane's pair quad in LDS
+    // (staged and read by the same wave), the prep waves' exchange of row
+    // sums of squares, and the exchange counter (zeroed before any wave can
+    // add to it).
+    float* const sPW = reinterpret_cast<float*>(smem + Lay::oPW);   // [2][N] gains, [2][R][N] biases
+    float* const sSS = reinterpret_cast<float*>(smem + Lay::oSS);   // [WA][2][T]
+    int* const sCnt = reinterpret_cast<int*>(smem + Lay::oCNT);
+    int pcall = 0;                                                 // prep calls of this wave
+    if constexpr (PM) {
+        if (arole) {
+            constexpr int PER = 8 * (R + 1);   // gains and R bias rows, 8 entries each
+            for (int idx = li; idx < 2 * PER; idx += LQ) {
+                const int m = idx / PER, rem = idx % PER, k = rem / 8, n = 8 * qd + rem % 8;
+                const float* W = m == 0 ? p.opt.Bw : p.opt.Cw;
+                const float* Bb = m == 0 ? p.opt.Bb : p.opt.Cb;
+                if (k == 0) sPW[m * N + n] = W != nullptr ? W[n] : 1.f;
+                else sPW[2 * N + (m * R + k - 1) * N + n] =
+                         Bb != nullptr ? Bb[((int64_t)h * R + (k - 1)) * N + n] : 0.f;
+            }
+        }
+        if (tid == 0) *sCnt = 0;
+        __syncthreads();
+    }
     double l2seg = 0.0, phiseg[4] = {0.0, 0.0, 0.0, 0.0};   // segment totals (state pass)
+    const int phase = p.opt.phase;
+    const float dtb_h = (PM && p.opt.dtb != nullptr) ? p.opt.dtb[h] : 0.f;
 
     // Load pointers at the next chunk to be loaded; advanced by every issue.
     const float* __restrict__ ldt = p.dt + tok0;
     const float* __restrict__ llam = p.lam + tok0;
-    const float* __restrict__ lth = p.theta + tok0 * NPR;
-    const io_t* __restrict__ lB = reinterpret_cast<const io_t*>(p.B) + tok0 * R * N;
-    const io_t* __restrict__ lC = reinterpret_cast<const io_t*>(p.C) + tok0 * R * N;
+    const float* __restrict__ lth = p.theta + (phase != 1 ? tok0 * NPR : 0);
+    const io_t* __restrict__ lB = reinterpret_cast<const io_t*>(p.B) + tok0g * R * N;
+    const io_t* __restrict__ lC = reinterpret_cast<const io_t*>(p.C) + tok0g * R * N;
+    // decay rate: per token (stride dt's) or one per head (stride 0)
+    const float* __restrict__ lA = p.A + (p.opt.a_tok ? tok0 : h);
+    const int sA = p.opt.a_tok ? sDT : 0;
     const io_t* __restrict__ lX = reinterpret_cast<const io_t*>(p.x) + tok0 * R * P + p0;
 
     auto xmap = [](int it, int& rho, int& cg) {
@@ -299,7 +349,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // Offsets inside a chunk are 32-bit byte offsets (token index times the
     // per-token byte stride, < 2^24, via the 24-bit multiplier) added to the
     // wave-uniform chunk base: no 64-bit vector address arithmetic.
-    const unsigned bDT = 4u * (unsigned)sDT, bTH = 4u * (unsigned)sTH;
+    const unsigned bDT = 4u * (unsigned)sDT, bTH = 4u * (unsigned)sTH, bA = 4u * (unsigned)sA;
     const unsigned bBN = (unsigned)sizeof(io_t) * (unsigned)sBN, bXP = (unsigned)sizeof(io_t) * (unsigned)sXP;
     const unsigned thq = 16u * (unsigned)qd;                                // theta quad
     const unsigned bcq = (unsigned)sizeof(io_t) * 8u * (unsigned)qd;       // B/C quad
@@ -320,6 +370,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 const unsigned jc = (unsigned)(j < jl ? j : jl);
                 const unsigned jnc = (unsigned)(j + 1 < jn ? j + 1 : jn);
                 st.a_dt[kk] = *at(ldt, __umul24(jc, bDT));
+                st.a_A[kk] = *at(lA, __umul24(jc, bA));
                 st.a_lm[kk] = *at(llam, __umul24(jc, bDT));
                 st.a_dn[kk] = *at(ldt, __umul24(jnc, bDT));
                 st.a_ln[kk] = *at(llam, __umul24(jnc, bDT));
@@ -339,7 +390,20 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         for (int kk = 0; kk < TPL; ++kk) {
             const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
             st.dtv[kk] = *at(ldt, __umul24(j, bDT));
-            st.thv[kk] = *reinterpret_cast<const f32x4*>(at(lth, __umul24(j, bTH) + thq));
+            if (phase == 0) {
+                st.thv[kk] = *reinterpret_cast<const f32x4*>(at(lth, __umul24(j, bTH) + thq));
+            } else if (phase == 1) {        // zero: theta is not read
+                st.thv[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+            } else if (phase == 2) {        // reverse
+                st.thv[kk] = -*reinterpret_cast<const f32x4*>(at(lth, __umul24(j, bTH) + thq));
+            } else {                        // shuffle: pair i reads pair perm[i]
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    int src = p.opt.perm[4 * qd + e];
+                    src = src < 0 ? 0 : (src >= NPR ? NPR - 1 : src);
+                    st.thv[kk][e] = *at(lth, __umul24(j, bTH) + 4u * (unsigned)src);
+                }
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < TPL; ++kk) {
@@ -351,12 +415,14 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 if constexpr (FULL) st.cq[kk][r].load(at(lC, off));
             }
         }
-        ldt += Q * sDT; llam += Q * sDT; lth += Q * sTH;
+        ldt += Q * sDT; llam += Q * sDT; lA += Q * sA;
+        if (phase != 1) lth += Q * sTH;
         lB += Q * sBN; lC += Q * sBN; lX += Q * sXP;
     };
 
     // Raw inputs of chunk c (in st) -> operands and scalars in buffer s.
     auto prep = [&](int64_t c, int s) {
+        ++pcall;
         op_t* sB = buf_B(s);
         op_t* sC = buf_C(s);
         op_t* sX = buf_X(s);
@@ -378,13 +444,20 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 const int j = lane * QPL + kk;
                 const bool ok = j < Q && j <= jl;
                 const bool okn = j < Q && t0 + j + 1 < L;
-                const float d = ok ? st.a_dt[kk] : 0.f;
-                const float lm = ok ? st.a_lm[kk] : 0.f;
-                const float dn = okn ? st.a_dn[kk] : 0.f;
-                const float ln = okn ? st.a_ln[kk] : 0.f;
+                float d = st.a_dt[kk], lm = st.a_lm[kk], dn = st.a_dn[kk], ln = st.a_ln[kk];
+                if constexpr (PM) {
+                    d = softplus_f(d + dtb_h);
+                    lm = sigmoid_f(lm);
+                    dn = softplus_f(dn + dtb_h);
+                    ln = sigmoid_f(ln);
+                }
+                d = ok ? d : 0.f;
+                lm = ok ? lm : 0.f;
+                dn = okn ? dn : 0.f;
+                ln = okn ? ln : 0.f;
                 gm[kk] = lm * d;
                 wt[kk] = gm[kk] + (1.f - ln) * dn;
-                run += d * Ah;
+                run += d * st.a_A[kk];
                 a[kk] = run;
             }
             const float incl = wave_inclusive_sum(run);
@@ -446,6 +519,48 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             // FULLC: every token of the chunk is valid (no masking needed)
             auto rotate_all = [&](auto fullc) {
                 constexpr bool FULLC = decltype(fullc)::value;
+                // Pre-mixer, step 1: this wave's share of every row's sum of
+                // squares (its pair quads), summed over the wave's quads and
+                // published to the other prep waves.
+                float scB[TPL][R], scC[TPL][R];
+                if constexpr (PM) {
+#pragma unroll
+                    for (int kk = 0; kk < TPL; ++kk)
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            float sb = 0.f, sc = 0.f;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const float vb = st.bq[kk][r].get(e);
+                                sb += vb * vb;
+                                if constexpr (FULL) {
+                                    const float vc = st.cq[kk][r].get(e);
+                                    sc += vc * vc;
+                                }
+                            }
+#pragma unroll
+                            for (int off = LQ; off < 64; off <<= 1) {
+                                sb += __shfl_xor(sb, off, 64);
+                                if constexpr (FULL) sc += __shfl_xor(sc, off, 64);
+                            }
+                            scB[kk][r] = sb;
+                            scC[kk][r] = sc;
+                        }
+                    if (lane < LQ) {
+#pragma unroll
+                        for (int kk = 0; kk < TPL; ++kk) {
+                            const int j = li * TPL + kk;
+                            if (LQ * TPL == Q || j < Q) {
+#pragma unroll
+                                for (int r = 0; r < R; ++r) {
+                                    sSS[(pw * 2 + 0) * T + j * R + r] = scB[kk][r];
+                                    if constexpr (FULL) sSS[(pw * 2 + 1) * T + j * R + r] = scC[kk][r];
+                                }
+                            }
+                        }
+                    }
+                    if (lane == 0) __hip_atomic_fetch_add(sCnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
                 f32x4 loc[TPL];
                 f32x4 run = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -453,14 +568,63 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                     // lanes past the chunk (LQ * TPL > Q) never contribute
                     const int j = li * TPL + kk;
                     const bool ok = FULLC ? (LQ * TPL == Q || j < Q) : j <= jl;
+                    const float dv = PM ? softplus_f(st.dtv[kk] + dtb_h) : st.dtv[kk];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) run[e] += ok ? st.dtv[kk] * st.thv[kk][e] : 0.f;
+                    for (int e = 0; e < 4; ++e) run[e] += ok ? dv * st.thv[kk][e] : 0.f;
                     loc[kk] = run;
                 }
                 f32x4 inc;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) inc[e] = group_inclusive_sum<LQ>(run[e]);
                 const f32x4 ex = inc - run;
+                // Pre-mixer, step 2: wait until every prep wave with pair quads
+                // has published this chunk's partial sums (a bounded wait: the
+                // waves reach it together), then the rows' RMS scales.
+                float gw[2][8];
+                if constexpr (PM) {
+                    const int target = WA * pcall;
+                    for (int it = 0; it < (1 << 22); ++it) {
+                        const int v = __builtin_amdgcn_readfirstlane(
+                            __hip_atomic_load(sCnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+                        if (v >= target) break;
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                    const float rn = 1.f / (float)N;
+#pragma unroll
+                    for (int kk = 0; kk < TPL; ++kk) {
+                        int j = li * TPL + kk;
+                        j = j < Q ? j : Q - 1;
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            float tb = 0.f, tc = 0.f;
+#pragma unroll
+                            for (int w = 0; w < WA; ++w) {
+                                tb += sSS[(w * 2 + 0) * T + j * R + r];
+                                if constexpr (FULL) tc += sSS[(w * 2 + 1) * T + j * R + r];
+                            }
+                            scB[kk][r] = rsqrtf(tb * rn + p.opt.eps);
+                            scC[kk][r] = FULL ? rsqrtf(tc * rn + p.opt.eps) : 0.f;
+                        }
+                    }
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        const f32x4 g0 = *reinterpret_cast<const f32x4*>(sPW + m * N + 8 * qd);
+                        const f32x4 g1 = *reinterpret_cast<const f32x4*>(sPW + m * N + 8 * qd + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { gw[m][e] = g0[e]; gw[m][4 + e] = g1[e]; }
+                    }
+                }
+                // B or C entry e (of 8) of rank r as the mixer uses it
+                auto bval = [&](int kk, int r, int e) -> float {
+                    const float v = st.bq[kk][r].get(e);
+                    if constexpr (!PM) return v;
+                    else return v * scB[kk][r] * gw[0][e] + sPW[2 * N + r * N + 8 * qd + e];
+                };
+                auto cval = [&](int kk, int r, int e) -> float {
+                    const float v = st.cq[kk][r].get(e);
+                    if constexpr (!PM) return v;
+                    else return v * scC[kk][r] * gw[1][e] + sPW[2 * N + (R + r) * N + 8 * qd + e];
+                };
 #pragma unroll
                 for (int kk = 0; kk < TPL; ++kk) {
                     const int j = li * TPL + kk;
@@ -476,8 +640,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                             float o[8];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const float b0 = ok ? st.bq[kk][r].get(2 * e) : 0.f;
-                                const float b1 = ok ? st.bq[kk][r].get(2 * e + 1) : 0.f;
+                                const float b0 = ok ? bval(kk, r, 2 * e) : 0.f;
+                                const float b1 = ok ? bval(kk, r, 2 * e + 1) : 0.f;
                                 o[2 * e] = cs[e] * b0 + sn[e] * b1;
                                 o[2 * e + 1] = cs[e] * b1 - sn[e] * b0;
                             }
@@ -485,8 +649,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                             if constexpr (FULL) {
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) {
-                                    const float c0 = ok ? st.cq[kk][r].get(2 * e) : 0.f;
-                                    const float c1 = ok ? st.cq[kk][r].get(2 * e + 1) : 0.f;
+                                    const float c0 = ok ? cval(kk, r, 2 * e) : 0.f;
+                                    const float c1 = ok ? cval(kk, r, 2 * e + 1) : 0.f;
                                     o[2 * e] = cs[e] * c0 + sn[e] * c1;
                                     o[2 * e + 1] = cs[e] * c1 - sn[e] * c0;
                                 }
@@ -570,7 +734,14 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                         for (int r = 0; r < R; ++r) bv[k][i][r] = to_f32(Bp[((int64_t)bh * R + r) * N + n]);
                     }
                 }
-                if (L > 0) bhat1 = (1.f - p.lam[(b * L) * H + h]) * p.dt[(b * L) * H + h];
+                if (L > 0) {
+                    float d0 = p.dt[(b * L) * H + h], l0 = p.lam[(b * L) * H + h];
+                    if constexpr (PM) {
+                        d0 = softplus_f(d0 + (p.opt.dtb != nullptr ? p.opt.dtb[h] : 0.f));
+                        l0 = sigmoid_f(l0);
+                    }
+                    bhat1 = (1.f - l0) * d0;
+                }
             } else {
 #pragma unroll
                 for (int k = 0; k < TPW; ++k) {
@@ -1036,11 +1207,34 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             const io_t* Bi = reinterpret_cast<const io_t*>(p.Bp_in);
             const io_t* xi = reinterpret_cast<const io_t*>(p.xp_in);
             const int64_t tl = (b * L + (L - 1)) * H + h;
-            for (int idx = tid; idx < R * N; idx += NT) {
-                io_t v = from_f32<io_t>(0.f);
-                if (L > 0) v = Bm[tl * R * N + idx];
-                else if (Bi != nullptr) v = Bi[(int64_t)bh * R * N + idx];
-                Bo[idx] = v;
+            const int64_t tlg = (b * L + (L - 1)) * G + hg;
+            if (PM && L > 0) {
+                // the last token's B through the pre-mixer (wave 0)
+                if (wv == 0) {
+                    for (int r = 0; r < R; ++r) {
+                        const io_t* row = Bm + (tlg * R + r) * N;
+                        float ss = 0.f;
+                        for (int n = lane; n < N; n += 64) {
+                            const float v = to_f32(row[n]);
+                            ss += v * v;
+                        }
+#pragma unroll
+                        for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                        const float sc = rsqrtf(ss / (float)N + p.opt.eps);
+                        for (int n = lane; n < N; n += 64) {
+                            const float w = p.opt.Bw != nullptr ? p.opt.Bw[n] : 1.f;
+                            const float bb = p.opt.Bb != nullptr ? p.opt.Bb[((int64_t)h * R + r) * N + n] : 0.f;
+                            Bo[r * N + n] = from_f32<io_t>(to_f32(row[n]) * sc * w + bb);
+                        }
+                    }
+                }
+            } else {
+                for (int idx = tid; idx < R * N; idx += NT) {
+                    io_t v = from_f32<io_t>(0.f);
+                    if (L > 0) v = Bm[tlg * R * N + idx];
+                    else if (Bi != nullptr) v = Bi[(int64_t)bh * R * N + idx];
+                    Bo[idx] = v;
+                }
             }
             for (int64_t idx = tid; idx < R * P; idx += NT) {
                 io_t v = from_f32<io_t>(0.f);
@@ -1059,36 +1253,45 @@ size_t scan_workspace_bytes(int64_t nbh, int64_t P, int nseg)
 }
 
 // Raise the dynamic-LDS limit of one kernel once per process.
-template <class Cf, bool FULL>
+template <class Cf, bool FULL, bool PM>
 hipError_t scan_set_lds_limit()
 {
     static hipError_t status = [] {
-        const void* f = reinterpret_cast<const void*>(&scan_kernel<Cf, FULL>);
+        const void* f = reinterpret_cast<const void*>(&scan_kernel<Cf, FULL, PM>);
         return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)(FULL ? Cf::lds_bytes : Cf::lds_bytes_state));
+                                   (int)Cf::template Lay<FULL, PM>::bytes);
     }();
     return status;
+}
+
+template <class Cf, bool PM>
+hipError_t launch_scan_t(const ScanParams& p, hipStream_t stream)
+{
+    const int64_t per_seg = (int64_t)((p.nbh + 7) / 8) * 8 * p.p_split;
+    constexpr size_t lds_state = Cf::template Lay<false, PM>::bytes;
+    constexpr size_t lds_full = Cf::template Lay<true, PM>::bytes;
+    auto* const k_state = &scan_kernel<Cf, false, PM>;
+    auto* const k_full = &scan_kernel<Cf, true, PM>;
+    hipError_t e;
+    (void)hipGetLastError();
+    if (p.nseg > 1) {
+        e = scan_set_lds_limit<Cf, false, PM>();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_state, dim3((unsigned)(per_seg * (p.nseg - 1))), dim3(Cf::NT),
+                           lds_state, stream, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    e = scan_set_lds_limit<Cf, true, PM>();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_full, dim3((unsigned)(per_seg * p.nseg)), dim3(Cf::NT), lds_full, stream, p);
+    return hipGetLastError();
 }
 
 template <class Cf>
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream)
 {
-    const int64_t per_seg = (int64_t)((p.nbh + 7) / 8) * 8 * p.p_split;
-    hipError_t e;
-    (void)hipGetLastError();
-    if (p.nseg > 1) {
-        e = scan_set_lds_limit<Cf, false>();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((scan_kernel<Cf, false>), dim3((unsigned)(per_seg * (p.nseg - 1))),
-                           dim3(Cf::NT), Cf::lds_bytes_state, stream, p);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    e = scan_set_lds_limit<Cf, true>();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_kernel<Cf, true>), dim3((unsigned)(per_seg * p.nseg)), dim3(Cf::NT),
-                       Cf::lds_bytes, stream, p);
-    return hipGetLastError();
+    return p.opt.premix ? launch_scan_t<Cf, true>(p, stream) : launch_scan_t<Cf, false>(p, stream);
 }
 
 }  // namespace m3

@@ -116,3 +116,42 @@ def make_decode_inputs(w: Workload, seed: int, step: int, A: torch.Tensor, devic
 def to_f64_numpy(t: torch.Tensor):
     """Exact upcast of a float32/bfloat16 tensor to a float64 numpy array (host)."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def make_option_inputs(w: Workload, seed: int, device="cpu", *, ngroups: int = 0,
+                       a_per_token: bool = False, phase: str = "native", premix: bool = False):
+    """A scan batch for ``w`` with the library's options drawn as well.
+
+    Returns (inputs, extras).  ``inputs`` has the keys of make_scan_inputs;
+    with ``ngroups`` B and C are [B,L,G,R,N]; with ``a_per_token`` A is
+    [B,L,H] = -exp(U(-1, 1)); with ``premix`` dt and lam are the raw
+    projections dt_raw ~ N(0, 1), lam_raw ~ N(0, 1).  ``extras`` holds
+    ``perm`` (int32 [N/2], a uniform random permutation, for phase "shuffle")
+    and ``premix`` parameters: gains U(0.5, 1.5) [N], biases N(0, 0.3^2)
+    [H,R,N], dt_bias = dt_mu + U(-0.5, 0.5) [H] (so that the mapped dt follows
+    the workload's softplus(N(dt_mu, 1))), eps 1e-5.  Seeded by ``seed``;
+    draws come after those of make_scan_inputs.
+    """
+    inp = make_scan_inputs(w, seed, device)
+    g = _gen(seed * 7919 + 17, device)
+    f32 = dict(dtype=torch.float32, device=device)
+    Bt, L, H, P, N, R = w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.rank
+    extras = {}
+    if ngroups:
+        inp["B"] = torch.randn((Bt, L, ngroups, R, N), generator=g, **f32).to(w.torch_dtype)
+        inp["C"] = torch.randn((Bt, L, ngroups, R, N), generator=g, **f32).to(w.torch_dtype)
+    if a_per_token:
+        inp["A"] = -torch.exp(torch.rand((Bt, L, H), generator=g, **f32) * 2.0 - 1.0)
+    if phase == "shuffle":
+        extras["perm"] = torch.randperm(N // 2, generator=g, device=device).to(torch.int32)
+    if premix:
+        inp["dt"] = torch.randn((Bt, L, H), generator=g, **f32)
+        inp["lam"] = torch.randn((Bt, L, H), generator=g, **f32)
+        extras["premix"] = dict(
+            B_norm_w=torch.rand((N,), generator=g, **f32) + 0.5,
+            C_norm_w=torch.rand((N,), generator=g, **f32) + 0.5,
+            B_bias=torch.randn((H, R, N), generator=g, **f32) * 0.3,
+            C_bias=torch.randn((H, R, N), generator=g, **f32) * 0.3,
+            dt_bias=w.dt_mu + torch.rand((H,), generator=g, **f32) - 0.5,
+            eps=1e-5)
+    return inp, extras

@@ -41,7 +41,11 @@ def test_struct_layout_matches_header(tmp_path):
     """Compile a tiny C program against the header and compare offsets."""
     fields_s = [f[0] for f in binding.ScanArgs._fields_]
     fields_d = [f[0] for f in binding.DecodeArgs._fields_]
+    fields_o = [f[0] for f in binding.Options._fields_]
     src = ['#include <stdio.h>', '#include <stddef.h>', '#include "m3scan.h"', "int main(void){"]
+    src.append('printf("%zu\\n", sizeof(m3_options));')
+    for f in fields_o:
+        src.append('printf("%%zu\\n", offsetof(m3_options, %s));' % f)
     src.append('printf("%zu\\n", sizeof(m3_scan_args));')
     for f in fields_s:
         src.append('printf("%%zu\\n", offsetof(m3_scan_args, %s));' % f)
@@ -55,7 +59,9 @@ def test_struct_layout_matches_header(tmp_path):
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(c)], check=True)
     vals = [int(v) for v in subprocess.run([str(exe)], stdout=subprocess.PIPE, text=True,
                                            check=True).stdout.split()]
-    expect = [ctypes.sizeof(binding.ScanArgs)]
+    expect = [ctypes.sizeof(binding.Options)]
+    expect += [getattr(binding.Options, f).offset for f in fields_o]
+    expect += [ctypes.sizeof(binding.ScanArgs)]
     expect += [getattr(binding.ScanArgs, f).offset for f in fields_s]
     expect += [ctypes.sizeof(binding.DecodeArgs)]
     expect += [getattr(binding.DecodeArgs, f).offset for f in fields_d]
@@ -63,8 +69,8 @@ def test_struct_layout_matches_header(tmp_path):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.m3_abi_version() == 1
-    for code in range(-8, 1):
+    assert lib.m3_abi_version() == 2
+    for code in range(-9, 1):
         s = lib.m3_status_string(code)
         assert s and s != b"unknown status"
     assert lib.m3_status_string(-99) == b"unknown status"
@@ -72,6 +78,9 @@ def test_version_and_status_strings(lib):
 
 
 FAKE = 0x7F0000000000   # never dereferenced: validation fails before any device access
+
+
+OPTION_FIELDS = {f[0] for f in binding.Options._fields_}
 
 
 def scan_args(**kw):
@@ -82,7 +91,7 @@ def scan_args(**kw):
     for i, p in enumerate(ptrs):
         setattr(a, p, FAKE + i * (1 << 32))
     for k, v in kw.items():
-        setattr(a, k, v)
+        setattr(a.opt if k in OPTION_FIELDS else a, k, v)
     return a
 
 
@@ -104,6 +113,16 @@ def run_scan(lib, a):
     (dict(x=FAKE + 8), -5), (dict(dt=FAKE + 4), -5),
     (dict(y=FAKE), -7),                                      # y aliases x
     (dict(y=FAKE + (1 << 32) + 64), -7),                     # y overlaps B
+    # options
+    (dict(ngroups=2), -9), (dict(ngroups=-1), -9), (dict(A_per_token=2), -9),
+    (dict(phase_mode=4), -9), (dict(phase_mode=-1), -9), (dict(premix=2), -9),
+    (dict(premix=1, norm_eps=-1.0), -9), (dict(premix=1, norm_eps=float("nan")), -9),
+    (dict(phase_mode=3), -1),                                # shuffle without a permutation
+    (dict(phase_mode=3, phase_perm=FAKE + (40 << 32) + 4), -5),
+    (dict(premix=1, B_bias=FAKE + (41 << 32) + 8), -5),
+    (dict(theta=None, phase_mode=1, x=FAKE + 8), -5),        # zero phase: theta may be NULL
+    (dict(theta=None, phase_mode=2, x=FAKE + 8), -1),
+    (dict(premix=1, C_bias=FAKE + (7 << 32)), -7),           # y overlaps the C bias
 ])
 def test_scan_validation_codes(lib, kw, code):
     assert run_scan(lib, scan_args(**kw)) == code
@@ -128,7 +147,7 @@ def decode_args(**kw):
     for i, p in enumerate(["x", "B", "C", "dt", "A", "theta", "lam", "h", "B_prev", "x_prev", "y"]):
         setattr(a, p, FAKE + i * (1 << 32))
     for k, v in kw.items():
-        setattr(a, k, v)
+        setattr(a.opt if k in OPTION_FIELDS else a, k, v)
     return a
 
 
@@ -139,6 +158,12 @@ def decode_args(**kw):
     (dict(h=FAKE + (7 << 32) + 4), -5),
     (dict(y=FAKE + (7 << 32)), -7),          # y aliases the state
     (dict(B_prev=FAKE + (1 << 32)), -7),     # state record aliases a step input
+    (dict(ngroups=3), -9), (dict(phase_mode=9), -9), (dict(premix=1, norm_eps=-2.0), -9),
+    (dict(phase_mode=3), -1),
+    (dict(theta=None, phase_mode=1, h=FAKE + (7 << 32) + 4), -5),   # zero phase: theta may be NULL
+    (dict(theta=None, h=FAKE + (7 << 32) + 4), -1),
+    (dict(premix=1, dt_bias=FAKE + (10 << 32)), -7),                # y overlaps the dt bias
+    (dict(premix=1, B_bias=FAKE + (7 << 32)), -7),                  # state overlaps the B bias
 ])
 def test_decode_validation_codes(lib, kw, code):
     assert lib.m3_decode_step(ctypes.byref(decode_args(**kw)), None) == code
