@@ -34,25 +34,35 @@ def io_bytes(w):
     return 4 if w.io_dtype == "f32" else 2
 
 
-def scan_algorithmic_bytes(w, L=None):
+def scan_algorithmic_bytes(w, L=None, ngroups=0, a_tok=False, phase="native", premix=False):
     """Minimum HBM bytes of one m3_scan_fwd: every input read once, y and the
-    final state record written once."""
+    final state record written once.  Options: B and C read once per head
+    group, A per token, no theta with the zero phase, the pre-mixer's
+    parameters (and the shuffle permutation) once."""
     L = w.seqlen if L is None else L
     e = io_bytes(w)
-    R, P, N = w.rank, w.headdim, w.dstate
-    per_tok = e * (2 * R * P + 2 * R * N) + 4 * (N // 2 + 2)
+    R, P, N, H = w.rank, w.headdim, w.dstate, w.heads
+    G = ngroups or H
+    per_tok = e * 2 * R * P + 4 * 2 + (0 if phase == "zero" else 4 * (N // 2)) + (4 if a_tok else 0)
+    per_grp_tok = e * 2 * R * N
     per_bh = 4 * N * P + e * (R * N + R * P)
-    return w.batch * w.heads * (L * per_tok + per_bh) + 4 * w.heads
+    extra = 0 if a_tok else 4 * H
+    if phase == "shuffle":
+        extra += 4 * (N // 2)
+    if premix:
+        extra += 4 * (2 * N + 2 * H * R * N + H)
+    return w.batch * (L * (H * per_tok + G * per_grp_tok) + H * per_bh) + extra
 
 
-def decode_algorithmic_bytes(w):
+def decode_algorithmic_bytes(w, premix=False):
     """One m3_decode_step: state h read and written, record (B, X) read and
-    written, step inputs read, y written."""
+    written, step inputs read, y written (plus the pre-mixer's parameters)."""
     e = io_bytes(w)
-    R, P, N = w.rank, w.headdim, w.dstate
+    R, P, N, H = w.rank, w.headdim, w.dstate, w.heads
     per_bh = 8 * N * P + 2 * e * (R * N + R * P) + e * (2 * R * N + R * P) + 4 * (N // 2 + 2) \
         + e * R * P
-    return w.batch * w.heads * per_bh + 4 * w.heads
+    extra = 4 * (2 * N + 2 * H * R * N + H) if premix else 0
+    return w.batch * H * per_bh + 4 * H + extra
 
 
 def _counter_rows(path, kernel_regex=None):
@@ -161,7 +171,51 @@ def bench_prefill(w, steps, warmup, torch, m3, synth, seed=1001):
                 kernel_ms=kms, bytes=nbytes, gbs=nbytes / (kms * 1e-3) / 1e9, inputs=inp)
 
 
-def bench_decode(w, steps, warmup, torch, m3, synth, seed=1004):
+# Option workloads measured beside the plain mixer, at the prefill_bf16 shape.
+OPTION_CASES = {
+    "prefill_bf16+premix": dict(premix=True),
+    "prefill_bf16+groups4+A_t": dict(ngroups=4, a_tok=True),
+    "prefill_bf16+phase_zero": dict(phase="zero"),
+    "prefill_bf16+phase_shuffle": dict(phase="shuffle"),
+    # the same 8192 tokens per head as 8 packed sequences of mixed lengths
+    "prefill_bf16+packed8": dict(packed=[1536, 256, 1024, 768, 2048, 512, 640, 1408]),
+}
+
+
+def _premix(m3, extras):
+    pm = extras["premix"]
+    return m3.Premix(pm["B_norm_w"], pm["C_norm_w"], pm["B_bias"], pm["C_bias"], pm["dt_bias"],
+                     pm["eps"])
+
+
+def bench_prefill_options(w, opts, steps, warmup, torch, m3, synth, seed=1002):
+    ngroups, a_tok = opts.get("ngroups", 0), opts.get("a_tok", False)
+    phase, premix = opts.get("phase", "native"), opts.get("premix", False)
+    lens = opts.get("packed")
+    cu = None
+    if lens is not None:
+        assert sum(lens) == w.batch * w.seqlen
+        w = w.with_(batch=1, seqlen=sum(lens))
+        cu = torch.tensor([0] + [sum(lens[:i + 1]) for i in range(len(lens))], dtype=torch.int32,
+                          device="cuda")
+    inp, ex = synth.make_option_inputs(w, seed, "cuda", ngroups=ngroups, a_per_token=a_tok,
+                                       phase=phase, premix=premix)
+    step = m3.ScanCall(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"],
+                       None if phase == "zero" else inp["theta"], inp["lam"], chunk=w.chunk,
+                       ngroups=ngroups, phase=phase, perm=ex.get("perm"),
+                       premix=_premix(m3, ex) if premix else None, cu_seqlens=cu,
+                       max_seqlen=max(lens) if lens else None)
+    total, kms = time_launches(step, steps, warmup, torch)
+    nbytes = scan_algorithmic_bytes(w, ngroups=ngroups, a_tok=a_tok, phase=phase, premix=premix)
+    if lens is not None:   # one state record per sequence instead of per batch row
+        e = io_bytes(w)
+        nbytes += (len(lens) - 1) * w.heads * (4 * w.dstate * w.headdim
+                                               + e * w.rank * (w.dstate + w.headdim)) + 4 * (len(lens) + 1)
+    return dict(tokens_per_s=w.batch * w.seqlen * steps / total, kernel_ms=kms, bytes=nbytes,
+                gbs=nbytes / (kms * 1e-3) / 1e9)
+
+
+def bench_decode(w, steps, warmup, torch, m3, synth, seed=1004, premix=False):
     """Decode workload: a 1024-token prefill builds the resident state, then
     `steps` single-token steps with fresh inputs, one launch each."""
     pre = synth.make_scan_inputs(w, seed, "cuda")
@@ -169,17 +223,22 @@ def bench_decode(w, steps, warmup, torch, m3, synth, seed=1004):
                            pre["lam"], chunk=w.chunk)
     A = pre["A"]
     del pre
+    pm = None
+    if premix:
+        # the pre-mixer's parameters as the option generator draws them
+        _, ex = synth.make_option_inputs(w.with_(seqlen=1, batch=1), seed, "cuda", premix=True)
+        pm = _premix(m3, ex)
     nsteps = warmup + steps
     ins = [synth.make_decode_inputs(w, seed, s, A, "cuda") for s in range(nsteps)]
     y = torch.empty(w.batch, w.heads, w.rank, w.headdim, dtype=w.torch_dtype, device="cuda")
     calls = iter([m3.DecodeCall(s["x"], s["B"], s["C"], s["dt"], s["A"], s["theta"], s["lam"],
-                                st, y=y) for s in ins])
+                                st, y=y, premix=pm) for s in ins])
 
     def step():
         next(calls)()
 
     total, kms = time_launches(step, steps, warmup, torch)
-    nbytes = decode_algorithmic_bytes(w)
+    nbytes = decode_algorithmic_bytes(w, premix=premix)
     return dict(steps_per_s=steps / total, tokens_per_s=w.batch * steps / total,
                 ms_per_step=1e3 * total / steps, kernel_ms=kms, bytes=nbytes,
                 gbs=nbytes / (kms * 1e-3) / 1e9)
@@ -218,6 +277,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="prefill_bf16")
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-options", action="store_true",
+                    help="skip the option workloads (pre-mixer, groups, phase modes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--decode-steps", type=int, default=1024)
@@ -310,6 +371,22 @@ def main(argv=None):
                          "hbm_gbs": round(rd["gbs"], 1),
                          "hbm_frac": round(rd["gbs"] / HBM_PEAK_GBS, 4),
                          "traffic": load_traffic("decode")}
+        if not args.no_options:
+            progress("timing decode with the pre-mixer")
+            rd = bench_decode(wd, min(args.decode_steps, 256), 8, torch, m3, synth, premix=True)
+            sec["decode+premix"] = {"steps_per_s": round(rd["steps_per_s"], 1),
+                                    "kernel_ms": round(rd["kernel_ms"], 5),
+                                    "hbm_gbs": round(rd["gbs"], 1),
+                                    "hbm_frac": round(rd["gbs"] / HBM_PEAK_GBS, 4)}
+            torch.cuda.empty_cache()
+        wp = synth.WORKLOADS["prefill_bf16"]
+        for name, opts in ({} if args.no_options else OPTION_CASES).items():
+            progress("timing %s" % name)
+            ro = bench_prefill_options(wp, opts, 20, 3, torch, m3, synth)
+            sec[name] = {"tokens_per_s": round(ro["tokens_per_s"], 1),
+                         "kernel_ms": round(ro["kernel_ms"], 5),
+                         "hbm_gbs": round(ro["gbs"], 1),
+                         "hbm_frac": round(ro["gbs"] / HBM_PEAK_GBS, 4)}
         out["secondary"] = sec
         torch.cuda.empty_cache()
 

@@ -61,6 +61,10 @@
  *     Dynamics" (section 5.3, appendix D.4): the phase increments dt_t theta_t
  *     are zeroed, negated, or shuffled across the rotary pairs (pair i uses
  *     theta[..., perm[i]] at every step); the decay is untouched;
+ *   - packed sequences (m3_scan_fwd only): cu_seqlens[batch + 1] gives the
+ *     token offsets of `batch` sequences of different lengths packed along
+ *     one token axis; the token arrays are then [seqlen, nheads, ...] with
+ *     seqlen the total, and each sequence has its own state record;
  *   - pre-mixer: the Towards AI explainer of Mamba-3 (section II) pairs the
  *     mixer with QKNorm-style RMSNorm and channel-wise biases on B and C.
  *     With premix set, dt and lam are raw projections and the mixer uses
@@ -125,6 +129,14 @@ typedef enum {
  *   premix       1 = apply the pre-mixer; B_norm_w, C_norm_w [dstate] (NULL =
  *                all ones), B_bias, C_bias [nheads, rank, dstate] and dt_bias
  *                [nheads] (NULL = zeros), norm_eps >= 0
+ *   cu_seqlens   m3_scan_fwd only (NULL in a decode step): int32 [batch + 1],
+ *                nondecreasing from 0 to seqlen; sequence b is tokens
+ *                cu_seqlens[b] .. cu_seqlens[b+1]-1 of x, B, C, dt, lam,
+ *                theta, y (and of A when it is per token, [seqlen, nheads]).
+ *                max_seqlen bounds every sequence's length (it sizes the
+ *                launch).  Offsets are clamped into [0, seqlen] and lengths
+ *                to max_seqlen on the device: bad entries give wrong
+ *                results, never accesses outside the arrays.
  */
 typedef struct {
     int64_t ngroups;
@@ -136,6 +148,8 @@ typedef struct {
     const float *B_norm_w, *C_norm_w;
     const float *B_bias, *C_bias;
     const float *dt_bias;
+    const int32_t *cu_seqlens;
+    int64_t max_seqlen;
 } m3_options;
 
 /*

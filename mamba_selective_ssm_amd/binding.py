@@ -18,6 +18,9 @@ decode calls:
     ngroups=G      B, C given per head group: [Bt, L, G, R, N] (decode [Bt, G, R, N])
     phase          "native" | "zero" | "reverse" | "shuffle"; perm: int32 [N/2]
     premix         a Premix: dt and lam are raw, B and C RMS-normalised
+    cu_seqlens     (scan only) int32 [nseq + 1]: nseq sequences packed along the
+                   token axis of [1, T, ...] token arrays; max_seqlen bounds
+                   their lengths (default: T); the state record is per sequence
 """
 from __future__ import annotations
 
@@ -44,7 +47,7 @@ class Options(ctypes.Structure):
                 ("phase_mode", ctypes.c_int32), ("phase_perm", _vp),
                 ("premix", ctypes.c_int32), ("norm_eps", ctypes.c_float),
                 ("B_norm_w", _vp), ("C_norm_w", _vp), ("B_bias", _vp), ("C_bias", _vp),
-                ("dt_bias", _vp)]
+                ("dt_bias", _vp), ("cu_seqlens", _vp), ("max_seqlen", ctypes.c_int64)]
 
 
 class Premix(NamedTuple):
@@ -206,25 +209,37 @@ def _stream_handle(stream) -> int:
 
 
 def _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, return_state,
-                  y, state_out, workspace, ngroups=0, phase="native", perm=None, premix=None):
+                  y, state_out, workspace, ngroups=0, phase="native", perm=None, premix=None,
+                  cu_seqlens=None, max_seqlen=None):
     lib = load_library()
-    Bt, L, H, R, P = x.shape
+    Bx, L, H, R, P = x.shape
     N = B.shape[-1]
     G = int(ngroups) if ngroups else H
     io = _io_code(x.dtype)
-    _check(x, "x", (Bt, L, H, R, P), x.dtype)
-    _check(B, "B", (Bt, L, G, R, N), x.dtype)
-    _check(C, "C", (Bt, L, G, R, N), x.dtype)
-    _check(dt, "dt", (Bt, L, H), torch.float32)
-    _check(lam, "lam", (Bt, L, H), torch.float32)
+    if cu_seqlens is not None:
+        if Bx != 1:
+            raise ValueError("packed sequences: token arrays must have a leading dimension of 1")
+        _check(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
+        Bt = cu_seqlens.numel() - 1     # sequences: the state record's batch
+    else:
+        Bt = Bx
+    _check(x, "x", (Bx, L, H, R, P), x.dtype)
+    _check(B, "B", (Bx, L, G, R, N), x.dtype)
+    _check(C, "C", (Bx, L, G, R, N), x.dtype)
+    _check(dt, "dt", (Bx, L, H), torch.float32)
+    _check(lam, "lam", (Bx, L, H), torch.float32)
     if theta is not None or phase != "zero":
-        _check(theta, "theta", (Bt, L, H, N // 2), torch.float32)
+        _check(theta, "theta", (Bx, L, H, N // 2), torch.float32)
     a_tok = A.dim() == 3
-    _check(A, "A", (Bt, L, H) if a_tok else (H,), torch.float32)
+    _check(A, "A", (Bx, L, H) if a_tok else (H,), torch.float32)
     opt, keep = _options(H, N, R, a_tok, ngroups, phase, perm, premix, x.device)
+    if cu_seqlens is not None:
+        opt.cu_seqlens = cu_seqlens.data_ptr()
+        opt.max_seqlen = int(L if max_seqlen is None else max_seqlen)
+        keep.append(cu_seqlens)
     if y is None:
         y = torch.empty_like(x)
-    _check(y, "y", (Bt, L, H, R, P), x.dtype)
+    _check(y, "y", (Bx, L, H, R, P), x.dtype)
     if state is not None:
         _check(state.h, "state.h", (Bt, H, N, P), torch.float32)
         _check(state.B_prev, "state.B_prev", (Bt, H, R, N), x.dtype)
@@ -260,11 +275,13 @@ def m3_scan_fwd(x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
                 return_state: bool = True, y: Optional[torch.Tensor] = None,
                 state_out: Optional[State] = None, workspace: Optional[torch.Tensor] = None,
                 ngroups: int = 0, phase="native", perm: Optional[torch.Tensor] = None,
-                premix: Optional[Premix] = None, stream=None):
-    """Chunked prefill.  Returns (y, State after the last token or None)."""
+                premix: Optional[Premix] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                max_seqlen: Optional[int] = None, stream=None):
+    """Chunked prefill.  Returns (y, State after the last token or None); with
+    packed sequences the State holds one record per sequence."""
     a, y, state_out, _ = _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split,
                                        segments, return_state, y, state_out, workspace,
-                                       ngroups, phase, perm, premix)
+                                       ngroups, phase, perm, premix, cu_seqlens, max_seqlen)
     st = load_library().m3_scan_fwd(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_fwd")
@@ -280,11 +297,12 @@ class ScanCall:
                  chunk: int = 0, p_split: int = 0, segments: int = 0, return_state: bool = True,
                  y: Optional[torch.Tensor] = None, state_out: Optional[State] = None,
                  workspace: Optional[torch.Tensor] = None, ngroups: int = 0, phase="native",
-                 perm: Optional[torch.Tensor] = None, premix: Optional[Premix] = None):
+                 perm: Optional[torch.Tensor] = None, premix: Optional[Premix] = None,
+                 cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None):
         self._keep = (x, B, C, dt, A, theta, lam, state)
         self.args, self.y, self.state_out, self.workspace = _prepare_scan(
             x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, return_state, y,
-            state_out, workspace, ngroups, phase, perm, premix)
+            state_out, workspace, ngroups, phase, perm, premix, cu_seqlens, max_seqlen)
         self._ref = ctypes.byref(self.args)
         self._fn = load_library().m3_scan_fwd
 
@@ -295,10 +313,15 @@ class ScanCall:
         return self.y, self.state_out
 
 
-def m3_scan_workspace_bytes(x, B, *, chunk=0, p_split=0, segments=0) -> int:
+def m3_scan_workspace_bytes(x, B, *, chunk=0, p_split=0, segments=0, cu_seqlens=None,
+                            max_seqlen=None) -> int:
     Bt, L, H, R, P = x.shape
     a = ScanArgs(batch=Bt, seqlen=L, nheads=H, headdim=P, dstate=B.shape[-1], rank=R,
                  chunk=chunk, io_dtype=_io_code(x.dtype), p_split=p_split, segments=segments)
+    if cu_seqlens is not None:
+        a.batch = cu_seqlens.numel() - 1
+        a.opt.cu_seqlens = cu_seqlens.data_ptr()
+        a.opt.max_seqlen = int(L if max_seqlen is None else max_seqlen)
     return int(load_library().m3_scan_workspace_bytes(ctypes.byref(a)))
 
 

@@ -76,21 +76,25 @@ m3_status hip_status(hipError_t e)
 }
 
 // Options common to both entry points: ranges, required pointers, alignment.
-// Fills the kernel-side fields; `ntok` is the number of (batch, token) rows
-// the per-token decay covers (batch * seqlen, or batch for a decode step).
+// Fills the kernel-side fields; `ntok` is the scan's seqlen (the bound of
+// packed-sequence lengths), or -1 for a decode step (no packed sequences).
 m3_status check_options(const m3_options& o, int64_t H, int64_t N, int64_t R, int64_t ntok,
                         m3::OptParams* k)
 {
+    // packed sequences: scan calls only (a decode step passes ntok < 0)
+    if (o.cu_seqlens != nullptr && (ntok < 0 || o.max_seqlen < 0 || o.max_seqlen > ntok))
+        return M3_ERR_OPTION;
     if (o.ngroups < 0 || (o.ngroups > 0 && H > 0 && H % o.ngroups != 0)) return M3_ERR_OPTION;
     if (o.A_per_token != 0 && o.A_per_token != 1) return M3_ERR_OPTION;
     if (o.phase_mode < M3_PHASE_NATIVE || o.phase_mode > M3_PHASE_SHUFFLE) return M3_ERR_OPTION;
     if (o.premix != 0 && o.premix != 1) return M3_ERR_OPTION;
     if (o.premix && !(o.norm_eps >= 0.f && o.norm_eps < 3.0e38f)) return M3_ERR_OPTION;
     if (o.phase_mode == M3_PHASE_SHUFFLE && o.phase_perm == nullptr) return M3_ERR_NULL;
-    const void* ptrs[] = {o.phase_perm, o.B_norm_w, o.C_norm_w, o.B_bias, o.C_bias, o.dt_bias};
+    const void* ptrs[] = {o.phase_perm, o.B_norm_w, o.C_norm_w, o.B_bias, o.C_bias, o.dt_bias,
+                          o.cu_seqlens};
     for (const void* q : ptrs)
         if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
-    (void)N; (void)R; (void)ntok;
+    (void)N; (void)R;
     k->groups = o.ngroups > 0 ? o.ngroups : H;
     k->a_tok = o.A_per_token;
     k->phase = o.phase_mode;
@@ -102,12 +106,15 @@ m3_status check_options(const m3_options& o, int64_t H, int64_t N, int64_t R, in
     k->Bb = o.premix ? o.B_bias : nullptr;
     k->Cb = o.premix ? o.C_bias : nullptr;
     k->dtb = o.premix ? o.dt_bias : nullptr;
+    k->cu = o.cu_seqlens;
+    k->max_len = o.max_seqlen;
     return M3_OK;
 }
 
 // Byte ranges of the option arrays (inputs of the call).
-void option_ranges(const m3_options& o, int64_t H, int64_t N, int64_t R, Range* out)
+void option_ranges(const m3_options& o, int64_t Bt, int64_t H, int64_t N, int64_t R, Range* out)
 {
+    out[6] = range_of(o.cu_seqlens, (Bt + 1) * 4);
     out[0] = range_of(o.phase_mode == M3_PHASE_SHUFFLE ? o.phase_perm : nullptr, (N / 2) * 4);
     out[1] = range_of(o.premix ? o.B_norm_w : nullptr, N * 4);
     out[2] = range_of(o.premix ? o.C_norm_w : nullptr, N * 4);
@@ -143,7 +150,9 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
     if ((int64_t)v->Q * H * wide >= ((int64_t)1 << 31)) return M3_ERR_UNSUPPORTED;
     if (H * wide * 4 >= ((int64_t)1 << 24)) return M3_ERR_UNSUPPORTED;
     const int p_split = (int)(P / v->PS);
-    const int64_t nchunks = (L + v->Q - 1) / v->Q;
+    // packed sequences: the launch is sized for the longest one
+    const int64_t Lrun = a->opt.cu_seqlens != nullptr ? (a->opt.max_seqlen >= 0 ? a->opt.max_seqlen : 0) : L;
+    const int64_t nchunks = (Lrun + v->Q - 1) / v->Q;
     int64_t nseg = a->segments;
     if (nseg == 0) {
         // Fill the chip: about `occ` workgroups per compute unit (256 CUs),
@@ -223,8 +232,9 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     if (nbh == 0) return M3_OK;
 
     m3::OptParams op;
-    const m3_status os = check_options(a->opt, H, N, R, Bt * L, &op);
+    const m3_status os = check_options(a->opt, H, N, R, L, &op);
     if (os != M3_OK) return os;
+    const bool packed = a->opt.cu_seqlens != nullptr;
     const bool st_in = a->h_in || a->B_prev_in || a->x_prev_in;
     const bool st_out = a->h_out || a->B_prev_out || a->x_prev_out;
     if (st_in && !(a->h_in && a->B_prev_in && a->x_prev_in)) return M3_ERR_NULL;
@@ -242,9 +252,9 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
         if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
 
     const int e = io_size(a->io_dtype);
-    const int64_t tok = Bt * L * H;
-    const int64_t tokg = Bt * L * op.groups;
-    Range in[16] = {
+    const int64_t tok = (packed ? 1 : Bt) * L * H;             // token arrays: rows x heads
+    const int64_t tokg = (packed ? 1 : Bt) * L * op.groups;
+    Range in[17] = {
         range_of(a->x, tok * R * P * e),         range_of(a->B, tokg * R * N * e),
         range_of(a->C, tokg * R * N * e),        range_of(a->dt, tok * 4),
         range_of(a->A, (a->opt.A_per_token ? tok : H) * 4),
@@ -252,7 +262,7 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
         range_of(a->lam, tok * 4),               range_of(a->h_in, nbh * N * P * 4),
         range_of(a->B_prev_in, nbh * R * N * e), range_of(a->x_prev_in, nbh * R * P * e),
     };
-    option_ranges(a->opt, H, N, R, in + 10);
+    option_ranges(a->opt, Bt, H, N, R, in + 10);
     const Range out[] = {
         range_of(a->y, tok * R * P * e),         range_of(a->h_out, nbh * N * P * 4),
         range_of(a->B_prev_out, nbh * R * N * e), range_of(a->x_prev_out, nbh * R * P * e),
@@ -298,7 +308,7 @@ m3_status m3_decode_step(const m3_decode_args* a, void* stream)
     const int64_t nbh = Bt * H;
     if (nbh > (int64_t)1 << 30) return M3_ERR_UNSUPPORTED;
     m3::OptParams op;
-    const m3_status os = check_options(a->opt, H, N, R, Bt, &op);
+    const m3_status os = check_options(a->opt, H, N, R, -1, &op);
     if (os != M3_OK) return os;
     if (nbh == 0) return M3_OK;
     const void* theta = a->opt.phase_mode != M3_PHASE_ZERO ? a->theta : nullptr;
@@ -310,13 +320,13 @@ m3_status m3_decode_step(const m3_decode_args* a, void* stream)
         if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
     const int e = io_size(a->io_dtype);
     const int64_t nbg = Bt * op.groups;
-    Range in[13] = {
+    Range in[14] = {
         range_of(a->x, nbh * R * P * e), range_of(a->B, nbg * R * N * e),
         range_of(a->C, nbg * R * N * e), range_of(a->dt, nbh * 4),
         range_of(a->A, (a->opt.A_per_token ? nbh : H) * 4),
         range_of(theta, nbh * (N / 2) * 4), range_of(a->lam, nbh * 4),
     };
-    option_ranges(a->opt, H, N, R, in + 7);
+    option_ranges(a->opt, Bt, H, N, R, in + 7);
     const Range rec[] = {
         range_of(a->h, nbh * N * P * 4), range_of(a->B_prev, nbh * R * N * e),
         range_of(a->x_prev, nbh * R * P * e),

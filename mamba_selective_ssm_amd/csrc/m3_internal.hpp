@@ -20,6 +20,8 @@ struct OptParams {
     const float *Bw, *Cw;  // [N] or NULL (ones)
     const float *Bb, *Cb;  // [H, R, N] or NULL (zeros)
     const float *dtb;      // [H] or NULL (zeros)
+    const int* cu;         // [batch + 1] packed-sequence offsets, or NULL (dense batch)
+    int64_t max_len;       // longest packed sequence
 };
 
 struct DecodeParams {

@@ -265,9 +265,20 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     const int bh = (bid >> 3) / p.p_split * 8 + (bid & 7);
     const int ps = (bid >> 3) % p.p_split;
     if (bh >= p.nbh) return;
-    const int64_t H = p.H, L = p.L, P = p.P;
+    const int64_t H = p.H, P = p.P;
     const int64_t b = bh / H, h = bh % H;
     const int p0 = ps * PS;
+    // This unit's sequence: tokens base .. base+L-1 of the token arrays.  A
+    // dense batch has L = p.L and base = b * p.L; packed sequences take them
+    // from cu_seqlens (clamped into the arrays and to max_seqlen).
+    int64_t L = p.L, base = b * p.L;
+    if (p.opt.cu != nullptr) {
+        int64_t lo = p.opt.cu[b], hi = p.opt.cu[b + 1];
+        lo = lo < 0 ? 0 : (lo > p.L ? p.L : lo);
+        hi = hi < lo ? lo : (hi > p.L ? p.L : hi);
+        base = lo;
+        L = hi - lo < p.opt.max_len ? hi - lo : p.opt.max_len;
+    }
 
     const int64_t nchunks_all = (L + Q - 1) / Q;
     const int64_t c_begin = (int64_t)seg * p.seg_chunks;
@@ -277,8 +288,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     const int64_t G = p.opt.groups;                 // B/C head groups
     const int64_t hg = h / (H / G);                  // this head's group
     const int sDT = (int)H, sTH = (int)(H * NPR), sBN = (int)(G * R * N), sXP = (int)(H * R * P);
-    const int64_t tok0 = (b * L + c_begin * Q) * H + h;
-    const int64_t tok0g = (b * L + c_begin * Q) * G + hg;   // B, C rows
+    const int64_t tok0 = (base + c_begin * Q) * H + h;
+    const int64_t tok0g = (base + c_begin * Q) * G + hg;   // B, C rows
     const int64_t rec_sz = Cf::rec_floats(P);
     float* recs = p.ws + (int64_t)bh * (p.nseg - 1) * rec_sz;   // this (b, h)'s records
 
@@ -580,7 +591,6 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 // Pre-mixer, step 2: wait until every prep wave with pair quads
                 // has published this chunk's partial sums (a bounded wait: the
                 // waves reach it together), then the rows' RMS scales.
-                float gw[2][8];
                 if constexpr (PM) {
                     const int target = WA * pcall;
                     for (int it = 0; it < (1 << 22); ++it) {
@@ -606,24 +616,27 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                             scC[kk][r] = FULL ? rsqrtf(tc * rn + p.opt.eps) : 0.f;
                         }
                     }
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        const f32x4 g0 = *reinterpret_cast<const f32x4*>(sPW + m * N + 8 * qd);
-                        const f32x4 g1 = *reinterpret_cast<const f32x4*>(sPW + m * N + 8 * qd + 4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) { gw[m][e] = g0[e]; gw[m][4 + e] = g1[e]; }
-                    }
                 }
-                // B or C entry e (of 8) of rank r as the mixer uses it
-                auto bval = [&](int kk, int r, int e) -> float {
-                    const float v = st.bq[kk][r].get(e);
-                    if constexpr (!PM) return v;
-                    else return v * scB[kk][r] * gw[0][e] + sPW[2 * N + r * N + 8 * qd + e];
-                };
-                auto cval = [&](int kk, int r, int e) -> float {
-                    const float v = st.cq[kk][r].get(e);
-                    if constexpr (!PM) return v;
-                    else return v * scC[kk][r] * gw[1][e] + sPW[2 * N + (R + r) * N + 8 * qd + e];
+                // The 8 entries of a B (m = 0) or C (m = 1) row piece as the
+                // mixer uses them: raw, or scaled, gained and biased (gains
+                // and biases read from LDS where they are used).
+                auto entries = [&](const IoRow8<io_t>& q, float sc, int m, int r, float (&v)[8]) {
+                    if constexpr (!PM) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = q.get(e);
+                    } else {
+                        const float* gp = sPW + m * N + 8 * qd;
+                        const float* bp = sPW + 2 * N + (m * R + r) * N + 8 * qd;
+                        const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp);
+                        const f32x4 g1 = *reinterpret_cast<const f32x4*>(gp + 4);
+                        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp);
+                        const f32x4 b1 = *reinterpret_cast<const f32x4*>(bp + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[e] = q.get(e) * sc * g0[e] + b0[e];
+                            v[4 + e] = q.get(4 + e) * sc * g1[e] + b1[e];
+                        }
+                    }
                 };
 #pragma unroll
                 for (int kk = 0; kk < TPL; ++kk) {
@@ -637,20 +650,22 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                         for (int r = 0; r < R; ++r) {
                             const int rho = j * R + r;
                             // R(Phi)^T applied to each pair
-                            float o[8];
+                            float o[8], v[8];
+                            entries(st.bq[kk][r], PM ? scB[kk][r] : 1.f, 0, r, v);
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const float b0 = ok ? bval(kk, r, 2 * e) : 0.f;
-                                const float b1 = ok ? bval(kk, r, 2 * e + 1) : 0.f;
+                                const float b0 = ok ? v[2 * e] : 0.f;
+                                const float b1 = ok ? v[2 * e + 1] : 0.f;
                                 o[2 * e] = cs[e] * b0 + sn[e] * b1;
                                 o[2 * e + 1] = cs[e] * b1 - sn[e] * b0;
                             }
                             lds_store8(sB + rho * LDB + 8 * qd, o);
                             if constexpr (FULL) {
+                                entries(st.cq[kk][r], PM ? scC[kk][r] : 1.f, 1, r, v);
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) {
-                                    const float c0 = ok ? cval(kk, r, 2 * e) : 0.f;
-                                    const float c1 = ok ? cval(kk, r, 2 * e + 1) : 0.f;
+                                    const float c0 = ok ? v[2 * e] : 0.f;
+                                    const float c1 = ok ? v[2 * e + 1] : 0.f;
                                     o[2 * e] = cs[e] * c0 + sn[e] * c1;
                                     o[2 * e + 1] = cs[e] * c1 - sn[e] * c0;
                                 }
@@ -735,7 +750,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                     }
                 }
                 if (L > 0) {
-                    float d0 = p.dt[(b * L) * H + h], l0 = p.lam[(b * L) * H + h];
+                    float d0 = p.dt[base * H + h], l0 = p.lam[base * H + h];
                     if constexpr (PM) {
                         d0 = softplus_f(d0 + (p.opt.dtb != nullptr ? p.opt.dtb[h] : 0.f));
                         l0 = sigmoid_f(l0);
@@ -1206,8 +1221,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             io_t* xo = reinterpret_cast<io_t*>(p.xp_out) + (int64_t)bh * R * P;
             const io_t* Bi = reinterpret_cast<const io_t*>(p.Bp_in);
             const io_t* xi = reinterpret_cast<const io_t*>(p.xp_in);
-            const int64_t tl = (b * L + (L - 1)) * H + h;
-            const int64_t tlg = (b * L + (L - 1)) * G + hg;
+            const int64_t tl = (base + (L - 1)) * H + h;
+            const int64_t tlg = (base + (L - 1)) * G + hg;
             if (PM && L > 0) {
                 // the last token's B through the pre-mixer (wave 0)
                 if (wv == 0) {

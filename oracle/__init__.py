@@ -236,3 +236,34 @@ def decode_step(x, Bm, Cm, dt, A, theta, lam, h, Bprev, xprev, *, ngroups=None,
     if rc != 0:
         raise RuntimeError("m3o_decode_step failed with code %d" % rc)
     return y, h, Bprev, xprev
+
+
+def scan_packed(x, Bm, Cm, dt, A, theta, lam, cu_seqlens, h0=None, Bprev=None, xprev=None,
+                threads=None, **options):
+    """Packed sequences: sequence i is tokens cu_seqlens[i] .. cu_seqlens[i+1]-1
+    of token arrays with a leading dimension of 1 ([1, T, ...]; A per token is
+    [1, T, H]).  Each sequence is an independent scan from its own state record
+    (h0, Bprev, xprev have one row per sequence); returns y [1, T, H, R, P] and
+    the per-sequence records, as ``scan`` does for a dense batch."""
+    cu = [int(v) for v in np.asarray(cu_seqlens).ravel()]
+    nseq = len(cu) - 1
+    x = np.asarray(x, dtype=np.float64)
+    _, T, H, R, P = x.shape
+    N = np.asarray(Bm).shape[-1]
+    if cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("oracle: cu_seqlens must rise from 0 to the packed length")
+    A = np.asarray(A, dtype=np.float64)
+    y = np.empty((1, T, H, R, P))
+    hs = np.empty((nseq, H, N, P))
+    Bs = np.empty((nseq, H, R, N))
+    xs = np.empty((nseq, H, R, P))
+    for i in range(nseq):
+        sl = slice(cu[i], cu[i + 1])
+        take = lambda a: None if a is None else np.asarray(a)[i:i + 1]
+        yi, hs[i:i + 1], Bs[i:i + 1], xs[i:i + 1] = scan(
+            x[:, sl], np.asarray(Bm)[:, sl], np.asarray(Cm)[:, sl], np.asarray(dt)[:, sl],
+            A[:, sl] if A.ndim == 3 else A,
+            np.asarray(theta)[:, sl], np.asarray(lam)[:, sl],
+            h0=take(h0), Bprev=take(Bprev), xprev=take(xprev), threads=threads, **options)
+        y[:, sl] = yi
+    return y, hs, Bs, xs

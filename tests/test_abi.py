@@ -123,6 +123,11 @@ def run_scan(lib, a):
     (dict(theta=None, phase_mode=1, x=FAKE + 8), -5),        # zero phase: theta may be NULL
     (dict(theta=None, phase_mode=2, x=FAKE + 8), -1),
     (dict(premix=1, C_bias=FAKE + (7 << 32)), -7),           # y overlaps the C bias
+    # packed sequences
+    (dict(cu_seqlens=FAKE + (42 << 32), max_seqlen=11), -9),  # longer than the packed axis
+    (dict(cu_seqlens=FAKE + (42 << 32), max_seqlen=-1), -9),
+    (dict(cu_seqlens=FAKE + (42 << 32) + 4, max_seqlen=10), -5),
+    (dict(cu_seqlens=FAKE + (7 << 32), max_seqlen=10), -7),   # y overlaps the offsets
 ])
 def test_scan_validation_codes(lib, kw, code):
     assert run_scan(lib, scan_args(**kw)) == code
@@ -164,6 +169,7 @@ def decode_args(**kw):
     (dict(theta=None, h=FAKE + (7 << 32) + 4), -1),
     (dict(premix=1, dt_bias=FAKE + (10 << 32)), -7),                # y overlaps the dt bias
     (dict(premix=1, B_bias=FAKE + (7 << 32)), -7),                  # state overlaps the B bias
+    (dict(cu_seqlens=FAKE + (20 << 32), max_seqlen=1), -9),         # scans only
 ])
 def test_decode_validation_codes(lib, kw, code):
     assert lib.m3_decode_step(ctypes.byref(decode_args(**kw)), None) == code

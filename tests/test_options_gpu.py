@@ -189,3 +189,62 @@ def test_prefill_then_decode_with_options(io):
     ey, eh = rel_err(f64(torch.cat(ys, 1)), yr), rel_err(f64(st.h), hr)
     say("   rel err y %.3e state %.3e" % (ey, eh))
     assert ey <= TOL[io] and eh <= TOL[io]
+
+
+PACKED_LENGTHS = [0, 1, 63, 64, 65, 300, 17, 129, 2, 200]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("segments,opts", [
+    (0, {}), (3, {}),
+    (2, dict(ngroups=2, a_tok=True, premix=True, phase="reverse")),
+])
+def test_packed_sequences(io, segments, opts):
+    """Sequences of different lengths (one empty) packed along the token axis,
+    each with its own state record."""
+    lens = PACKED_LENGTHS
+    T = sum(lens)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=DEV)
+    ngroups, a_tok = opts.get("ngroups", 0), opts.get("a_tok", False)
+    phase, premix = opts.get("phase", "native"), opts.get("premix", False)
+    w = workload(1, T, 4, 2, 32, 64, io=io, dt_mu=-1.0)
+    say("case packed %s seg=%d %s lengths=%s" % (io, segments, opts, lens))
+    inp, ex = synth.make_option_inputs(w, 440 + segments, DEV, ngroups=ngroups, a_per_token=a_tok,
+                                       phase=phase, premix=premix)
+    st = random_state(w.with_(batch=len(lens)), 441, DEV)
+    y, so = m3_scan_fwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
+                        inp["lam"], State(*st), segments=segments, ngroups=ngroups, phase=phase,
+                        perm=ex.get("perm"), premix=premix_obj(ex), cu_seqlens=cu,
+                        max_seqlen=max(lens))
+    torch.cuda.synchronize()
+    yr, hr, br, xr = oracle.scan_packed(f64(inp["x"]), f64(inp["B"]), f64(inp["C"]),
+                                        f64(inp["dt"]), f64(inp["A"]), f64(inp["theta"]),
+                                        f64(inp["lam"]), cu.cpu().numpy(), h0=f64(st[0]),
+                                        Bprev=f64(st[1]), xprev=f64(st[2]),
+                                        **oracle_kw(ex, ngroups, phase))
+    tol = TOL[io]
+    ey, eh = rel_err(f64(y), yr), rel_err(f64(so.h), hr)
+    say("   rel err y %.3e state %.3e" % (ey, eh))
+    assert ey <= tol and eh <= tol
+    if premix:
+        assert rel_err(f64(so.B_prev), br) <= tol
+    else:
+        np.testing.assert_array_equal(f64(so.B_prev), br)
+    np.testing.assert_array_equal(f64(so.x_prev), xr)
+
+
+def test_packed_equal_lengths_match_dense_batch():
+    """Packing equal-length sequences gives the dense batch's results bit for bit."""
+    w = workload(3, 257, 4, 1, 64, 64, io="bf16")
+    say("case packed == dense")
+    inp = synth.make_scan_inputs(w, 450, DEV)
+    y, so = m3_scan_fwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
+                        inp["lam"], segments=3)
+    pk = {k: (v if k == "A" else v.reshape((1, -1) + tuple(v.shape[2:])).contiguous())
+          for k, v in inp.items()}
+    cu = torch.arange(0, 4 * 257, 257, dtype=torch.int32, device=DEV)
+    yp, sp = m3_scan_fwd(pk["x"], pk["B"], pk["C"], pk["dt"], pk["A"], pk["theta"], pk["lam"],
+                         segments=3, cu_seqlens=cu, max_seqlen=257)
+    torch.cuda.synchronize()
+    assert torch.equal(yp.reshape(y.shape), y)
+    assert torch.equal(sp.h, so.h)

@@ -588,3 +588,39 @@ def test_premix_scan_consumes_torch_maps():
     yb, _, _, _ = oracle.scan(x, Bg * scale, Cg / scale, dt_raw, A, theta, lam_raw, ngroups=G,
                               premix=pm0)
     assert rel_err(yb, ya) < 1e-12
+
+
+# Packed sequences are independent scans: equal lengths give the dense batch,
+# and reordering the sequences reorders the outputs and records.
+def test_packed_sequences_match_dense_batch_and_reorder():
+    rng = np.random.default_rng(28)
+    Bt, L, H, R, P, N = 3, 11, 2, 2, 3, 6
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N)
+    h0 = rng.standard_normal((Bt, H, N, P))
+    Bp = rng.standard_normal((Bt, H, R, N))
+    xp = rng.standard_normal((Bt, H, R, P))
+    pack = lambda a: a.reshape((1, Bt * L) + a.shape[2:])
+    cu = np.arange(Bt + 1) * L
+    yd, hd, Bd, xd = oracle.scan(x, Bm, Cm, dt, A, theta, lam, h0=h0, Bprev=Bp, xprev=xp)
+    yp, hp, Bpk, xpk = oracle.scan_packed(pack(x), pack(Bm), pack(Cm), pack(dt), A, pack(theta),
+                                          pack(lam), cu, h0=h0, Bprev=Bp, xprev=xp)
+    np.testing.assert_array_equal(yp.reshape(yd.shape), yd)
+    np.testing.assert_array_equal(hp, hd)
+    np.testing.assert_array_equal(Bpk, Bd)
+    # ragged lengths (one empty), then the same sequences in reverse order
+    lens = [5, 0, 9, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    xx, BB, CC, dd, _, tt, ll = rand_inputs(rng, 1, T, H, R, P, N)
+    hh = rng.standard_normal((4, H, N, P))
+    y1, h1, _, _ = oracle.scan_packed(xx, BB, CC, dd, A, tt, ll, cu, h0=hh,
+                                      Bprev=np.zeros((4, H, R, N)), xprev=np.zeros((4, H, R, P)))
+    order = [3, 2, 1, 0]
+    idx = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in order]).astype(int)
+    cu_r = np.concatenate([[0], np.cumsum([lens[i] for i in order])])
+    y2, h2, _, _ = oracle.scan_packed(xx[:, idx], BB[:, idx], CC[:, idx], dd[:, idx], A,
+                                      tt[:, idx], ll[:, idx], cu_r, h0=hh[order],
+                                      Bprev=np.zeros((4, H, R, N)), xprev=np.zeros((4, H, R, P)))
+    np.testing.assert_array_equal(y2, y1[:, idx])
+    np.testing.assert_array_equal(h2, h1[order])
+    np.testing.assert_array_equal(h1[1], hh[1])      # the empty sequence passes its state through
