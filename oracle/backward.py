@@ -1,0 +1,67 @@
+"""fp64 oracle for the gradient of the Mamba-3 scan -- TEST INFRASTRUCTURE ONLY
+(loaded only by tests/, the smoke check and the benchmark's CPU leg).
+
+The forward recurrence is written out step by step in plain float64 PyTorch
+on the CPU (the same definition as m3_oracle.c: Mamba-3 summary on
+b-lab.team, section 1 recurrence, section 2 block rotations R(dt theta_i) on
+adjacent rows, section 3 MIMO; the rotation also carries the previous
+endpoint), and its gradient is taken by reverse-mode automatic
+differentiation of that loop: the gradient of L = sum(dy * y) + sum(dh * h_L)
+with respect to every input, the decay rate A and the state record.
+
+Layouts as the scan: x [Bt,L,H,R,P], Bm/Cm [Bt,L,H,R,N], dt/lam [Bt,L,H],
+theta [Bt,L,H,N/2], A [H]; h0 [Bt,H,N,P], Bprev [Bt,H,R,N], xprev [Bt,H,R,P].
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def forward_torch(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev):
+    """y [Bt,L,H,R,P] and h_L, stepping the recurrence on float64 tensors."""
+    Bt, L, H, R, P = x.shape
+    N = Bm.shape[-1]
+    h = h0                                               # [Bt,H,N,P]
+    Uprev = torch.einsum("bhrn,bhrp->bhnp", Bprev, xprev)
+    ys = []
+    for t in range(L):
+        d = dt[:, t]                                     # [Bt,H]
+        alpha = torch.exp(d * A)
+        beta = (1.0 - lam[:, t]) * d * alpha
+        gamma = lam[:, t] * d
+        U = torch.einsum("bhrn,bhrp->bhnp", Bm[:, t], x[:, t])
+        a = alpha[..., None, None] * h + beta[..., None, None] * Uprev
+        phi = d[..., None] * theta[:, t]                 # [Bt,H,N/2]
+        c, s = torch.cos(phi)[..., None], torch.sin(phi)[..., None]
+        a0, a1 = a[:, :, 0::2], a[:, :, 1::2]
+        r0 = c * a0 - s * a1                             # R(phi) on rows (2i, 2i+1)
+        r1 = s * a0 + c * a1
+        ra = torch.stack([r0, r1], dim=3).reshape(Bt, H, N, P)
+        h = ra + gamma[..., None, None] * U
+        ys.append(torch.einsum("bhrn,bhnp->bhrp", Cm[:, t], h))
+        Uprev = U
+    y = torch.stack(ys, dim=1) if ys else x.new_zeros((Bt, 0, H, R, P))
+    return y, h
+
+
+def scan_backward(x, Bm, Cm, dt, A, theta, lam, dy, dh=None, h0=None, Bprev=None, xprev=None):
+    """Gradients of sum(dy * y) + sum(dh * h_L).  Returns a dict of float64
+    numpy arrays: dx, dB, dC, ddt, dA, dtheta, dlam, dh0, dBprev, dxprev."""
+    t64 = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
+    x, Bm, Cm, dt, A, theta, lam = map(t64, (x, Bm, Cm, dt, A, theta, lam))
+    Bt, L, H, R, P = x.shape
+    N = Bm.shape[-1]
+    z = lambda *s: np.zeros(s)
+    h0 = t64(z(Bt, H, N, P) if h0 is None else h0)
+    Bprev = t64(z(Bt, H, R, N) if Bprev is None else Bprev)
+    xprev = t64(z(Bt, H, R, P) if xprev is None else xprev)
+    y, hL = forward_torch(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev)
+    loss = (y * torch.as_tensor(np.asarray(dy, dtype=np.float64))).sum()
+    if dh is not None:
+        loss = loss + (hL * torch.as_tensor(np.asarray(dh, dtype=np.float64))).sum()
+    names = ["dx", "dB", "dC", "ddt", "dA", "dtheta", "dlam", "dh0", "dBprev", "dxprev"]
+    leaves = [x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev]
+    grads = torch.autograd.grad(loss, leaves, allow_unused=True)
+    return {n: (np.zeros(v.shape) if g is None else g.detach().numpy())
+            for n, v, g in zip(names, leaves, grads)}

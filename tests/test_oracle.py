@@ -624,3 +624,52 @@ def test_packed_sequences_match_dense_batch_and_reorder():
     np.testing.assert_array_equal(y2, y1[:, idx])
     np.testing.assert_array_equal(h2, h1[order])
     np.testing.assert_array_equal(h1[1], hh[1])      # the empty sequence passes its state through
+
+
+# ===========================================================================
+# Gradient oracle (oracle/backward.py): its forward equals the C oracle, and
+# every gradient matches central finite differences of the C oracle's loss.
+def _bwd_case(rng, Bt=1, L=7, H=2, R=2, P=3, N=4):
+    x, Bm, Cm, dt, A, theta, lam = rand_inputs(rng, Bt, L, H, R, P, N)
+    h0 = rng.standard_normal((Bt, H, N, P))
+    Bp = rng.standard_normal((Bt, H, R, N))
+    xp = rng.standard_normal((Bt, H, R, P))
+    dy = rng.standard_normal((Bt, L, H, R, P))
+    dh = rng.standard_normal((Bt, H, N, P))
+    return [x, Bm, Cm, dt, A, theta, lam, h0, Bp, xp], dy, dh
+
+
+def test_backward_forward_matches_c_oracle():
+    import torch
+    from oracle.backward import forward_torch
+    rng = np.random.default_rng(31)
+    ins, _, _ = _bwd_case(rng, Bt=2, L=13, H=2, R=2, P=3, N=6)
+    y_c, h_c, _, _ = oracle.scan(*ins[:7], h0=ins[7], Bprev=ins[8], xprev=ins[9])
+    y_t, h_t = forward_torch(*[torch.tensor(a) for a in ins])
+    assert rel_err(y_t.numpy(), y_c) < 1e-13
+    assert rel_err(h_t.numpy(), h_c) < 1e-13
+
+
+def test_backward_matches_finite_differences():
+    from oracle.backward import scan_backward
+    rng = np.random.default_rng(32)
+    ins, dy, dh = _bwd_case(rng)
+    g = scan_backward(*ins[:7], dy, dh, h0=ins[7], Bprev=ins[8], xprev=ins[9])
+
+    def loss(args):
+        y, hL, _, _ = oracle.scan(*args[:7], h0=args[7], Bprev=args[8], xprev=args[9])
+        return float(np.sum(y * dy) + np.sum(hL * dh))
+    names = ["dx", "dB", "dC", "ddt", "dA", "dtheta", "dlam", "dh0", "dBprev", "dxprev"]
+    eps = 1e-6
+    for k, name in enumerate(names):
+        fd = np.zeros_like(ins[k])
+        it = np.nditer(ins[k], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [a.copy() for a in ins]
+            minus = [a.copy() for a in ins]
+            plus[k][idx] += eps
+            minus[k][idx] -= eps
+            fd[idx] = (loss(plus) - loss(minus)) / (2 * eps)
+        err = np.max(np.abs(fd - g[name])) / max(np.max(np.abs(g[name])), 1e-12)
+        assert err < 1e-6, (name, err)
