@@ -54,6 +54,15 @@ def scan_algorithmic_bytes(w, L=None, ngroups=0, a_tok=False, phase="native", pr
     return w.batch * (L * (H * per_tok + G * per_grp_tok) + H * per_bh) + extra
 
 
+def bwd_algorithmic_bytes(w):
+    """One m3_scan_bwd: x, B, C, dy, dt, theta, lam read once; dx, dB, dC,
+    ddt, dtheta, dlam written once in float32 (checkpoint traffic excluded)."""
+    e = io_bytes(w)
+    R, P, N, H = w.rank, w.headdim, w.dstate, w.heads
+    per_tok = e * (2 * R * P + 2 * R * N) + 4 * (N // 2 + 2) + 4 * (R * P + 2 * R * N + N // 2 + 2)
+    return w.batch * w.seqlen * H * per_tok + 8 * H
+
+
 def decode_algorithmic_bytes(w, premix=False):
     """One m3_decode_step: state h read and written, record (B, X) read and
     written, step inputs read, y written (plus the pre-mixer's parameters)."""
@@ -211,6 +220,18 @@ def bench_prefill_options(w, opts, steps, warmup, torch, m3, synth, seed=1002):
         e = io_bytes(w)
         nbytes += (len(lens) - 1) * w.heads * (4 * w.dstate * w.headdim
                                                + e * w.rank * (w.dstate + w.headdim)) + 4 * (len(lens) + 1)
+    return dict(tokens_per_s=w.batch * w.seqlen * steps / total, kernel_ms=kms, bytes=nbytes,
+                gbs=nbytes / (kms * 1e-3) / 1e9)
+
+
+def bench_backward(w, steps, warmup, torch, m3, synth, seed=1003):
+    inp = synth.make_scan_inputs(w, seed, "cuda")
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    dy = torch.randn(inp["x"].shape, generator=g, device="cuda").to(w.torch_dtype)
+    step = m3.ScanBwdCall(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
+                          inp["lam"], dy, state_grads=False)
+    total, kms = time_launches(step, steps, warmup, torch)
+    nbytes = bwd_algorithmic_bytes(w)
     return dict(tokens_per_s=w.batch * w.seqlen * steps / total, kernel_ms=kms, bytes=nbytes,
                 gbs=nbytes / (kms * 1e-3) / 1e9)
 
@@ -387,6 +408,14 @@ def main(argv=None):
                          "kernel_ms": round(ro["kernel_ms"], 5),
                          "hbm_gbs": round(ro["gbs"], 1),
                          "hbm_frac": round(ro["gbs"] / HBM_PEAK_GBS, 4)}
+        for name in ("prefill_bf16", "mimo_prefill_bf16"):
+            progress("timing the backward on %s" % name)
+            rb = bench_backward(synth.WORKLOADS[name], 3, 1, torch, m3, synth)
+            sec["backward:" + name] = {"tokens_per_s": round(rb["tokens_per_s"], 1),
+                                       "kernel_ms": round(rb["kernel_ms"], 4),
+                                       "hbm_gbs": round(rb["gbs"], 1),
+                                       "hbm_frac": round(rb["gbs"] / HBM_PEAK_GBS, 4)}
+            torch.cuda.empty_cache()
         out["secondary"] = sec
         torch.cuda.empty_cache()
 

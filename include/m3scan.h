@@ -214,6 +214,43 @@ typedef struct {
     m3_options opt;
 } m3_decode_args;
 
+/*
+ * Arguments of m3_scan_bwd: the gradient of a scan (m3_scan_fwd without
+ * options) for training.  Given dy = dLoss/dy and optionally dh_out =
+ * dLoss/dh_L, it returns the gradients of Loss = sum(dy * y) + sum(dh_out *
+ * h_L) with respect to every input.  The recurrence is differentiated step by
+ * step (the adjoint runs backward in time; forward states are recomputed from
+ * checkpoints kept in the workspace).
+ *   inputs   as m3_scan_args: x, B, C (io dtype), dt, A [nheads], theta, lam
+ *            (float32), optional state record h_in, B_prev_in, x_prev_in
+ *   dy       [batch, seqlen, nheads, rank, headdim] io dtype
+ *   dh_out   [batch, nheads, dstate, headdim] float32, or NULL (zero)
+ *   outputs  float32, same shapes as their inputs: dx, dB, dC, ddt, dtheta,
+ *            dlam, dA [nheads]; optionally all of dh_in [batch, nheads,
+ *            dstate, headdim], dB_prev [batch, nheads, rank, dstate],
+ *            dx_prev [batch, nheads, rank, headdim] (gradients with respect to
+ *            the input state record, zero record when none was given)
+ *   workspace  m3_scan_bwd_workspace_bytes(args) bytes, 256-byte aligned
+ * Supported: dstate even and <= 128, headdim 16, 32 or 64, rank 1, 2 or 4.
+ * Every output is written (no accumulation into the caller's buffers); the
+ * result is deterministic.
+ */
+typedef struct {
+    int64_t batch, seqlen, nheads, headdim, dstate, rank;
+    int32_t io_dtype;
+    int32_t reserved;
+    const void *x, *B, *C;
+    const float *dt, *A, *theta, *lam;
+    const float *h_in;
+    const void *B_prev_in, *x_prev_in;
+    const void *dy;
+    const float *dh_out;
+    float *dx, *dB, *dC, *ddt, *dA, *dtheta, *dlam;
+    float *dh_in, *dB_prev, *dx_prev;
+    void *workspace;
+    size_t workspace_bytes;
+} m3_scan_bwd_args;
+
 /* Chunked prefill: y and (optionally) the state record after the last token.
  * Enqueued on `stream`; returns before the work completes. */
 m3_status m3_scan_fwd(const m3_scan_args *args, void *stream);
@@ -222,6 +259,16 @@ m3_status m3_scan_fwd(const m3_scan_args *args, void *stream);
  * runs in a single pass).  Depends only on sizes, dtype, chunk, p_split and
  * segments.  Returns 0 for arguments that m3_scan_fwd would reject. */
 size_t m3_scan_workspace_bytes(const m3_scan_args *args);
+
+/* Gradient of a scan.  Enqueued on `stream`; allocates nothing. */
+m3_status m3_scan_bwd(const m3_scan_bwd_args *args, void *stream);
+
+/* Workspace bytes m3_scan_bwd needs (checkpointed states every few steps per
+ * (batch, head)); 0 for arguments it would reject. */
+size_t m3_scan_bwd_workspace_bytes(const m3_scan_bwd_args *args);
+
+/* 1 when (dstate, headdim, rank, io_dtype) is supported by m3_scan_bwd. */
+int m3_scan_bwd_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t io_dtype);
 
 /* One decode step, state record updated in place.  Enqueued on `stream`. */
 m3_status m3_decode_step(const m3_decode_args *args, void *stream);

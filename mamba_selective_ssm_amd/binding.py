@@ -87,6 +87,21 @@ class DecodeArgs(ctypes.Structure):
                 ("opt", Options)]
 
 
+class ScanBwdArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("rank", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("x", _vp), ("B", _vp), ("C", _vp),
+                ("dt", _vp), ("A", _vp), ("theta", _vp), ("lam", _vp),
+                ("h_in", _vp), ("B_prev_in", _vp), ("x_prev_in", _vp),
+                ("dy", _vp), ("dh_out", _vp),
+                ("dx", _vp), ("dB", _vp), ("dC", _vp), ("ddt", _vp), ("dA", _vp),
+                ("dtheta", _vp), ("dlam", _vp),
+                ("dh_in", _vp), ("dB_prev", _vp), ("dx_prev", _vp),
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class M3Error(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -107,6 +122,13 @@ def load_library():
         lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
         lib.m3_scan_fwd.restype = ctypes.c_int
         lib.m3_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp]
+        lib.m3_scan_bwd.restype = ctypes.c_int
+        lib.m3_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _vp]
+        lib.m3_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.m3_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ScanBwdArgs)]
+        lib.m3_scan_bwd_supported.restype = ctypes.c_int
+        lib.m3_scan_bwd_supported.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_int32]
         lib.m3_decode_step.restype = ctypes.c_int
         lib.m3_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         lib.m3_scan_workspace_bytes.restype = ctypes.c_size_t
@@ -385,3 +407,96 @@ class DecodeCall:
         if st != 0:
             raise M3Error(st, "m3_decode_step")
         return self.y
+
+
+class ScanGrads(NamedTuple):
+    """Gradients from m3_scan_bwd (float32, shapes of the inputs)."""
+    dx: torch.Tensor
+    dB: torch.Tensor
+    dC: torch.Tensor
+    ddt: torch.Tensor
+    dA: torch.Tensor
+    dtheta: torch.Tensor
+    dlam: torch.Tensor
+    dh_in: Optional[torch.Tensor]
+    dB_prev: Optional[torch.Tensor]
+    dx_prev: Optional[torch.Tensor]
+
+
+def m3_scan_bwd_supported(dstate: int, headdim: int, rank: int, io_dtype: int) -> bool:
+    return bool(load_library().m3_scan_bwd_supported(dstate, headdim, rank, io_dtype))
+
+
+def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace):
+    lib = load_library()
+    Bt, L, H, R, P = x.shape
+    N = B.shape[-1]
+    io = _io_code(x.dtype)
+    for t, n, shp, dt_ in ((x, "x", (Bt, L, H, R, P), x.dtype), (B, "B", (Bt, L, H, R, N), x.dtype),
+                           (C, "C", (Bt, L, H, R, N), x.dtype), (dt, "dt", (Bt, L, H), torch.float32),
+                           (lam, "lam", (Bt, L, H), torch.float32),
+                           (theta, "theta", (Bt, L, H, N // 2), torch.float32),
+                           (A, "A", (H,), torch.float32), (dy, "dy", (Bt, L, H, R, P), x.dtype)):
+        _check(t, n, shp, dt_)
+    if state is not None:
+        _check(state.h, "state.h", (Bt, H, N, P), torch.float32)
+        _check(state.B_prev, "state.B_prev", (Bt, H, R, N), x.dtype)
+        _check(state.x_prev, "state.x_prev", (Bt, H, R, P), x.dtype)
+    if dh_out is not None:
+        _check(dh_out, "dh_out", (Bt, H, N, P), torch.float32)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    g = ScanGrads(torch.empty(x.shape, **f32), torch.empty(B.shape, **f32),
+                  torch.empty(C.shape, **f32), torch.empty(dt.shape, **f32),
+                  torch.empty(A.shape, **f32), torch.empty(theta.shape, **f32),
+                  torch.empty(lam.shape, **f32),
+                  torch.empty(Bt, H, N, P, **f32) if state_grads else None,
+                  torch.empty(Bt, H, R, N, **f32) if state_grads else None,
+                  torch.empty(Bt, H, R, P, **f32) if state_grads else None)
+    a = ScanBwdArgs(batch=Bt, seqlen=L, nheads=H, headdim=P, dstate=N, rank=R, io_dtype=io,
+                    x=_ptr(x), B=_ptr(B), C=_ptr(C), dt=_ptr(dt), A=_ptr(A), theta=_ptr(theta),
+                    lam=_ptr(lam),
+                    h_in=_ptr(state.h) if state else None,
+                    B_prev_in=_ptr(state.B_prev) if state else None,
+                    x_prev_in=_ptr(state.x_prev) if state else None,
+                    dy=_ptr(dy), dh_out=_ptr(dh_out),
+                    dx=_ptr(g.dx), dB=_ptr(g.dB), dC=_ptr(g.dC), ddt=_ptr(g.ddt), dA=_ptr(g.dA),
+                    dtheta=_ptr(g.dtheta), dlam=_ptr(g.dlam), dh_in=_ptr(g.dh_in),
+                    dB_prev=_ptr(g.dB_prev), dx_prev=_ptr(g.dx_prev))
+    need = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(a))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=x.device)
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a, g, workspace
+
+
+def m3_scan_bwd(x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
+                dh_out: Optional[torch.Tensor] = None, *, state_grads: bool = True,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> ScanGrads:
+    """Gradients of sum(dy * y) + sum(dh_out * h_L) of m3_scan_fwd (no options)
+    with respect to every input; ``state_grads`` also returns those of the
+    input state record (zero record when ``state`` is None)."""
+    a, g, _ = _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace)
+    st = load_library().m3_scan_bwd(ctypes.byref(a), _stream_handle(stream))
+    if st != 0:
+        raise M3Error(st, "m3_scan_bwd")
+    return g
+
+
+class ScanBwdCall:
+    """An m3_scan_bwd call marshalled once; calling it re-issues it."""
+
+    def __init__(self, x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
+                 dh_out: Optional[torch.Tensor] = None, *, state_grads: bool = True,
+                 workspace: Optional[torch.Tensor] = None):
+        self._keep = (x, B, C, dt, A, theta, lam, dy, state, dh_out)
+        self.args, self.grads, self.workspace = _prepare_bwd(x, B, C, dt, A, theta, lam, dy,
+                                                             state, dh_out, state_grads, workspace)
+        self._ref = ctypes.byref(self.args)
+        self._fn = load_library().m3_scan_bwd
+
+    def __call__(self, stream=None):
+        st = self._fn(self._ref, _stream_handle(stream))
+        if st != 0:
+            raise M3Error(st, "m3_scan_bwd")
+        return self.grads

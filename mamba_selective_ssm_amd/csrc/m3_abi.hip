@@ -176,9 +176,122 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
     return M3_OK;
 }
 
+// Backward: sub-block length TB, sub-blocks per checkpoint K, checkpoints per
+// (b, h) and the workspace carve-up (checkpoints, scratch, dA shares).
+struct BwdPlan {
+    int TB, K;
+    int64_t nsup;
+    size_t unit_floats, ck_bytes, scr_bytes, part_bytes, ws;
+};
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+m3_status plan_bwd(const m3_scan_bwd_args* a, BwdPlan* out)
+{
+    if (a == nullptr) return M3_ERR_NULL;
+    const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
+    const int64_t P = a->headdim, N = a->dstate, R = a->rank;
+    if (Bt < 0 || L < 0 || H < 0 || P < 1 || N < 1 || R < 1 || (N % 2) != 0) return M3_ERR_SHAPE;
+    if (a->io_dtype != M3_F32 && a->io_dtype != M3_BF16) return M3_ERR_DTYPE;
+    if (!m3::bwd_supported(N, P, R, a->io_dtype)) return M3_ERR_UNSUPPORTED;
+    const int64_t nbh = Bt * H;
+    if (nbh > (int64_t)1 << 24) return M3_ERR_UNSUPPORTED;
+    const int KP = N <= 32 ? 1 : (N <= 64 ? 2 : 4);
+    out->TB = m3::bwd_sub_steps(N);
+    out->K = 8;
+    const int64_t T1 = (int64_t)out->TB * out->K;
+    out->nsup = (L + T1 - 1) / T1;
+    out->unit_floats = (size_t)P * 32 * KP;                 // N x P with the pairs padded to 16k
+    out->ck_bytes = round256((size_t)nbh * (size_t)(out->nsup > 0 ? out->nsup : 1) * out->unit_floats * 4);
+    out->scr_bytes = round256((size_t)nbh * out->K * out->unit_floats * 4);
+    out->part_bytes = round256((size_t)nbh * 4);
+    out->ws = nbh > 0 ? out->ck_bytes + out->scr_bytes + out->part_bytes : 0;
+    return M3_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t m3_scan_bwd_workspace_bytes(const m3_scan_bwd_args* a)
+{
+    BwdPlan plan;
+    if (plan_bwd(a, &plan) != M3_OK) return 0;
+    return plan.ws;
+}
+
+int m3_scan_bwd_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t io_dtype)
+{
+    return m3::bwd_supported(dstate, headdim, rank, io_dtype) ? 1 : 0;
+}
+
+m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
+{
+    BwdPlan plan;
+    const m3_status ps = plan_bwd(a, &plan);
+    if (ps != M3_OK) return ps;
+    const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
+    const int64_t P = a->headdim, N = a->dstate, R = a->rank;
+    const int64_t nbh = Bt * H;
+    if (nbh == 0) return M3_OK;
+    const bool st_in = a->h_in || a->B_prev_in || a->x_prev_in;
+    const bool st_out = a->dh_in || a->dB_prev || a->dx_prev;
+    if (st_in && !(a->h_in && a->B_prev_in && a->x_prev_in)) return M3_ERR_NULL;
+    if (st_out && !(a->dh_in && a->dB_prev && a->dx_prev)) return M3_ERR_NULL;
+    if (a->A == nullptr || a->dA == nullptr) return M3_ERR_NULL;
+    if (L > 0 && (!a->x || !a->B || !a->C || !a->dt || !a->theta || !a->lam || !a->dy ||
+                  !a->dx || !a->dB || !a->dC || !a->ddt || !a->dtheta || !a->dlam))
+        return M3_ERR_NULL;
+    const void* ptrs[] = {a->x, a->B, a->C, a->dt, a->A, a->theta, a->lam, a->h_in,
+                          a->B_prev_in, a->x_prev_in, a->dy, a->dh_out, a->dx, a->dB, a->dC,
+                          a->ddt, a->dA, a->dtheta, a->dlam, a->dh_in, a->dB_prev, a->dx_prev};
+    for (const void* q : ptrs)
+        if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
+    const int e = io_size(a->io_dtype);
+    const int64_t tok = Bt * L * H;
+    const Range in[] = {
+        range_of(a->x, tok * R * P * e),         range_of(a->B, tok * R * N * e),
+        range_of(a->C, tok * R * N * e),         range_of(a->dt, tok * 4),
+        range_of(a->A, H * 4),                   range_of(a->theta, tok * (N / 2) * 4),
+        range_of(a->lam, tok * 4),               range_of(a->h_in, nbh * N * P * 4),
+        range_of(a->B_prev_in, nbh * R * N * e), range_of(a->x_prev_in, nbh * R * P * e),
+        range_of(a->dy, tok * R * P * e),        range_of(a->dh_out, nbh * N * P * 4),
+    };
+    const Range out[] = {
+        range_of(a->dx, tok * R * P * 4),        range_of(a->dB, tok * R * N * 4),
+        range_of(a->dC, tok * R * N * 4),        range_of(a->ddt, tok * 4),
+        range_of(a->dA, H * 4),                  range_of(a->dtheta, tok * (N / 2) * 4),
+        range_of(a->dlam, tok * 4),              range_of(a->dh_in, nbh * N * P * 4),
+        range_of(a->dB_prev, nbh * R * N * 4),   range_of(a->dx_prev, nbh * R * P * 4),
+        range_of(a->workspace, (int64_t)plan.ws),
+    };
+    const int nout = sizeof(out) / sizeof(out[0]);
+    for (const Range& o : out)
+        for (const Range& i : in)
+            if (overlaps(o, i)) return M3_ERR_ALIAS;
+    for (int i = 0; i < nout; ++i)
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(out[i], out[j])) return M3_ERR_ALIAS;
+    if (a->workspace == nullptr || a->workspace_bytes < plan.ws) return M3_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0) return M3_ERR_ALIGN;
+
+    m3::BwdParams p;
+    memset(&p, 0, sizeof(p));
+    p.x = a->x; p.B = a->B; p.C = a->C; p.dy = a->dy;
+    p.dt = a->dt; p.A = a->A; p.theta = a->theta; p.lam = a->lam;
+    p.h_in = a->h_in; p.Bp_in = a->B_prev_in; p.xp_in = a->x_prev_in; p.dh_out = a->dh_out;
+    p.dx = a->dx; p.dB = a->dB; p.dC = a->dC; p.ddt = a->ddt; p.dtheta = a->dtheta;
+    p.dlam = a->dlam; p.dh_in = a->dh_in; p.dBp = a->dB_prev; p.dxp = a->dx_prev;
+    char* ws = static_cast<char*>(a->workspace);
+    p.ckpt = reinterpret_cast<float*>(ws);
+    p.scr = reinterpret_cast<float*>(ws + plan.ck_bytes);
+    p.dA_part = reinterpret_cast<float*>(ws + plan.ck_bytes + plan.scr_bytes);
+    p.L = L; p.H = H; p.N = (int)N; p.P = (int)P; p.R = (int)R;
+    p.nbh = (int)nbh;
+    p.TB = plan.TB; p.K = plan.K;
+    return hip_status(m3::launch_bwd(p, a->io_dtype, a->dA, static_cast<hipStream_t>(stream)));
+}
+
 
 int m3_abi_version(void) { return M3_ABI_VERSION; }
 

@@ -36,6 +36,28 @@ struct DecodeParams {
     OptParams opt;
 };
 
+// Gradient of the scan (reverse-time recurrence with checkpointed recompute).
+struct BwdParams {
+    const void *x, *B, *C, *dy;
+    const float *dt, *A, *theta, *lam;
+    const float *h_in;
+    const void *Bp_in, *xp_in;
+    const float *dh_out;
+    float *dx, *dB, *dC, *ddt, *dtheta, *dlam;
+    float *dh_in, *dBp, *dxp;
+    float *ckpt;      // [B*H][nsup][N*P] states every T1 steps
+    float *scr;       // [B*H][K][N*P] sub-block start states of one superblock
+    float *dA_part;   // [B*H] this unit's share of dA
+    int64_t L, H;
+    int N, P, R;
+    int nbh;
+    int TB, K;        // sub-block steps, sub-blocks per superblock (T1 = K * TB)
+};
+
+bool bwd_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
+int bwd_sub_steps(int64_t N);
+hipError_t launch_bwd(const BwdParams& p, int io_dtype, float* dA, hipStream_t stream);
+
 bool decode_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
 hipError_t launch_decode(const DecodeParams& p, int io_dtype, hipStream_t stream);
 

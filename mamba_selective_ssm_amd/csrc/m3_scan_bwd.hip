@@ -1,0 +1,580 @@
+// Gradient of the Mamba-3 scan: a reverse-time recurrence over the adjoint
+// state, with the forward states recomputed from checkpoints.
+//
+// Forward (Mamba-3 summary on b-lab.team, section 1 recurrence, section 2
+// block rotations R(phi_i), phi = dt theta_i, on adjacent rows, section 3
+// MIMO), per (b, h) and step t:
+//   a_t = alpha_t h_{t-1} + beta_t U_{t-1},  h_t = R_t a_t + gamma_t U_t,
+//   U_t = B_t X_t,  y_t = C_t^T h_t.
+// Adjoint, t = L-1 .. 0 (g_t = dLoss/dh_t, da_t = dLoss/da_t):
+//   g_t  = C_t dy_t + alpha_{t+1} da_{t+1}        (dh_out enters as da_L)
+//   da_t = R_t^T g_t
+//   dU_t = gamma_t g_t + beta_{t+1} da_{t+1}
+//   dX_t = B_t^T dU_t,  dB_t = dU_t X_t^T,  dC_t = h_t dy_t^T
+//   dalpha_t = <da_t, h_{t-1}>,  dbeta_t = <da_t, U_{t-1}>,  dgamma_t = <g_t, U_t>
+//   dphi_t,i = sum_p (g1 r0 - g0 r1) over pair i, r = R_t a_t = h_t - gamma_t U_t
+// and through alpha = e^{dt A}, beta = (1-lam) dt alpha, gamma = lam dt,
+// phi_i = dt theta_i to dt, A, lam, theta.  The initial record gets
+// dh_in = alpha_0 da_0 and dU_prev = beta_0 da_0.
+//
+// One workgroup per (b, h); wave w owns headdim columns 16w .. 16w+15 of the
+// N x P state (lane: 4 columns x the rows of pairs rg + 16k), so each wave
+// reduces dX over its own rows, and the column sums (dB, dC, dphi and the
+// scalar gradients) of the waves meet in LDS once per step (one barrier).
+// States: a checkpoint every T1 = K*TB steps in HBM (pass A); per superblock
+// the K sub-block start states go to a scratch area (pass B1); per sub-block
+// the TB step states are recomputed into the wave's LDS slots (pass B2) and
+// the adjoint steps run backward over them.  Each lane only reads back what
+// it wrote (checkpoints, scratch and LDS slots), so those need no barriers.
+#include "m3_device.hpp"
+#include "m3_internal.hpp"
+
+namespace m3 {
+namespace {
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+__device__ __forceinline__ float2 ld2(const bf16* p) {
+    const bf16x2 v = *reinterpret_cast<const bf16x2*>(p);
+    return make_float2((float)v[0], (float)v[1]);
+}
+__device__ __forceinline__ float2 ld2(const float* p) { return *reinterpret_cast<const float2*>(p); }
+__device__ __forceinline__ void ld4(float (&d)[4], const bf16* p) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = (float)v[e];
+}
+__device__ __forceinline__ void ld4(float (&d)[4], const float* p) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = v[e];
+}
+
+template <int R, int KP> struct StepIn {
+    float B[KP][R][2];    // rows 2i, 2i+1 of this lane's pairs
+    float X[R][4];        // this lane's 4 columns
+};
+
+template <typename IO, int R, int KP, int TB>
+__global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) float bsm[];
+    constexpr int E = 8 * KP;                     // state elements per lane
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int NW = blockDim.x >> 6, NT = blockDim.x, tid = threadIdx.x;
+    const int N = p.N, NPR = N / 2, P = p.P;
+    const int64_t L = p.L, H = p.H;
+    const int bh = blockIdx.x;
+    const int64_t b = bh / H, h = bh % H;
+    const int cg = lane & 3, rg = lane >> 2;
+    const int col0 = 16 * wv + 4 * cg;
+    const int V = 2 * R * N + NPR + 4;            // per-wave partial sums of one step
+    float* slots = bsm + (size_t)wv * TB * E * 64;               // this wave's step states
+    float* red = bsm + (size_t)NW * TB * E * 64;                 // [2][NW][V]
+
+    const IO* Xg = reinterpret_cast<const IO*>(p.x);
+    const IO* Bg = reinterpret_cast<const IO*>(p.B);
+    const IO* Cg = reinterpret_cast<const IO*>(p.C);
+    const IO* dYg = reinterpret_cast<const IO*>(p.dy);
+    const IO* Bpr = reinterpret_cast<const IO*>(p.Bp_in);
+    const IO* Xpr = reinterpret_cast<const IO*>(p.xp_in);
+    const float A = p.A[h];
+    auto tok = [&](int64_t t) -> int64_t { return (b * L + t) * H + h; };
+    auto pair_of = [&](int k) { return rg + 16 * k; };
+    auto pvalid = [&](int k) { return rg + 16 * k < NPR; };
+
+    // Inputs of step t (t = -1: the state record's previous token, or zeros).
+    auto load_in = [&](int64_t t, StepIn<R, KP>& s) {
+        if (t < 0 && Bpr == nullptr) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) s.X[r][q] = 0.f;
+#pragma unroll
+                for (int k = 0; k < KP; ++k) s.B[k][r][0] = s.B[k][r][1] = 0.f;
+            }
+            return;
+        }
+        const IO* xb = t < 0 ? Xpr + (int64_t)bh * R * P : Xg + tok(t) * R * P;
+        const IO* bb = t < 0 ? Bpr + (int64_t)bh * R * N : Bg + tok(t) * R * N;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ld4(s.X[r], xb + r * P + col0);
+#pragma unroll
+            for (int k = 0; k < KP; ++k) {
+                const int i = pvalid(k) ? pair_of(k) : 0;
+                const float2 v = ld2(bb + r * N + 2 * i);
+                s.B[k][r][0] = pvalid(k) ? v.x : 0.f;
+                s.B[k][r][1] = pvalid(k) ? v.y : 0.f;
+            }
+        }
+    };
+    auto outer = [&](const StepIn<R, KP>& s, float (&U)[E]) {
+#pragma unroll
+        for (int k = 0; k < KP; ++k)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float u = 0.f;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) u += s.B[k][r][j] * s.X[r][q];
+                    U[(k * 2 + j) * 4 + q] = u;
+                }
+    };
+    struct Sc { float d, lm, al, be, ga, cs[KP], sn[KP], th[KP]; };
+    auto scalars = [&](int64_t t, Sc& c) {
+        const int64_t tk = tok(t);
+        c.d = p.dt[tk];
+        c.lm = p.lam[tk];
+        c.al = expf(c.d * A);
+        c.be = (1.f - c.lm) * c.d * c.al;
+        c.ga = c.lm * c.d;
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            c.th[k] = pvalid(k) ? p.theta[tk * NPR + pair_of(k)] : 0.f;
+            sincosf(c.d * c.th[k], &c.sn[k], &c.cs[k]);
+        }
+    };
+    // One forward step on this lane's elements: hs <- R(alpha hs + beta Uprev) + gamma U.
+    auto fwd_step = [&](int64_t t, float (&hs)[E], float (&Uprev)[E]) {
+        Sc c;
+        scalars(t, c);
+        StepIn<R, KP> s;
+        load_in(t, s);
+        float U[E];
+        outer(s, U);
+#pragma unroll
+        for (int k = 0; k < KP; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int e0 = (k * 2) * 4 + q, e1 = (k * 2 + 1) * 4 + q;
+                const float a0 = c.al * hs[e0] + c.be * Uprev[e0];
+                const float a1 = c.al * hs[e1] + c.be * Uprev[e1];
+                hs[e0] = c.cs[k] * a0 - c.sn[k] * a1 + c.ga * U[e0];
+                hs[e1] = c.sn[k] * a0 + c.cs[k] * a1 + c.ga * U[e1];
+            }
+#pragma unroll
+        for (int e = 0; e < E; ++e) Uprev[e] = U[e];
+    };
+    // Lane-ordered state storage (16-byte pieces, consecutive lanes adjacent).
+    auto st_state = [&](float* base, const float (&hs)[E]) {
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4)
+            *reinterpret_cast<f32x4*>(base + ((size_t)e4 * 64 + lane) * 4) =
+                f32x4{hs[4 * e4], hs[4 * e4 + 1], hs[4 * e4 + 2], hs[4 * e4 + 3]};
+    };
+    auto ld_state = [&](const float* base, float (&hs)[E]) {
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(base + ((size_t)e4 * 64 + lane) * 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hs[4 * e4 + q] = v[q];
+        }
+    };
+    const size_t unit_sz = (size_t)NW * E * 64;                 // = N * P floats (padded pairs)
+    const int64_t T1 = (int64_t)p.K * TB;
+    const int64_t nsup = (L + T1 - 1) / T1;
+    float* ck = p.ckpt + (size_t)bh * (size_t)(nsup > 0 ? nsup : 1) * unit_sz + (size_t)wv * E * 64;
+    float* sc = p.scr + (size_t)bh * p.K * unit_sz + (size_t)wv * E * 64;
+    // ck/sc point at this wave's part of entry 0; entry j adds j * unit_sz.
+
+    // ---- pass A: checkpoints every T1 steps ------------------------------
+    float hs[E], Up[E];
+#pragma unroll
+    for (int k = 0; k < KP; ++k)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = 2 * (pvalid(k) ? pair_of(k) : 0) + j;
+                hs[(k * 2 + j) * 4 + q] =
+                    (p.h_in != nullptr && pvalid(k)) ? p.h_in[((int64_t)bh * N + n) * P + col0 + q] : 0.f;
+            }
+    {
+        StepIn<R, KP> s;
+        load_in(-1, s);
+        outer(s, Up);
+    }
+    if (nsup > 0) st_state(ck, hs);
+    for (int64_t t = 0; t < L; ++t) {
+        fwd_step(t, hs, Up);
+        if ((t + 1) % T1 == 0 && t + 1 < L) st_state(ck + (size_t)((t + 1) / T1) * unit_sz, hs);
+    }
+
+    // ---- pass B: adjoint, superblocks and sub-blocks from the end --------
+    // A virtual step L with alpha = 1, no rotation and beta = 0 carries dh_out.
+    float dan[E];
+#pragma unroll
+    for (int k = 0; k < KP; ++k)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = 2 * (pvalid(k) ? pair_of(k) : 0) + j;
+                dan[(k * 2 + j) * 4 + q] = (p.dh_out != nullptr && pvalid(k))
+                    ? p.dh_out[((int64_t)bh * N + n) * P + col0 + q] : 0.f;
+            }
+    float a_nx = 1.f, b_nx = 0.f;
+    float dA_acc = 0.f;
+    int par = 0;
+
+    for (int64_t sup = nsup - 1; sup >= 0; --sup) {
+        const int64_t s0 = sup * T1, s1 = s0 + T1 < L ? s0 + T1 : L;
+        const int nsub = (int)((s1 - s0 + TB - 1) / TB);
+        // B1: sub-block start states of this superblock
+        ld_state(ck + (size_t)sup * unit_sz, hs);
+        {
+            StepIn<R, KP> s;
+            load_in(s0 - 1, s);
+            outer(s, Up);
+        }
+        for (int sb = 0; sb < nsub; ++sb) {
+            st_state(sc + (size_t)sb * unit_sz, hs);
+            const int64_t tA = s0 + (int64_t)sb * TB, tB = tA + TB < s1 ? tA + TB : s1;
+            for (int64_t t = tA; t < tB; ++t) fwd_step(t, hs, Up);
+        }
+        for (int sb = nsub - 1; sb >= 0; --sb) {
+            const int64_t tA = s0 + (int64_t)sb * TB, tB = tA + TB < s1 ? tA + TB : s1;
+            // B2: the sub-block's step states into this wave's LDS slots
+            float hb[E];
+            ld_state(sc + (size_t)sb * unit_sz, hs);
+            {
+                StepIn<R, KP> s;
+                load_in(tA - 1, s);
+                outer(s, Up);
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) hb[e] = hs[e];
+            for (int64_t t = tA; t < tB; ++t) {
+                fwd_step(t, hs, Up);
+                st_state(slots + (size_t)(t - tA) * E * 64, hs);
+            }
+            // adjoint steps tB-1 .. tA
+            for (int64_t t = tB - 1; t >= tA; --t) {
+                Sc c;
+                scalars(t, c);
+                StepIn<R, KP> cur, prv;
+                load_in(t, cur);
+                load_in(t - 1, prv);
+                float Cv[KP][R][2], dyv[R][4];
+                {
+                    const int64_t tk = tok(t);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        ld4(dyv[r], dYg + tk * R * P + r * P + col0);
+#pragma unroll
+                        for (int k = 0; k < KP; ++k) {
+                            const int i = pvalid(k) ? pair_of(k) : 0;
+                            const float2 v = ld2(Cg + tk * R * N + r * N + 2 * i);
+                            Cv[k][r][0] = pvalid(k) ? v.x : 0.f;
+                            Cv[k][r][1] = pvalid(k) ? v.y : 0.f;
+                        }
+                    }
+                }
+                float ht[E], hp[E], Ut[E], Upv[E];
+                ld_state(slots + (size_t)(t - tA) * E * 64, ht);
+                if (t > tA) ld_state(slots + (size_t)(t - tA - 1) * E * 64, hp);
+                else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) hp[e] = hb[e];
+                }
+                outer(cur, Ut);
+                outer(prv, Upv);
+                float g[E], da[E], dU[E];
+#pragma unroll
+                for (int k = 0; k < KP; ++k)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int e = (k * 2 + j) * 4 + q;
+                            float v = a_nx * dan[e];
+#pragma unroll
+                            for (int r = 0; r < R; ++r) v += Cv[k][r][j] * dyv[r][q];
+                            g[e] = v;
+                        }
+                float s_a = 0.f, s_b = 0.f, s_g = 0.f, s_th = 0.f;
+                float dph[KP];
+#pragma unroll
+                for (int k = 0; k < KP; ++k) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int e0 = (k * 2) * 4 + q, e1 = (k * 2 + 1) * 4 + q;
+                        da[e0] = c.cs[k] * g[e0] + c.sn[k] * g[e1];     // R^T g
+                        da[e1] = -c.sn[k] * g[e0] + c.cs[k] * g[e1];
+                        const float r0 = ht[e0] - c.ga * Ut[e0], r1 = ht[e1] - c.ga * Ut[e1];
+                        acc += g[e1] * r0 - g[e0] * r1;
+                    }
+                    dph[k] = acc;
+                    s_th += c.th[k] * acc;
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    dU[e] = c.ga * g[e] + b_nx * dan[e];
+                    s_a += da[e] * hp[e];
+                    s_b += da[e] * Upv[e];
+                    s_g += g[e] * Ut[e];
+                }
+                float dBp[KP][R][2], dCp[KP][R][2], dXp[R][4];
+#pragma unroll
+                for (int k = 0; k < KP; ++k)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            float sb_ = 0.f, sc_ = 0.f;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int e = (k * 2 + j) * 4 + q;
+                                sb_ += dU[e] * cur.X[r][q];
+                                sc_ += ht[e] * dyv[r][q];
+                            }
+                            dBp[k][r][j] = sb_;
+                            dCp[k][r][j] = sc_;
+                        }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float v = 0.f;
+#pragma unroll
+                        for (int k = 0; k < KP; ++k)
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) v += cur.B[k][r][j] * dU[(k * 2 + j) * 4 + q];
+                        dXp[r][q] = v;
+                    }
+                // column sums within the wave: over the 4 lanes of a row group
+#pragma unroll
+                for (int off = 1; off < 4; off <<= 1) {
+#pragma unroll
+                    for (int k = 0; k < KP; ++k) {
+                        dph[k] += __shfl_xor(dph[k], off, 64);
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                dBp[k][r][j] += __shfl_xor(dBp[k][r][j], off, 64);
+                                dCp[k][r][j] += __shfl_xor(dCp[k][r][j], off, 64);
+                            }
+                    }
+                }
+                // row sums within the wave: over the 16 row groups
+#pragma unroll
+                for (int off = 4; off < 64; off <<= 1)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) dXp[r][q] += __shfl_xor(dXp[r][q], off, 64);
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    s_a += __shfl_xor(s_a, off, 64);
+                    s_b += __shfl_xor(s_b, off, 64);
+                    s_g += __shfl_xor(s_g, off, 64);
+                    s_th += __shfl_xor(s_th, off, 64);
+                }
+                const int64_t tk = tok(t);
+                if (rg == 0) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        *reinterpret_cast<f32x4*>(p.dx + tk * R * P + r * P + col0) =
+                            f32x4{dXp[r][0], dXp[r][1], dXp[r][2], dXp[r][3]};
+                }
+                float* rb = red + ((size_t)par * NW + wv) * V;
+                if (cg == 0) {
+#pragma unroll
+                    for (int k = 0; k < KP; ++k) {
+                        if (pvalid(k)) {
+                            const int i = pair_of(k);
+#pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                *reinterpret_cast<float2*>(rb + r * N + 2 * i) =
+                                    make_float2(dBp[k][r][0], dBp[k][r][1]);
+                                *reinterpret_cast<float2*>(rb + R * N + r * N + 2 * i) =
+                                    make_float2(dCp[k][r][0], dCp[k][r][1]);
+                            }
+                            rb[2 * R * N + i] = dph[k];
+                        }
+                    }
+                }
+                if (lane == 0) {
+                    rb[2 * R * N + NPR + 0] = s_a;
+                    rb[2 * R * N + NPR + 1] = s_b;
+                    rb[2 * R * N + NPR + 2] = s_g;
+                    rb[2 * R * N + NPR + 3] = s_th;
+                }
+                __syncthreads();
+                // sums over the waves (column slices); buffers alternate by step
+                const float* r0b = red + (size_t)par * NW * V;
+                for (int v = tid; v < 2 * R * N + NPR; v += NT) {
+                    float sum = 0.f;
+                    for (int w = 0; w < NW; ++w) sum += r0b[(size_t)w * V + v];
+                    if (v < R * N) p.dB[tk * R * N + v] = sum;
+                    else if (v < 2 * R * N) p.dC[tk * R * N + (v - R * N)] = sum;
+                    else p.dtheta[tk * NPR + (v - 2 * R * N)] = c.d * sum;
+                }
+                if (tid == 0) {
+                    float da_ = 0.f, db_ = 0.f, dg_ = 0.f, dth_ = 0.f;
+                    for (int w = 0; w < NW; ++w) {
+                        const float* q = r0b + (size_t)w * V + 2 * R * N + NPR;
+                        da_ += q[0]; db_ += q[1]; dg_ += q[2]; dth_ += q[3];
+                    }
+                    p.ddt[tk] = da_ * c.al * A + db_ * (1.f - c.lm) * c.al * (1.f + c.d * A)
+                                + dg_ * c.lm + dth_;
+                    p.dlam[tk] = -c.d * c.al * db_ + c.d * dg_;
+                    dA_acc += da_ * c.al * c.d + db_ * (1.f - c.lm) * c.d * c.d * c.al;
+                }
+                par ^= 1;
+#pragma unroll
+                for (int e = 0; e < E; ++e) dan[e] = da[e];
+                a_nx = c.al;
+                b_nx = c.be;
+            }
+        }
+    }
+
+    // ---- the state record's gradients -------------------------------------
+    if (p.dh_in != nullptr) {
+#pragma unroll
+        for (int k = 0; k < KP; ++k)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (pvalid(k)) {
+                    const int n = 2 * pair_of(k) + j;
+                    const int e = (k * 2 + j) * 4;
+                    *reinterpret_cast<f32x4*>(p.dh_in + ((int64_t)bh * N + n) * P + col0) =
+                        f32x4{a_nx * dan[e], a_nx * dan[e + 1], a_nx * dan[e + 2], a_nx * dan[e + 3]};
+                }
+        StepIn<R, KP> s;
+        load_in(-1, s);
+        float dXp[R][4], dBp[KP][R][2];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v = 0.f;
+#pragma unroll
+                for (int k = 0; k < KP; ++k)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) v += s.B[k][r][j] * b_nx * dan[(k * 2 + j) * 4 + q];
+                dXp[r][q] = v;
+            }
+#pragma unroll
+            for (int k = 0; k < KP; ++k)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v += b_nx * dan[(k * 2 + j) * 4 + q] * s.X[r][q];
+                    dBp[k][r][j] = v;
+                }
+        }
+#pragma unroll
+        for (int off = 4; off < 64; off <<= 1)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dXp[r][q] += __shfl_xor(dXp[r][q], off, 64);
+#pragma unroll
+        for (int off = 1; off < 4; off <<= 1)
+#pragma unroll
+            for (int k = 0; k < KP; ++k)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) dBp[k][r][j] += __shfl_xor(dBp[k][r][j], off, 64);
+        if (rg == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                *reinterpret_cast<f32x4*>(p.dxp + (int64_t)bh * R * P + r * P + col0) =
+                    f32x4{dXp[r][0], dXp[r][1], dXp[r][2], dXp[r][3]};
+        }
+        float* rb = red + ((size_t)par * NW + wv) * V;
+        if (cg == 0) {
+#pragma unroll
+            for (int k = 0; k < KP; ++k)
+                if (pvalid(k))
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        *reinterpret_cast<float2*>(rb + r * N + 2 * pair_of(k)) =
+                            make_float2(dBp[k][r][0], dBp[k][r][1]);
+        }
+        __syncthreads();
+        const float* r0b = red + (size_t)par * NW * V;
+        for (int v = tid; v < R * N; v += NT) {
+            float sum = 0.f;
+            for (int w = 0; w < NW; ++w) sum += r0b[(size_t)w * V + v];
+            p.dBp[(int64_t)bh * R * N + v] = sum;
+        }
+    }
+    if (tid == 0) p.dA_part[bh] = dA_acc;
+}
+
+// dA[h] = sum over the batch rows of the units' shares (fixed order).
+__global__ void bwd_dA_kernel(const float* part, float* dA, int64_t batch, int64_t H)
+{
+    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    float s = 0.f;
+    for (int64_t b = 0; b < batch; ++b) s += part[b * H + h];
+    dA[h] = s;
+}
+
+template <typename IO, int R, int KP, int TB>
+hipError_t launch_bwd_t(const BwdParams& p, float* dA, hipStream_t stream)
+{
+    const int NW = p.P / 16;
+    const size_t lds = sizeof(float) * ((size_t)NW * TB * 8 * KP * 64 + 2 * (size_t)NW * (2 * R * p.N + p.N / 2 + 4));
+    auto* kern = &bwd_kernel<IO, R, KP, TB>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.nbh), dim3(64 * NW), lds, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t batch = p.nbh / p.H;
+    hipLaunchKernelGGL(bwd_dA_kernel, dim3((unsigned)((p.H + 63) / 64)), dim3(64), 0, stream,
+                       (const float*)p.dA_part, dA, batch, p.H);
+    return hipGetLastError();
+}
+
+template <typename IO, int R>
+hipError_t launch_bwd_r(const BwdParams& p, float* dA, hipStream_t stream)
+{
+    if (p.N <= 32) return launch_bwd_t<IO, R, 1, 4>(p, dA, stream);
+    if (p.N <= 64) return launch_bwd_t<IO, R, 2, 4>(p, dA, stream);
+    return launch_bwd_t<IO, R, 4, 2>(p, dA, stream);
+}
+
+}  // namespace
+
+bool bwd_supported(int64_t N, int64_t P, int64_t R, int io_dtype)
+{
+    if (io_dtype != 0 && io_dtype != 1) return false;
+    if (R != 1 && R != 2 && R != 4) return false;
+    if (N < 2 || N > 128 || (N % 2) != 0) return false;
+    return P == 16 || P == 32 || P == 64;
+}
+
+int bwd_sub_steps(int64_t N) { return N <= 64 ? 4 : 2; }
+
+hipError_t launch_bwd(const BwdParams& p, int io_dtype, float* dA, hipStream_t stream)
+{
+    if (io_dtype == 0) {
+        switch (p.R) {
+        case 1: return launch_bwd_r<float, 1>(p, dA, stream);
+        case 2: return launch_bwd_r<float, 2>(p, dA, stream);
+        default: return launch_bwd_r<float, 4>(p, dA, stream);
+        }
+    }
+    switch (p.R) {
+    case 1: return launch_bwd_r<bf16, 1>(p, dA, stream);
+    case 2: return launch_bwd_r<bf16, 2>(p, dA, stream);
+    default: return launch_bwd_r<bf16, 4>(p, dA, stream);
+    }
+}
+
+}  // namespace m3

@@ -14,6 +14,8 @@ HEADER = os.path.join(ROOT, "include", "m3scan.h")
 
 from mamba_selective_ssm_amd import binding  # noqa: E402
 
+FAKE = 0x7F0000000000   # never dereferenced: validation fails before any device access
+
 
 def declared_functions():
     text = open(HEADER).read()
@@ -68,6 +70,64 @@ def test_struct_layout_matches_header(tmp_path):
     assert vals == expect
 
 
+def test_bwd_struct_layout_matches_header(tmp_path):
+    fields = [f[0] for f in binding.ScanBwdArgs._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "m3scan.h"', "int main(void){",
+           'printf("%zu\\n", sizeof(m3_scan_bwd_args));']
+    src += ['printf("%%zu\\n", offsetof(m3_scan_bwd_args, %s));' % f for f in fields]
+    src.append("return 0;}")
+    c = tmp_path / "layout_bwd.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout_bwd"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(c)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], stdout=subprocess.PIPE, text=True,
+                                           check=True).stdout.split()]
+    assert vals == [ctypes.sizeof(binding.ScanBwdArgs)] + \
+        [getattr(binding.ScanBwdArgs, f).offset for f in fields]
+
+
+def bwd_args(**kw):
+    a = binding.ScanBwdArgs(batch=2, seqlen=10, nheads=3, headdim=64, dstate=64, rank=1,
+                            io_dtype=1)
+    ptrs = ["x", "B", "C", "dt", "A", "theta", "lam", "dy", "dx", "dB", "dC", "ddt", "dA",
+            "dtheta", "dlam"]
+    for i, p in enumerate(ptrs):
+        setattr(a, p, FAKE + i * (1 << 32))
+    a.workspace = FAKE + (30 << 32)
+    a.workspace_bytes = 1 << 40
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dstate=5), -2), (dict(headdim=0), -2), (dict(io_dtype=3), -4),
+    (dict(headdim=128), -3), (dict(dstate=256), -3), (dict(rank=3), -3),
+    (dict(dy=None), -1), (dict(dA=None), -1), (dict(dx=None), -1),
+    (dict(h_in=FAKE + (20 << 32)), -1),                    # partial state record
+    (dict(dh_in=FAKE + (21 << 32)), -1),                   # partial record gradients
+    (dict(dx=FAKE + 8), -5),
+    (dict(dx=FAKE), -7),                                   # dx aliases x
+    (dict(dB=FAKE + (10 << 32) + 64), -7),                 # dB overlaps dC
+    (dict(workspace=None), -6), (dict(workspace_bytes=16), -6),
+    (dict(workspace=FAKE + (30 << 32) + 16), -5),
+])
+def test_bwd_validation_codes(lib, kw, code):
+    assert lib.m3_scan_bwd(ctypes.byref(bwd_args(**kw)), None) == code
+
+
+def test_bwd_supported_and_workspace(lib):
+    for io in (0, 1):
+        for N in (16, 32, 64, 128):
+            for P in (16, 32, 64):
+                for R in (1, 2, 4):
+                    assert lib.m3_scan_bwd_supported(N, P, R, io) == 1
+    assert lib.m3_scan_bwd_supported(64, 128, 1, 1) == 0
+    ws = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(seqlen=2048)))
+    # one checkpoint per 32 steps per (b, h), N x P floats, plus scratch
+    assert ws >= 6 * 64 * 64 * 64 * 4
+
+
 def test_version_and_status_strings(lib):
     assert lib.m3_abi_version() == 2
     for code in range(-9, 1):
@@ -77,7 +137,6 @@ def test_version_and_status_strings(lib):
     assert lib.m3_last_hip_error() == 0
 
 
-FAKE = 0x7F0000000000   # never dereferenced: validation fails before any device access
 
 
 OPTION_FIELDS = {f[0] for f in binding.Options._fields_}
