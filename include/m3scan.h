@@ -231,7 +231,8 @@ typedef struct {
  *            dx_prev [batch, nheads, rank, headdim] (gradients with respect to
  *            the input state record, zero record when none was given)
  *   workspace  m3_scan_bwd_workspace_bytes(args) bytes, 256-byte aligned
- * Supported: dstate even and <= 128, headdim 16, 32 or 64, rank 1, 2 or 4.
+ * Supported: dstate a multiple of 8 up to 128, headdim 16, 32 or 64, rank 1,
+ * 2 or 4.
  * Every output is written (no accumulation into the caller's buffers); the
  * result is deterministic.
  */

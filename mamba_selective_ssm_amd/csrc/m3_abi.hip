@@ -198,7 +198,7 @@ m3_status plan_bwd(const m3_scan_bwd_args* a, BwdPlan* out)
     if (nbh > (int64_t)1 << 24) return M3_ERR_UNSUPPORTED;
     const int KP = N <= 32 ? 1 : (N <= 64 ? 2 : 4);
     out->TB = m3::bwd_sub_steps(N);
-    out->K = 8;
+    out->K = m3::bwd_blocks_per_checkpoint(N, P, R, a->io_dtype);
     const int64_t T1 = (int64_t)out->TB * out->K;
     out->nsup = (L + T1 - 1) / T1;
     out->unit_floats = (size_t)P * 32 * KP;                 // N x P with the pairs padded to 16k

@@ -56,6 +56,7 @@ struct BwdParams {
 
 bool bwd_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
 int bwd_sub_steps(int64_t N);
+int bwd_blocks_per_checkpoint(int64_t N, int64_t P, int64_t R, int io_dtype);
 hipError_t launch_bwd(const BwdParams& p, int io_dtype, float* dA, hipStream_t stream);
 
 bool decode_supported(int64_t N, int64_t P, int64_t R, int io_dtype);

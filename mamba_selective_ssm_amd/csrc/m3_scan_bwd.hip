@@ -26,6 +26,9 @@
 // the TB step states are recomputed into the wave's LDS slots (pass B2) and
 // the adjoint steps run backward over them.  Each lane only reads back what
 // it wrote (checkpoints, scratch and LDS slots), so those need no barriers.
+// The inputs of a superblock's steps (and of the step before it) are staged
+// in LDS by the whole workgroup with one batch of 16-byte loads, so the
+// sequential steps read them at LDS latency instead of waiting on memory.
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
 
@@ -72,6 +75,15 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
     const int V = 2 * R * N + NPR + 4;            // per-wave partial sums of one step
     float* slots = bsm + (size_t)wv * TB * E * 64;               // this wave's step states
     float* red = bsm + (size_t)NW * TB * E * 64;                 // [2][NW][V]
+    // Staged step inputs, per step: B, C [R][N] and X, dy [R][P] (io), then
+    // float32 [dt, lam, alpha, beta, gamma, -, -, -], theta, cos phi, sin phi
+    // [N/2 each]; a step's block is SB bytes.
+    constexpr int ESZ = (int)sizeof(IO);
+    const int oC = ESZ * R * N, oX = 2 * ESZ * R * N, oDY = oX + ESZ * R * P;
+    const int oSC = oDY + ESZ * R * P;
+    const int SB = (oSC + 4 * (8 + 3 * NPR) + 15) / 16 * 16;
+    unsigned char* stg = reinterpret_cast<unsigned char*>(red + 2 * (size_t)NW * V);
+    int64_t stg_t0 = 0;                                          // step held in block 0
 
     const IO* Xg = reinterpret_cast<const IO*>(p.x);
     const IO* Bg = reinterpret_cast<const IO*>(p.B);
@@ -84,27 +96,69 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
     auto pair_of = [&](int k) { return rg + 16 * k; };
     auto pvalid = [&](int k) { return rg + 16 * k < NPR; };
 
-    // Inputs of step t (t = -1: the state record's previous token, or zeros).
-    auto load_in = [&](int64_t t, StepIn<R, KP>& s) {
-        if (t < 0 && Bpr == nullptr) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) s.X[r][q] = 0.f;
-#pragma unroll
-                for (int k = 0; k < KP; ++k) s.B[k][r][0] = s.B[k][r][1] = 0.f;
+    // Stage steps t0 .. t0+cnt-1 (t0 may be -1: the state record's previous
+    // token, or zeros) into LDS; every thread of the workgroup takes part.
+    auto stage = [&](int64_t t0, int cnt) {
+        __syncthreads();                                         // previous block's readers done
+        stg_t0 = t0;
+        const int q_io = (2 * ESZ * R * N + 2 * ESZ * R * P) / 16;   // 16-byte pieces per step
+        for (int idx = tid; idx < cnt * q_io; idx += NT) {
+            const int sidx = idx / q_io, piece = idx % q_io;
+            const int64_t t = t0 + sidx;
+            const int off = piece * 16;                          // byte offset in the step block
+            const unsigned char* src = nullptr;
+            if (off < oX) {                                      // B or C
+                const int m = off / oC, o = off % oC;
+                if (t >= 0) src = reinterpret_cast<const unsigned char*>(m == 0 ? Bg : Cg) + tok(t) * (int64_t)oC + o;
+                else if (m == 0 && Bpr != nullptr) src = reinterpret_cast<const unsigned char*>(Bpr) + (int64_t)bh * oC + o;
+            } else {                                             // X or dy
+                const int m = (off - oX) / (ESZ * R * P), o = (off - oX) % (ESZ * R * P);
+                if (t >= 0) src = reinterpret_cast<const unsigned char*>(m == 0 ? Xg : dYg) + tok(t) * (int64_t)(ESZ * R * P) + o;
+                else if (m == 0 && Xpr != nullptr) src = reinterpret_cast<const unsigned char*>(Xpr) + (int64_t)bh * (ESZ * R * P) + o;
             }
-            return;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (src != nullptr) v = *reinterpret_cast<const uint4*>(src);
+            *reinterpret_cast<uint4*>(stg + (size_t)sidx * SB + off) = v;
         }
-        const IO* xb = t < 0 ? Xpr + (int64_t)bh * R * P : Xg + tok(t) * R * P;
-        const IO* bb = t < 0 ? Bpr + (int64_t)bh * R * N : Bg + tok(t) * R * N;
+        // per-step scalars and per-pair rotations, computed once per stage
+        for (int idx = tid; idx < cnt * (NPR + 1); idx += NT) {
+            const int sidx = idx / (NPR + 1), j = idx % (NPR + 1);
+            const int64_t t = t0 + sidx;
+            float* f = reinterpret_cast<float*>(stg + (size_t)sidx * SB + oSC);
+            const float d = t >= 0 ? p.dt[tok(t)] : 0.f;
+            if (j == NPR) {
+                const float lm = t >= 0 ? p.lam[tok(t)] : 0.f;
+                const float al = expf(d * A);
+                f[0] = d;
+                f[1] = lm;
+                f[2] = al;
+                f[3] = (1.f - lm) * d * al;
+                f[4] = lm * d;
+            } else {
+                const float th = t >= 0 ? p.theta[tok(t) * NPR + j] : 0.f;
+                float sn, cs;
+                sincosf(d * th, &sn, &cs);
+                f[8 + j] = th;
+                f[8 + NPR + j] = cs;
+                f[8 + 2 * NPR + j] = sn;
+            }
+        }
+        __syncthreads();
+    };
+    auto blk = [&](int64_t t) { return stg + (size_t)(t - stg_t0) * SB; };
+    auto io_at = [&](const unsigned char* base, int o) -> const IO* {
+        return reinterpret_cast<const IO*>(base + o);
+    };
+    // Inputs of a staged step t (t = -1 allowed when staged).
+    auto load_in = [&](int64_t t, StepIn<R, KP>& s) {
+        const unsigned char* bb = blk(t);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            ld4(s.X[r], xb + r * P + col0);
+            ld4(s.X[r], io_at(bb, oX) + r * P + col0);
 #pragma unroll
             for (int k = 0; k < KP; ++k) {
                 const int i = pvalid(k) ? pair_of(k) : 0;
-                const float2 v = ld2(bb + r * N + 2 * i);
+                const float2 v = ld2(io_at(bb, 0) + r * N + 2 * i);
                 s.B[k][r][0] = pvalid(k) ? v.x : 0.f;
                 s.B[k][r][1] = pvalid(k) ? v.y : 0.f;
             }
@@ -125,16 +179,19 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
     };
     struct Sc { float d, lm, al, be, ga, cs[KP], sn[KP], th[KP]; };
     auto scalars = [&](int64_t t, Sc& c) {
-        const int64_t tk = tok(t);
-        c.d = p.dt[tk];
-        c.lm = p.lam[tk];
-        c.al = expf(c.d * A);
-        c.be = (1.f - c.lm) * c.d * c.al;
-        c.ga = c.lm * c.d;
+        const float* f = reinterpret_cast<const float*>(blk(t) + oSC);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(f);
+        c.d = s4[0];
+        c.lm = s4[1];
+        c.al = s4[2];
+        c.be = s4[3];
+        c.ga = f[4];
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
-            c.th[k] = pvalid(k) ? p.theta[tk * NPR + pair_of(k)] : 0.f;
-            sincosf(c.d * c.th[k], &c.sn[k], &c.cs[k]);
+            const int i = pvalid(k) ? pair_of(k) : 0;
+            c.th[k] = pvalid(k) ? f[8 + i] : 0.f;
+            c.cs[k] = pvalid(k) ? f[8 + NPR + i] : 1.f;
+            c.sn[k] = pvalid(k) ? f[8 + 2 * NPR + i] : 0.f;
         }
     };
     // One forward step on this lane's elements: hs <- R(alpha hs + beta Uprev) + gamma U.
@@ -192,15 +249,17 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
                 hs[(k * 2 + j) * 4 + q] =
                     (p.h_in != nullptr && pvalid(k)) ? p.h_in[((int64_t)bh * N + n) * P + col0 + q] : 0.f;
             }
-    {
-        StepIn<R, KP> s;
-        load_in(-1, s);
-        outer(s, Up);
-    }
     if (nsup > 0) st_state(ck, hs);
-    for (int64_t t = 0; t < L; ++t) {
-        fwd_step(t, hs, Up);
-        if ((t + 1) % T1 == 0 && t + 1 < L) st_state(ck + (size_t)((t + 1) / T1) * unit_sz, hs);
+    for (int64_t sup = 0; sup < nsup; ++sup) {
+        const int64_t s0 = sup * T1, s1 = s0 + T1 < L ? s0 + T1 : L;
+        stage(s0 - 1, (int)(s1 - s0 + 1));
+        {
+            StepIn<R, KP> s;
+            load_in(s0 - 1, s);
+            outer(s, Up);
+        }
+        for (int64_t t = s0; t < s1; ++t) fwd_step(t, hs, Up);
+        if (s1 < L) st_state(ck + (size_t)(sup + 1) * unit_sz, hs);
     }
 
     // ---- pass B: adjoint, superblocks and sub-blocks from the end --------
@@ -223,6 +282,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
     for (int64_t sup = nsup - 1; sup >= 0; --sup) {
         const int64_t s0 = sup * T1, s1 = s0 + T1 < L ? s0 + T1 : L;
         const int nsub = (int)((s1 - s0 + TB - 1) / TB);
+        stage(s0 - 1, (int)(s1 - s0 + 1));
         // B1: sub-block start states of this superblock
         ld_state(ck + (size_t)sup * unit_sz, hs);
         {
@@ -260,14 +320,14 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
                 load_in(t - 1, prv);
                 float Cv[KP][R][2], dyv[R][4];
                 {
-                    const int64_t tk = tok(t);
+                    const unsigned char* bb = blk(t);
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        ld4(dyv[r], dYg + tk * R * P + r * P + col0);
+                        ld4(dyv[r], io_at(bb, oDY) + r * P + col0);
 #pragma unroll
                         for (int k = 0; k < KP; ++k) {
                             const int i = pvalid(k) ? pair_of(k) : 0;
-                            const float2 v = ld2(Cg + tk * R * N + r * N + 2 * i);
+                            const float2 v = ld2(io_at(bb, oC) + r * N + 2 * i);
                             Cv[k][r][0] = pvalid(k) ? v.x : 0.f;
                             Cv[k][r][1] = pvalid(k) ? v.y : 0.f;
                         }
@@ -447,6 +507,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
                     *reinterpret_cast<f32x4*>(p.dh_in + ((int64_t)bh * N + n) * P + col0) =
                         f32x4{a_nx * dan[e], a_nx * dan[e + 1], a_nx * dan[e + 2], a_nx * dan[e + 3]};
                 }
+        stage(-1, 1);
         StepIn<R, KP> s;
         load_in(-1, s);
         float dXp[R][4], dBp[KP][R][2];
@@ -522,11 +583,27 @@ __global__ void bwd_dA_kernel(const float* part, float* dA, int64_t batch, int64
     dA[h] = s;
 }
 
+// LDS of one workgroup: step states, the per-step partial sums and the
+// staged inputs of T1 + 1 steps.
+size_t bwd_fixed_lds(int64_t N, int64_t P, int64_t R)
+{
+    const int KP = N <= 32 ? 1 : (N <= 64 ? 2 : 4);
+    const int TB = bwd_sub_steps(N);
+    const int64_t NW = P / 16;
+    return sizeof(float) * ((size_t)NW * TB * 8 * KP * 64 + 2 * (size_t)NW * (2 * R * N + N / 2 + 4));
+}
+size_t bwd_step_bytes(int64_t N, int64_t P, int64_t R, int io)
+{
+    const int64_t e = io == 0 ? 4 : 2;
+    return (size_t)((2 * e * R * N + 2 * e * R * P + 4 * (8 + 3 * (N / 2)) + 15) / 16 * 16);
+}
+
 template <typename IO, int R, int KP, int TB>
 hipError_t launch_bwd_t(const BwdParams& p, float* dA, hipStream_t stream)
 {
     const int NW = p.P / 16;
-    const size_t lds = sizeof(float) * ((size_t)NW * TB * 8 * KP * 64 + 2 * (size_t)NW * (2 * R * p.N + p.N / 2 + 4));
+    const size_t lds = bwd_fixed_lds(p.N, p.P, R) +
+                       (size_t)(p.K * TB + 1) * bwd_step_bytes(p.N, p.P, R, sizeof(IO) == 4 ? 0 : 1);
     auto* kern = &bwd_kernel<IO, R, KP, TB>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -551,15 +628,24 @@ hipError_t launch_bwd_r(const BwdParams& p, float* dA, hipStream_t stream)
 
 }  // namespace
 
+int bwd_sub_steps(int64_t N) { return N <= 64 ? 4 : 2; }
+
+int bwd_blocks_per_checkpoint(int64_t N, int64_t P, int64_t R, int io_dtype)
+{
+    const size_t avail = 160 * 1024 - bwd_fixed_lds(N, P, R);
+    const int64_t steps = (int64_t)(avail / bwd_step_bytes(N, P, R, io_dtype)) - 1;
+    const int64_t K = steps / bwd_sub_steps(N);
+    return (int)(K > 8 ? 8 : K);
+}
+
 bool bwd_supported(int64_t N, int64_t P, int64_t R, int io_dtype)
 {
     if (io_dtype != 0 && io_dtype != 1) return false;
     if (R != 1 && R != 2 && R != 4) return false;
-    if (N < 2 || N > 128 || (N % 2) != 0) return false;
-    return P == 16 || P == 32 || P == 64;
+    if (N < 8 || N > 128 || (N % 8) != 0) return false;
+    if (P != 16 && P != 32 && P != 64) return false;
+    return bwd_blocks_per_checkpoint(N, P, R, io_dtype) >= 1;
 }
-
-int bwd_sub_steps(int64_t N) { return N <= 64 ? 4 : 2; }
 
 hipError_t launch_bwd(const BwdParams& p, int io_dtype, float* dA, hipStream_t stream)
 {
