@@ -116,20 +116,32 @@ def traffic_summary(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     out = {"workload": name, "bytes_per_launch": round(fetch + write),
            "fetch_bytes": round(fetch), "write_bytes": round(write),
            "fetch_scale": round(ffac, 4), "write_scale": round(wfac, 4),
-           "calls": ncalls_f, "source_hash": kernel_source_hash()}
+           "calls": ncalls_f, "source_hash": kernel_source_hash(_kind(name))}
     os.makedirs(PROFILE_DIR, exist_ok=True)
     with open(os.path.join(PROFILE_DIR, "%s_traffic.json" % name), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
 
 
-def kernel_source_hash():
+# Device sources each measured kernel is compiled from.
+KERNEL_SOURCES = {
+    "scan": ["m3_device.hpp", "m3_scan_kernel.hpp", "m3_scan_inst.hpp", "m3_scan_f32.hip",
+             "m3_scan_bf16_a.hip", "m3_scan_bf16_b.hip"],
+    "decode": ["m3_device.hpp", "m3_decode.hip"],
+}
+
+
+def kernel_source_hash(kind):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mamba_selective_ssm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def _kind(name):
+    return "decode" if name == "decode" else "scan"
 
 
 def load_traffic(name):
@@ -140,7 +152,7 @@ def load_traffic(name):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_hash") != kernel_source_hash():
+    if d.get("source_hash") != kernel_source_hash(_kind(name)):
         return None
     return d.get("bytes_per_launch")
 
