@@ -179,9 +179,9 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
 // Backward: sub-block length TB, sub-blocks per checkpoint K, checkpoints per
 // (b, h) and the workspace carve-up (checkpoints, scratch, dA shares).
 struct BwdPlan {
-    int TB, K;
+    int TB, K, parts;
     int64_t nsup;
-    size_t unit_floats, ck_bytes, scr_bytes, part_bytes, ws;
+    size_t unit_floats, ck_bytes, scr_bytes, dx_bytes, scal_bytes, dxp_bytes, part_bytes, ws;
 };
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
@@ -196,16 +196,21 @@ m3_status plan_bwd(const m3_scan_bwd_args* a, BwdPlan* out)
     if (!m3::bwd_supported(N, P, R, a->io_dtype)) return M3_ERR_UNSUPPORTED;
     const int64_t nbh = Bt * H;
     if (nbh > (int64_t)1 << 24) return M3_ERR_UNSUPPORTED;
-    const int KP = N <= 32 ? 1 : (N <= 64 ? 2 : 4);
     out->TB = m3::bwd_sub_steps(N);
     out->K = m3::bwd_blocks_per_checkpoint(N, P, R, a->io_dtype);
+    out->parts = m3::bwd_pair_parts(N);
     const int64_t T1 = (int64_t)out->TB * out->K;
     out->nsup = (L + T1 - 1) / T1;
-    out->unit_floats = (size_t)P * 32 * KP;                 // N x P with the pairs padded to 16k
-    out->ck_bytes = round256((size_t)nbh * (size_t)(out->nsup > 0 ? out->nsup : 1) * out->unit_floats * 4);
-    out->scr_bytes = round256((size_t)nbh * out->K * out->unit_floats * 4);
+    const size_t units = (size_t)nbh * out->parts, ntok = (size_t)Bt * L * H;
+    out->unit_floats = (size_t)P * 32;                       // 16 pairs x P of one part
+    out->ck_bytes = round256(units * (size_t)(out->nsup > 0 ? out->nsup : 1) * out->unit_floats * 4);
+    out->scr_bytes = round256(units * out->K * out->unit_floats * 4);
+    out->dx_bytes = round256((size_t)out->parts * ntok * R * P * 4);
+    out->scal_bytes = round256((size_t)out->parts * ntok * 16);
+    out->dxp_bytes = round256((size_t)out->parts * nbh * R * P * 4);
     out->part_bytes = round256((size_t)nbh * 4);
-    out->ws = nbh > 0 ? out->ck_bytes + out->scr_bytes + out->part_bytes : 0;
+    out->ws = nbh > 0 ? out->ck_bytes + out->scr_bytes + out->dx_bytes + out->scal_bytes +
+                            out->dxp_bytes + out->part_bytes : 0;
     return M3_OK;
 }
 
@@ -284,10 +289,20 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
     p.dlam = a->dlam; p.dh_in = a->dh_in; p.dBp = a->dB_prev; p.dxp = a->dx_prev;
     char* ws = static_cast<char*>(a->workspace);
     p.ckpt = reinterpret_cast<float*>(ws);
-    p.scr = reinterpret_cast<float*>(ws + plan.ck_bytes);
-    p.dA_part = reinterpret_cast<float*>(ws + plan.ck_bytes + plan.scr_bytes);
+    ws += plan.ck_bytes;
+    p.scr = reinterpret_cast<float*>(ws);
+    ws += plan.scr_bytes;
+    p.dx_part = reinterpret_cast<float*>(ws);
+    ws += plan.dx_bytes;
+    p.scal = reinterpret_cast<float*>(ws);
+    ws += plan.scal_bytes;
+    p.dxprev_part = reinterpret_cast<float*>(ws);
+    ws += plan.dxp_bytes;
+    p.dA_part = reinterpret_cast<float*>(ws);
     p.L = L; p.H = H; p.N = (int)N; p.P = (int)P; p.R = (int)R;
+    p.ntok = Bt * L * H;
     p.nbh = (int)nbh;
+    p.parts = plan.parts;
     p.TB = plan.TB; p.K = plan.K;
     return hip_status(m3::launch_bwd(p, a->io_dtype, a->dA, static_cast<hipStream_t>(stream)));
 }

@@ -45,18 +45,22 @@ struct BwdParams {
     const float *dh_out;
     float *dx, *dB, *dC, *ddt, *dtheta, *dlam;
     float *dh_in, *dBp, *dxp;
-    float *ckpt;      // [B*H][nsup][N*P] states every T1 steps
-    float *scr;       // [B*H][K][N*P] sub-block start states of one superblock
+    float *ckpt;      // [B*H*parts][nsup][32 P] states every T1 steps
+    float *scr;       // [B*H*parts][K][32 P] sub-block start states of one superblock
+    float *dx_part;   // [parts][B*L*H][R][P] each pair part's share of dX
+    float *scal;      // [parts][B*L*H][4] each part's dalpha, dbeta, dgamma, theta.dphi
+    float *dxprev_part;  // [parts][B*H][R][P]
     float *dA_part;   // [B*H] this unit's share of dA
-    int64_t L, H;
+    int64_t L, H, ntok;
     int N, P, R;
-    int nbh;
+    int nbh, parts;   // (b, h) units; pair parts (16 pairs) per unit
     int TB, K;        // sub-block steps, sub-blocks per superblock (T1 = K * TB)
 };
 
 bool bwd_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
 int bwd_sub_steps(int64_t N);
 int bwd_blocks_per_checkpoint(int64_t N, int64_t P, int64_t R, int io_dtype);
+int bwd_pair_parts(int64_t N);
 hipError_t launch_bwd(const BwdParams& p, int io_dtype, float* dA, hipStream_t stream);
 
 bool decode_supported(int64_t N, int64_t P, int64_t R, int io_dtype);

@@ -17,10 +17,13 @@
 // phi_i = dt theta_i to dt, A, lam, theta.  The initial record gets
 // dh_in = alpha_0 da_0 and dU_prev = beta_0 da_0.
 //
-// One workgroup per (b, h); wave w owns headdim columns 16w .. 16w+15 of the
-// N x P state (lane: 4 columns x the rows of pairs rg + 16k), so each wave
-// reduces dX over its own rows, and the column sums (dB, dC, dphi and the
-// scalar gradients) of the waves meet in LDS once per step (one barrier).
+// One workgroup per (b, h, part of PP = 16 KP rotation pairs); wave w owns
+// headdim columns 16w .. 16w+15 of the part's rows (lane: 4 columns x the rows
+// of pairs rg + 16k), so each wave reduces dX over its own rows, and the column
+// sums (dB, dC, dphi and the scalar gradients) of the waves meet in LDS once
+// per step (one barrier).  dX and the scalar sums of the parts are added in a
+// second kernel in a fixed order (deterministic), which also maps the scalar
+// sums to dt, lam and A.
 // States: a checkpoint every T1 = K*TB steps in HBM (pass A); per superblock
 // the K sub-block start states go to a scratch area (pass B1); per sub-block
 // the TB step states are recomputed into the wave's LDS slots (pass B2) and
@@ -68,20 +71,24 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
     const int NW = blockDim.x >> 6, NT = blockDim.x, tid = threadIdx.x;
     const int N = p.N, NPR = N / 2, P = p.P;
     const int64_t L = p.L, H = p.H;
-    const int bh = blockIdx.x;
+    constexpr int PP = 16 * KP;                   // pairs of one part
+    const int part = blockIdx.x % p.parts;
+    const int bh = blockIdx.x / p.parts;
     const int64_t b = bh / H, h = bh % H;
+    const int p_lo = part * PP;                   // first pair of this part
+    const int NPRp = NPR - p_lo < PP ? NPR - p_lo : PP;
     const int cg = lane & 3, rg = lane >> 2;
     const int col0 = 16 * wv + 4 * cg;
-    const int V = 2 * R * N + NPR + 4;            // per-wave partial sums of one step
+    const int V = 4 * R * PP + PP + 4;            // per-wave partial sums of one step
     float* slots = bsm + (size_t)wv * TB * E * 64;               // this wave's step states
     float* red = bsm + (size_t)NW * TB * E * 64;                 // [2][NW][V]
-    // Staged step inputs, per step: B, C [R][N] and X, dy [R][P] (io), then
-    // float32 [dt, lam, alpha, beta, gamma, -, -, -], theta, cos phi, sin phi
-    // [N/2 each]; a step's block is SB bytes.
+    // Staged step inputs, per step: the part's rows of B, C [R][2 PP] and X,
+    // dy [R][P] (io), then float32 [dt, lam, alpha, beta, gamma, -, -, -],
+    // theta, cos phi, sin phi [PP each]; a step's block is SB bytes.
     constexpr int ESZ = (int)sizeof(IO);
-    const int oC = ESZ * R * N, oX = 2 * ESZ * R * N, oDY = oX + ESZ * R * P;
+    const int oC = ESZ * R * 2 * PP, oX = 2 * oC, oDY = oX + ESZ * R * P;
     const int oSC = oDY + ESZ * R * P;
-    const int SB = (oSC + 4 * (8 + 3 * NPR) + 15) / 16 * 16;
+    const int SB = (oSC + 4 * (8 + 3 * PP) + 15) / 16 * 16;
     unsigned char* stg = reinterpret_cast<unsigned char*>(red + 2 * (size_t)NW * V);
     int64_t stg_t0 = 0;                                          // step held in block 0
 
@@ -93,24 +100,29 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
     const IO* Xpr = reinterpret_cast<const IO*>(p.xp_in);
     const float A = p.A[h];
     auto tok = [&](int64_t t) -> int64_t { return (b * L + t) * H + h; };
-    auto pair_of = [&](int k) { return rg + 16 * k; };
-    auto pvalid = [&](int k) { return rg + 16 * k < NPR; };
+    auto lp_of = [&](int k) { return rg + 16 * k; };             // pair within the part
+    auto pair_of = [&](int k) { return p_lo + rg + 16 * k; };    // pair of the state
+    auto pvalid = [&](int k) { return rg + 16 * k < NPRp; };
 
     // Stage steps t0 .. t0+cnt-1 (t0 may be -1: the state record's previous
     // token, or zeros) into LDS; every thread of the workgroup takes part.
     auto stage = [&](int64_t t0, int cnt) {
         __syncthreads();                                         // previous block's readers done
         stg_t0 = t0;
-        const int q_io = (2 * ESZ * R * N + 2 * ESZ * R * P) / 16;   // 16-byte pieces per step
+        const int q_io = (2 * oC + 2 * ESZ * R * P) / 16;          // 16-byte pieces per step
+        const int rowb = ESZ * 2 * PP;                           // staged bytes of one B/C row
         for (int idx = tid; idx < cnt * q_io; idx += NT) {
             const int sidx = idx / q_io, piece = idx % q_io;
             const int64_t t = t0 + sidx;
             const int off = piece * 16;                          // byte offset in the step block
             const unsigned char* src = nullptr;
-            if (off < oX) {                                      // B or C
-                const int m = off / oC, o = off % oC;
-                if (t >= 0) src = reinterpret_cast<const unsigned char*>(m == 0 ? Bg : Cg) + tok(t) * (int64_t)oC + o;
-                else if (m == 0 && Bpr != nullptr) src = reinterpret_cast<const unsigned char*>(Bpr) + (int64_t)bh * oC + o;
+            if (off < oX) {                                      // the part's rows of B or C
+                const int m = off / oC, o = off % oC, r = o / rowb, ob = o % rowb;
+                const int64_t go = (int64_t)ESZ * (r * N + 2 * p_lo) + ob;
+                if (ob < ESZ * 2 * NPRp) {
+                    if (t >= 0) src = reinterpret_cast<const unsigned char*>(m == 0 ? Bg : Cg) + tok(t) * (int64_t)(ESZ * R * N) + go;
+                    else if (m == 0 && Bpr != nullptr) src = reinterpret_cast<const unsigned char*>(Bpr) + (int64_t)bh * (ESZ * R * N) + go;
+                }
             } else {                                             // X or dy
                 const int m = (off - oX) / (ESZ * R * P), o = (off - oX) % (ESZ * R * P);
                 if (t >= 0) src = reinterpret_cast<const unsigned char*>(m == 0 ? Xg : dYg) + tok(t) * (int64_t)(ESZ * R * P) + o;
@@ -121,12 +133,12 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
             *reinterpret_cast<uint4*>(stg + (size_t)sidx * SB + off) = v;
         }
         // per-step scalars and per-pair rotations, computed once per stage
-        for (int idx = tid; idx < cnt * (NPR + 1); idx += NT) {
-            const int sidx = idx / (NPR + 1), j = idx % (NPR + 1);
+        for (int idx = tid; idx < cnt * (PP + 1); idx += NT) {
+            const int sidx = idx / (PP + 1), j = idx % (PP + 1);
             const int64_t t = t0 + sidx;
             float* f = reinterpret_cast<float*>(stg + (size_t)sidx * SB + oSC);
             const float d = t >= 0 ? p.dt[tok(t)] : 0.f;
-            if (j == NPR) {
+            if (j == PP) {
                 const float lm = t >= 0 ? p.lam[tok(t)] : 0.f;
                 const float al = expf(d * A);
                 f[0] = d;
@@ -135,12 +147,12 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
                 f[3] = (1.f - lm) * d * al;
                 f[4] = lm * d;
             } else {
-                const float th = t >= 0 ? p.theta[tok(t) * NPR + j] : 0.f;
+                const float th = (t >= 0 && j < NPRp) ? p.theta[tok(t) * NPR + p_lo + j] : 0.f;
                 float sn, cs;
                 sincosf(d * th, &sn, &cs);
                 f[8 + j] = th;
-                f[8 + NPR + j] = cs;
-                f[8 + 2 * NPR + j] = sn;
+                f[8 + PP + j] = cs;
+                f[8 + 2 * PP + j] = sn;
             }
         }
         __syncthreads();
@@ -157,10 +169,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
             ld4(s.X[r], io_at(bb, oX) + r * P + col0);
 #pragma unroll
             for (int k = 0; k < KP; ++k) {
-                const int i = pvalid(k) ? pair_of(k) : 0;
-                const float2 v = ld2(io_at(bb, 0) + r * N + 2 * i);
-                s.B[k][r][0] = pvalid(k) ? v.x : 0.f;
-                s.B[k][r][1] = pvalid(k) ? v.y : 0.f;
+                const float2 v = ld2(io_at(bb, 0) + r * 2 * PP + 2 * lp_of(k));
+                s.B[k][r][0] = v.x;                              // zero-padded past the part's pairs
+                s.B[k][r][1] = v.y;
             }
         }
     };
@@ -188,10 +199,10 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
         c.ga = f[4];
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
-            const int i = pvalid(k) ? pair_of(k) : 0;
-            c.th[k] = pvalid(k) ? f[8 + i] : 0.f;
-            c.cs[k] = pvalid(k) ? f[8 + NPR + i] : 1.f;
-            c.sn[k] = pvalid(k) ? f[8 + 2 * NPR + i] : 0.f;
+            const int i = lp_of(k);
+            c.th[k] = f[8 + i];                                  // zero past the part's pairs
+            c.cs[k] = f[8 + PP + i];
+            c.sn[k] = f[8 + 2 * PP + i];
         }
     };
     // One forward step on this lane's elements: hs <- R(alpha hs + beta Uprev) + gamma U.
@@ -233,8 +244,8 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
     const size_t unit_sz = (size_t)NW * E * 64;                 // = N * P floats (padded pairs)
     const int64_t T1 = (int64_t)p.K * TB;
     const int64_t nsup = (L + T1 - 1) / T1;
-    float* ck = p.ckpt + (size_t)bh * (size_t)(nsup > 0 ? nsup : 1) * unit_sz + (size_t)wv * E * 64;
-    float* sc = p.scr + (size_t)bh * p.K * unit_sz + (size_t)wv * E * 64;
+    float* ck = p.ckpt + (size_t)blockIdx.x * (size_t)(nsup > 0 ? nsup : 1) * unit_sz + (size_t)wv * E * 64;
+    float* sc = p.scr + (size_t)blockIdx.x * p.K * unit_sz + (size_t)wv * E * 64;
     // ck/sc point at this wave's part of entry 0; entry j adds j * unit_sz.
 
     // ---- pass A: checkpoints every T1 steps ------------------------------
@@ -276,7 +287,6 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
                     ? p.dh_out[((int64_t)bh * N + n) * P + col0 + q] : 0.f;
             }
     float a_nx = 1.f, b_nx = 0.f;
-    float dA_acc = 0.f;
     int par = 0;
 
     for (int64_t sup = nsup - 1; sup >= 0; --sup) {
@@ -326,10 +336,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
                         ld4(dyv[r], io_at(bb, oDY) + r * P + col0);
 #pragma unroll
                         for (int k = 0; k < KP; ++k) {
-                            const int i = pvalid(k) ? pair_of(k) : 0;
-                            const float2 v = ld2(io_at(bb, oC) + r * N + 2 * i);
-                            Cv[k][r][0] = pvalid(k) ? v.x : 0.f;
-                            Cv[k][r][1] = pvalid(k) ? v.y : 0.f;
+                            const float2 v = ld2(io_at(bb, oC) + r * 2 * PP + 2 * lp_of(k));
+                            Cv[k][r][0] = v.x;
+                            Cv[k][r][1] = v.y;
                         }
                     }
                 }
@@ -436,55 +445,44 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
                     s_th += __shfl_xor(s_th, off, 64);
                 }
                 const int64_t tk = tok(t);
-                if (rg == 0) {
+                if (rg == 0) {                                   // this part's share of dX
 #pragma unroll
                     for (int r = 0; r < R; ++r)
-                        *reinterpret_cast<f32x4*>(p.dx + tk * R * P + r * P + col0) =
+                        *reinterpret_cast<f32x4*>(p.dx_part + ((size_t)part * p.ntok + tk) * R * P + r * P + col0) =
                             f32x4{dXp[r][0], dXp[r][1], dXp[r][2], dXp[r][3]};
                 }
                 float* rb = red + ((size_t)par * NW + wv) * V;
                 if (cg == 0) {
 #pragma unroll
                     for (int k = 0; k < KP; ++k) {
-                        if (pvalid(k)) {
-                            const int i = pair_of(k);
+                        const int i = lp_of(k);
 #pragma unroll
-                            for (int r = 0; r < R; ++r) {
-                                *reinterpret_cast<float2*>(rb + r * N + 2 * i) =
-                                    make_float2(dBp[k][r][0], dBp[k][r][1]);
-                                *reinterpret_cast<float2*>(rb + R * N + r * N + 2 * i) =
-                                    make_float2(dCp[k][r][0], dCp[k][r][1]);
-                            }
-                            rb[2 * R * N + i] = dph[k];
+                        for (int r = 0; r < R; ++r) {
+                            *reinterpret_cast<float2*>(rb + r * 2 * PP + 2 * i) =
+                                make_float2(dBp[k][r][0], dBp[k][r][1]);
+                            *reinterpret_cast<float2*>(rb + 2 * R * PP + r * 2 * PP + 2 * i) =
+                                make_float2(dCp[k][r][0], dCp[k][r][1]);
                         }
+                        rb[4 * R * PP + i] = dph[k];
                     }
                 }
-                if (lane == 0) {
-                    rb[2 * R * N + NPR + 0] = s_a;
-                    rb[2 * R * N + NPR + 1] = s_b;
-                    rb[2 * R * N + NPR + 2] = s_g;
-                    rb[2 * R * N + NPR + 3] = s_th;
-                }
+                if (lane == 0)
+                    *reinterpret_cast<f32x4*>(rb + 4 * R * PP + PP) = f32x4{s_a, s_b, s_g, s_th};
                 __syncthreads();
                 // sums over the waves (column slices); buffers alternate by step
                 const float* r0b = red + (size_t)par * NW * V;
-                for (int v = tid; v < 2 * R * N + NPR; v += NT) {
+                for (int v = tid; v < 4 * R * PP + PP + 4; v += NT) {
                     float sum = 0.f;
                     for (int w = 0; w < NW; ++w) sum += r0b[(size_t)w * V + v];
-                    if (v < R * N) p.dB[tk * R * N + v] = sum;
-                    else if (v < 2 * R * N) p.dC[tk * R * N + (v - R * N)] = sum;
-                    else p.dtheta[tk * NPR + (v - 2 * R * N)] = c.d * sum;
-                }
-                if (tid == 0) {
-                    float da_ = 0.f, db_ = 0.f, dg_ = 0.f, dth_ = 0.f;
-                    for (int w = 0; w < NW; ++w) {
-                        const float* q = r0b + (size_t)w * V + 2 * R * N + NPR;
-                        da_ += q[0]; db_ += q[1]; dg_ += q[2]; dth_ += q[3];
+                    if (v < 4 * R * PP) {
+                        const int m = v / (2 * R * PP), o = v % (2 * R * PP), r = o / (2 * PP), ro = o % (2 * PP);
+                        if (ro < 2 * NPRp) (m == 0 ? p.dB : p.dC)[tk * R * N + r * N + 2 * p_lo + ro] = sum;
+                    } else if (v < 4 * R * PP + PP) {
+                        const int i = v - 4 * R * PP;
+                        if (i < NPRp) p.dtheta[tk * NPR + p_lo + i] = c.d * sum;
+                    } else {                                     // this part's scalar sums
+                        p.scal[((size_t)part * p.ntok + tk) * 4 + (v - 4 * R * PP - PP)] = sum;
                     }
-                    p.ddt[tk] = da_ * c.al * A + db_ * (1.f - c.lm) * c.al * (1.f + c.d * A)
-                                + dg_ * c.lm + dth_;
-                    p.dlam[tk] = -c.d * c.al * db_ + c.d * dg_;
-                    dA_acc += da_ * c.al * c.d + db_ * (1.f - c.lm) * c.d * c.d * c.al;
                 }
                 par ^= 1;
 #pragma unroll
@@ -549,28 +547,76 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
         if (rg == 0) {
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                *reinterpret_cast<f32x4*>(p.dxp + (int64_t)bh * R * P + r * P + col0) =
+                *reinterpret_cast<f32x4*>(p.dxprev_part + ((size_t)part * p.nbh + bh) * R * P + r * P + col0) =
                     f32x4{dXp[r][0], dXp[r][1], dXp[r][2], dXp[r][3]};
         }
         float* rb = red + ((size_t)par * NW + wv) * V;
         if (cg == 0) {
 #pragma unroll
             for (int k = 0; k < KP; ++k)
-                if (pvalid(k))
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        *reinterpret_cast<float2*>(rb + r * N + 2 * pair_of(k)) =
-                            make_float2(dBp[k][r][0], dBp[k][r][1]);
+                for (int r = 0; r < R; ++r)
+                    *reinterpret_cast<float2*>(rb + r * 2 * PP + 2 * lp_of(k)) =
+                        make_float2(dBp[k][r][0], dBp[k][r][1]);
         }
         __syncthreads();
         const float* r0b = red + (size_t)par * NW * V;
-        for (int v = tid; v < R * N; v += NT) {
+        for (int v = tid; v < 2 * R * PP; v += NT) {
             float sum = 0.f;
             for (int w = 0; w < NW; ++w) sum += r0b[(size_t)w * V + v];
-            p.dBp[(int64_t)bh * R * N + v] = sum;
+            const int r = v / (2 * PP), ro = v % (2 * PP);
+            if (ro < 2 * NPRp) p.dBp[(int64_t)bh * R * N + r * N + 2 * p_lo + ro] = sum;
         }
     }
-    if (tid == 0) p.dA_part[bh] = dA_acc;
+}
+
+// Per (b, h): dX and the scalar sums of the pair parts added in part order,
+// the scalar sums mapped through alpha = e^{dt A}, beta = (1-lam) dt alpha,
+// gamma = lam dt (and phi = dt theta) to dt and lam, and this unit's share of
+// dA; the record's dx_prev likewise.
+template <int R>
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdParams p)
+{
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int64_t H = p.H, L = p.L, b = bh / H, h = bh % H;
+    const int P = p.P, S = p.parts;
+    const float A = p.A[h];
+    const int64_t RP4 = (int64_t)R * P / 4;
+    for (int64_t idx = tid; idx < L * RP4; idx += 256) {
+        const int64_t t = idx / RP4, q = idx % RP4;
+        const int64_t tk = (b * L + t) * H + h;
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < S; ++k)
+            sum += *reinterpret_cast<const f32x4*>(p.dx_part + ((size_t)k * p.ntok + tk) * R * P + 4 * q);
+        *reinterpret_cast<f32x4*>(p.dx + tk * R * P + 4 * q) = sum;
+    }
+    float dA_acc = 0.f;
+    for (int64_t t = tid; t < L; t += 256) {
+        const int64_t tk = (b * L + t) * H + h;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};      // dalpha, dbeta, dgamma, sum_i theta_i dphi_i
+        for (int k = 0; k < S; ++k) sc += *reinterpret_cast<const f32x4*>(p.scal + ((size_t)k * p.ntok + tk) * 4);
+        const float d = p.dt[tk], lm = p.lam[tk], al = expf(d * A);
+        p.ddt[tk] = sc[0] * al * A + sc[1] * (1.f - lm) * al * (1.f + d * A) + sc[2] * lm + sc[3];
+        p.dlam[tk] = -d * al * sc[1] + d * sc[2];
+        dA_acc += sc[0] * al * d + sc[1] * (1.f - lm) * d * d * al;
+    }
+    if (p.dxp != nullptr) {
+        for (int64_t q = tid; q < RP4; q += 256) {
+            f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < S; ++k)
+                sum += *reinterpret_cast<const f32x4*>(p.dxprev_part + ((size_t)k * p.nbh + bh) * R * P + 4 * q);
+            *reinterpret_cast<f32x4*>(p.dxp + (int64_t)bh * R * P + 4 * q) = sum;
+        }
+    }
+    // this unit's dA share: a fixed-order tree over the workgroup
+    __shared__ float red[256];
+    red[tid] = dA_acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) p.dA_part[bh] = red[0];
 }
 
 // dA[h] = sum over the batch rows of the units' shares (fixed order).
@@ -584,18 +630,21 @@ __global__ void bwd_dA_kernel(const float* part, float* dA, int64_t batch, int64
 }
 
 // LDS of one workgroup: step states, the per-step partial sums and the
-// staged inputs of T1 + 1 steps.
+// staged inputs of T1 + 1 steps (16 pairs per part: KP = 1).
+constexpr int kBwdPP = 16;
+constexpr size_t kBwdLds = 80 * 1024;     // two workgroups per compute unit
 size_t bwd_fixed_lds(int64_t N, int64_t P, int64_t R)
 {
-    const int KP = N <= 32 ? 1 : (N <= 64 ? 2 : 4);
+    (void)N;
     const int TB = bwd_sub_steps(N);
     const int64_t NW = P / 16;
-    return sizeof(float) * ((size_t)NW * TB * 8 * KP * 64 + 2 * (size_t)NW * (2 * R * N + N / 2 + 4));
+    return sizeof(float) * ((size_t)NW * TB * 8 * 64 + 2 * (size_t)NW * (4 * R * kBwdPP + kBwdPP + 4));
 }
 size_t bwd_step_bytes(int64_t N, int64_t P, int64_t R, int io)
 {
+    (void)N;
     const int64_t e = io == 0 ? 4 : 2;
-    return (size_t)((2 * e * R * N + 2 * e * R * P + 4 * (8 + 3 * (N / 2)) + 15) / 16 * 16);
+    return (size_t)((4 * e * R * kBwdPP + 2 * e * R * P + 4 * (8 + 3 * kBwdPP) + 15) / 16 * 16);
 }
 
 template <typename IO, int R, int KP, int TB>
@@ -609,8 +658,11 @@ hipError_t launch_bwd_t(const BwdParams& p, float* dA, hipStream_t stream)
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.nbh), dim3(64 * NW), lds, stream, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(p.nbh * p.parts)), dim3(64 * NW), lds, stream, p);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_finalize_kernel<R>, dim3((unsigned)p.nbh), dim3(256), 0, stream, p);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t batch = p.nbh / p.H;
     hipLaunchKernelGGL(bwd_dA_kernel, dim3((unsigned)((p.H + 63) / 64)), dim3(64), 0, stream,
@@ -621,18 +673,18 @@ hipError_t launch_bwd_t(const BwdParams& p, float* dA, hipStream_t stream)
 template <typename IO, int R>
 hipError_t launch_bwd_r(const BwdParams& p, float* dA, hipStream_t stream)
 {
-    if (p.N <= 32) return launch_bwd_t<IO, R, 1, 4>(p, dA, stream);
-    if (p.N <= 64) return launch_bwd_t<IO, R, 2, 4>(p, dA, stream);
-    return launch_bwd_t<IO, R, 4, 2>(p, dA, stream);
+    return launch_bwd_t<IO, R, 1, 4>(p, dA, stream);
 }
 
 }  // namespace
 
-int bwd_sub_steps(int64_t N) { return N <= 64 ? 4 : 2; }
+int bwd_sub_steps(int64_t N) { (void)N; return 4; }
+
+int bwd_pair_parts(int64_t N) { return (int)((N / 2 + kBwdPP - 1) / kBwdPP); }
 
 int bwd_blocks_per_checkpoint(int64_t N, int64_t P, int64_t R, int io_dtype)
 {
-    const size_t avail = 160 * 1024 - bwd_fixed_lds(N, P, R);
+    const size_t avail = kBwdLds - bwd_fixed_lds(N, P, R);
     const int64_t steps = (int64_t)(avail / bwd_step_bytes(N, P, R, io_dtype)) - 1;
     const int64_t K = steps / bwd_sub_steps(N);
     return (int)(K > 8 ? 8 : K);
