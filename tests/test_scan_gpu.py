@@ -145,3 +145,31 @@ def test_segment_workspace_reused_and_uncleared():
     for y, h in outs:
         assert rel_err(f64(y), yr) <= TOL["bf16"] and rel_err(f64(h), hr) <= TOL["bf16"]
         assert torch.equal(y, outs[0][0]) and torch.equal(h, outs[0][1])
+
+
+def test_segmented_scan_graph_replays():
+    """A segmented scan captured in a HIP graph: every replay (with eager work
+    and synchronisation between replays) equals the eager call."""
+    w = workload(2, 1200, 4, 1, 64, 64, io="bf16", dt_mu=-1.0)
+    say("case graph replay: %s segments=5" % (w,))
+    inp = synth.make_scan_inputs(w, 72, DEV)
+    args = [inp[k] for k in ("x", "B", "C", "dt", "A", "theta", "lam")]
+    need = m3_scan_workspace_bytes(inp["x"], inp["B"], segments=5)
+    ws = torch.zeros((need,), dtype=torch.uint8, device=DEV)
+    y_ref, s_ref = m3_scan_fwd(*args, segments=5, workspace=ws)
+    y = torch.empty_like(y_ref)
+    st = State(torch.empty_like(s_ref.h), torch.empty_like(s_ref.B_prev), torch.empty_like(s_ref.x_prev))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            m3_scan_fwd(*args, segments=5, workspace=ws, y=y, state_out=st)
+    torch.cuda.synchronize()
+    for i in range(4):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), i
+        assert torch.equal(st.h, s_ref.h), i
+        _ = (inp["x"].float() * 2).sum().item()      # eager work between replays
