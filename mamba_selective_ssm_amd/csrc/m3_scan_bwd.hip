@@ -56,6 +56,23 @@ __device__ __forceinline__ void ld4(float (&d)[4], const float* p) {
     for (int e = 0; e < 4; ++e) d[e] = v[e];
 }
 
+// Cross-lane sums on the DPP paths (no LDS round trip): over the 4 lanes of
+// a quad (one row group's columns), over the lanes of a 16-lane row with the
+// same lane % 4, and over the whole wave (inclusive scan, then lane 63).
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v += dpp_moved<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]
+    v += dpp_moved<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]
+    return v;
+}
+__device__ __forceinline__ float row_class_sum(float v)
+{
+    v += dpp_moved<0x124, 0xf>(v);  // row_ror:4
+    v += dpp_moved<0x128, 0xf>(v);  // row_ror:8
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) { return wave_read_lane(wave_inclusive_sum(v), 63); }
+
 template <int R, int KP> struct StepIn {
     float B[KP][R][2];    // rows 2i, 2i+1 of this lane's pairs
     float X[R][4];        // this lane's 4 columns
@@ -417,33 +434,31 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
                     }
                 // column sums within the wave: over the 4 lanes of a row group
 #pragma unroll
-                for (int off = 1; off < 4; off <<= 1) {
-#pragma unroll
-                    for (int k = 0; k < KP; ++k) {
-                        dph[k] += __shfl_xor(dph[k], off, 64);
-#pragma unroll
-                        for (int r = 0; r < R; ++r)
-#pragma unroll
-                            for (int j = 0; j < 2; ++j) {
-                                dBp[k][r][j] += __shfl_xor(dBp[k][r][j], off, 64);
-                                dCp[k][r][j] += __shfl_xor(dCp[k][r][j], off, 64);
-                            }
-                    }
-                }
-                // row sums within the wave: over the 16 row groups
-#pragma unroll
-                for (int off = 4; off < 64; off <<= 1)
+                for (int k = 0; k < KP; ++k) {
+                    dph[k] = quad_sum(dph[k]);
 #pragma unroll
                     for (int r = 0; r < R; ++r)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) dXp[r][q] += __shfl_xor(dXp[r][q], off, 64);
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    s_a += __shfl_xor(s_a, off, 64);
-                    s_b += __shfl_xor(s_b, off, 64);
-                    s_g += __shfl_xor(s_g, off, 64);
-                    s_th += __shfl_xor(s_th, off, 64);
+                        for (int j = 0; j < 2; ++j) {
+                            dBp[k][r][j] = quad_sum(dBp[k][r][j]);
+                            dCp[k][r][j] = quad_sum(dCp[k][r][j]);
+                        }
                 }
+                // row sums within the wave: over the 16 row groups (4 per
+                // 16-lane row on DPP, then across the 4 rows)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float v = row_class_sum(dXp[r][q]);
+                        v += __shfl_xor(v, 16, 64);
+                        v += __shfl_xor(v, 32, 64);
+                        dXp[r][q] = v;
+                    }
+                s_a = wave_sum(s_a);
+                s_b = wave_sum(s_b);
+                s_g = wave_sum(s_g);
+                s_th = wave_sum(s_th);
                 const int64_t tk = tok(t);
                 if (rg == 0) {                                   // this part's share of dX
 #pragma unroll
