@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define M3_ABI_VERSION 2
+#define M3_ABI_VERSION 3
 
 typedef enum {
     M3_F32 = 0,
@@ -105,6 +105,12 @@ typedef enum {
 } m3_phase_mode;
 
 typedef enum {
+    M3_BWD_AUTO = 0,       /* chunked where supported, else step by step */
+    M3_BWD_STEP = 1,       /* adjoint recurrence step by step */
+    M3_BWD_CHUNKED = 2     /* reverse mode of the chunked form */
+} m3_bwd_method;
+
+typedef enum {
     M3_OK = 0,
     M3_ERR_NULL = -1,        /* a required pointer is NULL, or the state record is partial */
     M3_ERR_SHAPE = -2,       /* a negative dimension, zero headdim/dstate/rank, odd dstate */
@@ -114,7 +120,7 @@ typedef enum {
     M3_ERR_WORKSPACE = -6,   /* workspace missing or smaller than m3_scan_workspace_bytes */
     M3_ERR_ALIAS = -7,       /* an output overlaps an input it must not overlap */
     M3_ERR_HIP = -8,         /* a HIP call failed; see m3_last_hip_error() */
-    M3_ERR_OPTION = -9       /* an m3_options field is out of range */
+    M3_ERR_OPTION = -9       /* an m3_options field or the gradient method is out of range */
 } m3_status;
 
 /*
@@ -218,9 +224,7 @@ typedef struct {
  * Arguments of m3_scan_bwd: the gradient of a scan (m3_scan_fwd without
  * options) for training.  Given dy = dLoss/dy and optionally dh_out =
  * dLoss/dh_L, it returns the gradients of Loss = sum(dy * y) + sum(dh_out *
- * h_L) with respect to every input.  The recurrence is differentiated step by
- * step (the adjoint runs backward in time; forward states are recomputed from
- * checkpoints kept in the workspace).
+ * h_L) with respect to every input, by one of two methods (see below).
  *   inputs   as m3_scan_args: x, B, C (io dtype), dt, A [nheads], theta, lam
  *            (float32), optional state record h_in, B_prev_in, x_prev_in
  *   dy       [batch, seqlen, nheads, rank, headdim] io dtype
@@ -231,15 +235,29 @@ typedef struct {
  *            dx_prev [batch, nheads, rank, headdim] (gradients with respect to
  *            the input state record, zero record when none was given)
  *   workspace  m3_scan_bwd_workspace_bytes(args) bytes, 256-byte aligned
- * Supported: dstate a multiple of 8 up to 128, headdim 16, 32 or 64, rank 1,
- * 2 or 4.
+ *   method   an m3_bwd_method: how the gradient is computed (below)
+ * Methods:
+ *   M3_BWD_STEP     the adjoint recurrence step by step, backward in time,
+ *                   forward states recomputed from checkpoints every few
+ *                   steps.  Supported: dstate a multiple of 8 up to 128,
+ *                   headdim 16, 32 or 64, rank 1, 2 or 4.
+ *   M3_BWD_CHUNKED  the reverse mode of the chunked (SSD) form the prefill
+ *                   evaluates: chunk-local sums, a scan of the chunk-boundary
+ *                   states forward and of their adjoints backward, then every
+ *                   gradient of a chunk from its boundary states on matrix
+ *                   cores (64 operand rows per chunk: 64 / rank tokens).
+ *                   Supported: dstate 32, 64 or 128 (float32: 32 or 64),
+ *                   headdim 32 or 64, rank 1, 2 or 4.
+ *   M3_BWD_AUTO     chunked where supported, else step by step.
+ * A method that does not support the sizes returns M3_ERR_UNSUPPORTED; any
+ * other value returns M3_ERR_OPTION.  The methods agree to rounding.
  * Every output is written (no accumulation into the caller's buffers); the
  * result is deterministic.
  */
 typedef struct {
     int64_t batch, seqlen, nheads, headdim, dstate, rank;
     int32_t io_dtype;
-    int32_t reserved;
+    int32_t method;                     /* m3_bwd_method */
     const void *x, *B, *C;
     const float *dt, *A, *theta, *lam;
     const float *h_in;
@@ -264,12 +282,20 @@ size_t m3_scan_workspace_bytes(const m3_scan_args *args);
 /* Gradient of a scan.  Enqueued on `stream`; allocates nothing. */
 m3_status m3_scan_bwd(const m3_scan_bwd_args *args, void *stream);
 
-/* Workspace bytes m3_scan_bwd needs (checkpointed states every few steps per
- * (batch, head)); 0 for arguments it would reject. */
+/* Workspace bytes m3_scan_bwd needs for these arguments and their method
+ * (step by step: states checkpointed every few steps per (batch, head);
+ * chunked: the chunk-local sums and the state and adjoint at every chunk
+ * boundary); 0 for arguments it would reject. */
 size_t m3_scan_bwd_workspace_bytes(const m3_scan_bwd_args *args);
 
-/* 1 when (dstate, headdim, rank, io_dtype) is supported by m3_scan_bwd. */
+/* 1 when (dstate, headdim, rank, io_dtype) is supported by m3_scan_bwd with
+ * some method (M3_BWD_AUTO), else 0. */
 int m3_scan_bwd_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t io_dtype);
+
+/* 1 when m3_scan_bwd supports (dstate, headdim, rank, io_dtype) with the
+ * given m3_bwd_method, else 0. */
+int m3_scan_bwd_method_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t io_dtype,
+                                 int32_t method);
 
 /* One decode step, state record updated in place.  Enqueued on `stream`. */
 m3_status m3_decode_step(const m3_decode_args *args, void *stream);

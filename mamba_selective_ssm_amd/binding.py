@@ -91,7 +91,7 @@ class ScanBwdArgs(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
                 ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("rank", ctypes.c_int64),
-                ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("method", ctypes.c_int32),
                 ("x", _vp), ("B", _vp), ("C", _vp),
                 ("dt", _vp), ("A", _vp), ("theta", _vp), ("lam", _vp),
                 ("h_in", _vp), ("B_prev_in", _vp), ("x_prev_in", _vp),
@@ -129,6 +129,9 @@ def load_library():
         lib.m3_scan_bwd_supported.restype = ctypes.c_int
         lib.m3_scan_bwd_supported.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                               ctypes.c_int32]
+        lib.m3_scan_bwd_method_supported.restype = ctypes.c_int
+        lib.m3_scan_bwd_method_supported.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                     ctypes.c_int32, ctypes.c_int32]
         lib.m3_decode_step.restype = ctypes.c_int
         lib.m3_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         lib.m3_scan_workspace_bytes.restype = ctypes.c_size_t
@@ -423,11 +426,17 @@ class ScanGrads(NamedTuple):
     dx_prev: Optional[torch.Tensor]
 
 
-def m3_scan_bwd_supported(dstate: int, headdim: int, rank: int, io_dtype: int) -> bool:
-    return bool(load_library().m3_scan_bwd_supported(dstate, headdim, rank, io_dtype))
+BWD_METHODS = {"auto": 0, "step": 1, "chunked": 2}
 
 
-def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace):
+def m3_scan_bwd_supported(dstate: int, headdim: int, rank: int, io_dtype: int,
+                          method: str = "auto") -> bool:
+    return bool(load_library().m3_scan_bwd_method_supported(dstate, headdim, rank, io_dtype,
+                                                            BWD_METHODS[method]))
+
+
+def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace,
+                 method="auto"):
     lib = load_library()
     Bt, L, H, R, P = x.shape
     N = B.shape[-1]
@@ -452,8 +461,10 @@ def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, wor
                   torch.empty(Bt, H, N, P, **f32) if state_grads else None,
                   torch.empty(Bt, H, R, N, **f32) if state_grads else None,
                   torch.empty(Bt, H, R, P, **f32) if state_grads else None)
+    if method not in BWD_METHODS:
+        raise ValueError("method must be one of %s" % sorted(BWD_METHODS))
     a = ScanBwdArgs(batch=Bt, seqlen=L, nheads=H, headdim=P, dstate=N, rank=R, io_dtype=io,
-                    x=_ptr(x), B=_ptr(B), C=_ptr(C), dt=_ptr(dt), A=_ptr(A), theta=_ptr(theta),
+                    method=BWD_METHODS[method], x=_ptr(x), B=_ptr(B), C=_ptr(C), dt=_ptr(dt), A=_ptr(A), theta=_ptr(theta),
                     lam=_ptr(lam),
                     h_in=_ptr(state.h) if state else None,
                     B_prev_in=_ptr(state.B_prev) if state else None,
@@ -472,11 +483,15 @@ def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, wor
 
 def m3_scan_bwd(x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
                 dh_out: Optional[torch.Tensor] = None, *, state_grads: bool = True,
-                workspace: Optional[torch.Tensor] = None, stream=None) -> ScanGrads:
+                workspace: Optional[torch.Tensor] = None, method: str = "auto",
+                stream=None) -> ScanGrads:
     """Gradients of sum(dy * y) + sum(dh_out * h_L) of m3_scan_fwd (no options)
     with respect to every input; ``state_grads`` also returns those of the
-    input state record (zero record when ``state`` is None)."""
-    a, g, _ = _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace)
+    input state record (zero record when ``state`` is None).  ``method``:
+    "chunked" (reverse mode of the chunked form), "step" (adjoint recurrence
+    step by step) or "auto" (chunked where supported)."""
+    a, g, _ = _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace,
+                           method)
     st = load_library().m3_scan_bwd(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_bwd")
@@ -488,10 +503,11 @@ class ScanBwdCall:
 
     def __init__(self, x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
                  dh_out: Optional[torch.Tensor] = None, *, state_grads: bool = True,
-                 workspace: Optional[torch.Tensor] = None):
+                 workspace: Optional[torch.Tensor] = None, method: str = "auto"):
         self._keep = (x, B, C, dt, A, theta, lam, dy, state, dh_out)
         self.args, self.grads, self.workspace = _prepare_bwd(x, B, C, dt, A, theta, lam, dy,
-                                                             state, dh_out, state_grads, workspace)
+                                                             state, dh_out, state_grads, workspace,
+                                                             method)
         self._ref = ctypes.byref(self.args)
         self._fn = load_library().m3_scan_bwd
 

@@ -176,15 +176,27 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
     return M3_OK;
 }
 
-// Backward: sub-block length TB, sub-blocks per checkpoint K, checkpoints per
-// (b, h) and the workspace carve-up (checkpoints, scratch, dA shares).
+// Backward.  Step method: sub-block length TB, sub-blocks per checkpoint K,
+// checkpoints per (b, h) and the workspace carve-up (checkpoints, scratch,
+// dA shares).  Chunked method: chunks per (b, h) and its carve-up.
 struct BwdPlan {
+    int method;                 // M3_BWD_STEP or M3_BWD_CHUNKED
     int TB, K, parts;
     int64_t nsup;
-    size_t unit_floats, ck_bytes, scr_bytes, dx_bytes, scal_bytes, dxp_bytes, part_bytes, ws;
+    size_t unit_floats, ck_bytes, scr_bytes, dx_bytes, scal_bytes, dxp_bytes, part_bytes;
+    int64_t nc;
+    size_t loc_bytes, cs_bytes, st_bytes, chunk_bytes, bh_bytes;
+    size_t ws;
 };
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+bool bwd_method_ok(int method, int64_t N, int64_t P, int64_t R, int io)
+{
+    if (method == M3_BWD_STEP) return m3::bwd_supported(N, P, R, io);
+    if (method == M3_BWD_CHUNKED) return m3::bwd_chunked_supported(N, P, R, io);
+    return m3::bwd_chunked_supported(N, P, R, io) || m3::bwd_supported(N, P, R, io);
+}
 
 m3_status plan_bwd(const m3_scan_bwd_args* a, BwdPlan* out)
 {
@@ -193,9 +205,29 @@ m3_status plan_bwd(const m3_scan_bwd_args* a, BwdPlan* out)
     const int64_t P = a->headdim, N = a->dstate, R = a->rank;
     if (Bt < 0 || L < 0 || H < 0 || P < 1 || N < 1 || R < 1 || (N % 2) != 0) return M3_ERR_SHAPE;
     if (a->io_dtype != M3_F32 && a->io_dtype != M3_BF16) return M3_ERR_DTYPE;
-    if (!m3::bwd_supported(N, P, R, a->io_dtype)) return M3_ERR_UNSUPPORTED;
+    if (a->method != M3_BWD_AUTO && a->method != M3_BWD_STEP && a->method != M3_BWD_CHUNKED)
+        return M3_ERR_OPTION;
+    if (!bwd_method_ok(a->method, N, P, R, a->io_dtype)) return M3_ERR_UNSUPPORTED;
     const int64_t nbh = Bt * H;
     if (nbh > (int64_t)1 << 24) return M3_ERR_UNSUPPORTED;
+    memset(out, 0, sizeof(*out));
+    out->method = a->method;
+    if (out->method == M3_BWD_AUTO)
+        out->method = m3::bwd_chunked_supported(N, P, R, a->io_dtype) ? M3_BWD_CHUNKED : M3_BWD_STEP;
+    if (out->method == M3_BWD_CHUNKED) {
+        const int64_t Q = m3::bwd_chunk_tokens(R);
+        out->nc = (L + Q - 1) / Q;
+        if (nbh * out->nc >= ((int64_t)1 << 31)) return M3_ERR_UNSUPPORTED;
+        const size_t NP = (size_t)N * P;
+        out->loc_bytes = round256((size_t)nbh * out->nc * 2 * NP * 4);
+        out->cs_bytes = round256((size_t)nbh * out->nc * (1 + N) * 4);
+        out->st_bytes = round256((size_t)nbh * (out->nc + 1) * NP * 4);
+        out->chunk_bytes = round256((size_t)nbh * out->nc * 4);
+        out->bh_bytes = round256((size_t)nbh * 4);
+        out->ws = nbh > 0 ? out->loc_bytes + out->cs_bytes + 2 * out->st_bytes + 2 * out->chunk_bytes +
+                                out->bh_bytes : 0;
+        return M3_OK;
+    }
     out->TB = m3::bwd_sub_steps(N);
     out->K = m3::bwd_blocks_per_checkpoint(N, P, R, a->io_dtype);
     out->parts = m3::bwd_pair_parts(N);
@@ -227,7 +259,14 @@ size_t m3_scan_bwd_workspace_bytes(const m3_scan_bwd_args* a)
 
 int m3_scan_bwd_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t io_dtype)
 {
-    return m3::bwd_supported(dstate, headdim, rank, io_dtype) ? 1 : 0;
+    return bwd_method_ok(M3_BWD_AUTO, dstate, headdim, rank, io_dtype) ? 1 : 0;
+}
+
+int m3_scan_bwd_method_supported(int64_t dstate, int64_t headdim, int64_t rank, int32_t io_dtype,
+                                 int32_t method)
+{
+    if (method != M3_BWD_AUTO && method != M3_BWD_STEP && method != M3_BWD_CHUNKED) return 0;
+    return bwd_method_ok(method, dstate, headdim, rank, io_dtype) ? 1 : 0;
 }
 
 m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
@@ -279,6 +318,34 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
             if (overlaps(out[i], out[j])) return M3_ERR_ALIAS;
     if (a->workspace == nullptr || a->workspace_bytes < plan.ws) return M3_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0) return M3_ERR_ALIGN;
+
+    if (plan.method == M3_BWD_CHUNKED) {
+        m3::BcParams q;
+        memset(&q, 0, sizeof(q));
+        q.x = a->x; q.B = a->B; q.C = a->C; q.dy = a->dy;
+        q.dt = a->dt; q.A = a->A; q.theta = a->theta; q.lam = a->lam;
+        q.h_in = a->h_in; q.Bp_in = a->B_prev_in; q.xp_in = a->x_prev_in; q.dh_out = a->dh_out;
+        q.dx = a->dx; q.dB = a->dB; q.dC = a->dC; q.ddt = a->ddt; q.dtheta = a->dtheta;
+        q.dlam = a->dlam; q.dh_in = a->dh_in; q.dBp = a->dB_prev; q.dxp = a->dx_prev; q.dA = a->dA;
+        char* w = static_cast<char*>(a->workspace);
+        q.loc = reinterpret_cast<float*>(w);
+        w += plan.loc_bytes;
+        q.csum = reinterpret_cast<float*>(w);
+        w += plan.cs_bytes;
+        q.gst = reinterpret_cast<float*>(w);
+        w += plan.st_bytes;
+        q.dgst = reinterpret_cast<float*>(w);
+        w += plan.st_bytes;
+        q.dA_part = reinterpret_cast<float*>(w);
+        w += plan.chunk_bytes;
+        q.dw_last = reinterpret_cast<float*>(w);
+        w += plan.chunk_bytes;
+        q.dA_bh = reinterpret_cast<float*>(w);
+        q.L = L; q.H = H; q.N = (int)N; q.P = (int)P; q.R = (int)R;
+        q.nbh = (int)nbh;
+        q.nc = (int)plan.nc;
+        return hip_status(m3::launch_bwd_chunked(q, a->io_dtype, static_cast<hipStream_t>(stream)));
+    }
 
     m3::BwdParams p;
     memset(&p, 0, sizeof(p));

@@ -1,0 +1,1066 @@
+// Gradient of the Mamba-3 scan in chunked (SSD) form on gfx950.
+//
+// Forward, per (b, h), in the augmented state g_t = h_t + bhat_{t+1} U_t,
+// bhat_t = (1 - lam_t) dt_t, U_t = B_t X_t (the exact rewrite the prefill
+// kernel evaluates; Mamba-3 summary on b-lab.team, sections 1-3):
+//   g_t = alpha_t R_t g_{t-1} + w_t U_t,   w_t = gamma_t + bhat_{t+1},
+//   y_t = C_t^T (alpha_t R_t g_{t-1} + gamma_t U_t).
+// For a chunk of Q tokens with chunk-local prefix sums Lam_j = sum_{k<=j} dt_k A
+// and Phi_j = sum_{k<=j} dt_k theta_k (per pair), and rotated rows
+// Bbar_j = R(Phi_j)^T B_j, Cbar_j = R(Phi_j)^T C_j (data-dependent RoPE):
+//   y_j   = e^{Lam_j} Cbar_j^T G_in + sum_{k<=j} M_jk (Cbar_j^T Bbar_k) X_k,
+//   M_jk  = e^{Lam_j - Lam_k} w_k (k < j),  gamma_j (k = j),
+//   G_out = R(Phi_tot) (e^{Lam_tot} G_in + sum_k d_k Bbar_k X_k),
+//   d_k   = e^{Lam_tot - Lam_k} w_k.
+// Reverse mode of that form (dGbar = R(Phi_tot)^T dG_out, S = Cbar Bbar^T,
+// dS = (dY X^T) o M, P = (dY X^T) o S o M):
+//   dG_in  = e^{Lam_tot} dGbar + sum_j e^{Lam_j} Cbar_j dY_j
+//   dX     = (S o M)^T dY + diag(d) Bbar dGbar^T
+//   dBbar  = dS^T Cbar + diag(d) X dGbar^T
+//   dCbar  = dS Bbar + diag(e^{Lam}) dY G_in^T
+//   dLam_j = sum_{k<j} P_jk - sum_{i>j} P_ij + e^{Lam_j} <Cbar_j, dY_j G_in^T>
+//            - d_j dd_j,  dd_j = <Bbar_j, X_j dGbar^T>
+//            (+ <Gbar_out, dGbar> = e^{Lam_tot} <G_in, dGbar> + sum_k d_k dd_k
+//            at the last token)
+//   dPhi_j = per pair and summed over ranks, dBbar_0 Bbar_1 - dBbar_1 Bbar_0
+//            + dCbar_0 Cbar_1 - dCbar_1 Cbar_0
+//            (+ sum_p Gbar_out,0 dGbar_1 - Gbar_out,1 dGbar_0 at the last token,
+//            split the same way into the G_in term and the per-token terms)
+//   dB = R(Phi) dBbar, dC = R(Phi) dCbar; suffix sums over the chunk turn dLam
+//   and dPhi into the gradients of dt A and dt theta; then dt, lam, theta and A
+//   follow from gamma = lam dt and w_k = gamma_k + (1 - lam_{k+1}) dt_{k+1}.
+//
+// Kernels (one launch each, in stream order):
+//   bc_local_kernel  per (b, h, chunk): Bbar^T diag(d) X and Cbar^T diag(e^Lam)
+//                    dY on matrix cores, e^{Lam_tot} and the total rotation.
+//   bc_scan_kernel   per (b, h, pair, column): the chunk-start states forward
+//                    and the chunk-end adjoints backward (elementwise).
+//   bc_grad_kernel   per (b, h, chunk): every gradient of the chunk from its
+//                    boundary states; wave w owns operand rows 16w..16w+15.
+//   bc_final_kernel  per (b, h): the look-ahead weight's gradient across chunk
+//                    boundaries, the state record's gradients, dA shares.
+//   bc_dA_kernel     per head: dA summed over the batch in a fixed order.
+// Every sum runs in a fixed order: the result is deterministic.
+#pragma once
+
+#include "m3_device.hpp"
+#include "m3_internal.hpp"
+
+namespace m3 {
+namespace bc {
+
+template <typename OP, int N_, int P_, int R_>
+struct Cfg {
+    using op_t = OP;
+    static constexpr int N = N_, P = P_, R = R_;
+    static constexpr int T = 64;                 // operand rows per chunk (tokens x ranks)
+    static constexpr int Q = T / R;              // tokens per chunk
+    static constexpr int NPR = N / 2;            // rotation pairs
+    static constexpr int E = (int)sizeof(OP);
+    static constexpr bool BF = (E == 2);
+    static constexpr int PAD = 16 / E;           // 16-byte row padding
+    static constexpr int LDN = N + PAD, LDP = P + PAD, LDT = T + PAD, LDH = NPR + 1;
+    static constexpr int NT = N / 16, PT = P / 16, NB = N / 32, PB = P / 32;
+    static constexpr int VE = 16 / E;            // elements per 16-byte vector
+    static constexpr int TS = 72;                // floats per token-scalar slot
+    static_assert(N % 32 == 0 && P % 32 == 0, "K blocks of 32");
+};
+
+// Token-scalar slots (TS floats each).
+enum { kDt, kLm, kLam, kEL, kW, kGa, kD, kRS, kCQ, kDiag = kCQ + 4, kE, kDD, kTD, kDW, kCross,
+       kDot, kZP, kNumSlots = kZP + 4 };
+
+constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
+
+// LDS carve-up (bytes).  GRAD adds the adjoint operands and the score tiles.
+template <class Cf, bool GRAD>
+struct Lay {
+    static constexpr size_t rowsN = a16((size_t)Cf::T * Cf::LDN * Cf::E);
+    static constexpr size_t rowsP = a16((size_t)Cf::T * Cf::LDP * Cf::E);
+    static constexpr size_t stNP = a16((size_t)Cf::N * Cf::LDP * Cf::E);
+    static constexpr size_t sqT = a16((size_t)Cf::T * Cf::LDT * Cf::E);
+    static constexpr size_t phi = a16((size_t)Cf::Q * Cf::LDH * 4);
+    static constexpr size_t oBb = 0, oCb = oBb + rowsN, oX = oCb + rowsN, oDY = oX + rowsP;
+    static constexpr size_t oDG = oDY + rowsP;
+    static constexpr size_t oGi = oDG + (GRAD ? stNP : 0);
+    static constexpr size_t oSM = oGi + (GRAD ? stNP : 0);
+    static constexpr size_t odS = oSM + (GRAD ? sqT : 0);
+    static constexpr size_t oPhi = odS + (GRAD ? sqT : 0);
+    static constexpr size_t oDPhi = oPhi + phi;
+    static constexpr size_t oTok = oDPhi + (GRAD ? phi : 0);
+    static constexpr size_t bytes = oTok + (size_t)kNumSlots * Cf::TS * 4;
+};
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename OP> __device__ __forceinline__ void sincos_op(float a, float* s, float* c);
+template <> __device__ __forceinline__ void sincos_op<bf16>(float a, float* s, float* c) { __sincosf(a, s, c); }
+template <> __device__ __forceinline__ void sincos_op<float>(float a, float* s, float* c) { sincosf(a, s, c); }
+
+// Sum over aligned groups of G lanes (4, 8 or 16) with DPP; every lane of a
+// group receives the group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v += dpp_moved<0xB1, 0xf>(v);    // quad_perm [1,0,3,2]
+    v += dpp_moved<0x4E, 0xf>(v);    // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v += dpp_moved<0x141, 0xf>(v);    // row_half_mirror
+    if constexpr (G >= 16) v += dpp_moved<0x140, 0xf>(v);   // row_mirror
+    return v;
+}
+// The value of the lane holding the other column of the same rotation pair.
+__device__ __forceinline__ float pair_swap(float v) { return dpp_moved<0xB1, 0xf>(v); }
+
+// Matrix-core operand whose K runs along the rows of a row-major LDS array:
+// lane (g, l16) takes arr[(r0 + l16) * ld + k0 + 8 g + e], e = 0..7.
+template <typename OP>
+__device__ __forceinline__ void frag_row(Frag<OP>& f, const OP* arr, int ld, int r0, int k0, int l16, int g)
+{
+    lds_frag8(f, arr + (r0 + l16) * ld + k0 + 8 * g);
+}
+// Operand whose K runs down the columns: lane (g, l16) takes
+// arr[(k0 + 8 g + e) * ld + c0 + l16] (bf16: two transposing reads).
+__device__ __forceinline__ void frag_col(Frag<bf16>& f, const bf16* arr, int ld, int k0, int c0, int l16, int g)
+{
+    const bf16* q = arr + (k0 + 8 * g + (l16 >> 2)) * ld + c0 + 4 * (l16 & 3);
+    const bf16x4 lo = lds_read_tr4(q);
+    const bf16x4 hi = lds_read_tr4(q + 4 * ld);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = lo[e]; f.v[4 + e] = hi[e]; }
+}
+__device__ __forceinline__ void frag_col(Frag<float>& f, const float* arr, int ld, int k0, int c0, int l16, int g)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = arr[(k0 + 8 * g + e) * ld + c0 + l16];
+}
+
+__device__ __forceinline__ void lds_load8(float (&v)[8], const bf16* q)
+{
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(q);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)a[e];
+}
+__device__ __forceinline__ void lds_load8(float (&v)[8], const float* q)
+{
+    const f32x4 a = *reinterpret_cast<const f32x4*>(q);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(q + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+}
+__device__ __forceinline__ void store4_op(bf16* q, const f32x4& v)
+{
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x4*>(q) = o;
+}
+__device__ __forceinline__ void store4_op(float* q, const f32x4& v) { *reinterpret_cast<f32x4*>(q) = v; }
+
+// Stage one chunk: token scalars, cumulative angles, rotated B and C rows, X
+// and dY rows (and for the gradient: the chunk-start state, the rotated
+// end-state adjoint and its dot / cross products with the end state).
+template <class Cf, bool GRAD>
+__device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int bh, int c)
+{
+    using op_t = typename Cf::op_t;
+    using L = Lay<Cf, GRAD>;
+    constexpr int T = Cf::T, Q = Cf::Q, R = Cf::R, N = Cf::N, P = Cf::P, NPR = Cf::NPR;
+    constexpr int LDN = Cf::LDN, LDP = Cf::LDP, LDH = Cf::LDH, VE = Cf::VE, TS = Cf::TS;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t L_ = p.L, H = p.H, b = bh / H, h = bh % H;
+    const int64_t t0 = (int64_t)c * Q;
+    auto tok = [&](int64_t t) -> int64_t { return (b * L_ + t) * H + h; };
+    op_t* sBb = reinterpret_cast<op_t*>(lds + L::oBb);
+    op_t* sCb = reinterpret_cast<op_t*>(lds + L::oCb);
+    op_t* sX = reinterpret_cast<op_t*>(lds + L::oX);
+    op_t* sDY = reinterpret_cast<op_t*>(lds + L::oDY);
+    float* sPhi = reinterpret_cast<float*>(lds + L::oPhi);
+    float* sT = reinterpret_cast<float*>(lds + L::oTok);
+    const float A = p.A[h];
+
+    // ---- S1: raw rows into LDS (16-byte vectors; zero past the sequence) ----
+    {
+        constexpr int VB = N / VE, VX = P / VE;              // vectors per B / X row
+        const uint4 z = {0u, 0u, 0u, 0u};
+        constexpr int IB = (T * VB + 255) / 256, IX = (T * VX + 255) / 256;
+        uint4 vb[IB], vc[IB], vx[IX], vy[IX];
+#pragma unroll
+        for (int it = 0; it < IB; ++it) {
+            const int v = tid + 256 * it;
+            vb[it] = z; vc[it] = z;
+            if (v < T * VB) {
+                const int rho = v / VB, q = v % VB;
+                const int64_t t = t0 + rho / R;
+                if (t < L_) {
+                    const size_t off = ((size_t)tok(t) * R + rho % R) * N + (size_t)q * VE;
+                    vb[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.B) + off);
+                    vc[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.C) + off);
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IX; ++it) {
+            const int v = tid + 256 * it;
+            vx[it] = z; vy[it] = z;
+            if (v < T * VX) {
+                const int rho = v / VX, q = v % VX;
+                const int64_t t = t0 + rho / R;
+                if (t < L_) {
+                    const size_t off = ((size_t)tok(t) * R + rho % R) * P + (size_t)q * VE;
+                    vx[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.x) + off);
+                    vy[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.dy) + off);
+                }
+            }
+        }
+        // angles (raw theta for now), dt and lam of the chunk and of the next token
+        constexpr int IT = (Q * (NPR / 4) + 255) / 256;
+        f32x4 th[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int v = tid + 256 * it;
+            th[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (v < Q * (NPR / 4)) {
+                const int j = v / (NPR / 4), q = v % (NPR / 4);
+                if (t0 + j < L_) th[it] = *reinterpret_cast<const f32x4*>(p.theta + tok(t0 + j) * NPR + 4 * q);
+            }
+        }
+        float dtv = 0.f, lmv = 0.f;
+        if (tid <= Q && t0 + tid < L_) { dtv = p.dt[tok(t0 + tid)]; lmv = p.lam[tok(t0 + tid)]; }
+#pragma unroll
+        for (int it = 0; it < IB; ++it) {
+            const int v = tid + 256 * it;
+            if (v < T * VB) {
+                const int rho = v / VB, q = v % VB;
+                *reinterpret_cast<uint4*>(sBb + rho * LDN + q * VE) = vb[it];
+                *reinterpret_cast<uint4*>(sCb + rho * LDN + q * VE) = vc[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IX; ++it) {
+            const int v = tid + 256 * it;
+            if (v < T * VX) {
+                const int rho = v / VX, q = v % VX;
+                *reinterpret_cast<uint4*>(sX + rho * LDP + q * VE) = vx[it];
+                *reinterpret_cast<uint4*>(sDY + rho * LDP + q * VE) = vy[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int v = tid + 256 * it;
+            if (v < Q * (NPR / 4)) {
+                const int j = v / (NPR / 4), q = v % (NPR / 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sPhi[j * LDH + 4 * q + e] = th[it][e];
+            }
+        }
+        if (tid <= Q) { sT[kDt * TS + tid] = dtv; sT[kLm * TS + tid] = lmv; }
+        if constexpr (GRAD) {
+            // chunk-start state, operand type, same [N][P] layout
+            op_t* sGi = reinterpret_cast<op_t*>(lds + L::oGi);
+            const float* gin = p.gst + ((size_t)bh * (p.nc + 1) + c) * N * P;
+            constexpr int IG = (N * P / 4 + 255) / 256;
+#pragma unroll
+            for (int it = 0; it < IG; ++it) {
+                const int v = tid + 256 * it;
+                if (v < N * P / 4) {
+                    const int n = v / (P / 4), q = v % (P / 4);
+                    store4_op(sGi + n * LDP + 4 * q, *reinterpret_cast<const f32x4*>(gin + (size_t)n * P + 4 * q));
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- S2: token scalars (wave 0) and cumulative angles (all waves) ------
+    if (wv == 0) {
+        const int j = lane;
+        const float dtj = j < Q ? sT[kDt * TS + j] : 0.f;
+        const float lmj = j < Q ? sT[kLm * TS + j] : 0.f;
+        const float lam_j = wave_inclusive_sum(dtj * A);
+        const float lam_tot = wave_read_lane(lam_j, 63);
+        const float dtn = sT[kDt * TS + j + 1], lmn = sT[kLm * TS + j + 1];
+        const float ga = lmj * dtj;
+        const float w = ga + (1.f - lmn) * dtn;
+        if (j < Q) {
+            sT[kLam * TS + j] = lam_j;
+            sT[kEL * TS + j] = ex2(lam_j * kLog2e);
+            sT[kW * TS + j] = w;
+            sT[kGa * TS + j] = ga;
+            sT[kD * TS + j] = w * ex2((lam_tot - lam_j) * kLog2e);
+        }
+    }
+    {
+        const float dtj = lane < Q ? sT[kDt * TS + lane] : 0.f;
+        for (int i = wv; i < NPR; i += 4) {
+            const float v = lane < Q ? dtj * sPhi[lane * LDH + i] : 0.f;
+            const float ph = wave_inclusive_sum(v);
+            if (lane < Q) sPhi[lane * LDH + i] = ph;
+        }
+    }
+    __syncthreads();
+
+    // ---- S3: rotate B and C rows by R(Phi)^T in place ------------------------
+    {
+        constexpr int NI = T * (NPR / 4);
+        for (int v = tid; v < NI; v += 256) {
+            const int rho = v / (NPR / 4), qd = v % (NPR / 4);
+            const int j = rho / R;
+            float cs[4], sn[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sincos_op<op_t>(sPhi[j * LDH + 4 * qd + e], &sn[e], &cs[e]);
+            float bv[8], cv[8], o[8];
+            lds_load8(bv, sBb + rho * LDN + 8 * qd);
+            lds_load8(cv, sCb + rho * LDN + 8 * qd);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[2 * e] = cs[e] * bv[2 * e] + sn[e] * bv[2 * e + 1];
+                o[2 * e + 1] = cs[e] * bv[2 * e + 1] - sn[e] * bv[2 * e];
+            }
+            lds_store8(sBb + rho * LDN + 8 * qd, o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[2 * e] = cs[e] * cv[2 * e] + sn[e] * cv[2 * e + 1];
+                o[2 * e + 1] = cs[e] * cv[2 * e + 1] - sn[e] * cv[2 * e];
+            }
+            lds_store8(sCb + rho * LDN + 8 * qd, o);
+        }
+    }
+    if constexpr (GRAD) {
+        // dGbar = R(Phi_tot)^T dG_out into LDS, and in float32 the chunk-start
+        // terms of the end state's angle and decay gradients: per pair
+        // e^{Lam_tot} sum_p (G_in,0 dGbar_1 - G_in,1 dGbar_0) and the whole
+        // e^{Lam_tot} <G_in, dGbar>.  (The end state's remaining share,
+        // sum_k d_k Bbar_k X_k, is added from the same per-token products that
+        // enter the tokens' own gradients, so the two cancel exactly where the
+        // reverse prefix sums say they must.)
+        op_t* sDG = reinterpret_cast<op_t*>(lds + L::oDG);
+        const float* dgo = p.dgst + ((size_t)bh * (p.nc + 1) + c) * N * P;
+        const float* gi = p.gst + ((size_t)bh * (p.nc + 1) + c) * N * P;
+        const float* cst = p.csum + ((size_t)bh * p.nc + c) * (1 + N);
+        const float el_tot = sT[kEL * TS + Q - 1];
+        constexpr int G4 = P / 4;                        // lanes per pair (8 or 16)
+        constexpr int NI = NPR * G4;
+        float dot = 0.f;
+        for (int v0 = 0; v0 < NI; v0 += 256) {
+            const int v = v0 + tid;
+            float cr = 0.f;
+            if (v < NI) {
+                const int i = v / G4, q = v % G4;
+                const float cc = cst[1 + 2 * i], ss = cst[2 + 2 * i];
+                const f32x4 d0 = *reinterpret_cast<const f32x4*>(dgo + (size_t)(2 * i) * P + 4 * q);
+                const f32x4 d1 = *reinterpret_cast<const f32x4*>(dgo + (size_t)(2 * i + 1) * P + 4 * q);
+                const f32x4 g0 = *reinterpret_cast<const f32x4*>(gi + (size_t)(2 * i) * P + 4 * q);
+                const f32x4 g1 = *reinterpret_cast<const f32x4*>(gi + (size_t)(2 * i + 1) * P + 4 * q);
+                f32x4 r0, r1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    r0[e] = cc * d0[e] + ss * d1[e];
+                    r1[e] = cc * d1[e] - ss * d0[e];
+                    cr += g0[e] * r1[e] - g1[e] * r0[e];
+                    dot += g0[e] * r0[e] + g1[e] * r1[e];
+                }
+                store4_op(sDG + (2 * i) * LDP + 4 * q, r0);
+                store4_op(sDG + (2 * i + 1) * LDP + 4 * q, r1);
+            }
+            cr = group_sum<G4>(cr);
+            if (v < NI && (v % G4) == 0) sT[kCross * TS + v / G4] = el_tot * cr;
+        }
+        dot = wave_read_lane(wave_inclusive_sum(dot), 63);
+        if (lane == 0) sT[kDot * TS + wv] = el_tot * dot;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk-local sums: Gloc = Bbar^T diag(d) X and V = Cbar^T diag(e^Lam) dY
+// (N x P each, chunk-local frame), e^{Lam_tot}, cos/sin of Phi_tot.
+template <class Cf>
+__global__ __launch_bounds__(256) void bc_local_kernel(const BcParams p)
+{
+    using op_t = typename Cf::op_t;
+    using L = Lay<Cf, false>;
+    constexpr int T = Cf::T, Q = Cf::Q, R = Cf::R, N = Cf::N, P = Cf::P, NPR = Cf::NPR;
+    constexpr int LDN = Cf::LDN, LDP = Cf::LDP, LDH = Cf::LDH, TS = Cf::TS, NT = Cf::NT, PT = Cf::PT;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int bh = blockIdx.x / p.nc, c = blockIdx.x % p.nc;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
+    stage<Cf, false>(p, lds, bh, c);
+    op_t* sBb = reinterpret_cast<op_t*>(lds + L::oBb);
+    op_t* sCb = reinterpret_cast<op_t*>(lds + L::oCb);
+    op_t* sX = reinterpret_cast<op_t*>(lds + L::oX);
+    op_t* sDY = reinterpret_cast<op_t*>(lds + L::oDY);
+    const float* sPhi = reinterpret_cast<const float*>(lds + L::oPhi);
+    const float* sT = reinterpret_cast<const float*>(lds + L::oTok);
+    // scale X rows by d and dY rows by e^{Lam} in place
+    for (int v = tid; v < T * (P / 8); v += 256) {
+        const int rho = v / (P / 8), q = v % (P / 8);
+        const int j = rho / R;
+        const float d = sT[kD * TS + j], el = sT[kEL * TS + j];
+        float xv[8], yv[8];
+        lds_load8(xv, sX + rho * LDP + 8 * q);
+        lds_load8(yv, sDY + rho * LDP + 8 * q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { xv[e] *= d; yv[e] *= el; }
+        lds_store8(sX + rho * LDP + 8 * q, xv);
+        lds_store8(sDY + rho * LDP + 8 * q, yv);
+    }
+    __syncthreads();
+    float* out = p.loc + ((size_t)bh * p.nc + c) * 2 * N * P;
+    constexpr int NTILE = 2 * NT * PT;
+    for (int tl = wv; tl < NTILE; tl += 4) {
+        const int prod = tl / (NT * PT), nt = (tl % (NT * PT)) / PT, pt = tl % PT;
+        const op_t* sa = prod ? sCb : sBb;
+        const op_t* sb = prod ? sDY : sX;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < T / 32; ++kb) {
+            Frag<op_t> a, bb;
+            frag_col(a, sa, LDN, 32 * kb, 16 * nt, l16, g);
+            frag_col(bb, sb, LDP, 32 * kb, 16 * pt, l16, g);
+            mma(a, bb, acc);
+        }
+        float* o = out + (size_t)prod * N * P + (size_t)(16 * nt + 4 * g) * P + 16 * pt + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[(size_t)i * P] = acc[i];
+    }
+    if (tid <= NPR) {
+        float* cs = p.csum + ((size_t)bh * p.nc + c) * (1 + N);
+        if (tid == 0) {
+            cs[0] = ex2(sT[kLam * TS + Q - 1] * kLog2e);
+        } else {
+            float sn, cn;
+            sincosf(sPhi[(Q - 1) * LDH + tid - 1], &sn, &cn);
+            cs[2 * tid - 1] = cn;
+            cs[2 * tid] = sn;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk-boundary states: forward G_in(c+1) = R(Phi_tot)(e^{Lam_tot} G_in(c) +
+// Gloc(c)) from G_in(0) = h_in + bhat_0 B_prev x_prev; backward
+// dG_in(c) = e^{Lam_tot} R(Phi_tot)^T dG_out(c) + V(c) from dG_out = dh_out.
+// One thread per (b, h, pair, column); blockIdx.y picks the direction.
+template <typename IO>
+__global__ __launch_bounds__(256) void bc_scan_kernel(const BcParams p)
+{
+    const int N = p.N, P = p.P, R = p.R, NPR = N / 2, nc = p.nc;
+    const int64_t per = (int64_t)NPR * P;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)p.nbh * per) return;
+    const int bh = (int)(idx / per);
+    const int rem = (int)(idx % per), i = rem / P, q = rem % P;
+    const size_t NP = (size_t)N * P;
+    const size_t o0 = (size_t)(2 * i) * P + q, o1 = o0 + P;
+    const float* cs = p.csum + (size_t)bh * nc * (1 + N);
+    const float* lc = p.loc + (size_t)bh * nc * 2 * NP;
+    constexpr int U = 8;
+    if (blockIdx.y == 0) {
+        float g0 = 0.f, g1 = 0.f;
+        if (p.h_in != nullptr) { g0 = p.h_in[bh * NP + o0]; g1 = p.h_in[bh * NP + o1]; }
+        if (p.Bp_in != nullptr && p.L > 0) {
+            const int64_t b = bh / p.H, h = bh % p.H, k0 = (b * p.L) * p.H + h;
+            const float bhat = (1.f - p.lam[k0]) * p.dt[k0];
+            const IO* Bp = reinterpret_cast<const IO*>(p.Bp_in) + (size_t)bh * R * N;
+            const IO* xp = reinterpret_cast<const IO*>(p.xp_in) + (size_t)bh * R * P;
+            float u0 = 0.f, u1 = 0.f;
+            for (int r = 0; r < R; ++r) {
+                const float xv = to_f32(xp[r * P + q]);
+                u0 += to_f32(Bp[r * N + 2 * i]) * xv;
+                u1 += to_f32(Bp[r * N + 2 * i + 1]) * xv;
+            }
+            g0 += bhat * u0;
+            g1 += bhat * u1;
+        }
+        float* G = p.gst + (size_t)bh * (nc + 1) * NP;
+        for (int c0 = 0; c0 < nc; c0 += U) {
+            float l0[U], l1[U], e[U], cc[U], ss[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u;
+                if (c < nc) {
+                    l0[u] = lc[(size_t)c * 2 * NP + o0];
+                    l1[u] = lc[(size_t)c * 2 * NP + o1];
+                    e[u] = cs[(size_t)c * (1 + N)];
+                    cc[u] = cs[(size_t)c * (1 + N) + 1 + 2 * i];
+                    ss[u] = cs[(size_t)c * (1 + N) + 2 + 2 * i];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u;
+                if (c < nc) {
+                    G[c * NP + o0] = g0;
+                    G[c * NP + o1] = g1;
+                    const float a0 = e[u] * g0 + l0[u], a1 = e[u] * g1 + l1[u];
+                    g0 = cc[u] * a0 - ss[u] * a1;
+                    g1 = ss[u] * a0 + cc[u] * a1;
+                }
+            }
+        }
+        G[nc * NP + o0] = g0;
+        G[nc * NP + o1] = g1;
+    } else {
+        float d0 = 0.f, d1 = 0.f;
+        if (p.dh_out != nullptr) { d0 = p.dh_out[bh * NP + o0]; d1 = p.dh_out[bh * NP + o1]; }
+        float* D = p.dgst + (size_t)bh * (nc + 1) * NP;
+        for (int c0 = nc - 1; c0 >= 0; c0 -= U) {
+            float v0[U], v1[U], e[U], cc[U], ss[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 - u;
+                if (c >= 0) {
+                    v0[u] = lc[((size_t)c * 2 + 1) * NP + o0];
+                    v1[u] = lc[((size_t)c * 2 + 1) * NP + o1];
+                    e[u] = cs[(size_t)c * (1 + N)];
+                    cc[u] = cs[(size_t)c * (1 + N) + 1 + 2 * i];
+                    ss[u] = cs[(size_t)c * (1 + N) + 2 + 2 * i];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 - u;
+                if (c >= 0) {
+                    D[c * NP + o0] = d0;
+                    D[c * NP + o1] = d1;
+                    const float r0 = cc[u] * d0 + ss[u] * d1, r1 = cc[u] * d1 - ss[u] * d0;
+                    d0 = e[u] * r0 + v0[u];
+                    d1 = e[u] * r1 + v1[u];
+                }
+            }
+        }
+        D[nc * NP + o0] = d0;
+        D[nc * NP + o1] = d1;
+        if (p.dh_in != nullptr) { p.dh_in[bh * NP + o0] = d0; p.dh_in[bh * NP + o1] = d1; }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Every gradient of one chunk.
+template <class Cf>
+__global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
+{
+    using op_t = typename Cf::op_t;
+    using L = Lay<Cf, true>;
+    constexpr int T = Cf::T, Q = Cf::Q, R = Cf::R, N = Cf::N, P = Cf::P, NPR = Cf::NPR;
+    constexpr int LDN = Cf::LDN, LDP = Cf::LDP, LDT = Cf::LDT, LDH = Cf::LDH, TS = Cf::TS;
+    constexpr int NT = Cf::NT, PT = Cf::PT, NB = Cf::NB, PB = Cf::PB;
+    constexpr int TPR = 4 / R;                    // tokens among a lane's 4 rows
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int bh = blockIdx.x / p.nc, c = blockIdx.x % p.nc;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
+    const int64_t L_ = p.L, H = p.H, b = bh / H, h = bh % H;
+    const int64_t t0 = (int64_t)c * Q;
+    auto tok = [&](int64_t t) -> int64_t { return (b * L_ + t) * H + h; };
+    stage<Cf, true>(p, lds, bh, c);
+    const op_t* sBb = reinterpret_cast<const op_t*>(lds + L::oBb);
+    const op_t* sCb = reinterpret_cast<const op_t*>(lds + L::oCb);
+    const op_t* sX = reinterpret_cast<const op_t*>(lds + L::oX);
+    const op_t* sDY = reinterpret_cast<const op_t*>(lds + L::oDY);
+    const op_t* sDG = reinterpret_cast<const op_t*>(lds + L::oDG);
+    const op_t* sGi = reinterpret_cast<const op_t*>(lds + L::oGi);
+    op_t* sSM = reinterpret_cast<op_t*>(lds + L::oSM);
+    op_t* sdS = reinterpret_cast<op_t*>(lds + L::odS);
+    const float* sPhi = reinterpret_cast<const float*>(lds + L::oPhi);
+    float* sDPhi = reinterpret_cast<float*>(lds + L::oDPhi);
+    float* sT = reinterpret_cast<float*>(lds + L::oTok);
+    __syncthreads();
+
+    const int r0w = 16 * wv;                      // this wave's operand rows
+    // ---- phase 1: S = Cbar Bbar^T, dSc = dY X^T on this wave's row tile ----
+    {
+        float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diagacc[4] = {0.f, 0.f, 0.f, 0.f};
+        float lam_r[4], ga_r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tj = (r0w + 4 * g + i) / R;
+            lam_r[i] = sT[kLam * TS + tj];
+            ga_r[i] = sT[kGa * TS + tj];
+        }
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const int ck = 16 * kt + l16;
+            if (kt > wv) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sSM[(r0w + 4 * g + i) * LDT + ck] = (op_t)0.f;
+                    sdS[(r0w + 4 * g + i) * LDT + ck] = (op_t)0.f;
+                }
+                if (g == 0) sT[(kCQ + wv) * TS + ck] = 0.f;
+                continue;
+            }
+            f32x4 S = {0.f, 0.f, 0.f, 0.f}, D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                Frag<op_t> a, bb;
+                frag_row(a, sCb, LDN, r0w, 32 * nb, l16, g);
+                frag_row(bb, sBb, LDN, 16 * kt, 32 * nb, l16, g);
+                mma(a, bb, S);
+            }
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                Frag<op_t> a, bb;
+                frag_row(a, sDY, LDP, r0w, 32 * pb, l16, g);
+                frag_row(bb, sX, LDP, 16 * kt, 32 * pb, l16, g);
+                mma(a, bb, D);
+            }
+            const int tk = ck / R;
+            const float lk = sT[kLam * TS + tk], wk = sT[kW * TS + tk];
+            float colacc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rj = r0w + 4 * g + i, tj = rj / R;
+                const float v = S[i] * D[i];
+                float m = 0.f;
+                if (tk < tj) {
+                    const float e = ex2((lam_r[i] - lk) * kLog2e);
+                    m = e * wk;
+                    rowacc[i] += v * m;
+                    colacc += v * e;
+                } else if (tk == tj) {
+                    m = ga_r[i];
+                    diagacc[i] += v;
+                }
+                sSM[rj * LDT + ck] = (op_t)(S[i] * m);
+                sdS[rj * LDT + ck] = (op_t)(D[i] * m);
+            }
+            colacc += __shfl_xor(colacc, 16, 64);
+            colacc += __shfl_xor(colacc, 32, 64);
+            if (g == 0) sT[(kCQ + wv) * TS + ck] = colacc;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float rs = group_sum<16>(rowacc[i]);
+            const float dg = group_sum<16>(diagacc[i]);
+            if (l16 == 0) {
+                sT[kRS * TS + r0w + 4 * g + i] = rs;
+                sT[kDiag * TS + r0w + 4 * g + i] = dg;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2a: dX = (S o M)^T dY + diag(d) Bbar dGbar^T ------------------
+    {
+        f32x4 ax[PT], axs[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) { ax[pt] = f32x4{0.f, 0.f, 0.f, 0.f}; axs[pt] = ax[pt]; }
+        for (int jb = wv >> 1; jb < T / 32; ++jb) {
+            Frag<op_t> a;
+            frag_col(a, sSM, LDT, 32 * jb, r0w, l16, g);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                Frag<op_t> bb;
+                frag_col(bb, sDY, LDP, 32 * jb, 16 * pt, l16, g);
+                mma(a, bb, ax[pt]);
+            }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            Frag<op_t> a;
+            frag_row(a, sBb, LDN, r0w, 32 * nb, l16, g);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                Frag<op_t> bb;
+                frag_col(bb, sDG, LDP, 32 * nb, 16 * pt, l16, g);
+                mma(a, bb, axs[pt]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rk = r0w + 4 * g + i, tk = rk / R;
+            if (t0 + tk < L_) {
+                const float dk = sT[kD * TS + tk];
+                float* o = p.dx + ((size_t)tok(t0 + tk) * R + rk % R) * P + l16;
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) o[16 * pt] = ax[pt][i] + dk * axs[pt][i];
+            }
+        }
+    }
+
+    // Back-rotation of dBbar / dCbar rows held in accumulators (lane: column
+    // n = 16 nt + l16, rows 4 g + i) to dB / dC, and the angle gradient of
+    // each (token, pair) summed over ranks into sDPhi (ADD: accumulate).
+    auto back_rotate = [&](f32x4 (&acc)[NT], const op_t* sBar, float* gout, bool add) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int n = 16 * nt + l16, pr = n >> 1;
+            const bool odd = (l16 & 1) != 0;
+            float dps[TPR];
+#pragma unroll
+            for (int u = 0; u < TPR; ++u) dps[u] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rk = r0w + 4 * g + i, tk = rk / R;
+                const float own = acc[nt][i];
+                const float oth = pair_swap(own);
+                const float d0 = odd ? oth : own, d1 = odd ? own : oth;
+                const float bo = to_f32(sBar[rk * LDN + n]);
+                const float bx = pair_swap(bo);
+                const float b0 = odd ? bx : bo, b1 = odd ? bo : bx;
+                float sn, cs;
+                sincos_op<op_t>(sPhi[tk * LDH + pr], &sn, &cs);
+                dps[i / R] += d0 * b1 - d1 * b0;
+                if (t0 + tk < L_)
+                    gout[((size_t)tok(t0 + tk) * R + rk % R) * N + n] = odd ? sn * d0 + cs * d1 : cs * d0 - sn * d1;
+            }
+            if (!odd) {
+#pragma unroll
+                for (int u = 0; u < TPR; ++u) {
+                    const int tk = (r0w + 4 * g) / R + u;
+                    float* dp = sDPhi + tk * LDH + pr;
+                    *dp = add ? *dp + dps[u] : dps[u];
+                }
+            }
+        }
+    };
+
+    // ---- phase 2b: dBbar = dS^T Cbar + diag(d) Zb, Zb = X dGbar^T -------------
+    {
+        f32x4 ab[NT], zb[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) { ab[nt] = f32x4{0.f, 0.f, 0.f, 0.f}; zb[nt] = ab[nt]; }
+        for (int jb = wv >> 1; jb < T / 32; ++jb) {
+            Frag<op_t> a;
+            frag_col(a, sdS, LDT, 32 * jb, r0w, l16, g);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                Frag<op_t> bb;
+                frag_col(bb, sCb, LDN, 32 * jb, 16 * nt, l16, g);
+                mma(a, bb, ab[nt]);
+            }
+        }
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) {
+            Frag<op_t> a;
+            frag_row(a, sX, LDP, r0w, 32 * pb, l16, g);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                Frag<op_t> bb;
+                frag_row(bb, sDG, LDP, 16 * nt, 32 * pb, l16, g);
+                mma(a, bb, zb[nt]);
+            }
+        }
+        // dd_k = <Bbar_k, Zb_k> per row, and per pair the sum over this wave's
+        // rows of d_k (Zb_0 Bbar_1 - Zb_1 Bbar_0) (the state term's share of
+        // the angle gradient)
+        float ddp[4] = {0.f, 0.f, 0.f, 0.f};
+        float zp[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) zp[nt] = 0.f;
+        const bool odd = (l16 & 1) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rk = r0w + 4 * g + i;
+            const float dk = sT[kD * TS + rk / R];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const float bo = to_f32(sBb[rk * LDN + 16 * nt + l16]);
+                const float bx = pair_swap(bo), zx = pair_swap(zb[nt][i]);
+                const float z0 = odd ? zx : zb[nt][i], z1 = odd ? zb[nt][i] : zx;
+                const float b0 = odd ? bx : bo, b1 = odd ? bo : bx;
+                zp[nt] += dk * (z0 * b1 - z1 * b0);
+                ddp[i] += zb[nt][i] * bo;
+                ab[nt][i] += dk * zb[nt][i];
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            float z = zp[nt];
+            z += __shfl_xor(z, 16, 64);
+            z += __shfl_xor(z, 32, 64);
+            if (g == 0 && !odd) sT[(kZP + wv) * TS + ((16 * nt + l16) >> 1)] = z;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float s = group_sum<16>(ddp[i]);
+            if (l16 == 0) sT[kDD * TS + r0w + 4 * g + i] = s;
+        }
+        back_rotate(ab, sBb, p.dB, false);
+    }
+
+    // ---- phase 2c: dCbar = dS Bbar + diag(e^Lam) Zc, Zc = dY G_in^T -----------
+    {
+        f32x4 ac[NT], zc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) { ac[nt] = f32x4{0.f, 0.f, 0.f, 0.f}; zc[nt] = ac[nt]; }
+        for (int kb = 0; kb <= (wv >> 1); ++kb) {
+            Frag<op_t> a;
+            frag_row(a, sdS, LDT, r0w, 32 * kb, l16, g);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                Frag<op_t> bb;
+                frag_col(bb, sBb, LDN, 32 * kb, 16 * nt, l16, g);
+                mma(a, bb, ac[nt]);
+            }
+        }
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) {
+            Frag<op_t> a;
+            frag_row(a, sDY, LDP, r0w, 32 * pb, l16, g);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                Frag<op_t> bb;
+                frag_row(bb, sGi, LDP, 16 * nt, 32 * pb, l16, g);
+                mma(a, bb, zc[nt]);
+            }
+        }
+        float ep[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rj = r0w + 4 * g + i;
+            const float el = sT[kEL * TS + rj / R];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                ep[i] += zc[nt][i] * to_f32(sCb[rj * LDN + 16 * nt + l16]);
+                ac[nt][i] += el * zc[nt][i];
+            }
+            ep[i] *= el;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float s = group_sum<16>(ep[i]);
+            if (l16 == 0) sT[kE * TS + r0w + 4 * g + i] = s;
+        }
+        back_rotate(ac, sCb, p.dC, true);
+    }
+    __syncthreads();
+
+    // ---- phase 3a: dphi = suffix sums of dPhi over the chunk's tokens ---------
+    for (int i = wv; i < NPR; i += 4) {
+        float v = 0.f;
+        if (lane < Q) {
+            v = sDPhi[lane * LDH + i];
+            if (lane == Q - 1)
+                v += sT[kCross * TS + i] - (sT[kZP * TS + i] + sT[(kZP + 1) * TS + i] +
+                                            sT[(kZP + 2) * TS + i] + sT[(kZP + 3) * TS + i]);
+        }
+        const float inc = wave_inclusive_sum(v);
+        const float tot = wave_read_lane(inc, 63);
+        if (lane < Q) sDPhi[lane * LDH + i] = tot - inc + v;
+    }
+    __syncthreads();
+
+    // ---- phase 3b: dtheta = dt dphi; sum_i theta_i dphi_i per token ------------
+    {
+        constexpr int G4 = NPR / 4;               // lanes per token (4, 8 or 16)
+        constexpr int NI = Q * G4;
+        for (int v0 = 0; v0 < NI; v0 += 256) {
+            const int v = v0 + tid;
+            float td = 0.f;
+            if (v < NI) {
+                const int j = v / G4, q = v % G4;
+                if (t0 + j < L_) {
+                    const int64_t k = tok(t0 + j);
+                    const f32x4 th = *reinterpret_cast<const f32x4*>(p.theta + k * NPR + 4 * q);
+                    const float dtj = sT[kDt * TS + j];
+                    f32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float dph = sDPhi[j * LDH + 4 * q + e];
+                        o[e] = dtj * dph;
+                        td += th[e] * dph;
+                    }
+                    *reinterpret_cast<f32x4*>(p.dtheta + k * NPR + 4 * q) = o;
+                }
+            }
+            td = group_sum<G4>(td);
+            if (v < NI && (v % G4) == 0) sT[kTD * TS + v / G4] = td;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3c: decay and weight gradients per token (wave 0) --------------
+    if (wv == 0) {
+        const int t = lane;
+        float dlam = 0.f, dw = 0.f, dgt = 0.f, ddk = 0.f;
+        if (t < Q) {
+            float rs = 0.f, q = 0.f, dg = 0.f, e = 0.f, dd = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int rho = t * R + r;
+                rs += sT[kRS * TS + rho];
+                dg += sT[kDiag * TS + rho];
+                e += sT[kE * TS + rho];
+                dd += sT[kDD * TS + rho];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) q += sT[(kCQ + w) * TS + rho];
+            }
+            const float wt = sT[kW * TS + t];
+            ddk = sT[kD * TS + t] * dd;
+            dlam = rs - wt * q + e - ddk;
+            const float lam_tot = sT[kLam * TS + Q - 1];
+            dw = q + dd * ex2((lam_tot - sT[kLam * TS + t]) * kLog2e);
+            dgt = dg + dw;
+        }
+        // the end state's decay term: e^{Lam_tot} <G_in, dGbar> + sum_k d_k dd_k
+        const float ddsum = wave_read_lane(wave_inclusive_sum(ddk), 63);
+        if (t == Q - 1)
+            dlam += sT[kDot * TS + 0] + sT[kDot * TS + 1] + sT[kDot * TS + 2] + sT[kDot * TS + 3] + ddsum;
+        const float inc = wave_inclusive_sum(dlam);
+        const float da = wave_read_lane(inc, 63) - inc + dlam;
+        const float dw_prev = __shfl_up(dw, 1, 64);
+        const float A = p.A[h];
+        float dAc = 0.f;
+        if (t < Q && t0 + t < L_) {
+            const float dtt = sT[kDt * TS + t], lm = sT[kLm * TS + t];
+            const float dwp = t > 0 ? dw_prev : 0.f;
+            const int64_t k = tok(t0 + t);
+            p.ddt[k] = A * da + sT[kTD * TS + t] + lm * dgt + (1.f - lm) * dwp;
+            p.dlam[k] = dtt * (dgt - dwp);
+            dAc = dtt * da;
+        }
+        const float dAs = wave_read_lane(wave_inclusive_sum(dAc), 63);
+        if (lane == 0) p.dA_part[(size_t)bh * p.nc + c] = dAs;
+        if (lane == Q - 1) p.dw_last[(size_t)bh * p.nc + c] = dw;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per (b, h): the look-ahead weight of the last token of chunk c - 1 reaches
+// bhat of the first token of chunk c (and the state record's bhat_0 term for
+// chunk 0); the record's gradients; this unit's dA share.
+template <typename IO>
+__global__ __launch_bounds__(256) void bc_final_kernel(const BcParams p)
+{
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int64_t H = p.H, b = bh / H, h = bh % H;
+    const int N = p.N, P = p.P, R = p.R, nc = p.nc, Q = 64 / R;
+    auto tok = [&](int64_t t) -> int64_t { return (b * p.L + t) * H + h; };
+    __shared__ float red[256];
+    const float* dG0 = p.dgst + ((size_t)bh * (nc + 1) + nc) * N * P;
+    const float bhat0 = p.L > 0 ? (1.f - p.lam[tok(0)]) * p.dt[tok(0)] : 0.f;
+    float part = 0.f;
+    if (p.Bp_in != nullptr) {
+        const IO* Bp = reinterpret_cast<const IO*>(p.Bp_in) + (size_t)bh * R * N;
+        const IO* xp = reinterpret_cast<const IO*>(p.xp_in) + (size_t)bh * R * P;
+        for (int v = tid; v < R * N; v += 256) {
+            const int r = v / N, n = v % N;
+            float z = 0.f;
+            for (int q = 0; q < P; ++q) z += dG0[(size_t)n * P + q] * to_f32(xp[r * P + q]);
+            part += to_f32(Bp[r * N + n]) * z;
+            if (p.dBp != nullptr) p.dBp[(size_t)bh * R * N + v] = bhat0 * z;
+        }
+        if (p.dxp != nullptr) {
+            for (int v = tid; v < R * P; v += 256) {
+                const int r = v / P, q = v % P;
+                float s = 0.f;
+                for (int n = 0; n < N; ++n) s += to_f32(Bp[r * N + n]) * dG0[(size_t)n * P + q];
+                p.dxp[(size_t)bh * R * P + v] = bhat0 * s;
+            }
+        }
+    } else {
+        if (p.dBp != nullptr)
+            for (int v = tid; v < R * N; v += 256) p.dBp[(size_t)bh * R * N + v] = 0.f;
+        if (p.dxp != nullptr)
+            for (int v = tid; v < R * P; v += 256) p.dxp[(size_t)bh * R * P + v] = 0.f;
+    }
+    red[tid] = part;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    const float dbhat0 = red[0];
+    __syncthreads();
+    for (int c = tid; c < nc; c += 256) {
+        const int64_t t = (int64_t)c * Q;
+        if (t >= p.L) continue;
+        const float dwp = c == 0 ? dbhat0 : p.dw_last[(size_t)bh * nc + c - 1];
+        const int64_t k = tok(t);
+        p.ddt[k] += (1.f - p.lam[k]) * dwp;
+        p.dlam[k] -= p.dt[k] * dwp;
+    }
+    float s = 0.f;
+    for (int c = tid; c < nc; c += 256) s += p.dA_part[(size_t)bh * nc + c];
+    red[tid] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) p.dA_bh[bh] = red[0];
+}
+
+// dA[h] = sum over the batch rows of the units' shares (fixed order).
+static __global__ void bc_dA_kernel(const float* part, float* dA, int64_t batch, int64_t H)
+{
+    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    float s = 0.f;
+    for (int64_t b = 0; b < batch; ++b) s += part[b * H + h];
+    dA[h] = s;
+}
+
+template <class Cf> constexpr size_t local_lds() { return Lay<Cf, false>::bytes; }
+template <class Cf> constexpr size_t grad_lds() { return Lay<Cf, true>::bytes; }
+
+template <class Cf>
+hipError_t launch_cfg(const BcParams& p, hipStream_t stream)
+{
+    using IO = typename Cf::op_t;
+    auto* k1 = &bc_local_kernel<Cf>;
+    auto* k3 = &bc_grad_kernel<Cf>;
+    static const hipError_t a1 = hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    static const hipError_t a3 = hipFuncSetAttribute(reinterpret_cast<const void*>(k3),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (a1 != hipSuccess) return a1;
+    if (a3 != hipSuccess) return a3;
+    (void)hipGetLastError();
+    const unsigned nunits = (unsigned)((int64_t)p.nbh * p.nc);
+    if (nunits > 0) {
+        hipLaunchKernelGGL(k1, dim3(nunits), dim3(256), local_lds<Cf>(), stream, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t nthr = (int64_t)p.nbh * (p.N / 2) * p.P;
+    hipLaunchKernelGGL(bc_scan_kernel<IO>, dim3((unsigned)((nthr + 255) / 256), 2), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (nunits > 0) {
+        hipLaunchKernelGGL(k3, dim3(nunits), dim3(256), grad_lds<Cf>(), stream, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(bc_final_kernel<IO>, dim3((unsigned)p.nbh), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t batch = p.nbh / p.H;
+    hipLaunchKernelGGL(bc_dA_kernel, dim3((unsigned)((p.H + 63) / 64)), dim3(64), 0, stream,
+                       (const float*)p.dA_bh, p.dA, batch, p.H);
+    return hipGetLastError();
+}
+
+}  // namespace bc
+}  // namespace m3
+
+namespace m3 {
+namespace bc {
+
+// Dispatch over headdim and rank for one (operand type, dstate).
+template <typename OP, int N>
+hipError_t launch_pr(const BcParams& p, hipStream_t s)
+{
+    if (p.P == 32) {
+        switch (p.R) {
+        case 1: return launch_cfg<Cfg<OP, N, 32, 1>>(p, s);
+        case 2: return launch_cfg<Cfg<OP, N, 32, 2>>(p, s);
+        default: return launch_cfg<Cfg<OP, N, 32, 4>>(p, s);
+        }
+    }
+    switch (p.R) {
+    case 1: return launch_cfg<Cfg<OP, N, 64, 1>>(p, s);
+    case 2: return launch_cfg<Cfg<OP, N, 64, 2>>(p, s);
+    default: return launch_cfg<Cfg<OP, N, 64, 4>>(p, s);
+    }
+}
+
+// One translation unit per (operand type, dstate) set.
+hipError_t launch_bf16_n32(const BcParams& p, hipStream_t s);
+hipError_t launch_bf16_n64(const BcParams& p, hipStream_t s);
+hipError_t launch_bf16_n128(const BcParams& p, hipStream_t s);
+hipError_t launch_f32_n32(const BcParams& p, hipStream_t s);
+hipError_t launch_f32_n64(const BcParams& p, hipStream_t s);
+
+}  // namespace bc
+}  // namespace m3

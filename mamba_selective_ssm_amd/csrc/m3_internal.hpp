@@ -63,6 +63,33 @@ int bwd_blocks_per_checkpoint(int64_t N, int64_t P, int64_t R, int io_dtype);
 int bwd_pair_parts(int64_t N);
 hipError_t launch_bwd(const BwdParams& p, int io_dtype, float* dA, hipStream_t stream);
 
+// Gradient of the scan in chunked (SSD) form: per-chunk local sums, a scan of
+// the chunk-boundary states forward and of their adjoints backward, then
+// every gradient of a chunk from its two boundary states on matrix cores.
+struct BcParams {
+    const void *x, *B, *C, *dy;
+    const float *dt, *A, *theta, *lam;
+    const float *h_in;
+    const void *Bp_in, *xp_in;
+    const float *dh_out;
+    float *dx, *dB, *dC, *ddt, *dtheta, *dlam;
+    float *dh_in, *dBp, *dxp, *dA;
+    float *loc;       // [B*H][nc][2][N][P] chunk-local state and adjoint sums
+    float *csum;      // [B*H][nc][1 + N] e^{Lam_tot}, then cos, sin of Phi_tot per pair
+    float *gst;       // [B*H][nc + 1][N][P] state at each chunk start, then the final state
+    float *dgst;      // [B*H][nc + 1][N][P] adjoint of each chunk's end state, then of the initial state
+    float *dA_part;   // [B*H][nc] each chunk's share of dA
+    float *dw_last;   // [B*H][nc] gradient of the look-ahead weight of a chunk's last token
+    float *dA_bh;     // [B*H] each unit's share of dA
+    int64_t L, H;
+    int N, P, R;
+    int nbh, nc;      // (b, h) units; chunks per unit
+};
+
+bool bwd_chunked_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
+int bwd_chunk_tokens(int64_t R);
+hipError_t launch_bwd_chunked(const BcParams& p, int io_dtype, hipStream_t stream);
+
 bool decode_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
 hipError_t launch_decode(const DecodeParams& p, int io_dtype, hipStream_t stream);
 

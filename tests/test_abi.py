@@ -111,6 +111,11 @@ def bwd_args(**kw):
     (dict(dB=FAKE + (10 << 32) + 64), -7),                 # dB overlaps dC
     (dict(workspace=None), -6), (dict(workspace_bytes=16), -6),
     (dict(workspace=FAKE + (30 << 32) + 16), -5),
+    (dict(method=3), -9), (dict(method=-1), -9),           # not an m3_bwd_method
+    (dict(method=2, headdim=16), -3),                      # chunked: headdim 32 or 64
+    (dict(method=2, dstate=48), -3),                       # chunked: dstate 32, 64, 128
+    (dict(method=2, dstate=128, io_dtype=0), -3),          # chunked float32: dstate <= 64
+    (dict(method=1, headdim=128), -3),
 ])
 def test_bwd_validation_codes(lib, kw, code):
     assert lib.m3_scan_bwd(ctypes.byref(bwd_args(**kw)), None) == code
@@ -122,14 +127,24 @@ def test_bwd_supported_and_workspace(lib):
             for P in (16, 32, 64):
                 for R in (1, 2, 4):
                     assert lib.m3_scan_bwd_supported(N, P, R, io) == 1
+                    assert lib.m3_scan_bwd_method_supported(N, P, R, io, 1) == 1
+                    chunked = P in (32, 64) and N in ((32, 64, 128) if io == 1 else (32, 64))
+                    assert lib.m3_scan_bwd_method_supported(N, P, R, io, 2) == int(chunked)
+                    assert lib.m3_scan_bwd_method_supported(N, P, R, io, 0) == 1
     assert lib.m3_scan_bwd_supported(64, 128, 1, 1) == 0
-    ws = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(seqlen=2048)))
+    assert lib.m3_scan_bwd_method_supported(64, 64, 1, 1, 3) == 0
+    ws = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(seqlen=2048, method=1)))
     # one checkpoint per 32 steps per (b, h), N x P floats, plus scratch
     assert ws >= 6 * 64 * 64 * 64 * 4
+    # chunked: per (b, h) the two local sums of 32 chunks and 33 states and adjoints
+    wc = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(seqlen=2048, method=2)))
+    assert wc >= 6 * (32 * 2 + 33 * 2) * 64 * 64 * 4
+    assert lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(seqlen=2048))) == wc
+    assert lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(method=5))) == 0
 
 
 def test_version_and_status_strings(lib):
-    assert lib.m3_abi_version() == 2
+    assert lib.m3_abi_version() == 3
     for code in range(-9, 1):
         s = lib.m3_status_string(code)
         assert s and s != b"unknown status"

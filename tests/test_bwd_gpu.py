@@ -1,5 +1,6 @@
-"""Parity of the HIP scan gradient (m3_scan_bwd) against the fp64 gradient
-oracle (reverse-mode differentiation of the step recurrence).
+"""Parity of the HIP scan gradient (m3_scan_bwd, both methods: the adjoint
+recurrence step by step and the reverse mode of the chunked form) against the
+fp64 gradient oracle (reverse-mode differentiation of the step recurrence).
 
 Metric per gradient tensor: max |got - ref| / max |ref|; tolerance 1e-4 for
 float32 inputs and 2e-2 for bfloat16 inputs (the kernel computes in float32
@@ -19,17 +20,22 @@ NAMES = ["dx", "dB", "dC", "ddt", "dA", "dtheta", "dlam", "dh_in", "dB_prev", "d
 ORACLE = {"dh_in": "dh0", "dB_prev": "dBprev", "dx_prev": "dxprev"}
 
 
-def grads_case(w, seed, with_state=True, with_dh=True, label=""):
-    say("case %s: B%d L%d H%d R%d P%d N%d %s state=%s dh=%s seed=%d" % (
-        label, w.batch, w.seqlen, w.heads, w.rank, w.headdim, w.dstate, w.io_dtype, with_state,
-        with_dh, seed))
+def chunked_ok(io, N, P, R):
+    """The chunked method's supported set (include/m3scan.h)."""
+    return P in (32, 64) and R in (1, 2, 4) and N in ((32, 64, 128) if io == "bf16" else (32, 64))
+
+
+def grads_case(w, seed, with_state=True, with_dh=True, label="", method="auto"):
+    say("case %s [%s]: B%d L%d H%d R%d P%d N%d %s state=%s dh=%s seed=%d" % (
+        label, method, w.batch, w.seqlen, w.heads, w.rank, w.headdim, w.dstate, w.io_dtype,
+        with_state, with_dh, seed))
     inp = synth.make_scan_inputs(w, seed, DEV)
     g = torch.Generator(device=DEV).manual_seed(seed + 1)
     dy = torch.randn(inp["x"].shape, generator=g, device=DEV).to(w.torch_dtype)
     dh = torch.randn(w.batch, w.heads, w.dstate, w.headdim, generator=g, device=DEV) if with_dh else None
     st = random_state(w, seed + 2, DEV) if with_state else None
     got = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
-                      inp["lam"], dy, State(*st) if st else None, dh)
+                      inp["lam"], dy, State(*st) if st else None, dh, method=method)
     torch.cuda.synchronize()
     ref = scan_backward(f64(inp["x"]), f64(inp["B"]), f64(inp["C"]), f64(inp["dt"]),
                         f64(inp["A"]), f64(inp["theta"]), f64(inp["lam"]), f64(dy),
@@ -47,48 +53,67 @@ def grads_case(w, seed, with_state=True, with_dh=True, label=""):
     return got, ref
 
 
-@pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N,P,R", [(16, 16, 1), (32, 32, 2), (64, 64, 1), (128, 64, 4),
-                                   (64, 16, 4), (128, 32, 1)])
-def test_bwd_shapes(io, N, P, R):
-    """Ragged length: several checkpoints, sub-blocks and a partial tail."""
+SHAPES = [(16, 16, 1), (32, 32, 2), (64, 64, 1), (128, 64, 4), (64, 16, 4), (128, 32, 1)]
+SHAPE_CASES = [(io, N, P, R, m) for io in ("f32", "bf16") for (N, P, R) in SHAPES
+               for m in ("step", "chunked") if m == "step" or chunked_ok(io, N, P, R)]
+
+
+@pytest.mark.parametrize("io,N,P,R,method", SHAPE_CASES)
+def test_bwd_shapes(io, N, P, R, method):
+    """Ragged length: several checkpoints (step) or chunks (chunked) and a
+    partial tail."""
     w = workload(2, 83, 3, R, P, N, io=io, dt_mu=-1.0, theta="uniform_pi")
-    grads_case(w, 500 + N + P + R, label="bwd-shapes")
+    grads_case(w, 500 + N + P + R, label="bwd-shapes", method=method)
 
 
+@pytest.mark.parametrize("method", ["step", "chunked"])
 @pytest.mark.parametrize("L", [0, 1, 2, 4, 5, 31, 32, 33, 65])
-def test_bwd_lengths(L):
-    """Lengths around the sub-block (4) and checkpoint (32) boundaries."""
+def test_bwd_lengths(L, method):
+    """Lengths around the sub-block (4), checkpoint (32) and chunk (32 tokens
+    at rank 2) boundaries."""
     w = workload(1, L, 2, 2, 32, 64, io="f32", dt_mu=-1.0, theta="uniform_pi")
-    grads_case(w, 520 + L, label="bwd-len")
+    grads_case(w, 520 + L, label="bwd-len", method=method)
 
 
-def test_bwd_without_state_or_final_gradient():
+@pytest.mark.parametrize("method", ["step", "chunked"])
+def test_bwd_without_state_or_final_gradient(method):
     w = workload(2, 40, 2, 1, 64, 64, io="f32", dt_mu=-1.0)
-    grads_case(w, 540, with_state=False, with_dh=False, label="bwd-plain")
+    grads_case(w, 540, with_state=False, with_dh=False, label="bwd-plain", method=method)
 
 
-def test_bwd_deterministic():
+@pytest.mark.parametrize("R", [1, 2, 4])
+def test_bwd_chunked_many_chunks(R):
+    """bf16, dstate 128: 5 chunks and a ragged tail, slow and fast decay."""
+    Q = 64 // R
+    w = workload(2, 4 * Q + 9, 3, R, 64, 128, io="bf16", dt_mu=-2.0)
+    grads_case(w, 570 + R, label="bwd-chunks", method="chunked")
+
+
+@pytest.mark.parametrize("method", ["step", "chunked"])
+def test_bwd_deterministic(method):
     w = workload(2, 70, 4, 2, 64, 128, io="bf16")
     inp = synth.make_scan_inputs(w, 550, DEV)
     dy = torch.randn(inp["x"].shape, device=DEV, generator=torch.Generator(device=DEV).manual_seed(1)).to(torch.bfloat16)
-    a = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"], inp["lam"], dy)
-    b = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"], inp["lam"], dy)
+    a = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"], inp["lam"], dy,
+                    method=method)
+    b = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"], inp["lam"], dy,
+                    method=method)
     torch.cuda.synchronize()
     for n in NAMES:
         assert torch.equal(getattr(a, n), getattr(b, n)), n
 
 
-def test_bwd_prefill_workload_sampled():
-    """The prefill_bf16 shapes (2048 steps, 64 checkpoints): one (b, h) unit's
-    gradients against the oracle run on that unit alone."""
+@pytest.mark.parametrize("method", ["step", "chunked"])
+def test_bwd_prefill_workload_sampled(method):
+    """The prefill_bf16 shapes (2048 steps: 64 checkpoints, or 32 chunks): two
+    (b, h) units' gradients against the oracle run on that unit alone."""
     w = synth.WORKLOADS["prefill_bf16"]
-    say("case bwd prefill_bf16 full size")
+    say("case bwd prefill_bf16 full size [%s]" % method)
     inp = synth.make_scan_inputs(w, 560, DEV)
     dy = torch.randn(inp["x"].shape, device=DEV,
                      generator=torch.Generator(device=DEV).manual_seed(561)).to(torch.bfloat16)
     got = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
-                      inp["lam"], dy)
+                      inp["lam"], dy, method=method)
     torch.cuda.synchronize()
     for b, h in [(0, 3), (3, 14)]:
         sel = lambda t: f64(t[b:b + 1, :, h:h + 1])
@@ -98,3 +123,24 @@ def test_bwd_prefill_workload_sampled():
             e = rel_err(sel(getattr(got, n)), ref[n])
             say("   unit (%d, %d) %s rel err %.2e" % (b, h, n, e))
             assert e <= TOL["bf16"], (n, e)
+
+
+def test_bwd_mimo_workload_sampled():
+    """The mimo_prefill_bf16 shapes (4096 steps, 256 chunks of 16 tokens,
+    dstate 128, rank 4): one (b, h) unit's gradients against the oracle."""
+    w = synth.WORKLOADS["mimo_prefill_bf16"]
+    say("case bwd mimo_prefill_bf16 full size [chunked]")
+    inp = synth.make_scan_inputs(w, 580, DEV)
+    dy = torch.randn(inp["x"].shape, device=DEV,
+                     generator=torch.Generator(device=DEV).manual_seed(581)).to(torch.bfloat16)
+    got = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
+                      inp["lam"], dy, method="chunked")
+    torch.cuda.synchronize()
+    b, h = 5, 17
+    sel = lambda t: f64(t[b:b + 1, :, h:h + 1])
+    ref = scan_backward(sel(inp["x"]), sel(inp["B"]), sel(inp["C"]), sel(inp["dt"]),
+                        f64(inp["A"][h:h + 1]), sel(inp["theta"]), sel(inp["lam"]), sel(dy))
+    for n in ["dx", "dB", "dC", "ddt", "dtheta", "dlam"]:
+        e = rel_err(sel(getattr(got, n)), ref[n])
+        say("   unit (%d, %d) %s rel err %.2e" % (b, h, n, e))
+        assert e <= TOL["bf16"], (n, e)
