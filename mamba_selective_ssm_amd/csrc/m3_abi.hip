@@ -218,10 +218,10 @@ m3_status plan_bwd(const m3_scan_bwd_args* a, BwdPlan* out)
         const int64_t Q = m3::bwd_chunk_tokens(R);
         out->nc = (L + Q - 1) / Q;
         if (nbh * out->nc >= ((int64_t)1 << 31)) return M3_ERR_UNSUPPORTED;
-        const size_t NP = (size_t)N * P;
-        out->loc_bytes = round256((size_t)nbh * out->nc * 2 * NP * 4);
+        const size_t NP = (size_t)N * P, es = (size_t)io_size(a->io_dtype);
+        out->loc_bytes = round256((size_t)nbh * out->nc * 2 * NP * es);
         out->cs_bytes = round256((size_t)nbh * out->nc * (1 + N) * 4);
-        out->st_bytes = round256((size_t)nbh * (out->nc + 1) * NP * 4);
+        out->st_bytes = round256((size_t)nbh * (out->nc + 1) * NP * es);
         out->chunk_bytes = round256((size_t)nbh * out->nc * 4);
         out->bh_bytes = round256((size_t)nbh * 4);
         out->ws = nbh > 0 ? out->loc_bytes + out->cs_bytes + 2 * out->st_bytes + 2 * out->chunk_bytes +
@@ -328,13 +328,13 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         q.dx = a->dx; q.dB = a->dB; q.dC = a->dC; q.ddt = a->ddt; q.dtheta = a->dtheta;
         q.dlam = a->dlam; q.dh_in = a->dh_in; q.dBp = a->dB_prev; q.dxp = a->dx_prev; q.dA = a->dA;
         char* w = static_cast<char*>(a->workspace);
-        q.loc = reinterpret_cast<float*>(w);
+        q.loc = w;
         w += plan.loc_bytes;
         q.csum = reinterpret_cast<float*>(w);
         w += plan.cs_bytes;
-        q.gst = reinterpret_cast<float*>(w);
+        q.gst = w;
         w += plan.st_bytes;
-        q.dgst = reinterpret_cast<float*>(w);
+        q.dgst = w;
         w += plan.st_bytes;
         q.dA_part = reinterpret_cast<float*>(w);
         w += plan.chunk_bytes;

@@ -51,7 +51,7 @@ namespace bc {
 
 template <typename OP, int N_, int P_, int R_>
 struct Cfg {
-    using op_t = OP;
+    using op_t = OP;                             // matrix-core operands and stored boundary states
     static constexpr int N = N_, P = P_, R = R_;
     static constexpr int T = 64;                 // operand rows per chunk (tokens x ranks)
     static constexpr int Q = T / R;              // tokens per chunk
@@ -63,16 +63,21 @@ struct Cfg {
     static constexpr int NT = N / 16, PT = P / 16, NB = N / 32, PB = P / 32;
     static constexpr int VE = 16 / E;            // elements per 16-byte vector
     static constexpr int TS = 72;                // floats per token-scalar slot
+    static constexpr int NW = 8, NTHR = 64 * NW; // waves / threads per workgroup
     static_assert(N % 32 == 0 && P % 32 == 0, "K blocks of 32");
 };
 
-// Token-scalar slots (TS floats each).
-enum { kDt, kLm, kLam, kEL, kW, kGa, kD, kRS, kCQ, kDiag = kCQ + 4, kE, kDD, kTD, kDW, kCross,
-       kDot, kZP, kNumSlots = kZP + 4 };
+// Token-scalar slots (TS floats each).  Partial sums carry one slot per
+// half of the output columns (RS, Diag, E, DD) or per row tile (CQ, ZP).
+enum { kDt, kLm, kLam, kEL, kW, kGa, kD, kRS, kCQ = kRS + 2, kDiag = kCQ + 4, kE = kDiag + 2,
+       kDD = kE + 2, kTD = kDD + 2, kCross, kDot, kZP, kNumSlots = kZP + 4 };
 
 constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
 
 // LDS carve-up (bytes).  GRAD adds the adjoint operands and the score tiles.
+// The chunk-start state, needed only after the (S o M)^T dY product, reuses
+// the S o M tile when it fits; the angle gradients of a token reuse that
+// token's X rows (X is last read before they are written) when they fit.
 template <class Cf, bool GRAD>
 struct Lay {
     static constexpr size_t rowsN = a16((size_t)Cf::T * Cf::LDN * Cf::E);
@@ -80,16 +85,39 @@ struct Lay {
     static constexpr size_t stNP = a16((size_t)Cf::N * Cf::LDP * Cf::E);
     static constexpr size_t sqT = a16((size_t)Cf::T * Cf::LDT * Cf::E);
     static constexpr size_t phi = a16((size_t)Cf::Q * Cf::LDH * 4);
+    static constexpr bool ALIAS_G = GRAD && stNP <= sqT;
+    static constexpr bool ALIAS_DPHI = GRAD && Cf::NPR * 4 <= Cf::R * Cf::LDP * Cf::E;
+    static constexpr int DPS = ALIAS_DPHI ? Cf::R * Cf::LDP * Cf::E / 4 : Cf::LDH;   // dPhi row stride
     static constexpr size_t oBb = 0, oCb = oBb + rowsN, oX = oCb + rowsN, oDY = oX + rowsP;
     static constexpr size_t oDG = oDY + rowsP;
-    static constexpr size_t oGi = oDG + (GRAD ? stNP : 0);
-    static constexpr size_t oSM = oGi + (GRAD ? stNP : 0);
+    static constexpr size_t oSM = oDG + (GRAD ? stNP : 0);
     static constexpr size_t odS = oSM + (GRAD ? sqT : 0);
-    static constexpr size_t oPhi = odS + (GRAD ? sqT : 0);
-    static constexpr size_t oDPhi = oPhi + phi;
-    static constexpr size_t oTok = oDPhi + (GRAD ? phi : 0);
+    static constexpr size_t oGi = ALIAS_G ? oSM : odS + (GRAD ? sqT : 0);
+    static constexpr size_t oPhi = odS + (GRAD ? sqT : 0) + (GRAD && !ALIAS_G ? stNP : 0);
+    static constexpr size_t oDPhi = ALIAS_DPHI ? oX : oPhi + phi;
+    static constexpr size_t oTok = oPhi + phi + (GRAD && !ALIAS_DPHI ? phi : 0);
     static constexpr size_t bytes = oTok + (size_t)kNumSlots * Cf::TS * 4;
 };
+
+template <typename OP> struct V4T;
+template <> struct V4T<bf16> { using type = bf16x4; };
+template <> struct V4T<float> { using type = f32x4; };
+template <typename OP> __device__ __forceinline__ typename V4T<OP>::type to_v4(const f32x4& v);
+template <> __device__ __forceinline__ bf16x4 to_v4<bf16>(const f32x4& v)
+{
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+    return o;
+}
+template <> __device__ __forceinline__ f32x4 to_v4<float>(const f32x4& v) { return v; }
+// Four consecutive stored-state elements as float32.
+__device__ __forceinline__ f32x4 ld4f(const bf16* q)
+{
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(q);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 ld4f(const float* q) { return *reinterpret_cast<const f32x4*>(q); }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -156,16 +184,34 @@ __device__ __forceinline__ void store4_op(bf16* q, const f32x4& v)
 }
 __device__ __forceinline__ void store4_op(float* q, const f32x4& v) { *reinterpret_cast<f32x4*>(q) = v; }
 
+// Values a thread keeps from the staging loads to the end of the gradient:
+// its theta items (for sum_i theta_i dphi_i) and its pair items of the
+// chunk-start state (written to LDS once its slot there is free).
+template <class Cf>
+struct Held {
+    static constexpr int IT = (Cf::Q * (Cf::NPR / 4) + Cf::NTHR - 1) / Cf::NTHR;
+    static constexpr int IG = (Cf::NPR * (Cf::P / 4) + Cf::NTHR - 1) / Cf::NTHR;
+    f32x4 th[IT];
+    typename V4T<typename Cf::op_t>::type g0[IG], g1[IG];
+};
+
 // Stage one chunk: token scalars, cumulative angles, rotated B and C rows, X
-// and dY rows (and for the gradient: the chunk-start state, the rotated
-// end-state adjoint and its dot / cross products with the end state).
+// and dY rows; for the gradient also the rotated end-state adjoint dGbar and,
+// in float32, the chunk-start terms e^{Lam_tot} <G_in, dGbar> and per pair
+// e^{Lam_tot} sum_p (G_in,0 dGbar_1 - G_in,1 dGbar_0) (the end state's
+// remaining share, sum_k d_k Bbar_k X_k, is added from the same per-token
+// products that enter the tokens' own gradients, so the two cancel exactly
+// where the reverse prefix sums say they must).  Every global load is issued
+// before the first barrier.
 template <class Cf, bool GRAD>
-__device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int bh, int c)
+__device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int bh, int c, Held<Cf>& hd)
 {
     using op_t = typename Cf::op_t;
     using L = Lay<Cf, GRAD>;
+    using HD = Held<Cf>;
     constexpr int T = Cf::T, Q = Cf::Q, R = Cf::R, N = Cf::N, P = Cf::P, NPR = Cf::NPR;
     constexpr int LDN = Cf::LDN, LDP = Cf::LDP, LDH = Cf::LDH, VE = Cf::VE, TS = Cf::TS;
+    constexpr int NTHR = Cf::NTHR, NW = Cf::NW;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t L_ = p.L, H = p.H, b = bh / H, h = bh % H;
     const int64_t t0 = (int64_t)c * Q;
@@ -177,98 +223,103 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
     float* sPhi = reinterpret_cast<float*>(lds + L::oPhi);
     float* sT = reinterpret_cast<float*>(lds + L::oTok);
     const float A = p.A[h];
+    const op_t* gin = reinterpret_cast<const op_t*>(p.gst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
+    const op_t* dgo = reinterpret_cast<const op_t*>(p.dgst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
+    const float* cst = p.csum + ((size_t)bh * p.nc + c) * (1 + N);
+    constexpr int G4 = P / 4;                        // lanes per pair in the state items
 
-    // ---- S1: raw rows into LDS (16-byte vectors; zero past the sequence) ----
-    {
-        constexpr int VB = N / VE, VX = P / VE;              // vectors per B / X row
-        const uint4 z = {0u, 0u, 0u, 0u};
-        constexpr int IB = (T * VB + 255) / 256, IX = (T * VX + 255) / 256;
-        uint4 vb[IB], vc[IB], vx[IX], vy[IX];
+    // ---- S1: every global load; raw rows into LDS ----------------------------
+    constexpr int VB = N / VE, VX = P / VE;          // vectors per B / X row
+    constexpr int IB = (T * VB + NTHR - 1) / NTHR, IX = (T * VX + NTHR - 1) / NTHR;
+    const uint4 z = {0u, 0u, 0u, 0u};
+    uint4 vb[IB], vc[IB], vx[IX], vy[IX];
 #pragma unroll
-        for (int it = 0; it < IB; ++it) {
-            const int v = tid + 256 * it;
-            vb[it] = z; vc[it] = z;
-            if (v < T * VB) {
-                const int rho = v / VB, q = v % VB;
-                const int64_t t = t0 + rho / R;
-                if (t < L_) {
-                    const size_t off = ((size_t)tok(t) * R + rho % R) * N + (size_t)q * VE;
-                    vb[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.B) + off);
-                    vc[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.C) + off);
-                }
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < IX; ++it) {
-            const int v = tid + 256 * it;
-            vx[it] = z; vy[it] = z;
-            if (v < T * VX) {
-                const int rho = v / VX, q = v % VX;
-                const int64_t t = t0 + rho / R;
-                if (t < L_) {
-                    const size_t off = ((size_t)tok(t) * R + rho % R) * P + (size_t)q * VE;
-                    vx[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.x) + off);
-                    vy[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.dy) + off);
-                }
-            }
-        }
-        // angles (raw theta for now), dt and lam of the chunk and of the next token
-        constexpr int IT = (Q * (NPR / 4) + 255) / 256;
-        f32x4 th[IT];
-#pragma unroll
-        for (int it = 0; it < IT; ++it) {
-            const int v = tid + 256 * it;
-            th[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (v < Q * (NPR / 4)) {
-                const int j = v / (NPR / 4), q = v % (NPR / 4);
-                if (t0 + j < L_) th[it] = *reinterpret_cast<const f32x4*>(p.theta + tok(t0 + j) * NPR + 4 * q);
-            }
-        }
-        float dtv = 0.f, lmv = 0.f;
-        if (tid <= Q && t0 + tid < L_) { dtv = p.dt[tok(t0 + tid)]; lmv = p.lam[tok(t0 + tid)]; }
-#pragma unroll
-        for (int it = 0; it < IB; ++it) {
-            const int v = tid + 256 * it;
-            if (v < T * VB) {
-                const int rho = v / VB, q = v % VB;
-                *reinterpret_cast<uint4*>(sBb + rho * LDN + q * VE) = vb[it];
-                *reinterpret_cast<uint4*>(sCb + rho * LDN + q * VE) = vc[it];
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < IX; ++it) {
-            const int v = tid + 256 * it;
-            if (v < T * VX) {
-                const int rho = v / VX, q = v % VX;
-                *reinterpret_cast<uint4*>(sX + rho * LDP + q * VE) = vx[it];
-                *reinterpret_cast<uint4*>(sDY + rho * LDP + q * VE) = vy[it];
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < IT; ++it) {
-            const int v = tid + 256 * it;
-            if (v < Q * (NPR / 4)) {
-                const int j = v / (NPR / 4), q = v % (NPR / 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sPhi[j * LDH + 4 * q + e] = th[it][e];
-            }
-        }
-        if (tid <= Q) { sT[kDt * TS + tid] = dtv; sT[kLm * TS + tid] = lmv; }
-        if constexpr (GRAD) {
-            // chunk-start state, operand type, same [N][P] layout
-            op_t* sGi = reinterpret_cast<op_t*>(lds + L::oGi);
-            const float* gin = p.gst + ((size_t)bh * (p.nc + 1) + c) * N * P;
-            constexpr int IG = (N * P / 4 + 255) / 256;
-#pragma unroll
-            for (int it = 0; it < IG; ++it) {
-                const int v = tid + 256 * it;
-                if (v < N * P / 4) {
-                    const int n = v / (P / 4), q = v % (P / 4);
-                    store4_op(sGi + n * LDP + 4 * q, *reinterpret_cast<const f32x4*>(gin + (size_t)n * P + 4 * q));
-                }
+    for (int it = 0; it < IB; ++it) {
+        const int v = tid + NTHR * it;
+        vb[it] = z; vc[it] = z;
+        if (v < T * VB) {
+            const int rho = v / VB, q = v % VB;
+            const int64_t t = t0 + rho / R;
+            if (t < L_) {
+                const size_t off = ((size_t)tok(t) * R + rho % R) * N + (size_t)q * VE;
+                vb[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.B) + off);
+                vc[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.C) + off);
             }
         }
     }
+#pragma unroll
+    for (int it = 0; it < IX; ++it) {
+        const int v = tid + NTHR * it;
+        vx[it] = z; vy[it] = z;
+        if (v < T * VX) {
+            const int rho = v / VX, q = v % VX;
+            const int64_t t = t0 + rho / R;
+            if (t < L_) {
+                const size_t off = ((size_t)tok(t) * R + rho % R) * P + (size_t)q * VE;
+                vx[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.x) + off);
+                vy[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.dy) + off);
+            }
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < HD::IT; ++it) {
+        const int v = tid + NTHR * it;
+        hd.th[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (v < Q * (NPR / 4)) {
+            const int j = v / (NPR / 4), q = v % (NPR / 4);
+            if (t0 + j < L_) hd.th[it] = *reinterpret_cast<const f32x4*>(p.theta + tok(t0 + j) * NPR + 4 * q);
+        }
+    }
+    float dtv = 0.f, lmv = 0.f;
+    if (tid <= Q && t0 + tid < L_) { dtv = p.dt[tok(t0 + tid)]; lmv = p.lam[tok(t0 + tid)]; }
+    // state pair items (i, q): rows 2i, 2i+1, columns 4q .. 4q+3
+    f32x4 sd0[HD::IG], sd1[HD::IG], sg0[HD::IG], sg1[HD::IG];
+    float scc[HD::IG], sss[HD::IG];
+    if constexpr (GRAD) {
+#pragma unroll
+        for (int it = 0; it < HD::IG; ++it) {
+            const int v = tid + NTHR * it;
+            sd0[it] = sd1[it] = sg0[it] = sg1[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+            scc[it] = 1.f; sss[it] = 0.f;
+            if (v < NPR * G4) {
+                const int i = v / G4, q = v % G4;
+                sd0[it] = ld4f(dgo + (size_t)(2 * i) * P + 4 * q);
+                sd1[it] = ld4f(dgo + (size_t)(2 * i + 1) * P + 4 * q);
+                sg0[it] = ld4f(gin + (size_t)(2 * i) * P + 4 * q);
+                sg1[it] = ld4f(gin + (size_t)(2 * i + 1) * P + 4 * q);
+                scc[it] = cst[1 + 2 * i];
+                sss[it] = cst[2 + 2 * i];
+            }
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < IB; ++it) {
+        const int v = tid + NTHR * it;
+        if (v < T * VB) {
+            const int rho = v / VB, q = v % VB;
+            *reinterpret_cast<uint4*>(sBb + rho * LDN + q * VE) = vb[it];
+            *reinterpret_cast<uint4*>(sCb + rho * LDN + q * VE) = vc[it];
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < IX; ++it) {
+        const int v = tid + NTHR * it;
+        if (v < T * VX) {
+            const int rho = v / VX, q = v % VX;
+            *reinterpret_cast<uint4*>(sX + rho * LDP + q * VE) = vx[it];
+            *reinterpret_cast<uint4*>(sDY + rho * LDP + q * VE) = vy[it];
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < HD::IT; ++it) {
+        const int v = tid + NTHR * it;
+        if (v < Q * (NPR / 4)) {
+            const int j = v / (NPR / 4), q = v % (NPR / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sPhi[j * LDH + 4 * q + e] = hd.th[it][e];
+        }
+    }
+    if (tid <= Q) { sT[kDt * TS + tid] = dtv; sT[kLm * TS + tid] = lmv; }
     __syncthreads();
 
     // ---- S2: token scalars (wave 0) and cumulative angles (all waves) ------
@@ -291,7 +342,7 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
     }
     {
         const float dtj = lane < Q ? sT[kDt * TS + lane] : 0.f;
-        for (int i = wv; i < NPR; i += 4) {
+        for (int i = wv; i < NPR; i += NW) {
             const float v = lane < Q ? dtj * sPhi[lane * LDH + i] : 0.f;
             const float ph = wave_inclusive_sum(v);
             if (lane < Q) sPhi[lane * LDH + i] = ph;
@@ -302,7 +353,7 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
     // ---- S3: rotate B and C rows by R(Phi)^T in place ------------------------
     {
         constexpr int NI = T * (NPR / 4);
-        for (int v = tid; v < NI; v += 256) {
+        for (int v = tid; v < NI; v += NTHR) {
             const int rho = v / (NPR / 4), qd = v % (NPR / 4);
             const int j = rho / R;
             float cs[4], sn[4];
@@ -326,64 +377,70 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
         }
     }
     if constexpr (GRAD) {
-        // dGbar = R(Phi_tot)^T dG_out into LDS, and in float32 the chunk-start
-        // terms of the end state's angle and decay gradients: per pair
-        // e^{Lam_tot} sum_p (G_in,0 dGbar_1 - G_in,1 dGbar_0) and the whole
-        // e^{Lam_tot} <G_in, dGbar>.  (The end state's remaining share,
-        // sum_k d_k Bbar_k X_k, is added from the same per-token products that
-        // enter the tokens' own gradients, so the two cancel exactly where the
-        // reverse prefix sums say they must.)
         op_t* sDG = reinterpret_cast<op_t*>(lds + L::oDG);
-        const float* dgo = p.dgst + ((size_t)bh * (p.nc + 1) + c) * N * P;
-        const float* gi = p.gst + ((size_t)bh * (p.nc + 1) + c) * N * P;
-        const float* cst = p.csum + ((size_t)bh * p.nc + c) * (1 + N);
         const float el_tot = sT[kEL * TS + Q - 1];
-        constexpr int G4 = P / 4;                        // lanes per pair (8 or 16)
-        constexpr int NI = NPR * G4;
         float dot = 0.f;
-        for (int v0 = 0; v0 < NI; v0 += 256) {
-            const int v = v0 + tid;
-            float cr = 0.f;
-            if (v < NI) {
-                const int i = v / G4, q = v % G4;
-                const float cc = cst[1 + 2 * i], ss = cst[2 + 2 * i];
-                const f32x4 d0 = *reinterpret_cast<const f32x4*>(dgo + (size_t)(2 * i) * P + 4 * q);
-                const f32x4 d1 = *reinterpret_cast<const f32x4*>(dgo + (size_t)(2 * i + 1) * P + 4 * q);
-                const f32x4 g0 = *reinterpret_cast<const f32x4*>(gi + (size_t)(2 * i) * P + 4 * q);
-                const f32x4 g1 = *reinterpret_cast<const f32x4*>(gi + (size_t)(2 * i + 1) * P + 4 * q);
-                f32x4 r0, r1;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    r0[e] = cc * d0[e] + ss * d1[e];
-                    r1[e] = cc * d1[e] - ss * d0[e];
-                    cr += g0[e] * r1[e] - g1[e] * r0[e];
-                    dot += g0[e] * r0[e] + g1[e] * r1[e];
-                }
-                store4_op(sDG + (2 * i) * LDP + 4 * q, r0);
-                store4_op(sDG + (2 * i + 1) * LDP + 4 * q, r1);
+        for (int it = 0; it < HD::IG; ++it) {
+            const int v = tid + NTHR * it;
+            float cr = 0.f;
+            f32x4 r0, r1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r0[e] = scc[it] * sd0[it][e] + sss[it] * sd1[it][e];
+                r1[e] = scc[it] * sd1[it][e] - sss[it] * sd0[it][e];
+                cr += sg0[it][e] * r1[e] - sg1[it][e] * r0[e];
+                dot += sg0[it][e] * r0[e] + sg1[it][e] * r1[e];
+            }
+            hd.g0[it] = to_v4<op_t>(sg0[it]);
+            hd.g1[it] = to_v4<op_t>(sg1[it]);
+            if (v < NPR * G4) {
+                const int i = v / G4, q = v % G4;
+                *reinterpret_cast<typename V4T<op_t>::type*>(sDG + (2 * i) * LDP + 4 * q) = to_v4<op_t>(r0);
+                *reinterpret_cast<typename V4T<op_t>::type*>(sDG + (2 * i + 1) * LDP + 4 * q) = to_v4<op_t>(r1);
             }
             cr = group_sum<G4>(cr);
-            if (v < NI && (v % G4) == 0) sT[kCross * TS + v / G4] = el_tot * cr;
+            if (v < NPR * G4 && (v % G4) == 0) sT[kCross * TS + v / G4] = el_tot * cr;
         }
         dot = wave_read_lane(wave_inclusive_sum(dot), 63);
         if (lane == 0) sT[kDot * TS + wv] = el_tot * dot;
     }
 }
 
+// The chunk-start state from the thread's held items into LDS.
+template <class Cf>
+__device__ __forceinline__ void put_gin(typename Cf::op_t* sGi, const Held<Cf>& hd)
+{
+    using HD = Held<Cf>;
+    constexpr int G4 = Cf::P / 4, LDP = Cf::LDP;
+#pragma unroll
+    for (int it = 0; it < HD::IG; ++it) {
+        const int v = threadIdx.x + Cf::NTHR * it;
+        if (v < Cf::NPR * G4) {
+            const int i = v / G4, q = v % G4;
+            *reinterpret_cast<typename V4T<typename Cf::op_t>::type*>(sGi + (2 * i) * LDP + 4 * q) = hd.g0[it];
+            *reinterpret_cast<typename V4T<typename Cf::op_t>::type*>(sGi + (2 * i + 1) * LDP + 4 * q) = hd.g1[it];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Chunk-local sums: Gloc = Bbar^T diag(d) X and V = Cbar^T diag(e^Lam) dY
-// (N x P each, chunk-local frame), e^{Lam_tot}, cos/sin of Phi_tot.
+// (N x P each, chunk-local frame, stored in the operand type), e^{Lam_tot},
+// cos/sin of Phi_tot.
 template <class Cf>
-__global__ __launch_bounds__(256) void bc_local_kernel(const BcParams p)
+__global__ __launch_bounds__(512) void bc_local_kernel(const BcParams p)
 {
     using op_t = typename Cf::op_t;
     using L = Lay<Cf, false>;
     constexpr int T = Cf::T, Q = Cf::Q, R = Cf::R, N = Cf::N, P = Cf::P, NPR = Cf::NPR;
     constexpr int LDN = Cf::LDN, LDP = Cf::LDP, LDH = Cf::LDH, TS = Cf::TS, NT = Cf::NT, PT = Cf::PT;
+    constexpr int NTHR = Cf::NTHR, NW = Cf::NW;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int bh = blockIdx.x / p.nc, c = blockIdx.x % p.nc;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
-    stage<Cf, false>(p, lds, bh, c);
+    Held<Cf> hd;
+    stage<Cf, false>(p, lds, bh, c, hd);
     op_t* sBb = reinterpret_cast<op_t*>(lds + L::oBb);
     op_t* sCb = reinterpret_cast<op_t*>(lds + L::oCb);
     op_t* sX = reinterpret_cast<op_t*>(lds + L::oX);
@@ -391,7 +448,7 @@ __global__ __launch_bounds__(256) void bc_local_kernel(const BcParams p)
     const float* sPhi = reinterpret_cast<const float*>(lds + L::oPhi);
     const float* sT = reinterpret_cast<const float*>(lds + L::oTok);
     // scale X rows by d and dY rows by e^{Lam} in place
-    for (int v = tid; v < T * (P / 8); v += 256) {
+    for (int v = tid; v < T * (P / 8); v += NTHR) {
         const int rho = v / (P / 8), q = v % (P / 8);
         const int j = rho / R;
         const float d = sT[kD * TS + j], el = sT[kEL * TS + j];
@@ -404,9 +461,9 @@ __global__ __launch_bounds__(256) void bc_local_kernel(const BcParams p)
         lds_store8(sDY + rho * LDP + 8 * q, yv);
     }
     __syncthreads();
-    float* out = p.loc + ((size_t)bh * p.nc + c) * 2 * N * P;
+    op_t* out = reinterpret_cast<op_t*>(p.loc) + ((size_t)bh * p.nc + c) * 2 * N * P;
     constexpr int NTILE = 2 * NT * PT;
-    for (int tl = wv; tl < NTILE; tl += 4) {
+    for (int tl = wv; tl < NTILE; tl += NW) {
         const int prod = tl / (NT * PT), nt = (tl % (NT * PT)) / PT, pt = tl % PT;
         const op_t* sa = prod ? sCb : sBb;
         const op_t* sb = prod ? sDY : sX;
@@ -418,9 +475,9 @@ __global__ __launch_bounds__(256) void bc_local_kernel(const BcParams p)
             frag_col(bb, sb, LDP, 32 * kb, 16 * pt, l16, g);
             mma(a, bb, acc);
         }
-        float* o = out + (size_t)prod * N * P + (size_t)(16 * nt + 4 * g) * P + 16 * pt + l16;
+        op_t* o = out + (size_t)prod * N * P + (size_t)(16 * nt + 4 * g) * P + 16 * pt + l16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[(size_t)i * P] = acc[i];
+        for (int i = 0; i < 4; ++i) o[(size_t)i * P] = (op_t)acc[i];
     }
     if (tid <= NPR) {
         float* cs = p.csum + ((size_t)bh * p.nc + c) * (1 + N);
@@ -439,8 +496,9 @@ __global__ __launch_bounds__(256) void bc_local_kernel(const BcParams p)
 // Chunk-boundary states: forward G_in(c+1) = R(Phi_tot)(e^{Lam_tot} G_in(c) +
 // Gloc(c)) from G_in(0) = h_in + bhat_0 B_prev x_prev; backward
 // dG_in(c) = e^{Lam_tot} R(Phi_tot)^T dG_out(c) + V(c) from dG_out = dh_out.
-// One thread per (b, h, pair, column); blockIdx.y picks the direction.
-template <typename IO>
+// One thread per (b, h, pair, column), float32 recurrence, states stored in
+// ST; blockIdx.y picks the direction.
+template <typename IO, typename ST>
 __global__ __launch_bounds__(256) void bc_scan_kernel(const BcParams p)
 {
     const int N = p.N, P = p.P, R = p.R, NPR = N / 2, nc = p.nc;
@@ -452,7 +510,7 @@ __global__ __launch_bounds__(256) void bc_scan_kernel(const BcParams p)
     const size_t NP = (size_t)N * P;
     const size_t o0 = (size_t)(2 * i) * P + q, o1 = o0 + P;
     const float* cs = p.csum + (size_t)bh * nc * (1 + N);
-    const float* lc = p.loc + (size_t)bh * nc * 2 * NP;
+    const ST* lc = reinterpret_cast<const ST*>(p.loc) + (size_t)bh * nc * 2 * NP;
     constexpr int U = 8;
     if (blockIdx.y == 0) {
         float g0 = 0.f, g1 = 0.f;
@@ -471,15 +529,15 @@ __global__ __launch_bounds__(256) void bc_scan_kernel(const BcParams p)
             g0 += bhat * u0;
             g1 += bhat * u1;
         }
-        float* G = p.gst + (size_t)bh * (nc + 1) * NP;
+        ST* G = reinterpret_cast<ST*>(p.gst) + (size_t)bh * (nc + 1) * NP;
         for (int c0 = 0; c0 < nc; c0 += U) {
             float l0[U], l1[U], e[U], cc[U], ss[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + u;
                 if (c < nc) {
-                    l0[u] = lc[(size_t)c * 2 * NP + o0];
-                    l1[u] = lc[(size_t)c * 2 * NP + o1];
+                    l0[u] = to_f32(lc[(size_t)c * 2 * NP + o0]);
+                    l1[u] = to_f32(lc[(size_t)c * 2 * NP + o1]);
                     e[u] = cs[(size_t)c * (1 + N)];
                     cc[u] = cs[(size_t)c * (1 + N) + 1 + 2 * i];
                     ss[u] = cs[(size_t)c * (1 + N) + 2 + 2 * i];
@@ -489,28 +547,26 @@ __global__ __launch_bounds__(256) void bc_scan_kernel(const BcParams p)
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + u;
                 if (c < nc) {
-                    G[c * NP + o0] = g0;
-                    G[c * NP + o1] = g1;
+                    G[c * NP + o0] = (ST)g0;
+                    G[c * NP + o1] = (ST)g1;
                     const float a0 = e[u] * g0 + l0[u], a1 = e[u] * g1 + l1[u];
                     g0 = cc[u] * a0 - ss[u] * a1;
                     g1 = ss[u] * a0 + cc[u] * a1;
                 }
             }
         }
-        G[nc * NP + o0] = g0;
-        G[nc * NP + o1] = g1;
     } else {
         float d0 = 0.f, d1 = 0.f;
         if (p.dh_out != nullptr) { d0 = p.dh_out[bh * NP + o0]; d1 = p.dh_out[bh * NP + o1]; }
-        float* D = p.dgst + (size_t)bh * (nc + 1) * NP;
+        ST* D = reinterpret_cast<ST*>(p.dgst) + (size_t)bh * (nc + 1) * NP;
         for (int c0 = nc - 1; c0 >= 0; c0 -= U) {
             float v0[U], v1[U], e[U], cc[U], ss[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 - u;
                 if (c >= 0) {
-                    v0[u] = lc[((size_t)c * 2 + 1) * NP + o0];
-                    v1[u] = lc[((size_t)c * 2 + 1) * NP + o1];
+                    v0[u] = to_f32(lc[((size_t)c * 2 + 1) * NP + o0]);
+                    v1[u] = to_f32(lc[((size_t)c * 2 + 1) * NP + o1]);
                     e[u] = cs[(size_t)c * (1 + N)];
                     cc[u] = cs[(size_t)c * (1 + N) + 1 + 2 * i];
                     ss[u] = cs[(size_t)c * (1 + N) + 2 + 2 * i];
@@ -520,44 +576,51 @@ __global__ __launch_bounds__(256) void bc_scan_kernel(const BcParams p)
             for (int u = 0; u < U; ++u) {
                 const int c = c0 - u;
                 if (c >= 0) {
-                    D[c * NP + o0] = d0;
-                    D[c * NP + o1] = d1;
+                    D[c * NP + o0] = (ST)d0;
+                    D[c * NP + o1] = (ST)d1;
                     const float r0 = cc[u] * d0 + ss[u] * d1, r1 = cc[u] * d1 - ss[u] * d0;
                     d0 = e[u] * r0 + v0[u];
                     d1 = e[u] * r1 + v1[u];
                 }
             }
         }
-        D[nc * NP + o0] = d0;
-        D[nc * NP + o1] = d1;
+        D[nc * NP + o0] = (ST)d0;
+        D[nc * NP + o1] = (ST)d1;
         if (p.dh_in != nullptr) { p.dh_in[bh * NP + o0] = d0; p.dh_in[bh * NP + o1] = d1; }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Every gradient of one chunk.
+// Every gradient of one chunk.  Wave w owns operand rows 16 (w % 4) ..
+// 16 (w % 4) + 15 and half w / 4 of the output columns (of the key tiles in
+// the score phase).
 template <class Cf>
-__global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
+__global__ __launch_bounds__(512) void bc_grad_kernel(const BcParams p)
 {
     using op_t = typename Cf::op_t;
     using L = Lay<Cf, true>;
+    using HD = Held<Cf>;
     constexpr int T = Cf::T, Q = Cf::Q, R = Cf::R, N = Cf::N, P = Cf::P, NPR = Cf::NPR;
     constexpr int LDN = Cf::LDN, LDP = Cf::LDP, LDT = Cf::LDT, LDH = Cf::LDH, TS = Cf::TS;
-    constexpr int NT = Cf::NT, PT = Cf::PT, NB = Cf::NB, PB = Cf::PB;
+    constexpr int NT = Cf::NT, PT = Cf::PT, NB = Cf::NB, PB = Cf::PB, NTHR = Cf::NTHR, NW = Cf::NW;
+    constexpr int NH = NT / 2, PH = PT / 2;       // output column tiles per half
     constexpr int TPR = 4 / R;                    // tokens among a lane's 4 rows
+    constexpr int DPS = L::DPS;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int bh = blockIdx.x / p.nc, c = blockIdx.x % p.nc;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
+    const int rt = wv & 3, hf = wv >> 2;
     const int64_t L_ = p.L, H = p.H, b = bh / H, h = bh % H;
     const int64_t t0 = (int64_t)c * Q;
     auto tok = [&](int64_t t) -> int64_t { return (b * L_ + t) * H + h; };
-    stage<Cf, true>(p, lds, bh, c);
+    Held<Cf> hd;
+    stage<Cf, true>(p, lds, bh, c, hd);
     const op_t* sBb = reinterpret_cast<const op_t*>(lds + L::oBb);
     const op_t* sCb = reinterpret_cast<const op_t*>(lds + L::oCb);
     const op_t* sX = reinterpret_cast<const op_t*>(lds + L::oX);
     const op_t* sDY = reinterpret_cast<const op_t*>(lds + L::oDY);
     const op_t* sDG = reinterpret_cast<const op_t*>(lds + L::oDG);
-    const op_t* sGi = reinterpret_cast<const op_t*>(lds + L::oGi);
+    op_t* sGi = reinterpret_cast<op_t*>(lds + L::oGi);
     op_t* sSM = reinterpret_cast<op_t*>(lds + L::oSM);
     op_t* sdS = reinterpret_cast<op_t*>(lds + L::odS);
     const float* sPhi = reinterpret_cast<const float*>(lds + L::oPhi);
@@ -565,8 +628,8 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
     float* sT = reinterpret_cast<float*>(lds + L::oTok);
     __syncthreads();
 
-    const int r0w = 16 * wv;                      // this wave's operand rows
-    // ---- phase 1: S = Cbar Bbar^T, dSc = dY X^T on this wave's row tile ----
+    const int r0w = 16 * rt;                      // this wave's operand rows
+    // ---- phase 1: S = Cbar Bbar^T, dSc = dY X^T on key tiles kt = hf, hf + 2 --
     {
         float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diagacc[4] = {0.f, 0.f, 0.f, 0.f};
         float lam_r[4], ga_r[4];
@@ -577,15 +640,16 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
             ga_r[i] = sT[kGa * TS + tj];
         }
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int kt = hf + 2 * k2;
             const int ck = 16 * kt + l16;
-            if (kt > wv) {
+            if (kt > rt) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     sSM[(r0w + 4 * g + i) * LDT + ck] = (op_t)0.f;
                     sdS[(r0w + 4 * g + i) * LDT + ck] = (op_t)0.f;
                 }
-                if (g == 0) sT[(kCQ + wv) * TS + ck] = 0.f;
+                if (g == 0) sT[(kCQ + rt) * TS + ck] = 0.f;
                 continue;
             }
             f32x4 S = {0.f, 0.f, 0.f, 0.f}, D = {0.f, 0.f, 0.f, 0.f};
@@ -625,15 +689,15 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
             }
             colacc += __shfl_xor(colacc, 16, 64);
             colacc += __shfl_xor(colacc, 32, 64);
-            if (g == 0) sT[(kCQ + wv) * TS + ck] = colacc;
+            if (g == 0) sT[(kCQ + rt) * TS + ck] = colacc;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float rs = group_sum<16>(rowacc[i]);
             const float dg = group_sum<16>(diagacc[i]);
             if (l16 == 0) {
-                sT[kRS * TS + r0w + 4 * g + i] = rs;
-                sT[kDiag * TS + r0w + 4 * g + i] = dg;
+                sT[(kRS + hf) * TS + r0w + 4 * g + i] = rs;
+                sT[(kDiag + hf) * TS + r0w + 4 * g + i] = dg;
             }
         }
     }
@@ -641,17 +705,17 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
 
     // ---- phase 2a: dX = (S o M)^T dY + diag(d) Bbar dGbar^T ------------------
     {
-        f32x4 ax[PT], axs[PT];
+        f32x4 ax[PH], axs[PH];
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) { ax[pt] = f32x4{0.f, 0.f, 0.f, 0.f}; axs[pt] = ax[pt]; }
-        for (int jb = wv >> 1; jb < T / 32; ++jb) {
+        for (int u = 0; u < PH; ++u) { ax[u] = f32x4{0.f, 0.f, 0.f, 0.f}; axs[u] = ax[u]; }
+        for (int jb = rt >> 1; jb < T / 32; ++jb) {
             Frag<op_t> a;
             frag_col(a, sSM, LDT, 32 * jb, r0w, l16, g);
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
+            for (int u = 0; u < PH; ++u) {
                 Frag<op_t> bb;
-                frag_col(bb, sDY, LDP, 32 * jb, 16 * pt, l16, g);
-                mma(a, bb, ax[pt]);
+                frag_col(bb, sDY, LDP, 32 * jb, 16 * (hf * PH + u), l16, g);
+                mma(a, bb, ax[u]);
             }
         }
 #pragma unroll
@@ -659,10 +723,10 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
             Frag<op_t> a;
             frag_row(a, sBb, LDN, r0w, 32 * nb, l16, g);
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
+            for (int u = 0; u < PH; ++u) {
                 Frag<op_t> bb;
-                frag_col(bb, sDG, LDP, 32 * nb, 16 * pt, l16, g);
-                mma(a, bb, axs[pt]);
+                frag_col(bb, sDG, LDP, 32 * nb, 16 * (hf * PH + u), l16, g);
+                mma(a, bb, axs[u]);
             }
         }
 #pragma unroll
@@ -670,28 +734,30 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
             const int rk = r0w + 4 * g + i, tk = rk / R;
             if (t0 + tk < L_) {
                 const float dk = sT[kD * TS + tk];
-                float* o = p.dx + ((size_t)tok(t0 + tk) * R + rk % R) * P + l16;
+                float* o = p.dx + ((size_t)tok(t0 + tk) * R + rk % R) * P + 16 * hf * PH + l16;
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) o[16 * pt] = ax[pt][i] + dk * axs[pt][i];
+                for (int u = 0; u < PH; ++u) o[16 * u] = ax[u][i] + dk * axs[u][i];
             }
         }
     }
+    __syncthreads();                              // the S o M tile is free
+    put_gin<Cf>(sGi, hd);
 
     // Back-rotation of dBbar / dCbar rows held in accumulators (lane: column
     // n = 16 nt + l16, rows 4 g + i) to dB / dC, and the angle gradient of
     // each (token, pair) summed over ranks into sDPhi (ADD: accumulate).
-    auto back_rotate = [&](f32x4 (&acc)[NT], const op_t* sBar, float* gout, bool add) {
+    auto back_rotate = [&](f32x4 (&acc)[NH], const op_t* sBar, float* gout, bool add) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int n = 16 * nt + l16, pr = n >> 1;
+        for (int u = 0; u < NH; ++u) {
+            const int n = 16 * (hf * NH + u) + l16, pr = n >> 1;
             const bool odd = (l16 & 1) != 0;
             float dps[TPR];
 #pragma unroll
-            for (int u = 0; u < TPR; ++u) dps[u] = 0.f;
+            for (int v = 0; v < TPR; ++v) dps[v] = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rk = r0w + 4 * g + i, tk = rk / R;
-                const float own = acc[nt][i];
+                const float own = acc[u][i];
                 const float oth = pair_swap(own);
                 const float d0 = odd ? oth : own, d1 = odd ? own : oth;
                 const float bo = to_f32(sBar[rk * LDN + n]);
@@ -705,10 +771,10 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
             }
             if (!odd) {
 #pragma unroll
-                for (int u = 0; u < TPR; ++u) {
-                    const int tk = (r0w + 4 * g) / R + u;
-                    float* dp = sDPhi + tk * LDH + pr;
-                    *dp = add ? *dp + dps[u] : dps[u];
+                for (int v = 0; v < TPR; ++v) {
+                    const int tk = (r0w + 4 * g) / R + v;
+                    float* dp = sDPhi + tk * DPS + pr;
+                    *dp = add ? *dp + dps[v] : dps[v];
                 }
             }
         }
@@ -716,17 +782,17 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
 
     // ---- phase 2b: dBbar = dS^T Cbar + diag(d) Zb, Zb = X dGbar^T -------------
     {
-        f32x4 ab[NT], zb[NT];
+        f32x4 ab[NH], zb[NH];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) { ab[nt] = f32x4{0.f, 0.f, 0.f, 0.f}; zb[nt] = ab[nt]; }
-        for (int jb = wv >> 1; jb < T / 32; ++jb) {
+        for (int u = 0; u < NH; ++u) { ab[u] = f32x4{0.f, 0.f, 0.f, 0.f}; zb[u] = ab[u]; }
+        for (int jb = rt >> 1; jb < T / 32; ++jb) {
             Frag<op_t> a;
             frag_col(a, sdS, LDT, 32 * jb, r0w, l16, g);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+            for (int u = 0; u < NH; ++u) {
                 Frag<op_t> bb;
-                frag_col(bb, sCb, LDN, 32 * jb, 16 * nt, l16, g);
-                mma(a, bb, ab[nt]);
+                frag_col(bb, sCb, LDN, 32 * jb, 16 * (hf * NH + u), l16, g);
+                mma(a, bb, ab[u]);
             }
         }
 #pragma unroll
@@ -734,63 +800,64 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
             Frag<op_t> a;
             frag_row(a, sX, LDP, r0w, 32 * pb, l16, g);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+            for (int u = 0; u < NH; ++u) {
                 Frag<op_t> bb;
-                frag_row(bb, sDG, LDP, 16 * nt, 32 * pb, l16, g);
-                mma(a, bb, zb[nt]);
+                frag_row(bb, sDG, LDP, 16 * (hf * NH + u), 32 * pb, l16, g);
+                mma(a, bb, zb[u]);
             }
         }
-        // dd_k = <Bbar_k, Zb_k> per row, and per pair the sum over this wave's
-        // rows of d_k (Zb_0 Bbar_1 - Zb_1 Bbar_0) (the state term's share of
-        // the angle gradient)
+        __syncthreads();                          // X is free (angle gradients); G_in is staged
+        // dd_k = <Bbar_k, Zb_k> per row over this half's columns, and per pair
+        // the sum over this wave's rows of d_k (Zb_0 Bbar_1 - Zb_1 Bbar_0)
+        // (the state term's share of the angle gradient)
         float ddp[4] = {0.f, 0.f, 0.f, 0.f};
-        float zp[NT];
+        float zp[NH];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) zp[nt] = 0.f;
+        for (int u = 0; u < NH; ++u) zp[u] = 0.f;
         const bool odd = (l16 & 1) != 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rk = r0w + 4 * g + i;
             const float dk = sT[kD * TS + rk / R];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const float bo = to_f32(sBb[rk * LDN + 16 * nt + l16]);
-                const float bx = pair_swap(bo), zx = pair_swap(zb[nt][i]);
-                const float z0 = odd ? zx : zb[nt][i], z1 = odd ? zb[nt][i] : zx;
+            for (int u = 0; u < NH; ++u) {
+                const float bo = to_f32(sBb[rk * LDN + 16 * (hf * NH + u) + l16]);
+                const float bx = pair_swap(bo), zx = pair_swap(zb[u][i]);
+                const float z0 = odd ? zx : zb[u][i], z1 = odd ? zb[u][i] : zx;
                 const float b0 = odd ? bx : bo, b1 = odd ? bo : bx;
-                zp[nt] += dk * (z0 * b1 - z1 * b0);
-                ddp[i] += zb[nt][i] * bo;
-                ab[nt][i] += dk * zb[nt][i];
+                zp[u] += dk * (z0 * b1 - z1 * b0);
+                ddp[i] += zb[u][i] * bo;
+                ab[u][i] += dk * zb[u][i];
             }
         }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            float z = zp[nt];
-            z += __shfl_xor(z, 16, 64);
-            z += __shfl_xor(z, 32, 64);
-            if (g == 0 && !odd) sT[(kZP + wv) * TS + ((16 * nt + l16) >> 1)] = z;
+        for (int u = 0; u < NH; ++u) {
+            float zz = zp[u];
+            zz += __shfl_xor(zz, 16, 64);
+            zz += __shfl_xor(zz, 32, 64);
+            if (g == 0 && !odd) sT[(kZP + rt) * TS + ((16 * (hf * NH + u) + l16) >> 1)] = zz;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float s = group_sum<16>(ddp[i]);
-            if (l16 == 0) sT[kDD * TS + r0w + 4 * g + i] = s;
+            const float sm = group_sum<16>(ddp[i]);
+            if (l16 == 0) sT[(kDD + hf) * TS + r0w + 4 * g + i] = sm;
         }
         back_rotate(ab, sBb, p.dB, false);
     }
 
     // ---- phase 2c: dCbar = dS Bbar + diag(e^Lam) Zc, Zc = dY G_in^T -----------
     {
-        f32x4 ac[NT], zc[NT];
+        f32x4 ac[NH], zc[NH];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) { ac[nt] = f32x4{0.f, 0.f, 0.f, 0.f}; zc[nt] = ac[nt]; }
-        for (int kb = 0; kb <= (wv >> 1); ++kb) {
+        for (int u = 0; u < NH; ++u) { ac[u] = f32x4{0.f, 0.f, 0.f, 0.f}; zc[u] = ac[u]; }
+        for (int kb = 0; kb <= (rt >> 1); ++kb) {
             Frag<op_t> a;
             frag_row(a, sdS, LDT, r0w, 32 * kb, l16, g);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+            for (int u = 0; u < NH; ++u) {
                 Frag<op_t> bb;
-                frag_col(bb, sBb, LDN, 32 * kb, 16 * nt, l16, g);
-                mma(a, bb, ac[nt]);
+                frag_col(bb, sBb, LDN, 32 * kb, 16 * (hf * NH + u), l16, g);
+                mma(a, bb, ac[u]);
             }
         }
 #pragma unroll
@@ -798,10 +865,10 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
             Frag<op_t> a;
             frag_row(a, sDY, LDP, r0w, 32 * pb, l16, g);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+            for (int u = 0; u < NH; ++u) {
                 Frag<op_t> bb;
-                frag_row(bb, sGi, LDP, 16 * nt, 32 * pb, l16, g);
-                mma(a, bb, zc[nt]);
+                frag_row(bb, sGi, LDP, 16 * (hf * NH + u), 32 * pb, l16, g);
+                mma(a, bb, zc[u]);
             }
         }
         float ep[4] = {0.f, 0.f, 0.f, 0.f};
@@ -810,33 +877,33 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
             const int rj = r0w + 4 * g + i;
             const float el = sT[kEL * TS + rj / R];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                ep[i] += zc[nt][i] * to_f32(sCb[rj * LDN + 16 * nt + l16]);
-                ac[nt][i] += el * zc[nt][i];
+            for (int u = 0; u < NH; ++u) {
+                ep[i] += zc[u][i] * to_f32(sCb[rj * LDN + 16 * (hf * NH + u) + l16]);
+                ac[u][i] += el * zc[u][i];
             }
             ep[i] *= el;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float s = group_sum<16>(ep[i]);
-            if (l16 == 0) sT[kE * TS + r0w + 4 * g + i] = s;
+            const float sm = group_sum<16>(ep[i]);
+            if (l16 == 0) sT[(kE + hf) * TS + r0w + 4 * g + i] = sm;
         }
         back_rotate(ac, sCb, p.dC, true);
     }
     __syncthreads();
 
     // ---- phase 3a: dphi = suffix sums of dPhi over the chunk's tokens ---------
-    for (int i = wv; i < NPR; i += 4) {
+    for (int i = wv; i < NPR; i += NW) {
         float v = 0.f;
         if (lane < Q) {
-            v = sDPhi[lane * LDH + i];
+            v = sDPhi[lane * DPS + i];
             if (lane == Q - 1)
                 v += sT[kCross * TS + i] - (sT[kZP * TS + i] + sT[(kZP + 1) * TS + i] +
                                             sT[(kZP + 2) * TS + i] + sT[(kZP + 3) * TS + i]);
         }
         const float inc = wave_inclusive_sum(v);
         const float tot = wave_read_lane(inc, 63);
-        if (lane < Q) sDPhi[lane * LDH + i] = tot - inc + v;
+        if (lane < Q) sDPhi[lane * DPS + i] = tot - inc + v;
     }
     __syncthreads();
 
@@ -844,21 +911,21 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
     {
         constexpr int G4 = NPR / 4;               // lanes per token (4, 8 or 16)
         constexpr int NI = Q * G4;
-        for (int v0 = 0; v0 < NI; v0 += 256) {
-            const int v = v0 + tid;
+#pragma unroll
+        for (int it = 0; it < HD::IT; ++it) {
+            const int v = tid + NTHR * it;
             float td = 0.f;
             if (v < NI) {
                 const int j = v / G4, q = v % G4;
                 if (t0 + j < L_) {
                     const int64_t k = tok(t0 + j);
-                    const f32x4 th = *reinterpret_cast<const f32x4*>(p.theta + k * NPR + 4 * q);
                     const float dtj = sT[kDt * TS + j];
                     f32x4 o;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float dph = sDPhi[j * LDH + 4 * q + e];
+                        const float dph = sDPhi[j * DPS + 4 * q + e];
                         o[e] = dtj * dph;
-                        td += th[e] * dph;
+                        td += hd.th[it][e] * dph;
                     }
                     *reinterpret_cast<f32x4*>(p.dtheta + k * NPR + 4 * q) = o;
                 }
@@ -878,10 +945,10 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int rho = t * R + r;
-                rs += sT[kRS * TS + rho];
-                dg += sT[kDiag * TS + rho];
-                e += sT[kE * TS + rho];
-                dd += sT[kDD * TS + rho];
+                rs += sT[kRS * TS + rho] + sT[(kRS + 1) * TS + rho];
+                dg += sT[kDiag * TS + rho] + sT[(kDiag + 1) * TS + rho];
+                e += sT[kE * TS + rho] + sT[(kE + 1) * TS + rho];
+                dd += sT[kDD * TS + rho] + sT[(kDD + 1) * TS + rho];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) q += sT[(kCQ + w) * TS + rho];
             }
@@ -894,8 +961,12 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
         }
         // the end state's decay term: e^{Lam_tot} <G_in, dGbar> + sum_k d_k dd_k
         const float ddsum = wave_read_lane(wave_inclusive_sum(ddk), 63);
-        if (t == Q - 1)
-            dlam += sT[kDot * TS + 0] + sT[kDot * TS + 1] + sT[kDot * TS + 2] + sT[kDot * TS + 3] + ddsum;
+        if (t == Q - 1) {
+            float dsum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) dsum += sT[kDot * TS + w];
+            dlam += dsum + ddsum;
+        }
         const float inc = wave_inclusive_sum(dlam);
         const float da = wave_read_lane(inc, 63) - inc + dlam;
         const float dw_prev = __shfl_up(dw, 1, 64);
@@ -919,7 +990,7 @@ __global__ __launch_bounds__(256) void bc_grad_kernel(const BcParams p)
 // Per (b, h): the look-ahead weight of the last token of chunk c - 1 reaches
 // bhat of the first token of chunk c (and the state record's bhat_0 term for
 // chunk 0); the record's gradients; this unit's dA share.
-template <typename IO>
+template <typename IO, typename ST>
 __global__ __launch_bounds__(256) void bc_final_kernel(const BcParams p)
 {
     const int bh = blockIdx.x, tid = threadIdx.x;
@@ -927,7 +998,7 @@ __global__ __launch_bounds__(256) void bc_final_kernel(const BcParams p)
     const int N = p.N, P = p.P, R = p.R, nc = p.nc, Q = 64 / R;
     auto tok = [&](int64_t t) -> int64_t { return (b * p.L + t) * H + h; };
     __shared__ float red[256];
-    const float* dG0 = p.dgst + ((size_t)bh * (nc + 1) + nc) * N * P;
+    const ST* dG0 = reinterpret_cast<const ST*>(p.dgst) + ((size_t)bh * (nc + 1) + nc) * N * P;
     const float bhat0 = p.L > 0 ? (1.f - p.lam[tok(0)]) * p.dt[tok(0)] : 0.f;
     float part = 0.f;
     if (p.Bp_in != nullptr) {
@@ -936,7 +1007,7 @@ __global__ __launch_bounds__(256) void bc_final_kernel(const BcParams p)
         for (int v = tid; v < R * N; v += 256) {
             const int r = v / N, n = v % N;
             float z = 0.f;
-            for (int q = 0; q < P; ++q) z += dG0[(size_t)n * P + q] * to_f32(xp[r * P + q]);
+            for (int q = 0; q < P; ++q) z += to_f32(dG0[(size_t)n * P + q]) * to_f32(xp[r * P + q]);
             part += to_f32(Bp[r * N + n]) * z;
             if (p.dBp != nullptr) p.dBp[(size_t)bh * R * N + v] = bhat0 * z;
         }
@@ -944,7 +1015,7 @@ __global__ __launch_bounds__(256) void bc_final_kernel(const BcParams p)
             for (int v = tid; v < R * P; v += 256) {
                 const int r = v / P, q = v % P;
                 float s = 0.f;
-                for (int n = 0; n < N; ++n) s += to_f32(Bp[r * N + n]) * dG0[(size_t)n * P + q];
+                for (int n = 0; n < N; ++n) s += to_f32(Bp[r * N + n]) * to_f32(dG0[(size_t)n * P + q]);
                 p.dxp[(size_t)bh * R * P + v] = bhat0 * s;
             }
         }
@@ -1009,20 +1080,20 @@ hipError_t launch_cfg(const BcParams& p, hipStream_t stream)
     (void)hipGetLastError();
     const unsigned nunits = (unsigned)((int64_t)p.nbh * p.nc);
     if (nunits > 0) {
-        hipLaunchKernelGGL(k1, dim3(nunits), dim3(256), local_lds<Cf>(), stream, p);
+        hipLaunchKernelGGL(k1, dim3(nunits), dim3(Cf::NTHR), local_lds<Cf>(), stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t nthr = (int64_t)p.nbh * (p.N / 2) * p.P;
-    hipLaunchKernelGGL(bc_scan_kernel<IO>, dim3((unsigned)((nthr + 255) / 256), 2), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bc_scan_kernel<IO, IO>), dim3((unsigned)((nthr + 255) / 256), 2), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (nunits > 0) {
-        hipLaunchKernelGGL(k3, dim3(nunits), dim3(256), grad_lds<Cf>(), stream, p);
+        hipLaunchKernelGGL(k3, dim3(nunits), dim3(Cf::NTHR), grad_lds<Cf>(), stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(bc_final_kernel<IO>, dim3((unsigned)p.nbh), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bc_final_kernel<IO, IO>), dim3((unsigned)p.nbh), dim3(256), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t batch = p.nbh / p.H;

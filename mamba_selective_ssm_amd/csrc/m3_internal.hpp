@@ -74,10 +74,11 @@ struct BcParams {
     const float *dh_out;
     float *dx, *dB, *dC, *ddt, *dtheta, *dlam;
     float *dh_in, *dBp, *dxp, *dA;
-    float *loc;       // [B*H][nc][2][N][P] chunk-local state and adjoint sums
+    // Chunk-boundary arrays, stored in the io type (bf16 or float32):
+    void *loc;        // [B*H][nc][2][N][P] chunk-local state and adjoint sums
     float *csum;      // [B*H][nc][1 + N] e^{Lam_tot}, then cos, sin of Phi_tot per pair
-    float *gst;       // [B*H][nc + 1][N][P] state at each chunk start, then the final state
-    float *dgst;      // [B*H][nc + 1][N][P] adjoint of each chunk's end state, then of the initial state
+    void *gst;        // [B*H][nc + 1][N][P] state at each chunk start (last slot unused)
+    void *dgst;       // [B*H][nc + 1][N][P] adjoint of each chunk's end state, then of the initial state
     float *dA_part;   // [B*H][nc] each chunk's share of dA
     float *dw_last;   // [B*H][nc] gradient of the look-ahead weight of a chunk's last token
     float *dA_bh;     // [B*H] each unit's share of dA
