@@ -63,14 +63,23 @@ struct Cfg {
     static constexpr int NT = N / 16, PT = P / 16, NB = N / 32, PB = P / 32;
     static constexpr int VE = 16 / E;            // elements per 16-byte vector
     static constexpr int TS = 72;                // floats per token-scalar slot
-    static constexpr int NW = 8, NTHR = 64 * NW; // waves / threads per workgroup
+    // Output columns split NS ways: wave w owns row tile w % 4 and column part
+    // w / 4.  Four parts where the operand tiles leave one workgroup per
+    // compute unit (dstate 128), else two.
+    static constexpr int NS = (N == 128 && P == 64) ? 4 : 2;
+    static constexpr int NW = 4 * NS, NTHR = 64 * NW;   // waves / threads per workgroup
     static_assert(N % 32 == 0 && P % 32 == 0, "K blocks of 32");
+    static_assert(NT % NS == 0 && PT % NS == 0, "column parts");
 };
 
-// Token-scalar slots (TS floats each).  Partial sums carry one slot per
-// half of the output columns (RS, Diag, E, DD) or per row tile (CQ, ZP).
-enum { kDt, kLm, kLam, kEL, kW, kGa, kD, kRS, kCQ = kRS + 2, kDiag = kCQ + 4, kE = kDiag + 2,
-       kDD = kE + 2, kTD = kDD + 2, kCross, kDot, kZP, kNumSlots = kZP + 4 };
+// Token-scalar slots (TS floats each).  Partial sums carry one slot per row
+// tile (CQ, ZP) or per column part (RS, Diag, E, DD: Cf::NS each, placed
+// after the fixed slots by slots<Cf>).
+enum { kDt, kLm, kLam, kEL, kW, kGa, kD, kCQ, kTD = kCQ + 4, kCross, kDot, kZP, kFixedSlots = kZP + 4 };
+template <class Cf> struct slots {
+    static constexpr int RS = kFixedSlots, Diag = RS + Cf::NS, E = Diag + Cf::NS, DD = E + Cf::NS,
+                         count = DD + Cf::NS;
+};
 
 constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
 
@@ -96,7 +105,7 @@ struct Lay {
     static constexpr size_t oPhi = odS + (GRAD ? sqT : 0) + (GRAD && !ALIAS_G ? stNP : 0);
     static constexpr size_t oDPhi = ALIAS_DPHI ? oX : oPhi + phi;
     static constexpr size_t oTok = oPhi + phi + (GRAD && !ALIAS_DPHI ? phi : 0);
-    static constexpr size_t bytes = oTok + (size_t)kNumSlots * Cf::TS * 4;
+    static constexpr size_t bytes = oTok + (size_t)slots<Cf>::count * Cf::TS * 4;
 };
 
 template <typename OP> struct V4T;
@@ -429,7 +438,7 @@ __device__ __forceinline__ void put_gin(typename Cf::op_t* sGi, const Held<Cf>& 
 // (N x P each, chunk-local frame, stored in the operand type), e^{Lam_tot},
 // cos/sin of Phi_tot.
 template <class Cf>
-__global__ __launch_bounds__(512) void bc_local_kernel(const BcParams p)
+__global__ __launch_bounds__(Cf::NTHR) void bc_local_kernel(const BcParams p)
 {
     using op_t = typename Cf::op_t;
     using L = Lay<Cf, false>;
@@ -496,106 +505,130 @@ __global__ __launch_bounds__(512) void bc_local_kernel(const BcParams p)
 // Chunk-boundary states: forward G_in(c+1) = R(Phi_tot)(e^{Lam_tot} G_in(c) +
 // Gloc(c)) from G_in(0) = h_in + bhat_0 B_prev x_prev; backward
 // dG_in(c) = e^{Lam_tot} R(Phi_tot)^T dG_out(c) + V(c) from dG_out = dh_out.
-// One thread per (b, h, pair, column), float32 recurrence, states stored in
-// ST; blockIdx.y picks the direction.
+// One thread per (b, h, pair, two columns), float32 recurrence, states stored
+// in ST; blockIdx.y picks the direction.  Each batch of U chunks issues all its
+// loads (indices clamped into range) before the first use.
+template <typename ST> struct ST2T;
+template <> struct ST2T<bf16> { using type = bf16x2; };
+template <> struct ST2T<float> { using type = float2; };
+__device__ __forceinline__ float2 f2(const bf16x2 v) { return make_float2((float)v[0], (float)v[1]); }
+__device__ __forceinline__ float2 f2(const float2 v) { return v; }
+template <typename ST> __device__ __forceinline__ typename ST2T<ST>::type st2(float a, float b);
+template <> __device__ __forceinline__ bf16x2 st2<bf16>(float a, float b)
+{
+    bf16x2 v;
+    v[0] = (bf16)a;
+    v[1] = (bf16)b;
+    return v;
+}
+template <> __device__ __forceinline__ float2 st2<float>(float a, float b) { return make_float2(a, b); }
+
 template <typename IO, typename ST>
 __global__ __launch_bounds__(256) void bc_scan_kernel(const BcParams p)
 {
-    const int N = p.N, P = p.P, R = p.R, NPR = N / 2, nc = p.nc;
-    const int64_t per = (int64_t)NPR * P;
+    using V2 = typename ST2T<ST>::type;
+    const int N = p.N, P = p.P, R = p.R, NPR = N / 2, nc = p.nc, P2 = P / 2;
+    const int64_t per = (int64_t)NPR * P2;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)p.nbh * per) return;
     const int bh = (int)(idx / per);
-    const int rem = (int)(idx % per), i = rem / P, q = rem % P;
+    const int rem = (int)(idx % per), i = rem / P2, q = 2 * (rem % P2);
     const size_t NP = (size_t)N * P;
     const size_t o0 = (size_t)(2 * i) * P + q, o1 = o0 + P;
     const float* cs = p.csum + (size_t)bh * nc * (1 + N);
     const ST* lc = reinterpret_cast<const ST*>(p.loc) + (size_t)bh * nc * 2 * NP;
     constexpr int U = 8;
     if (blockIdx.y == 0) {
-        float g0 = 0.f, g1 = 0.f;
-        if (p.h_in != nullptr) { g0 = p.h_in[bh * NP + o0]; g1 = p.h_in[bh * NP + o1]; }
+        float2 g0 = make_float2(0.f, 0.f), g1 = g0;
+        if (p.h_in != nullptr) {
+            g0 = *reinterpret_cast<const float2*>(p.h_in + bh * NP + o0);
+            g1 = *reinterpret_cast<const float2*>(p.h_in + bh * NP + o1);
+        }
         if (p.Bp_in != nullptr && p.L > 0) {
             const int64_t b = bh / p.H, h = bh % p.H, k0 = (b * p.L) * p.H + h;
             const float bhat = (1.f - p.lam[k0]) * p.dt[k0];
             const IO* Bp = reinterpret_cast<const IO*>(p.Bp_in) + (size_t)bh * R * N;
             const IO* xp = reinterpret_cast<const IO*>(p.xp_in) + (size_t)bh * R * P;
-            float u0 = 0.f, u1 = 0.f;
             for (int r = 0; r < R; ++r) {
-                const float xv = to_f32(xp[r * P + q]);
-                u0 += to_f32(Bp[r * N + 2 * i]) * xv;
-                u1 += to_f32(Bp[r * N + 2 * i + 1]) * xv;
+                const float xa = to_f32(xp[r * P + q]), xb = to_f32(xp[r * P + q + 1]);
+                const float b0 = bhat * to_f32(Bp[r * N + 2 * i]), b1 = bhat * to_f32(Bp[r * N + 2 * i + 1]);
+                g0.x += b0 * xa; g0.y += b0 * xb;
+                g1.x += b1 * xa; g1.y += b1 * xb;
             }
-            g0 += bhat * u0;
-            g1 += bhat * u1;
         }
         ST* G = reinterpret_cast<ST*>(p.gst) + (size_t)bh * (nc + 1) * NP;
         for (int c0 = 0; c0 < nc; c0 += U) {
-            float l0[U], l1[U], e[U], cc[U], ss[U];
+            float2 l0[U], l1[U];
+            float e[U], cc[U], ss[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int c = c0 + u;
-                if (c < nc) {
-                    l0[u] = to_f32(lc[(size_t)c * 2 * NP + o0]);
-                    l1[u] = to_f32(lc[(size_t)c * 2 * NP + o1]);
-                    e[u] = cs[(size_t)c * (1 + N)];
-                    cc[u] = cs[(size_t)c * (1 + N) + 1 + 2 * i];
-                    ss[u] = cs[(size_t)c * (1 + N) + 2 + 2 * i];
-                }
+                const int c = c0 + u < nc ? c0 + u : nc - 1;
+                l0[u] = f2(*reinterpret_cast<const V2*>(lc + (size_t)c * 2 * NP + o0));
+                l1[u] = f2(*reinterpret_cast<const V2*>(lc + (size_t)c * 2 * NP + o1));
+                e[u] = cs[(size_t)c * (1 + N)];
+                cc[u] = cs[(size_t)c * (1 + N) + 1 + 2 * i];
+                ss[u] = cs[(size_t)c * (1 + N) + 2 + 2 * i];
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + u;
                 if (c < nc) {
-                    G[c * NP + o0] = (ST)g0;
-                    G[c * NP + o1] = (ST)g1;
-                    const float a0 = e[u] * g0 + l0[u], a1 = e[u] * g1 + l1[u];
-                    g0 = cc[u] * a0 - ss[u] * a1;
-                    g1 = ss[u] * a0 + cc[u] * a1;
+                    *reinterpret_cast<V2*>(G + c * NP + o0) = st2<ST>(g0.x, g0.y);
+                    *reinterpret_cast<V2*>(G + c * NP + o1) = st2<ST>(g1.x, g1.y);
+                    const float a0x = e[u] * g0.x + l0[u].x, a0y = e[u] * g0.y + l0[u].y;
+                    const float a1x = e[u] * g1.x + l1[u].x, a1y = e[u] * g1.y + l1[u].y;
+                    g0 = make_float2(cc[u] * a0x - ss[u] * a1x, cc[u] * a0y - ss[u] * a1y);
+                    g1 = make_float2(ss[u] * a0x + cc[u] * a1x, ss[u] * a0y + cc[u] * a1y);
                 }
             }
         }
     } else {
-        float d0 = 0.f, d1 = 0.f;
-        if (p.dh_out != nullptr) { d0 = p.dh_out[bh * NP + o0]; d1 = p.dh_out[bh * NP + o1]; }
+        float2 d0 = make_float2(0.f, 0.f), d1 = d0;
+        if (p.dh_out != nullptr) {
+            d0 = *reinterpret_cast<const float2*>(p.dh_out + bh * NP + o0);
+            d1 = *reinterpret_cast<const float2*>(p.dh_out + bh * NP + o1);
+        }
         ST* D = reinterpret_cast<ST*>(p.dgst) + (size_t)bh * (nc + 1) * NP;
         for (int c0 = nc - 1; c0 >= 0; c0 -= U) {
-            float v0[U], v1[U], e[U], cc[U], ss[U];
+            float2 v0[U], v1[U];
+            float e[U], cc[U], ss[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int c = c0 - u;
-                if (c >= 0) {
-                    v0[u] = to_f32(lc[((size_t)c * 2 + 1) * NP + o0]);
-                    v1[u] = to_f32(lc[((size_t)c * 2 + 1) * NP + o1]);
-                    e[u] = cs[(size_t)c * (1 + N)];
-                    cc[u] = cs[(size_t)c * (1 + N) + 1 + 2 * i];
-                    ss[u] = cs[(size_t)c * (1 + N) + 2 + 2 * i];
-                }
+                const int c = c0 - u >= 0 ? c0 - u : 0;
+                v0[u] = f2(*reinterpret_cast<const V2*>(lc + ((size_t)c * 2 + 1) * NP + o0));
+                v1[u] = f2(*reinterpret_cast<const V2*>(lc + ((size_t)c * 2 + 1) * NP + o1));
+                e[u] = cs[(size_t)c * (1 + N)];
+                cc[u] = cs[(size_t)c * (1 + N) + 1 + 2 * i];
+                ss[u] = cs[(size_t)c * (1 + N) + 2 + 2 * i];
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 - u;
                 if (c >= 0) {
-                    D[c * NP + o0] = (ST)d0;
-                    D[c * NP + o1] = (ST)d1;
-                    const float r0 = cc[u] * d0 + ss[u] * d1, r1 = cc[u] * d1 - ss[u] * d0;
-                    d0 = e[u] * r0 + v0[u];
-                    d1 = e[u] * r1 + v1[u];
+                    *reinterpret_cast<V2*>(D + c * NP + o0) = st2<ST>(d0.x, d0.y);
+                    *reinterpret_cast<V2*>(D + c * NP + o1) = st2<ST>(d1.x, d1.y);
+                    const float r0x = cc[u] * d0.x + ss[u] * d1.x, r0y = cc[u] * d0.y + ss[u] * d1.y;
+                    const float r1x = cc[u] * d1.x - ss[u] * d0.x, r1y = cc[u] * d1.y - ss[u] * d0.y;
+                    d0 = make_float2(e[u] * r0x + v0[u].x, e[u] * r0y + v0[u].y);
+                    d1 = make_float2(e[u] * r1x + v1[u].x, e[u] * r1y + v1[u].y);
                 }
             }
         }
-        D[nc * NP + o0] = (ST)d0;
-        D[nc * NP + o1] = (ST)d1;
-        if (p.dh_in != nullptr) { p.dh_in[bh * NP + o0] = d0; p.dh_in[bh * NP + o1] = d1; }
+        *reinterpret_cast<V2*>(D + nc * NP + o0) = st2<ST>(d0.x, d0.y);
+        *reinterpret_cast<V2*>(D + nc * NP + o1) = st2<ST>(d1.x, d1.y);
+        if (p.dh_in != nullptr) {
+            *reinterpret_cast<float2*>(p.dh_in + bh * NP + o0) = d0;
+            *reinterpret_cast<float2*>(p.dh_in + bh * NP + o1) = d1;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Every gradient of one chunk.  Wave w owns operand rows 16 (w % 4) ..
-// 16 (w % 4) + 15 and half w / 4 of the output columns (of the key tiles in
+// 16 (w % 4) + 15 and part w / 4 of the output columns (of the key tiles in
 // the score phase).
 template <class Cf>
-__global__ __launch_bounds__(512) void bc_grad_kernel(const BcParams p)
+__global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
 {
     using op_t = typename Cf::op_t;
     using L = Lay<Cf, true>;
@@ -603,7 +636,9 @@ __global__ __launch_bounds__(512) void bc_grad_kernel(const BcParams p)
     constexpr int T = Cf::T, Q = Cf::Q, R = Cf::R, N = Cf::N, P = Cf::P, NPR = Cf::NPR;
     constexpr int LDN = Cf::LDN, LDP = Cf::LDP, LDT = Cf::LDT, LDH = Cf::LDH, TS = Cf::TS;
     constexpr int NT = Cf::NT, PT = Cf::PT, NB = Cf::NB, PB = Cf::PB, NTHR = Cf::NTHR, NW = Cf::NW;
-    constexpr int NH = NT / 2, PH = PT / 2;       // output column tiles per half
+    constexpr int NS = Cf::NS;
+    constexpr int NH = NT / NS, PH = PT / NS;     // output column tiles per part
+    constexpr int kRS = slots<Cf>::RS, kDiag = slots<Cf>::Diag, kE = slots<Cf>::E, kDD = slots<Cf>::DD;
     constexpr int TPR = 4 / R;                    // tokens among a lane's 4 rows
     constexpr int DPS = L::DPS;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -629,7 +664,7 @@ __global__ __launch_bounds__(512) void bc_grad_kernel(const BcParams p)
     __syncthreads();
 
     const int r0w = 16 * rt;                      // this wave's operand rows
-    // ---- phase 1: S = Cbar Bbar^T, dSc = dY X^T on key tiles kt = hf, hf + 2 --
+    // ---- phase 1: S = Cbar Bbar^T, dSc = dY X^T on key tiles kt = hf (mod NS) --
     {
         float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diagacc[4] = {0.f, 0.f, 0.f, 0.f};
         float lam_r[4], ga_r[4];
@@ -640,8 +675,8 @@ __global__ __launch_bounds__(512) void bc_grad_kernel(const BcParams p)
             ga_r[i] = sT[kGa * TS + tj];
         }
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const int kt = hf + 2 * k2;
+        for (int k2 = 0; k2 < 4 / NS; ++k2) {
+            const int kt = hf + NS * k2;
             const int ck = 16 * kt + l16;
             if (kt > rt) {
 #pragma unroll
@@ -945,10 +980,13 @@ __global__ __launch_bounds__(512) void bc_grad_kernel(const BcParams p)
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int rho = t * R + r;
-                rs += sT[kRS * TS + rho] + sT[(kRS + 1) * TS + rho];
-                dg += sT[kDiag * TS + rho] + sT[(kDiag + 1) * TS + rho];
-                e += sT[kE * TS + rho] + sT[(kE + 1) * TS + rho];
-                dd += sT[kDD * TS + rho] + sT[(kDD + 1) * TS + rho];
+#pragma unroll
+                for (int u = 0; u < NS; ++u) {
+                    rs += sT[(kRS + u) * TS + rho];
+                    dg += sT[(kDiag + u) * TS + rho];
+                    e += sT[(kE + u) * TS + rho];
+                    dd += sT[(kDD + u) * TS + rho];
+                }
 #pragma unroll
                 for (int w = 0; w < 4; ++w) q += sT[(kCQ + w) * TS + rho];
             }
@@ -1084,7 +1122,7 @@ hipError_t launch_cfg(const BcParams& p, hipStream_t stream)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t nthr = (int64_t)p.nbh * (p.N / 2) * p.P;
+    const int64_t nthr = (int64_t)p.nbh * (p.N / 2) * (p.P / 2);
     hipLaunchKernelGGL((bc_scan_kernel<IO, IO>), dim3((unsigned)((nthr + 255) / 256), 2), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
