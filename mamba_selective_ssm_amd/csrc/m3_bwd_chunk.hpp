@@ -193,38 +193,129 @@ __device__ __forceinline__ void store4_op(bf16* q, const f32x4& v)
 }
 __device__ __forceinline__ void store4_op(float* q, const f32x4& v) { *reinterpret_cast<f32x4*>(q) = v; }
 
-// Values a thread keeps from the staging loads to the end of the gradient:
-// its theta items (for sum_i theta_i dphi_i) and its pair items of the
-// chunk-start state (written to LDS once its slot there is free).
+// One chunk's global inputs as a thread holds them between issuing the loads
+// and writing them to LDS (a workgroup loads the next chunk while it works on
+// the current one).
 template <class Cf>
-struct Held {
+struct Raw {
+    using V4 = typename V4T<typename Cf::op_t>::type;
+    static constexpr int VB = Cf::N / Cf::VE, VX = Cf::P / Cf::VE;      // vectors per B / X row
+    static constexpr int IB = (Cf::T * VB + Cf::NTHR - 1) / Cf::NTHR;
+    static constexpr int IX = (Cf::T * VX + Cf::NTHR - 1) / Cf::NTHR;
     static constexpr int IT = (Cf::Q * (Cf::NPR / 4) + Cf::NTHR - 1) / Cf::NTHR;
-    static constexpr int IG = (Cf::NPR * (Cf::P / 4) + Cf::NTHR - 1) / Cf::NTHR;
+    static constexpr int G4 = Cf::P / 4;                                // lanes per pair in state items
+    static constexpr int IG = (Cf::NPR * G4 + Cf::NTHR - 1) / Cf::NTHR;
+    uint4 vb[IB], vc[IB], vx[IX], vy[IX];
     f32x4 th[IT];
-    typename V4T<typename Cf::op_t>::type g0[IG], g1[IG];
+    float dtv, lmv;
+    V4 sd0[IG], sd1[IG], sg0[IG], sg1[IG];    // state pair items (rows 2i, 2i+1, columns 4q..4q+3)
+    float scc[IG], sss[IG];
 };
 
-// Stage one chunk: token scalars, cumulative angles, rotated B and C rows, X
-// and dY rows; for the gradient also the rotated end-state adjoint dGbar and,
-// in float32, the chunk-start terms e^{Lam_tot} <G_in, dGbar> and per pair
-// e^{Lam_tot} sum_p (G_in,0 dGbar_1 - G_in,1 dGbar_0) (the end state's
-// remaining share, sum_k d_k Bbar_k X_k, is added from the same per-token
-// products that enter the tokens' own gradients, so the two cancel exactly
-// where the reverse prefix sums say they must).  Every global load is issued
-// before the first barrier.
+// Values a thread keeps from staging to the end of the gradient: its theta
+// items (for sum_i theta_i dphi_i) and its pair items of the chunk-start
+// state (written to LDS once its slot there is free).
+template <class Cf>
+struct Held {
+    using V4 = typename V4T<typename Cf::op_t>::type;
+    static constexpr int IT = Raw<Cf>::IT, IG = Raw<Cf>::IG;
+    f32x4 th[IT];
+    V4 g0[IG], g1[IG];
+};
+
+__device__ __forceinline__ f32x4 v4f(const bf16x4& v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
+__device__ __forceinline__ f32x4 v4f(const f32x4& v) { return v; }
+
+// Issue every global load of chunk c of unit bh (zero past the sequence).
 template <class Cf, bool GRAD>
-__device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int bh, int c, Held<Cf>& hd)
+__device__ __forceinline__ void load_raw(const BcParams& p, int bh, int c, Raw<Cf>& rw, int tid)
 {
     using op_t = typename Cf::op_t;
-    using L = Lay<Cf, GRAD>;
-    using HD = Held<Cf>;
+    using RW = Raw<Cf>;
+    using V4 = typename RW::V4;
     constexpr int T = Cf::T, Q = Cf::Q, R = Cf::R, N = Cf::N, P = Cf::P, NPR = Cf::NPR;
-    constexpr int LDN = Cf::LDN, LDP = Cf::LDP, LDH = Cf::LDH, VE = Cf::VE, TS = Cf::TS;
-    constexpr int NTHR = Cf::NTHR, NW = Cf::NW;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    constexpr int VE = Cf::VE, NTHR = Cf::NTHR, VB = RW::VB, VX = RW::VX, G4 = RW::G4;
     const int64_t L_ = p.L, H = p.H, b = bh / H, h = bh % H;
     const int64_t t0 = (int64_t)c * Q;
     auto tok = [&](int64_t t) -> int64_t { return (b * L_ + t) * H + h; };
+    const uint4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int it = 0; it < RW::IB; ++it) {
+        const int v = tid + NTHR * it;
+        rw.vb[it] = z; rw.vc[it] = z;
+        if (v < T * VB) {
+            const int rho = v / VB, q = v % VB;
+            const int64_t t = t0 + rho / R;
+            if (t < L_) {
+                const size_t off = ((size_t)tok(t) * R + rho % R) * N + (size_t)q * VE;
+                rw.vb[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.B) + off);
+                rw.vc[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.C) + off);
+            }
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < RW::IX; ++it) {
+        const int v = tid + NTHR * it;
+        rw.vx[it] = z; rw.vy[it] = z;
+        if (v < T * VX) {
+            const int rho = v / VX, q = v % VX;
+            const int64_t t = t0 + rho / R;
+            if (t < L_) {
+                const size_t off = ((size_t)tok(t) * R + rho % R) * P + (size_t)q * VE;
+                rw.vx[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.x) + off);
+                rw.vy[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.dy) + off);
+            }
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < RW::IT; ++it) {
+        const int v = tid + NTHR * it;
+        rw.th[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (v < Q * (NPR / 4)) {
+            const int j = v / (NPR / 4), q = v % (NPR / 4);
+            if (t0 + j < L_) rw.th[it] = *reinterpret_cast<const f32x4*>(p.theta + tok(t0 + j) * NPR + 4 * q);
+        }
+    }
+    rw.dtv = 0.f; rw.lmv = 0.f;
+    if (tid <= Q && t0 + tid < L_) { rw.dtv = p.dt[tok(t0 + tid)]; rw.lmv = p.lam[tok(t0 + tid)]; }
+    if constexpr (GRAD) {
+        const op_t* gin = reinterpret_cast<const op_t*>(p.gst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
+        const op_t* dgo = reinterpret_cast<const op_t*>(p.dgst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
+        const float* cst = p.csum + ((size_t)bh * p.nc + c) * (1 + N);
+#pragma unroll
+        for (int it = 0; it < RW::IG; ++it) {
+            const int v = tid + NTHR * it;
+            const int i = v < NPR * G4 ? v / G4 : 0, q = v < NPR * G4 ? v % G4 : 0;
+            rw.sd0[it] = *reinterpret_cast<const V4*>(dgo + (size_t)(2 * i) * P + 4 * q);
+            rw.sd1[it] = *reinterpret_cast<const V4*>(dgo + (size_t)(2 * i + 1) * P + 4 * q);
+            rw.sg0[it] = *reinterpret_cast<const V4*>(gin + (size_t)(2 * i) * P + 4 * q);
+            rw.sg1[it] = *reinterpret_cast<const V4*>(gin + (size_t)(2 * i + 1) * P + 4 * q);
+            rw.scc[it] = cst[1 + 2 * i];
+            rw.sss[it] = cst[2 + 2 * i];
+        }
+    }
+}
+
+// Stage one chunk from its loaded inputs: token scalars, cumulative angles,
+// rotated B and C rows, X and dY rows; for the gradient also the rotated
+// end-state adjoint dGbar and, in float32, the chunk-start terms
+// e^{Lam_tot} <G_in, dGbar> and per pair e^{Lam_tot} sum_p (G_in,0 dGbar_1 -
+// G_in,1 dGbar_0) (the end state's remaining share, sum_k d_k Bbar_k X_k, is
+// added from the same per-token products that enter the tokens' own
+// gradients, so the two cancel exactly where the reverse prefix sums say they
+// must).  The caller has finished with every LDS array of a previous chunk.
+template <class Cf, bool GRAD>
+__device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int bh, int c, const Raw<Cf>& rw,
+                                      Held<Cf>& hd, int tid)
+{
+    using op_t = typename Cf::op_t;
+    using L = Lay<Cf, GRAD>;
+    using RW = Raw<Cf>;
+    constexpr int T = Cf::T, Q = Cf::Q, R = Cf::R, N = Cf::N, P = Cf::P, NPR = Cf::NPR;
+    constexpr int LDN = Cf::LDN, LDP = Cf::LDP, LDH = Cf::LDH, VE = Cf::VE, TS = Cf::TS;
+    constexpr int NTHR = Cf::NTHR, NW = Cf::NW, VB = RW::VB, VX = RW::VX, G4 = RW::G4;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t H = p.H, h = bh % H;
     op_t* sBb = reinterpret_cast<op_t*>(lds + L::oBb);
     op_t* sCb = reinterpret_cast<op_t*>(lds + L::oCb);
     op_t* sX = reinterpret_cast<op_t*>(lds + L::oX);
@@ -232,103 +323,37 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
     float* sPhi = reinterpret_cast<float*>(lds + L::oPhi);
     float* sT = reinterpret_cast<float*>(lds + L::oTok);
     const float A = p.A[h];
-    const op_t* gin = reinterpret_cast<const op_t*>(p.gst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
-    const op_t* dgo = reinterpret_cast<const op_t*>(p.dgst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
-    const float* cst = p.csum + ((size_t)bh * p.nc + c) * (1 + N);
-    constexpr int G4 = P / 4;                        // lanes per pair in the state items
 
-    // ---- S1: every global load; raw rows into LDS ----------------------------
-    constexpr int VB = N / VE, VX = P / VE;          // vectors per B / X row
-    constexpr int IB = (T * VB + NTHR - 1) / NTHR, IX = (T * VX + NTHR - 1) / NTHR;
-    const uint4 z = {0u, 0u, 0u, 0u};
-    uint4 vb[IB], vc[IB], vx[IX], vy[IX];
+    // ---- S1: raw rows into LDS ----------------------------------------------
 #pragma unroll
-    for (int it = 0; it < IB; ++it) {
-        const int v = tid + NTHR * it;
-        vb[it] = z; vc[it] = z;
-        if (v < T * VB) {
-            const int rho = v / VB, q = v % VB;
-            const int64_t t = t0 + rho / R;
-            if (t < L_) {
-                const size_t off = ((size_t)tok(t) * R + rho % R) * N + (size_t)q * VE;
-                vb[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.B) + off);
-                vc[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.C) + off);
-            }
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < IX; ++it) {
-        const int v = tid + NTHR * it;
-        vx[it] = z; vy[it] = z;
-        if (v < T * VX) {
-            const int rho = v / VX, q = v % VX;
-            const int64_t t = t0 + rho / R;
-            if (t < L_) {
-                const size_t off = ((size_t)tok(t) * R + rho % R) * P + (size_t)q * VE;
-                vx[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.x) + off);
-                vy[it] = *reinterpret_cast<const uint4*>(reinterpret_cast<const op_t*>(p.dy) + off);
-            }
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < HD::IT; ++it) {
-        const int v = tid + NTHR * it;
-        hd.th[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (v < Q * (NPR / 4)) {
-            const int j = v / (NPR / 4), q = v % (NPR / 4);
-            if (t0 + j < L_) hd.th[it] = *reinterpret_cast<const f32x4*>(p.theta + tok(t0 + j) * NPR + 4 * q);
-        }
-    }
-    float dtv = 0.f, lmv = 0.f;
-    if (tid <= Q && t0 + tid < L_) { dtv = p.dt[tok(t0 + tid)]; lmv = p.lam[tok(t0 + tid)]; }
-    // state pair items (i, q): rows 2i, 2i+1, columns 4q .. 4q+3
-    f32x4 sd0[HD::IG], sd1[HD::IG], sg0[HD::IG], sg1[HD::IG];
-    float scc[HD::IG], sss[HD::IG];
-    if constexpr (GRAD) {
-#pragma unroll
-        for (int it = 0; it < HD::IG; ++it) {
-            const int v = tid + NTHR * it;
-            sd0[it] = sd1[it] = sg0[it] = sg1[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-            scc[it] = 1.f; sss[it] = 0.f;
-            if (v < NPR * G4) {
-                const int i = v / G4, q = v % G4;
-                sd0[it] = ld4f(dgo + (size_t)(2 * i) * P + 4 * q);
-                sd1[it] = ld4f(dgo + (size_t)(2 * i + 1) * P + 4 * q);
-                sg0[it] = ld4f(gin + (size_t)(2 * i) * P + 4 * q);
-                sg1[it] = ld4f(gin + (size_t)(2 * i + 1) * P + 4 * q);
-                scc[it] = cst[1 + 2 * i];
-                sss[it] = cst[2 + 2 * i];
-            }
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < IB; ++it) {
+    for (int it = 0; it < RW::IB; ++it) {
         const int v = tid + NTHR * it;
         if (v < T * VB) {
             const int rho = v / VB, q = v % VB;
-            *reinterpret_cast<uint4*>(sBb + rho * LDN + q * VE) = vb[it];
-            *reinterpret_cast<uint4*>(sCb + rho * LDN + q * VE) = vc[it];
+            *reinterpret_cast<uint4*>(sBb + rho * LDN + q * VE) = rw.vb[it];
+            *reinterpret_cast<uint4*>(sCb + rho * LDN + q * VE) = rw.vc[it];
         }
     }
 #pragma unroll
-    for (int it = 0; it < IX; ++it) {
+    for (int it = 0; it < RW::IX; ++it) {
         const int v = tid + NTHR * it;
         if (v < T * VX) {
             const int rho = v / VX, q = v % VX;
-            *reinterpret_cast<uint4*>(sX + rho * LDP + q * VE) = vx[it];
-            *reinterpret_cast<uint4*>(sDY + rho * LDP + q * VE) = vy[it];
+            *reinterpret_cast<uint4*>(sX + rho * LDP + q * VE) = rw.vx[it];
+            *reinterpret_cast<uint4*>(sDY + rho * LDP + q * VE) = rw.vy[it];
         }
     }
 #pragma unroll
-    for (int it = 0; it < HD::IT; ++it) {
+    for (int it = 0; it < RW::IT; ++it) {
         const int v = tid + NTHR * it;
+        hd.th[it] = rw.th[it];
         if (v < Q * (NPR / 4)) {
             const int j = v / (NPR / 4), q = v % (NPR / 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sPhi[j * LDH + 4 * q + e] = hd.th[it][e];
+            for (int e = 0; e < 4; ++e) sPhi[j * LDH + 4 * q + e] = rw.th[it][e];
         }
     }
-    if (tid <= Q) { sT[kDt * TS + tid] = dtv; sT[kLm * TS + tid] = lmv; }
+    if (tid <= Q) { sT[kDt * TS + tid] = rw.dtv; sT[kLm * TS + tid] = rw.lmv; }
     __syncthreads();
 
     // ---- S2: token scalars (wave 0) and cumulative angles (all waves) ------
@@ -390,26 +415,29 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
         const float el_tot = sT[kEL * TS + Q - 1];
         float dot = 0.f;
 #pragma unroll
-        for (int it = 0; it < HD::IG; ++it) {
+        for (int it = 0; it < RW::IG; ++it) {
             const int v = tid + NTHR * it;
+            const bool ok = v < NPR * G4;
+            const f32x4 d0 = v4f(rw.sd0[it]), d1 = v4f(rw.sd1[it]);
+            const f32x4 g0 = v4f(rw.sg0[it]), g1 = v4f(rw.sg1[it]);
             float cr = 0.f;
             f32x4 r0, r1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                r0[e] = scc[it] * sd0[it][e] + sss[it] * sd1[it][e];
-                r1[e] = scc[it] * sd1[it][e] - sss[it] * sd0[it][e];
-                cr += sg0[it][e] * r1[e] - sg1[it][e] * r0[e];
-                dot += sg0[it][e] * r0[e] + sg1[it][e] * r1[e];
+                r0[e] = rw.scc[it] * d0[e] + rw.sss[it] * d1[e];
+                r1[e] = rw.scc[it] * d1[e] - rw.sss[it] * d0[e];
+                cr += g0[e] * r1[e] - g1[e] * r0[e];
+                dot += ok ? g0[e] * r0[e] + g1[e] * r1[e] : 0.f;
             }
-            hd.g0[it] = to_v4<op_t>(sg0[it]);
-            hd.g1[it] = to_v4<op_t>(sg1[it]);
-            if (v < NPR * G4) {
+            hd.g0[it] = rw.sg0[it];
+            hd.g1[it] = rw.sg1[it];
+            if (ok) {
                 const int i = v / G4, q = v % G4;
                 *reinterpret_cast<typename V4T<op_t>::type*>(sDG + (2 * i) * LDP + 4 * q) = to_v4<op_t>(r0);
                 *reinterpret_cast<typename V4T<op_t>::type*>(sDG + (2 * i + 1) * LDP + 4 * q) = to_v4<op_t>(r1);
             }
             cr = group_sum<G4>(cr);
-            if (v < NPR * G4 && (v % G4) == 0) sT[kCross * TS + v / G4] = el_tot * cr;
+            if (ok && (v % G4) == 0) sT[kCross * TS + v / G4] = el_tot * cr;
         }
         dot = wave_read_lane(wave_inclusive_sum(dot), 63);
         if (lane == 0) sT[kDot * TS + wv] = el_tot * dot;
@@ -418,13 +446,13 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
 
 // The chunk-start state from the thread's held items into LDS.
 template <class Cf>
-__device__ __forceinline__ void put_gin(typename Cf::op_t* sGi, const Held<Cf>& hd)
+__device__ __forceinline__ void put_gin(typename Cf::op_t* sGi, const Held<Cf>& hd, int tid)
 {
     using HD = Held<Cf>;
     constexpr int G4 = Cf::P / 4, LDP = Cf::LDP;
 #pragma unroll
     for (int it = 0; it < HD::IG; ++it) {
-        const int v = threadIdx.x + Cf::NTHR * it;
+        const int v = tid + Cf::NTHR * it;
         if (v < Cf::NPR * G4) {
             const int i = v / G4, q = v % G4;
             *reinterpret_cast<typename V4T<typename Cf::op_t>::type*>(sGi + (2 * i) * LDP + 4 * q) = hd.g0[it];
@@ -448,8 +476,10 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_local_kernel(const BcParams p)
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int bh = blockIdx.x / p.nc, c = blockIdx.x % p.nc;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
+    Raw<Cf> rw;
     Held<Cf> hd;
-    stage<Cf, false>(p, lds, bh, c, hd);
+    load_raw<Cf, false>(p, bh, c, rw, tid);
+    stage<Cf, false>(p, lds, bh, c, rw, hd, tid);
     op_t* sBb = reinterpret_cast<op_t*>(lds + L::oBb);
     op_t* sCb = reinterpret_cast<op_t*>(lds + L::oCb);
     op_t* sX = reinterpret_cast<op_t*>(lds + L::oX);
@@ -642,14 +672,30 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
     constexpr int TPR = 4 / R;                    // tokens among a lane's 4 rows
     constexpr int DPS = L::DPS;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    const int bh = blockIdx.x / p.nc, c = blockIdx.x % p.nc;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
-    const int rt = wv & 3, hf = wv >> 2;
-    const int64_t L_ = p.L, H = p.H, b = bh / H, h = bh % H;
+    const int64_t L_ = p.L, H = p.H;
+    const int nunits = p.nbh * p.nc;
+    // Persistent: this workgroup takes units blockIdx.x, + gridDim.x, ...,
+    // loading the next one's inputs while it works on the current one.
+    Raw<Cf> rw;
+    if ((int)blockIdx.x < nunits) load_raw<Cf, true>(p, blockIdx.x / p.nc, blockIdx.x % p.nc, rw, threadIdx.x);
+    for (int unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
+    // The lane's indices are made opaque per unit, so that the compiler
+    // recomputes the (cheap) LDS addresses inside the loop instead of keeping
+    // them all live across it.
+    int tid_v = threadIdx.x;
+    asm volatile("" : "+v"(tid_v));
+    const int tid = tid_v, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), rt = wv & 3, hf = wv >> 2;
+    const int bh = unit / p.nc, c = unit % p.nc;
+    const int64_t b = bh / H, h = bh % H;
     const int64_t t0 = (int64_t)c * Q;
     auto tok = [&](int64_t t) -> int64_t { return (b * L_ + t) * H + h; };
     Held<Cf> hd;
-    stage<Cf, true>(p, lds, bh, c, hd);
+    stage<Cf, true>(p, lds, bh, c, rw, hd, tid);
+    if (unit + (int)gridDim.x < nunits) {
+        const int un = unit + gridDim.x;
+        load_raw<Cf, true>(p, un / p.nc, un % p.nc, rw, tid);
+    }
     const op_t* sBb = reinterpret_cast<const op_t*>(lds + L::oBb);
     const op_t* sCb = reinterpret_cast<const op_t*>(lds + L::oCb);
     const op_t* sX = reinterpret_cast<const op_t*>(lds + L::oX);
@@ -776,7 +822,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
         }
     }
     __syncthreads();                              // the S o M tile is free
-    put_gin<Cf>(sGi, hd);
+    put_gin<Cf>(sGi, hd, tid);
 
     // Back-rotation of dBbar / dCbar rows held in accumulators (lane: column
     // n = 16 nt + l16, rows 4 g + i) to dB / dC, and the angle gradient of
@@ -1022,6 +1068,8 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
         if (lane == 0) p.dA_part[(size_t)bh * p.nc + c] = dAs;
         if (lane == Q - 1) p.dw_last[(size_t)bh * p.nc + c] = dw;
     }
+    __syncthreads();                              // LDS is reused by the next unit
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1127,7 +1175,22 @@ hipError_t launch_cfg(const BcParams& p, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (nunits > 0) {
-        hipLaunchKernelGGL(k3, dim3(nunits), dim3(Cf::NTHR), grad_lds<Cf>(), stream, p);
+        // persistent grid: as many workgroups as fit on the device at once
+        static int occ = -1;
+        if (occ < 0) {
+            int o = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, reinterpret_cast<const void*>(k3), Cf::NTHR,
+                                                             grad_lds<Cf>()) != hipSuccess || o < 1)
+                o = 1;
+            occ = o;
+        }
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+            ncu = 256;
+        (void)hipGetLastError();
+        const unsigned ngrid = nunits < (unsigned)(occ * ncu) ? nunits : (unsigned)(occ * ncu);
+        hipLaunchKernelGGL(k3, dim3(ngrid), dim3(Cf::NTHR), grad_lds<Cf>(), stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
