@@ -236,12 +236,14 @@ def bench_prefill_options(w, opts, steps, warmup, torch, m3, synth, seed=1002):
                 gbs=nbytes / (kms * 1e-3) / 1e9)
 
 
-def bench_backward(w, steps, warmup, torch, m3, synth, seed=1003):
+def bench_backward(w, steps, warmup, torch, m3, synth, seed=1003, method="auto"):
+    """One m3_scan_bwd call per step on resident inputs and dy ("auto" picks
+    the chunked method where it is supported)."""
     inp = synth.make_scan_inputs(w, seed, "cuda")
     g = torch.Generator(device="cuda").manual_seed(seed)
     dy = torch.randn(inp["x"].shape, generator=g, device="cuda").to(w.torch_dtype)
     step = m3.ScanBwdCall(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
-                          inp["lam"], dy, state_grads=False)
+                          inp["lam"], dy, state_grads=False, method=method)
     total, kms = time_launches(step, steps, warmup, torch)
     nbytes = bwd_algorithmic_bytes(w)
     return dict(tokens_per_s=w.batch * w.seqlen * steps / total, kernel_ms=kms, bytes=nbytes,
@@ -302,6 +304,22 @@ def progress(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+def backward_lines(steps, torch, m3, synth):
+    """Backward secondary lines: the chunked method (what "auto" picks) and
+    the step-by-step adjoint, on prefill_bf16 and mimo_prefill_bf16."""
+    sec = {}
+    for name in ("prefill_bf16", "mimo_prefill_bf16"):
+        for method, tag, n in (("chunked", "backward", min(steps, 10)), ("step", "backward_step", 3)):
+            progress("timing the %s backward on %s" % (method, name))
+            rb = bench_backward(synth.WORKLOADS[name], n, 1, torch, m3, synth, method=method)
+            sec[tag + ":" + name] = {"tokens_per_s": round(rb["tokens_per_s"], 1),
+                                     "kernel_ms": round(rb["kernel_ms"], 4),
+                                     "hbm_gbs": round(rb["gbs"], 1),
+                                     "hbm_frac": round(rb["gbs"] / HBM_PEAK_GBS, 4)}
+            torch.cuda.empty_cache()
+    return sec
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +337,9 @@ def main(argv=None):
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time the decode workload (for per-kernel counter runs)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time the backward (both methods) on prefill_bf16 and "
+                         "mimo_prefill_bf16, one JSON line each (for per-kernel traces)")
     ap.add_argument("--traffic-summary", nargs=5,
                     metavar=("NAME", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE csv files into "
@@ -341,6 +362,11 @@ def main(argv=None):
     import torch
     import mamba_selective_ssm_amd as m3
     from mamba_selective_ssm_amd import synth
+
+    if args.backward_only:
+        for k, v in backward_lines(args.steps, torch, m3, synth).items():
+            print(json.dumps({"line": k, **v}), flush=True)
+        return 0
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -420,14 +446,7 @@ def main(argv=None):
                          "kernel_ms": round(ro["kernel_ms"], 5),
                          "hbm_gbs": round(ro["gbs"], 1),
                          "hbm_frac": round(ro["gbs"] / HBM_PEAK_GBS, 4)}
-        for name in ("prefill_bf16", "mimo_prefill_bf16"):
-            progress("timing the backward on %s" % name)
-            rb = bench_backward(synth.WORKLOADS[name], 3, 1, torch, m3, synth)
-            sec["backward:" + name] = {"tokens_per_s": round(rb["tokens_per_s"], 1),
-                                       "kernel_ms": round(rb["kernel_ms"], 4),
-                                       "hbm_gbs": round(rb["gbs"], 1),
-                                       "hbm_frac": round(rb["gbs"] / HBM_PEAK_GBS, 4)}
-            torch.cuda.empty_cache()
+        sec.update(backward_lines(args.steps, torch, m3, synth))
         out["secondary"] = sec
         torch.cuda.empty_cache()
 
