@@ -136,9 +136,12 @@ def test_bwd_supported_and_workspace(lib):
     ws = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(seqlen=2048, method=1)))
     # one checkpoint per 32 steps per (b, h), N x P floats, plus scratch
     assert ws >= 6 * 64 * 64 * 64 * 4
-    # chunked: per (b, h) the two local sums of 32 chunks and 33 states and adjoints
+    # chunked: per (b, h) the two local sums of 32 chunks and 33 states and
+    # adjoints, stored in the io type (bf16: 2 bytes)
     wc = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(seqlen=2048, method=2)))
-    assert wc >= 6 * (32 * 2 + 33 * 2) * 64 * 64 * 4
+    assert wc >= 6 * (32 * 2 + 33 * 2) * 64 * 64 * 2
+    wf = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(seqlen=2048, method=2, io_dtype=0)))
+    assert wf >= 6 * (32 * 2 + 33 * 2) * 64 * 64 * 4
     assert lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(seqlen=2048))) == wc
     assert lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(method=5))) == 0
 
