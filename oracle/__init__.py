@@ -15,10 +15,13 @@ inputs, applied before the recurrence, written out below):
     A per token      A of shape [Bt,L,H] (scan) or [Bt,H] (decode) instead of [H]
     ngroups=G        Bm, Cm given per head group, [Bt,L,G,R,N]; head h reads
                      group h // (H/G)
-    phase            "native", "zero", "reverse" or "shuffle" (with ``perm``)
+    phase            "native", "zero", "reverse" or "shuffle" (with ``perm``);
+                     for a decode step also "no_write", "no_read" or
+                     "no_write_read" (``decode_step_rotation_removed``)
     premix           dict of pre-mixer parameters: dt and lam are then the raw
                      projections, and B, C are RMS-normalised with gains and
                      biases
+The accumulated rotation angle (``accumulated_phase``) is a plain sum.
 """
 from __future__ import annotations
 
@@ -267,3 +270,104 @@ def scan_packed(x, Bm, Cm, dt, A, theta, lam, cu_seqlens, h0=None, Bprev=None, x
             h0=take(h0), Bprev=take(Bprev), xprev=take(xprev), threads=threads, **options)
         y[:, sl] = yi
     return y, hs, Bs, xs
+
+
+# ---------------------------------------------------------------------------
+# Accumulated rotation angle and the write / read phase interventions.
+
+def wrap_angle(a):
+    """An angle reduced into [-pi, pi)."""
+    return (np.asarray(a, dtype=np.float64) + np.pi) % (2.0 * np.pi) - np.pi
+
+
+def accumulated_phase(dt, theta, phase_in=None):
+    """The accumulated rotation angle per (batch, head, pair) after a scan:
+    phase_in + sum over the call's tokens of dt_t theta_t[i], reduced mod 2 pi.
+
+    Mamba-3 summary on b-lab.team, section 2 (the RoPE trick, Proposition 3):
+    the product of the per-step rotations R(dt_s theta_s) up to step t is the
+    rotation by the running sum Phi_t of the step angles; the frame that turns
+    with Phi_t carries B and C as R(Phi_t)^T B_t, R(Phi_t)^T C_t.  ``dt`` and
+    ``theta`` are the values the recurrence uses (after any option
+    transforms): dt [Bt, L, H], theta [Bt, L, H, N/2]; phase_in [Bt, H, N/2]
+    (None: zero, the sequence start)."""
+    dt = np.asarray(dt, dtype=np.float64)
+    theta = np.asarray(theta, dtype=np.float64)
+    total = np.einsum("blh,blhi->bhi", dt, theta)
+    if phase_in is not None:
+        total = total + np.asarray(phase_in, dtype=np.float64)
+    return wrap_angle(total)
+
+
+ROTATION_REMOVED = {"no_write": (True, False), "no_read": (False, True),
+                    "no_write_read": (True, True)}
+
+
+def _rotate_rows(M, c, s):
+    """R(angle) applied to the pairs (2i, 2i+1) along axis -2 of M [..., N, P];
+    c, s [..., N/2] are the cosine and sine of the angle per pair."""
+    M = np.asarray(M, dtype=np.float64)
+    c = c[..., None]
+    s = s[..., None]
+    out = np.empty_like(M)
+    out[..., 0::2, :] = c * M[..., 0::2, :] - s * M[..., 1::2, :]
+    out[..., 1::2, :] = s * M[..., 0::2, :] + c * M[..., 1::2, :]
+    return out
+
+
+def decode_step_rotation_removed(x, Bm, Cm, dt, A, theta, lam, h, Bprev, xprev, phase,
+                                 phase_in=None):
+    """One decode step with the rotation removed from writing ("no_write"),
+    from readout ("no_read") or from both ("no_write_read"); returns (y_t, h',
+    Bprev', xprev', phase_out).
+
+    "Understanding Mamba-3 Through Oscillatory Dynamics", section 5.3 (Table 7)
+    removes the rotation from the write or the readout of a pretrained model,
+    and appendix D.4 applies these interventions to prediction steps after a
+    native context.  In the frame that turns with the accumulated angle Phi_t
+    (Mamba-3 summary, section 2, Proposition 3) the native model writes
+    R(Phi_s)^T B_s and reads R(Phi_t)^T C_t; the interventions use B_s, C_t
+    unrotated instead (the reading taken here).  In the state's own frame,
+    h = R(Phi) h_rot, that is, with Phi_t = phase_in + dt_t theta_t (the angle
+    after this step), U = B_t X_t, Uprev = Bprev Xprev (N x P, summed over the
+    ranks) and phi_t = dt_t theta_t:
+        h' = alpha R(phi_t) h + beta Wp + gamma W
+        W  = R(Phi_t) U       (write rotation removed)   else U
+        Wp = R(Phi_t) Uprev   (write rotation removed)   else R(phi_t) Uprev
+        y  = (R(Phi_t) C_t)^T h'  (read rotation removed)  else C_t^T h'
+    with alpha, beta, gamma as in the native step (Mamba-3 summary, section 1).
+    Shapes as ``decode_step`` without options; phase_in [Bt, H, N/2] (None:
+    zero).  phase_out = Phi_t reduced mod 2 pi."""
+    no_write, no_read = ROTATION_REMOVED[phase]
+    x = np.asarray(x, dtype=np.float64)
+    Bt, H, R, P = x.shape
+    Bm = np.asarray(Bm, dtype=np.float64)
+    Cm = np.asarray(Cm, dtype=np.float64)
+    N = Bm.shape[-1]
+    dt = np.asarray(dt, dtype=np.float64)
+    A = np.broadcast_to(np.asarray(A, dtype=np.float64), (Bt, H)) if np.ndim(A) == 1 \
+        else np.asarray(A, dtype=np.float64)
+    theta = np.asarray(theta, dtype=np.float64)
+    lam = np.asarray(lam, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    Bprev = np.asarray(Bprev, dtype=np.float64)
+    xprev = np.asarray(xprev, dtype=np.float64)
+    ph_in = np.zeros((Bt, H, N // 2)) if phase_in is None else np.asarray(phase_in, np.float64)
+    phi = dt[..., None] * theta                          # this step's angle per pair
+    Phi = ph_in + phi                                    # accumulated angle after the step
+    alpha = np.exp(dt * A)[..., None, None]
+    beta = ((1.0 - lam) * dt)[..., None, None] * alpha
+    gamma = (lam * dt)[..., None, None]
+    U = np.einsum("bhrn,bhrp->bhnp", Bm, x)
+    Uprev = np.einsum("bhrn,bhrp->bhnp", Bprev, xprev)
+    cp, sp = np.cos(phi), np.sin(phi)
+    cP, sP = np.cos(Phi), np.sin(Phi)
+    W = _rotate_rows(U, cP, sP) if no_write else U
+    Wp = _rotate_rows(Uprev, cP, sP) if no_write else _rotate_rows(Uprev, cp, sp)
+    h_new = alpha * _rotate_rows(h, cp, sp) + beta * Wp + gamma * W
+    if no_read:
+        # (R(Phi) C)^T h = C^T R(Phi)^T h = C^T R(-Phi) h
+        y = np.einsum("bhrn,bhnp->bhrp", Cm, _rotate_rows(h_new, cP, -sP))
+    else:
+        y = np.einsum("bhrn,bhnp->bhrp", Cm, h_new)
+    return y, h_new, Bm.copy(), x.copy(), wrap_angle(Phi)

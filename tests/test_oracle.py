@@ -673,3 +673,110 @@ def test_backward_matches_finite_differences():
             fd[idx] = (loss(plus) - loss(minus)) / (2 * eps)
         err = np.max(np.abs(fd - g[name])) / max(np.max(np.abs(g[name])), 1e-12)
         assert err < 1e-6, (name, err)
+
+
+# ---------------------------------------------------------------------------
+# Accumulated angle and the write / read phase interventions.
+
+def _draw_tokens(rng, Bt, L, H, R, P, N):
+    return dict(x=rng.standard_normal((Bt, L, H, R, P)), B=rng.standard_normal((Bt, L, H, R, N)),
+                C=rng.standard_normal((Bt, L, H, R, N)), dt=np.log1p(np.exp(rng.standard_normal((Bt, L, H)))),
+                A=-np.exp(rng.uniform(-1, 1, H)), theta=rng.uniform(-np.pi, np.pi, (Bt, L, H, N // 2)),
+                lam=1.0 / (1.0 + np.exp(-rng.standard_normal((Bt, L, H)))))
+
+
+def test_accumulated_phase_is_the_composed_rotation():
+    """R(phase_out) = R(phi_L) ... R(phi_1) R(phase_in), multiplied out as
+    2x2 matrices (commuting plane rotations compose by adding angles)."""
+    rng = np.random.default_rng(40)
+    d = _draw_tokens(rng, 2, 37, 3, 1, 2, 6)
+    ph_in = rng.uniform(-10, 10, (2, 3, 3))
+    out = oracle.accumulated_phase(d["dt"], d["theta"], ph_in)
+    assert np.all(out >= -np.pi) and np.all(out < np.pi)
+    for b in range(2):
+        for h in range(3):
+            for i in range(3):
+                M = np.array([[math.cos(ph_in[b, h, i]), -math.sin(ph_in[b, h, i])],
+                              [math.sin(ph_in[b, h, i]), math.cos(ph_in[b, h, i])]])
+                for t in range(37):
+                    a = d["dt"][b, t, h] * d["theta"][b, t, h, i]
+                    M = np.array([[math.cos(a), -math.sin(a)], [math.sin(a), math.cos(a)]]) @ M
+                assert abs(M[0, 0] - math.cos(out[b, h, i])) < 1e-12
+                assert abs(M[1, 0] - math.sin(out[b, h, i])) < 1e-12
+
+
+@pytest.mark.parametrize("mode", ["no_write", "no_read", "no_write_read"])
+def test_rotation_removal_without_rotation_is_native(mode):
+    """theta = 0: there is no rotation to remove, every intervention is the
+    native step (the C oracle) and the angle does not move."""
+    rng = np.random.default_rng(41)
+    Bt, H, R, P, N = 2, 3, 2, 4, 8
+    x, Bm, Cm = (rng.standard_normal((Bt, H, R, k)) for k in (P, N, N))
+    dt = np.log1p(np.exp(rng.standard_normal((Bt, H))))
+    lam = rng.uniform(0, 1, (Bt, H))
+    A = -np.exp(rng.uniform(-1, 1, H))
+    th = np.zeros((Bt, H, N // 2))
+    h = rng.standard_normal((Bt, H, N, P))
+    Bp, xp = rng.standard_normal((Bt, H, R, N)), rng.standard_normal((Bt, H, R, P))
+    ph = rng.uniform(-3, 3, (Bt, H, N // 2))
+    y0, h0, _, _ = oracle.decode_step(x, Bm, Cm, dt, A, th, lam, h, Bp, xp)
+    y1, h1, _, _, ph1 = oracle.decode_step_rotation_removed(x, Bm, Cm, dt, A, th, lam, h, Bp, xp,
+                                                            mode, ph)
+    # with theta = 0 the removed rotations are R(phase_in), applied to writes
+    # (no_write) or reads (no_read); phase_in = 0 makes them the identity
+    y2, h2, _, _, _ = oracle.decode_step_rotation_removed(x, Bm, Cm, dt, A, th, lam, h, Bp, xp,
+                                                          mode, np.zeros_like(ph))
+    assert np.allclose(y2, y0, rtol=1e-12, atol=1e-12) and np.allclose(h2, h0, rtol=1e-12, atol=1e-12)
+    assert np.allclose(ph1, oracle.wrap_angle(ph), atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["no_write", "no_read", "no_write_read"])
+def test_rotation_removal_matches_rotating_frame_sum(mode):
+    """A native scan of T tokens from the sequence start, then K decode steps
+    with the rotation removed, against an independent O(L^2) sum in the frame
+    that turns with the accumulated angle Phi_t: there the state never
+    rotates, token s is written as R(Phi_s)^T B_s X_s (natively) or B_s X_s
+    (write rotation removed at that step) with weight gamma_s at step s and
+    beta_{s+1} at step s+1, decays by e^{Lambda_t - Lambda_k} after step k,
+    and is read with R(Phi_t)^T C_t or C_t."""
+    no_write, no_read = oracle.ROTATION_REMOVED[mode]
+    rng = np.random.default_rng(42)
+    Bt, H, R, P, N, T, K = 1, 2, 2, 3, 8, 6, 5
+    d = _draw_tokens(rng, Bt, T + K, H, R, P, N)
+    y_nat, h, Bp, xp = oracle.scan(d["x"][:, :T], d["B"][:, :T], d["C"][:, :T], d["dt"][:, :T],
+                                   d["A"], d["theta"][:, :T], d["lam"][:, :T])
+    ph = oracle.accumulated_phase(d["dt"][:, :T], d["theta"][:, :T])
+    got = [y_nat[:, t] for t in range(T)]
+    for t in range(T, T + K):
+        y, h, Bp, xp, ph = oracle.decode_step_rotation_removed(
+            d["x"][:, t], d["B"][:, t], d["C"][:, t], d["dt"][:, t], d["A"], d["theta"][:, t],
+            d["lam"][:, t], h, Bp, xp, mode, ph)
+        got.append(y)
+    # the rotating-frame sum
+    Phi = np.cumsum(d["dt"][..., None] * d["theta"], axis=1)      # [Bt, L, H, N/2]
+    Lam = np.cumsum(d["dt"] * d["A"][None, None, :], axis=1)       # [Bt, L, H]
+    beta = (1 - d["lam"]) * d["dt"] * np.exp(d["dt"] * d["A"][None, None, :])
+    gamma = d["lam"] * d["dt"]
+
+    def rotT(v, ang):                                               # R(ang)^T on pairs of v [..., N]
+        c, s = np.cos(ang), np.sin(ang)
+        out = np.empty_like(v)
+        out[..., 0::2] = c * v[..., 0::2] + s * v[..., 1::2]
+        out[..., 1::2] = -s * v[..., 0::2] + c * v[..., 1::2]
+        return out
+
+    for b in range(Bt):
+        for hh in range(H):
+            for t in range(T + K):
+                hr = np.zeros((N, P))
+                for s in range(t + 1):
+                    for k, wgt in ((s, gamma[b, s, hh]), (s + 1, beta[b, s + 1, hh] if s + 1 <= t else 0.0)):
+                        if k > t or wgt == 0.0:
+                            continue
+                        Bs = d["B"][b, s, hh]                       # [R, N]
+                        W = Bs if (no_write and k >= T) else rotT(Bs, Phi[b, s, hh])
+                        hr += math.exp(Lam[b, t, hh] - Lam[b, k, hh]) * wgt * W.T @ d["x"][b, s, hh]
+                Ct = d["C"][b, t, hh]
+                Cr = Ct if (no_read and t >= T) else rotT(Ct, Phi[b, t, hh])
+                ref = Cr @ hr                                       # [R, P]
+                assert np.allclose(got[t][b, hh], ref, rtol=1e-10, atol=1e-10), (mode, b, hh, t)
