@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define M3_ABI_VERSION 3
+#define M3_ABI_VERSION 4
 
 typedef enum {
     M3_F32 = 0,
@@ -101,7 +101,19 @@ typedef enum {
     M3_PHASE_NATIVE = 0,   /* theta as given */
     M3_PHASE_ZERO = 1,     /* no rotation; theta is not read and may be NULL */
     M3_PHASE_REVERSE = 2,  /* theta negated */
-    M3_PHASE_SHUFFLE = 3   /* pair i uses theta[..., phase_perm[i]] */
+    M3_PHASE_SHUFFLE = 3,  /* pair i uses theta[..., phase_perm[i]] */
+    /* m3_decode_step only: the rotation removed from writing, from readout, or
+     * from both, for prediction steps after a native context ("Understanding
+     * Mamba-3 Through Oscillatory Dynamics", section 5.3 and appendix D.4).
+     * In the frame that turns with the accumulated angle Phi (phase_in plus
+     * this step's dt theta), the native model writes R(Phi)^T B and reads
+     * R(Phi)^T C; these modes use B, C unrotated there.  In the state's own
+     * frame: the write terms beta B_prev x_prev + gamma B x are rotated by
+     * R(Phi) instead of (R(dt theta) on the first, none on the second), and
+     * the readout uses R(Phi) C.  theta is used as given. */
+    M3_PHASE_NO_WRITE = 4,
+    M3_PHASE_NO_READ = 5,
+    M3_PHASE_NO_WRITE_READ = 6
 } m3_phase_mode;
 
 typedef enum {
@@ -143,6 +155,16 @@ typedef enum {
  *                launch).  Offsets are clamped into [0, seqlen] and lengths
  *                to max_seqlen on the device: bad entries give wrong
  *                results, never accesses outside the arrays.
+ *   phase_in     float32 [batch, nheads, dstate/2] or NULL (zero): the
+ *                accumulated rotation angle Phi per (batch row or sequence,
+ *                head, pair) before the call's first token -- the sum of
+ *                dt theta (after the phase transform and the pre-mixer) over
+ *                every earlier token of the sequence, in radians
+ *   phase_out    float32 [batch, nheads, dstate/2] or NULL (not written):
+ *                receives Phi after the call's last token, reduced into
+ *                [-pi, pi).  May be the same array as phase_in (updated in
+ *                place); no other overlap.  A scan that writes it needs the
+ *                workspace m3_scan_workspace_bytes reports for it.
  */
 typedef struct {
     int64_t ngroups;
@@ -156,6 +178,8 @@ typedef struct {
     const float *dt_bias;
     const int32_t *cu_seqlens;
     int64_t max_seqlen;
+    const float *phase_in;
+    float *phase_out;
 } m3_options;
 
 /*

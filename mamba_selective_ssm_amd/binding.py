@@ -37,7 +37,9 @@ M3_F32, M3_BF16 = 0, 1
 _STATUS = {0: "M3_OK", -1: "M3_ERR_NULL", -2: "M3_ERR_SHAPE", -3: "M3_ERR_UNSUPPORTED",
            -4: "M3_ERR_DTYPE", -5: "M3_ERR_ALIGN", -6: "M3_ERR_WORKSPACE", -7: "M3_ERR_ALIAS",
            -8: "M3_ERR_HIP", -9: "M3_ERR_OPTION"}
-PHASE_MODES = {"native": 0, "zero": 1, "reverse": 2, "shuffle": 3}
+PHASE_MODES = {"native": 0, "zero": 1, "reverse": 2, "shuffle": 3,
+               # decode steps only: the rotation removed from writing / readout
+               "no_write": 4, "no_read": 5, "no_write_read": 6}
 
 _vp = ctypes.c_void_p
 
@@ -47,7 +49,8 @@ class Options(ctypes.Structure):
                 ("phase_mode", ctypes.c_int32), ("phase_perm", _vp),
                 ("premix", ctypes.c_int32), ("norm_eps", ctypes.c_float),
                 ("B_norm_w", _vp), ("C_norm_w", _vp), ("B_bias", _vp), ("C_bias", _vp),
-                ("dt_bias", _vp), ("cu_seqlens", _vp), ("max_seqlen", ctypes.c_int64)]
+                ("dt_bias", _vp), ("cu_seqlens", _vp), ("max_seqlen", ctypes.c_int64),
+                ("phase_in", _vp), ("phase_out", _vp)]
 
 
 class Premix(NamedTuple):
@@ -204,11 +207,19 @@ def _check(t: torch.Tensor, name: str, shape, dtype):
         raise ValueError("%s must be a device tensor" % name)
 
 
-def _options(H, N, R, A_per_token, ngroups, phase, perm, premix, device):
-    """m3_options from the keyword arguments (plus the tensors to keep alive)."""
+def _options(H, N, R, A_per_token, ngroups, phase, perm, premix, device, rows=None,
+             phase_in=None, phase_out=None):
+    """m3_options from the keyword arguments (plus the tensors to keep alive).
+    phase_in / phase_out: accumulated rotation angle [rows, H, N/2] float32
+    (may be the same tensor: updated in place)."""
     mode = PHASE_MODES[phase] if isinstance(phase, str) else int(phase)
     o = Options(ngroups=int(ngroups or 0), A_per_token=int(bool(A_per_token)), phase_mode=mode)
     keep = []
+    for name, t in (("phase_in", phase_in), ("phase_out", phase_out)):
+        if t is not None:
+            _check(t, name, (rows, H, N // 2), torch.float32)
+            setattr(o, name, t.data_ptr())
+            keep.append(t)
     if mode == PHASE_MODES["shuffle"]:
         if perm is None:
             raise ValueError("phase='shuffle' needs perm")
@@ -235,7 +246,7 @@ def _stream_handle(stream) -> int:
 
 def _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, return_state,
                   y, state_out, workspace, ngroups=0, phase="native", perm=None, premix=None,
-                  cu_seqlens=None, max_seqlen=None):
+                  cu_seqlens=None, max_seqlen=None, phase_in=None, phase_out=None):
     lib = load_library()
     Bx, L, H, R, P = x.shape
     N = B.shape[-1]
@@ -257,7 +268,8 @@ def _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, r
         _check(theta, "theta", (Bx, L, H, N // 2), torch.float32)
     a_tok = A.dim() == 3
     _check(A, "A", (Bx, L, H) if a_tok else (H,), torch.float32)
-    opt, keep = _options(H, N, R, a_tok, ngroups, phase, perm, premix, x.device)
+    opt, keep = _options(H, N, R, a_tok, ngroups, phase, perm, premix, x.device, Bt,
+                         phase_in, phase_out)
     if cu_seqlens is not None:
         opt.cu_seqlens = cu_seqlens.data_ptr()
         opt.max_seqlen = int(L if max_seqlen is None else max_seqlen)
@@ -301,12 +313,16 @@ def m3_scan_fwd(x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
                 state_out: Optional[State] = None, workspace: Optional[torch.Tensor] = None,
                 ngroups: int = 0, phase="native", perm: Optional[torch.Tensor] = None,
                 premix: Optional[Premix] = None, cu_seqlens: Optional[torch.Tensor] = None,
-                max_seqlen: Optional[int] = None, stream=None):
+                max_seqlen: Optional[int] = None, phase_in: Optional[torch.Tensor] = None,
+                phase_out: Optional[torch.Tensor] = None, stream=None):
     """Chunked prefill.  Returns (y, State after the last token or None); with
-    packed sequences the State holds one record per sequence."""
+    packed sequences the State holds one record per sequence.  ``phase_out``
+    (float32 [batch or sequences, H, N/2]) receives the accumulated rotation
+    angle after the last token, starting from ``phase_in`` (None: zero)."""
     a, y, state_out, _ = _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split,
                                        segments, return_state, y, state_out, workspace,
-                                       ngroups, phase, perm, premix, cu_seqlens, max_seqlen)
+                                       ngroups, phase, perm, premix, cu_seqlens, max_seqlen,
+                                       phase_in, phase_out)
     st = load_library().m3_scan_fwd(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_fwd")
@@ -323,11 +339,13 @@ class ScanCall:
                  y: Optional[torch.Tensor] = None, state_out: Optional[State] = None,
                  workspace: Optional[torch.Tensor] = None, ngroups: int = 0, phase="native",
                  perm: Optional[torch.Tensor] = None, premix: Optional[Premix] = None,
-                 cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None):
+                 cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+                 phase_in: Optional[torch.Tensor] = None, phase_out: Optional[torch.Tensor] = None):
         self._keep = (x, B, C, dt, A, theta, lam, state)
         self.args, self.y, self.state_out, self.workspace = _prepare_scan(
             x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, return_state, y,
-            state_out, workspace, ngroups, phase, perm, premix, cu_seqlens, max_seqlen)
+            state_out, workspace, ngroups, phase, perm, premix, cu_seqlens, max_seqlen,
+            phase_in, phase_out)
         self._ref = ctypes.byref(self.args)
         self._fn = load_library().m3_scan_fwd
 
@@ -351,7 +369,7 @@ def m3_scan_workspace_bytes(x, B, *, chunk=0, p_split=0, segments=0, cu_seqlens=
 
 
 def _prepare_decode(x, B, C, dt, A, theta, lam, state, y, ngroups=0, phase="native", perm=None,
-                    premix=None):
+                    premix=None, phase_in=None, phase_out=None):
     Bt, H, R, P = x.shape
     N = B.shape[-1]
     G = int(ngroups) if ngroups else H
@@ -365,7 +383,8 @@ def _prepare_decode(x, B, C, dt, A, theta, lam, state, y, ngroups=0, phase="nati
         _check(theta, "theta", (Bt, H, N // 2), torch.float32)
     a_tok = A.dim() == 2
     _check(A, "A", (Bt, H) if a_tok else (H,), torch.float32)
-    opt, keep = _options(H, N, R, a_tok, ngroups, phase, perm, premix, x.device)
+    opt, keep = _options(H, N, R, a_tok, ngroups, phase, perm, premix, x.device, Bt,
+                         phase_in, phase_out)
     _check(state.h, "state.h", (Bt, H, N, P), torch.float32)
     _check(state.B_prev, "state.B_prev", (Bt, H, R, N), x.dtype)
     _check(state.x_prev, "state.x_prev", (Bt, H, R, P), x.dtype)
@@ -383,9 +402,15 @@ def _prepare_decode(x, B, C, dt, A, theta, lam, state, y, ngroups=0, phase="nati
 def m3_decode_step(x, B, C, dt, A, theta, lam, state: State, *,
                    y: Optional[torch.Tensor] = None, ngroups: int = 0, phase="native",
                    perm: Optional[torch.Tensor] = None, premix: Optional[Premix] = None,
+                   phase_in: Optional[torch.Tensor] = None, phase_out: Optional[torch.Tensor] = None,
                    stream=None):
-    """One token for every (batch, head); ``state`` is updated in place.  Returns y_t."""
-    a, y = _prepare_decode(x, B, C, dt, A, theta, lam, state, y, ngroups, phase, perm, premix)
+    """One token for every (batch, head); ``state`` is updated in place.  Returns y_t.
+    ``phase_in`` / ``phase_out``: the accumulated rotation angle before / after
+    this step (float32 [batch, H, N/2]; may be one tensor, updated in place);
+    the phases "no_write", "no_read", "no_write_read" rotate the write / read
+    terms by it."""
+    a, y = _prepare_decode(x, B, C, dt, A, theta, lam, state, y, ngroups, phase, perm, premix,
+                           phase_in, phase_out)
     st = load_library().m3_decode_step(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_decode_step")
@@ -398,10 +423,11 @@ class DecodeCall:
 
     def __init__(self, x, B, C, dt, A, theta, lam, state: State, *,
                  y: Optional[torch.Tensor] = None, ngroups: int = 0, phase="native",
-                 perm: Optional[torch.Tensor] = None, premix: Optional[Premix] = None):
+                 perm: Optional[torch.Tensor] = None, premix: Optional[Premix] = None,
+                 phase_in: Optional[torch.Tensor] = None, phase_out: Optional[torch.Tensor] = None):
         self._keep = (x, B, C, dt, A, theta, lam, state)
         self.args, self.y = _prepare_decode(x, B, C, dt, A, theta, lam, state, y, ngroups, phase,
-                                            perm, premix)
+                                            perm, premix, phase_in, phase_out)
         self._ref = ctypes.byref(self.args)
         self._fn = load_library().m3_decode_step
 

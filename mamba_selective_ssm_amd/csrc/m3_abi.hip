@@ -86,12 +86,14 @@ m3_status check_options(const m3_options& o, int64_t H, int64_t N, int64_t R, in
         return M3_ERR_OPTION;
     if (o.ngroups < 0 || (o.ngroups > 0 && H > 0 && H % o.ngroups != 0)) return M3_ERR_OPTION;
     if (o.A_per_token != 0 && o.A_per_token != 1) return M3_ERR_OPTION;
-    if (o.phase_mode < M3_PHASE_NATIVE || o.phase_mode > M3_PHASE_SHUFFLE) return M3_ERR_OPTION;
+    if (o.phase_mode < M3_PHASE_NATIVE || o.phase_mode > M3_PHASE_NO_WRITE_READ) return M3_ERR_OPTION;
+    // rotation removed from writing / readout: decode steps only
+    if (o.phase_mode >= M3_PHASE_NO_WRITE && ntok >= 0) return M3_ERR_OPTION;
     if (o.premix != 0 && o.premix != 1) return M3_ERR_OPTION;
     if (o.premix && !(o.norm_eps >= 0.f && o.norm_eps < 3.0e38f)) return M3_ERR_OPTION;
     if (o.phase_mode == M3_PHASE_SHUFFLE && o.phase_perm == nullptr) return M3_ERR_NULL;
     const void* ptrs[] = {o.phase_perm, o.B_norm_w, o.C_norm_w, o.B_bias, o.C_bias, o.dt_bias,
-                          o.cu_seqlens};
+                          o.cu_seqlens, o.phase_in, o.phase_out};
     for (const void* q : ptrs)
         if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
     (void)N; (void)R;
@@ -108,6 +110,8 @@ m3_status check_options(const m3_options& o, int64_t H, int64_t N, int64_t R, in
     k->dtb = o.premix ? o.dt_bias : nullptr;
     k->cu = o.cu_seqlens;
     k->max_len = o.max_seqlen;
+    k->phase_in = o.phase_in;
+    k->phase_out = o.phase_out;
     return M3_OK;
 }
 
@@ -121,11 +125,14 @@ void option_ranges(const m3_options& o, int64_t Bt, int64_t H, int64_t N, int64_
     out[3] = range_of(o.premix ? o.B_bias : nullptr, H * R * N * 4);
     out[4] = range_of(o.premix ? o.C_bias : nullptr, H * R * N * 4);
     out[5] = range_of(o.premix ? o.dt_bias : nullptr, H * 4);
+    out[7] = range_of(o.phase_in != o.phase_out ? o.phase_in : nullptr, Bt * H * (N / 2) * 4);
 }
 
 struct ScanPlan {
     const m3::ScanVariant* v;
     int p_split, nseg, seg_chunks;
+    int64_t phase_blocks;      // 64-token blocks per sequence (accumulated angle)
+    size_t phase_off;          // workspace offset of the angle's partial sums
     size_t ws;
 };
 
@@ -173,6 +180,15 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
     out->nseg = (int)nseg;
     out->seg_chunks = (int)seg_chunks;
     out->ws = v->ws_bytes(nbh, P, (int)nseg);
+    out->phase_blocks = 0;
+    out->phase_off = 0;
+    if (a->opt.phase_out != nullptr) {
+        // float64 partial sums of the accumulated angle, per (row, head, block, pair)
+        out->phase_blocks = (Lrun + m3::kPhaseBlock - 1) / m3::kPhaseBlock;
+        if (out->phase_blocks > 65535) return M3_ERR_UNSUPPORTED;
+        out->phase_off = (out->ws + 255) / 256 * 256;
+        out->ws = out->phase_off + (size_t)nbh * out->phase_blocks * (N / 2) * 8;
+    }
     return M3_OK;
 }
 
@@ -449,7 +465,7 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     const int e = io_size(a->io_dtype);
     const int64_t tok = (packed ? 1 : Bt) * L * H;             // token arrays: rows x heads
     const int64_t tokg = (packed ? 1 : Bt) * L * op.groups;
-    Range in[17] = {
+    Range in[18] = {
         range_of(a->x, tok * R * P * e),         range_of(a->B, tokg * R * N * e),
         range_of(a->C, tokg * R * N * e),        range_of(a->dt, tok * 4),
         range_of(a->A, (a->opt.A_per_token ? tok : H) * 4),
@@ -462,6 +478,7 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
         range_of(a->y, tok * R * P * e),         range_of(a->h_out, nbh * N * P * 4),
         range_of(a->B_prev_out, nbh * R * N * e), range_of(a->x_prev_out, nbh * R * P * e),
         range_of(a->workspace, (int64_t)plan.ws),
+        range_of(a->opt.phase_out, nbh * (N / 2) * 4),
     };
     const int nout = sizeof(out) / sizeof(out[0]);
     for (const Range& o : out) {
@@ -490,7 +507,17 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     p.nbh = (int)nbh;
     p.nseg = plan.nseg;
     p.seg_chunks = plan.seg_chunks;
-    return hip_status(plan.v->fn(p, static_cast<hipStream_t>(stream)));
+    const hipError_t e1 = plan.v->fn(p, static_cast<hipStream_t>(stream));
+    if (e1 != hipSuccess || a->opt.phase_out == nullptr) return hip_status(e1);
+    m3::PhaseParams q;
+    memset(&q, 0, sizeof(q));
+    q.dt = a->dt;
+    q.theta = static_cast<const float*>(theta);
+    q.opt = op;
+    q.rows = Bt; q.L = L; q.H = H; q.NPR = (int)(N / 2);
+    q.nblk = plan.phase_blocks;
+    q.part = reinterpret_cast<double*>(static_cast<char*>(a->workspace) + plan.phase_off);
+    return hip_status(m3::launch_phase_accumulate(q, static_cast<hipStream_t>(stream)));
 }
 
 m3_status m3_decode_step(const m3_decode_args* a, void* stream)
@@ -515,7 +542,7 @@ m3_status m3_decode_step(const m3_decode_args* a, void* stream)
         if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
     const int e = io_size(a->io_dtype);
     const int64_t nbg = Bt * op.groups;
-    Range in[14] = {
+    Range in[15] = {
         range_of(a->x, nbh * R * P * e), range_of(a->B, nbg * R * N * e),
         range_of(a->C, nbg * R * N * e), range_of(a->dt, nbh * 4),
         range_of(a->A, (a->opt.A_per_token ? nbh : H) * 4),
@@ -527,13 +554,15 @@ m3_status m3_decode_step(const m3_decode_args* a, void* stream)
         range_of(a->x_prev, nbh * R * P * e),
     };
     const Range y = range_of(a->y, nbh * R * P * e);
+    const Range ph = range_of(a->opt.phase_out, nbh * (N / 2) * 4);
     for (const Range& r : rec) {
-        if (overlaps(y, r)) return M3_ERR_ALIAS;
+        if (overlaps(y, r) || overlaps(ph, r)) return M3_ERR_ALIAS;
         for (const Range& i : in)
             if (overlaps(r, i)) return M3_ERR_ALIAS;
     }
     for (const Range& i : in)
-        if (overlaps(y, i)) return M3_ERR_ALIAS;
+        if (overlaps(y, i) || overlaps(ph, i)) return M3_ERR_ALIAS;
+    if (overlaps(y, ph)) return M3_ERR_ALIAS;
     for (int i = 0; i < 3; ++i)
         for (int j = i + 1; j < 3; ++j)
             if (overlaps(rec[i], rec[j])) return M3_ERR_ALIAS;

@@ -21,7 +21,10 @@
 //   * the rank-R readout of each column is reduced across the row groups
 //     with lane shuffles.
 // Options: per-token decay A_t, B/C shared by head groups, phase
-// interventions (zero / reverse / shuffled increments) and the pre-mixer
+// interventions (zero / reverse / shuffled increments; the rotation removed
+// from writing or readout, with the accumulated angle carried in and out:
+// "Understanding Mamba-3 Through Oscillatory Dynamics", section 5.3 and
+// appendix D.4) and the pre-mixer
 // (softplus / sigmoid of the raw dt / lam, RMSNorm with gains and biases on
 // B and C, applied to the wave's LDS copy; the record keeps the normalised B).
 #include "m3_device.hpp"
@@ -105,10 +108,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
     const int64_t G = p.opt.groups;
     const int64_t bg = (bh / p.H) * G + h / (p.H / G);   // B/C row of this head's group
 
-    float* sBp = dsm + (int64_t)wv * (3 * R * N + N);   // this wave's slice: [N][R]
+    float* sBp = dsm + (int64_t)wv * (3 * R * N + 2 * N);   // this wave's slice: [N][R]
     float* sB = sBp + R * N;                            // [N][R]
     float* sC = sB + R * N;                             // [N][R]
-    float* sCS = sC + R * N;                            // [NPR][2] cos, sin
+    float* sCS = sC + R * N;                            // [NPR][2] cos, sin of dt theta
+    float* sCW = sCS + N;                               // [NPR][2] cos, sin of the accumulated angle
+    // rotation removed from writing / readout (wave-uniform)
+    const bool no_write = p.opt.phase == 4 || p.opt.phase == 6;
+    const bool no_read = p.opt.phase == 5 || p.opt.phase == 6;
 
     const IO* x = reinterpret_cast<const IO*>(p.x) + bh * R * P;
     const IO* Bt = reinterpret_cast<const IO*>(p.B) + bg * R * N;
@@ -166,16 +173,31 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
     }
     for (int i = lane; i < NPR; i += 64) {
         float th = 0.f;                                        // zero: theta not read
-        if (p.opt.phase == 0) th = p.theta[bh * NPR + i];
+        if (p.opt.phase == 0 || p.opt.phase >= 4) th = p.theta[bh * NPR + i];
         else if (p.opt.phase == 2) th = -p.theta[bh * NPR + i];
         else if (p.opt.phase == 3) {
             int src = p.opt.perm[i];
             src = src < 0 ? 0 : (src >= NPR ? NPR - 1 : src);
             th = p.theta[bh * NPR + src];
         }
+        const float phi = d * th;
         float sn, cs;
-        sincosf(d * th, &sn, &cs);
+        sincosf(phi, &sn, &cs);
         *reinterpret_cast<float2*>(sCS + 2 * i) = make_float2(cs, sn);
+        // accumulated angle after this step (read before it is overwritten
+        // when phase_out is phase_in: same lane, same element)
+        const float Phi = (p.opt.phase_in != nullptr ? p.opt.phase_in[bh * NPR + i] : 0.f) + phi;
+        if (no_write || no_read) {
+            float sw, cw;
+            sincosf(Phi, &sw, &cw);
+            *reinterpret_cast<float2*>(sCW + 2 * i) = make_float2(cw, sw);
+        }
+        if (p.opt.phase_out != nullptr) {
+            const float twopi = 6.28318530717958648f, pi = 3.14159265358979324f;
+            float w = Phi - twopi * floorf((Phi + pi) / twopi);
+            if (w >= pi) w -= twopi;
+            p.opt.phase_out[bh * NPR + i] = w;
+        }
     }
     float xv[R][4], xpv[R][4];
 #pragma unroll
@@ -235,6 +257,21 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (no_read) {
+        // readout through R(Phi) C: rotate the wave's copy of C per pair
+        for (int i = lane; i < NPR; i += 64) {
+            const float2 cw = *reinterpret_cast<const float2*>(sCW + 2 * i);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float c0 = sC[(2 * i) * R + r], c1 = sC[(2 * i + 1) * R + r];
+                sC[(2 * i) * R + r] = cw.x * c0 - cw.y * c1;
+                sC[(2 * i + 1) * R + r] = cw.y * c0 + cw.x * c1;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 
     float yacc[R][4];
 #pragma unroll
@@ -264,11 +301,21 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
                         u0 += b0.v[r] * xv[r][q];
                         u1 += b1.v[r] * xv[r][q];
                     }
-                    // alpha R h + beta R U_prev = R (alpha h + beta U_prev)
-                    const float a0 = alpha * hv[k][0][q] + beta * up0;
-                    const float a1 = alpha * hv[k][1][q] + beta * up1;
-                    const float n0 = csn.x * a0 - csn.y * a1 + gamma * u0;
-                    const float n1 = csn.y * a0 + csn.x * a1 + gamma * u1;
+                    float n0, n1;
+                    if (!no_write) {
+                        // alpha R h + beta R U_prev = R (alpha h + beta U_prev)
+                        const float a0 = alpha * hv[k][0][q] + beta * up0;
+                        const float a1 = alpha * hv[k][1][q] + beta * up1;
+                        n0 = csn.x * a0 - csn.y * a1 + gamma * u0;
+                        n1 = csn.y * a0 + csn.x * a1 + gamma * u1;
+                    } else {
+                        // alpha R(dt theta) h + R(Phi) (beta U_prev + gamma U)
+                        const float2 cw = *reinterpret_cast<const float2*>(sCW + 2 * i);
+                        const float a0 = alpha * hv[k][0][q], a1 = alpha * hv[k][1][q];
+                        const float w0 = beta * up0 + gamma * u0, w1 = beta * up1 + gamma * u1;
+                        n0 = csn.x * a0 - csn.y * a1 + cw.x * w0 - cw.y * w1;
+                        n1 = csn.y * a0 + csn.x * a1 + cw.y * w0 + cw.x * w1;
+                    }
                     n0v[q] = n0;
                     n1v[q] = n1;
 #pragma unroll
@@ -307,14 +354,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
     }
 }
 
-// LDS slice of one wavefront: B_prev, B, C as [N][R] and the pair rotations.
-size_t decode_wave_lds(int N, int R) { return sizeof(float) * (size_t)(3 * R * N + N); }
+// LDS slice of one wavefront: B_prev, B, C as [N][R] and the pair rotations
+// (of this step's angle and of the accumulated angle).
+size_t decode_wave_lds(int N, int R) { return sizeof(float) * (size_t)(3 * R * N + 2 * N); }
 
 template <typename IO, int R, bool PM>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream)
 {
     // Up to kDecWaves wavefronts per workgroup, as many as fit in LDS (the
-    // largest supported shape, N = 1024 and R = 4, takes 52 KiB per wave).
+    // largest supported shape, N = 1024 and R = 4, takes 56 KiB per wave).
     const size_t per_wave = decode_wave_lds(p.N, R);
     int waves = (int)((160 * 1024) / per_wave);
     if (waves > kDecWaves) waves = kDecWaves;

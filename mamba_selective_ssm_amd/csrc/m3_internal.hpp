@@ -22,6 +22,8 @@ struct OptParams {
     const float *dtb;      // [H] or NULL (zeros)
     const int* cu;         // [batch + 1] packed-sequence offsets, or NULL (dense batch)
     int64_t max_len;       // longest packed sequence
+    const float* phase_in; // [batch, H, N/2] accumulated angle before the call, or NULL (zero)
+    float* phase_out;      // [batch, H, N/2] accumulated angle after the call, or NULL
 };
 
 struct DecodeParams {
@@ -90,6 +92,20 @@ struct BcParams {
 bool bwd_chunked_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
 int bwd_chunk_tokens(int64_t R);
 hipError_t launch_bwd_chunked(const BcParams& p, int io_dtype, hipStream_t stream);
+
+// Accumulated rotation angle of a scan: per (row, head, 64-token block) the
+// float64 partial sums of dt theta per pair into `part`, then per (row, head,
+// pair) their sum in block order plus phase_in, reduced into [-pi, pi).
+struct PhaseParams {
+    const float *dt, *theta;
+    OptParams opt;
+    int64_t rows, L, H;    // batch rows (sequences when packed), token rows per sequence bound
+    int NPR;
+    int64_t nblk;          // 64-token blocks per sequence
+    double* part;          // [rows * H][nblk][NPR]
+};
+constexpr int kPhaseBlock = 64;
+hipError_t launch_phase_accumulate(const PhaseParams& p, hipStream_t stream);
 
 bool decode_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
 hipError_t launch_decode(const DecodeParams& p, int io_dtype, hipStream_t stream);

@@ -147,7 +147,7 @@ def test_bwd_supported_and_workspace(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.m3_abi_version() == 3
+    assert lib.m3_abi_version() == 4
     for code in range(-9, 1):
         s = lib.m3_status_string(code)
         assert s and s != b"unknown status"
@@ -205,6 +205,12 @@ def run_scan(lib, a):
     (dict(cu_seqlens=FAKE + (42 << 32), max_seqlen=-1), -9),
     (dict(cu_seqlens=FAKE + (42 << 32) + 4, max_seqlen=10), -5),
     (dict(cu_seqlens=FAKE + (7 << 32), max_seqlen=10), -7),   # y overlaps the offsets
+    # accumulated angle; rotation removed from writing / readout (decode only)
+    (dict(phase_mode=5), -9), (dict(phase_mode=6), -9), (dict(phase_mode=7), -9),
+    (dict(phase_in=FAKE + (43 << 32) + 4), -5),
+    (dict(phase_out=FAKE + (43 << 32) + 8), -5),
+    (dict(phase_out=FAKE + (7 << 32)), -7),                  # phase_out overlaps y
+    (dict(phase_out=FAKE + (43 << 32)), -6),                 # needs a workspace
 ])
 def test_scan_validation_codes(lib, kw, code):
     assert run_scan(lib, scan_args(**kw)) == code
@@ -247,6 +253,13 @@ def decode_args(**kw):
     (dict(premix=1, dt_bias=FAKE + (10 << 32)), -7),                # y overlaps the dt bias
     (dict(premix=1, B_bias=FAKE + (7 << 32)), -7),                  # state overlaps the B bias
     (dict(cu_seqlens=FAKE + (20 << 32), max_seqlen=1), -9),         # scans only
+    (dict(phase_mode=7), -9), (dict(phase_mode=-2), -9),
+    (dict(theta=None, phase_mode=4, h=FAKE + (7 << 32) + 4), -1),   # removal modes read theta
+    (dict(phase_in=FAKE + (12 << 32) + 4), -5),
+    (dict(phase_out=FAKE + (7 << 32)), -7),                         # phase_out overlaps the state
+    (dict(phase_out=FAKE + (10 << 32) + 16), -7),                   # ... or y
+    (dict(phase_out=FAKE + (5 << 32)), -7),                         # ... or theta
+    (dict(phase_in=FAKE + (7 << 32)), -7),                          # state overlaps phase_in
 ])
 def test_decode_validation_codes(lib, kw, code):
     assert lib.m3_decode_step(ctypes.byref(decode_args(**kw)), None) == code
@@ -267,3 +280,10 @@ def test_supported_sets(lib):
     ws = lib.m3_scan_workspace_bytes(ctypes.byref(scan_args(seqlen=1000, segments=4)))
     assert ws >= 2 * 3 * 3 * 64 * 32 * 4
     assert lib.m3_scan_workspace_bytes(ctypes.byref(scan_args(dstate=63))) == 0
+
+
+def test_scan_workspace_for_the_accumulated_angle(lib):
+    """phase_out needs float64 partial sums per (row, head, 64-token block, pair)."""
+    base = lib.m3_scan_workspace_bytes(ctypes.byref(scan_args(seqlen=1000)))
+    ws = lib.m3_scan_workspace_bytes(ctypes.byref(scan_args(seqlen=1000, phase_out=FAKE + (43 << 32))))
+    assert ws >= base + 2 * 3 * 16 * 32 * 8
