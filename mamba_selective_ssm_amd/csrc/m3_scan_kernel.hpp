@@ -111,6 +111,20 @@ struct ScanCfg {
     static constexpr int LQ = 64 / QPWV;
     static constexpr int TPL = (Q + LQ - 1) / LQ;
     static constexpr int QPL = (Q + 63) / 64;        // tokens per lane in A0
+    // Row-coalesced prep (CL): prep wave w owns the operand rows
+    // [RPW w, RPW (w+1)) of a chunk, and lane l takes pair quad l % NPR4 of
+    // rows RPW w + KP (l / NPR4) + k, k < KP, so that the lanes of one load
+    // instruction cover MQ whole rows of B, C and theta.  The angle prefix
+    // over the rows is then a sum within the lane, a scan across the wave's
+    // MQ lane groups and a scan across the prep waves (their totals
+    // exchanged in LDS).  Otherwise a prep wave owns pair quads over all rows
+    // (16-byte pieces of many rows per load instruction).
+    static constexpr int RPW = T / NWP;              // operand rows per prep wave
+    static constexpr int MQ = 64 / NPR4;             // rows per load instruction
+    static constexpr bool CL = (64 % NPR4 == 0) && (T % NWP == 0) && (RPW % MQ == 0);
+    static constexpr int KP = CL ? RPW / MQ : 1;     // rows per lane
+    static constexpr int SL = CL ? KP : TPL;         // raw B/C/theta slots per prep lane
+    static constexpr int SRK = CL ? 1 : R;           // ranks per slot
     static constexpr int XITEMS = T * (PS / 8);      // 8-element X row pieces
     static constexpr int XI = (XITEMS + 64 * NWP - 1) / (64 * NWP);
     // math waves
@@ -145,6 +159,8 @@ struct ScanCfg {
     // [WA][2][T] exchanged between the prep waves, and their counter.
     static constexpr size_t sz_PMW = 2 * (size_t)(R + 1) * N * 4;
     static constexpr size_t sz_SS = (size_t)WA * 2 * T * 4;
+    // CL: each prep wave's angle totals per pair, exchanged once per chunk.
+    static constexpr size_t sz_XW = (size_t)NWP * NPR * 4;
     template <bool FULL, bool PM = false> struct Lay {
         static constexpr size_t oB = 0;
         static constexpr size_t oC = sz_B;
@@ -154,8 +170,9 @@ struct ScanCfg {
         static constexpr size_t oH = 2 * BUF;
         static constexpr size_t oPW = oH + (FULL ? (SH1 ? 1 : 2) * sz_H1 : 0);
         static constexpr size_t oSS = oPW + (PM ? sz_PMW : 0);
-        static constexpr size_t oCNT = oSS + (PM ? sz_SS : 0);
-        static constexpr size_t bytes = oCNT + (PM ? 16 : 0);
+        static constexpr size_t oXW = oSS + ((PM && !CL) ? sz_SS : 0);
+        static constexpr size_t oCNT = oXW + (CL ? sz_XW : 0);
+        static constexpr size_t bytes = oCNT + ((PM || CL) ? 16 : 0);
     };
     static constexpr size_t lds_bytes = Lay<true>::bytes;
     static constexpr size_t lds_bytes_state = Lay<false>::bytes;
@@ -180,9 +197,9 @@ template <class Cf> struct PrepStage {
     using io_t = typename Cf::io_t;
     float a_dt[Cf::QPL], a_lm[Cf::QPL], a_dn[Cf::QPL], a_ln[Cf::QPL];  // dt, lam at t, t+1
     float a_A[Cf::QPL];                                                 // decay rate at t
-    float dtv[Cf::TPL];                                                 // dt of the lane's tokens
-    f32x4 thv[Cf::TPL];                                                 // theta, 4 pairs
-    IoRow8<io_t> bq[Cf::TPL][Cf::R], cq[Cf::TPL][Cf::R];                // B, C: 4 pairs
+    float dtv[Cf::SL];                                                  // dt of the lane's tokens
+    f32x4 thv[Cf::SL];                                                  // theta, 4 pairs
+    IoRow8<io_t> bq[Cf::SL][Cf::SRK], cq[Cf::SL][Cf::SRK];              // B, C: 4 pairs
     IoRow8<io_t> xq[Cf::XI];                                            // X row pieces
 };
 
@@ -211,6 +228,19 @@ __device__ __forceinline__ float group_inclusive_sum(float v)
     v += dpp_moved<0x118, 0xf>(v);   // row_shr:8
     if constexpr (LQ >= 32) v += dpp_moved<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
     if constexpr (LQ >= 64) v += dpp_moved<0x143, 0xc>(v);   // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+// Inclusive prefix sum over lanes l, l - S, l - 2S, ... (M lane groups of S
+// lanes: lanes with equal l % S form one sequence, ordered by l / S).
+template <int S, int M>
+__device__ __forceinline__ float strided_inclusive_sum(float v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < M; d <<= 1) {
+        const float u = __shfl_up(v, (unsigned)(d * S), 64);
+        v += lane >= d * S ? u : 0.f;
+    }
     return v;
 }
 
@@ -309,6 +339,14 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     const bool arole = !is_math && pw < WA;
     const int qd = (arole ? pw : 0) * QPWV + lane / LQ;   // pair quad: rows 8qd .. 8qd+7
     const int li = lane % LQ;                              // lane within the quad's group
+    // CL layout: this lane's pair quad and its first operand row
+    constexpr bool CL = Cf::CL;
+    constexpr int KP = Cf::KP, MQ = Cf::MQ, RPW = Cf::RPW, NPR4 = Cf::NPR4;
+    const int lq = lane % NPR4;
+    const int lr0 = pw * RPW + (lane / NPR4) * KP;
+    // the lanes that hold a chunk's total angle (pair quad tq)
+    const bool tlane = CL ? (pw == NWP - 1 && lane >= (MQ - 1) * NPR4) : (arole && li == LQ - 1);
+    const int tq = CL ? lq : qd;
 
     // Pre-mixer state: gains and biases of this lane's pair quad in LDS
     // (staged and read by the same wave), the prep waves' exchange of row
@@ -316,10 +354,22 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // add to it).
     float* const sPW = reinterpret_cast<float*>(smem + Lay::oPW);   // [2][N] gains, [2][R][N] biases
     float* const sSS = reinterpret_cast<float*>(smem + Lay::oSS);   // [WA][2][T]
+    float* const sXW = reinterpret_cast<float*>(smem + Lay::oXW);   // CL: [NWP][NPR] angle totals
     int* const sCnt = reinterpret_cast<int*>(smem + Lay::oCNT);
     int pcall = 0;                                                 // prep calls of this wave
-    if constexpr (PM) {
-        if (arole) {
+    if constexpr (PM && CL) {
+        // every gain and bias (a prep lane reads its own pair quad's)
+        for (int idx = tid; idx < 2 * (R + 1) * N; idx += NT) {
+            const int m = idx / ((R + 1) * N), rem = idx % ((R + 1) * N), k = rem / N, n = rem % N;
+            const float* W = m == 0 ? p.opt.Bw : p.opt.Cw;
+            const float* Bb = m == 0 ? p.opt.Bb : p.opt.Cb;
+            if (k == 0) sPW[m * N + n] = W != nullptr ? W[n] : 1.f;
+            else sPW[2 * N + (m * R + k - 1) * N + n] =
+                     Bb != nullptr ? Bb[((int64_t)h * R + (k - 1)) * N + n] : 0.f;
+        }
+    }
+    if constexpr (PM || CL) {
+        if (!CL && arole) {
             constexpr int PER = 8 * (R + 1);   // gains and R bias rows, 8 entries each
             for (int idx = li; idx < 2 * PER; idx += LQ) {
                 const int m = idx / PER, rem = idx % PER, k = rem / 8, n = 8 * qd + rem % 8;
@@ -362,7 +412,6 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // wave-uniform chunk base: no 64-bit vector address arithmetic.
     const unsigned bDT = 4u * (unsigned)sDT, bTH = 4u * (unsigned)sTH, bA = 4u * (unsigned)sA;
     const unsigned bBN = (unsigned)sizeof(io_t) * (unsigned)sBN, bXP = (unsigned)sizeof(io_t) * (unsigned)sXP;
-    const unsigned thq = 16u * (unsigned)qd;                                // theta quad
     const unsigned bcq = (unsigned)sizeof(io_t) * 8u * (unsigned)qd;       // B/C quad
     auto at = [](const auto* base, unsigned off) {
         return reinterpret_cast<decltype(base)>(reinterpret_cast<const char*>(base) + off);
@@ -397,33 +446,58 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             const unsigned lo = (unsigned)sizeof(io_t) * ((unsigned)(rho % R) * (unsigned)P + 8u * (unsigned)cg);
             st.xq[k].load(at(lX, __umul24(j, bXP) + lo));
         }
-#pragma unroll
-        for (int kk = 0; kk < TPL; ++kk) {
-            const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
-            st.dtv[kk] = *at(ldt, __umul24(j, bDT));
+        // theta (by phase mode) of 4 pairs from quad q of token j
+        auto load_theta = [&](unsigned j, int q, f32x4& th) {
+            const unsigned tq16 = 16u * (unsigned)q;
             if (phase == 0) {
-                st.thv[kk] = *reinterpret_cast<const f32x4*>(at(lth, __umul24(j, bTH) + thq));
+                th = *reinterpret_cast<const f32x4*>(at(lth, __umul24(j, bTH) + tq16));
             } else if (phase == 1) {        // zero: theta is not read
-                st.thv[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+                th = f32x4{0.f, 0.f, 0.f, 0.f};
             } else if (phase == 2) {        // reverse
-                st.thv[kk] = -*reinterpret_cast<const f32x4*>(at(lth, __umul24(j, bTH) + thq));
+                th = -*reinterpret_cast<const f32x4*>(at(lth, __umul24(j, bTH) + tq16));
             } else {                        // shuffle: pair i reads pair perm[i]
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    int src = p.opt.perm[4 * qd + e];
+                    int src = p.opt.perm[4 * q + e];
                     src = src < 0 ? 0 : (src >= NPR ? NPR - 1 : src);
-                    st.thv[kk][e] = *at(lth, __umul24(j, bTH) + 4u * (unsigned)src);
+                    th[e] = *at(lth, __umul24(j, bTH) + 4u * (unsigned)src);
                 }
             }
-        }
+        };
+        if constexpr (CL) {
+            // whole rows per instruction: row lr0 + k of token (lr0 + k) / R
 #pragma unroll
-        for (int kk = 0; kk < TPL; ++kk) {
-            const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
+            for (int k = 0; k < KP; ++k) {
+                const int jj = (lr0 + k) / R;
+                const unsigned j = (unsigned)(jj < jl ? jj : jl);
+                st.dtv[k] = *at(ldt, __umul24(j, bDT));
+                load_theta(j, lq, st.thv[k]);
+            }
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const unsigned off = __umul24(j, bBN) + (unsigned)sizeof(io_t) * (unsigned)(r * N) + bcq;
-                st.bq[kk][r].load(at(lB, off));
-                if constexpr (FULL) st.cq[kk][r].load(at(lC, off));
+            for (int k = 0; k < KP; ++k) {
+                const int rho = lr0 + k, jj = rho / R;
+                const unsigned j = (unsigned)(jj < jl ? jj : jl);
+                const unsigned off = __umul24(j, bBN)
+                                     + (unsigned)sizeof(io_t) * (unsigned)((rho % R) * N + 8 * lq);
+                st.bq[k][0].load(at(lB, off));
+                if constexpr (FULL) st.cq[k][0].load(at(lC, off));
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < TPL; ++kk) {
+                const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
+                st.dtv[kk] = *at(ldt, __umul24(j, bDT));
+                load_theta(j, qd, st.thv[kk]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < TPL; ++kk) {
+                const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const unsigned off = __umul24(j, bBN) + (unsigned)sizeof(io_t) * (unsigned)(r * N) + bcq;
+                    st.bq[kk][r].load(at(lB, off));
+                    if constexpr (FULL) st.cq[kk][r].load(at(lC, off));
+                }
             }
         }
         ldt += Q * sDT; llam += Q * sDT; lA += Q * sA;
@@ -445,6 +519,32 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         float* sU = sMisc + 4;
         const int64_t t0 = c * Q;
         const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
+
+        // ---- CL, A1 part 1: angle increments of the lane's rows, their scan
+        // within the wave, and the wave's totals published to the other prep
+        // waves (before A0 and A2, so that the totals are there when needed).
+        f32x4 cl_loc[KP];     // lane: angle at each of its rows, relative to the wave's first row
+        if constexpr (CL) {
+            f32x4 run = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < KP; ++k) {
+                // one increment per token (its rank-0 row); none past the sequence
+                const int rho = lr0 + k;
+                const bool ok = rho / R <= jl && rho % R == 0;
+                const float dv = PM ? softplus_f(st.dtv[k] + dtb_h) : st.dtv[k];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) run[e] += ok ? dv * st.thv[k][e] : 0.f;
+                cl_loc[k] = run;
+            }
+            f32x4 inc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) inc[e] = strided_inclusive_sum<NPR4, MQ>(run[e], lane);
+            const f32x4 ex = inc - run;
+#pragma unroll
+            for (int k = 0; k < KP; ++k) cl_loc[k] += ex;   // (cl_loc[KP-1] is now inc)
+            if (lane >= (MQ - 1) * NPR4) *reinterpret_cast<f32x4*>(sXW + pw * NPR + 4 * lq) = inc;
+            if (lane == 0) __hip_atomic_fetch_add(sCnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
 
         // ---- A0: decay prefix scan and trapezoid weights (one wave) -------
         if (pw == 0) {
@@ -526,7 +626,126 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         }
 
         // ---- A1: angle prefix per pair quad, rotate B and C ----------------
-        if (arole) {
+        if constexpr (CL) {
+            // Wait until every prep wave has published this chunk's totals (a
+            // bounded wait: the waves reach it together), then this wave's
+            // offset is the sum of the totals of the waves before it.
+            const int target = NWP * pcall;
+            for (int it = 0; it < (1 << 22); ++it) {
+                const int v = __builtin_amdgcn_readfirstlane(
+                    __hip_atomic_load(sCnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+                if (v >= target) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            f32x4 off = {0.f, 0.f, 0.f, 0.f};
+            for (int w = 0; w < pw; ++w) off += *reinterpret_cast<const f32x4*>(sXW + w * NPR + 4 * lq);
+            auto rotate_cl = [&](auto fullc) {
+                constexpr bool FULLC = decltype(fullc)::value;
+                // Pre-mixer: each row's RMS scale from the NPR4 lanes that hold it.
+                float scB[KP], scC[KP];
+                if constexpr (PM) {
+                    const float rn = 1.f / (float)N;
+#pragma unroll
+                    for (int k = 0; k < KP; ++k) {
+                        float sb = 0.f, sc = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float vb = st.bq[k][0].get(e);
+                            sb += vb * vb;
+                            if constexpr (FULL) {
+                                const float vc = st.cq[k][0].get(e);
+                                sc += vc * vc;
+                            }
+                        }
+#pragma unroll
+                        for (int o2 = 1; o2 < NPR4; o2 <<= 1) {
+                            sb += __shfl_xor(sb, o2, 64);
+                            if constexpr (FULL) sc += __shfl_xor(sc, o2, 64);
+                        }
+                        scB[k] = rsqrtf(sb * rn + p.opt.eps);
+                        scC[k] = FULL ? rsqrtf(sc * rn + p.opt.eps) : 0.f;
+                    }
+                }
+                // the 8 entries of row piece q as the mixer uses them
+                auto entries = [&](const IoRow8<io_t>& q, float sc, int m, int r, float (&v)[8]) {
+                    if constexpr (!PM) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = q.get(e);
+                    } else {
+                        const float* gp = sPW + m * N + 8 * lq;
+                        const float* bp = sPW + 2 * N + (m * R + r) * N + 8 * lq;
+                        const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp);
+                        const f32x4 g1 = *reinterpret_cast<const f32x4*>(gp + 4);
+                        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp);
+                        const f32x4 b1 = *reinterpret_cast<const f32x4*>(bp + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[e] = q.get(e) * sc * g0[e] + b0[e];
+                            v[4 + e] = q.get(4 + e) * sc * g1[e] + b1[e];
+                        }
+                    }
+                };
+#pragma unroll
+                for (int k = 0; k < KP; ++k) {
+                    const int rho = lr0 + k, r = rho % R;
+                    const bool ok = FULLC || rho / R <= jl;
+                    float cs[4], sn[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rope_sincos<op_t>(off[e] + cl_loc[k][e], &sn[e], &cs[e]);
+                    // R(Phi)^T applied to each pair
+                    float o[8], v[8];
+                    entries(st.bq[k][0], PM ? scB[k] : 1.f, 0, r, v);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float b0 = ok ? v[2 * e] : 0.f;
+                        const float b1 = ok ? v[2 * e + 1] : 0.f;
+                        o[2 * e] = cs[e] * b0 + sn[e] * b1;
+                        o[2 * e + 1] = cs[e] * b1 - sn[e] * b0;
+                    }
+                    lds_store8(sB + rho * LDB + 8 * lq, o);
+                    if constexpr (FULL) {
+                        entries(st.cq[k][0], PM ? scC[k] : 1.f, 1, r, v);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float c0 = ok ? v[2 * e] : 0.f;
+                            const float c1 = ok ? v[2 * e + 1] : 0.f;
+                            o[2 * e] = cs[e] * c0 + sn[e] * c1;
+                            o[2 * e + 1] = cs[e] * c1 - sn[e] * c0;
+                        }
+                        lds_store8(sC + rho * LDB + 8 * lq, o);
+                    }
+                }
+            };
+            if (jl == Q - 1) rotate_cl(std::true_type{});
+            else rotate_cl(std::false_type{});
+            // The last wave's last lane group holds the chunk's total angle.
+            if (pw == NWP - 1) {
+                const f32x4 tot = off + cl_loc[KP - 1];
+                if constexpr (BF) {
+                    float cs[4], sn[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) __sincosf(tot[e], &sn[e], &cs[e]);
+                    if (tlane) {
+                        *reinterpret_cast<f32x4*>(sCSt + 8 * lq) = f32x4{cs[0], sn[0], cs[1], sn[1]};
+                        *reinterpret_cast<f32x4*>(sCSt + 8 * lq + 4) = f32x4{cs[2], sn[2], cs[3], sn[3]};
+                    }
+                } else if (tlane) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float sn, cs;
+                        sincosf(tot[e], &sn, &cs);
+                        sCSt[2 * (4 * lq + e)] = cs;
+                        sCSt[2 * (4 * lq + e) + 1] = sn;
+                    }
+                }
+                if constexpr (!FULL) {
+                    if (tlane) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) phiseg[e] += (double)tot[e];
+                    }
+                }
+            }
+        } else if (arole) {
             // FULLC: every token of the chunk is valid (no masking needed)
             auto rotate_all = [&](auto fullc) {
                 constexpr bool FULLC = decltype(fullc)::value;
@@ -1157,15 +1376,15 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             float* rec = recs + (int64_t)seg * rec_sz;
             if (ps == 0) {
                 if (pw == 0 && lane == 0) rec[(int64_t)NP * P] = (float)l2seg;
-                if (arole && li == LQ - 1) {
+                if (tlane) {
                     const double twopi = 6.283185307179586;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float phi = (float)(phiseg[e] - twopi * floor(phiseg[e] / twopi));
                         float sn, cs;
                         sincosf(phi, &sn, &cs);
-                        rec[(int64_t)NP * P + 4 + 2 * (4 * qd + e)] = cs;
-                        rec[(int64_t)NP * P + 5 + 2 * (4 * qd + e)] = sn;
+                        rec[(int64_t)NP * P + 4 + 2 * (4 * tq + e)] = cs;
+                        rec[(int64_t)NP * P + 5 + 2 * (4 * tq + e)] = sn;
                     }
                 }
             }
