@@ -417,13 +417,19 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         return reinterpret_cast<decltype(base)>(reinterpret_cast<const char*>(base) + off);
     };
     PrepStage<Cf> st;
-    auto issue_loads = [&](int64_t c) {
+    // Loads of chunk c into the prep stage, by part (LD_A0: per-token dt, lam
+    // and decay rate for A0; LD_X: the X slice; LD_TH: dt and theta of the
+    // lane's rows; LD_BC: B and C); `advance` then moves the pointers to the
+    // next chunk.
+    constexpr int LD_A0 = 1, LD_X = 2, LD_TH = 4, LD_BC = 8;
+    auto issue_part = [&](int64_t c, auto partc) {
+        constexpr int part = decltype(partc)::value;
         const int64_t t0 = c * Q;
         const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));  // last valid j
         const int jn = (int)((L - 1 - t0) < Q ? (L - 1 - t0) : Q);              // last valid j+1
         // per-token dt / lam (at t and t+1) for A0: only the wave that runs A0
         // (each lane reads its own token's cache line)
-        if (pw == 0) {
+        if ((part & LD_A0) && pw == 0) {
 #pragma unroll
             for (int kk = 0; kk < QPL; ++kk) {
                 const int j = lane * QPL + kk;
@@ -436,15 +442,17 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 st.a_ln[kk] = *at(llam, __umul24(jnc, bDT));
             }
         }
+        if constexpr ((part & LD_X) != 0) {
 #pragma unroll
-        for (int k = 0; k < XI; ++k) {
-            int it = ptid + k * 64 * NWP;
-            if (XITEMS % (64 * NWP) != 0 && it >= XITEMS) it = XITEMS - 1;   // duplicate
-            int rho, cg;
-            xmap(it, rho, cg);
-            const unsigned j = (unsigned)(rho / R < jl ? rho / R : jl);
-            const unsigned lo = (unsigned)sizeof(io_t) * ((unsigned)(rho % R) * (unsigned)P + 8u * (unsigned)cg);
-            st.xq[k].load(at(lX, __umul24(j, bXP) + lo));
+            for (int k = 0; k < XI; ++k) {
+                int it = ptid + k * 64 * NWP;
+                if (XITEMS % (64 * NWP) != 0 && it >= XITEMS) it = XITEMS - 1;   // duplicate
+                int rho, cg;
+                xmap(it, rho, cg);
+                const unsigned j = (unsigned)(rho / R < jl ? rho / R : jl);
+                const unsigned lo = (unsigned)sizeof(io_t) * ((unsigned)(rho % R) * (unsigned)P + 8u * (unsigned)cg);
+                st.xq[k].load(at(lX, __umul24(j, bXP) + lo));
+            }
         }
         // theta (by phase mode) of 4 pairs from quad q of token j
         auto load_theta = [&](unsigned j, int q, f32x4& th) {
@@ -466,47 +474,76 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         };
         if constexpr (CL) {
             // whole rows per instruction: row lr0 + k of token (lr0 + k) / R
+            if constexpr ((part & LD_TH) != 0) {
 #pragma unroll
-            for (int k = 0; k < KP; ++k) {
-                const int jj = (lr0 + k) / R;
-                const unsigned j = (unsigned)(jj < jl ? jj : jl);
-                st.dtv[k] = *at(ldt, __umul24(j, bDT));
-                load_theta(j, lq, st.thv[k]);
+                for (int k = 0; k < KP; ++k) {
+                    const int jj = (lr0 + k) / R;
+                    const unsigned j = (unsigned)(jj < jl ? jj : jl);
+                    st.dtv[k] = *at(ldt, __umul24(j, bDT));
+                    load_theta(j, lq, st.thv[k]);
+                }
             }
+            if constexpr ((part & LD_BC) != 0) {
 #pragma unroll
-            for (int k = 0; k < KP; ++k) {
-                const int rho = lr0 + k, jj = rho / R;
-                const unsigned j = (unsigned)(jj < jl ? jj : jl);
-                const unsigned off = __umul24(j, bBN)
-                                     + (unsigned)sizeof(io_t) * (unsigned)((rho % R) * N + 8 * lq);
-                st.bq[k][0].load(at(lB, off));
-                if constexpr (FULL) st.cq[k][0].load(at(lC, off));
+                for (int k = 0; k < KP; ++k) {
+                    const int rho = lr0 + k, jj = rho / R;
+                    const unsigned j = (unsigned)(jj < jl ? jj : jl);
+                    const unsigned off = __umul24(j, bBN)
+                                         + (unsigned)sizeof(io_t) * (unsigned)((rho % R) * N + 8 * lq);
+                    st.bq[k][0].load(at(lB, off));
+                    if constexpr (FULL) st.cq[k][0].load(at(lC, off));
+                }
             }
         } else {
+            if constexpr ((part & LD_TH) != 0) {
 #pragma unroll
-            for (int kk = 0; kk < TPL; ++kk) {
-                const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
-                st.dtv[kk] = *at(ldt, __umul24(j, bDT));
-                load_theta(j, qd, st.thv[kk]);
+                for (int kk = 0; kk < TPL; ++kk) {
+                    const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
+                    st.dtv[kk] = *at(ldt, __umul24(j, bDT));
+                    load_theta(j, qd, st.thv[kk]);
+                }
             }
+            if constexpr ((part & LD_BC) != 0) {
 #pragma unroll
-            for (int kk = 0; kk < TPL; ++kk) {
-                const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
+                for (int kk = 0; kk < TPL; ++kk) {
+                    const unsigned j = (unsigned)(li * TPL + kk < jl ? li * TPL + kk : jl);
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const unsigned off = __umul24(j, bBN) + (unsigned)sizeof(io_t) * (unsigned)(r * N) + bcq;
-                    st.bq[kk][r].load(at(lB, off));
-                    if constexpr (FULL) st.cq[kk][r].load(at(lC, off));
+                    for (int r = 0; r < R; ++r) {
+                        const unsigned off = __umul24(j, bBN) + (unsigned)sizeof(io_t) * (unsigned)(r * N) + bcq;
+                        st.bq[kk][r].load(at(lB, off));
+                        if constexpr (FULL) st.cq[kk][r].load(at(lC, off));
+                    }
                 }
             }
         }
+    };
+    auto advance = [&]() {
         ldt += Q * sDT; llam += Q * sDT; lA += Q * sA;
         if (phase != 1) lth += Q * sTH;
         lB += Q * sBN; lC += Q * sBN; lX += Q * sXP;
     };
+    using ld_th = std::integral_constant<int, LD_TH>;
+    using ld_a0 = std::integral_constant<int, LD_A0>;
+    using ld_x = std::integral_constant<int, LD_X>;
+    using ld_bc = std::integral_constant<int, LD_BC>;
+    // Every part of chunk c, in the order prep consumes them, then advance.
+    auto issue_loads = [&](int64_t c) {
+        if constexpr (CL) {
+            issue_part(c, ld_th{});
+            issue_part(c, ld_a0{});
+            issue_part(c, ld_x{});
+            issue_part(c, ld_bc{});
+        } else {
+            issue_part(c, std::integral_constant<int, LD_A0 | LD_X | LD_TH | LD_BC>{});
+        }
+        advance();
+    };
 
     // Raw inputs of chunk c (in st) -> operands and scalars in buffer s.
-    auto prep = [&](int64_t c, int s) {
+    // CL with nx: each part of chunk c+1's loads is issued as soon as this
+    // step has consumed the registers it refills (a longer prefetch distance
+    // than issuing them all at the end).
+    auto prep = [&](int64_t c, int s, bool nx) {
         ++pcall;
         op_t* sB = buf_B(s);
         op_t* sC = buf_C(s);
@@ -544,6 +581,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             for (int k = 0; k < KP; ++k) cl_loc[k] += ex;   // (cl_loc[KP-1] is now inc)
             if (lane >= (MQ - 1) * NPR4) *reinterpret_cast<f32x4*>(sXW + pw * NPR + 4 * lq) = inc;
             if (lane == 0) __hip_atomic_fetch_add(sCnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (nx) issue_part(c + 1, ld_th{});
         }
 
         // ---- A0: decay prefix scan and trapezoid weights (one wave) -------
@@ -594,6 +632,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             if (lane == 0) sMisc[0] = l2tot;
             if constexpr (!FULL) l2seg += (double)l2tot;
         }
+        if (CL && nx) issue_part(c + 1, ld_a0{});
 
         // ---- A2: X slice into LDS ------------------------------------------
         if (BF && jl == Q - 1) {
@@ -624,6 +663,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 for (int e = 0; e < 8; ++e) sX[(8 * cg + e) * LDX + rho] = v[e];
             }
         }
+        if (CL && nx) issue_part(c + 1, ld_x{});
 
         // ---- A1: angle prefix per pair quad, rotate B and C ----------------
         if constexpr (CL) {
@@ -718,6 +758,10 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             };
             if (jl == Q - 1) rotate_cl(std::true_type{});
             else rotate_cl(std::false_type{});
+            if (nx) {
+                issue_part(c + 1, ld_bc{});
+                advance();
+            }
             // The last wave's last lane group holds the chunk's total angle.
             if (pw == NWP - 1) {
                 const f32x4 tot = off + cl_loc[KP - 1];
@@ -1358,16 +1402,16 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         // prologue: chunk c_begin into buffer 0, chunk c_begin+1's loads out
         if (c_begin < c_end) {
             issue_loads(c_begin);
-            prep(c_begin, 0);
-            if (c_begin + 1 < c_end) issue_loads(c_begin + 1);
+            prep(c_begin, 0, CL && c_begin + 1 < c_end);
+            if (!CL && c_begin + 1 < c_end) issue_loads(c_begin + 1);
         }
         __syncthreads();
         __builtin_amdgcn_s_setprio(0);
         for (int64_t c = c_begin; c < c_end; ++c) {
             const int s = (int)((c - c_begin) & 1);
             if (c + 1 < c_end) {
-                prep(c + 1, s ^ 1);
-                if (c + 2 < c_end) issue_loads(c + 2);
+                prep(c + 1, s ^ 1, CL && c + 2 < c_end);
+                if (!CL && c + 2 < c_end) issue_loads(c + 2);
             }
             __syncthreads();
         }
