@@ -250,6 +250,17 @@ __device__ __forceinline__ float strided_inclusive_sum(float v, int lane)
 // softplus(z) = log(1 + e^z) (z itself above 20, where the difference is
 // below float32 resolution) and sigmoid(z) = 1 / (1 + e^-z): the pre-mixer's
 // maps of the raw dt and lam projections.
+// Calls f(std::integral_constant<int, v>) for the runtime value v in [I, NV)
+// (a scalar branch per candidate when v is wave-uniform).
+template <int I, int NV, class F>
+__device__ __forceinline__ void static_dispatch(int v, F&& f)
+{
+    if constexpr (I < NV) {
+        if (v == I) f(std::integral_constant<int, I>{});
+        else static_dispatch<I + 1, NV>(v, f);
+    }
+}
+
 __device__ __forceinline__ float softplus_f(float z) { return z > 20.f ? z : log1pf(expf(z)); }
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + expf(-z)); }
 
@@ -1132,7 +1143,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         const int64_t t0 = c * Q;
         const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
         io_t* __restrict__ Yc = Y0 + (c - c_begin) * Q * (int64_t)sXP;
-        const int pg = wv % PG, qg = wv / PG;
+        const int pg = wv % PG;
         // A operands G^T of this wave's headdim tiles, shared by its query tiles
         Frag<op_t> gfr[PPW][NP / 32];
 #pragma unroll
@@ -1140,6 +1151,11 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
 #pragma unroll
             for (int s2 = 0; s2 < NP / 32; ++s2)
                 lds_frag8(gfr[k][s2], sHc + (16 * (pg * PPW + k) + l16) * LDH + 32 * s2 + 8 * g);
+        // The wave's query group as a compile-time constant (one copy of the
+        // body per group): its query tiles and their key ranges are then
+        // known, and the tile loops unroll with constant bounds.
+        static_dispatch<0, QG>(wv / PG, [&](auto qgc) {
+        constexpr int qg = decltype(qgc)::value;
 #pragma unroll
         for (int qi = 0; qi < QPW; ++qi) {
             // query tiles of this wave; with several query groups, alternate
@@ -1274,6 +1290,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 }
             }
         }
+        });
     };
 
     // ---- D: state update  G <- R(Phi_tot)(e^{Lam_tot} G + Bbar_d^T X) ------
