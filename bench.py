@@ -159,23 +159,25 @@ def load_traffic(name):
 
 def time_launches(fn, steps, warmup, torch):
     """Run fn() warmup + steps times; returns (total seconds, mean kernel ms).
-    One HIP event is recorded on the launch stream at every step boundary of
-    the timed region, so each step's duration is the span between the events
-    around it (the step's kernels and the gaps between them)."""
+    Two HIP events on the launch stream bracket the timed region, so the mean
+    step duration is their span over the steps: the steps' kernels and the
+    gaps between them, with no other work queued in between (an event record
+    per step would add its own barrier to every step)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(steps):
+    ev0.record(stream)
+    for _ in range(steps):
         fn()
-        ev[i + 1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
-    kms = ev[0].elapsed_time(ev[steps]) / max(steps, 1)
+    kms = ev0.elapsed_time(ev1) / max(steps, 1)
     return total, kms
 
 
