@@ -41,12 +41,18 @@
 //        chunk's state term.
 //   prep waves (NWP) meanwhile turn chunk c+1's raw inputs (loaded into
 //     registers one chunk earlier) into matrix-core operands in the other LDS
-//     buffer, then issue the loads of chunk c+2:
+//     buffer, issuing the loads of chunk c+2 part by part as the registers
+//     they refill are consumed:
 //     A0 one wave: wavefront prefix scan of dt*A (DPP), weights w, gamma and
 //        d_k = w_k e^{Lam_tot-Lam_k}.
-//     A1 per pair quad (4 rotation pairs, 16 bytes of bf16 B/C per lane):
-//        angle prefix sums over the chunk's tokens with a DPP scan inside the
-//        wave, sine/cosine, rotation of B and C rows into LDS.
+//     A1 row-coalesced: a prep wave owns a contiguous run of the chunk's
+//        operand rows and a lane one pair quad (4 rotation pairs, 16 bytes of
+//        bf16 B/C/theta) of some of them, so one load instruction covers
+//        whole rows; the angle prefix is a sum over the lane's rows, a scan
+//        across the wave's lane groups and, through LDS, across the prep
+//        waves; then sine/cosine and the rotation of B and C rows into LDS.
+//        (Shapes whose rows do not split that way: a wave owns pair quads
+//        over all rows and scans the angles with DPP inside the wave.)
 //     A2 the X slice into LDS (bf16 as rows, read transposed by
 //        ds_read_tr16_b64; fp32 as X^T).
 // One barrier per chunk separates producer and consumer buffers.
