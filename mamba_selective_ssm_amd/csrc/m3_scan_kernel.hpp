@@ -267,7 +267,18 @@ __device__ __forceinline__ void static_dispatch(int v, F&& f)
     }
 }
 
-__device__ __forceinline__ float softplus_f(float z) { return z > 20.f ? z : log1pf(expf(z)); }
+// softplus(z) = max(z, 0) + log1p(e), e = e^{-|z|} in (0, 1], on the hardware
+// exp2/log2: for e < 2^-10 the series e (1 - e/2 + e^2/3) (truncation below
+// 2^-40 relative), otherwise log(u) with u = 1 + e corrected for the rounding
+// of u (log1p(e) = log(u) - ((u - 1) - e) / u to first order).
+__device__ __forceinline__ float softplus_f(float z)
+{
+    const float e = __builtin_amdgcn_exp2f(-fabsf(z) * kLog2e);
+    const float u = 1.f + e;
+    const float lp = e < 0x1p-10f ? e * (1.f - e * (0.5f - e * (1.f / 3.f)))
+                                  : __builtin_amdgcn_logf(u) * 0.6931471805599453f - ((u - 1.f) - e) / u;
+    return fmaxf(z, 0.f) + lp;
+}
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + expf(-z)); }
 
 // PM: pre-mixer on (the raw dt, lam, B and C are normalised in the prep waves).
@@ -543,6 +554,9 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     using ld_a0 = std::integral_constant<int, LD_A0>;
     using ld_x = std::integral_constant<int, LD_X>;
     using ld_bc = std::integral_constant<int, LD_BC>;
+    // Part-wise early issue inside prep (row-coalesced layout; not with the
+    // pre-mixer, whose prep step has no registers to spare for it).
+    constexpr bool EARLY = CL && !PM;
     // Every part of chunk c, in the order prep consumes them, then advance.
     auto issue_loads = [&](int64_t c) {
         if constexpr (CL) {
@@ -1425,16 +1439,16 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         // prologue: chunk c_begin into buffer 0, chunk c_begin+1's loads out
         if (c_begin < c_end) {
             issue_loads(c_begin);
-            prep(c_begin, 0, CL && c_begin + 1 < c_end);
-            if (!CL && c_begin + 1 < c_end) issue_loads(c_begin + 1);
+            prep(c_begin, 0, EARLY && c_begin + 1 < c_end);
+            if (!EARLY && c_begin + 1 < c_end) issue_loads(c_begin + 1);
         }
         __syncthreads();
         __builtin_amdgcn_s_setprio(0);
         for (int64_t c = c_begin; c < c_end; ++c) {
             const int s = (int)((c - c_begin) & 1);
             if (c + 1 < c_end) {
-                prep(c + 1, s ^ 1, CL && c + 2 < c_end);
-                if (!CL && c + 2 < c_end) issue_loads(c + 2);
+                prep(c + 1, s ^ 1, EARLY && c + 2 < c_end);
+                if (!EARLY && c + 2 < c_end) issue_loads(c + 2);
             }
             __syncthreads();
         }
