@@ -269,7 +269,7 @@ __device__ __forceinline__ void static_dispatch(int v, F&& f)
 
 // softplus(z) = max(z, 0) + log1p(e), e = e^{-|z|} in (0, 1], on the hardware
 // exp2/log2: for e < 2^-10 the series e (1 - e/2 + e^2/3) (truncation below
-// 2^-40 relative), otherwise log(u) with u = 1 + e corrected for the rounding
+// 2^-32 relative), otherwise log(u) with u = 1 + e corrected for the rounding
 // of u (log1p(e) = log(u) - ((u - 1) - e) / u to first order).
 __device__ __forceinline__ float softplus_f(float z)
 {
