@@ -143,6 +143,27 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
     };
     if (npl > 0) load_batch(ha, 0);
 
+    // Pre-mixer gains and biases of this lane's first GPF entries n = lane +
+    // 64 k, loaded now so that they are in flight with the state (entries past
+    // 64 GPF, for N > 128, are read where they are used).
+    constexpr int GPF = 2;
+    float gwb[GPF], gwc[GPF], gbb[GPF][R], gbc[GPF][R];
+    if constexpr (PM) {
+#pragma unroll
+        for (int k = 0; k < GPF; ++k) {
+            const int n = lane + 64 * k;
+            const bool ok = n < N;
+            gwb[k] = (ok && p.opt.Bw != nullptr) ? p.opt.Bw[n] : 1.f;
+            gwc[k] = (ok && p.opt.Cw != nullptr) ? p.opt.Cw[n] : 1.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int64_t bi = (h * R + r) * (int64_t)N + n;
+                gbb[k][r] = (ok && p.opt.Bb != nullptr) ? p.opt.Bb[bi] : 0.f;
+                gbc[k][r] = (ok && p.opt.Cb != nullptr) ? p.opt.Cb[bi] : 0.f;
+            }
+        }
+    }
+
     // Small operands: B_prev, B, C transposed into the wave's LDS slice, the
     // pair rotations, this lane's columns of X_prev and X.
     // 8 consecutive elements (one rank row) per lane and load when N % 8 == 0.
@@ -217,6 +238,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // Row sums of squares: the 2R rows' wavefront sums (DPP scans) are
+        // independent chains.
         float sc[2][R];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -225,25 +248,35 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
                 const float* row = m == 0 ? sB : sC;
                 float ss = 0.f;
                 for (int n = lane; n < N; n += 64) ss += row[n * R + r] * row[n * R + r];
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                ss = wave_read_lane(wave_inclusive_sum(ss), 63);
                 sc[m][r] = rsqrtf(ss / (float)N + p.opt.eps);
             }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int n = lane; n < N; n += 64) {
-            const float wb = p.opt.Bw != nullptr ? p.opt.Bw[n] : 1.f;
-            const float wc = p.opt.Cw != nullptr ? p.opt.Cw[n] : 1.f;
+        auto premix_entry = [&](int n, float wb, float wc, const float (&bb)[R], const float (&bcv)[R]) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int64_t bi = (h * R + r) * (int64_t)N + n;
-                const float vb = sB[n * R + r] * sc[0][r] * wb + (p.opt.Bb != nullptr ? p.opt.Bb[bi] : 0.f);
-                const float vc = sC[n * R + r] * sc[1][r] * wc + (p.opt.Cb != nullptr ? p.opt.Cb[bi] : 0.f);
+                const float vb = sB[n * R + r] * sc[0][r] * wb + bb[r];
+                const float vc = sC[n * R + r] * sc[1][r] * wc + bcv[r];
                 sB[n * R + r] = vb;
                 sC[n * R + r] = vc;
                 Bp[r * N + n] = from_f32<IO>(vb);
             }
+        };
+#pragma unroll
+        for (int k = 0; k < GPF; ++k)
+            if (lane + 64 * k < N) premix_entry(lane + 64 * k, gwb[k], gwc[k], gbb[k], gbc[k]);
+        for (int n = lane + 64 * GPF; n < N; n += 64) {
+            float bb[R], bcv[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int64_t bi = (h * R + r) * (int64_t)N + n;
+                bb[r] = p.opt.Bb != nullptr ? p.opt.Bb[bi] : 0.f;
+                bcv[r] = p.opt.Cb != nullptr ? p.opt.Cb[bi] : 0.f;
+            }
+            premix_entry(n, p.opt.Bw != nullptr ? p.opt.Bw[n] : 1.f, p.opt.Cw != nullptr ? p.opt.Cw[n] : 1.f,
+                         bb, bcv);
         }
     } else {
         for (int idx = 8 * lane; idx < n8; idx += 512) copy8(Bp + idx, Bt + idx);
