@@ -10,7 +10,13 @@ differentiation of that loop: the gradient of L = sum(dy * y) + sum(dh * h_L)
 with respect to every input, the decay rate A and the state record.
 
 Layouts as the scan: x [Bt,L,H,R,P], Bm/Cm [Bt,L,H,R,N], dt/lam [Bt,L,H],
-theta [Bt,L,H,N/2], A [H]; h0 [Bt,H,N,P], Bprev [Bt,H,R,N], xprev [Bt,H,R,P].
+theta [Bt,L,H,N/2], A [H] (or per token [Bt,L,H] in forward_torch);
+h0 [Bt,H,N,P], Bprev [Bt,H,R,N], xprev [Bt,H,R,P].
+
+dA is a sum over batch and tokens of per-token terms (the decay rate enters
+every step's alpha_t = exp(dt_t A)); scan_backward differentiates with
+respect to A repeated per token, so that it can also return the size of what
+that sum adds up: dA_scale[h] = sum over (b, t) of |dL/dA_{b,t,h}|.
 """
 from __future__ import annotations
 
@@ -27,7 +33,7 @@ def forward_torch(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev):
     ys = []
     for t in range(L):
         d = dt[:, t]                                     # [Bt,H]
-        alpha = torch.exp(d * A)
+        alpha = torch.exp(d * (A if A.dim() == 1 else A[:, t]))
         beta = (1.0 - lam[:, t]) * d * alpha
         gamma = lam[:, t] * d
         U = torch.einsum("bhrn,bhrp->bhnp", Bm[:, t], x[:, t])
@@ -47,11 +53,14 @@ def forward_torch(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev):
 
 def scan_backward(x, Bm, Cm, dt, A, theta, lam, dy, dh=None, h0=None, Bprev=None, xprev=None):
     """Gradients of sum(dy * y) + sum(dh * h_L).  Returns a dict of float64
-    numpy arrays: dx, dB, dC, ddt, dA, dtheta, dlam, dh0, dBprev, dxprev."""
+    numpy arrays: dx, dB, dC, ddt, dA, dtheta, dlam, dh0, dBprev, dxprev, and
+    dA_scale [H] (the sum of |per-token terms| that dA adds up)."""
     t64 = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
-    x, Bm, Cm, dt, A, theta, lam = map(t64, (x, Bm, Cm, dt, A, theta, lam))
+    x, Bm, Cm, dt, theta, lam = map(t64, (x, Bm, Cm, dt, theta, lam))
     Bt, L, H, R, P = x.shape
     N = Bm.shape[-1]
+    # A repeated per (b, t): its gradient holds the per-token terms of dA
+    A = t64(np.broadcast_to(np.asarray(A, dtype=np.float64), (Bt, L, H)))
     z = lambda *s: np.zeros(s)
     h0 = t64(z(Bt, H, N, P) if h0 is None else h0)
     Bprev = t64(z(Bt, H, R, N) if Bprev is None else Bprev)
@@ -63,5 +72,9 @@ def scan_backward(x, Bm, Cm, dt, A, theta, lam, dy, dh=None, h0=None, Bprev=None
     names = ["dx", "dB", "dC", "ddt", "dA", "dtheta", "dlam", "dh0", "dBprev", "dxprev"]
     leaves = [x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev]
     grads = torch.autograd.grad(loss, leaves, allow_unused=True)
-    return {n: (np.zeros(v.shape) if g is None else g.detach().numpy())
-            for n, v, g in zip(names, leaves, grads)}
+    out = {n: (np.zeros(v.shape) if g is None else g.detach().numpy())
+           for n, v, g in zip(names, leaves, grads)}
+    terms = out["dA"]                                    # [Bt, L, H]
+    out["dA"] = terms.sum(axis=(0, 1))
+    out["dA_scale"] = np.abs(terms).sum(axis=(0, 1))
+    return out

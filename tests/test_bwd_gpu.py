@@ -4,7 +4,11 @@ fp64 gradient oracle (reverse-mode differentiation of the step recurrence).
 
 Metric per gradient tensor: max |got - ref| / max |ref|; tolerance 1e-4 for
 float32 inputs and 2e-2 for bfloat16 inputs (the kernel computes in float32
-from the same rounded inputs the oracle consumes).
+from the same rounded inputs the oracle consumes).  dA is a sum over batch
+and tokens of per-token terms that can cancel almost completely (a reference
+hundreds of times smaller than its terms occurs), so its error is measured
+against the size of what it adds up: max |got - ref| / max dA_scale, with
+dA_scale the oracle's sum of |per-token terms|.
 """
 import numpy as np
 import pytest
@@ -46,7 +50,10 @@ def grads_case(w, seed, with_state=True, with_dh=True, label="", method="auto"):
     tol = TOL[w.io_dtype]
     errs = {}
     for n in NAMES:
-        errs[n] = rel_err(f64(getattr(got, n)), ref[ORACLE.get(n, n)])
+        if n == "dA":
+            errs[n] = float(np.max(np.abs(f64(got.dA) - ref["dA"])) / max(np.max(ref["dA_scale"]), 1e-300))
+        else:
+            errs[n] = rel_err(f64(getattr(got, n)), ref[ORACLE.get(n, n)])
     say("   " + "  ".join("%s %.2e" % (n, e) for n, e in errs.items()) + "  (tol %.0e)" % tol)
     bad = {n: e for n, e in errs.items() if not e <= tol}
     assert not bad, bad

@@ -675,6 +675,34 @@ def test_backward_matches_finite_differences():
         assert err < 1e-6, (name, err)
 
 
+def test_backward_dA_terms_match_finite_differences():
+    """dA is the sum over (b, t) of the loss's derivative with respect to a
+    per-token decay rate: with A given per token to the C oracle, central
+    differences of its loss reproduce each term, their sum is dA and the sum
+    of their absolute values is dA_scale."""
+    from oracle.backward import scan_backward
+    rng = np.random.default_rng(33)
+    ins, dy, dh = _bwd_case(rng, Bt=2, L=5, H=2, R=1, P=3, N=4)
+    g = scan_backward(*ins[:7], dy, dh, h0=ins[7], Bprev=ins[8], xprev=ins[9])
+    Bt, L, H = ins[3].shape
+    A_tok = np.broadcast_to(ins[4], (Bt, L, H)).copy()
+
+    def loss(At):
+        y, hL, _, _ = oracle.scan(*ins[:4], At, *ins[5:7], h0=ins[7], Bprev=ins[8], xprev=ins[9])
+        return float(np.sum(y * dy) + np.sum(hL * dh))
+    eps = 1e-6
+    terms = np.zeros((Bt, L, H))
+    for idx in np.ndindex(Bt, L, H):
+        plus, minus = A_tok.copy(), A_tok.copy()
+        plus[idx] += eps
+        minus[idx] -= eps
+        terms[idx] = (loss(plus) - loss(minus)) / (2 * eps)
+    scale = np.abs(terms).sum(axis=(0, 1))
+    assert np.max(np.abs(terms.sum(axis=(0, 1)) - g["dA"])) / np.max(scale) < 1e-6
+    assert np.max(np.abs(scale - g["dA_scale"])) / np.max(scale) < 1e-6
+    assert np.all(g["dA_scale"] >= np.abs(g["dA"]) - 1e-9)
+
+
 # ---------------------------------------------------------------------------
 # Accumulated angle and the write / read phase interventions.
 

@@ -105,3 +105,28 @@ def test_random_decode_case(case):
         say("   step %d rel err y %.3e state %.3e B_prev %.3e" % (t, ey, eh, eb))
         assert ey <= tol and eh <= tol and eb <= tol, (ey, eh, eb)
         np.testing.assert_array_equal(f64(st.x_prev), xr)
+
+
+def draw_bwd(case):
+    rnd = random.Random(9800 + case)
+    N, P, R = rnd.choice([(16, 16, 1), (32, 32, 2), (32, 64, 4), (64, 32, 1), (64, 64, 2),
+                          (128, 64, 1), (128, 32, 4), (64, 16, 2)])
+    io = rnd.choice(["f32", "bf16"])
+    return dict(N=N, P=P, R=R, io=io, L=rnd.randint(1, 160), Bt=rnd.randint(1, 2),
+                H=rnd.randint(1, 3), with_state=rnd.random() < 0.7, with_dh=rnd.random() < 0.7,
+                dt_mu=rnd.choice([-2.0, -1.0, 0.0]))
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_bwd_case(case):
+    """The scan gradient by both methods (where the chunked one supports the
+    shape) against the fp64 gradient oracle."""
+    import test_bwd_gpu as bwd
+
+    c = draw_bwd(case)
+    w = workload(c["Bt"], c["L"], c["H"], c["R"], c["P"], c["N"], io=c["io"], dt_mu=c["dt_mu"],
+                 theta="uniform_pi")
+    methods = ["step"] + (["chunked"] if bwd.chunked_ok(c["io"], c["N"], c["P"], c["R"]) else [])
+    for m in methods:
+        bwd.grads_case(w, 9900 + case, with_state=c["with_state"], with_dh=c["with_dh"],
+                       label="random bwd %d" % case, method=m)
