@@ -13,6 +13,16 @@ Layouts as the scan: x [Bt,L,H,R,P], Bm/Cm [Bt,L,H,R,N], dt/lam [Bt,L,H],
 theta [Bt,L,H,N/2], A [H] (or per token [Bt,L,H] in forward_torch);
 h0 [Bt,H,N,P], Bprev [Bt,H,R,N], xprev [Bt,H,R,P].
 
+Options (the same maps as oracle.scan applies before the recurrence, here on
+float64 tensors so that autograd carries the gradient back through them):
+head groups (B, C given per group of nheads/ngroups heads and repeated per
+head), the phase interventions of "Understanding Mamba-3 Through Oscillatory
+Dynamics" (section 5.3: theta zeroed, negated or shuffled across the pairs)
+and the pre-mixer of the Towards AI explainer (section II: RMSNorm with a gain
+per state channel and a bias per head, rank and channel on B and C; softplus
+of the raw step plus its bias; sigmoid of the raw trapezoid weight).  With the
+pre-mixer the gradients are those of the raw inputs and of its parameters.
+
 dA is a sum over batch and tokens of per-token terms (the decay rate enters
 every step's alpha_t = exp(dt_t A)); scan_backward differentiates with
 respect to A repeated per token, so that it can also return the size of what
@@ -24,10 +34,41 @@ import numpy as np
 import torch
 
 
-def forward_torch(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev):
-    """y [Bt,L,H,R,P] and h_L, stepping the recurrence on float64 tensors."""
+def options_torch(Bm, Cm, dt, theta, lam, H, ngroups=None, phase="native", perm=None,
+                  premix=None):
+    """(B, C, dt, theta, lam) as the recurrence uses them.  ``premix`` holds
+    float64 tensors B_norm_w, C_norm_w [N], B_bias, C_bias [H,R,N], dt_bias
+    [H] and the float eps."""
+    if ngroups:
+        Bm = torch.repeat_interleave(Bm, H // Bm.shape[2], dim=2)
+        Cm = torch.repeat_interleave(Cm, H // Cm.shape[2], dim=2)
+    if phase == "zero":
+        theta = torch.zeros_like(theta)
+    elif phase == "reverse":
+        theta = -theta
+    elif phase == "shuffle":
+        theta = theta[..., torch.as_tensor(np.asarray(perm), dtype=torch.long)]
+    elif phase not in (None, "native"):
+        raise ValueError("oracle: unknown phase mode %r" % (phase,))
+    if premix is not None:
+        eps = float(premix["eps"])
+
+        def norm(M, w, b):
+            return M / torch.sqrt(torch.mean(M * M, dim=-1, keepdim=True) + eps) * w + b
+        Bm = norm(Bm, premix["B_norm_w"], premix["B_bias"])
+        Cm = norm(Cm, premix["C_norm_w"], premix["C_bias"])
+        dt = torch.logaddexp(torch.zeros_like(dt), dt + premix["dt_bias"])
+        lam = torch.sigmoid(lam)
+    return Bm, Cm, dt, theta, lam
+
+
+def forward_torch(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev, **options):
+    """y [Bt,L,H,R,P] and h_L, stepping the recurrence on float64 tensors
+    (``options`` as options_torch takes them)."""
     Bt, L, H, R, P = x.shape
     N = Bm.shape[-1]
+    if options:
+        Bm, Cm, dt, theta, lam = options_torch(Bm, Cm, dt, theta, lam, H, **options)
     h = h0                                               # [Bt,H,N,P]
     Uprev = torch.einsum("bhrn,bhrp->bhnp", Bprev, xprev)
     ys = []
@@ -51,10 +92,17 @@ def forward_torch(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev):
     return y, h
 
 
-def scan_backward(x, Bm, Cm, dt, A, theta, lam, dy, dh=None, h0=None, Bprev=None, xprev=None):
+PREMIX_GRADS = ("dB_norm_w", "dC_norm_w", "dB_bias", "dC_bias", "ddt_bias")
+
+
+def scan_backward(x, Bm, Cm, dt, A, theta, lam, dy, dh=None, h0=None, Bprev=None, xprev=None, *,
+                  ngroups=None, phase="native", perm=None, premix=None):
     """Gradients of sum(dy * y) + sum(dh * h_L).  Returns a dict of float64
-    numpy arrays: dx, dB, dC, ddt, dA, dtheta, dlam, dh0, dBprev, dxprev, and
-    dA_scale [H] (the sum of |per-token terms| that dA adds up)."""
+    numpy arrays: dx, dB, dC, ddt, dA, dtheta, dlam, dh0, dBprev, dxprev,
+    dA_scale [H] (the sum of |per-token terms| that dA adds up) and, with
+    ``premix`` (a dict of arrays B_norm_w, C_norm_w, B_bias, C_bias, dt_bias
+    and eps), the parameter gradients dB_norm_w, dC_norm_w, dB_bias, dC_bias,
+    ddt_bias."""
     t64 = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
     x, Bm, Cm, dt, theta, lam = map(t64, (x, Bm, Cm, dt, theta, lam))
     Bt, L, H, R, P = x.shape
@@ -65,12 +113,20 @@ def scan_backward(x, Bm, Cm, dt, A, theta, lam, dy, dh=None, h0=None, Bprev=None
     h0 = t64(z(Bt, H, N, P) if h0 is None else h0)
     Bprev = t64(z(Bt, H, R, N) if Bprev is None else Bprev)
     xprev = t64(z(Bt, H, R, P) if xprev is None else xprev)
-    y, hL = forward_torch(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev)
+    pm = None
+    if premix is not None:
+        pm = {k: t64(premix[k]) for k in ("B_norm_w", "C_norm_w", "B_bias", "C_bias", "dt_bias")}
+        pm["eps"] = float(premix.get("eps", 1e-6))
+    y, hL = forward_torch(x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev, ngroups=ngroups,
+                          phase=phase, perm=perm, premix=pm)
     loss = (y * torch.as_tensor(np.asarray(dy, dtype=np.float64))).sum()
     if dh is not None:
         loss = loss + (hL * torch.as_tensor(np.asarray(dh, dtype=np.float64))).sum()
     names = ["dx", "dB", "dC", "ddt", "dA", "dtheta", "dlam", "dh0", "dBprev", "dxprev"]
     leaves = [x, Bm, Cm, dt, A, theta, lam, h0, Bprev, xprev]
+    if pm is not None:
+        names += list(PREMIX_GRADS)
+        leaves += [pm[n[1:]] for n in PREMIX_GRADS]
     grads = torch.autograd.grad(loss, leaves, allow_unused=True)
     out = {n: (np.zeros(v.shape) if g is None else g.detach().numpy())
            for n, v, g in zip(names, leaves, grads)}

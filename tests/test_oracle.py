@@ -703,6 +703,84 @@ def test_backward_dA_terms_match_finite_differences():
     assert np.all(g["dA_scale"] >= np.abs(g["dA"]) - 1e-9)
 
 
+def _bwd_option_case(rng, ngroups, phase, premix, Bt=1, L=5, H=2, R=2, P=2, N=4):
+    """A gradient case with options: B, C per group, a permutation for
+    "shuffle", and with the pre-mixer raw dt, lam and its parameters."""
+    ins, dy, dh = _bwd_case(rng, Bt, L, H, R, P, N)
+    if ngroups:
+        ins[1] = rng.standard_normal((Bt, L, ngroups, R, N))
+        ins[2] = rng.standard_normal((Bt, L, ngroups, R, N))
+    kw = dict(ngroups=ngroups or None, phase=phase)
+    if phase == "shuffle":
+        kw["perm"] = rng.permutation(N // 2)
+    pm = None
+    if premix:
+        ins[3] = rng.standard_normal((Bt, L, H))
+        ins[6] = rng.standard_normal((Bt, L, H))
+        pm = dict(B_norm_w=rng.uniform(0.5, 1.5, N), C_norm_w=rng.uniform(0.5, 1.5, N),
+                  B_bias=0.3 * rng.standard_normal((H, R, N)),
+                  C_bias=0.3 * rng.standard_normal((H, R, N)),
+                  dt_bias=rng.uniform(-1.0, 0.0, H), eps=1e-5)
+    return ins, dy, dh, kw, pm
+
+
+OPTION_GRAD_CASES = [(1, "shuffle", True), (2, "reverse", False), (0, "zero", True),
+                     (1, "native", False), (0, "reverse", True)]
+
+
+@pytest.mark.parametrize("ngroups,phase,premix", OPTION_GRAD_CASES)
+def test_backward_options_forward_matches_c_oracle(ngroups, phase, premix):
+    """The gradient oracle's option maps (group repeat, phase transform,
+    pre-mixer) give the C oracle's forward with the same options."""
+    import torch
+    from oracle.backward import forward_torch
+    rng = np.random.default_rng(34)
+    ins, _, _, kw, pm = _bwd_option_case(rng, ngroups, phase, premix, Bt=2, L=9, H=4, N=8)
+    y_c, h_c, _, _ = oracle.scan(*ins[:7], h0=ins[7], Bprev=ins[8], xprev=ins[9], premix=pm, **kw)
+    tpm = None if pm is None else {k: (v if k == "eps" else torch.tensor(v)) for k, v in pm.items()}
+    y_t, h_t = forward_torch(*[torch.tensor(a) for a in ins], premix=tpm, **kw)
+    assert rel_err(y_t.numpy(), y_c) < 1e-13
+    assert rel_err(h_t.numpy(), h_c) < 1e-13
+
+
+@pytest.mark.parametrize("ngroups,phase,premix", OPTION_GRAD_CASES)
+def test_backward_options_match_finite_differences(ngroups, phase, premix):
+    """Every gradient with options, the pre-mixer's parameters included,
+    against central differences of the C oracle's loss with those options:
+    the group gradients sum over the heads of a group, dtheta follows the
+    phase map back (zero, negated, permuted), and the raw inputs' gradients
+    pass through RMSNorm, softplus and sigmoid."""
+    from oracle.backward import PREMIX_GRADS, scan_backward
+    rng = np.random.default_rng(35 + OPTION_GRAD_CASES.index((ngroups, phase, premix)))
+    ins, dy, dh, kw, pm = _bwd_option_case(rng, ngroups, phase, premix)
+    g = scan_backward(*ins[:7], dy, dh, h0=ins[7], Bprev=ins[8], xprev=ins[9], premix=pm, **kw)
+    pnames = list(PREMIX_GRADS) if pm is not None else []
+    params = [pm[n[1:]] for n in pnames]
+
+    def loss(args, prm):
+        pmx = None if pm is None else dict(zip([n[1:] for n in pnames], prm), eps=pm["eps"])
+        y, hL, _, _ = oracle.scan(*args[:7], h0=args[7], Bprev=args[8], xprev=args[9],
+                                  premix=pmx, **kw)
+        return float(np.sum(y * dy) + np.sum(hL * dh))
+    names = ["dx", "dB", "dC", "ddt", "dA", "dtheta", "dlam", "dh0", "dBprev", "dxprev"]
+    eps = 1e-6
+    for k, name in enumerate(names + pnames):
+        base = ins[k] if k < len(names) else params[k - len(names)]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            plus, minus = [a.copy() for a in ins], [a.copy() for a in ins]
+            pp, pmn = [a.copy() for a in params], [a.copy() for a in params]
+            (plus[k] if k < len(names) else pp[k - len(names)])[idx] += eps
+            (minus[k] if k < len(names) else pmn[k - len(names)])[idx] -= eps
+            fd[idx] = (loss(plus, pp) - loss(minus, pmn)) / (2 * eps)
+        assert g[name].shape == base.shape, name
+        err = np.max(np.abs(fd - g[name])) / max(np.max(np.abs(g[name])), 1e-12)
+        if phase == "zero" and name == "dtheta":
+            assert np.all(g[name] == 0) and np.max(np.abs(fd)) < 1e-8
+            continue
+        assert err < 1e-6, (name, err)
+
+
 # ---------------------------------------------------------------------------
 # Accumulated angle and the write / read phase interventions.
 
