@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define M3_ABI_VERSION 4
+#define M3_ABI_VERSION 5
 
 typedef enum {
     M3_F32 = 0,
@@ -136,8 +136,8 @@ typedef enum {
 } m3_status;
 
 /*
- * Options shared by m3_scan_fwd and m3_decode_step (all zero = the plain
- * mixer).  Pointers are device pointers owned by the caller.
+ * Options shared by m3_scan_fwd and m3_decode_step, a subset of them also by
+ * m3_scan_bwd (all zero = the plain mixer).  Pointers are device pointers owned by the caller.
  *   ngroups      0 = one B and C per head; else a divisor of nheads
  *   A_per_token  0: A is [nheads]; 1: A is [batch, seqlen, nheads] in a scan,
  *                [batch, nheads] in a decode step
@@ -245,8 +245,8 @@ typedef struct {
 } m3_decode_args;
 
 /*
- * Arguments of m3_scan_bwd: the gradient of a scan (m3_scan_fwd without
- * options) for training.  Given dy = dLoss/dy and optionally dh_out =
+ * Arguments of m3_scan_bwd: the gradient of a scan (m3_scan_fwd, with or
+ * without the options below) for training.  Given dy = dLoss/dy and optionally dh_out =
  * dLoss/dh_L, it returns the gradients of Loss = sum(dy * y) + sum(dh_out *
  * h_L) with respect to every input, by one of two methods (see below).
  *   inputs   as m3_scan_args: x, B, C (io dtype), dt, A [nheads], theta, lam
@@ -275,6 +275,27 @@ typedef struct {
  *   M3_BWD_AUTO     chunked where supported, else step by step.
  * A method that does not support the sizes returns M3_ERR_UNSUPPORTED; any
  * other value returns M3_ERR_OPTION.  The methods agree to rounding.
+ * Options (opt, as m3_options for m3_scan_fwd; all zero = the plain mixer):
+ *   ngroups      B, C and dB, dC are [batch, seqlen, ngroups, rank, dstate];
+ *                a group's gradient sums those of its heads
+ *   phase_mode   M3_PHASE_ZERO, _REVERSE or _SHUFFLE: dtheta is the gradient
+ *                with respect to theta as given (zero: theta is not read and
+ *                may be NULL, dtheta may be NULL, else it is zero-filled;
+ *                shuffle: phase_perm must be a permutation -- entries are
+ *                clamped, never checked -- and pair j receives the gradient of
+ *                every pair i with phase_perm[i] = j)
+ *   premix       dt and lam are the raw projections and ddt, dlam, dB, dC the
+ *                gradients with respect to them and to the raw B, C; the
+ *                pre-mixer's parameter gradients go to dB_norm_w, dC_norm_w
+ *                [dstate], dB_bias, dC_bias [nheads, rank, dstate] and
+ *                ddt_bias [nheads], each optional (NULL = not computed; a
+ *                NULL parameter is differentiated at its default, ones or
+ *                zeros).  The state record (B_prev_in) holds the pre-mixed B,
+ *                as m3_scan_fwd writes it, and dB_prev is with respect to it.
+ *   A_per_token, cu_seqlens, phase_in and phase_out are not supported here
+ *   (M3_ERR_UNSUPPORTED), nor the decode-only phase modes (M3_ERR_OPTION).
+ * With options, the inputs are first materialised in the workspace as the
+ * recurrence uses them, and the gradients are mapped back afterwards.
  * Every output is written (no accumulation into the caller's buffers); the
  * result is deterministic.
  */
@@ -292,6 +313,8 @@ typedef struct {
     float *dh_in, *dB_prev, *dx_prev;
     void *workspace;
     size_t workspace_bytes;
+    m3_options opt;
+    float *dB_norm_w, *dC_norm_w, *dB_bias, *dC_bias, *ddt_bias;
 } m3_scan_bwd_args;
 
 /* Chunked prefill: y and (optionally) the state record after the last token.

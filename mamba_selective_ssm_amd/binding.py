@@ -102,7 +102,10 @@ class ScanBwdArgs(ctypes.Structure):
                 ("dx", _vp), ("dB", _vp), ("dC", _vp), ("ddt", _vp), ("dA", _vp),
                 ("dtheta", _vp), ("dlam", _vp),
                 ("dh_in", _vp), ("dB_prev", _vp), ("dx_prev", _vp),
-                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("opt", Options),
+                ("dB_norm_w", _vp), ("dC_norm_w", _vp), ("dB_bias", _vp), ("dC_bias", _vp),
+                ("ddt_bias", _vp)]
 
 
 class M3Error(RuntimeError):
@@ -450,6 +453,7 @@ class ScanGrads(NamedTuple):
     dh_in: Optional[torch.Tensor]
     dB_prev: Optional[torch.Tensor]
     dx_prev: Optional[torch.Tensor]
+    premix: Optional[Premix] = None   # the pre-mixer's parameter gradients (premix set)
 
 
 BWD_METHODS = {"auto": 0, "step": 1, "chunked": 2}
@@ -462,16 +466,20 @@ def m3_scan_bwd_supported(dstate: int, headdim: int, rank: int, io_dtype: int,
 
 
 def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace,
-                 method="auto"):
+                 method="auto", ngroups=0, phase="native", perm=None, premix=None):
     lib = load_library()
     Bt, L, H, R, P = x.shape
     N = B.shape[-1]
+    G = int(ngroups) if ngroups else H
     io = _io_code(x.dtype)
-    for t, n, shp, dt_ in ((x, "x", (Bt, L, H, R, P), x.dtype), (B, "B", (Bt, L, H, R, N), x.dtype),
-                           (C, "C", (Bt, L, H, R, N), x.dtype), (dt, "dt", (Bt, L, H), torch.float32),
+    zero = phase == "zero"
+    for t, n, shp, dt_ in ((x, "x", (Bt, L, H, R, P), x.dtype), (B, "B", (Bt, L, G, R, N), x.dtype),
+                           (C, "C", (Bt, L, G, R, N), x.dtype), (dt, "dt", (Bt, L, H), torch.float32),
                            (lam, "lam", (Bt, L, H), torch.float32),
                            (theta, "theta", (Bt, L, H, N // 2), torch.float32),
                            (A, "A", (H,), torch.float32), (dy, "dy", (Bt, L, H, R, P), x.dtype)):
+        if t is None and n == "theta" and zero:
+            continue
         _check(t, n, shp, dt_)
     if state is not None:
         _check(state.h, "state.h", (Bt, H, N, P), torch.float32)
@@ -479,45 +487,56 @@ def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, wor
         _check(state.x_prev, "state.x_prev", (Bt, H, R, P), x.dtype)
     if dh_out is not None:
         _check(dh_out, "dh_out", (Bt, H, N, P), torch.float32)
+    opt, keep = _options(H, N, R, False, ngroups, phase, perm, premix, x.device)
     f32 = dict(dtype=torch.float32, device=x.device)
+    pg = None
+    if premix is not None:
+        pg = Premix(torch.empty(N, **f32), torch.empty(N, **f32), torch.empty(H, R, N, **f32),
+                    torch.empty(H, R, N, **f32), torch.empty(H, **f32), premix.eps)
     g = ScanGrads(torch.empty(x.shape, **f32), torch.empty(B.shape, **f32),
                   torch.empty(C.shape, **f32), torch.empty(dt.shape, **f32),
-                  torch.empty(A.shape, **f32), torch.empty(theta.shape, **f32),
+                  torch.empty(A.shape, **f32), torch.empty(Bt, L, H, N // 2, **f32),
                   torch.empty(lam.shape, **f32),
                   torch.empty(Bt, H, N, P, **f32) if state_grads else None,
                   torch.empty(Bt, H, R, N, **f32) if state_grads else None,
-                  torch.empty(Bt, H, R, P, **f32) if state_grads else None)
+                  torch.empty(Bt, H, R, P, **f32) if state_grads else None, pg)
     if method not in BWD_METHODS:
         raise ValueError("method must be one of %s" % sorted(BWD_METHODS))
     a = ScanBwdArgs(batch=Bt, seqlen=L, nheads=H, headdim=P, dstate=N, rank=R, io_dtype=io,
-                    method=BWD_METHODS[method], x=_ptr(x), B=_ptr(B), C=_ptr(C), dt=_ptr(dt), A=_ptr(A), theta=_ptr(theta),
-                    lam=_ptr(lam),
+                    method=BWD_METHODS[method], x=_ptr(x), B=_ptr(B), C=_ptr(C), dt=_ptr(dt), A=_ptr(A),
+                    theta=None if zero else _ptr(theta), lam=_ptr(lam),
                     h_in=_ptr(state.h) if state else None,
                     B_prev_in=_ptr(state.B_prev) if state else None,
                     x_prev_in=_ptr(state.x_prev) if state else None,
                     dy=_ptr(dy), dh_out=_ptr(dh_out),
                     dx=_ptr(g.dx), dB=_ptr(g.dB), dC=_ptr(g.dC), ddt=_ptr(g.ddt), dA=_ptr(g.dA),
                     dtheta=_ptr(g.dtheta), dlam=_ptr(g.dlam), dh_in=_ptr(g.dh_in),
-                    dB_prev=_ptr(g.dB_prev), dx_prev=_ptr(g.dx_prev))
+                    dB_prev=_ptr(g.dB_prev), dx_prev=_ptr(g.dx_prev), opt=opt)
+    if pg is not None:
+        a.dB_norm_w, a.dC_norm_w = _ptr(pg.B_norm_w), _ptr(pg.C_norm_w)
+        a.dB_bias, a.dC_bias, a.ddt_bias = _ptr(pg.B_bias), _ptr(pg.C_bias), _ptr(pg.dt_bias)
     need = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(a))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=x.device)
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
-    return a, g, workspace
+    return a, g, workspace, keep
 
 
 def m3_scan_bwd(x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
                 dh_out: Optional[torch.Tensor] = None, *, state_grads: bool = True,
                 workspace: Optional[torch.Tensor] = None, method: str = "auto",
-                stream=None) -> ScanGrads:
-    """Gradients of sum(dy * y) + sum(dh_out * h_L) of m3_scan_fwd (no options)
-    with respect to every input; ``state_grads`` also returns those of the
-    input state record (zero record when ``state`` is None).  ``method``:
-    "chunked" (reverse mode of the chunked form), "step" (adjoint recurrence
-    step by step) or "auto" (chunked where supported)."""
-    a, g, _ = _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace,
-                           method)
+                ngroups: int = 0, phase: str = "native", perm: Optional[torch.Tensor] = None,
+                premix: Optional[Premix] = None, stream=None) -> ScanGrads:
+    """Gradients of sum(dy * y) + sum(dh_out * h_L) of m3_scan_fwd with respect
+    to every input; ``state_grads`` also returns those of the input state
+    record (zero record when ``state`` is None).  ``method``: "chunked"
+    (reverse mode of the chunked form), "step" (adjoint recurrence step by
+    step) or "auto" (chunked where supported).  Options as m3_scan_fwd takes
+    them (head groups, the phase modes of a scan, the pre-mixer); with
+    ``premix`` the result's ``premix`` field holds the parameter gradients."""
+    a, g, _, _keep = _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads,
+                                  workspace, method, ngroups, phase, perm, premix)
     st = load_library().m3_scan_bwd(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_bwd")
@@ -531,9 +550,8 @@ class ScanBwdCall:
                  dh_out: Optional[torch.Tensor] = None, *, state_grads: bool = True,
                  workspace: Optional[torch.Tensor] = None, method: str = "auto"):
         self._keep = (x, B, C, dt, A, theta, lam, dy, state, dh_out)
-        self.args, self.grads, self.workspace = _prepare_bwd(x, B, C, dt, A, theta, lam, dy,
-                                                             state, dh_out, state_grads, workspace,
-                                                             method)
+        self.args, self.grads, self.workspace, self._keep_opt = _prepare_bwd(
+            x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace, method)
         self._ref = ctypes.byref(self.args)
         self._fn = load_library().m3_scan_bwd
 

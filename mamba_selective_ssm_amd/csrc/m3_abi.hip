@@ -202,6 +202,12 @@ struct BwdPlan {
     size_t unit_floats, ck_bytes, scr_bytes, dx_bytes, scal_bytes, dxp_bytes, part_bytes;
     int64_t nc;
     size_t loc_bytes, cs_bytes, st_bytes, chunk_bytes, bh_bytes;
+    size_t core_ws;             // the plain gradient's workspace
+    // Options: the maps around the plain gradient and their workspace, which
+    // follows the plain gradient's.
+    bool opt_bc, opt_scal, opt_theta;
+    int64_t groups;
+    size_t be_bytes, dbe_bytes, se_bytes, te_bytes, q_bytes, sum_bytes;
     size_t ws;
 };
 
@@ -214,7 +220,56 @@ bool bwd_method_ok(int method, int64_t N, int64_t P, int64_t R, int io)
     return m3::bwd_chunked_supported(N, P, R, io) || m3::bwd_supported(N, P, R, io);
 }
 
+m3_status plan_bwd_core(const m3_scan_bwd_args* a, BwdPlan* out);
+
+// The options a gradient call supports (head groups, the phase maps of a scan,
+// the pre-mixer) and the workspace of their maps.
+m3_status plan_bwd_options(const m3_scan_bwd_args* a, BwdPlan* out)
+{
+    const m3_options& o = a->opt;
+    const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
+    const int64_t N = a->dstate, R = a->rank;
+    if (o.A_per_token != 0 || o.cu_seqlens != nullptr || o.phase_in != nullptr || o.phase_out != nullptr)
+        return M3_ERR_UNSUPPORTED;
+    if (o.phase_mode < M3_PHASE_NATIVE || o.phase_mode > M3_PHASE_SHUFFLE) return M3_ERR_OPTION;
+    if (o.ngroups < 0 || (o.ngroups > 0 && H > 0 && H % o.ngroups != 0)) return M3_ERR_OPTION;
+    if (o.premix != 0 && o.premix != 1) return M3_ERR_OPTION;
+    if (o.premix && !(o.norm_eps >= 0.f && o.norm_eps < 3.0e38f)) return M3_ERR_OPTION;
+    const float* pg[] = {a->dB_norm_w, a->dC_norm_w, a->dB_bias, a->dC_bias, a->ddt_bias};
+    for (const float* q : pg)
+        if (q != nullptr && !o.premix) return M3_ERR_OPTION;
+    out->groups = o.ngroups > 0 ? o.ngroups : H;
+    out->opt_bc = o.premix || out->groups != H;
+    out->opt_scal = o.premix != 0;
+    out->opt_theta = o.phase_mode != M3_PHASE_NATIVE;
+    if ((out->opt_bc || out->opt_theta) && N > 256) return M3_ERR_UNSUPPORTED;
+    const size_t tok = (size_t)Bt * L * H, es = (size_t)io_size(a->io_dtype);
+    if (out->opt_bc) {
+        out->be_bytes = round256(tok * R * N * es);
+        out->dbe_bytes = round256(tok * R * N * 4);
+    }
+    if (out->opt_scal) {
+        out->se_bytes = round256(tok * 4);
+        out->q_bytes = round256((size_t)Bt * L * out->groups * R * N * 4);
+        out->sum_bytes = round256(m3::bwd_options_partial_floats(Bt * L, H, out->groups, (int)N,
+                                                                  (int)R) * 4);
+    }
+    if (out->opt_theta) out->te_bytes = round256(tok * (N / 2) * 4);
+    if (Bt * H == 0) return M3_OK;
+    out->ws = out->core_ws + 2 * out->be_bytes + 2 * out->dbe_bytes + 2 * out->se_bytes +
+              2 * out->te_bytes + 2 * out->q_bytes + out->sum_bytes;
+    return M3_OK;
+}
+
 m3_status plan_bwd(const m3_scan_bwd_args* a, BwdPlan* out)
+{
+    const m3_status s = plan_bwd_core(a, out);
+    if (s != M3_OK) return s;
+    out->core_ws = out->ws;
+    return plan_bwd_options(a, out);
+}
+
+m3_status plan_bwd_core(const m3_scan_bwd_args* a, BwdPlan* out)
 {
     if (a == nullptr) return M3_ERR_NULL;
     const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
@@ -294,36 +349,46 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
     const int64_t P = a->headdim, N = a->dstate, R = a->rank;
     const int64_t nbh = Bt * H;
     if (nbh == 0) return M3_OK;
+    m3::OptParams op;
+    const m3_status os = check_options(a->opt, H, N, R, L, &op);
+    if (os != M3_OK) return os;
+    const bool zero_phase = a->opt.phase_mode == M3_PHASE_ZERO;
     const bool st_in = a->h_in || a->B_prev_in || a->x_prev_in;
     const bool st_out = a->dh_in || a->dB_prev || a->dx_prev;
     if (st_in && !(a->h_in && a->B_prev_in && a->x_prev_in)) return M3_ERR_NULL;
     if (st_out && !(a->dh_in && a->dB_prev && a->dx_prev)) return M3_ERR_NULL;
     if (a->A == nullptr || a->dA == nullptr) return M3_ERR_NULL;
-    if (L > 0 && (!a->x || !a->B || !a->C || !a->dt || !a->theta || !a->lam || !a->dy ||
-                  !a->dx || !a->dB || !a->dC || !a->ddt || !a->dtheta || !a->dlam))
+    if (L > 0 && (!a->x || !a->B || !a->C || !a->dt || (!zero_phase && !a->theta) || !a->lam ||
+                  !a->dy || !a->dx || !a->dB || !a->dC || !a->ddt ||
+                  (!zero_phase && !a->dtheta) || !a->dlam))
         return M3_ERR_NULL;
-    const void* ptrs[] = {a->x, a->B, a->C, a->dt, a->A, a->theta, a->lam, a->h_in,
+    const float* theta_in = zero_phase ? nullptr : a->theta;
+    const void* ptrs[] = {a->x, a->B, a->C, a->dt, a->A, theta_in, a->lam, a->h_in,
                           a->B_prev_in, a->x_prev_in, a->dy, a->dh_out, a->dx, a->dB, a->dC,
-                          a->ddt, a->dA, a->dtheta, a->dlam, a->dh_in, a->dB_prev, a->dx_prev};
+                          a->ddt, a->dA, a->dtheta, a->dlam, a->dh_in, a->dB_prev, a->dx_prev,
+                          a->dB_norm_w, a->dC_norm_w, a->dB_bias, a->dC_bias, a->ddt_bias};
     for (const void* q : ptrs)
         if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
     const int e = io_size(a->io_dtype);
-    const int64_t tok = Bt * L * H;
-    const Range in[] = {
-        range_of(a->x, tok * R * P * e),         range_of(a->B, tok * R * N * e),
-        range_of(a->C, tok * R * N * e),         range_of(a->dt, tok * 4),
-        range_of(a->A, H * 4),                   range_of(a->theta, tok * (N / 2) * 4),
+    const int64_t tok = Bt * L * H, tokg = Bt * L * plan.groups;
+    Range in[20] = {
+        range_of(a->x, tok * R * P * e),         range_of(a->B, tokg * R * N * e),
+        range_of(a->C, tokg * R * N * e),        range_of(a->dt, tok * 4),
+        range_of(a->A, H * 4),                   range_of(theta_in, tok * (N / 2) * 4),
         range_of(a->lam, tok * 4),               range_of(a->h_in, nbh * N * P * 4),
         range_of(a->B_prev_in, nbh * R * N * e), range_of(a->x_prev_in, nbh * R * P * e),
         range_of(a->dy, tok * R * P * e),        range_of(a->dh_out, nbh * N * P * 4),
     };
+    option_ranges(a->opt, Bt, H, N, R, in + 12);
     const Range out[] = {
-        range_of(a->dx, tok * R * P * 4),        range_of(a->dB, tok * R * N * 4),
-        range_of(a->dC, tok * R * N * 4),        range_of(a->ddt, tok * 4),
+        range_of(a->dx, tok * R * P * 4),        range_of(a->dB, tokg * R * N * 4),
+        range_of(a->dC, tokg * R * N * 4),       range_of(a->ddt, tok * 4),
         range_of(a->dA, H * 4),                  range_of(a->dtheta, tok * (N / 2) * 4),
         range_of(a->dlam, tok * 4),              range_of(a->dh_in, nbh * N * P * 4),
         range_of(a->dB_prev, nbh * R * N * 4),   range_of(a->dx_prev, nbh * R * P * 4),
-        range_of(a->workspace, (int64_t)plan.ws),
+        range_of(a->dB_norm_w, N * 4),           range_of(a->dC_norm_w, N * 4),
+        range_of(a->dB_bias, H * R * N * 4),     range_of(a->dC_bias, H * R * N * 4),
+        range_of(a->ddt_bias, H * 4),            range_of(a->workspace, (int64_t)plan.ws),
     };
     const int nout = sizeof(out) / sizeof(out[0]);
     for (const Range& o : out)
@@ -334,14 +399,56 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
             if (overlaps(out[i], out[j])) return M3_ERR_ALIAS;
     if (a->workspace == nullptr || a->workspace_bytes < plan.ws) return M3_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0) return M3_ERR_ALIGN;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
 
+    // With options the plain gradient runs on the inputs as the recurrence
+    // uses them (materialised behind its workspace) and writes the gradients
+    // with respect to those there; the option maps carry them back after it.
+    const void *Bx = a->B, *Cx = a->C;
+    const float *dtx = a->dt, *lamx = a->lam, *thx = a->theta;
+    float *dBx = a->dB, *dCx = a->dC, *dthx = a->dtheta;
+    m3::BwdOptParams bo;
+    memset(&bo, 0, sizeof(bo));
+    const bool opts = plan.opt_bc || plan.opt_scal || plan.opt_theta;
+    if (opts) {
+        char* w = static_cast<char*>(a->workspace) + plan.core_ws;
+        auto take = [&w](size_t bytes) { char* q = bytes ? w : nullptr; w += bytes; return q; };
+        bo.B = a->B; bo.C = a->C; bo.dt = a->dt; bo.lam = a->lam; bo.theta = theta_in;
+        bo.opt = op;
+        bo.Be = take(plan.be_bytes);
+        bo.Ce = take(plan.be_bytes);
+        float* dBe = reinterpret_cast<float*>(take(plan.dbe_bytes));
+        float* dCe = reinterpret_cast<float*>(take(plan.dbe_bytes));
+        bo.dBe = dBe; bo.dCe = dCe;
+        bo.dte = reinterpret_cast<float*>(take(plan.se_bytes));
+        bo.lame = reinterpret_cast<float*>(take(plan.se_bytes));
+        bo.thetae = reinterpret_cast<float*>(take(plan.te_bytes));
+        float* dthe = reinterpret_cast<float*>(take(plan.te_bytes));
+        bo.dthetae = dthe;
+        float* qB = reinterpret_cast<float*>(take(plan.q_bytes));
+        float* qC = reinterpret_cast<float*>(take(plan.q_bytes));
+        bo.qB = a->dB_norm_w ? qB : nullptr;
+        bo.qC = a->dC_norm_w ? qC : nullptr;
+        bo.part = reinterpret_cast<float*>(take(plan.sum_bytes));
+        bo.dB = a->dB; bo.dC = a->dC; bo.ddt = a->ddt; bo.dlam = a->dlam; bo.dtheta = a->dtheta;
+        bo.dBw = a->dB_norm_w; bo.dCw = a->dC_norm_w; bo.dBb = a->dB_bias; bo.dCb = a->dC_bias;
+        bo.ddtb = a->ddt_bias;
+        bo.BtL = Bt * L; bo.H = H; bo.G = plan.groups; bo.N = (int)N; bo.R = (int)R;
+        if (plan.opt_bc) { Bx = bo.Be; Cx = bo.Ce; dBx = dBe; dCx = dCe; }
+        if (plan.opt_scal) { dtx = bo.dte; lamx = bo.lame; }
+        if (plan.opt_theta) { thx = bo.thetae; dthx = dthe; }
+        const hipError_t e0 = m3::launch_bwd_options_pre(bo, a->io_dtype, st);
+        if (e0 != hipSuccess) return hip_status(e0);
+    }
+
+    hipError_t err;
     if (plan.method == M3_BWD_CHUNKED) {
         m3::BcParams q;
         memset(&q, 0, sizeof(q));
-        q.x = a->x; q.B = a->B; q.C = a->C; q.dy = a->dy;
-        q.dt = a->dt; q.A = a->A; q.theta = a->theta; q.lam = a->lam;
+        q.x = a->x; q.B = Bx; q.C = Cx; q.dy = a->dy;
+        q.dt = dtx; q.A = a->A; q.theta = thx; q.lam = lamx;
         q.h_in = a->h_in; q.Bp_in = a->B_prev_in; q.xp_in = a->x_prev_in; q.dh_out = a->dh_out;
-        q.dx = a->dx; q.dB = a->dB; q.dC = a->dC; q.ddt = a->ddt; q.dtheta = a->dtheta;
+        q.dx = a->dx; q.dB = dBx; q.dC = dCx; q.ddt = a->ddt; q.dtheta = dthx;
         q.dlam = a->dlam; q.dh_in = a->dh_in; q.dBp = a->dB_prev; q.dxp = a->dx_prev; q.dA = a->dA;
         char* w = static_cast<char*>(a->workspace);
         q.loc = w;
@@ -360,34 +467,36 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         q.L = L; q.H = H; q.N = (int)N; q.P = (int)P; q.R = (int)R;
         q.nbh = (int)nbh;
         q.nc = (int)plan.nc;
-        return hip_status(m3::launch_bwd_chunked(q, a->io_dtype, static_cast<hipStream_t>(stream)));
+        err = m3::launch_bwd_chunked(q, a->io_dtype, st);
+    } else {
+        m3::BwdParams p;
+        memset(&p, 0, sizeof(p));
+        p.x = a->x; p.B = Bx; p.C = Cx; p.dy = a->dy;
+        p.dt = dtx; p.A = a->A; p.theta = thx; p.lam = lamx;
+        p.h_in = a->h_in; p.Bp_in = a->B_prev_in; p.xp_in = a->x_prev_in; p.dh_out = a->dh_out;
+        p.dx = a->dx; p.dB = dBx; p.dC = dCx; p.ddt = a->ddt; p.dtheta = dthx;
+        p.dlam = a->dlam; p.dh_in = a->dh_in; p.dBp = a->dB_prev; p.dxp = a->dx_prev;
+        char* ws = static_cast<char*>(a->workspace);
+        p.ckpt = reinterpret_cast<float*>(ws);
+        ws += plan.ck_bytes;
+        p.scr = reinterpret_cast<float*>(ws);
+        ws += plan.scr_bytes;
+        p.dx_part = reinterpret_cast<float*>(ws);
+        ws += plan.dx_bytes;
+        p.scal = reinterpret_cast<float*>(ws);
+        ws += plan.scal_bytes;
+        p.dxprev_part = reinterpret_cast<float*>(ws);
+        ws += plan.dxp_bytes;
+        p.dA_part = reinterpret_cast<float*>(ws);
+        p.L = L; p.H = H; p.N = (int)N; p.P = (int)P; p.R = (int)R;
+        p.ntok = Bt * L * H;
+        p.nbh = (int)nbh;
+        p.parts = plan.parts;
+        p.TB = plan.TB; p.K = plan.K;
+        err = m3::launch_bwd(p, a->io_dtype, a->dA, st);
     }
-
-    m3::BwdParams p;
-    memset(&p, 0, sizeof(p));
-    p.x = a->x; p.B = a->B; p.C = a->C; p.dy = a->dy;
-    p.dt = a->dt; p.A = a->A; p.theta = a->theta; p.lam = a->lam;
-    p.h_in = a->h_in; p.Bp_in = a->B_prev_in; p.xp_in = a->x_prev_in; p.dh_out = a->dh_out;
-    p.dx = a->dx; p.dB = a->dB; p.dC = a->dC; p.ddt = a->ddt; p.dtheta = a->dtheta;
-    p.dlam = a->dlam; p.dh_in = a->dh_in; p.dBp = a->dB_prev; p.dxp = a->dx_prev;
-    char* ws = static_cast<char*>(a->workspace);
-    p.ckpt = reinterpret_cast<float*>(ws);
-    ws += plan.ck_bytes;
-    p.scr = reinterpret_cast<float*>(ws);
-    ws += plan.scr_bytes;
-    p.dx_part = reinterpret_cast<float*>(ws);
-    ws += plan.dx_bytes;
-    p.scal = reinterpret_cast<float*>(ws);
-    ws += plan.scal_bytes;
-    p.dxprev_part = reinterpret_cast<float*>(ws);
-    ws += plan.dxp_bytes;
-    p.dA_part = reinterpret_cast<float*>(ws);
-    p.L = L; p.H = H; p.N = (int)N; p.P = (int)P; p.R = (int)R;
-    p.ntok = Bt * L * H;
-    p.nbh = (int)nbh;
-    p.parts = plan.parts;
-    p.TB = plan.TB; p.K = plan.K;
-    return hip_status(m3::launch_bwd(p, a->io_dtype, a->dA, static_cast<hipStream_t>(stream)));
+    if (err != hipSuccess || !opts) return hip_status(err);
+    return hip_status(m3::launch_bwd_options_post(bo, a->io_dtype, st));
 }
 
 

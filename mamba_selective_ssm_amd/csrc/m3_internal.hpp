@@ -93,6 +93,33 @@ bool bwd_chunked_supported(int64_t N, int64_t P, int64_t R, int io_dtype);
 int bwd_chunk_tokens(int64_t R);
 hipError_t launch_bwd_chunked(const BcParams& p, int io_dtype, hipStream_t stream);
 
+// Options of the scan gradient, as maps around the plain gradient: the
+// inputs materialised as the recurrence uses them before it (B, C repeated
+// per head and pre-mixed, theta after the phase map, dt and lam through
+// softplus and sigmoid), the gradients carried back to the caller's inputs
+// and the pre-mixer's parameters after it.
+struct BwdOptParams {
+    const void *B, *C;             // caller's [B*L*G*R][N] io type
+    const float *dt, *lam, *theta; // caller's (raw with the pre-mixer)
+    OptParams opt;
+    void *Be, *Ce;                 // [B*L*H*R][N] io type (groups or pre-mixer)
+    float *dte, *lame;             // [B*L*H] (pre-mixer)
+    float *thetae;                 // [B*L*H][N/2] (phase map)
+    const float *dBe, *dCe;        // gradients with respect to Be, Ce
+    const float *dthetae;          // gradient with respect to thetae
+    float *dB, *dC;                // caller's [B*L*G*R][N]
+    float *ddt, *dlam;             // caller's, mapped in place (pre-mixer)
+    float *dtheta;                 // caller's or NULL
+    float *dBw, *dCw, *dBb, *dCb, *ddtb;   // parameter gradients or NULL
+    float *qB, *qC;                // [B*L*G*R][N] per-row gain terms (workspace)
+    float *part;                   // column-sum partials (workspace)
+    int64_t BtL, H, G;
+    int N, R;
+};
+size_t bwd_options_partial_floats(int64_t BtL, int64_t H, int64_t G, int N, int R);
+hipError_t launch_bwd_options_pre(const BwdOptParams& p, int io_dtype, hipStream_t stream);
+hipError_t launch_bwd_options_post(const BwdOptParams& p, int io_dtype, hipStream_t stream);
+
 // Accumulated rotation angle of a scan: per (row, head, 64-token block) the
 // float64 partial sums of dt theta per pair into `part`, then per (row, head,
 // pair) their sum in block order plus phase_in, reduced into [-pi, pi).

@@ -116,6 +116,23 @@ def bwd_args(**kw):
     (dict(method=2, dstate=48), -3),                       # chunked: dstate 32, 64, 128
     (dict(method=2, dstate=128, io_dtype=0), -3),          # chunked float32: dstate <= 64
     (dict(method=1, headdim=128), -3),
+    # options of the gradient
+    (dict(opt=binding.Options(A_per_token=1)), -3),          # per-token decay: not supported
+    (dict(opt=binding.Options(max_seqlen=4, cu_seqlens=FAKE + (23 << 32))), -3),
+    (dict(opt=binding.Options(phase_out=FAKE + (23 << 32))), -3),
+    (dict(opt=binding.Options(phase_mode=4)), -9),           # decode-only phase mode
+    (dict(opt=binding.Options(phase_mode=7)), -9),
+    (dict(opt=binding.Options(ngroups=2)), -9),              # 3 heads
+    (dict(opt=binding.Options(ngroups=-1)), -9),
+    (dict(opt=binding.Options(phase_mode=3)), -1),           # shuffle without a permutation
+    (dict(opt=binding.Options(phase_mode=1), theta=None, dtheta=None, dx=None), -1),
+    (dict(theta=None), -1),                                  # theta needed unless zeroed
+    (dict(opt=binding.Options(premix=1, norm_eps=-1.0)), -9),
+    (dict(opt=binding.Options(premix=2)), -9),
+    (dict(dB_norm_w=FAKE + (22 << 32)), -9),                 # parameter gradient without premix
+    (dict(opt=binding.Options(premix=1), dB_bias=FAKE + (10 << 32)), -7),   # overlaps dC
+    (dict(opt=binding.Options(premix=1), ddt_bias=FAKE + (22 << 32) + 4), -5),
+    (dict(opt=binding.Options(premix=1, B_norm_w=FAKE + (24 << 32)), dx=FAKE + (24 << 32)), -7),
 ])
 def test_bwd_validation_codes(lib, kw, code):
     assert lib.m3_scan_bwd(ctypes.byref(bwd_args(**kw)), None) == code
@@ -146,8 +163,26 @@ def test_bwd_supported_and_workspace(lib):
     assert lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(method=5))) == 0
 
 
+def test_bwd_option_workspace(lib):
+    """The option maps' buffers follow the plain gradient's workspace: the
+    pre-mixer and head groups add the materialised B, C and their gradients,
+    the phase maps theta and its gradient; rejected options size nothing."""
+    ws = lambda **kw: lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(seqlen=256, **kw)))
+    plain = ws()
+    tok, N, R = 2 * 256 * 3, 64, 1
+    assert ws(opt=binding.Options(phase_mode=2)) >= plain + 2 * tok * (N // 2) * 4
+    assert ws(opt=binding.Options(ngroups=1)) >= plain + tok * R * N * (2 * 2 + 2 * 4)
+    assert ws(opt=binding.Options(premix=1)) > ws(opt=binding.Options(ngroups=1))
+    assert ws(opt=binding.Options(ngroups=3)) == plain          # one group per head
+    assert ws(opt=binding.Options(A_per_token=1)) == 0
+    assert ws(opt=binding.Options(phase_mode=5)) == 0
+    assert lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(batch=0))) == 0
+    assert lib.m3_scan_bwd_workspace_bytes(
+        ctypes.byref(bwd_args(batch=0, opt=binding.Options(premix=1)))) == 0
+
+
 def test_version_and_status_strings(lib):
-    assert lib.m3_abi_version() == 4
+    assert lib.m3_abi_version() == 5
     for code in range(-9, 1):
         s = lib.m3_status_string(code)
         assert s and s != b"unknown status"

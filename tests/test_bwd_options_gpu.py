@@ -1,0 +1,151 @@
+"""Parity of m3_scan_bwd with options -- head groups, the phase modes of a
+scan (theta zeroed, negated, shuffled) and the pre-mixer (RMSNorm + biases on
+B and C, softplus and sigmoid of the raw step and weight) -- against the fp64
+gradient oracle with the same options, by both methods.  With the pre-mixer
+the gradients are those of the raw inputs, plus the parameter gradients
+dB_norm_w, dC_norm_w, dB_bias, dC_bias and ddt_bias.
+
+Metric as for the plain gradient: max |got - ref| / max |ref| per tensor,
+tolerance 1e-4 for float32 inputs, 2e-2 for bfloat16; dA and ddt_bias, which
+sum per-token terms over batch and tokens, against the sum of the terms'
+magnitudes (for ddt_bias: sum over (b, t) of |ddt_raw| of the head).
+"""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import test_bwd_gpu as bwd
+import test_options_gpu as opt
+from oracle.backward import PREMIX_GRADS, scan_backward
+from mamba_selective_ssm_amd import State, m3_scan_bwd, synth
+from helpers import TOL, f64, random_state, rel_err, say, workload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def option_grads_case(w, seed, ngroups=0, phase="native", premix=False, with_state=True,
+                      with_dh=True, method="auto", label=""):
+    say("case %s [%s]: B%d L%d H%d R%d P%d N%d %s groups=%d phase=%s premix=%s state=%s seed=%d"
+        % (label, method, w.batch, w.seqlen, w.heads, w.rank, w.headdim, w.dstate, w.io_dtype,
+           ngroups, phase, premix, with_state, seed))
+    inp, ex = synth.make_option_inputs(w, seed, DEV, ngroups=ngroups, phase=phase, premix=premix)
+    g = torch.Generator(device=DEV).manual_seed(seed + 1)
+    dy = torch.randn(inp["x"].shape, generator=g, device=DEV).to(w.torch_dtype)
+    dh = torch.randn(w.batch, w.heads, w.dstate, w.headdim, generator=g, device=DEV) if with_dh else None
+    st = random_state(w, seed + 2, DEV) if with_state else None
+    theta = None if phase == "zero" else inp["theta"]
+    got = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], theta, inp["lam"], dy,
+                      State(*st) if st else None, dh, method=method, ngroups=ngroups, phase=phase,
+                      perm=ex.get("perm"), premix=opt.premix_obj(ex))
+    torch.cuda.synchronize()
+    ref = scan_backward(f64(inp["x"]), f64(inp["B"]), f64(inp["C"]), f64(inp["dt"]),
+                        f64(inp["A"]), f64(inp["theta"]), f64(inp["lam"]), f64(dy),
+                        None if dh is None else f64(dh),
+                        h0=None if st is None else f64(st[0]),
+                        Bprev=None if st is None else f64(st[1]),
+                        xprev=None if st is None else f64(st[2]),
+                        **opt.oracle_kw(ex, ngroups, phase))
+    tol = TOL[w.io_dtype]
+    errs = {}
+    for n in bwd.NAMES:
+        if n == "dA":
+            errs[n] = float(np.max(np.abs(f64(got.dA) - ref["dA"])) / max(np.max(ref["dA_scale"]), 1e-300))
+        else:
+            errs[n] = rel_err(f64(getattr(got, n)), ref[bwd.ORACLE.get(n, n)])
+    if premix:
+        for n in PREMIX_GRADS:
+            gv = f64(getattr(got.premix, n[1:]))
+            if n == "ddt_bias":
+                scale = np.abs(ref["ddt"]).sum(axis=(0, 1))
+                errs[n] = float(np.max(np.abs(gv - ref[n])) / max(np.max(scale), 1e-300))
+            else:
+                errs[n] = rel_err(gv, ref[n])
+    if phase == "zero":
+        assert torch.count_nonzero(got.dtheta) == 0
+    say("   " + "  ".join("%s %.2e" % (n, e) for n, e in errs.items()) + "  (tol %.0e)" % tol)
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, bad
+    return got
+
+
+COMBOS = [(2, "native", False), (0, "reverse", False), (0, "shuffle", False), (0, "zero", False),
+          (0, "native", True), (2, "shuffle", True), (1, "zero", True), (4, "reverse", True)]
+
+
+@pytest.mark.parametrize("method", ["step", "chunked"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("ngroups,phase,premix", COMBOS)
+def test_bwd_options(ngroups, phase, premix, io, method):
+    """Several chunks (32 tokens at rank 2) and checkpoints, ragged tail."""
+    w = workload(2, 70, 4, 2, 32, 64, io=io, dt_mu=-1.0, theta="uniform_pi")
+    option_grads_case(w, 1200 + 10 * COMBOS.index((ngroups, phase, premix)) + (io == "bf16"),
+                      ngroups, phase, premix, method=method, label="bwd-options")
+
+
+@pytest.mark.parametrize("method", ["step", "chunked"])
+def test_bwd_options_longer_dstate128(method):
+    """bf16, dstate 128, rank 4 (16-token chunks), 300 tokens, head groups,
+    shuffled phases and the pre-mixer together."""
+    w = workload(1, 300, 4, 4, 64, 128, io="bf16", dt_mu=-2.0)
+    option_grads_case(w, 1300, 2, "shuffle", True, method=method, label="bwd-options-long")
+
+
+def test_bwd_options_without_state_or_final_gradient():
+    w = workload(2, 40, 2, 1, 64, 64, io="f32", dt_mu=-1.0)
+    option_grads_case(w, 1310, 1, "reverse", True, with_state=False, with_dh=False,
+                      label="bwd-options-plain")
+
+
+def test_bwd_options_empty_sequence():
+    """seqlen 0: the state-record gradients pass through, the parameter
+    gradients are zero."""
+    w = workload(2, 0, 2, 1, 32, 32, io="f32", dt_mu=-1.0)
+    got = option_grads_case(w, 1320, 1, "shuffle", True, label="bwd-options-empty")
+    for n in PREMIX_GRADS:
+        assert torch.count_nonzero(getattr(got.premix, n[1:])) == 0, n
+
+
+@pytest.mark.parametrize("method", ["step", "chunked"])
+def test_bwd_options_deterministic(method):
+    w = workload(2, 90, 4, 2, 64, 128, io="bf16")
+    inp, ex = synth.make_option_inputs(w, 1330, DEV, ngroups=2, phase="shuffle", premix=True)
+    dy = torch.randn(inp["x"].shape, device=DEV,
+                     generator=torch.Generator(device=DEV).manual_seed(2)).to(torch.bfloat16)
+    run = lambda: m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
+                              inp["lam"], dy, method=method, ngroups=2, phase="shuffle",
+                              perm=ex["perm"], premix=opt.premix_obj(ex))
+    a, b = run(), run()
+    torch.cuda.synchronize()
+    for n in bwd.NAMES:
+        assert torch.equal(getattr(a, n), getattr(b, n)), n
+    for n in PREMIX_GRADS:
+        assert torch.equal(getattr(a.premix, n[1:]), getattr(b.premix, n[1:])), n
+
+
+def draw_bwd_options(case):
+    rnd = random.Random(9850 + case)
+    N, P, R = rnd.choice([(16, 16, 1), (32, 32, 2), (32, 64, 4), (64, 32, 1), (64, 64, 2),
+                          (128, 64, 1), (128, 32, 4), (64, 16, 2)])
+    H = rnd.choice([1, 2, 3, 4, 6])
+    return dict(N=N, P=P, R=R, io=rnd.choice(["f32", "bf16"]), L=rnd.randint(1, 140),
+                Bt=rnd.randint(1, 2), H=H,
+                groups=rnd.choice([0] + [g for g in (1, 2, 3) if H % g == 0 and g < H]),
+                phase=rnd.choice(["native", "zero", "reverse", "shuffle"]),
+                premix=rnd.random() < 0.5, with_state=rnd.random() < 0.7,
+                dt_mu=rnd.choice([-2.0, -1.0, 0.0]))
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_bwd_options_case(case):
+    """Seeded random shapes and option combinations, both methods where the
+    chunked one supports the shape."""
+    c = draw_bwd_options(case)
+    w = workload(c["Bt"], c["L"], c["H"], c["R"], c["P"], c["N"], io=c["io"], dt_mu=c["dt_mu"],
+                 theta="uniform_pi")
+    methods = ["step"] + (["chunked"] if bwd.chunked_ok(c["io"], c["N"], c["P"], c["R"]) else [])
+    for m in methods:
+        option_grads_case(w, 9950 + case, c["groups"], c["phase"], c["premix"],
+                          with_state=c["with_state"], method=m, label="random bwd options %d" % case)
