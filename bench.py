@@ -54,13 +54,18 @@ def scan_algorithmic_bytes(w, L=None, ngroups=0, a_tok=False, phase="native", pr
     return w.batch * (L * (H * per_tok + G * per_grp_tok) + H * per_bh) + extra
 
 
-def bwd_algorithmic_bytes(w):
+def bwd_algorithmic_bytes(w, ngroups=0, premix=False):
     """One m3_scan_bwd: x, B, C, dy, dt, theta, lam read once; dx, dB, dC,
-    ddt, dtheta, dlam written once in float32 (checkpoint traffic excluded)."""
+    ddt, dtheta, dlam written once in float32 (checkpoint traffic excluded).
+    With head groups B, C and their gradients are per group; the pre-mixer
+    adds its parameters read and their gradients written."""
     e = io_bytes(w)
     R, P, N, H = w.rank, w.headdim, w.dstate, w.heads
-    per_tok = e * (2 * R * P + 2 * R * N) + 4 * (N // 2 + 2) + 4 * (R * P + 2 * R * N + N // 2 + 2)
-    return w.batch * w.seqlen * H * per_tok + 8 * H
+    G = ngroups or H
+    per_head_tok = e * 2 * R * P + 4 * (N // 2 + 2) + 4 * (R * P + N // 2 + 2)
+    per_grp_tok = e * 2 * R * N + 4 * 2 * R * N
+    extra = 2 * 4 * (2 * N + 2 * H * R * N + H) if premix else 0
+    return w.batch * w.seqlen * (H * per_head_tok + G * per_grp_tok) + 8 * H + extra
 
 
 def decode_algorithmic_bytes(w, premix=False):
@@ -238,16 +243,21 @@ def bench_prefill_options(w, opts, steps, warmup, torch, m3, synth, seed=1002):
                 gbs=nbytes / (kms * 1e-3) / 1e9)
 
 
-def bench_backward(w, steps, warmup, torch, m3, synth, seed=1003, method="auto"):
+def bench_backward(w, steps, warmup, torch, m3, synth, seed=1003, method="auto", ngroups=0,
+                   phase="native", premix=False):
     """One m3_scan_bwd call per step on resident inputs and dy ("auto" picks
-    the chunked method where it is supported)."""
-    inp = synth.make_scan_inputs(w, seed, "cuda")
+    the chunked method where it is supported), optionally with head groups, a
+    phase mode and the pre-mixer."""
+    inp, ex = synth.make_option_inputs(w, seed, "cuda", ngroups=ngroups, phase=phase,
+                                       premix=premix)
     g = torch.Generator(device="cuda").manual_seed(seed)
     dy = torch.randn(inp["x"].shape, generator=g, device="cuda").to(w.torch_dtype)
     step = m3.ScanBwdCall(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
-                          inp["lam"], dy, state_grads=False, method=method)
+                          inp["lam"], dy, state_grads=False, method=method, ngroups=ngroups,
+                          phase=phase, perm=ex.get("perm"),
+                          premix=_premix(m3, ex) if premix else None)
     total, kms = time_launches(step, steps, warmup, torch)
-    nbytes = bwd_algorithmic_bytes(w)
+    nbytes = bwd_algorithmic_bytes(w, ngroups=ngroups, premix=premix)
     return dict(tokens_per_s=w.batch * w.seqlen * steps / total, kernel_ms=kms, bytes=nbytes,
                 gbs=nbytes / (kms * 1e-3) / 1e9)
 
@@ -319,6 +329,18 @@ def backward_lines(steps, torch, m3, synth):
                                      "hbm_gbs": round(rb["gbs"], 1),
                                      "hbm_frac": round(rb["gbs"] / HBM_PEAK_GBS, 4)}
             torch.cuda.empty_cache()
+    # the option maps around the chunked gradient: 8 head groups of 2, shuffled
+    # phases and the pre-mixer
+    w = synth.WORKLOADS["prefill_bf16"]
+    progress("timing the chunked backward with options on prefill_bf16")
+    rb = bench_backward(w, min(steps, 10), 1, torch, m3, synth, method="chunked",
+                        ngroups=w.heads // 2, phase="shuffle", premix=True)
+    sec["backward_options:prefill_bf16"] = {"tokens_per_s": round(rb["tokens_per_s"], 1),
+                                            "kernel_ms": round(rb["kernel_ms"], 4),
+                                            "hbm_gbs": round(rb["gbs"], 1),
+                                            "hbm_frac": round(rb["gbs"] / HBM_PEAK_GBS, 4),
+                                            "options": "ngroups=8 phase=shuffle premix"}
+    torch.cuda.empty_cache()
     return sec
 
 

@@ -548,10 +548,13 @@ class ScanBwdCall:
 
     def __init__(self, x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
                  dh_out: Optional[torch.Tensor] = None, *, state_grads: bool = True,
-                 workspace: Optional[torch.Tensor] = None, method: str = "auto"):
+                 workspace: Optional[torch.Tensor] = None, method: str = "auto",
+                 ngroups: int = 0, phase: str = "native", perm: Optional[torch.Tensor] = None,
+                 premix: Optional[Premix] = None):
         self._keep = (x, B, C, dt, A, theta, lam, dy, state, dh_out)
         self.args, self.grads, self.workspace, self._keep_opt = _prepare_bwd(
-            x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace, method)
+            x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace, method,
+            ngroups, phase, perm, premix)
         self._ref = ctypes.byref(self.args)
         self._fn = load_library().m3_scan_bwd
 

@@ -242,7 +242,8 @@ m3_status plan_bwd_options(const m3_scan_bwd_args* a, BwdPlan* out)
     out->opt_bc = o.premix || out->groups != H;
     out->opt_scal = o.premix != 0;
     out->opt_theta = o.phase_mode != M3_PHASE_NATIVE;
-    if ((out->opt_bc || out->opt_theta) && N > 256) return M3_ERR_UNSUPPORTED;
+    // the option maps move rows of dstate values 4 at a time, pairs through LDS
+    if ((out->opt_bc || out->opt_theta) && (N > 256 || N % 4 != 0)) return M3_ERR_UNSUPPORTED;
     const size_t tok = (size_t)Bt * L * H, es = (size_t)io_size(a->io_dtype);
     if (out->opt_bc) {
         out->be_bytes = round256(tok * R * N * es);
@@ -250,14 +251,14 @@ m3_status plan_bwd_options(const m3_scan_bwd_args* a, BwdPlan* out)
     }
     if (out->opt_scal) {
         out->se_bytes = round256(tok * 4);
-        out->q_bytes = round256((size_t)Bt * L * out->groups * R * N * 4);
+        out->q_bytes = round256(m3::bwd_options_gain_floats(Bt * L, out->groups, (int)N, (int)R) * 4);
         out->sum_bytes = round256(m3::bwd_options_partial_floats(Bt * L, H, out->groups, (int)N,
                                                                   (int)R) * 4);
     }
     if (out->opt_theta) out->te_bytes = round256(tok * (N / 2) * 4);
     if (Bt * H == 0) return M3_OK;
     out->ws = out->core_ws + 2 * out->be_bytes + 2 * out->dbe_bytes + 2 * out->se_bytes +
-              2 * out->te_bytes + 2 * out->q_bytes + out->sum_bytes;
+              2 * out->te_bytes + out->q_bytes + out->sum_bytes;
     return M3_OK;
 }
 
@@ -425,10 +426,7 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         bo.thetae = reinterpret_cast<float*>(take(plan.te_bytes));
         float* dthe = reinterpret_cast<float*>(take(plan.te_bytes));
         bo.dthetae = dthe;
-        float* qB = reinterpret_cast<float*>(take(plan.q_bytes));
-        float* qC = reinterpret_cast<float*>(take(plan.q_bytes));
-        bo.qB = a->dB_norm_w ? qB : nullptr;
-        bo.qC = a->dC_norm_w ? qC : nullptr;
+        bo.qpart = reinterpret_cast<float*>(take(plan.q_bytes));
         bo.part = reinterpret_cast<float*>(take(plan.sum_bytes));
         bo.dB = a->dB; bo.dC = a->dC; bo.ddt = a->ddt; bo.dlam = a->dlam; bo.dtheta = a->dtheta;
         bo.dBw = a->dB_norm_w; bo.dCw = a->dC_norm_w; bo.dBb = a->dB_bias; bo.dCb = a->dC_bias;

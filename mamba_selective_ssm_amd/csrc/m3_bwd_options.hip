@@ -19,9 +19,12 @@
 // (RMSNorm with gains and channel biases on B and C); the phase maps follow
 // "Understanding Mamba-3 Through Oscillatory Dynamics", section 5.3.
 //
-// Every kernel here is bound by HBM bytes and runs once per call.  Sums over
-// tokens are column sums in two fixed-order stages (partials per block of
-// rows, then the partials in block order): the result is deterministic.
+// Every kernel here is bound by HBM bytes and runs once per call.  Rows of
+// dstate values are processed by groups of lanes, 4 consecutive entries per
+// lane (LPR = the power of two >= dstate/4 lanes per row, 64/LPR rows per wave
+// at once).  Sums over tokens run in two fixed-order stages (partials per
+// block of rows, then the partials in block order): the result is
+// deterministic.
 #include "m3scan.h"
 
 #include "m3_device.hpp"
@@ -31,15 +34,40 @@ namespace m3 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = kThreads / 64;   // one wave per row of dstate values
-constexpr int kMaxNK = 4;                      // dstate <= 256: 4 values per lane
+constexpr int kWaves = kThreads / 64;
 constexpr int kMaxPairs = 128;
+constexpr int kMaxBlocks = 2048;     // grid-stride kernels: enough to fill 256 CUs
+constexpr int kFinalLanes = 16;      // partial lanes per column in the final sum
 
-__device__ __forceinline__ float wave_sum(float v)
+__device__ __forceinline__ void ld4(const float* p, float (&v)[4])
 {
-    // butterfly: every lane ends with the same value (each step adds a
-    // commutative pair)
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+__device__ __forceinline__ void ld4(const bf16* p, float (&v)[4])
+{
+    const bf16x4 t = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (float)t[i];
+}
+__device__ __forceinline__ void st4(float* p, const float (&v)[4])
+{
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st4(bf16* p, const float (&v)[4])
+{
+    bf16x4 t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x4*>(p) = t;
+}
+
+// Sum over the aligned group of `lpr` lanes (a power of two); every lane of
+// the group ends with the same value (each butterfly step adds a commutative
+// pair).
+__device__ __forceinline__ float group_sum(float v, int lpr)
+{
+    for (int off = lpr >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;
 }
 
@@ -53,6 +81,23 @@ __device__ __forceinline__ float sigmoid_acc(float z)
     const float e = expf(-fabsf(z));
     return z >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
 }
+
+__device__ __forceinline__ int clamp_pair(int s, int npr) { return s < 0 ? 0 : (s >= npr ? npr - 1 : s); }
+
+// Lane layout of the row kernels.
+struct RowLanes {
+    int lpr, sub, c;       // lanes per row, row within the wave's group, first entry
+    int64_t stride;        // rows advanced per grid-stride iteration
+    __device__ RowLanes(int N, int lane)
+    {
+        lpr = 1;
+        while (lpr * 4 < N) lpr <<= 1;
+        sub = lane / lpr;
+        c = (lane % lpr) * 4;
+        stride = (int64_t)gridDim.x * kWaves * (64 / lpr);
+    }
+    __device__ int64_t first(int wave) const { return ((int64_t)blockIdx.x * kWaves + wave) * (64 / lpr); }
+};
 
 struct RowIdx {
     int64_t bt, g;
@@ -68,51 +113,49 @@ __device__ __forceinline__ RowIdx row_index(const BwdOptParams& p, int64_t row)
     return i;
 }
 
-// The row's dstate values (zero past N) and its RMS scale r (1 without the
-// pre-mixer).
-template <typename IO>
-__device__ __forceinline__ float load_row(const IO* src, int N, int lane, float eps, bool norm,
-                                          float (&v)[kMaxNK])
+__device__ __forceinline__ void gain4(const float* w, int c, bool ok, float (&wv)[4])
 {
-    float ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMaxNK; ++k) {
-        const int n = lane + 64 * k;
-        v[k] = n < N ? to_f32(src[n]) : 0.f;
-        ss += v[k] * v[k];
-    }
-    if (!norm) return 1.f;
-    return rsqrtf(wave_sum(ss) / (float)N + eps);
+    if (w != nullptr && ok) ld4(w + c, wv);
+    else wv[0] = wv[1] = wv[2] = wv[3] = 1.f;
 }
 
-// B' and C' for every head: one wave per (token, group, rank) row; blockIdx.y
-// picks B (0) or C (1).
+// B' and C' for every head of a row's group: rows are (token, group, rank);
+// blockIdx.y picks B (0) or C (1).
 template <typename IO>
 __global__ void __launch_bounds__(kThreads) bo_prep_bc_kernel(BwdOptParams p)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (row >= p.BtL * p.G * p.R) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const RowLanes rl(p.N, lane);
     const bool isC = blockIdx.y != 0;
-    const IO* src = static_cast<const IO*>(isC ? p.C : p.B) + row * p.N;
+    const IO* src = static_cast<const IO*>(isC ? p.C : p.B);
     IO* dst = static_cast<IO*>(isC ? p.Ce : p.Be);
-    const float* w = isC ? p.opt.Cw : p.opt.Bw;
     const float* bias = isC ? p.opt.Cb : p.opt.Bb;
-    const RowIdx ri = row_index(p, row);
-    float v[kMaxNK];
-    const float sc = load_row(src, p.N, lane, p.opt.eps, p.opt.premix != 0, v);
-    const int64_t hpg = p.H / p.G;
-    for (int64_t j = 0; j < hpg; ++j) {
-        const int64_t h = ri.g * hpg + j;
-        IO* out = dst + ((ri.bt * p.H + h) * p.R + ri.r) * p.N;
-        const float* bh = bias ? bias + (h * p.R + ri.r) * p.N : nullptr;
+    const bool colok = rl.c < p.N;
+    float wv[4];
+    gain4(isC ? p.opt.Cw : p.opt.Bw, rl.c, colok, wv);
+    const int64_t rows = p.BtL * p.G * p.R, hpg = p.H / p.G;
+    for (int64_t r0 = rl.first(wave); r0 < rows; r0 += rl.stride) {
+        const int64_t row = r0 + rl.sub;
+        const bool ok = colok && row < rows;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (ok) ld4(src + row * p.N + rl.c, v);
+        float sc = 1.f;
+        if (p.opt.premix) {
+            const float ss = group_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3], rl.lpr);
+            sc = rsqrtf(ss / (float)p.N + p.opt.eps);
+        }
+        if (!ok) continue;
+        const RowIdx ri = row_index(p, row);
+        for (int64_t j = 0; j < hpg; ++j) {
+            const int64_t h = ri.g * hpg + j;
+            float o[4] = {v[0], v[1], v[2], v[3]};
+            if (p.opt.premix) {
+                float b[4] = {0.f, 0.f, 0.f, 0.f};
+                if (bias) ld4(bias + (h * p.R + ri.r) * p.N + rl.c, b);
 #pragma unroll
-        for (int k = 0; k < kMaxNK; ++k) {
-            const int n = lane + 64 * k;
-            if (n >= p.N) continue;
-            float o = v[k];
-            if (p.opt.premix) o = v[k] * sc * (w ? w[n] : 1.f) + (bh ? bh[n] : 0.f);
-            out[n] = from_f32<IO>(o);
+                for (int i = 0; i < 4; ++i) o[i] = v[i] * sc * wv[i] + b[i];
+            }
+            st4(dst + ((ri.bt * p.H + h) * p.R + ri.r) * p.N + rl.c, o);
         }
     }
 }
@@ -129,74 +172,93 @@ __global__ void __launch_bounds__(kThreads) bo_prep_scalar_kernel(BwdOptParams p
     }
 }
 
-__device__ __forceinline__ int clamp_pair(int s, int npr) { return s < 0 ? 0 : (s >= npr ? npr - 1 : s); }
-
 // theta after the phase map (zero mode: theta is not read).
 __global__ void __launch_bounds__(kThreads) bo_prep_theta_kernel(BwdOptParams p)
 {
+    __shared__ int sperm[kMaxPairs];
     const int npr = p.N / 2;
+    const bool shuffle = p.opt.phase == M3_PHASE_SHUFFLE;
+    if (shuffle) {
+        for (int j = threadIdx.x; j < npr; j += kThreads) sperm[j] = clamp_pair(p.opt.perm[j], npr);
+        __syncthreads();
+    }
     const int64_t total = p.BtL * p.H * npr;
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * kThreads) {
         const int j = (int)(i % npr);
         float t = 0.f;
         if (p.opt.phase == M3_PHASE_REVERSE) t = -p.theta[i];
-        else if (p.opt.phase == M3_PHASE_SHUFFLE) t = p.theta[i - j + clamp_pair(p.opt.perm[j], npr)];
+        else if (shuffle) t = p.theta[i - j + sperm[j]];
         p.thetae[i] = t;
     }
 }
 
-// Group sums of dB', dC' and, with the pre-mixer, the RMSNorm backward and the
-// gain terms G xh of every row.  One wave per (token, group, rank) row.
+// Group sums of dB', dC' and, with the pre-mixer, the RMSNorm backward; the
+// gain terms G xh are summed over this block's rows into qpart[y][block][N]
+// (lanes' row sums, then the block's lanes in fixed order).
 template <typename IO>
 __global__ void __launch_bounds__(kThreads) bo_post_bc_kernel(BwdOptParams p)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (row >= p.BtL * p.G * p.R) return;
+    __shared__ float red[kWaves][64][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const RowLanes rl(p.N, lane);
     const bool isC = blockIdx.y != 0;
     const float* dsrc = isC ? p.dCe : p.dBe;
-    float* dout = (isC ? p.dC : p.dB) + row * p.N;
-    float* q = isC ? p.qC : p.qB;
-    const float* w = isC ? p.opt.Cw : p.opt.Bw;
-    const RowIdx ri = row_index(p, row);
-    const int64_t hpg = p.H / p.G;
-    float G[kMaxNK];
+    float* dout = isC ? p.dC : p.dB;
+    const IO* src = static_cast<const IO*>(isC ? p.C : p.B);
+    const bool colok = rl.c < p.N;
+    float wv[4];
+    gain4(isC ? p.opt.Cw : p.opt.Bw, rl.c, colok, wv);
+    const int64_t rows = p.BtL * p.G * p.R, hpg = p.H / p.G;
+    float qacc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t r0 = rl.first(wave); r0 < rows; r0 += rl.stride) {
+        const int64_t row = r0 + rl.sub;
+        const bool ok = colok && row < rows;
+        float G[4] = {0.f, 0.f, 0.f, 0.f};
+        if (ok) {
+            const RowIdx ri = row_index(p, row);
+            for (int64_t j = 0; j < hpg; ++j) {
+                float d[4];
+                ld4(dsrc + ((ri.bt * p.H + ri.g * hpg + j) * p.R + ri.r) * p.N + rl.c, d);
 #pragma unroll
-    for (int k = 0; k < kMaxNK; ++k) G[k] = 0.f;
-    for (int64_t j = 0; j < hpg; ++j) {
-        const float* d = dsrc + ((ri.bt * p.H + ri.g * hpg + j) * p.R + ri.r) * p.N;
-#pragma unroll
-        for (int k = 0; k < kMaxNK; ++k) {
-            const int n = lane + 64 * k;
-            if (n < p.N) G[k] += d[n];
+                for (int i = 0; i < 4; ++i) G[i] += d[i];
+            }
         }
-    }
-    if (!p.opt.premix) {
-#pragma unroll
-        for (int k = 0; k < kMaxNK; ++k) {
-            const int n = lane + 64 * k;
-            if (n < p.N) dout[n] = G[k];
+        if (!p.opt.premix) {
+            if (ok) st4(dout + row * p.N + rl.c, G);
+            continue;
         }
-        return;
-    }
-    float v[kMaxNK];
-    const float sc = load_row(static_cast<const IO*>(isC ? p.C : p.B) + row * p.N, p.N, lane,
-                              p.opt.eps, true, v);
-    float gx = 0.f;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (ok) ld4(src + row * p.N + rl.c, v);
+        const float ss = group_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3], rl.lpr);
+        const float sc = rsqrtf(ss / (float)p.N + p.opt.eps);
+        float gx = 0.f;
 #pragma unroll
-    for (int k = 0; k < kMaxNK; ++k) {
-        const int n = lane + 64 * k;
-        if (n < p.N) gx += G[k] * (w ? w[n] : 1.f) * (v[k] * sc);
-    }
-    gx = wave_sum(gx) / (float)p.N;
+        for (int i = 0; i < 4; ++i) gx += G[i] * wv[i] * (v[i] * sc);
+        gx = group_sum(gx, rl.lpr) / (float)p.N;
+        if (!ok) continue;
+        float o[4];
 #pragma unroll
-    for (int k = 0; k < kMaxNK; ++k) {
-        const int n = lane + 64 * k;
-        if (n >= p.N) continue;
-        const float xh = v[k] * sc;
-        dout[n] = sc * (G[k] * (w ? w[n] : 1.f) - xh * gx);
-        if (q) q[row * p.N + n] = G[k] * xh;
+        for (int i = 0; i < 4; ++i) {
+            const float xh = v[i] * sc;
+            o[i] = sc * (G[i] * wv[i] - xh * gx);
+            qacc[i] += G[i] * xh;
+        }
+        st4(dout + row * p.N + rl.c, o);
+    }
+    if (!p.opt.premix || p.qpart == nullptr) return;   // uniform over the block
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][lane][i] = qacc[i];
+    __syncthreads();
+    // column quad t: the block's lanes holding it, wave by wave, group by group
+    for (int t = threadIdx.x; t < rl.lpr; t += kThreads) {
+        if (t * 4 >= p.N) continue;
+        float s[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < kWaves; ++w)
+            for (int g = 0; g < 64 / rl.lpr; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[i] += red[w][g * rl.lpr + t][i];
+        st4(p.qpart + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * p.N + t * 4, s);
     }
 }
 
@@ -213,20 +275,22 @@ __global__ void __launch_bounds__(kThreads) bo_post_scalar_kernel(BwdOptParams p
     }
 }
 
-// dtheta from the gradient of the mapped theta.  Shuffle: each block first
-// lists, per pair j, the pairs i with perm[i] = j in increasing order (a chain
+// dtheta from the gradient of the mapped theta.  Shuffle: each block lists,
+// per pair j, the pairs i with perm[i] = j in increasing order (a chain
 // first[j] -> next[i] -> ...); every i is on exactly one chain.
 __global__ void __launch_bounds__(kThreads) bo_post_theta_kernel(BwdOptParams p)
 {
-    __shared__ int first[kMaxPairs], next[kMaxPairs];
+    __shared__ int sperm[kMaxPairs], first[kMaxPairs], next[kMaxPairs];
     const int npr = p.N / 2;
     const bool shuffle = p.opt.phase == M3_PHASE_SHUFFLE;
     if (shuffle) {
+        for (int j = threadIdx.x; j < npr; j += kThreads) sperm[j] = clamp_pair(p.opt.perm[j], npr);
+        __syncthreads();
         for (int j = threadIdx.x; j < npr; j += kThreads) {
             int prev = -1;
             first[j] = -1;
             for (int i = 0; i < npr; ++i) {
-                if (clamp_pair(p.opt.perm[i], npr) != j) continue;
+                if (sperm[i] != j) continue;
                 if (prev < 0) first[j] = i;
                 else next[prev] = i;
                 prev = i;
@@ -250,38 +314,59 @@ __global__ void __launch_bounds__(kThreads) bo_post_theta_kernel(BwdOptParams p)
     }
 }
 
-// Column sums of a [rows][cols] float32 array, stage 1: block (x, y) sums
-// rows y*rpc .. y*rpc + rpc - 1 of 256 columns into part[y][cols].
+// Column sums of a [rows][cols] float32 array, stage 1: block (x, y) = 64
+// columns x 4 row lanes over rows y*rpc .. y*rpc + rpc - 1; lane k takes every
+// 4th row from k, then the 4 lanes are added in order into part[y][cols].
 __global__ void __launch_bounds__(kThreads) bo_colsum_partial_kernel(const float* src, int64_t rows,
                                                                       int64_t cols, int64_t rpc,
                                                                       float* part)
 {
-    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (c >= cols) return;
+    __shared__ float red[kWaves][64];
+    const int cl = threadIdx.x & 63, k = threadIdx.x >> 6;
+    const int64_t c = (int64_t)blockIdx.x * 64 + cl;
     const int64_t r0 = (int64_t)blockIdx.y * rpc;
     const int64_t r1 = r0 + rpc < rows ? r0 + rpc : rows;
     float acc = 0.f;
-    for (int64_t r = r0; r < r1; ++r) acc += src[r * cols + c];
-    part[(int64_t)blockIdx.y * cols + c] = acc;
+    if (c < cols) {
+#pragma unroll 8
+        for (int64_t r = r0 + k; r < r1; r += kWaves) acc += src[r * cols + c];
+    }
+    red[k][cl] = acc;
+    __syncthreads();
+    if (k == 0 && c < cols)
+        part[(int64_t)blockIdx.y * cols + c] = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
 }
 
-// Stage 2: the partials of each column in block order.
-__global__ void __launch_bounds__(kThreads) bo_colsum_final_kernel(const float* part, int nchunk,
-                                                                    int64_t cols, float* dst)
+// Stage 2: block = 64 columns x 16 partial lanes; lane k adds partials k,
+// k + 16, ... in order, then the 16 lanes are added in order.
+__global__ void __launch_bounds__(64 * kFinalLanes) bo_colsum_final_kernel(const float* part, int nchunk,
+                                                                          int64_t cols, float* dst)
 {
-    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (c >= cols) return;
+    __shared__ float red[kFinalLanes][64];
+    const int cl = threadIdx.x & 63, k = threadIdx.x >> 6;
+    const int64_t c = (int64_t)blockIdx.x * 64 + cl;
     float acc = 0.f;
-    for (int k = 0; k < nchunk; ++k) acc += part[(int64_t)k * cols + c];
-    dst[c] = acc;
+    if (c < cols) {
+#pragma unroll 8
+        for (int q = k; q < nchunk; q += kFinalLanes) acc += part[(int64_t)q * cols + c];
+    }
+    red[k][cl] = acc;
+    __syncthreads();
+    if (k == 0 && c < cols) {
+        float s = 0.f;
+        for (int q = 0; q < kFinalLanes; ++q) s += red[q][cl];
+        dst[c] = s;
+    }
 }
 
-// Row blocks of a column sum: at least 32 rows each, at most 1024 blocks, and
-// at most 4 Mi partial values.
+// Row chunks of a stage-1 column sum: about 2048 blocks in all, at least 16
+// rows per chunk, at most 4 Mi partial values.
 void colsum_plan(int64_t rows, int64_t cols, int64_t* rpc, int* nchunk)
 {
-    int64_t nc = (rows + 31) / 32;
-    if (nc > 1024) nc = 1024;
+    const int64_t tiles = (cols + 63) / 64 > 0 ? (cols + 63) / 64 : 1;
+    int64_t nc = kMaxBlocks / tiles;
+    const int64_t by_rows = (rows + 15) / 16;
+    if (nc > by_rows) nc = by_rows;
     const int64_t cap = ((int64_t)1 << 22) / (cols > 0 ? cols : 1);
     if (nc > cap) nc = cap;
     if (nc < 1) nc = 1;
@@ -292,6 +377,21 @@ void colsum_plan(int64_t rows, int64_t cols, int64_t* rpc, int* nchunk)
     if (*nchunk < 1) *nchunk = 1;
 }
 
+size_t colsum_partial_floats(int64_t rows, int64_t cols)
+{
+    int64_t rpc;
+    int nchunk;
+    colsum_plan(rows, cols, &rpc, &nchunk);
+    return (size_t)nchunk * (size_t)(cols > 0 ? cols : 0);
+}
+
+hipError_t colsum_final(const float* part, int nchunk, int64_t cols, float* dst, hipStream_t s)
+{
+    hipLaunchKernelGGL(bo_colsum_final_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(64 * kFinalLanes),
+                       0, s, part, nchunk, cols, dst);
+    return hipGetLastError();
+}
+
 hipError_t colsum(const float* src, int64_t rows, int64_t cols, float* part, float* dst,
                   hipStream_t s)
 {
@@ -299,18 +399,26 @@ hipError_t colsum(const float* src, int64_t rows, int64_t cols, float* part, flo
     int64_t rpc;
     int nchunk;
     colsum_plan(rows, cols, &rpc, &nchunk);
-    const unsigned gx = (unsigned)((cols + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(bo_colsum_partial_kernel, dim3(gx, nchunk), dim3(kThreads), 0, s, src, rows,
-                       cols, rpc, part);
-    hipLaunchKernelGGL(bo_colsum_final_kernel, dim3(gx), dim3(kThreads), 0, s, part, nchunk, cols,
-                       dst);
-    return hipGetLastError();
+    hipLaunchKernelGGL(bo_colsum_partial_kernel, dim3((unsigned)((cols + 63) / 64), nchunk), dim3(kThreads),
+                       0, s, src, rows, cols, rpc, part);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : colsum_final(part, nchunk, cols, dst, s);
 }
 
 unsigned stride_grid(int64_t n)
 {
     const int64_t b = (n + kThreads - 1) / kThreads;
-    return (unsigned)(b < ((int64_t)1 << 20) ? b : ((int64_t)1 << 20));
+    return (unsigned)(b < kMaxBlocks ? b : kMaxBlocks);
+}
+
+// Blocks of the row kernels: 4 waves, 64/LPR rows per wave at once.
+unsigned row_grid(int64_t rows, int N)
+{
+    int lpr = 1;
+    while (lpr * 4 < N) lpr <<= 1;
+    const int64_t per_block = (int64_t)kWaves * (64 / lpr);
+    const int64_t b = (rows + per_block - 1) / per_block;
+    return (unsigned)(b < 1 ? 1 : (b < kMaxBlocks ? b : kMaxBlocks));
 }
 
 template <typename IO>
@@ -318,8 +426,7 @@ hipError_t pre_impl(const BwdOptParams& p, hipStream_t s)
 {
     const int64_t rows = p.BtL * p.G * p.R, tok = p.BtL * p.H;
     if (p.Be != nullptr && rows > 0)
-        hipLaunchKernelGGL(bo_prep_bc_kernel<IO>, dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock), 2),
-                           dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(bo_prep_bc_kernel<IO>, dim3(row_grid(rows, p.N), 2), dim3(kThreads), 0, s, p);
     if (p.dte != nullptr && tok > 0)
         hipLaunchKernelGGL(bo_prep_scalar_kernel, dim3(stride_grid(tok)), dim3(kThreads), 0, s, p);
     if (p.thetae != nullptr && tok > 0)
@@ -332,20 +439,24 @@ template <typename IO>
 hipError_t post_impl(const BwdOptParams& p, hipStream_t s)
 {
     const int64_t rows = p.BtL * p.G * p.R, tok = p.BtL * p.H;
+    const unsigned gbc = row_grid(rows, p.N);
     if (p.opt.premix && tok > 0)
         hipLaunchKernelGGL(bo_post_scalar_kernel, dim3(stride_grid(tok)), dim3(kThreads), 0, s, p);
     if (p.dBe != nullptr && rows > 0)
-        hipLaunchKernelGGL(bo_post_bc_kernel<IO>, dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock), 2),
-                           dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(bo_post_bc_kernel<IO>, dim3(gbc, 2), dim3(kThreads), 0, s, p);
     if (p.dthetae != nullptr && p.dtheta != nullptr && tok > 0)
         hipLaunchKernelGGL(bo_post_theta_kernel, dim3(stride_grid(tok * (p.N / 2))), dim3(kThreads), 0,
                            s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.opt.premix) return e;
     const int64_t hrn = p.H * p.R * p.N;
+    // gain gradients: the row kernel's per-block partials (none written when
+    // there are no rows: the sums are then zero)
+    const int nq = rows > 0 ? (int)gbc : 0;
+    if (p.dBw && (e = colsum_final(p.qpart, nq, p.N, p.dBw, s)) != hipSuccess) return e;
+    if (p.dCw && (e = colsum_final(p.qpart + (int64_t)gbc * p.N, nq, p.N, p.dCw, s)) != hipSuccess)
+        return e;
     if (p.ddtb && (e = colsum(p.ddt, p.BtL, p.H, p.part, p.ddtb, s)) != hipSuccess) return e;
-    if (p.dBw && (e = colsum(p.qB, rows, p.N, p.part, p.dBw, s)) != hipSuccess) return e;
-    if (p.dCw && (e = colsum(p.qC, rows, p.N, p.part, p.dCw, s)) != hipSuccess) return e;
     if (p.dBb && (e = colsum(p.dBe, p.BtL, hrn, p.part, p.dBb, s)) != hipSuccess) return e;
     if (p.dCb && (e = colsum(p.dCe, p.BtL, hrn, p.part, p.dCb, s)) != hipSuccess) return e;
     return hipSuccess;
@@ -355,16 +466,13 @@ hipError_t post_impl(const BwdOptParams& p, hipStream_t s)
 
 size_t bwd_options_partial_floats(int64_t BtL, int64_t H, int64_t G, int N, int R)
 {
-    size_t most = 0;
-    const int64_t shapes[3][2] = {{BtL, H}, {BtL * G * R, N}, {BtL, H * R * N}};
-    for (const auto& sh : shapes) {
-        int64_t rpc;
-        int nchunk;
-        colsum_plan(sh[0], sh[1], &rpc, &nchunk);
-        const size_t n = (size_t)nchunk * (size_t)(sh[1] > 0 ? sh[1] : 0);
-        if (n > most) most = n;
-    }
-    return most;
+    size_t a = colsum_partial_floats(BtL, H), b = colsum_partial_floats(BtL, H * R * N);
+    return a > b ? a : b;
+}
+
+size_t bwd_options_gain_floats(int64_t BtL, int64_t G, int N, int R)
+{
+    return 2 * (size_t)row_grid(BtL * G * R, N) * (size_t)N;
 }
 
 hipError_t launch_bwd_options_pre(const BwdOptParams& p, int io_dtype, hipStream_t stream)

@@ -111,12 +111,13 @@ struct BwdOptParams {
     float *ddt, *dlam;             // caller's, mapped in place (pre-mixer)
     float *dtheta;                 // caller's or NULL
     float *dBw, *dCw, *dBb, *dCb, *ddtb;   // parameter gradients or NULL
-    float *qB, *qC;                // [B*L*G*R][N] per-row gain terms (workspace)
+    float *qpart;                  // [2][row blocks][N] gain-gradient partials (workspace)
     float *part;                   // column-sum partials (workspace)
     int64_t BtL, H, G;
     int N, R;
 };
 size_t bwd_options_partial_floats(int64_t BtL, int64_t H, int64_t G, int N, int R);
+size_t bwd_options_gain_floats(int64_t BtL, int64_t G, int N, int R);
 hipError_t launch_bwd_options_pre(const BwdOptParams& p, int io_dtype, hipStream_t stream);
 hipError_t launch_bwd_options_post(const BwdOptParams& p, int io_dtype, hipStream_t stream);
 
