@@ -10,7 +10,8 @@ differentiation of that loop: the gradient of L = sum(dy * y) + sum(dh * h_L)
 with respect to every input, the decay rate A and the state record.
 
 Layouts as the scan: x [Bt,L,H,R,P], Bm/Cm [Bt,L,H,R,N], dt/lam [Bt,L,H],
-theta [Bt,L,H,N/2], A [H] (or per token [Bt,L,H] in forward_torch);
+theta [Bt,L,H,N/2], A [H] or per token [Bt,L,H] (the decay exp(dt_t A_t) of
+the Mamba-3 summary's section 1);
 h0 [Bt,H,N,P], Bprev [Bt,H,R,N], xprev [Bt,H,R,P].
 
 Options (the same maps as oracle.scan applies before the recurrence, here on
@@ -99,7 +100,8 @@ def scan_backward(x, Bm, Cm, dt, A, theta, lam, dy, dh=None, h0=None, Bprev=None
                   ngroups=None, phase="native", perm=None, premix=None):
     """Gradients of sum(dy * y) + sum(dh * h_L).  Returns a dict of float64
     numpy arrays: dx, dB, dC, ddt, dA, dtheta, dlam, dh0, dBprev, dxprev,
-    dA_scale [H] (the sum of |per-token terms| that dA adds up) and, with
+    dA_scale [H] (the sum of |per-token terms| that dA adds up; with A given
+    per token, [Bt,L,H], dA is per token and dA_scale its magnitude) and, with
     ``premix`` (a dict of arrays B_norm_w, C_norm_w, B_bias, C_bias, dt_bias
     and eps), the parameter gradients dB_norm_w, dC_norm_w, dB_bias, dC_bias,
     ddt_bias."""
@@ -107,8 +109,10 @@ def scan_backward(x, Bm, Cm, dt, A, theta, lam, dy, dh=None, h0=None, Bprev=None
     x, Bm, Cm, dt, theta, lam = map(t64, (x, Bm, Cm, dt, theta, lam))
     Bt, L, H, R, P = x.shape
     N = Bm.shape[-1]
-    # A repeated per (b, t): its gradient holds the per-token terms of dA
-    A = t64(np.broadcast_to(np.asarray(A, dtype=np.float64), (Bt, L, H)))
+    # A repeated per (b, t) (or given per token): its gradient holds the
+    # per-token terms of dA
+    A_in = np.asarray(A, dtype=np.float64)
+    A = t64(np.broadcast_to(A_in, (Bt, L, H)))
     z = lambda *s: np.zeros(s)
     h0 = t64(z(Bt, H, N, P) if h0 is None else h0)
     Bprev = t64(z(Bt, H, R, N) if Bprev is None else Bprev)
@@ -131,6 +135,10 @@ def scan_backward(x, Bm, Cm, dt, A, theta, lam, dy, dh=None, h0=None, Bprev=None
     out = {n: (np.zeros(v.shape) if g is None else g.detach().numpy())
            for n, v, g in zip(names, leaves, grads)}
     terms = out["dA"]                                    # [Bt, L, H]
+    if np.ndim(A_in) == 3:
+        # a decay rate per token: each term is its own gradient
+        out["dA_scale"] = np.abs(terms)
+        return out
     out["dA"] = terms.sum(axis=(0, 1))
     out["dA_scale"] = np.abs(terms).sum(axis=(0, 1))
     return out

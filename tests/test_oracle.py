@@ -703,10 +703,13 @@ def test_backward_dA_terms_match_finite_differences():
     assert np.all(g["dA_scale"] >= np.abs(g["dA"]) - 1e-9)
 
 
-def _bwd_option_case(rng, ngroups, phase, premix, Bt=1, L=5, H=2, R=2, P=2, N=4):
+def _bwd_option_case(rng, ngroups, phase, premix, Bt=1, L=5, H=2, R=2, P=2, N=4, a_tok=False):
     """A gradient case with options: B, C per group, a permutation for
-    "shuffle", and with the pre-mixer raw dt, lam and its parameters."""
+    "shuffle", with the pre-mixer raw dt, lam and its parameters, and A per
+    token."""
     ins, dy, dh = _bwd_case(rng, Bt, L, H, R, P, N)
+    if a_tok:
+        ins[4] = -np.exp(rng.uniform(-1.0, 1.0, (Bt, L, H)))
     if ngroups:
         ins[1] = rng.standard_normal((Bt, L, ngroups, R, N))
         ins[2] = rng.standard_normal((Bt, L, ngroups, R, N))
@@ -728,6 +731,33 @@ OPTION_GRAD_CASES = [(1, "shuffle", True), (2, "reverse", False), (0, "zero", Tr
                      (1, "native", False), (0, "reverse", True)]
 
 
+def test_backward_per_token_decay_matches_finite_differences():
+    """A per token (the decay exp(dt_t A_t)), with groups, shuffled phases
+    and the pre-mixer: dA is the per-token gradient, every other gradient as
+    before; central differences of the C oracle's loss."""
+    from oracle.backward import scan_backward
+    rng = np.random.default_rng(41)
+    ins, dy, dh, kw, pm = _bwd_option_case(rng, 1, "shuffle", True, a_tok=True)
+    g = scan_backward(*ins[:7], dy, dh, h0=ins[7], Bprev=ins[8], xprev=ins[9], premix=pm, **kw)
+    assert g["dA"].shape == ins[4].shape
+
+    def loss(args):
+        y, hL, _, _ = oracle.scan(*args[:7], h0=args[7], Bprev=args[8], xprev=args[9],
+                                  premix=pm, **kw)
+        return float(np.sum(y * dy) + np.sum(hL * dh))
+    names = ["dx", "dB", "dC", "ddt", "dA", "dtheta", "dlam", "dh0", "dBprev", "dxprev"]
+    eps = 1e-6
+    for k, name in enumerate(names):
+        fd = np.zeros_like(ins[k])
+        for idx in np.ndindex(ins[k].shape):
+            plus, minus = [a.copy() for a in ins], [a.copy() for a in ins]
+            plus[k][idx] += eps
+            minus[k][idx] -= eps
+            fd[idx] = (loss(plus) - loss(minus)) / (2 * eps)
+        err = np.max(np.abs(fd - g[name])) / max(np.max(np.abs(g[name])), 1e-12)
+        assert err < 1e-6, (name, err)
+
+
 @pytest.mark.parametrize("ngroups,phase,premix", OPTION_GRAD_CASES)
 def test_backward_options_forward_matches_c_oracle(ngroups, phase, premix):
     """The gradient oracle's option maps (group repeat, phase transform,
@@ -735,7 +765,8 @@ def test_backward_options_forward_matches_c_oracle(ngroups, phase, premix):
     import torch
     from oracle.backward import forward_torch
     rng = np.random.default_rng(34)
-    ins, _, _, kw, pm = _bwd_option_case(rng, ngroups, phase, premix, Bt=2, L=9, H=4, N=8)
+    ins, _, _, kw, pm = _bwd_option_case(rng, ngroups, phase, premix, Bt=2, L=9, H=4, N=8,
+                                         a_tok=premix)
     y_c, h_c, _, _ = oracle.scan(*ins[:7], h0=ins[7], Bprev=ins[8], xprev=ins[9], premix=pm, **kw)
     tpm = None if pm is None else {k: (v if k == "eps" else torch.tensor(v)) for k, v in pm.items()}
     y_t, h_t = forward_torch(*[torch.tensor(a) for a in ins], premix=tpm, **kw)
