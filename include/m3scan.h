@@ -276,6 +276,7 @@ typedef struct {
  * A method that does not support the sizes returns M3_ERR_UNSUPPORTED; any
  * other value returns M3_ERR_OPTION.  The methods agree to rounding.
  * Options (opt, as m3_options for m3_scan_fwd; all zero = the plain mixer):
+ *   A_per_token  A and dA are [batch, seqlen, nheads] (dA per token)
  *   ngroups      B, C and dB, dC are [batch, seqlen, ngroups, rank, dstate];
  *                a group's gradient sums those of its heads
  *   phase_mode   M3_PHASE_ZERO, _REVERSE or _SHUFFLE: dtheta is the gradient
@@ -292,7 +293,7 @@ typedef struct {
  *                NULL parameter is differentiated at its default, ones or
  *                zeros).  The state record (B_prev_in) holds the pre-mixed B,
  *                as m3_scan_fwd writes it, and dB_prev is with respect to it.
- *   A_per_token, cu_seqlens, phase_in and phase_out are not supported here
+ *   cu_seqlens, phase_in and phase_out are not supported here
  *   (M3_ERR_UNSUPPORTED), nor the decode-only phase modes (M3_ERR_OPTION).
  * With options, the inputs are first materialised in the workspace as the
  * recurrence uses them, and the gradients are mapped back afterwards.

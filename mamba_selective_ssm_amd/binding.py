@@ -466,7 +466,8 @@ def m3_scan_bwd_supported(dstate: int, headdim: int, rank: int, io_dtype: int,
 
 
 def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace,
-                 method="auto", ngroups=0, phase="native", perm=None, premix=None):
+                 method="auto", ngroups=0, phase="native", perm=None, premix=None,
+                 A_per_token=False):
     lib = load_library()
     Bt, L, H, R, P = x.shape
     N = B.shape[-1]
@@ -477,7 +478,8 @@ def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, wor
                            (C, "C", (Bt, L, G, R, N), x.dtype), (dt, "dt", (Bt, L, H), torch.float32),
                            (lam, "lam", (Bt, L, H), torch.float32),
                            (theta, "theta", (Bt, L, H, N // 2), torch.float32),
-                           (A, "A", (H,), torch.float32), (dy, "dy", (Bt, L, H, R, P), x.dtype)):
+                           (A, "A", (Bt, L, H) if A_per_token else (H,), torch.float32),
+                           (dy, "dy", (Bt, L, H, R, P), x.dtype)):
         if t is None and n == "theta" and zero:
             continue
         _check(t, n, shp, dt_)
@@ -487,7 +489,7 @@ def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, wor
         _check(state.x_prev, "state.x_prev", (Bt, H, R, P), x.dtype)
     if dh_out is not None:
         _check(dh_out, "dh_out", (Bt, H, N, P), torch.float32)
-    opt, keep = _options(H, N, R, False, ngroups, phase, perm, premix, x.device)
+    opt, keep = _options(H, N, R, A_per_token, ngroups, phase, perm, premix, x.device)
     f32 = dict(dtype=torch.float32, device=x.device)
     pg = None
     if premix is not None:
@@ -527,16 +529,18 @@ def m3_scan_bwd(x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
                 dh_out: Optional[torch.Tensor] = None, *, state_grads: bool = True,
                 workspace: Optional[torch.Tensor] = None, method: str = "auto",
                 ngroups: int = 0, phase: str = "native", perm: Optional[torch.Tensor] = None,
-                premix: Optional[Premix] = None, stream=None) -> ScanGrads:
+                premix: Optional[Premix] = None, A_per_token: bool = False,
+                stream=None) -> ScanGrads:
     """Gradients of sum(dy * y) + sum(dh_out * h_L) of m3_scan_fwd with respect
     to every input; ``state_grads`` also returns those of the input state
     record (zero record when ``state`` is None).  ``method``: "chunked"
     (reverse mode of the chunked form), "step" (adjoint recurrence step by
     step) or "auto" (chunked where supported).  Options as m3_scan_fwd takes
-    them (head groups, the phase modes of a scan, the pre-mixer); with
-    ``premix`` the result's ``premix`` field holds the parameter gradients."""
+    them (A per token, head groups, the phase modes of a scan, the
+    pre-mixer); with ``A_per_token`` dA is per token, with ``premix`` the
+    result's ``premix`` field holds the parameter gradients."""
     a, g, _, _keep = _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads,
-                                  workspace, method, ngroups, phase, perm, premix)
+                                  workspace, method, ngroups, phase, perm, premix, A_per_token)
     st = load_library().m3_scan_bwd(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_bwd")

@@ -222,15 +222,16 @@ bool bwd_method_ok(int method, int64_t N, int64_t P, int64_t R, int io)
 
 m3_status plan_bwd_core(const m3_scan_bwd_args* a, BwdPlan* out);
 
-// The options a gradient call supports (head groups, the phase maps of a scan,
-// the pre-mixer) and the workspace of their maps.
+// The options a gradient call supports (per-token decay, head groups, the
+// phase maps of a scan, the pre-mixer) and the workspace of their maps.
 m3_status plan_bwd_options(const m3_scan_bwd_args* a, BwdPlan* out)
 {
     const m3_options& o = a->opt;
     const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
     const int64_t N = a->dstate, R = a->rank;
-    if (o.A_per_token != 0 || o.cu_seqlens != nullptr || o.phase_in != nullptr || o.phase_out != nullptr)
+    if (o.cu_seqlens != nullptr || o.phase_in != nullptr || o.phase_out != nullptr)
         return M3_ERR_UNSUPPORTED;
+    if (o.A_per_token != 0 && o.A_per_token != 1) return M3_ERR_OPTION;
     if (o.phase_mode < M3_PHASE_NATIVE || o.phase_mode > M3_PHASE_SHUFFLE) return M3_ERR_OPTION;
     if (o.ngroups < 0 || (o.ngroups > 0 && H > 0 && H % o.ngroups != 0)) return M3_ERR_OPTION;
     if (o.premix != 0 && o.premix != 1) return M3_ERR_OPTION;
@@ -358,7 +359,8 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
     const bool st_out = a->dh_in || a->dB_prev || a->dx_prev;
     if (st_in && !(a->h_in && a->B_prev_in && a->x_prev_in)) return M3_ERR_NULL;
     if (st_out && !(a->dh_in && a->dB_prev && a->dx_prev)) return M3_ERR_NULL;
-    if (a->A == nullptr || a->dA == nullptr) return M3_ERR_NULL;
+    // per-token A and dA are empty when there are no tokens
+    if ((a->A == nullptr || a->dA == nullptr) && !(a->opt.A_per_token && L == 0)) return M3_ERR_NULL;
     if (L > 0 && (!a->x || !a->B || !a->C || !a->dt || (!zero_phase && !a->theta) || !a->lam ||
                   !a->dy || !a->dx || !a->dB || !a->dC || !a->ddt ||
                   (!zero_phase && !a->dtheta) || !a->dlam))
@@ -372,10 +374,11 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
     const int e = io_size(a->io_dtype);
     const int64_t tok = Bt * L * H, tokg = Bt * L * plan.groups;
+    const int64_t nA = a->opt.A_per_token ? tok : H;       // A and dA
     Range in[20] = {
         range_of(a->x, tok * R * P * e),         range_of(a->B, tokg * R * N * e),
         range_of(a->C, tokg * R * N * e),        range_of(a->dt, tok * 4),
-        range_of(a->A, H * 4),                   range_of(theta_in, tok * (N / 2) * 4),
+        range_of(a->A, nA * 4),                  range_of(theta_in, tok * (N / 2) * 4),
         range_of(a->lam, tok * 4),               range_of(a->h_in, nbh * N * P * 4),
         range_of(a->B_prev_in, nbh * R * N * e), range_of(a->x_prev_in, nbh * R * P * e),
         range_of(a->dy, tok * R * P * e),        range_of(a->dh_out, nbh * N * P * 4),
@@ -384,7 +387,7 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
     const Range out[] = {
         range_of(a->dx, tok * R * P * 4),        range_of(a->dB, tokg * R * N * 4),
         range_of(a->dC, tokg * R * N * 4),       range_of(a->ddt, tok * 4),
-        range_of(a->dA, H * 4),                  range_of(a->dtheta, tok * (N / 2) * 4),
+        range_of(a->dA, nA * 4),                 range_of(a->dtheta, tok * (N / 2) * 4),
         range_of(a->dlam, tok * 4),              range_of(a->dh_in, nbh * N * P * 4),
         range_of(a->dB_prev, nbh * R * N * 4),   range_of(a->dx_prev, nbh * R * P * 4),
         range_of(a->dB_norm_w, N * 4),           range_of(a->dC_norm_w, N * 4),
@@ -462,6 +465,7 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         q.dw_last = reinterpret_cast<float*>(w);
         w += plan.chunk_bytes;
         q.dA_bh = reinterpret_cast<float*>(w);
+        q.a_tok = a->opt.A_per_token;
         q.L = L; q.H = H; q.N = (int)N; q.P = (int)P; q.R = (int)R;
         q.nbh = (int)nbh;
         q.nc = (int)plan.nc;
@@ -486,6 +490,8 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         p.dxprev_part = reinterpret_cast<float*>(ws);
         ws += plan.dxp_bytes;
         p.dA_part = reinterpret_cast<float*>(ws);
+        p.a_tok = a->opt.A_per_token;
+        p.dAt = a->dA;
         p.L = L; p.H = H; p.N = (int)N; p.P = (int)P; p.R = (int)R;
         p.ntok = Bt * L * H;
         p.nbh = (int)nbh;

@@ -207,7 +207,7 @@ struct Raw {
     static constexpr int IG = (Cf::NPR * G4 + Cf::NTHR - 1) / Cf::NTHR;
     uint4 vb[IB], vc[IB], vx[IX], vy[IX];
     f32x4 th[IT];
-    float dtv, lmv;
+    float dtv, lmv, av;   // av: the token's decay rate when it is given per token
     V4 sd0[IG], sd1[IG], sg0[IG], sg1[IG];    // state pair items (rows 2i, 2i+1, columns 4q..4q+3)
     float scc[IG], sss[IG];
 };
@@ -276,8 +276,9 @@ __device__ __forceinline__ void load_raw(const BcParams& p, int bh, int c, Raw<C
             if (t0 + j < L_) rw.th[it] = *reinterpret_cast<const f32x4*>(p.theta + tok(t0 + j) * NPR + 4 * q);
         }
     }
-    rw.dtv = 0.f; rw.lmv = 0.f;
+    rw.dtv = 0.f; rw.lmv = 0.f; rw.av = 0.f;
     if (tid <= Q && t0 + tid < L_) { rw.dtv = p.dt[tok(t0 + tid)]; rw.lmv = p.lam[tok(t0 + tid)]; }
+    if (p.a_tok && tid < Q && t0 + tid < L_) rw.av = p.A[tok(t0 + tid)];
     if constexpr (GRAD) {
         const op_t* gin = reinterpret_cast<const op_t*>(p.gst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
         const op_t* dgo = reinterpret_cast<const op_t*>(p.dgst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
@@ -322,7 +323,7 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
     op_t* sDY = reinterpret_cast<op_t*>(lds + L::oDY);
     float* sPhi = reinterpret_cast<float*>(lds + L::oPhi);
     float* sT = reinterpret_cast<float*>(lds + L::oTok);
-    const float A = p.A[h];
+    const float A = p.a_tok ? 0.f : p.A[h];
 
     // ---- S1: raw rows into LDS ----------------------------------------------
 #pragma unroll
@@ -361,7 +362,7 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
         const int j = lane;
         const float dtj = j < Q ? sT[kDt * TS + j] : 0.f;
         const float lmj = j < Q ? sT[kLm * TS + j] : 0.f;
-        const float lam_j = wave_inclusive_sum(dtj * A);
+        const float lam_j = wave_inclusive_sum(dtj * (p.a_tok ? rw.av : A));
         const float lam_tot = wave_read_lane(lam_j, 63);
         const float dtn = sT[kDt * TS + j + 1], lmn = sT[kLm * TS + j + 1];
         const float ga = lmj * dtj;
@@ -1054,15 +1055,16 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
         const float inc = wave_inclusive_sum(dlam);
         const float da = wave_read_lane(inc, 63) - inc + dlam;
         const float dw_prev = __shfl_up(dw, 1, 64);
-        const float A = p.A[h];
         float dAc = 0.f;
         if (t < Q && t0 + t < L_) {
             const float dtt = sT[kDt * TS + t], lm = sT[kLm * TS + t];
             const float dwp = t > 0 ? dw_prev : 0.f;
             const int64_t k = tok(t0 + t);
+            const float A = p.A[p.a_tok ? k : h];
             p.ddt[k] = A * da + sT[kTD * TS + t] + lm * dgt + (1.f - lm) * dwp;
             p.dlam[k] = dtt * (dgt - dwp);
             dAc = dtt * da;
+            if (p.a_tok) p.dA[k] = dAc;      // a per-token rate: its own gradient
         }
         const float dAs = wave_read_lane(wave_inclusive_sum(dAc), 63);
         if (lane == 0) p.dA_part[(size_t)bh * p.nc + c] = dAs;
@@ -1197,6 +1199,7 @@ hipError_t launch_cfg(const BcParams& p, hipStream_t stream)
     hipLaunchKernelGGL((bc_final_kernel<IO, IO>), dim3((unsigned)p.nbh), dim3(256), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (p.a_tok) return hipSuccess;               // dA was written per token
     const int64_t batch = p.nbh / p.H;
     hipLaunchKernelGGL(bc_dA_kernel, dim3((unsigned)((p.H + 63) / 64)), dim3(64), 0, stream,
                        (const float*)p.dA_bh, p.dA, batch, p.H);

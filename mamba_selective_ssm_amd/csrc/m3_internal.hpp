@@ -53,6 +53,8 @@ struct BwdParams {
     float *scal;      // [parts][B*L*H][4] each part's dalpha, dbeta, dgamma, theta.dphi
     float *dxprev_part;  // [parts][B*H][R][P]
     float *dA_part;   // [B*H] this unit's share of dA
+    float *dAt;       // [B*L*H] dA per token (a_tok), else unused
+    int a_tok;        // A given per (batch, token, head)
     int64_t L, H, ntok;
     int N, P, R;
     int nbh, parts;   // (b, h) units; pair parts (16 pairs) per unit
@@ -84,6 +86,7 @@ struct BcParams {
     float *dA_part;   // [B*H][nc] each chunk's share of dA
     float *dw_last;   // [B*H][nc] gradient of the look-ahead weight of a chunk's last token
     float *dA_bh;     // [B*H] each unit's share of dA
+    int a_tok;        // A (and dA) per (batch, token, head)
     int64_t L, H;
     int N, P, R;
     int nbh, nc;      // (b, h) units; chunks per unit

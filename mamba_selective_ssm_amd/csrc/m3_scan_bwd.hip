@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
     const IO* dYg = reinterpret_cast<const IO*>(p.dy);
     const IO* Bpr = reinterpret_cast<const IO*>(p.Bp_in);
     const IO* Xpr = reinterpret_cast<const IO*>(p.xp_in);
-    const float A = p.A[h];
+    const float A = p.a_tok ? 0.f : p.A[h];
     auto tok = [&](int64_t t) -> int64_t { return (b * L + t) * H + h; };
     auto lp_of = [&](int k) { return rg + 16 * k; };             // pair within the part
     auto pair_of = [&](int k) { return p_lo + rg + 16 * k; };    // pair of the state
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
             const float d = t >= 0 ? p.dt[tok(t)] : 0.f;
             if (j == PP) {
                 const float lm = t >= 0 ? p.lam[tok(t)] : 0.f;
-                const float al = expf(d * A);
+                const float al = expf(d * (p.a_tok && t >= 0 ? p.A[tok(t)] : A));
                 f[0] = d;
                 f[1] = lm;
                 f[2] = al;
@@ -595,7 +595,6 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdParams p)
     const int bh = blockIdx.x, tid = threadIdx.x;
     const int64_t H = p.H, L = p.L, b = bh / H, h = bh % H;
     const int P = p.P, S = p.parts;
-    const float A = p.A[h];
     const int64_t RP4 = (int64_t)R * P / 4;
     for (int64_t idx = tid; idx < L * RP4; idx += 256) {
         const int64_t t = idx / RP4, q = idx % RP4;
@@ -610,10 +609,13 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdParams p)
         const int64_t tk = (b * L + t) * H + h;
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};      // dalpha, dbeta, dgamma, sum_i theta_i dphi_i
         for (int k = 0; k < S; ++k) sc += *reinterpret_cast<const f32x4*>(p.scal + ((size_t)k * p.ntok + tk) * 4);
+        const float A = p.A[p.a_tok ? tk : h];
         const float d = p.dt[tk], lm = p.lam[tk], al = expf(d * A);
         p.ddt[tk] = sc[0] * al * A + sc[1] * (1.f - lm) * al * (1.f + d * A) + sc[2] * lm + sc[3];
         p.dlam[tk] = -d * al * sc[1] + d * sc[2];
-        dA_acc += sc[0] * al * d + sc[1] * (1.f - lm) * d * d * al;
+        const float dAk = sc[0] * al * d + sc[1] * (1.f - lm) * d * d * al;
+        if (p.a_tok) p.dAt[tk] = dAk;                 // a per-token rate: its own gradient
+        dA_acc += dAk;
     }
     if (p.dxp != nullptr) {
         for (int64_t q = tid; q < RP4; q += 256) {
@@ -679,6 +681,7 @@ hipError_t launch_bwd_t(const BwdParams& p, float* dA, hipStream_t stream)
     hipLaunchKernelGGL(bwd_finalize_kernel<R>, dim3((unsigned)p.nbh), dim3(256), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (p.a_tok) return hipSuccess;               // dA was written per token
     const int64_t batch = p.nbh / p.H;
     hipLaunchKernelGGL(bwd_dA_kernel, dim3((unsigned)((p.H + 63) / 64)), dim3(64), 0, stream,
                        (const float*)p.dA_part, dA, batch, p.H);

@@ -117,7 +117,10 @@ def bwd_args(**kw):
     (dict(method=2, dstate=128, io_dtype=0), -3),          # chunked float32: dstate <= 64
     (dict(method=1, headdim=128), -3),
     # options of the gradient
-    (dict(opt=binding.Options(A_per_token=1)), -3),          # per-token decay: not supported
+    (dict(opt=binding.Options(A_per_token=2)), -9),
+    # per-token decay: A and dA are [batch, seqlen, nheads] (dA 128 bytes into A overlaps it)
+    (dict(opt=binding.Options(A_per_token=1), dA=FAKE + (4 << 32) + 128), -7),
+    (dict(opt=binding.Options(A_per_token=1), A=None), -1),
     (dict(opt=binding.Options(max_seqlen=4, cu_seqlens=FAKE + (23 << 32))), -3),
     (dict(opt=binding.Options(phase_out=FAKE + (23 << 32))), -3),
     (dict(opt=binding.Options(phase_mode=4)), -9),           # decode-only phase mode
@@ -174,7 +177,8 @@ def test_bwd_option_workspace(lib):
     assert ws(opt=binding.Options(ngroups=1)) >= plain + tok * R * N * (2 * 2 + 2 * 4)
     assert ws(opt=binding.Options(premix=1)) > ws(opt=binding.Options(ngroups=1))
     assert ws(opt=binding.Options(ngroups=3)) == plain          # one group per head
-    assert ws(opt=binding.Options(A_per_token=1)) == 0
+    assert ws(opt=binding.Options(A_per_token=1)) == plain       # no maps needed
+    assert ws(opt=binding.Options(A_per_token=2)) == 0
     assert ws(opt=binding.Options(phase_mode=5)) == 0
     assert lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(batch=0))) == 0
     assert lib.m3_scan_bwd_workspace_bytes(

@@ -1,6 +1,7 @@
-"""Parity of m3_scan_bwd with options -- head groups, the phase modes of a
-scan (theta zeroed, negated, shuffled) and the pre-mixer (RMSNorm + biases on
-B and C, softplus and sigmoid of the raw step and weight) -- against the fp64
+"""Parity of m3_scan_bwd with options -- a decay rate per token, head groups,
+the phase modes of a scan (theta zeroed, negated, shuffled) and the pre-mixer
+(RMSNorm + biases on B and C, softplus and sigmoid of the raw step and
+weight) -- against the fp64
 gradient oracle with the same options, by both methods.  With the pre-mixer
 the gradients are those of the raw inputs, plus the parameter gradients
 dB_norm_w, dC_norm_w, dB_bias, dC_bias and ddt_bias.
@@ -8,7 +9,8 @@ dB_norm_w, dC_norm_w, dB_bias, dC_bias and ddt_bias.
 Metric as for the plain gradient: max |got - ref| / max |ref| per tensor,
 tolerance 1e-4 for float32 inputs, 2e-2 for bfloat16; dA and ddt_bias, which
 sum per-token terms over batch and tokens, against the sum of the terms'
-magnitudes (for ddt_bias: sum over (b, t) of |ddt_raw| of the head).
+magnitudes (for ddt_bias: sum over (b, t) of |ddt_raw| of the head); dA per
+token (A per token) elementwise like the other gradients.
 """
 import random
 
@@ -27,11 +29,12 @@ DEV = "cuda"
 
 
 def option_grads_case(w, seed, ngroups=0, phase="native", premix=False, with_state=True,
-                      with_dh=True, method="auto", label=""):
-    say("case %s [%s]: B%d L%d H%d R%d P%d N%d %s groups=%d phase=%s premix=%s state=%s seed=%d"
-        % (label, method, w.batch, w.seqlen, w.heads, w.rank, w.headdim, w.dstate, w.io_dtype,
-           ngroups, phase, premix, with_state, seed))
-    inp, ex = synth.make_option_inputs(w, seed, DEV, ngroups=ngroups, phase=phase, premix=premix)
+                      with_dh=True, method="auto", label="", a_tok=False):
+    say("case %s [%s]: B%d L%d H%d R%d P%d N%d %s groups=%d phase=%s premix=%s a_tok=%s state=%s "
+        "seed=%d" % (label, method, w.batch, w.seqlen, w.heads, w.rank, w.headdim, w.dstate,
+                     w.io_dtype, ngroups, phase, premix, a_tok, with_state, seed))
+    inp, ex = synth.make_option_inputs(w, seed, DEV, ngroups=ngroups, phase=phase, premix=premix,
+                                       a_per_token=a_tok)
     g = torch.Generator(device=DEV).manual_seed(seed + 1)
     dy = torch.randn(inp["x"].shape, generator=g, device=DEV).to(w.torch_dtype)
     dh = torch.randn(w.batch, w.heads, w.dstate, w.headdim, generator=g, device=DEV) if with_dh else None
@@ -39,7 +42,7 @@ def option_grads_case(w, seed, ngroups=0, phase="native", premix=False, with_sta
     theta = None if phase == "zero" else inp["theta"]
     got = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], theta, inp["lam"], dy,
                       State(*st) if st else None, dh, method=method, ngroups=ngroups, phase=phase,
-                      perm=ex.get("perm"), premix=opt.premix_obj(ex))
+                      perm=ex.get("perm"), premix=opt.premix_obj(ex), A_per_token=a_tok)
     torch.cuda.synchronize()
     ref = scan_backward(f64(inp["x"]), f64(inp["B"]), f64(inp["C"]), f64(inp["dt"]),
                         f64(inp["A"]), f64(inp["theta"]), f64(inp["lam"]), f64(dy),
@@ -51,7 +54,7 @@ def option_grads_case(w, seed, ngroups=0, phase="native", premix=False, with_sta
     tol = TOL[w.io_dtype]
     errs = {}
     for n in bwd.NAMES:
-        if n == "dA":
+        if n == "dA" and not a_tok:
             errs[n] = float(np.max(np.abs(f64(got.dA) - ref["dA"])) / max(np.max(ref["dA_scale"]), 1e-300))
         else:
             errs[n] = rel_err(f64(getattr(got, n)), ref[bwd.ORACLE.get(n, n)])
@@ -71,26 +74,29 @@ def option_grads_case(w, seed, ngroups=0, phase="native", premix=False, with_sta
     return got
 
 
-COMBOS = [(2, "native", False), (0, "reverse", False), (0, "shuffle", False), (0, "zero", False),
-          (0, "native", True), (2, "shuffle", True), (1, "zero", True), (4, "reverse", True)]
+COMBOS = [(2, "native", False, False), (0, "reverse", False, False), (0, "shuffle", False, False),
+          (0, "zero", False, False), (0, "native", True, False), (2, "shuffle", True, False),
+          (1, "zero", True, False), (4, "reverse", True, False), (0, "native", False, True),
+          (2, "shuffle", True, True)]
 
 
 @pytest.mark.parametrize("method", ["step", "chunked"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("ngroups,phase,premix", COMBOS)
-def test_bwd_options(ngroups, phase, premix, io, method):
+@pytest.mark.parametrize("ngroups,phase,premix,a_tok", COMBOS)
+def test_bwd_options(ngroups, phase, premix, a_tok, io, method):
     """Several chunks (32 tokens at rank 2) and checkpoints, ragged tail."""
     w = workload(2, 70, 4, 2, 32, 64, io=io, dt_mu=-1.0, theta="uniform_pi")
-    option_grads_case(w, 1200 + 10 * COMBOS.index((ngroups, phase, premix)) + (io == "bf16"),
-                      ngroups, phase, premix, method=method, label="bwd-options")
+    option_grads_case(w, 1200 + 10 * COMBOS.index((ngroups, phase, premix, a_tok)) + (io == "bf16"),
+                      ngroups, phase, premix, method=method, label="bwd-options", a_tok=a_tok)
 
 
 @pytest.mark.parametrize("method", ["step", "chunked"])
 def test_bwd_options_longer_dstate128(method):
-    """bf16, dstate 128, rank 4 (16-token chunks), 300 tokens, head groups,
-    shuffled phases and the pre-mixer together."""
+    """bf16, dstate 128, rank 4 (16-token chunks), 300 tokens, per-token decay,
+    head groups, shuffled phases and the pre-mixer together."""
     w = workload(1, 300, 4, 4, 64, 128, io="bf16", dt_mu=-2.0)
-    option_grads_case(w, 1300, 2, "shuffle", True, method=method, label="bwd-options-long")
+    option_grads_case(w, 1300, 2, "shuffle", True, method=method, label="bwd-options-long",
+                      a_tok=True)
 
 
 def test_bwd_options_without_state_or_final_gradient():
@@ -103,7 +109,7 @@ def test_bwd_options_empty_sequence():
     """seqlen 0: the state-record gradients pass through, the parameter
     gradients are zero."""
     w = workload(2, 0, 2, 1, 32, 32, io="f32", dt_mu=-1.0)
-    got = option_grads_case(w, 1320, 1, "shuffle", True, label="bwd-options-empty")
+    got = option_grads_case(w, 1320, 1, "shuffle", True, label="bwd-options-empty", a_tok=True)
     for n in PREMIX_GRADS:
         assert torch.count_nonzero(getattr(got.premix, n[1:])) == 0, n
 
@@ -134,7 +140,7 @@ def draw_bwd_options(case):
                 Bt=rnd.randint(1, 2), H=H,
                 groups=rnd.choice([0] + [g for g in (1, 2, 3) if H % g == 0 and g < H]),
                 phase=rnd.choice(["native", "zero", "reverse", "shuffle"]),
-                premix=rnd.random() < 0.5, with_state=rnd.random() < 0.7,
+                premix=rnd.random() < 0.5, a_tok=rnd.random() < 0.3, with_state=rnd.random() < 0.7,
                 dt_mu=rnd.choice([-2.0, -1.0, 0.0]))
 
 
@@ -148,4 +154,5 @@ def test_random_bwd_options_case(case):
     methods = ["step"] + (["chunked"] if bwd.chunked_ok(c["io"], c["N"], c["P"], c["R"]) else [])
     for m in methods:
         option_grads_case(w, 9950 + case, c["groups"], c["phase"], c["premix"],
-                          with_state=c["with_state"], method=m, label="random bwd options %d" % case)
+                          with_state=c["with_state"], method=m, label="random bwd options %d" % case,
+                          a_tok=c["a_tok"])
