@@ -142,3 +142,54 @@ def scan_backward(x, Bm, Cm, dt, A, theta, lam, dy, dh=None, h0=None, Bprev=None
     out["dA"] = terms.sum(axis=(0, 1))
     out["dA_scale"] = np.abs(terms).sum(axis=(0, 1))
     return out
+
+
+def scan_backward_packed(x, Bm, Cm, dt, A, theta, lam, cu_seqlens, dy, dh=None, h0=None,
+                         Bprev=None, xprev=None, **options):
+    """Gradients for packed sequences (oracle.scan_packed's layout: token arrays
+    [1, T, ...], sequence i = tokens cu_seqlens[i] .. cu_seqlens[i+1]-1, one
+    state record and one dh row per sequence).  Each sequence is an independent
+    scan, so its gradients are scan_backward's on its own tokens and record;
+    the token gradients are placed back at the sequence's tokens, the decay
+    rate's and the pre-mixer's parameter gradients add over the sequences."""
+    cu = [int(v) for v in np.asarray(cu_seqlens).ravel()]
+    nseq = len(cu) - 1
+    x = np.asarray(x, dtype=np.float64)
+    _, T, H, R, P = x.shape
+    N = np.asarray(Bm).shape[-1]
+    A = np.asarray(A, dtype=np.float64)
+    z = lambda *s: np.zeros(s)
+    h0 = z(nseq, H, N, P) if h0 is None else np.asarray(h0, dtype=np.float64)
+    Bprev = z(nseq, H, R, N) if Bprev is None else np.asarray(Bprev, dtype=np.float64)
+    xprev = z(nseq, H, R, P) if xprev is None else np.asarray(xprev, dtype=np.float64)
+    tok_names = {"dx": x, "dB": Bm, "dC": Cm, "ddt": dt, "dtheta": theta, "dlam": lam}
+    out = {n: np.zeros(np.shape(v)) for n, v in tok_names.items()}
+    out["dA"] = np.zeros(A.shape)
+    out["dA_scale"] = np.zeros(A.shape)
+    out["dh0"], out["dBprev"], out["dxprev"] = z(nseq, H, N, P), z(nseq, H, R, N), z(nseq, H, R, P)
+    for i in range(nseq):
+        sl = slice(cu[i], cu[i + 1])
+        g = scan_backward(x[:, sl], np.asarray(Bm)[:, sl], np.asarray(Cm)[:, sl],
+                          np.asarray(dt)[:, sl], A[:, sl] if A.ndim == 3 else A,
+                          np.asarray(theta)[:, sl], np.asarray(lam)[:, sl],
+                          np.asarray(dy)[:, sl], None if dh is None else np.asarray(dh)[i:i + 1],
+                          h0=h0[i:i + 1], Bprev=Bprev[i:i + 1], xprev=xprev[i:i + 1], **options)
+        for n in tok_names:
+            out[n][:, sl] = g[n]
+        if A.ndim == 3:
+            out["dA"][:, sl] = g["dA"]
+            out["dA_scale"][:, sl] = g["dA_scale"]
+        else:
+            out["dA"] += g["dA"]
+            out["dA_scale"] += g["dA_scale"]
+        for n in ("dh0", "dBprev", "dxprev"):
+            out[n][i:i + 1] = g[n]
+        for n in PREMIX_GRADS:
+            if n in g:
+                out[n] = out.get(n, 0.0) + g[n]
+    if options.get("premix") is not None:
+        pm = options["premix"]
+        for n in PREMIX_GRADS:
+            if n not in out:
+                out[n] = np.zeros(np.shape(pm[n[1:]]))
+    return out

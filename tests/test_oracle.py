@@ -758,6 +758,45 @@ def test_backward_per_token_decay_matches_finite_differences():
         assert err < 1e-6, (name, err)
 
 
+def test_backward_packed_matches_finite_differences():
+    """Packed sequences (one empty) with head groups and the pre-mixer:
+    every gradient against central differences of oracle.scan_packed's loss,
+    the record gradients one row per sequence and the parameter gradients
+    summed over the sequences."""
+    from oracle.backward import PREMIX_GRADS, scan_backward_packed
+    rng = np.random.default_rng(42)
+    cu = np.array([0, 3, 3, 7])
+    ins, dy, _, kw, pm = _bwd_option_case(rng, 1, "reverse", True, Bt=1, L=7, H=2, R=1, P=2, N=4)
+    nseq = len(cu) - 1
+    ins[7] = rng.standard_normal((nseq, 2, 4, 2))
+    ins[8] = rng.standard_normal((nseq, 2, 1, 4))
+    ins[9] = rng.standard_normal((nseq, 2, 1, 2))
+    dh = rng.standard_normal((nseq, 2, 4, 2))
+    g = scan_backward_packed(*ins[:7], cu, dy, dh, h0=ins[7], Bprev=ins[8], xprev=ins[9],
+                             premix=pm, **kw)
+    pnames = list(PREMIX_GRADS)
+    params = [pm[n[1:]] for n in pnames]
+
+    def loss(args, prm):
+        pmx = dict(zip([n[1:] for n in pnames], prm), eps=pm["eps"])
+        y, hs, _, _ = oracle.scan_packed(*args[:7], cu, h0=args[7], Bprev=args[8], xprev=args[9],
+                                         premix=pmx, **kw)
+        return float(np.sum(y * dy) + np.sum(hs * dh))
+    names = ["dx", "dB", "dC", "ddt", "dA", "dtheta", "dlam", "dh0", "dBprev", "dxprev"]
+    eps = 1e-6
+    for k, name in enumerate(names + pnames):
+        base = ins[k] if k < len(names) else params[k - len(names)]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            plus, minus = [a.copy() for a in ins], [a.copy() for a in ins]
+            pp, pmn = [a.copy() for a in params], [a.copy() for a in params]
+            (plus[k] if k < len(names) else pp[k - len(names)])[idx] += eps
+            (minus[k] if k < len(names) else pmn[k - len(names)])[idx] -= eps
+            fd[idx] = (loss(plus, pp) - loss(minus, pmn)) / (2 * eps)
+        err = np.max(np.abs(fd - g[name])) / max(np.max(np.abs(g[name])), 1e-12)
+        assert err < 1e-6, (name, err)
+
+
 @pytest.mark.parametrize("ngroups,phase,premix", OPTION_GRAD_CASES)
 def test_backward_options_forward_matches_c_oracle(ngroups, phase, premix):
     """The gradient oracle's option maps (group repeat, phase transform,
