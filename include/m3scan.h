@@ -293,8 +293,14 @@ typedef struct {
  *                NULL parameter is differentiated at its default, ones or
  *                zeros).  The state record (B_prev_in) holds the pre-mixed B,
  *                as m3_scan_fwd writes it, and dB_prev is with respect to it.
- *   cu_seqlens, phase_in and phase_out are not supported here
- *   (M3_ERR_UNSUPPORTED), nor the decode-only phase modes (M3_ERR_OPTION).
+ *   cu_seqlens   packed sequences as in m3_scan_fwd: token arrays and their
+ *                gradients [seqlen, nheads, ...], one state record, dh_out
+ *                and record gradient per sequence; the gradient runs on a
+ *                padded batch of max_seqlen tokens per sequence (zero steps
+ *                past each end, which leave the state unchanged), so the
+ *                workspace grows with batch * max_seqlen
+ *   phase_in and phase_out are not supported here (M3_ERR_UNSUPPORTED), nor
+ *   the decode-only phase modes (M3_ERR_OPTION).
  * With options, the inputs are first materialised in the workspace as the
  * recurrence uses them, and the gradients are mapped back afterwards.
  * Every output is written (no accumulation into the caller's buffers); the

@@ -467,19 +467,25 @@ def m3_scan_bwd_supported(dstate: int, headdim: int, rank: int, io_dtype: int,
 
 def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace,
                  method="auto", ngroups=0, phase="native", perm=None, premix=None,
-                 A_per_token=False):
+                 A_per_token=False, cu_seqlens=None, max_seqlen=None):
     lib = load_library()
-    Bt, L, H, R, P = x.shape
+    Bx, L, H, R, P = x.shape
     N = B.shape[-1]
     G = int(ngroups) if ngroups else H
     io = _io_code(x.dtype)
     zero = phase == "zero"
-    for t, n, shp, dt_ in ((x, "x", (Bt, L, H, R, P), x.dtype), (B, "B", (Bt, L, G, R, N), x.dtype),
-                           (C, "C", (Bt, L, G, R, N), x.dtype), (dt, "dt", (Bt, L, H), torch.float32),
-                           (lam, "lam", (Bt, L, H), torch.float32),
-                           (theta, "theta", (Bt, L, H, N // 2), torch.float32),
-                           (A, "A", (Bt, L, H) if A_per_token else (H,), torch.float32),
-                           (dy, "dy", (Bt, L, H, R, P), x.dtype)):
+    Bt = Bx
+    if cu_seqlens is not None:
+        if Bx != 1:
+            raise ValueError("packed sequences: token arrays must have a leading dimension of 1")
+        _check(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32)
+        Bt = cu_seqlens.numel() - 1     # sequences: the state record's batch
+    for t, n, shp, dt_ in ((x, "x", (Bx, L, H, R, P), x.dtype), (B, "B", (Bx, L, G, R, N), x.dtype),
+                           (C, "C", (Bx, L, G, R, N), x.dtype), (dt, "dt", (Bx, L, H), torch.float32),
+                           (lam, "lam", (Bx, L, H), torch.float32),
+                           (theta, "theta", (Bx, L, H, N // 2), torch.float32),
+                           (A, "A", (Bx, L, H) if A_per_token else (H,), torch.float32),
+                           (dy, "dy", (Bx, L, H, R, P), x.dtype)):
         if t is None and n == "theta" and zero:
             continue
         _check(t, n, shp, dt_)
@@ -497,7 +503,7 @@ def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, wor
                     torch.empty(H, R, N, **f32), torch.empty(H, **f32), premix.eps)
     g = ScanGrads(torch.empty(x.shape, **f32), torch.empty(B.shape, **f32),
                   torch.empty(C.shape, **f32), torch.empty(dt.shape, **f32),
-                  torch.empty(A.shape, **f32), torch.empty(Bt, L, H, N // 2, **f32),
+                  torch.empty(A.shape, **f32), torch.empty(Bx, L, H, N // 2, **f32),
                   torch.empty(lam.shape, **f32),
                   torch.empty(Bt, H, N, P, **f32) if state_grads else None,
                   torch.empty(Bt, H, R, N, **f32) if state_grads else None,
@@ -514,6 +520,10 @@ def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, wor
                     dx=_ptr(g.dx), dB=_ptr(g.dB), dC=_ptr(g.dC), ddt=_ptr(g.ddt), dA=_ptr(g.dA),
                     dtheta=_ptr(g.dtheta), dlam=_ptr(g.dlam), dh_in=_ptr(g.dh_in),
                     dB_prev=_ptr(g.dB_prev), dx_prev=_ptr(g.dx_prev), opt=opt)
+    if cu_seqlens is not None:
+        a.opt.cu_seqlens = cu_seqlens.data_ptr()
+        a.opt.max_seqlen = int(L if max_seqlen is None else max_seqlen)
+        keep.append(cu_seqlens)
     if pg is not None:
         a.dB_norm_w, a.dC_norm_w = _ptr(pg.B_norm_w), _ptr(pg.C_norm_w)
         a.dB_bias, a.dC_bias, a.ddt_bias = _ptr(pg.B_bias), _ptr(pg.C_bias), _ptr(pg.dt_bias)
@@ -530,6 +540,7 @@ def m3_scan_bwd(x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
                 workspace: Optional[torch.Tensor] = None, method: str = "auto",
                 ngroups: int = 0, phase: str = "native", perm: Optional[torch.Tensor] = None,
                 premix: Optional[Premix] = None, A_per_token: bool = False,
+                cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
                 stream=None) -> ScanGrads:
     """Gradients of sum(dy * y) + sum(dh_out * h_L) of m3_scan_fwd with respect
     to every input; ``state_grads`` also returns those of the input state
@@ -537,10 +548,14 @@ def m3_scan_bwd(x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
     (reverse mode of the chunked form), "step" (adjoint recurrence step by
     step) or "auto" (chunked where supported).  Options as m3_scan_fwd takes
     them (A per token, head groups, the phase modes of a scan, the
-    pre-mixer); with ``A_per_token`` dA is per token, with ``premix`` the
-    result's ``premix`` field holds the parameter gradients."""
+    pre-mixer, packed sequences); with ``A_per_token`` dA is per token, with
+    ``premix`` the result's ``premix`` field holds the parameter gradients.
+    Packed sequences: token arrays [1, T, ...], ``cu_seqlens`` int32 [nseq+1],
+    one state record, dh_out and record gradient row per sequence;
+    ``max_seqlen`` (default T) sizes the padded batch the gradient runs on."""
     a, g, _, _keep = _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads,
-                                  workspace, method, ngroups, phase, perm, premix, A_per_token)
+                                  workspace, method, ngroups, phase, perm, premix, A_per_token,
+                                  cu_seqlens, max_seqlen)
     st = load_library().m3_scan_bwd(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_bwd")

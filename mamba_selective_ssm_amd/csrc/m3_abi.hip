@@ -208,6 +208,13 @@ struct BwdPlan {
     bool opt_bc, opt_scal, opt_theta;
     int64_t groups;
     size_t be_bytes, dbe_bytes, se_bytes, te_bytes, q_bytes, sum_bytes;
+    // Packed sequences: the plain gradient runs on a padded batch of
+    // [batch][max_seqlen] tokens (inputs and gradients), packed <-> padded
+    // around it.
+    bool packed;
+    int64_t Lp;                 // max_seqlen
+    size_t px_bytes, pb_bytes, ps_bytes, pt_bytes;        // io rows x, B; float rows dt, theta
+    size_t gx_bytes, gb_bytes, gs_bytes;                  // float32 gradient rows
     size_t ws;
 };
 
@@ -223,14 +230,14 @@ bool bwd_method_ok(int method, int64_t N, int64_t P, int64_t R, int io)
 m3_status plan_bwd_core(const m3_scan_bwd_args* a, BwdPlan* out);
 
 // The options a gradient call supports (per-token decay, head groups, the
-// phase maps of a scan, the pre-mixer) and the workspace of their maps.
+// phase maps of a scan, the pre-mixer, packed sequences) and the workspace of
+// their maps.
 m3_status plan_bwd_options(const m3_scan_bwd_args* a, BwdPlan* out)
 {
     const m3_options& o = a->opt;
     const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
-    const int64_t N = a->dstate, R = a->rank;
-    if (o.cu_seqlens != nullptr || o.phase_in != nullptr || o.phase_out != nullptr)
-        return M3_ERR_UNSUPPORTED;
+    const int64_t P = a->headdim, N = a->dstate, R = a->rank;
+    if (o.phase_in != nullptr || o.phase_out != nullptr) return M3_ERR_UNSUPPORTED;
     if (o.A_per_token != 0 && o.A_per_token != 1) return M3_ERR_OPTION;
     if (o.phase_mode < M3_PHASE_NATIVE || o.phase_mode > M3_PHASE_SHUFFLE) return M3_ERR_OPTION;
     if (o.ngroups < 0 || (o.ngroups > 0 && H > 0 && H % o.ngroups != 0)) return M3_ERR_OPTION;
@@ -245,29 +252,54 @@ m3_status plan_bwd_options(const m3_scan_bwd_args* a, BwdPlan* out)
     out->opt_theta = o.phase_mode != M3_PHASE_NATIVE;
     // the option maps move rows of dstate values 4 at a time, pairs through LDS
     if ((out->opt_bc || out->opt_theta) && (N > 256 || N % 4 != 0)) return M3_ERR_UNSUPPORTED;
-    const size_t tok = (size_t)Bt * L * H, es = (size_t)io_size(a->io_dtype);
+    // token rows of the caller's arrays (packed: one row of seqlen tokens)
+    const int64_t BtL = (out->packed ? 1 : Bt) * L;
+    const size_t tok = (size_t)BtL * H, es = (size_t)io_size(a->io_dtype);
     if (out->opt_bc) {
         out->be_bytes = round256(tok * R * N * es);
         out->dbe_bytes = round256(tok * R * N * 4);
     }
     if (out->opt_scal) {
         out->se_bytes = round256(tok * 4);
-        out->q_bytes = round256(m3::bwd_options_gain_floats(Bt * L, out->groups, (int)N, (int)R) * 4);
-        out->sum_bytes = round256(m3::bwd_options_partial_floats(Bt * L, H, out->groups, (int)N,
+        out->q_bytes = round256(m3::bwd_options_gain_floats(BtL, out->groups, (int)N, (int)R) * 4);
+        out->sum_bytes = round256(m3::bwd_options_partial_floats(BtL, H, out->groups, (int)N,
                                                                   (int)R) * 4);
     }
     if (out->opt_theta) out->te_bytes = round256(tok * (N / 2) * 4);
+    if (out->packed) {
+        const size_t tp = (size_t)Bt * out->Lp * H;
+        out->px_bytes = round256(tp * R * P * es);
+        out->pb_bytes = round256(tp * R * N * es);
+        out->ps_bytes = round256(tp * 4);
+        out->pt_bytes = round256(tp * (N / 2) * 4);
+        out->gx_bytes = round256(tp * R * P * 4);
+        out->gb_bytes = round256(tp * R * N * 4);
+        out->gs_bytes = round256(tp * 4);
+    }
     if (Bt * H == 0) return M3_OK;
+    // padded: x, dy; B, C; dt, lam, A; theta; dx; dB, dC; ddt, dlam, dA; dtheta
     out->ws = out->core_ws + 2 * out->be_bytes + 2 * out->dbe_bytes + 2 * out->se_bytes +
-              2 * out->te_bytes + out->q_bytes + out->sum_bytes;
+              2 * out->te_bytes + out->q_bytes + out->sum_bytes + 2 * out->px_bytes +
+              2 * out->pb_bytes + 3 * out->ps_bytes + 2 * out->pt_bytes + out->gx_bytes +
+              2 * out->gb_bytes + 3 * out->gs_bytes;
     return M3_OK;
 }
 
 m3_status plan_bwd(const m3_scan_bwd_args* a, BwdPlan* out)
 {
-    const m3_status s = plan_bwd_core(a, out);
+    if (a == nullptr) return M3_ERR_NULL;
+    // packed sequences: the plain gradient's part is that of the padded batch
+    m3_scan_bwd_args core = *a;
+    const bool packed = a->opt.cu_seqlens != nullptr;
+    if (packed) {
+        if (a->opt.max_seqlen < 0 || a->opt.max_seqlen > a->seqlen) return M3_ERR_OPTION;
+        core.seqlen = a->opt.max_seqlen;
+    }
+    const m3_status s = plan_bwd_core(&core, out);
     if (s != M3_OK) return s;
     out->core_ws = out->ws;
+    out->packed = packed;
+    out->Lp = packed ? a->opt.max_seqlen : a->seqlen;
     return plan_bwd_options(a, out);
 }
 
@@ -373,7 +405,9 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
     for (const void* q : ptrs)
         if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
     const int e = io_size(a->io_dtype);
-    const int64_t tok = Bt * L * H, tokg = Bt * L * plan.groups;
+    // token arrays: batch rows x seqlen, or one row of seqlen packed tokens
+    const int64_t rowsL = (plan.packed ? 1 : Bt) * L;
+    const int64_t tok = rowsL * H, tokg = rowsL * plan.groups;
     const int64_t nA = a->opt.A_per_token ? tok : H;       // A and dA
     Range in[20] = {
         range_of(a->x, tok * R * P * e),         range_of(a->B, tokg * R * N * e),
@@ -414,9 +448,9 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
     m3::BwdOptParams bo;
     memset(&bo, 0, sizeof(bo));
     const bool opts = plan.opt_bc || plan.opt_scal || plan.opt_theta;
+    char* w = static_cast<char*>(a->workspace) + plan.core_ws;
+    auto take = [&w](size_t bytes) { char* q = bytes ? w : nullptr; w += bytes; return q; };
     if (opts) {
-        char* w = static_cast<char*>(a->workspace) + plan.core_ws;
-        auto take = [&w](size_t bytes) { char* q = bytes ? w : nullptr; w += bytes; return q; };
         bo.B = a->B; bo.C = a->C; bo.dt = a->dt; bo.lam = a->lam; bo.theta = theta_in;
         bo.opt = op;
         bo.Be = take(plan.be_bytes);
@@ -434,7 +468,7 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         bo.dB = a->dB; bo.dC = a->dC; bo.ddt = a->ddt; bo.dlam = a->dlam; bo.dtheta = a->dtheta;
         bo.dBw = a->dB_norm_w; bo.dCw = a->dC_norm_w; bo.dBb = a->dB_bias; bo.dCb = a->dC_bias;
         bo.ddtb = a->ddt_bias;
-        bo.BtL = Bt * L; bo.H = H; bo.G = plan.groups; bo.N = (int)N; bo.R = (int)R;
+        bo.BtL = rowsL; bo.H = H; bo.G = plan.groups; bo.N = (int)N; bo.R = (int)R;
         if (plan.opt_bc) { Bx = bo.Be; Cx = bo.Ce; dBx = dBe; dCx = dCe; }
         if (plan.opt_scal) { dtx = bo.dte; lamx = bo.lame; }
         if (plan.opt_theta) { thx = bo.thetae; dthx = dthe; }
@@ -442,15 +476,63 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         if (e0 != hipSuccess) return hip_status(e0);
     }
 
+    // The plain gradient's operands: as above, or (packed sequences) those
+    // moved into a padded batch of max_seqlen tokens per sequence, zero past
+    // each sequence's end -- a zero step dt_t makes a padding step the
+    // identity (no decay, rotation or input), so the padded batch has the
+    // packed sequences' gradients.
+    const void *xc = a->x, *Bc = Bx, *Cc = Cx, *dyc = a->dy;
+    const float *dtc = dtx, *lamc = lamx, *thc = thx, *Ac = a->A;
+    float *dxc = a->dx, *dBc = dBx, *dCc = dCx, *ddtc = a->ddt, *dlamc = a->dlam, *dthc = dthx;
+    float* dAc = a->dA;
+    const int64_t Lc = plan.Lp;
+    m3::PackParams un;
+    memset(&un, 0, sizeof(un));
+    if (plan.packed) {
+        m3::PackParams pk;
+        memset(&pk, 0, sizeof(pk));
+        pk.cu = a->opt.cu_seqlens; pk.nseq = Bt; pk.T = L; pk.maxL = plan.Lp;
+        un = pk;
+        un.unpack = 1;
+        const int wx = (int)(H * R * P * e / 4), wb = (int)(H * R * N * e / 4), ws = (int)H;
+        const int wt = (int)(H * (N / 2)), wgx = (int)(H * R * P), wgb = (int)(H * R * N);
+        auto move = [](m3::PackParams& q, const void* s, void* d, int words) {
+            q.src[q.n] = s; q.dst[q.n] = d; q.words[q.n] = words; ++q.n;
+        };
+        void* px = take(plan.px_bytes); void* pdy = take(plan.px_bytes);
+        void* pB = take(plan.pb_bytes); void* pC = take(plan.pb_bytes);
+        float* pdt = reinterpret_cast<float*>(take(plan.ps_bytes));
+        float* plam = reinterpret_cast<float*>(take(plan.ps_bytes));
+        float* pA = reinterpret_cast<float*>(take(plan.ps_bytes));
+        float* pth = reinterpret_cast<float*>(take(plan.pt_bytes));
+        float* gth = reinterpret_cast<float*>(take(plan.pt_bytes));
+        float* gx = reinterpret_cast<float*>(take(plan.gx_bytes));
+        float* gB = reinterpret_cast<float*>(take(plan.gb_bytes));
+        float* gC = reinterpret_cast<float*>(take(plan.gb_bytes));
+        float* gdt = reinterpret_cast<float*>(take(plan.gs_bytes));
+        float* glam = reinterpret_cast<float*>(take(plan.gs_bytes));
+        float* gA = reinterpret_cast<float*>(take(plan.gs_bytes));
+        move(pk, a->x, px, wx); move(pk, a->dy, pdy, wx);
+        move(pk, Bx, pB, wb); move(pk, Cx, pC, wb);
+        move(pk, dtx, pdt, ws); move(pk, lamx, plam, ws); move(pk, thx, pth, wt);
+        move(un, gx, a->dx, wgx); move(un, gB, dBx, wgb); move(un, gC, dCx, wgb);
+        move(un, gdt, a->ddt, ws); move(un, glam, a->dlam, ws); move(un, gth, dthx, wt);
+        if (a->opt.A_per_token) { move(pk, a->A, pA, ws); move(un, gA, a->dA, ws); Ac = pA; dAc = gA; }
+        xc = px; dyc = pdy; Bc = pB; Cc = pC; dtc = pdt; lamc = plam; thc = pth;
+        dxc = gx; dBc = gB; dCc = gC; ddtc = gdt; dlamc = glam; dthc = gth;
+        const hipError_t e1 = m3::launch_bwd_pack(pk, st);
+        if (e1 != hipSuccess) return hip_status(e1);
+    }
+
     hipError_t err;
     if (plan.method == M3_BWD_CHUNKED) {
         m3::BcParams q;
         memset(&q, 0, sizeof(q));
-        q.x = a->x; q.B = Bx; q.C = Cx; q.dy = a->dy;
-        q.dt = dtx; q.A = a->A; q.theta = thx; q.lam = lamx;
+        q.x = xc; q.B = Bc; q.C = Cc; q.dy = dyc;
+        q.dt = dtc; q.A = Ac; q.theta = thc; q.lam = lamc;
         q.h_in = a->h_in; q.Bp_in = a->B_prev_in; q.xp_in = a->x_prev_in; q.dh_out = a->dh_out;
-        q.dx = a->dx; q.dB = dBx; q.dC = dCx; q.ddt = a->ddt; q.dtheta = dthx;
-        q.dlam = a->dlam; q.dh_in = a->dh_in; q.dBp = a->dB_prev; q.dxp = a->dx_prev; q.dA = a->dA;
+        q.dx = dxc; q.dB = dBc; q.dC = dCc; q.ddt = ddtc; q.dtheta = dthc;
+        q.dlam = dlamc; q.dh_in = a->dh_in; q.dBp = a->dB_prev; q.dxp = a->dx_prev; q.dA = dAc;
         char* w = static_cast<char*>(a->workspace);
         q.loc = w;
         w += plan.loc_bytes;
@@ -466,18 +548,18 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         w += plan.chunk_bytes;
         q.dA_bh = reinterpret_cast<float*>(w);
         q.a_tok = a->opt.A_per_token;
-        q.L = L; q.H = H; q.N = (int)N; q.P = (int)P; q.R = (int)R;
+        q.L = Lc; q.H = H; q.N = (int)N; q.P = (int)P; q.R = (int)R;
         q.nbh = (int)nbh;
         q.nc = (int)plan.nc;
         err = m3::launch_bwd_chunked(q, a->io_dtype, st);
     } else {
         m3::BwdParams p;
         memset(&p, 0, sizeof(p));
-        p.x = a->x; p.B = Bx; p.C = Cx; p.dy = a->dy;
-        p.dt = dtx; p.A = a->A; p.theta = thx; p.lam = lamx;
+        p.x = xc; p.B = Bc; p.C = Cc; p.dy = dyc;
+        p.dt = dtc; p.A = Ac; p.theta = thc; p.lam = lamc;
         p.h_in = a->h_in; p.Bp_in = a->B_prev_in; p.xp_in = a->x_prev_in; p.dh_out = a->dh_out;
-        p.dx = a->dx; p.dB = dBx; p.dC = dCx; p.ddt = a->ddt; p.dtheta = dthx;
-        p.dlam = a->dlam; p.dh_in = a->dh_in; p.dBp = a->dB_prev; p.dxp = a->dx_prev;
+        p.dx = dxc; p.dB = dBc; p.dC = dCc; p.ddt = ddtc; p.dtheta = dthc;
+        p.dlam = dlamc; p.dh_in = a->dh_in; p.dBp = a->dB_prev; p.dxp = a->dx_prev;
         char* ws = static_cast<char*>(a->workspace);
         p.ckpt = reinterpret_cast<float*>(ws);
         ws += plan.ck_bytes;
@@ -491,14 +573,15 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         ws += plan.dxp_bytes;
         p.dA_part = reinterpret_cast<float*>(ws);
         p.a_tok = a->opt.A_per_token;
-        p.dAt = a->dA;
-        p.L = L; p.H = H; p.N = (int)N; p.P = (int)P; p.R = (int)R;
-        p.ntok = Bt * L * H;
+        p.dAt = dAc;
+        p.L = Lc; p.H = H; p.N = (int)N; p.P = (int)P; p.R = (int)R;
+        p.ntok = Bt * Lc * H;
         p.nbh = (int)nbh;
         p.parts = plan.parts;
         p.TB = plan.TB; p.K = plan.K;
         err = m3::launch_bwd(p, a->io_dtype, a->dA, st);
     }
+    if (err == hipSuccess && plan.packed) err = m3::launch_bwd_pack(un, st);
     if (err != hipSuccess || !opts) return hip_status(err);
     return hip_status(m3::launch_bwd_options_post(bo, a->io_dtype, st));
 }

@@ -314,6 +314,33 @@ __global__ void __launch_bounds__(kThreads) bo_post_theta_kernel(BwdOptParams p)
     }
 }
 
+// Token rows between packed and padded layouts: one block per padded token
+// (s, t); a sequence's offsets are clamped into [0, T] and its length to maxL
+// (bad offsets give wrong results, never accesses outside the arrays).
+__global__ void __launch_bounds__(kThreads) bo_pack_kernel(PackParams q)
+{
+    const int64_t ntok = q.nseq * q.maxL;
+    for (int64_t i = blockIdx.x; i < ntok; i += gridDim.x) {
+        const int64_t s = i / q.maxL, t = i % q.maxL;
+        int64_t st = q.cu[s], en = q.cu[s + 1];
+        st = st < 0 ? 0 : (st > q.T ? q.T : st);
+        en = en < st ? st : (en > q.T ? q.T : en);
+        const int64_t len = en - st < q.maxL ? en - st : q.maxL;
+        const bool real = t < len;
+        if (q.unpack && !real) continue;                // uniform over the block
+        for (int k = 0; k < q.n; ++k) {
+            const int W = q.words[k];
+            const uint32_t* src = static_cast<const uint32_t*>(q.src[k]);
+            uint32_t* dst = static_cast<uint32_t*>(q.dst[k]);
+            const int64_t pad = i * W, pk = (st + t) * W;
+            for (int w = threadIdx.x; w < W; w += kThreads) {
+                if (q.unpack) dst[pk + w] = src[pad + w];
+                else dst[pad + w] = real ? src[pk + w] : 0u;
+            }
+        }
+    }
+}
+
 // Column sums of a [rows][cols] float32 array, stage 1: block (x, y) = 64
 // columns x 4 row lanes over rows y*rpc .. y*rpc + rpc - 1; lane k takes every
 // 4th row from k, then the 4 lanes are added in order into part[y][cols].
@@ -473,6 +500,15 @@ size_t bwd_options_partial_floats(int64_t BtL, int64_t H, int64_t G, int N, int 
 size_t bwd_options_gain_floats(int64_t BtL, int64_t G, int N, int R)
 {
     return 2 * (size_t)row_grid(BtL * G * R, N) * (size_t)N;
+}
+
+hipError_t launch_bwd_pack(const PackParams& p, hipStream_t stream)
+{
+    const int64_t ntok = p.nseq * p.maxL;
+    if (ntok <= 0 || p.n <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)(ntok < 8192 ? ntok : 8192);
+    hipLaunchKernelGGL(bo_pack_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_options_pre(const BwdOptParams& p, int io_dtype, hipStream_t stream)

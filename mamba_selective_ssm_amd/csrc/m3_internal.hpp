@@ -119,6 +119,19 @@ struct BwdOptParams {
     int64_t BtL, H, G;
     int N, R;
 };
+// Packed sequences around the gradient: token rows moved between the packed
+// arrays ([T] token rows, sequence s = rows cu[s] .. cu[s+1]-1) and a padded
+// batch ([nseq][maxL] token rows, zero past each sequence's end).
+struct PackParams {
+    const int* cu;            // [nseq + 1], clamped on the device
+    int64_t nseq, T, maxL;
+    int n;                    // arrays moved by one launch
+    int unpack;               // 0: packed -> padded; 1: padded -> packed (real tokens only)
+    const void* src[8];
+    void* dst[8];
+    int words[8];             // 4-byte words per token row
+};
+hipError_t launch_bwd_pack(const PackParams& p, hipStream_t stream);
 size_t bwd_options_partial_floats(int64_t BtL, int64_t H, int64_t G, int N, int R);
 size_t bwd_options_gain_floats(int64_t BtL, int64_t G, int N, int R);
 hipError_t launch_bwd_options_pre(const BwdOptParams& p, int io_dtype, hipStream_t stream);

@@ -121,7 +121,10 @@ def bwd_args(**kw):
     # per-token decay: A and dA are [batch, seqlen, nheads] (dA 128 bytes into A overlaps it)
     (dict(opt=binding.Options(A_per_token=1), dA=FAKE + (4 << 32) + 128), -7),
     (dict(opt=binding.Options(A_per_token=1), A=None), -1),
-    (dict(opt=binding.Options(max_seqlen=4, cu_seqlens=FAKE + (23 << 32))), -3),
+    (dict(opt=binding.Options(max_seqlen=11, cu_seqlens=FAKE + (23 << 32))), -9),  # > seqlen
+    (dict(opt=binding.Options(max_seqlen=-1, cu_seqlens=FAKE + (23 << 32))), -9),
+    (dict(opt=binding.Options(max_seqlen=4, cu_seqlens=FAKE + (23 << 32) + 4)), -5),
+    (dict(opt=binding.Options(max_seqlen=4, cu_seqlens=FAKE + (23 << 32)), dx=FAKE + (23 << 32)), -7),
     (dict(opt=binding.Options(phase_out=FAKE + (23 << 32))), -3),
     (dict(opt=binding.Options(phase_mode=4)), -9),           # decode-only phase mode
     (dict(opt=binding.Options(phase_mode=7)), -9),
@@ -179,6 +182,13 @@ def test_bwd_option_workspace(lib):
     assert ws(opt=binding.Options(ngroups=3)) == plain          # one group per head
     assert ws(opt=binding.Options(A_per_token=1)) == plain       # no maps needed
     assert ws(opt=binding.Options(A_per_token=2)) == 0
+    # packed sequences (2 of them in 256 tokens): the gradient runs on a padded
+    # batch of max_seqlen tokens each, its inputs and gradients moved there
+    cu = FAKE + (23 << 32)
+    p64, p128 = (ws(opt=binding.Options(cu_seqlens=cu, max_seqlen=m)) for m in (64, 128))
+    assert p128 > p64 > 0
+    assert p128 - p64 >= 2 * 64 * 3 * (2 * 64 * 2 + 2 * 64 * 2 + 64 * 4 + 2 * 64 * 4)
+    assert ws(opt=binding.Options(cu_seqlens=cu, max_seqlen=257)) == 0
     assert ws(opt=binding.Options(phase_mode=5)) == 0
     assert lib.m3_scan_bwd_workspace_bytes(ctypes.byref(bwd_args(batch=0))) == 0
     assert lib.m3_scan_bwd_workspace_bytes(

@@ -20,7 +20,7 @@ import torch
 
 import test_bwd_gpu as bwd
 import test_options_gpu as opt
-from oracle.backward import PREMIX_GRADS, scan_backward
+from oracle.backward import PREMIX_GRADS, scan_backward, scan_backward_packed
 from mamba_selective_ssm_amd import State, m3_scan_bwd, synth
 from helpers import TOL, f64, random_state, rel_err, say, workload
 
@@ -51,7 +51,11 @@ def option_grads_case(w, seed, ngroups=0, phase="native", premix=False, with_sta
                         Bprev=None if st is None else f64(st[1]),
                         xprev=None if st is None else f64(st[2]),
                         **opt.oracle_kw(ex, ngroups, phase))
-    tol = TOL[w.io_dtype]
+    return check_grads(got, ref, w.io_dtype, a_tok, premix, phase)
+
+
+def check_grads(got, ref, io, a_tok, premix, phase):
+    tol = TOL[io]
     errs = {}
     for n in bwd.NAMES:
         if n == "dA" and not a_tok:
@@ -156,3 +160,67 @@ def test_random_bwd_options_case(case):
         option_grads_case(w, 9950 + case, c["groups"], c["phase"], c["premix"],
                           with_state=c["with_state"], method=m, label="random bwd options %d" % case,
                           a_tok=c["a_tok"])
+
+
+PACKED_LENGTHS = [3, 0, 70, 1, 33, 64]
+
+
+@pytest.mark.parametrize("method", ["step", "chunked"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("opts,max_len", [
+    ({}, True), ({}, False),
+    (dict(ngroups=2, a_tok=True, premix=True, phase="shuffle"), True),
+])
+def test_bwd_packed(opts, max_len, io, method):
+    """Packed sequences of different lengths (one empty, one of a single
+    token), each with its own state record and final-state gradient: the
+    gradient runs on the padded batch (max_seqlen = the longest sequence, or
+    by default the packed length) and comes back to the packed tokens."""
+    lens = PACKED_LENGTHS
+    nseq, T = len(lens), sum(lens)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=DEV)
+    ngroups, a_tok = opts.get("ngroups", 0), opts.get("a_tok", False)
+    phase, premix = opts.get("phase", "native"), opts.get("premix", False)
+    w = workload(1, T, 4, 2, 32, 64, io=io, dt_mu=-1.0, theta="uniform_pi")
+    say("case bwd packed [%s] %s %s lengths=%s max_seqlen=%s" % (method, io, opts, lens,
+                                                               max(lens) if max_len else T))
+    inp, ex = synth.make_option_inputs(w, 1400, DEV, ngroups=ngroups, a_per_token=a_tok,
+                                       phase=phase, premix=premix)
+    g = torch.Generator(device=DEV).manual_seed(1401)
+    dy = torch.randn(inp["x"].shape, generator=g, device=DEV).to(w.torch_dtype)
+    dh = torch.randn(nseq, w.heads, w.dstate, w.headdim, generator=g, device=DEV)
+    st = random_state(w.with_(batch=nseq), 1402, DEV)
+    got = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"],
+                      None if phase == "zero" else inp["theta"], inp["lam"], dy, State(*st), dh,
+                      method=method, ngroups=ngroups, phase=phase, perm=ex.get("perm"),
+                      premix=opt.premix_obj(ex), A_per_token=a_tok, cu_seqlens=cu,
+                      max_seqlen=max(lens) if max_len else None)
+    torch.cuda.synchronize()
+    ref = scan_backward_packed(f64(inp["x"]), f64(inp["B"]), f64(inp["C"]), f64(inp["dt"]),
+                               f64(inp["A"]), f64(inp["theta"]), f64(inp["lam"]),
+                               cu.cpu().numpy(), f64(dy), f64(dh), h0=f64(st[0]),
+                               Bprev=f64(st[1]), xprev=f64(st[2]),
+                               **opt.oracle_kw(ex, ngroups, phase))
+    check_grads(got, ref, io, a_tok, premix, phase)
+
+
+def test_bwd_packed_equal_lengths_match_dense_batch():
+    """Four sequences of 64 tokens packed = the dense batch of four: the same
+    gradients to rounding (the padded batch is the dense batch)."""
+    w = workload(4, 64, 2, 1, 64, 64, io="bf16", dt_mu=-1.0)
+    inp = synth.make_scan_inputs(w, 1410, DEV)
+    dy = torch.randn(inp["x"].shape, device=DEV,
+                     generator=torch.Generator(device=DEV).manual_seed(1411)).to(torch.bfloat16)
+    dense = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
+                        inp["lam"], dy)
+    flat = lambda t: t.reshape(1, -1, *t.shape[2:]).contiguous()
+    cu = torch.arange(0, 257, 64, dtype=torch.int32, device=DEV)
+    packed = m3_scan_bwd(flat(inp["x"]), flat(inp["B"]), flat(inp["C"]), flat(inp["dt"]),
+                         inp["A"], flat(inp["theta"]), flat(inp["lam"]), flat(dy), cu_seqlens=cu,
+                         max_seqlen=64)
+    torch.cuda.synchronize()
+    for n in bwd.NAMES:
+        a, b = getattr(dense, n), getattr(packed, n)
+        if n in ("dx", "dB", "dC", "ddt", "dtheta", "dlam"):
+            a = a.reshape(b.shape)
+        assert torch.equal(a, b), n
