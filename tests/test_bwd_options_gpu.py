@@ -224,3 +224,36 @@ def test_bwd_packed_equal_lengths_match_dense_batch():
         if n in ("dx", "dB", "dC", "ddt", "dtheta", "dlam"):
             a = a.reshape(b.shape)
         assert torch.equal(a, b), n
+
+
+def test_bwd_options_prefill_workload_sampled():
+    """The prefill_bf16 shapes (4 x 2048 tokens, 16 heads: 32 chunks of 64
+    tokens per head) with 8 head groups of 2, shuffled phases,
+    the pre-mixer and A per token, chunked method: every per-token gradient
+    of batch row 1 and group 3 (heads 6 and 7) against the oracle run on that
+    slice with the same options (one group of two heads, the group's biases)."""
+    w = synth.WORKLOADS["prefill_bf16"]
+    say("case bwd options prefill_bf16 full size [chunked]")
+    inp, ex = synth.make_option_inputs(w, 1500, DEV, ngroups=8, a_per_token=True, phase="shuffle",
+                                       premix=True)
+    dy = torch.randn(inp["x"].shape, device=DEV,
+                     generator=torch.Generator(device=DEV).manual_seed(1501)).to(torch.bfloat16)
+    got = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"], inp["lam"],
+                      dy, method="chunked", ngroups=8, phase="shuffle", perm=ex["perm"],
+                      premix=opt.premix_obj(ex), A_per_token=True)
+    torch.cuda.synchronize()
+    b, g = 1, 3
+    hs = slice(2 * g, 2 * g + 2)
+    tok = lambda t: f64(t[b:b + 1, :, hs])
+    grp = lambda t: f64(t[b:b + 1, :, g:g + 1])
+    pm = dict(ex["premix"])
+    kw = opt.oracle_kw(ex, 1, "shuffle")
+    kw["premix"] = {k: (f64(v[hs]) if k in ("B_bias", "C_bias", "dt_bias") else
+                        (f64(v) if torch.is_tensor(v) else v)) for k, v in pm.items()}
+    ref = scan_backward(tok(inp["x"]), grp(inp["B"]), grp(inp["C"]), tok(inp["dt"]), tok(inp["A"]),
+                        tok(inp["theta"]), tok(inp["lam"]), tok(dy), **kw)
+    for n, sel in (("dx", tok), ("dB", grp), ("dC", grp), ("ddt", tok), ("dA", tok),
+                   ("dtheta", tok), ("dlam", tok)):
+        e = rel_err(sel(getattr(got, n)), ref[n])
+        say("   row %d group %d %s rel err %.2e" % (b, g, n, e))
+        assert e <= TOL["bf16"], (n, e)
