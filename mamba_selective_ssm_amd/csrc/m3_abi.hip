@@ -250,8 +250,10 @@ m3_status plan_bwd_options(const m3_scan_bwd_args* a, BwdPlan* out)
     out->opt_bc = o.premix || out->groups != H;
     out->opt_scal = o.premix != 0;
     out->opt_theta = o.phase_mode != M3_PHASE_NATIVE;
-    // the option maps move rows of dstate values 4 at a time, pairs through LDS
-    if ((out->opt_bc || out->opt_theta) && (N > 256 || N % 4 != 0)) return M3_ERR_UNSUPPORTED;
+    // the option maps move rows of dstate values and of rotary pairs 4 at a
+    // time, pairs through LDS
+    if ((out->opt_bc || out->opt_scal || out->opt_theta) && (N > 256 || N % 8 != 0))
+        return M3_ERR_UNSUPPORTED;
     // token rows of the caller's arrays (packed: one row of seqlen tokens)
     const int64_t BtL = (out->packed ? 1 : Bt) * L;
     const size_t tok = (size_t)BtL * H, es = (size_t)io_size(a->io_dtype);

@@ -160,36 +160,56 @@ __global__ void __launch_bounds__(kThreads) bo_prep_bc_kernel(BwdOptParams p)
     }
 }
 
-// dt = softplus(dt_raw + dt_bias_h), lam = sigmoid(lam_raw).
-__global__ void __launch_bounds__(kThreads) bo_prep_scalar_kernel(BwdOptParams p)
-{
-    const int64_t tok = p.BtL * p.H;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < tok;
-         i += (int64_t)gridDim.x * kThreads) {
-        const int64_t h = i % p.H;
-        p.dte[i] = softplus_acc(p.dt[i] + (p.opt.dtb ? p.opt.dtb[h] : 0.f));
-        p.lame[i] = sigmoid_acc(p.lam[i]);
+// Thread layout of the per-token maps: with theta rows, nq threads per token
+// (4 pairs each) and 256/nq tokens per block step; else one token per thread.
+struct TokLanes {
+    int rpb, lr, q4;
+    bool ok;
+    __device__ TokLanes(bool th, int nq)
+    {
+        rpb = th ? kThreads / nq : kThreads;
+        lr = th ? (int)threadIdx.x / nq : (int)threadIdx.x;
+        q4 = th ? ((int)threadIdx.x % nq) * 4 : 0;
+        ok = lr < rpb;
     }
-}
+};
 
-// theta after the phase map (zero mode: theta is not read).
-__global__ void __launch_bounds__(kThreads) bo_prep_theta_kernel(BwdOptParams p)
+// Per-token maps before the gradient, 4 rotary pairs per thread (dstate is a
+// multiple of 8): theta after the phase map (zero mode: theta is not read)
+// and, with the pre-mixer, dt = softplus(dt_raw + dt_bias_h) and
+// lam = sigmoid(lam_raw) (by the thread holding the token's first pairs).
+__global__ void __launch_bounds__(kThreads) bo_prep_tok_kernel(BwdOptParams p)
 {
     __shared__ int sperm[kMaxPairs];
-    const int npr = p.N / 2;
-    const bool shuffle = p.opt.phase == M3_PHASE_SHUFFLE;
+    const int npr = p.N / 2, nq = npr / 4;
+    const bool shuffle = p.opt.phase == M3_PHASE_SHUFFLE, th = p.thetae != nullptr;
     if (shuffle) {
         for (int j = threadIdx.x; j < npr; j += kThreads) sperm[j] = clamp_pair(p.opt.perm[j], npr);
         __syncthreads();
     }
-    const int64_t total = p.BtL * p.H * npr;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * kThreads) {
-        const int j = (int)(i % npr);
-        float t = 0.f;
-        if (p.opt.phase == M3_PHASE_REVERSE) t = -p.theta[i];
-        else if (shuffle) t = p.theta[i - j + sperm[j]];
-        p.thetae[i] = t;
+    const int64_t tok = p.BtL * p.H;
+    const TokLanes tl(th, nq);
+    for (int64_t r0 = (int64_t)blockIdx.x * tl.rpb; r0 < tok; r0 += (int64_t)gridDim.x * tl.rpb) {
+        const int64_t row = r0 + tl.lr;
+        if (!tl.ok || row >= tok) continue;
+        const int q4 = tl.q4;
+        if (th) {
+            float o[4] = {0.f, 0.f, 0.f, 0.f};
+            const float* src = p.theta + row * npr;
+            if (p.opt.phase == M3_PHASE_REVERSE) {
+                ld4(src + q4, o);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) o[k] = -o[k];
+            } else if (shuffle) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) o[k] = src[sperm[q4 + k]];
+            }
+            st4(p.thetae + row * npr + q4, o);
+        }
+        if (p.dte != nullptr && q4 == 0) {
+            p.dte[row] = softplus_acc(p.dt[row] + (p.opt.dtb ? p.opt.dtb[row % p.H] : 0.f));
+            p.lame[row] = sigmoid_acc(p.lam[row]);
+        }
     }
 }
 
@@ -262,28 +282,18 @@ __global__ void __launch_bounds__(kThreads) bo_post_bc_kernel(BwdOptParams p)
     }
 }
 
-// ddt and dlam through softplus and sigmoid, in place.
-__global__ void __launch_bounds__(kThreads) bo_post_scalar_kernel(BwdOptParams p)
-{
-    const int64_t tok = p.BtL * p.H;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < tok;
-         i += (int64_t)gridDim.x * kThreads) {
-        const int64_t h = i % p.H;
-        p.ddt[i] *= sigmoid_acc(p.dt[i] + (p.opt.dtb ? p.opt.dtb[h] : 0.f));
-        const float s = sigmoid_acc(p.lam[i]);
-        p.dlam[i] *= s * (1.f - s);
-    }
-}
-
-// dtheta from the gradient of the mapped theta.  Shuffle: each block lists,
-// per pair j, the pairs i with perm[i] = j in increasing order (a chain
-// first[j] -> next[i] -> ...); every i is on exactly one chain.
-__global__ void __launch_bounds__(kThreads) bo_post_theta_kernel(BwdOptParams p)
+// Per-token maps after the gradient, 4 rotary pairs per thread: dtheta from
+// the gradient of the mapped theta and, with the pre-mixer, ddt and dlam
+// through softplus and sigmoid (in place).  Shuffle: each block lists, per
+// pair j, the pairs i with perm[i] = j in increasing order (a chain first[j]
+// -> next[i] -> ...); every i is on exactly one chain.
+__global__ void __launch_bounds__(kThreads) bo_post_tok_kernel(BwdOptParams p)
 {
     __shared__ int sperm[kMaxPairs], first[kMaxPairs], next[kMaxPairs];
-    const int npr = p.N / 2;
+    const int npr = p.N / 2, nq = npr / 4;
     const bool shuffle = p.opt.phase == M3_PHASE_SHUFFLE;
-    if (shuffle) {
+    const bool th = p.dthetae != nullptr && p.dtheta != nullptr;
+    if (shuffle && th) {
         for (int j = threadIdx.x; j < npr; j += kThreads) sperm[j] = clamp_pair(p.opt.perm[j], npr);
         __syncthreads();
         for (int j = threadIdx.x; j < npr; j += kThreads) {
@@ -299,18 +309,31 @@ __global__ void __launch_bounds__(kThreads) bo_post_theta_kernel(BwdOptParams p)
         }
         __syncthreads();
     }
-    const int64_t total = p.BtL * p.H * npr;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * kThreads) {
-        float o = 0.f;
-        if (p.opt.phase == M3_PHASE_REVERSE) {
-            o = -p.dthetae[i];
-        } else if (shuffle) {
-            const int j = (int)(i % npr);
-            const float* d = p.dthetae + (i - j);
-            for (int c = first[j]; c >= 0; c = next[c]) o += d[c];
+    const int64_t tok = p.BtL * p.H;
+    const TokLanes tl(th, nq);
+    for (int64_t r0 = (int64_t)blockIdx.x * tl.rpb; r0 < tok; r0 += (int64_t)gridDim.x * tl.rpb) {
+        const int64_t row = r0 + tl.lr;
+        if (!tl.ok || row >= tok) continue;
+        const int q4 = tl.q4;
+        if (th) {
+            float o[4] = {0.f, 0.f, 0.f, 0.f};
+            const float* d = p.dthetae + row * npr;
+            if (p.opt.phase == M3_PHASE_REVERSE) {
+                ld4(d + q4, o);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) o[k] = -o[k];
+            } else if (shuffle) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    for (int c = first[q4 + k]; c >= 0; c = next[c]) o[k] += d[c];
+            }
+            st4(p.dtheta + row * npr + q4, o);
         }
-        p.dtheta[i] = o;
+        if (p.opt.premix && q4 == 0) {
+            p.ddt[row] *= sigmoid_acc(p.dt[row] + (p.opt.dtb ? p.opt.dtb[row % p.H] : 0.f));
+            const float sg = sigmoid_acc(p.lam[row]);
+            p.dlam[row] *= sg * (1.f - sg);
+        }
     }
 }
 
@@ -341,14 +364,24 @@ __global__ void __launch_bounds__(kThreads) bo_pack_kernel(PackParams q)
     }
 }
 
-// Column sums of a [rows][cols] float32 array, stage 1: block (x, y) = 64
-// columns x 4 row lanes over rows y*rpc .. y*rpc + rpc - 1; lane k takes every
-// 4th row from k, then the 4 lanes are added in order into part[y][cols].
-__global__ void __launch_bounds__(kThreads) bo_colsum_partial_kernel(const float* src, int64_t rows,
+// Column sums of [rows][cols] float32 arrays, one or two per launch
+// (blockIdx.z picks the array; a NULL destination is skipped).
+struct ColPair {
+    const float* src[2];
+    float* dst[2];
+};
+
+// Stage 1: block (x, y) = 64 columns x 4 row lanes over rows y*rpc .. y*rpc +
+// rpc - 1; lane k takes every 4th row from k, then the 4 lanes are added in
+// order into part[z][y][cols].
+__global__ void __launch_bounds__(kThreads) bo_colsum_partial_kernel(ColPair cp, int64_t rows,
                                                                       int64_t cols, int64_t rpc,
-                                                                      float* part)
+                                                                      float* part, int64_t pstride)
 {
     __shared__ float red[kWaves][64];
+    const int z = blockIdx.z;
+    if (cp.dst[z] == nullptr) return;                   // uniform over the block
+    const float* src = cp.src[z];
     const int cl = threadIdx.x & 63, k = threadIdx.x >> 6;
     const int64_t c = (int64_t)blockIdx.x * 64 + cl;
     const int64_t r0 = (int64_t)blockIdx.y * rpc;
@@ -361,15 +394,21 @@ __global__ void __launch_bounds__(kThreads) bo_colsum_partial_kernel(const float
     red[k][cl] = acc;
     __syncthreads();
     if (k == 0 && c < cols)
-        part[(int64_t)blockIdx.y * cols + c] = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
+        part[z * pstride + (int64_t)blockIdx.y * cols + c] =
+            ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
 }
 
 // Stage 2: block = 64 columns x 16 partial lanes; lane k adds partials k,
 // k + 16, ... in order, then the 16 lanes are added in order.
-__global__ void __launch_bounds__(64 * kFinalLanes) bo_colsum_final_kernel(const float* part, int nchunk,
-                                                                          int64_t cols, float* dst)
+__global__ void __launch_bounds__(64 * kFinalLanes) bo_colsum_final_kernel(const float* part, int64_t pstride,
+                                                                          int nchunk, int64_t cols,
+                                                                          ColPair cp)
 {
     __shared__ float red[kFinalLanes][64];
+    const int z = blockIdx.z;
+    float* dst = cp.dst[z];
+    if (dst == nullptr) return;                         // uniform over the block
+    part += z * pstride;
     const int cl = threadIdx.x & 63, k = threadIdx.x >> 6;
     const int64_t c = (int64_t)blockIdx.x * 64 + cl;
     float acc = 0.f;
@@ -412,30 +451,35 @@ size_t colsum_partial_floats(int64_t rows, int64_t cols)
     return (size_t)nchunk * (size_t)(cols > 0 ? cols : 0);
 }
 
-hipError_t colsum_final(const float* part, int nchunk, int64_t cols, float* dst, hipStream_t s)
+hipError_t colsum_final(const float* part, int64_t pstride, int nchunk, int64_t cols,
+                        const ColPair& cp, hipStream_t s)
 {
-    hipLaunchKernelGGL(bo_colsum_final_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(64 * kFinalLanes),
-                       0, s, part, nchunk, cols, dst);
+    hipLaunchKernelGGL(bo_colsum_final_kernel, dim3((unsigned)((cols + 63) / 64), 1, 2),
+                       dim3(64 * kFinalLanes), 0, s, part, pstride, nchunk, cols, cp);
     return hipGetLastError();
 }
 
-hipError_t colsum(const float* src, int64_t rows, int64_t cols, float* part, float* dst,
-                  hipStream_t s)
+// Column sums of one or two [rows][cols] arrays; `part` holds two partial
+// sets of colsum_partial_floats(rows, cols) values.
+hipError_t colsum(const ColPair& cp, int64_t rows, int64_t cols, float* part, hipStream_t s)
 {
     if (cols <= 0) return hipSuccess;
     int64_t rpc;
     int nchunk;
     colsum_plan(rows, cols, &rpc, &nchunk);
-    hipLaunchKernelGGL(bo_colsum_partial_kernel, dim3((unsigned)((cols + 63) / 64), nchunk), dim3(kThreads),
-                       0, s, src, rows, cols, rpc, part);
+    const int64_t pstride = (int64_t)nchunk * cols;
+    hipLaunchKernelGGL(bo_colsum_partial_kernel, dim3((unsigned)((cols + 63) / 64), nchunk, 2),
+                       dim3(kThreads), 0, s, cp, rows, cols, rpc, part, pstride);
     const hipError_t e = hipGetLastError();
-    return e != hipSuccess ? e : colsum_final(part, nchunk, cols, dst, s);
+    return e != hipSuccess ? e : colsum_final(part, pstride, nchunk, cols, cp, s);
 }
 
-unsigned stride_grid(int64_t n)
+// Blocks of the per-token maps (TokLanes: 256/nq tokens per block step).
+unsigned tok_grid(int64_t tok, bool th, int N)
 {
-    const int64_t b = (n + kThreads - 1) / kThreads;
-    return (unsigned)(b < kMaxBlocks ? b : kMaxBlocks);
+    const int64_t rpb = th ? kThreads / (N / 8) : kThreads;
+    const int64_t b = (tok + rpb - 1) / rpb;
+    return (unsigned)(b < 1 ? 1 : (b < kMaxBlocks ? b : kMaxBlocks));
 }
 
 // Blocks of the row kernels: 4 waves, 64/LPR rows per wave at once.
@@ -454,11 +498,9 @@ hipError_t pre_impl(const BwdOptParams& p, hipStream_t s)
     const int64_t rows = p.BtL * p.G * p.R, tok = p.BtL * p.H;
     if (p.Be != nullptr && rows > 0)
         hipLaunchKernelGGL(bo_prep_bc_kernel<IO>, dim3(row_grid(rows, p.N), 2), dim3(kThreads), 0, s, p);
-    if (p.dte != nullptr && tok > 0)
-        hipLaunchKernelGGL(bo_prep_scalar_kernel, dim3(stride_grid(tok)), dim3(kThreads), 0, s, p);
-    if (p.thetae != nullptr && tok > 0)
-        hipLaunchKernelGGL(bo_prep_theta_kernel, dim3(stride_grid(tok * (p.N / 2))), dim3(kThreads), 0,
-                           s, p);
+    if ((p.thetae != nullptr || p.dte != nullptr) && tok > 0)
+        hipLaunchKernelGGL(bo_prep_tok_kernel, dim3(tok_grid(tok, p.thetae != nullptr, p.N)), dim3(kThreads),
+                           0, s, p);
     return hipGetLastError();
 }
 
@@ -467,25 +509,23 @@ hipError_t post_impl(const BwdOptParams& p, hipStream_t s)
 {
     const int64_t rows = p.BtL * p.G * p.R, tok = p.BtL * p.H;
     const unsigned gbc = row_grid(rows, p.N);
-    if (p.opt.premix && tok > 0)
-        hipLaunchKernelGGL(bo_post_scalar_kernel, dim3(stride_grid(tok)), dim3(kThreads), 0, s, p);
     if (p.dBe != nullptr && rows > 0)
         hipLaunchKernelGGL(bo_post_bc_kernel<IO>, dim3(gbc, 2), dim3(kThreads), 0, s, p);
-    if (p.dthetae != nullptr && p.dtheta != nullptr && tok > 0)
-        hipLaunchKernelGGL(bo_post_theta_kernel, dim3(stride_grid(tok * (p.N / 2))), dim3(kThreads), 0,
-                           s, p);
+    const bool th = p.dthetae != nullptr && p.dtheta != nullptr;
+    if ((th || p.opt.premix) && tok > 0)
+        hipLaunchKernelGGL(bo_post_tok_kernel, dim3(tok_grid(tok, th, p.N)), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.opt.premix) return e;
-    const int64_t hrn = p.H * p.R * p.N;
     // gain gradients: the row kernel's per-block partials (none written when
     // there are no rows: the sums are then zero)
-    const int nq = rows > 0 ? (int)gbc : 0;
-    if (p.dBw && (e = colsum_final(p.qpart, nq, p.N, p.dBw, s)) != hipSuccess) return e;
-    if (p.dCw && (e = colsum_final(p.qpart + (int64_t)gbc * p.N, nq, p.N, p.dCw, s)) != hipSuccess)
+    const ColPair gains = {{nullptr, nullptr}, {p.dBw, p.dCw}};
+    if ((p.dBw || p.dCw) &&
+        (e = colsum_final(p.qpart, (int64_t)gbc * p.N, rows > 0 ? (int)gbc : 0, p.N, gains, s)) != hipSuccess)
         return e;
-    if (p.ddtb && (e = colsum(p.ddt, p.BtL, p.H, p.part, p.ddtb, s)) != hipSuccess) return e;
-    if (p.dBb && (e = colsum(p.dBe, p.BtL, hrn, p.part, p.dBb, s)) != hipSuccess) return e;
-    if (p.dCb && (e = colsum(p.dCe, p.BtL, hrn, p.part, p.dCb, s)) != hipSuccess) return e;
+    const ColPair dtb = {{p.ddt, nullptr}, {p.ddtb, nullptr}};
+    if (p.ddtb && (e = colsum(dtb, p.BtL, p.H, p.part, s)) != hipSuccess) return e;
+    const ColPair bias = {{p.dBe, p.dCe}, {p.dBb, p.dCb}};
+    if ((p.dBb || p.dCb) && (e = colsum(bias, p.BtL, p.H * p.R * p.N, p.part, s)) != hipSuccess) return e;
     return hipSuccess;
 }
 
@@ -493,8 +533,9 @@ hipError_t post_impl(const BwdOptParams& p, hipStream_t s)
 
 size_t bwd_options_partial_floats(int64_t BtL, int64_t H, int64_t G, int N, int R)
 {
+    // two partial sets (B and C) of the larger of the two column sums
     size_t a = colsum_partial_floats(BtL, H), b = colsum_partial_floats(BtL, H * R * N);
-    return a > b ? a : b;
+    return 2 * (a > b ? a : b);
 }
 
 size_t bwd_options_gain_floats(int64_t BtL, int64_t G, int N, int R)
