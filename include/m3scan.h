@@ -137,7 +137,8 @@ typedef enum {
 
 /*
  * Options shared by m3_scan_fwd and m3_decode_step, a subset of them also by
- * m3_scan_bwd (all zero = the plain mixer).  Pointers are device pointers owned by the caller.
+ * m3_scan_bwd (all zero = the plain mixer).  Pointers are device pointers
+ * owned by the caller.
  *   ngroups      0 = one B and C per head; else a divisor of nheads
  *   A_per_token  0: A is [nheads]; 1: A is [batch, seqlen, nheads] in a scan,
  *                [batch, nheads] in a decode step
