@@ -254,6 +254,13 @@ typedef struct {
  *            (float32), optional state record h_in, B_prev_in, x_prev_in
  *   dy       [batch, seqlen, nheads, rank, headdim] io dtype
  *   dh_out   [batch, nheads, dstate, headdim] float32, or NULL (zero)
+ *   dB_prev_out, dx_prev_out  float32 [batch, nheads, rank, dstate] and
+ *            [batch, nheads, rank, headdim], or NULL (zero): the gradient
+ *            with respect to the output record's (B_L, x_L), e.g. a later
+ *            call's dB_prev, dx_prev when a sequence is split into calls.
+ *            Added to the last token's gradients (B_L is B as the recurrence
+ *            used it: per head, pre-mixed), or, for a sequence without
+ *            tokens, to the input record's.
  *   outputs  float32, same shapes as their inputs: dx, dB, dC, ddt, dtheta,
  *            dlam, dA [nheads]; optionally all of dh_in [batch, nheads,
  *            dstate, headdim], dB_prev [batch, nheads, rank, dstate],
@@ -323,6 +330,7 @@ typedef struct {
     size_t workspace_bytes;
     m3_options opt;
     float *dB_norm_w, *dC_norm_w, *dB_bias, *dC_bias, *ddt_bias;
+    const float *dB_prev_out, *dx_prev_out;
 } m3_scan_bwd_args;
 
 /* Chunked prefill: y and (optionally) the state record after the last token.

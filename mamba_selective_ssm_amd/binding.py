@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import NamedTuple, Optional
+from typing import NamedTuple, Optional, Tuple
 
 import torch
 
@@ -105,7 +105,7 @@ class ScanBwdArgs(ctypes.Structure):
                 ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
                 ("opt", Options),
                 ("dB_norm_w", _vp), ("dC_norm_w", _vp), ("dB_bias", _vp), ("dC_bias", _vp),
-                ("ddt_bias", _vp)]
+                ("ddt_bias", _vp), ("dB_prev_out", _vp), ("dx_prev_out", _vp)]
 
 
 class M3Error(RuntimeError):
@@ -467,7 +467,7 @@ def m3_scan_bwd_supported(dstate: int, headdim: int, rank: int, io_dtype: int,
 
 def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, workspace,
                  method="auto", ngroups=0, phase="native", perm=None, premix=None,
-                 A_per_token=False, cu_seqlens=None, max_seqlen=None):
+                 A_per_token=False, cu_seqlens=None, max_seqlen=None, record_grad=None):
     lib = load_library()
     Bx, L, H, R, P = x.shape
     N = B.shape[-1]
@@ -520,6 +520,12 @@ def _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads, wor
                     dx=_ptr(g.dx), dB=_ptr(g.dB), dC=_ptr(g.dC), ddt=_ptr(g.ddt), dA=_ptr(g.dA),
                     dtheta=_ptr(g.dtheta), dlam=_ptr(g.dlam), dh_in=_ptr(g.dh_in),
                     dB_prev=_ptr(g.dB_prev), dx_prev=_ptr(g.dx_prev), opt=opt)
+    if record_grad is not None:
+        dBL, dxL = record_grad
+        _check(dBL, "record_grad[0] (dB_L)", (Bt, H, R, N), torch.float32)
+        _check(dxL, "record_grad[1] (dx_L)", (Bt, H, R, P), torch.float32)
+        a.dB_prev_out, a.dx_prev_out = dBL.data_ptr(), dxL.data_ptr()
+        keep += [dBL, dxL]
     if cu_seqlens is not None:
         a.opt.cu_seqlens = cu_seqlens.data_ptr()
         a.opt.max_seqlen = int(L if max_seqlen is None else max_seqlen)
@@ -541,6 +547,7 @@ def m3_scan_bwd(x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
                 ngroups: int = 0, phase: str = "native", perm: Optional[torch.Tensor] = None,
                 premix: Optional[Premix] = None, A_per_token: bool = False,
                 cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+                record_grad: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
                 stream=None) -> ScanGrads:
     """Gradients of sum(dy * y) + sum(dh_out * h_L) of m3_scan_fwd with respect
     to every input; ``state_grads`` also returns those of the input state
@@ -552,10 +559,13 @@ def m3_scan_bwd(x, B, C, dt, A, theta, lam, dy, state: Optional[State] = None,
     ``premix`` the result's ``premix`` field holds the parameter gradients.
     Packed sequences: token arrays [1, T, ...], ``cu_seqlens`` int32 [nseq+1],
     one state record, dh_out and record gradient row per sequence;
-    ``max_seqlen`` (default T) sizes the padded batch the gradient runs on."""
+    ``max_seqlen`` (default T) sizes the padded batch the gradient runs on.
+    ``record_grad`` = (dB_L, dx_L), float32 [batch, H, R, N] and [batch, H,
+    R, P]: the gradient with respect to the output record (for a sequence
+    split into calls, the next call's dB_prev, dx_prev)."""
     a, g, _, _keep = _prepare_bwd(x, B, C, dt, A, theta, lam, dy, state, dh_out, state_grads,
                                   workspace, method, ngroups, phase, perm, premix, A_per_token,
-                                  cu_seqlens, max_seqlen)
+                                  cu_seqlens, max_seqlen, record_grad)
     st = load_library().m3_scan_bwd(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_bwd")

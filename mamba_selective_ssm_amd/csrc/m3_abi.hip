@@ -393,6 +393,8 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
     const bool st_out = a->dh_in || a->dB_prev || a->dx_prev;
     if (st_in && !(a->h_in && a->B_prev_in && a->x_prev_in)) return M3_ERR_NULL;
     if (st_out && !(a->dh_in && a->dB_prev && a->dx_prev)) return M3_ERR_NULL;
+    const bool rec_g = a->dB_prev_out || a->dx_prev_out;      // output record's gradient
+    if (rec_g && !(a->dB_prev_out && a->dx_prev_out)) return M3_ERR_NULL;
     // per-token A and dA are empty when there are no tokens
     if ((a->A == nullptr || a->dA == nullptr) && !(a->opt.A_per_token && L == 0)) return M3_ERR_NULL;
     if (L > 0 && (!a->x || !a->B || !a->C || !a->dt || (!zero_phase && !a->theta) || !a->lam ||
@@ -403,7 +405,8 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
     const void* ptrs[] = {a->x, a->B, a->C, a->dt, a->A, theta_in, a->lam, a->h_in,
                           a->B_prev_in, a->x_prev_in, a->dy, a->dh_out, a->dx, a->dB, a->dC,
                           a->ddt, a->dA, a->dtheta, a->dlam, a->dh_in, a->dB_prev, a->dx_prev,
-                          a->dB_norm_w, a->dC_norm_w, a->dB_bias, a->dC_bias, a->ddt_bias};
+                          a->dB_norm_w, a->dC_norm_w, a->dB_bias, a->dC_bias, a->ddt_bias,
+                          a->dB_prev_out, a->dx_prev_out};
     for (const void* q : ptrs)
         if (q != nullptr && !aligned16(q)) return M3_ERR_ALIGN;
     const int e = io_size(a->io_dtype);
@@ -411,7 +414,7 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
     const int64_t rowsL = (plan.packed ? 1 : Bt) * L;
     const int64_t tok = rowsL * H, tokg = rowsL * plan.groups;
     const int64_t nA = a->opt.A_per_token ? tok : H;       // A and dA
-    Range in[20] = {
+    Range in[22] = {
         range_of(a->x, tok * R * P * e),         range_of(a->B, tokg * R * N * e),
         range_of(a->C, tokg * R * N * e),        range_of(a->dt, tok * 4),
         range_of(a->A, nA * 4),                  range_of(theta_in, tok * (N / 2) * 4),
@@ -420,6 +423,8 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         range_of(a->dy, tok * R * P * e),        range_of(a->dh_out, nbh * N * P * 4),
     };
     option_ranges(a->opt, Bt, H, N, R, in + 12);
+    in[20] = range_of(a->dB_prev_out, nbh * R * N * 4);
+    in[21] = range_of(a->dx_prev_out, nbh * R * P * 4);
     const Range out[] = {
         range_of(a->dx, tok * R * P * 4),        range_of(a->dB, tokg * R * N * 4),
         range_of(a->dC, tokg * R * N * 4),       range_of(a->ddt, tok * 4),
@@ -584,6 +589,16 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         err = m3::launch_bwd(p, a->io_dtype, a->dA, st);
     }
     if (err == hipSuccess && plan.packed) err = m3::launch_bwd_pack(un, st);
+    if (err == hipSuccess && rec_g) {
+        // the output record's (B_L, x_L) are the last token's B (as used) and x
+        m3::RecGradParams rg;
+        memset(&rg, 0, sizeof(rg));
+        rg.dBL = a->dB_prev_out; rg.dxL = a->dx_prev_out;
+        rg.dB = dBx; rg.dx = a->dx; rg.dBp = a->dB_prev; rg.dxp = a->dx_prev;
+        rg.cu = a->opt.cu_seqlens;
+        rg.batch = Bt; rg.L = L; rg.H = H; rg.N = (int)N; rg.P = (int)P; rg.R = (int)R;
+        err = m3::launch_bwd_record_grad(rg, st);
+    }
     if (err != hipSuccess || !opts) return hip_status(err);
     return hip_status(m3::launch_bwd_options_post(bo, a->io_dtype, st));
 }

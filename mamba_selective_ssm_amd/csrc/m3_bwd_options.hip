@@ -474,6 +474,12 @@ hipError_t colsum(const ColPair& cp, int64_t rows, int64_t cols, float* part, hi
     return e != hipSuccess ? e : colsum_final(part, pstride, nchunk, cols, cp, s);
 }
 
+unsigned stride_grid_n(int64_t n)
+{
+    const int64_t b = (n + kThreads - 1) / kThreads;
+    return (unsigned)(b < 1 ? 1 : (b < kMaxBlocks ? b : kMaxBlocks));
+}
+
 // Blocks of the per-token maps (TokLanes: 256/nq tokens per block step).
 unsigned tok_grid(int64_t tok, bool th, int N)
 {
@@ -549,6 +555,46 @@ hipError_t launch_bwd_pack(const PackParams& p, hipStream_t stream)
     if (ntok <= 0 || p.n <= 0) return hipSuccess;
     const unsigned grid = (unsigned)(ntok < 8192 ? ntok : 8192);
     hipLaunchKernelGGL(bo_pack_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+// One thread per (sequence, head, rank, entry) of the record gradient.
+__global__ void __launch_bounds__(kThreads) bo_record_grad_kernel(RecGradParams q)
+{
+    const int64_t per = (int64_t)q.R * (q.N + q.P);
+    const int64_t total = q.batch * q.H * per;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * kThreads) {
+        const int64_t bh = i / per, b = bh / q.H, h = bh % q.H;
+        const int64_t e = i % per;
+        const bool isB = e < (int64_t)q.R * q.N;
+        const int64_t k = isB ? e : e - (int64_t)q.R * q.N;     // (r, n) or (r, p)
+        const int W = isB ? q.N : q.P;
+        const float g = isB ? q.dBL[bh * q.R * q.N + k] : q.dxL[bh * q.R * q.P + k];
+        int64_t last = -1;                                       // token row of the last token
+        if (q.cu != nullptr) {
+            int64_t st = q.cu[b], en = q.cu[b + 1];
+            st = st < 0 ? 0 : (st > q.L ? q.L : st);
+            en = en < st ? st : (en > q.L ? q.L : en);
+            if (en > st) last = en - 1;
+        } else if (q.L > 0) {
+            last = b * q.L + q.L - 1;
+        }
+        if (last >= 0) {
+            float* dst = isB ? q.dB : q.dx;
+            dst[(last * q.H + h) * q.R * W + k] += g;
+        } else {
+            float* dst = isB ? q.dBp : q.dxp;
+            if (dst != nullptr) dst[bh * q.R * W + k] += g;
+        }
+    }
+}
+
+hipError_t launch_bwd_record_grad(const RecGradParams& p, hipStream_t stream)
+{
+    const int64_t total = p.batch * p.H * (int64_t)p.R * (p.N + p.P);
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bo_record_grad_kernel, dim3(stride_grid_n(total)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -132,6 +132,19 @@ struct PackParams {
     int words[8];             // 4-byte words per token row
 };
 hipError_t launch_bwd_pack(const PackParams& p, hipStream_t stream);
+
+// The gradient of the output record (B_L, x_L) added to each sequence's last
+// token's dB (per head) and dx, or to the input record's dB_prev, dx_prev for a
+// sequence without tokens.
+struct RecGradParams {
+    const float *dBL, *dxL;   // [B*H][R][N], [B*H][R][P]
+    float *dB, *dx;           // token gradients [rows][L or T][H][R][N or P]
+    float *dBp, *dxp;         // input record gradients, or NULL
+    const int* cu;            // packed: [batch + 1], else NULL
+    int64_t batch, L, H;      // L: tokens per row (dense) or the packed length
+    int N, P, R;
+};
+hipError_t launch_bwd_record_grad(const RecGradParams& p, hipStream_t stream);
 size_t bwd_options_partial_floats(int64_t BtL, int64_t H, int64_t G, int N, int R);
 size_t bwd_options_gain_floats(int64_t BtL, int64_t G, int N, int R);
 hipError_t launch_bwd_options_pre(const BwdOptParams& p, int io_dtype, hipStream_t stream);

@@ -257,3 +257,67 @@ def test_bwd_options_prefill_workload_sampled():
         e = rel_err(sel(getattr(got, n)), ref[n])
         say("   row %d group %d %s rel err %.2e" % (b, g, n, e))
         assert e <= TOL["bf16"], (n, e)
+
+
+@pytest.mark.parametrize("method", ["step", "chunked"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("opts", [{}, dict(ngroups=2, premix=True, phase="reverse")])
+def test_bwd_split_sequence_chains_record_gradients(opts, io, method):
+    """A sequence of 150 tokens run as two calls (70 + 80) with the state
+    record carried between them: the second call's gradient of its input
+    record (dh_in, dB_prev, dx_prev) goes into the first call as dh_out and
+    the output record's gradient; the two calls' gradients together are the
+    whole sequence's (the oracle on all 150 tokens)."""
+    from mamba_selective_ssm_amd import m3_scan_fwd
+    ngroups, phase, premix = opts.get("ngroups", 0), opts.get("phase", "native"), opts.get("premix", False)
+    w = workload(2, 150, 4, 2, 32, 64, io=io, dt_mu=-1.0, theta="uniform_pi")
+    say("case bwd split 70+80 [%s] %s %s" % (method, io, opts))
+    inp, ex = synth.make_option_inputs(w, 1600, DEV, ngroups=ngroups, phase=phase, premix=premix)
+    g = torch.Generator(device=DEV).manual_seed(1601)
+    dy = torch.randn(inp["x"].shape, generator=g, device=DEV).to(w.torch_dtype)
+    dh = torch.randn(w.batch, w.heads, w.dstate, w.headdim, generator=g, device=DEV)
+    st = random_state(w, 1602, DEV)
+    kw = dict(ngroups=ngroups, phase=phase, perm=ex.get("perm"), premix=opt.premix_obj(ex))
+    part = lambda t, a, b: t[:, a:b].contiguous()
+    cut = 70
+    args = lambda a, b: [part(inp[k], a, b) for k in ("x", "B", "C", "dt")] + [inp["A"]] + \
+        [part(inp[k], a, b) for k in ("theta", "lam")]
+    _, rec = m3_scan_fwd(*args(0, cut), State(*st), **kw)
+    g2 = m3_scan_bwd(*args(cut, 150), part(dy, cut, 150), rec, dh, method=method, **kw)
+    g1 = m3_scan_bwd(*args(0, cut), part(dy, 0, cut), State(*st), g2.dh_in, method=method,
+                     record_grad=(g2.dB_prev, g2.dx_prev), **kw)
+    torch.cuda.synchronize()
+    ref = scan_backward(f64(inp["x"]), f64(inp["B"]), f64(inp["C"]), f64(inp["dt"]),
+                        f64(inp["A"]), f64(inp["theta"]), f64(inp["lam"]), f64(dy), f64(dh),
+                        h0=f64(st[0]), Bprev=f64(st[1]), xprev=f64(st[2]),
+                        **opt.oracle_kw(ex, ngroups, phase))
+    tol = TOL[io]
+    cat = lambda n: np.concatenate([f64(getattr(g1, n)), f64(getattr(g2, n))], axis=1)
+    errs = {n: rel_err(cat(n), ref[n]) for n in ("dx", "dB", "dC", "ddt", "dtheta", "dlam")}
+    errs["dA"] = float(np.max(np.abs(f64(g1.dA) + f64(g2.dA) - ref["dA"])) / np.max(ref["dA_scale"]))
+    for n, o in (("dh_in", "dh0"), ("dB_prev", "dBprev"), ("dx_prev", "dxprev")):
+        errs[n] = rel_err(f64(getattr(g1, n)), ref[o])
+    if premix:
+        for n in PREMIX_GRADS:
+            s = f64(getattr(g1.premix, n[1:])) + f64(getattr(g2.premix, n[1:]))
+            errs[n] = (float(np.max(np.abs(s - ref[n])) / np.max(np.abs(ref["ddt"]).sum(axis=(0, 1))))
+                       if n == "ddt_bias" else rel_err(s, ref[n]))
+    say("   " + "  ".join("%s %.2e" % (n, e) for n, e in errs.items()) + "  (tol %.0e)" % tol)
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, bad
+
+
+def test_bwd_record_gradient_without_tokens_reaches_the_input_record():
+    """seqlen 0: the output record is the input record, so its gradient is
+    the input record's."""
+    w = workload(2, 0, 3, 2, 32, 64, io="bf16", dt_mu=-1.0)
+    inp = synth.make_scan_inputs(w, 1610, DEV)
+    st = random_state(w, 1611, DEV)
+    g = torch.Generator(device=DEV).manual_seed(1612)
+    dBL = torch.randn(2, 3, 2, 64, generator=g, device=DEV)
+    dxL = torch.randn(2, 3, 2, 32, generator=g, device=DEV)
+    got = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"], inp["lam"],
+                      torch.empty_like(inp["x"]), State(*st), record_grad=(dBL, dxL))
+    torch.cuda.synchronize()
+    assert torch.equal(got.dB_prev, dBL) and torch.equal(got.dx_prev, dxL)
+    assert torch.count_nonzero(got.dh_in) == 0
