@@ -118,6 +118,10 @@ def bwd_args(**kw):
     (dict(method=1, headdim=128), -3),
     # options of the gradient
     (dict(opt=binding.Options(A_per_token=2)), -9),
+    # the output record's gradient: both or neither, aligned, not an output
+    (dict(dB_prev_out=FAKE + (25 << 32)), -1),
+    (dict(dB_prev_out=FAKE + (25 << 32), dx_prev_out=FAKE + (26 << 32) + 4), -5),
+    (dict(dB_prev_out=FAKE + (25 << 32), dx_prev_out=FAKE + (26 << 32), dx=FAKE + (26 << 32)), -7),
     # per-token decay: A and dA are [batch, seqlen, nheads] (dA 128 bytes into A overlaps it)
     (dict(opt=binding.Options(A_per_token=1), dA=FAKE + (4 << 32) + 128), -7),
     (dict(opt=binding.Options(A_per_token=1), A=None), -1),
