@@ -5,12 +5,15 @@
 
 A step is one m3_scan_fwd call (the whole chunked prefill: prefix scans,
 data-RoPE, intra-chunk tiles, state passing, outputs and final state) over one
-batch of the prefill_bf16 workload (batch 4, 16 heads, L = 2048, P = 64,
-N = 64, R = 1, bf16 I/O, fp32 state), inputs resident in HBM.  Prints one
-JSON line: whole-job tokens/s, the roofline of the scan kernel (algorithmic
-bytes per launch / its average launch time from HIP events on the launch
-stream, against 8 TB/s), the fp64 oracle's rate on this host's cores, and
-secondary lines for the MIMO, long-context and decode workloads.
+batch of the MIMO prefill workload (batch 8, 32 heads, L = 4096, P = 64,
+N = 128, rank 4, bf16 I/O, fp32 state), inputs resident in HBM.  Prints one
+JSON line: whole-job tokens/s; the roofline of the scan kernel (algorithmic
+bytes per launch over its average launch time from HIP events on the launch
+stream, against 8 TB/s, and its dense-tile bf16 flops against 2.5 PFLOP/s);
+the fp64 oracle's rate on this host's cores over a sample of the same
+workload; and secondary lines, each with its own roofline, for the
+single-layer, long-context (with its chunk sweep) and decode workloads, the
+options and the gradient.
 """
 from __future__ import annotations
 
@@ -52,6 +55,18 @@ def scan_algorithmic_bytes(w, L=None, ngroups=0, a_tok=False, phase="native", pr
     if premix:
         extra += 4 * (2 * N + 2 * H * R * N + H)
     return w.batch * (L * (H * per_tok + G * per_grp_tok) + H * per_bh) + extra
+
+
+def scan_dense_flops(w, Q=None, L=None):
+    """Dense-tile flops of one m3_scan_fwd by the chunked method at chunk Q:
+    per head-token 2 Q R^2 N (score tiles C B^T) + 2 Q R^2 P ((S o M) X, both
+    over whole Q R x Q R tiles, masked half included) + 4 R N P (the chunk
+    state B^T X and the state term C G)."""
+    Q = Q or w.chunk
+    L = w.seqlen if L is None else L
+    R, P, N = w.rank, w.headdim, w.dstate
+    per_ht = 2 * Q * R * R * N + 2 * Q * R * R * P + 4 * R * N * P
+    return w.batch * L * w.heads * per_ht
 
 
 def bwd_algorithmic_bytes(w, ngroups=0, premix=False):
@@ -186,8 +201,8 @@ def time_launches(fn, steps, warmup, torch):
     return total, kms
 
 
-def bench_prefill(w, steps, warmup, torch, m3, synth, seed=1001):
-    inp = synth.make_scan_inputs(w, seed, "cuda")
+def bench_prefill(w, steps, warmup, torch, m3, synth, seed=1001, inp=None):
+    inp = synth.make_scan_inputs(w, seed, "cuda") if inp is None else inp
     # Arguments, outputs and workspace are prepared once; each step is one
     # m3_scan_fwd call on the same resident inputs.
     step = m3.ScanCall(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
@@ -195,8 +210,50 @@ def bench_prefill(w, steps, warmup, torch, m3, synth, seed=1001):
     total, kms = time_launches(step, steps, warmup, torch)
     tokens = w.batch * w.seqlen
     nbytes = scan_algorithmic_bytes(w)
+    flops = scan_dense_flops(w)
     return dict(tokens_per_s=tokens * steps / total, ms_per_step=1e3 * total / steps,
-                kernel_ms=kms, bytes=nbytes, gbs=nbytes / (kms * 1e-3) / 1e9, inputs=inp)
+                kernel_ms=kms, bytes=nbytes, gbs=nbytes / (kms * 1e-3) / 1e9, flops=flops,
+                tflops=flops / (kms * 1e-3) / 1e12, inputs=inp)
+
+
+def roofline(r, name, kernel="m3::scan_kernel", flops=True):
+    """Roofline object of one measured workload: algorithmic HBM bytes per
+    call over the call's average span against 8 TB/s (the binding roof of
+    every workload here), the committed HBM traffic counters when they match
+    the current kernel sources, and -- for the prefill -- the dense-tile bf16
+    flops against the 2.5 PFLOP/s matrix-core peak."""
+    roof = {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(name), "kernel": kernel,
+            "kernel_ms": round(r["kernel_ms"], 5),
+            "algorithmic_bytes_per_launch": r["bytes"]}
+    if flops:
+        roof["mfma"] = {"achieved": round(r["tflops"], 1), "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(r["tflops"] / BF16_PEAK_TFLOPS, 4),
+                        "flops_per_launch": r["flops"]}
+    return roof
+
+
+def chunk_sweep(w, steps, warmup, torch, m3, synth, chunks=(32, 64, 128, 256), seed=1001):
+    """The long-context workload at each chunk length: time per call, HBM and
+    matrix-core fractions; chunk lengths outside the compiled set are listed
+    as unsupported."""
+    from mamba_selective_ssm_amd import M3_BF16
+    inp = synth.make_scan_inputs(w, seed, "cuda")
+    out = []
+    for Q in chunks:
+        wq = w.with_(chunk=Q)
+        if not m3.m3_scan_supported(w.dstate, w.headdim, w.rank, Q, M3_BF16):
+            out.append({"chunk": Q, "status": "unsupported"})
+            continue
+        r = bench_prefill(wq, steps, warmup, torch, m3, synth, inp=inp)
+        out.append({"chunk": Q, "kernel_ms": round(r["kernel_ms"], 4),
+                    "tokens_per_s": round(r["tokens_per_s"], 1),
+                    "hbm_frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                    "mfma_frac": round(r["tflops"] / BF16_PEAK_TFLOPS, 4)})
+    del inp
+    torch.cuda.empty_cache()
+    return out
 
 
 # Option workloads measured beside the plain mixer, at the prefill_bf16 shape.
@@ -291,25 +348,46 @@ def bench_decode(w, steps, warmup, torch, m3, synth, seed=1004, premix=False):
                 gbs=nbytes / (kms * 1e-3) / 1e9)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, budget_s, torch):
-    """fp64 oracle on this host's cores over the same inputs (whole workload,
-    repeated until about budget_s seconds have been spent)."""
+    """The fp64 oracle on this host's cores over a bounded sample of the same
+    inputs: whole batch rows (every head, every token) in order until about
+    budget_s seconds are spent, on all visible cores; then one (batch, head)
+    unit on one thread for the single-thread rate.  Rates are tokens/s of the
+    workload (a token is one sequence position of one batch row, all heads)."""
     import oracle
     from mamba_selective_ssm_amd.synth import to_f64_numpy
-    args = [to_f64_numpy(inp[k]) for k in ("x", "B", "C", "dt", "A", "theta", "lam")]
+    keys = ("x", "B", "C", "dt", "A", "theta", "lam")
     threads = oracle.default_threads()
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
+    rows, el = 0, 0.0
+    for b in range(w.batch):
+        args = [to_f64_numpy(inp[k] if k == "A" else inp[k][b:b + 1]) for k in keys]
+        t0 = time.perf_counter()
         oracle.scan(*args, threads=threads)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s or reps >= 1000:
+        el += time.perf_counter() - t0
+        rows += 1
+        if el >= budget_s:
             break
-    el = time.perf_counter() - t0
-    return {"value": w.batch * w.seqlen * reps / el, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "whole %s workload (%d x %d tokens, %d heads) x %d repetitions, %.1f s"
-                      % (w.name, w.batch, w.seqlen, w.heads, reps, el)}
+    one = [to_f64_numpy(inp[k][0:1] if k == "A" else inp[k][0:1, :, 0:1]) for k in keys]
+    t0 = time.perf_counter()
+    oracle.scan(*one, threads=1)
+    el1 = time.perf_counter() - t0
+    return {"value": rows * w.seqlen / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "single_thread_tokens_per_s": w.seqlen / w.heads / el1,
+            "sample": "%d of %d batch rows of %s (each %d tokens x %d heads), %.1f s on %d "
+                      "threads; single thread: one (batch, head) unit of %d tokens, %.1f s"
+                      % (rows, w.batch, w.name, w.seqlen, w.heads, el, threads, w.seqlen, el1)}
 
 
 def progress(msg):
@@ -347,9 +425,9 @@ def backward_lines(steps, torch, m3, synth):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill_bf16")
+    ap.add_argument("--workload", default="mimo_prefill_bf16")
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-options", action="store_true",
@@ -416,11 +494,6 @@ def main(argv=None):
         w = w.with_(chunk=args.chunk)
     progress("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
     r = bench_prefill(w, args.steps, args.warmup, torch, m3, synth)
-    traffic = load_traffic(w.name)
-    roof = {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "m3::scan_kernel", "kernel_ms": round(r["kernel_ms"], 5),
-            "algorithmic_bytes_per_launch": r["bytes"]}
     out = {"metric": METRIC, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
@@ -429,31 +502,41 @@ def main(argv=None):
                       "seqlen": w.seqlen, "headdim": w.headdim, "dstate": w.dstate,
                       "rank": w.rank, "chunk": w.chunk, "state": "fp32",
                       "accumulate": "fp32"},
-           "roofline": roof}
+           "roofline": roofline(r, w.name)}
     inp = r.pop("inputs")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on the headline's own inputs, before they are freed
+        progress("timing the fp64 oracle on the host")
+        cpu = cpu_baseline(w, inp, args.cpu_budget, torch)
+    del inp
+    torch.cuda.empty_cache()
 
     if not args.no_secondary:
         sec = {}
-        for name in ("mimo_prefill_bf16", "long_prefill_bf16"):
+        nsec = max(args.steps, 20)
+        for name in ("prefill_bf16", "long_prefill_bf16", "mimo_prefill_bf16"):
+            if name == w.name:
+                continue
             ws = synth.WORKLOADS[name]
             progress("timing %s" % name)
-            rs = bench_prefill(ws, 5, 2, torch, m3, synth)
+            rs = bench_prefill(ws, nsec, 3, torch, m3, synth)
             rs.pop("inputs")
-            sec[name] = {"tokens_per_s": round(rs["tokens_per_s"], 1),
-                         "kernel_ms": round(rs["kernel_ms"], 4),
-                         "hbm_gbs": round(rs["gbs"], 1),
-                         "hbm_frac": round(rs["gbs"] / HBM_PEAK_GBS, 4),
-                         "traffic": load_traffic(name)}
+            sec[name] = {"tokens_per_s": round(rs["tokens_per_s"], 1), "calls": nsec,
+                         "roofline": roofline(rs, name)}
             torch.cuda.empty_cache()
+        wl = synth.WORKLOADS["long_prefill_bf16"]
+        progress("long_prefill_bf16 chunk sweep")
+        sec.setdefault("long_prefill_bf16", {})["chunk_sweep"] = chunk_sweep(
+            wl, nsec, 3, torch, m3, synth)
         wd = synth.WORKLOADS["decode"]
         progress("timing decode: prefill + %d steps" % args.decode_steps)
         rd = bench_decode(wd, args.decode_steps, 8, torch, m3, synth)
         sec["decode"] = {"steps_per_s": round(rd["steps_per_s"], 1),
                          "tokens_per_s": round(rd["tokens_per_s"], 1),
-                         "kernel_ms": round(rd["kernel_ms"], 5),
-                         "hbm_gbs": round(rd["gbs"], 1),
-                         "hbm_frac": round(rd["gbs"] / HBM_PEAK_GBS, 4),
-                         "traffic": load_traffic("decode")}
+                         "calls": args.decode_steps,
+                         "roofline": roofline(rd, "decode", kernel="m3::decode_kernel",
+                                              flops=False)}
         if not args.no_options:
             progress("timing decode with the pre-mixer")
             rd = bench_decode(wd, min(args.decode_steps, 256), 8, torch, m3, synth, premix=True)
@@ -465,7 +548,7 @@ def main(argv=None):
         wp = synth.WORKLOADS["prefill_bf16"]
         for name, opts in ({} if args.no_options else OPTION_CASES).items():
             progress("timing %s" % name)
-            ro = bench_prefill_options(wp, opts, 20, 3, torch, m3, synth)
+            ro = bench_prefill_options(wp, opts, nsec, 3, torch, m3, synth)
             sec[name] = {"tokens_per_s": round(ro["tokens_per_s"], 1),
                          "kernel_ms": round(ro["kernel_ms"], 5),
                          "hbm_gbs": round(ro["gbs"], 1),
@@ -474,9 +557,8 @@ def main(argv=None):
         out["secondary"] = sec
         torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline:
-        progress("timing the fp64 oracle on the host")
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, torch)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0
 

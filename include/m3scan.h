@@ -78,7 +78,11 @@
  * call and returns M3_OK or one of the negative m3_status codes below.  On an
  * error nothing has been enqueued.  NaN or Inf inputs are not errors: they
  * propagate into the outputs (within the dense chunk form a non-finite input
- * may reach outputs of earlier tokens of the same chunk).
+ * may reach outputs of earlier tokens of the same chunk).  The waves of one
+ * prefill workgroup hand chunk totals to each other through a counter with a
+ * bounded wait (so that no defect can hang the device); if such a wait ever
+ * ran out, that (batch, head)'s y and final state are NaN rather than
+ * silently wrong.
  */
 #ifndef M3SCAN_H
 #define M3SCAN_H
@@ -90,7 +94,7 @@
 extern "C" {
 #endif
 
-#define M3_ABI_VERSION 5
+#define M3_ABI_VERSION 6
 
 typedef enum {
     M3_F32 = 0,
@@ -200,8 +204,14 @@ typedef struct {
  * State record in (h_in, B_prev_in, x_prev_in): all three NULL means a zero
  * state and no previous token; otherwise all three must be given.
  * State record out (h_out, B_prev_out, x_prev_out): all three NULL, or all
- * three given; they must not overlap any input of the call.  With seqlen = 0
- * the record is copied through (or zeroed when no input record is given).
+ * three given.  They may be exactly the input record (h_out == h_in,
+ * B_prev_out == B_prev_in, x_prev_out == x_prev_in: the record is updated in
+ * place, as a decode step does -- the fixed-size state that a sequence split
+ * into calls carries, "Unlocking Rotational Dynamics via data-RoPE", TL;DR);
+ * then the call first copies the input record into its workspace, which
+ * m3_scan_workspace_bytes sizes for it.  Any other overlap with an input of
+ * the call is rejected.  With seqlen = 0 the record is copied through (or
+ * zeroed when no input record is given).
  * y may be NULL only when seqlen * batch * nheads == 0.
  * workspace: device memory of at least m3_scan_workspace_bytes(args) bytes,
  * 256-byte aligned (may be NULL when that size is 0).
@@ -339,7 +349,9 @@ m3_status m3_scan_fwd(const m3_scan_args *args, void *stream);
 
 /* Workspace bytes that m3_scan_fwd needs for these arguments (0 when the call
  * runs in a single pass).  Depends only on sizes, dtype, chunk, p_split and
- * segments.  Returns 0 for arguments that m3_scan_fwd would reject. */
+ * segments, on whether phase_out is given and on whether the output state
+ * record is the input record (in place).  Returns 0 for arguments that
+ * m3_scan_fwd would reject. */
 size_t m3_scan_workspace_bytes(const m3_scan_args *args);
 
 /* Gradient of a scan.  Enqueued on `stream`; allocates nothing. */

@@ -133,8 +133,18 @@ struct ScanPlan {
     int p_split, nseg, seg_chunks;
     int64_t phase_blocks;      // 64-token blocks per sequence (accumulated angle)
     size_t phase_off;          // workspace offset of the angle's partial sums
+    bool rec_alias;            // the output state record is the input record
+    size_t snap_off;           // workspace offset of the input record's copy (rec_alias)
+    size_t snap_h, snap_b;     // its h and B_prev parts in bytes (x_prev follows)
     size_t ws;
 };
+
+// The output state record is exactly the input record (updated in place).
+bool record_in_place(const m3_scan_args* a)
+{
+    return a->h_in != nullptr && a->h_out == a->h_in && a->B_prev_out == a->B_prev_in &&
+           a->x_prev_out == a->x_prev_in;
+}
 
 // Everything about a call that depends only on sizes: the compiled variant,
 // the headdim split, the sequence segments and the workspace they need.
@@ -188,6 +198,18 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
         if (out->phase_blocks > 65535) return M3_ERR_UNSUPPORTED;
         out->phase_off = (out->ws + 255) / 256 * 256;
         out->ws = out->phase_off + (size_t)nbh * out->phase_blocks * (N / 2) * 8;
+    }
+    // An in-place record: the kernels read a copy of the input record taken
+    // at the start of the call (the last segment's workgroups write the new
+    // record while others may still be about to read the old one).
+    out->rec_alias = record_in_place(a);
+    out->snap_off = out->snap_h = out->snap_b = 0;
+    if (out->rec_alias && nbh > 0) {
+        const size_t e = a->io_dtype == M3_F32 ? 4 : 2;
+        out->snap_off = (out->ws + 255) / 256 * 256;
+        out->snap_h = (size_t)nbh * N * P * 4;
+        out->snap_b = ((size_t)nbh * R * N * e + 15) / 16 * 16;
+        out->ws = out->snap_off + out->snap_h + out->snap_b + (size_t)nbh * R * P * e;
     }
     return M3_OK;
 }
@@ -596,6 +618,7 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         rg.dBL = a->dB_prev_out; rg.dxL = a->dx_prev_out;
         rg.dB = dBx; rg.dx = a->dx; rg.dBp = a->dB_prev; rg.dxp = a->dx_prev;
         rg.cu = a->opt.cu_seqlens;
+        rg.max_len = a->opt.max_seqlen;
         rg.batch = Bt; rg.L = L; rg.H = H; rg.N = (int)N; rg.P = (int)P; rg.R = (int)R;
         err = m3::launch_bwd_record_grad(rg, st);
     }
@@ -694,9 +717,13 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
         range_of(a->opt.phase_out, nbh * (N / 2) * 4),
     };
     const int nout = sizeof(out) / sizeof(out[0]);
-    for (const Range& o : out) {
-        for (const Range& i : in)
-            if (overlaps(o, i)) return M3_ERR_ALIAS;
+    // out[1..3] may be exactly the input record in[7..9] (updated in place);
+    // any other overlap is rejected.
+    for (int k = 0; k < nout; ++k) {
+        for (int i = 0; i < 18; ++i) {
+            if (plan.rec_alias && k >= 1 && k <= 3 && i >= 7 && i <= 9) continue;
+            if (overlaps(out[k], in[i])) return M3_ERR_ALIAS;
+        }
     }
     for (int i = 0; i < nout; ++i)
         for (int j = i + 1; j < nout; ++j)
@@ -711,6 +738,23 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     p.x = a->x; p.B = a->B; p.C = a->C;
     p.dt = a->dt; p.A = a->A; p.theta = a->theta; p.lam = a->lam;
     p.h_in = a->h_in; p.Bp_in = a->B_prev_in; p.xp_in = a->x_prev_in;
+    if (plan.rec_alias) {
+        // copy the input record to the workspace; the kernels read the copy
+        char* snap = static_cast<char*>(a->workspace) + plan.snap_off;
+        const hipStream_t s0 = static_cast<hipStream_t>(stream);
+        const size_t bx = (size_t)nbh * R * P * e;
+        hipError_t ec = hipMemcpyAsync(snap, a->h_in, plan.snap_h, hipMemcpyDeviceToDevice, s0);
+        if (ec == hipSuccess)
+            ec = hipMemcpyAsync(snap + plan.snap_h, a->B_prev_in, (size_t)nbh * R * N * e,
+                                hipMemcpyDeviceToDevice, s0);
+        if (ec == hipSuccess)
+            ec = hipMemcpyAsync(snap + plan.snap_h + plan.snap_b, a->x_prev_in, bx,
+                                hipMemcpyDeviceToDevice, s0);
+        if (ec != hipSuccess) return hip_status(ec);
+        p.h_in = reinterpret_cast<const float*>(snap);
+        p.Bp_in = snap + plan.snap_h;
+        p.xp_in = snap + plan.snap_h + plan.snap_b;
+    }
     p.y = a->y; p.h_out = a->h_out; p.Bp_out = a->B_prev_out; p.xp_out = a->x_prev_out;
     p.ws = static_cast<float*>(a->workspace);
     p.opt = op;

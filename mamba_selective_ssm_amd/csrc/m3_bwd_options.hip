@@ -573,10 +573,14 @@ __global__ void __launch_bounds__(kThreads) bo_record_grad_kernel(RecGradParams 
         const float g = isB ? q.dBL[bh * q.R * q.N + k] : q.dxL[bh * q.R * q.P + k];
         int64_t last = -1;                                       // token row of the last token
         if (q.cu != nullptr) {
+            // offsets clamped and the length capped at max_seqlen, as the
+            // forward and the padding kernel do: the record holds token
+            // st + len - 1
             int64_t st = q.cu[b], en = q.cu[b + 1];
             st = st < 0 ? 0 : (st > q.L ? q.L : st);
             en = en < st ? st : (en > q.L ? q.L : en);
-            if (en > st) last = en - 1;
+            const int64_t len = en - st < q.max_len ? en - st : q.max_len;
+            if (len > 0) last = st + len - 1;
         } else if (q.L > 0) {
             last = b * q.L + q.L - 1;
         }

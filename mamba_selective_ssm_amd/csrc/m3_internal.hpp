@@ -141,6 +141,7 @@ struct RecGradParams {
     float *dB, *dx;           // token gradients [rows][L or T][H][R][N or P]
     float *dBp, *dxp;         // input record gradients, or NULL
     const int* cu;            // packed: [batch + 1], else NULL
+    int64_t max_len;          // packed: the length cap (max_seqlen)
     int64_t batch, L, H;      // L: tokens per row (dense) or the packed length
     int N, P, R;
 };

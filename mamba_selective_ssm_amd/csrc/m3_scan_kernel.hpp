@@ -250,6 +250,21 @@ __device__ __forceinline__ float strided_inclusive_sum(float v, int lane)
     return v;
 }
 
+// Wait until the workgroup-shared counter *cnt reaches target (the other
+// waves of the workgroup publish before they wait, so it always does), with
+// a bound of 2^22 polls so that a defect can never hang the device.  Returns
+// false only if the bound ran out; the caller then poisons its results.
+__device__ __forceinline__ bool bounded_wait_at_least(int* cnt, int target)
+{
+    for (int it = 0; it < (1 << 22); ++it) {
+        const int v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (v >= target) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
 // FULL: outputs y (and the state record when this is the last segment).
 // !FULL: state pass -- each segment except the last writes its end state
 // (from a zero start, except segment 0 which starts from the true state).
@@ -702,14 +717,14 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             // bounded wait: the waves reach it together), then this wave's
             // offset is the sum of the totals of the waves before it.
             const int target = NWP * pcall;
-            for (int it = 0; it < (1 << 22); ++it) {
-                const int v = __builtin_amdgcn_readfirstlane(
-                    __hip_atomic_load(sCnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-                if (v >= target) break;
-                __builtin_amdgcn_s_sleep(1);
-            }
+            const bool waited = bounded_wait_at_least(sCnt, target);
             f32x4 off = {0.f, 0.f, 0.f, 0.f};
             for (int w = 0; w < pw; ++w) off += *reinterpret_cast<const f32x4*>(sXW + w * NPR + 4 * lq);
+            // A wait that ran out (never observed: every prep wave publishes
+            // before it waits) poisons the rotated operands, so y and the
+            // state of this unit come out NaN instead of silently wrong.
+            if (!waited) off = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                     __builtin_nanf("")};
             auto rotate_cl = [&](auto fullc) {
                 constexpr bool FULLC = decltype(fullc)::value;
                 // Pre-mixer: each row's RMS scale from the NPR4 lanes that hold it.
@@ -887,13 +902,9 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 // waves reach it together), then the rows' RMS scales.
                 if constexpr (PM) {
                     const int target = WA * pcall;
-                    for (int it = 0; it < (1 << 22); ++it) {
-                        const int v = __builtin_amdgcn_readfirstlane(
-                            __hip_atomic_load(sCnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-                        if (v >= target) break;
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                    const float rn = 1.f / (float)N;
+                    // a wait that ran out poisons the row scales (NaN outputs)
+                    const float rn = bounded_wait_at_least(sCnt, target) ? 1.f / (float)N
+                                                                         : __builtin_nanf("");
 #pragma unroll
                     for (int kk = 0; kk < TPL; ++kk) {
                         int j = li * TPL + kk;

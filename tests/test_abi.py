@@ -200,7 +200,7 @@ def test_bwd_option_workspace(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.m3_abi_version() == 5
+    assert lib.m3_abi_version() == 6
     for code in range(-9, 1):
         s = lib.m3_status_string(code)
         assert s and s != b"unknown status"
@@ -267,6 +267,30 @@ def run_scan(lib, a):
 ])
 def test_scan_validation_codes(lib, kw, code):
     assert run_scan(lib, scan_args(**kw)) == code
+
+
+def test_scan_state_record_in_place(lib):
+    """The output state record may be exactly the input record: validation
+    accepts it (the workspace then holds a copy of the input record, so it
+    grows by the record's size); any partial overlap is still rejected."""
+    h, bp, xp = FAKE + (20 << 32), FAKE + (21 << 32), FAKE + (22 << 32)
+    rec_in = dict(h_in=h, B_prev_in=bp, x_prev_in=xp)
+    ws = lambda **kw: lib.m3_scan_workspace_bytes(ctypes.byref(scan_args(**kw)))
+    base = ws(**rec_in, h_out=FAKE + (23 << 32), B_prev_out=FAKE + (24 << 32),
+              x_prev_out=FAKE + (25 << 32))
+    inplace = ws(**rec_in, h_out=h, B_prev_out=bp, x_prev_out=xp)
+    nbh, N, P, R = 2 * 3, 64, 32, 1
+    assert base == 0
+    assert inplace >= nbh * N * P * 4 + nbh * R * (N + P) * 2
+    # in place needs that workspace
+    assert run_scan(lib, scan_args(**rec_in, h_out=h, B_prev_out=bp, x_prev_out=xp)) == -6
+    # partial overlaps of the two records, and a record that is only partly in place
+    assert run_scan(lib, scan_args(**rec_in, h_out=h + 16, B_prev_out=bp, x_prev_out=xp)) == -7
+    assert run_scan(lib, scan_args(**rec_in, h_out=h, B_prev_out=FAKE + (24 << 32),
+                                   x_prev_out=xp)) == -7
+    # the in-place record must still not overlap y or the workspace
+    assert run_scan(lib, scan_args(**rec_in, h_out=h, B_prev_out=bp, x_prev_out=xp,
+                                   workspace=h, workspace_bytes=inplace)) == -7
 
 
 def test_scan_zero_work_is_ok_without_pointers(lib):
@@ -340,3 +364,29 @@ def test_scan_workspace_for_the_accumulated_angle(lib):
     base = lib.m3_scan_workspace_bytes(ctypes.byref(scan_args(seqlen=1000)))
     ws = lib.m3_scan_workspace_bytes(ctypes.byref(scan_args(seqlen=1000, phase_out=FAKE + (43 << 32))))
     assert ws >= base + 2 * 3 * 16 * 32 * 8
+
+
+def test_bench_algorithmic_sizes():
+    """The benchmark's per-call byte and flop counts at the workloads' sizes:
+    bf16 x, B, C, y (2 bytes), float32 theta, dt, lam, A and state record; the
+    per head-token bytes e (2RP + 2RN) + 4 (N/2 + 2) are 648, 3336 and 1032
+    for the single-layer, MIMO and long-context workloads."""
+    import bench
+    from mamba_selective_ssm_amd import synth
+    for name, per_ht in (("prefill_bf16", 648), ("mimo_prefill_bf16", 3336),
+                         ("long_prefill_bf16", 1032)):
+        w = synth.WORKLOADS[name]
+        R, P, N, H = w.rank, w.headdim, w.dstate, w.heads
+        rec = w.batch * H * (4 * N * P + 2 * R * (N + P))
+        assert bench.scan_algorithmic_bytes(w) == w.batch * w.seqlen * H * per_ht + rec + 4 * H
+        Q = w.chunk
+        assert bench.scan_dense_flops(w) == w.batch * w.seqlen * H * (
+            2 * Q * R * R * (N + P) + 4 * R * N * P)
+    # decode: state in and out, record in and out, step inputs, y
+    wd = synth.WORKLOADS["decode"]
+    assert bench.decode_algorithmic_bytes(wd) == 256 * 32 * 71944 + 4 * 32
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import bench
+    assert bench.main(["--gpus", "2"]) == 2

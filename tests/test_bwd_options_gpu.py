@@ -321,3 +321,33 @@ def test_bwd_record_gradient_without_tokens_reaches_the_input_record():
     torch.cuda.synchronize()
     assert torch.equal(got.dB_prev, dBL) and torch.equal(got.dx_prev, dxL)
     assert torch.count_nonzero(got.dh_in) == 0
+
+
+@pytest.mark.parametrize("method", ["step", "chunked"])
+def test_bwd_record_gradient_follows_the_max_seqlen_cap(method):
+    """Packed sequences of 5 and 12 tokens with max_seqlen = 8: the forward
+    scans only the first 8 tokens of the second sequence, so its output record
+    holds token 8 (packed row 12), and the record's gradient belongs there,
+    not on the sequence's last packed row.  With dy = 0 and dh_out = 0 the
+    record gradient is the only gradient: dx and dB equal it on each
+    sequence's recorded token and vanish on every other scanned token."""
+    lens, cap = [5, 12], 8
+    cu = torch.tensor([0, 5, 17], dtype=torch.int32, device=DEV)
+    w = workload(1, sum(lens), 2, 2, 32, 64, io="f32", dt_mu=-1.0)
+    inp = synth.make_scan_inputs(w, 1620, DEV)
+    g = torch.Generator(device=DEV).manual_seed(1621)
+    dBL = torch.randn(2, 2, 2, 64, generator=g, device=DEV)
+    dxL = torch.randn(2, 2, 2, 32, generator=g, device=DEV)
+    say("case bwd record gradient with a max_seqlen cap [%s] lengths=%s cap=%d" % (method, lens, cap))
+    got = m3_scan_bwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"], inp["lam"],
+                      torch.zeros_like(inp["x"]), method=method, cu_seqlens=cu, max_seqlen=cap,
+                      record_grad=(dBL, dxL))
+    torch.cuda.synchronize()
+    rec_row = {0: 4, 1: 5 + cap - 1}
+    scanned = list(range(0, 5)) + list(range(5, 5 + cap))
+    for s, row in rec_row.items():
+        assert torch.equal(got.dx[0, row], dxL[s]), (s, row)
+        assert torch.equal(got.dB[0, row], dBL[s]), (s, row)
+    others = [r for r in scanned if r not in rec_row.values()]
+    assert torch.count_nonzero(got.dx[0, others]) == 0
+    assert torch.count_nonzero(got.dB[0, others]) == 0

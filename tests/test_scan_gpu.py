@@ -99,6 +99,36 @@ def test_split_scan_equals_one_scan():
     assert rel_err(f64(s2.h), f64(so.h)) < 1e-5
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("segments,p_split", [(1, 0), (1, 4), (5, 0), (3, 4)])
+def test_split_scan_with_the_record_in_place(io, segments, p_split):
+    """A sequence of 1000 tokens run as calls of 333, 1, 400 and 266 tokens
+    that update one state record in place (state_out is state_in), with
+    forced sequence segments and headdim slices: y of every call and the final
+    record against the oracle on the whole sequence."""
+    w = workload(2, 1000, 3, 1, 64, 64, io=io, dt_mu=-1.0)
+    say("case in-place record split: %s segments=%d p_split=%d" % (w, segments, p_split))
+    inp = synth.make_scan_inputs(w, 78, DEV)
+    st0 = random_state(w, 79, DEV)
+    rec = State(st0[0].clone(), st0[1].clone(), st0[2].clone())
+    ys, a = [], 0
+    for b in (333, 334, 734, 1000):
+        part = [inp[k][:, a:b].contiguous() if k != "A" else inp[k]
+                for k in ("x", "B", "C", "dt", "A", "theta", "lam")]
+        y, out = m3_scan_fwd(*part, rec, state_out=rec, segments=segments, p_split=p_split)
+        assert out is rec
+        ys.append(y)
+        a = b
+    torch.cuda.synchronize()
+    yr, hr, br, xr = oracle_scan(inp, st0)
+    tol = TOL[io]
+    ey, eh = rel_err(f64(torch.cat(ys, 1)), yr), rel_err(f64(rec.h), hr)
+    say("   rel err y %.3e  state %.3e" % (ey, eh))
+    assert ey <= tol and eh <= tol
+    np.testing.assert_array_equal(f64(rec.B_prev), br)
+    np.testing.assert_array_equal(f64(rec.x_prev), xr)
+
+
 def test_hand_set_parity_tracking_exact_sign():
     """theta_t = pi * bit_t, A = 0, dt = 1, lam = 1, B = 0, h0 = C = e_1:
     y_t = (-1)^(number of ones so far), for 4096 tokens through 64 chunks."""
