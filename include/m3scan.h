@@ -136,7 +136,8 @@ typedef enum {
     M3_ERR_WORKSPACE = -6,   /* workspace missing or smaller than m3_scan_workspace_bytes */
     M3_ERR_ALIAS = -7,       /* an output overlaps an input it must not overlap */
     M3_ERR_HIP = -8,         /* a HIP call failed; see m3_last_hip_error() */
-    M3_ERR_OPTION = -9       /* an m3_options field or the gradient method is out of range */
+    M3_ERR_OPTION = -9,      /* an m3_options field or the gradient method is out of range */
+    M3_ERR_SCRATCH = -10     /* m3_scan_fwd_noalloc: the call needs more scratch than the library holds */
 } m3_status;
 
 /*
@@ -346,6 +347,25 @@ typedef struct {
 /* Chunked prefill: y and (optionally) the state record after the last token.
  * Enqueued on `stream`; returns before the work completes. */
 m3_status m3_scan_fwd(const m3_scan_args *args, void *stream);
+
+/* m3_scan_fwd for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid device allocation): the same
+ * scan, but every byte of scratch the call needs (the segment records, the
+ * accumulated angle's partial sums, the copy of an in-place state record) is
+ * taken from one static device array of M3_NOALLOC_SCRATCH_BYTES bytes inside
+ * the library instead of a workspace argument; args->workspace and
+ * args->workspace_bytes are ignored.  The caller still provides the inputs
+ * and outputs.  A call whose m3_scan_workspace_bytes exceeds
+ * M3_NOALLOC_SCRATCH_BYTES returns M3_ERR_SCRATCH (checked, like every other
+ * argument, before any HIP call).  It calls no allocating routine; each GPU
+ * it runs on holds the array until the process ends, and the first call on a
+ * device looks its address up there.  `stream` must belong to the current
+ * device (else M3_ERR_HIP with hipErrorInvalidDevice).  Every call on one GPU
+ * shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, or threads) race and must be serialised by the caller.  Nothing in
+ * the array needs clearing: every call writes the scratch it reads. */
+#define M3_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+m3_status m3_scan_fwd_noalloc(const m3_scan_args *args, void *stream);
 
 /* Workspace bytes that m3_scan_fwd needs for these arguments (0 when the call
  * runs in a single pass).  Depends only on sizes, dtype, chunk, p_split and

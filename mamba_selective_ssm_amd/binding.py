@@ -36,7 +36,7 @@ LIB_PATH = os.path.join(_HERE, "libm3scan.so")
 M3_F32, M3_BF16 = 0, 1
 _STATUS = {0: "M3_OK", -1: "M3_ERR_NULL", -2: "M3_ERR_SHAPE", -3: "M3_ERR_UNSUPPORTED",
            -4: "M3_ERR_DTYPE", -5: "M3_ERR_ALIGN", -6: "M3_ERR_WORKSPACE", -7: "M3_ERR_ALIAS",
-           -8: "M3_ERR_HIP", -9: "M3_ERR_OPTION"}
+           -8: "M3_ERR_HIP", -9: "M3_ERR_OPTION", -10: "M3_ERR_SCRATCH"}
 PHASE_MODES = {"native": 0, "zero": 1, "reverse": 2, "shuffle": 3,
                # decode steps only: the rotation removed from writing / readout
                "no_write": 4, "no_read": 5, "no_write_read": 6}
@@ -128,6 +128,8 @@ def load_library():
         lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
         lib.m3_scan_fwd.restype = ctypes.c_int
         lib.m3_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp]
+        lib.m3_scan_fwd_noalloc.restype = ctypes.c_int
+        lib.m3_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanArgs), _vp]
         lib.m3_scan_bwd.restype = ctypes.c_int
         lib.m3_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _vp]
         lib.m3_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -249,7 +251,8 @@ def _stream_handle(stream) -> int:
 
 def _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, return_state,
                   y, state_out, workspace, ngroups=0, phase="native", perm=None, premix=None,
-                  cu_seqlens=None, max_seqlen=None, phase_in=None, phase_out=None):
+                  cu_seqlens=None, max_seqlen=None, phase_in=None, phase_out=None,
+                  alloc_workspace=True):
     lib = load_library()
     Bx, L, H, R, P = x.shape
     N = B.shape[-1]
@@ -301,7 +304,7 @@ def _prepare_scan(x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, r
                  x_prev_out=_ptr(state_out.x_prev) if state_out else None,
                  workspace=None, workspace_bytes=0, opt=opt)
     a._keep = keep
-    need = lib.m3_scan_workspace_bytes(ctypes.byref(a))
+    need = lib.m3_scan_workspace_bytes(ctypes.byref(a)) if alloc_workspace else 0
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(int(need), dtype=torch.uint8, device=x.device)
@@ -329,6 +332,26 @@ def m3_scan_fwd(x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
     st = load_library().m3_scan_fwd(ctypes.byref(a), _stream_handle(stream))
     if st != 0:
         raise M3Error(st, "m3_scan_fwd")
+    return y, state_out
+
+
+def m3_scan_fwd_noalloc(x, B, C, dt, A, theta, lam, state: Optional[State] = None, *,
+                        chunk: int = 0, p_split: int = 0, segments: int = 0,
+                        return_state: bool = True, y: Optional[torch.Tensor] = None,
+                        state_out: Optional[State] = None, stream=None, **options):
+    """m3_scan_fwd_noalloc: the same scan as m3_scan_fwd, its scratch taken
+    from the library's static device array (M3_NOALLOC_SCRATCH_BYTES) instead
+    of a workspace.  ``y`` and ``state_out`` may be given so that the call
+    itself allocates nothing; options as m3_scan_fwd (ngroups, phase, perm,
+    premix, cu_seqlens, max_seqlen, phase_in, phase_out)."""
+    a, y, state_out, _ = _prepare_scan(
+        x, B, C, dt, A, theta, lam, state, chunk, p_split, segments, return_state, y, state_out,
+        None, options.get("ngroups", 0), options.get("phase", "native"), options.get("perm"),
+        options.get("premix"), options.get("cu_seqlens"), options.get("max_seqlen"),
+        options.get("phase_in"), options.get("phase_out"), alloc_workspace=False)
+    st = load_library().m3_scan_fwd_noalloc(ctypes.byref(a), _stream_handle(stream))
+    if st != 0:
+        raise M3Error(st, "m3_scan_fwd_noalloc")
     return y, state_out
 
 

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "m3_internal.hpp"
 #include "m3_scan_kernel.hpp"
 
@@ -375,6 +377,45 @@ m3_status plan_bwd_core(const m3_scan_bwd_args* a, BwdPlan* out)
     return M3_OK;
 }
 
+// Scratch memory of m3_scan_fwd_noalloc: one file-scope device array that
+// each GPU the library runs on holds until the process ends.  In host code
+// `scratch` is only a stand-in for the symbol; its device address on each
+// device comes from hipGetSymbolAddress, taken once per device (with that
+// device current) on the first call there, and only that address is used.
+constexpr size_t kScratchBytes = M3_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the current device, which must be
+// the device of `stream` (NULL: the current device's default stream).
+m3_status scratch_address(void* stream, void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (stream != nullptr) {
+        int sdev = -1;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+        if (e != hipSuccess) return hip_status(e);
+        if (sdev != dev) return hip_status(hipErrorInvalidDevice);
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hip_status(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0)
+            return hip_status(hipErrorInvalidSymbol);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return M3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -644,6 +685,7 @@ const char* m3_status_string(m3_status s)
     case M3_ERR_ALIAS: return "output overlaps an input";
     case M3_ERR_HIP: return "HIP call failed";
     case M3_ERR_OPTION: return "option out of range (groups, phase mode, premix, eps)";
+    case M3_ERR_SCRATCH: return "call needs more scratch than M3_NOALLOC_SCRATCH_BYTES";
     }
     return "unknown status";
 }
@@ -668,9 +710,16 @@ size_t m3_scan_workspace_bytes(const m3_scan_args* a)
     return plan.ws;
 }
 
-m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Every argument check of m3_scan_fwd (no HIP call).  Without `own_ws` the
+// workspace is the library's scratch array: the caller's workspace fields are
+// not used and the plan's size is checked against the array instead.
+m3_status scan_check(const m3_scan_args* a, bool own_ws, ScanPlan* planp, m3::OptParams* opp)
 {
-    ScanPlan plan;
+    ScanPlan& plan = *planp;
     const m3_status ps = plan_scan(a, &plan);
     if (ps != M3_OK) return ps;
     const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
@@ -678,7 +727,7 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     const int64_t nbh = Bt * H;
     if (nbh == 0) return M3_OK;
 
-    m3::OptParams op;
+    m3::OptParams& op = *opp;
     const m3_status os = check_options(a->opt, H, N, R, L, &op);
     if (os != M3_OK) return os;
     const bool packed = a->opt.cu_seqlens != nullptr;
@@ -713,7 +762,7 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     const Range out[] = {
         range_of(a->y, tok * R * P * e),         range_of(a->h_out, nbh * N * P * 4),
         range_of(a->B_prev_out, nbh * R * N * e), range_of(a->x_prev_out, nbh * R * P * e),
-        range_of(a->workspace, (int64_t)plan.ws),
+        range_of(own_ws ? a->workspace : nullptr, (int64_t)plan.ws),
         range_of(a->opt.phase_out, nbh * (N / 2) * 4),
     };
     const int nout = sizeof(out) / sizeof(out[0]);
@@ -728,10 +777,24 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     for (int i = 0; i < nout; ++i)
         for (int j = i + 1; j < nout; ++j)
             if (overlaps(out[i], out[j])) return M3_ERR_ALIAS;
-    if (plan.ws > 0) {
+    if (plan.ws > 0 && own_ws) {
         if (a->workspace == nullptr || a->workspace_bytes < plan.ws) return M3_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0) return M3_ERR_ALIGN;
     }
+    if (plan.ws > kScratchBytes && !own_ws) return M3_ERR_SCRATCH;
+    return M3_OK;
+}
+
+// The launches of a checked m3_scan_fwd call, with workspace `ws`.
+m3_status scan_launch(const m3_scan_args* a, const ScanPlan& plan, const m3::OptParams& op, void* ws,
+                      void* stream)
+{
+    const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads;
+    const int64_t P = a->headdim, N = a->dstate, R = a->rank;
+    const int64_t nbh = Bt * H;
+    if (nbh == 0) return M3_OK;
+    const int e = io_size(a->io_dtype);
+    const void* theta = a->opt.phase_mode != M3_PHASE_ZERO ? a->theta : nullptr;
 
     m3::ScanParams p;
     memset(&p, 0, sizeof(p));
@@ -740,7 +803,7 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     p.h_in = a->h_in; p.Bp_in = a->B_prev_in; p.xp_in = a->x_prev_in;
     if (plan.rec_alias) {
         // copy the input record to the workspace; the kernels read the copy
-        char* snap = static_cast<char*>(a->workspace) + plan.snap_off;
+        char* snap = static_cast<char*>(ws) + plan.snap_off;
         const hipStream_t s0 = static_cast<hipStream_t>(stream);
         const size_t bx = (size_t)nbh * R * P * e;
         hipError_t ec = hipMemcpyAsync(snap, a->h_in, plan.snap_h, hipMemcpyDeviceToDevice, s0);
@@ -756,7 +819,7 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
         p.xp_in = snap + plan.snap_h + plan.snap_b;
     }
     p.y = a->y; p.h_out = a->h_out; p.Bp_out = a->B_prev_out; p.xp_out = a->x_prev_out;
-    p.ws = static_cast<float*>(a->workspace);
+    p.ws = static_cast<float*>(ws);
     p.opt = op;
     p.theta = static_cast<const float*>(theta);
     p.batch = Bt; p.L = L; p.H = H; p.P = P;
@@ -773,8 +836,35 @@ m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
     q.opt = op;
     q.rows = Bt; q.L = L; q.H = H; q.NPR = (int)(N / 2);
     q.nblk = plan.phase_blocks;
-    q.part = reinterpret_cast<double*>(static_cast<char*>(a->workspace) + plan.phase_off);
+    q.part = reinterpret_cast<double*>(static_cast<char*>(ws) + plan.phase_off);
     return hip_status(m3::launch_phase_accumulate(q, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_scan_fwd(const m3_scan_args* a, void* stream)
+{
+    ScanPlan plan;
+    m3::OptParams op;
+    const m3_status st = scan_check(a, true, &plan, &op);
+    if (st != M3_OK) return st;
+    return scan_launch(a, plan, op, a->workspace, stream);
+}
+
+m3_status m3_scan_fwd_noalloc(const m3_scan_args* a, void* stream)
+{
+    ScanPlan plan;
+    m3::OptParams op;
+    const m3_status st = scan_check(a, false, &plan, &op);
+    if (st != M3_OK) return st;
+    void* ws = nullptr;
+    if (plan.ws > 0 && a->batch * a->nheads > 0) {
+        const m3_status ss = scratch_address(stream, &ws);
+        if (ss != M3_OK) return ss;
+    }
+    return scan_launch(a, plan, op, ws, stream);
 }
 
 m3_status m3_decode_step(const m3_decode_args* a, void* stream)

@@ -201,7 +201,7 @@ def test_bwd_option_workspace(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.m3_abi_version() == 6
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         s = lib.m3_status_string(code)
         assert s and s != b"unknown status"
     assert lib.m3_status_string(-99) == b"unknown status"
@@ -291,6 +291,24 @@ def test_scan_state_record_in_place(lib):
     # the in-place record must still not overlap y or the workspace
     assert run_scan(lib, scan_args(**rec_in, h_out=h, B_prev_out=bp, x_prev_out=xp,
                                    workspace=h, workspace_bytes=inplace)) == -7
+
+
+def test_scan_noalloc_validation(lib):
+    """The allocation-free scan checks its arguments like m3_scan_fwd (before
+    any HIP call), ignores the workspace fields, and rejects a call whose
+    scratch exceeds M3_NOALLOC_SCRATCH_BYTES with M3_ERR_SCRATCH."""
+    noalloc = lambda a: lib.m3_scan_fwd_noalloc(ctypes.byref(a), None)
+    assert noalloc(scan_args(dstate=63)) == -2
+    assert noalloc(scan_args(x=None)) == -1
+    assert noalloc(scan_args(y=FAKE)) == -7
+    # 64 x 16 heads x 64 segments of 4096-token chunks: far more than 32 MiB of records
+    big = dict(batch=64, nheads=16, seqlen=1 << 16, headdim=64, dstate=64, segments=64)
+    ws = lib.m3_scan_workspace_bytes(ctypes.byref(scan_args(**big)))
+    assert ws > 32 << 20
+    assert noalloc(scan_args(**big)) == -10
+    # a caller's (bogus) workspace is ignored, not validated
+    assert noalloc(scan_args(**big, workspace=FAKE + 8, workspace_bytes=1)) == -10
+    assert lib.m3_status_string(-10) != b"unknown status"
 
 
 def test_scan_zero_work_is_ok_without_pointers(lib):
