@@ -158,6 +158,10 @@ template <> struct IoRow8<bf16> {
     __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
     __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
     __device__ __forceinline__ void store_raw(bf16* p) const { *reinterpret_cast<bf16x8*>(p) = v; }
+    __device__ __forceinline__ void set8(const float (&x)[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
+    }
 };
 template <> struct IoRow8<float> {
     f32x4 a, b;

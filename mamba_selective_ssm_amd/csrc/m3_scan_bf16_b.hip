@@ -17,6 +17,11 @@ const ScanVariant* scan_variants_bf16b(int* count)
     M3_SCAN_VARIANT(bf16, 1, 128, 1, 32, 64, 4, 4, 2),
     M3_SCAN_VARIANT(bf16, 1, 128, 4, 16, 64, 4, 8, 1),
     M3_SCAN_VARIANT(bf16, 1, 128, 4, 8, 64, 4, 4, 1),
+    // 128-row chunks at dstate 128 (the long-context chunk sweep's 128 and
+    // the MIMO prefill at chunk 32), with one chunk buffer: two do not fit
+    // in LDS
+    M3_SCAN_VARIANT_SB(bf16, 1, 128, 1, 128, 64, 4, 8, 1),
+    M3_SCAN_VARIANT_SB(bf16, 1, 128, 4, 32, 64, 4, 8, 1),
     M3_SCAN_VARIANT(bf16, 1, 64, 1, 32, 16, 4, 4, 1),
     M3_SCAN_VARIANT(bf16, 1, 64, 1, 128, 16, 4, 4, 1),
     };

@@ -93,11 +93,17 @@ struct ScanParams {
     int seg_chunks;     // chunks per segment
 };
 
-template <typename IO, int N_, int PS_, int R_, int Q_, int NWM_, int NWP_, int OCC_>
+// NBUF_ = 2: two chunk buffers in LDS (the prep waves fill one while the
+// math waves read the other); 1: one chunk buffer for chunks too long for two
+// (128 operand rows at dstate 128): the prep waves keep chunk c+1's prepared
+// operands in registers while the math waves run chunk c, and store them
+// after a second barrier per chunk.
+template <typename IO, int N_, int PS_, int R_, int Q_, int NWM_, int NWP_, int OCC_, int NBUF_ = 2>
 struct ScanCfg {
     using io_t = IO;
     using op_t = IO;
     static constexpr int N = N_, PS = PS_, R = R_, Q = Q_, NWM = NWM_, NWP = NWP_, OCC = OCC_;
+    static constexpr int NBUF = NBUF_;
     static constexpr int NW = NWM + NWP;
     static constexpr int NT = 64 * NW;
     static constexpr int NP = N < 32 ? 32 : N;      // state rows padded to the K block
@@ -107,9 +113,15 @@ struct ScanCfg {
     static constexpr int E = (int)sizeof(op_t);
     static constexpr bool BF = (E == 2);
     static constexpr int PADE = 16 / E;              // 16-byte row padding
-    static constexpr int LDB = NP + PADE;
+#ifndef M3_PAD_BC_BYTES
+#define M3_PAD_BC_BYTES 16
+#endif
+#ifndef M3_PAD_X_BYTES
+#define M3_PAD_X_BYTES 16
+#endif
+    static constexpr int LDB = NP + M3_PAD_BC_BYTES / E;   // Bbar, Cbar rows
     static constexpr int LDX = T + PADE;             // fp32: X^T rows
-    static constexpr int LDXR = PS + PADE;           // bf16: X rows
+    static constexpr int LDXR = PS + M3_PAD_X_BYTES / E;   // bf16: X rows
     static constexpr int LDH = NP + PADE;
     // prep waves: pair quads per wave, lanes per quad, tokens per lane
     static constexpr int QPWV = NPR4 >= NWP ? NPR4 / NWP : 1;
@@ -168,12 +180,18 @@ struct ScanCfg {
     // CL: each prep wave's angle totals per pair, exchanged once per chunk.
     static constexpr size_t sz_XW = (size_t)NWP * NPR * 4;
     template <bool FULL, bool PM = false> struct Lay {
+        // single chunk buffer (the state pass, without Cbar, keeps two)
+        static constexpr bool SB = NBUF == 1 && FULL;
         static constexpr size_t oB = 0;
         static constexpr size_t oC = sz_B;
         static constexpr size_t oX = oC + (FULL ? sz_B : 0);
         static constexpr size_t oF = oX + sz_X;
         static constexpr size_t BUF = (oF + nF * 4 + 15) / 16 * 16;
-        static constexpr size_t oH = 2 * BUF;
+        static constexpr size_t FST = (nF * 4 + 15) / 16 * 16;
+        // stride between the two buffers of {Bbar, Cbar, X} and of the scalars
+        static constexpr size_t BSTR = SB ? 0 : BUF;
+        static constexpr size_t FSTR = SB ? FST : BUF;
+        static constexpr size_t oH = SB ? oF + 2 * FST : 2 * BUF;
         static constexpr size_t oPW = oH + (FULL ? (SH1 ? 1 : 2) * sz_H1 : 0);
         static constexpr size_t oSS = oPW + (PM ? sz_PMW : 0);
         static constexpr size_t oXW = oSS + ((PM && !CL) ? sz_SS : 0);
@@ -196,6 +214,7 @@ struct ScanCfg {
     static_assert(NPR4 < NWP || NPR4 % NWP == 0, "pair quads must split evenly over prep waves");
     static_assert(PT % PG == 0 && NWM % PG == 0, "headdim tiles must split evenly over math waves");
     static_assert(lds_bytes <= 160 * 1024 && lds_bytes_pm <= 160 * 1024, "LDS budget");
+    static_assert(NBUF == 2 || (NBUF == 1 && BF && CL), "one chunk buffer: bf16 row-coalesced prep only");
 };
 
 // One prep thread's share of a chunk's raw inputs, loaded a chunk ahead.
@@ -254,13 +273,16 @@ __device__ __forceinline__ float strided_inclusive_sum(float v, int lane)
 // waves of the workgroup publish before they wait, so it always does), with
 // a bound of 2^22 polls so that a defect can never hang the device.  Returns
 // false only if the bound ran out; the caller then poisons its results.
+#ifndef M3_WAIT_SLEEP
+#define M3_WAIT_SLEEP 1
+#endif
 __device__ __forceinline__ bool bounded_wait_at_least(int* cnt, int target)
 {
     for (int it = 0; it < (1 << 22); ++it) {
         const int v = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
         if (v >= target) return true;
-        __builtin_amdgcn_s_sleep(1);
+        if constexpr (M3_WAIT_SLEEP > 0) __builtin_amdgcn_s_sleep(M3_WAIT_SLEEP);
     }
     return false;
 }
@@ -315,12 +337,13 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     op_t* sH = reinterpret_cast<op_t*>(smem + Lay::oH);   // [1 or 2][PS][LDH] G^T
-    auto buf_B = [&](int s) { return reinterpret_cast<op_t*>(smem + s * Lay::BUF + Lay::oB); };
-    auto buf_C = [&](int s) { return reinterpret_cast<op_t*>(smem + s * Lay::BUF + Lay::oC); };
-    auto buf_X = [&](int s) { return reinterpret_cast<op_t*>(smem + s * Lay::BUF + Lay::oX); };
+    constexpr bool SBUF = Lay::SB;
+    auto buf_B = [&](int s) { return reinterpret_cast<op_t*>(smem + s * Lay::BSTR + Lay::oB); };
+    auto buf_C = [&](int s) { return reinterpret_cast<op_t*>(smem + s * Lay::BSTR + Lay::oC); };
+    auto buf_X = [&](int s) { return reinterpret_cast<op_t*>(smem + s * Lay::BSTR + Lay::oX); };
     //   scalars: [Q][2] = (Lam_j * log2(e), w_j), [Q] gamma_j, [Q] w_j e^{Lam_tot-Lam_j},
     //   [NPR][2] cos/sin Phi_tot, [0] = Lam_tot * log2(e)
-    auto buf_F = [&](int s) { return reinterpret_cast<float*>(smem + s * Lay::BUF + Lay::oF); };
+    auto buf_F = [&](int s) { return reinterpret_cast<float*>(smem + s * Lay::FSTR + Lay::oF); };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -460,6 +483,11 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         return reinterpret_cast<decltype(base)>(reinterpret_cast<const char*>(base) + off);
     };
     PrepStage<Cf> st;
+    // One chunk buffer: chunk c+1's rotated Bbar, Cbar rows and X rows,
+    // held here until the math waves are done with chunk c.
+    // (The X rows stay in the raw stage until then: the next chunk's X loads
+    // are issued after they are stored.)
+    IoRow8<io_t> pend_b[SBUF ? KP : 1], pend_c[SBUF ? KP : 1];
     // Loads of chunk c into the prep stage, by part (LD_A0: per-token dt, lam
     // and decay rate for A0; LD_X: the X slice; LD_TH: dt and theta of the
     // lane's rows; LD_BC: B and C); `advance` then moves the pointers to the
@@ -627,7 +655,9 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             for (int k = 0; k < KP; ++k) cl_loc[k] += ex;   // (cl_loc[KP-1] is now inc)
             if (lane >= (MQ - 1) * NPR4) *reinterpret_cast<f32x4*>(sXW + pw * NPR + 4 * lq) = inc;
             if (lane == 0) __hip_atomic_fetch_add(sCnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (nx) issue_part(c + 1, ld_th{});
+            // (one chunk buffer: issued after the rotation, so that these
+            // registers are free while the rotated rows are held)
+            if (nx && !SBUF) issue_part(c + 1, ld_th{});
         }
 
         // ---- A0: decay prefix scan and trapezoid weights (one wave) -------
@@ -689,7 +719,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 if (XITEMS % (64 * NWP) != 0 && it >= XITEMS) it = XITEMS - 1;
                 int rho, cg;
                 xmap(it, rho, cg);
-                st.xq[k].store_raw(sX + rho * LDXR + 8 * cg);
+                if constexpr (!SBUF) st.xq[k].store_raw(sX + rho * LDXR + 8 * cg);
             }
         } else
 #pragma unroll
@@ -702,14 +732,16 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = ok ? st.xq[k].get(e) : 0.f;
-            if constexpr (BF) {
+            if constexpr (SBUF) {
+                st.xq[k].set8(v);   // masked rows, stored by the flush
+            } else if constexpr (BF) {
                 lds_store8(sX + rho * LDXR + 8 * cg, v);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sX[(8 * cg + e) * LDX + rho] = v[e];
             }
         }
-        if (CL && nx) issue_part(c + 1, ld_x{});
+        if (CL && nx && !SBUF) issue_part(c + 1, ld_x{});
 
         // ---- A1: angle prefix per pair quad, rotate B and C ----------------
         if constexpr (CL) {
@@ -771,13 +803,20 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                         }
                     }
                 };
+                // The rows of one token (its R ranks) share its angle: the
+                // sine and cosine are taken once per token.  A lane's first
+                // row starts a token (RPW and KP are multiples of R, or KP
+                // divides R), so token starts are the rows k % R == 0.
+                static_assert(RPW % R == 0 && (KP % R == 0 || R % KP == 0), "row groups must align with tokens");
+                float cs[4], sn[4];
 #pragma unroll
                 for (int k = 0; k < KP; ++k) {
                     const int rho = lr0 + k, r = rho % R;
                     const bool ok = FULLC || rho / R <= jl;
-                    float cs[4], sn[4];
+                    if (k % R == 0) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) rope_sincos<op_t>(off[e] + cl_loc[k][e], &sn[e], &cs[e]);
+                        for (int e = 0; e < 4; ++e) rope_sincos<op_t>(off[e] + cl_loc[k][e], &sn[e], &cs[e]);
+                    }
                     // R(Phi)^T applied to each pair
                     float o[8], v[8];
                     entries(st.bq[k][0], PM ? scB[k] : 1.f, 0, r, v);
@@ -788,7 +827,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                         o[2 * e] = cs[e] * b0 + sn[e] * b1;
                         o[2 * e + 1] = cs[e] * b1 - sn[e] * b0;
                     }
-                    lds_store8(sB + rho * LDB + 8 * lq, o);
+                    if constexpr (SBUF) pend_b[k].set8(o);
+                    else lds_store8(sB + rho * LDB + 8 * lq, o);
                     if constexpr (FULL) {
                         entries(st.cq[k][0], PM ? scC[k] : 1.f, 1, r, v);
 #pragma unroll
@@ -798,13 +838,15 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                             o[2 * e] = cs[e] * c0 + sn[e] * c1;
                             o[2 * e + 1] = cs[e] * c1 - sn[e] * c0;
                         }
-                        lds_store8(sC + rho * LDB + 8 * lq, o);
+                        if constexpr (SBUF) pend_c[k].set8(o);
+                        else lds_store8(sC + rho * LDB + 8 * lq, o);
                     }
                 }
             };
             if (jl == Q - 1) rotate_cl(std::true_type{});
             else rotate_cl(std::false_type{});
             if (nx) {
+                if constexpr (SBUF) issue_part(c + 1, ld_th{});
                 issue_part(c + 1, ld_bc{});
                 advance();
             }
@@ -1010,6 +1052,41 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         }
     };
 
+    // One chunk buffer: the held operands of prepared chunk c into LDS, then
+    // (cn: chunk c+1 exists) chunk c+1's X loads into the raw stage.  The
+    // other parts of chunk c+1 were issued during its prep step, after which
+    // the load pointers moved on; X is addressed one chunk back.
+    auto flush = [&](int64_t c, bool cn) {
+        if constexpr (SBUF) {
+            op_t* sB = buf_B(0);
+            op_t* sC = buf_C(0);
+            op_t* sX = buf_X(0);
+#pragma unroll
+            for (int k = 0; k < KP; ++k) {
+                const int rho = lr0 + k;
+                pend_b[k].store_raw(sB + rho * LDB + 8 * lq);
+                pend_c[k].store_raw(sC + rho * LDB + 8 * lq);
+            }
+#pragma unroll
+            for (int k = 0; k < XI; ++k) {
+                int it = ptid + k * 64 * NWP;
+                if (XITEMS % (64 * NWP) != 0 && it >= XITEMS) it = XITEMS - 1;
+                int rho, cg;
+                xmap(it, rho, cg);
+                st.xq[k].store_raw(sX + rho * LDXR + 8 * cg);
+            }
+            if (cn) {
+                if constexpr (EARLY) {
+                    lX -= Q * sXP;
+                    issue_part(c + 1, ld_x{});
+                    lX += Q * sXP;
+                } else {
+                    issue_loads(c + 1);
+                }
+            }
+        }
+    };
+
     // ========================= math waves ===================================
     // Math wave wv owns state tiles tau = wv*TPW + k, p-tile major
     // (pt = tau / NTL, nt = tau % NTL): rows 16*nt + 4*g + i, column
@@ -1187,7 +1264,10 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         // known, and the tile loops unroll with constant bounds.
         static_dispatch<0, QG>(wv / PG, [&](auto qgc) {
         constexpr int qg = decltype(qgc)::value;
-#pragma unroll
+        // (up to two query tiles per wave the loop unrolls, so the tiles'
+        // key ranges are compile-time constants; more are walked in a loop,
+        // which keeps the register footprint of one tile)
+#pragma unroll (QPW <= 2 ? QPW : 1)
         for (int qi = 0; qi < QPW; ++qi) {
             // query tiles of this wave; with several query groups, alternate
             // direction so that long and short key ranges pair up
@@ -1395,7 +1475,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         const float* sD = buf_F(s) + 3 * Q;
         const float* sCSt = sD + Q;
         const float aT = fast_exp2(sCSt[2 * NPR]);
-        if constexpr (TPW % NTL == 0 && NTILES % NWM == 0) {
+        if constexpr (TPW % NTL == 0 && NTILES % NWM == 0 && KB <= 2) {
             // A wave owns whole columns of tiles: every Bbar^T operand is
             // loaded once, up front, and reused for each of its p tiles.
             constexpr int PPD = TPW / NTL;
@@ -1451,7 +1531,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         if (c_begin < c_end) {
             issue_loads(c_begin);
             prep(c_begin, 0, EARLY && c_begin + 1 < c_end);
-            if (!EARLY && c_begin + 1 < c_end) issue_loads(c_begin + 1);
+            if (!EARLY && !SBUF && c_begin + 1 < c_end) issue_loads(c_begin + 1);
+            flush(c_begin, c_begin + 1 < c_end);
         }
         __syncthreads();
         __builtin_amdgcn_s_setprio(0);
@@ -1459,7 +1540,13 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             const int s = (int)((c - c_begin) & 1);
             if (c + 1 < c_end) {
                 prep(c + 1, s ^ 1, EARLY && c + 2 < c_end);
-                if (!EARLY && c + 2 < c_end) issue_loads(c + 2);
+                if (!EARLY && !SBUF && c + 2 < c_end) issue_loads(c + 2);
+            }
+            if constexpr (SBUF) {
+                // one chunk buffer: store chunk c+1's operands once the math
+                // waves are done reading chunk c's
+                __syncthreads();
+                if (c + 1 < c_end) flush(c + 1, c + 2 < c_end);
             }
             __syncthreads();
         }
@@ -1492,6 +1579,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             if constexpr (FULL) {
                 phase_C(c, s, sH + hs * HSTAGE);
                 phase_D(s);
+                if constexpr (SBUF) __syncthreads();   // the operands may now be overwritten
                 if constexpr (!Cf::SH1) hs ^= 1;
                 stage_state(hs);
             } else {

@@ -63,6 +63,17 @@ def test_chunk_invariance_bf16(chunk):
     check_scan(w, 5, with_state=True, chunk=chunk, label="chunk")
 
 
+@pytest.mark.parametrize("R,chunk", [(1, 128), (4, 32)])
+@pytest.mark.parametrize("segments", [0, 3])
+def test_one_chunk_buffer_variants(R, chunk, segments):
+    """128 operand rows per chunk at dstate 128 (one LDS chunk buffer, the
+    prepared rows held in registers across a second barrier per chunk): a
+    ragged tail, a random state record, with and without segments."""
+    w = workload(2, 1000 + 37, 3, R, 64, 128, io="bf16", dt_mu=-1.0)
+    check_scan(w, 90 + R + segments, with_state=True, chunk=chunk, segments=segments,
+               label="one-buffer")
+
+
 @pytest.mark.parametrize("p_split", [1, 4])
 def test_headdim_split_invariance(p_split):
     w = workload(2, 300, 2, 1, 64, 64, io="bf16")

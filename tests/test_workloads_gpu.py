@@ -66,9 +66,11 @@ def test_prefill_bf16_full_every_unit():
     run_workload("prefill_bf16", 2001, by_batch_row)
 
 
-def test_mimo_prefill_bf16_full_every_unit():
-    """batch 8, 32 heads, L=4096, P=64, N=128, R=4: all 256 units."""
-    run_workload("mimo_prefill_bf16", 2002, by_batch_row)
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_mimo_prefill_bf16_full_every_unit(chunk):
+    """batch 8, 32 heads, L=4096, P=64, N=128, R=4: all 256 units, at the
+    benchmark's chunk (16 tokens, 64 operand rows) and at 32 (128 rows)."""
+    run_workload("mimo_prefill_bf16", 2002, by_batch_row, chunk=chunk)
 
 
 def test_long_prefill_bf16_every_unit_at_each_chunk():
