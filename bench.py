@@ -361,23 +361,22 @@ def cpu_model():
 
 def cpu_baseline(w, inp, budget_s, torch):
     """The fp64 oracle on this host's cores over a bounded sample of the same
-    inputs: whole batch rows (every head, every token) in order until about
-    budget_s seconds are spent, on all visible cores; then one (batch, head)
-    unit on one thread for the single-thread rate.  Rates are tokens/s of the
+    inputs: whole batch rows (every head, every token), taken in turn until
+    about budget_s seconds are spent, on all visible cores; then one
+    (batch, head) unit on one thread for the single-thread rate.  Rates are tokens/s of the
     workload (a token is one sequence position of one batch row, all heads)."""
     import oracle
     from mamba_selective_ssm_amd.synth import to_f64_numpy
     keys = ("x", "B", "C", "dt", "A", "theta", "lam")
     threads = oracle.default_threads()
     rows, el = 0, 0.0
-    for b in range(w.batch):
+    while el < budget_s and rows < 64 * w.batch:
+        b = rows % w.batch
         args = [to_f64_numpy(inp[k] if k == "A" else inp[k][b:b + 1]) for k in keys]
         t0 = time.perf_counter()
         oracle.scan(*args, threads=threads)
         el += time.perf_counter() - t0
         rows += 1
-        if el >= budget_s:
-            break
     one = [to_f64_numpy(inp[k][0:1] if k == "A" else inp[k][0:1, :, 0:1]) for k in keys]
     t0 = time.perf_counter()
     oracle.scan(*one, threads=1)
@@ -385,9 +384,9 @@ def cpu_baseline(w, inp, budget_s, torch):
     return {"value": rows * w.seqlen / el, "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "cpu_model": cpu_model(),
             "single_thread_tokens_per_s": w.seqlen / w.heads / el1,
-            "sample": "%d of %d batch rows of %s (each %d tokens x %d heads), %.1f s on %d "
-                      "threads; single thread: one (batch, head) unit of %d tokens, %.1f s"
-                      % (rows, w.batch, w.name, w.seqlen, w.heads, el, threads, w.seqlen, el1)}
+            "sample": "%d batch rows of %s in turn (each %d tokens x %d heads; the workload has %d), "
+                      "%.1f s on %d threads; single thread: one (batch, head) unit of %d tokens, %.1f s"
+                      % (rows, w.name, w.seqlen, w.heads, w.batch, el, threads, w.seqlen, el1)}
 
 
 def progress(msg):
@@ -492,26 +491,11 @@ def main(argv=None):
     w = synth.WORKLOADS[args.workload]
     if args.chunk:
         w = w.with_(chunk=args.chunk)
-    progress("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
-    r = bench_prefill(w, args.steps, args.warmup, torch, m3, synth)
-    out = {"metric": METRIC, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
-           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": w.io_dtype, "data": "synthetic",
-           "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
-                      "seqlen": w.seqlen, "headdim": w.headdim, "dstate": w.dstate,
-                      "rank": w.rank, "chunk": w.chunk, "state": "fp32",
-                      "accumulate": "fp32"},
-           "roofline": roofline(r, w.name)}
-    inp = r.pop("inputs")
-    cpu = None
-    if not args.no_cpu_baseline:
-        # the oracle on the headline's own inputs, before they are freed
-        progress("timing the fp64 oracle on the host")
-        cpu = cpu_baseline(w, inp, args.cpu_budget, torch)
-    del inp
-    torch.cuda.empty_cache()
-
+    # The secondary workloads run first: the device clock settles under
+    # sustained load (in a kernel trace the first MIMO dispatches after an
+    # idle spell ran 687, 705, then 1004 us, easing to 742 us over twenty
+    # calls), so the headline's warm-up and timed steps follow them.
+    sec = None
     if not args.no_secondary:
         sec = {}
         nsec = max(args.steps, 20)
@@ -554,9 +538,30 @@ def main(argv=None):
                          "hbm_gbs": round(ro["gbs"], 1),
                          "hbm_frac": round(ro["gbs"] / HBM_PEAK_GBS, 4)}
         sec.update(backward_lines(args.steps, torch, m3, synth))
-        out["secondary"] = sec
         torch.cuda.empty_cache()
 
+    progress("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
+    r = bench_prefill(w, args.steps, args.warmup, torch, m3, synth)
+    out = {"metric": METRIC, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": w.io_dtype, "data": "synthetic",
+           "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
+                      "seqlen": w.seqlen, "headdim": w.headdim, "dstate": w.dstate,
+                      "rank": w.rank, "chunk": w.chunk, "state": "fp32",
+                      "accumulate": "fp32"},
+           "roofline": roofline(r, w.name)}
+    inp = r.pop("inputs")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on the headline's own inputs, before they are freed
+        progress("timing the fp64 oracle on the host")
+        cpu = cpu_baseline(w, inp, args.cpu_budget, torch)
+    del inp
+    torch.cuda.empty_cache()
+
+    if sec is not None:
+        out["secondary"] = sec
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -56,7 +56,7 @@ void for_each_variant(F&& f)
 // the widest headdim slice (no work repeated across slices); sequence
 // segments then supply the parallelism.
 const m3::ScanVariant* pick_scan(int io, int64_t N, int64_t R, int64_t P, int chunk,
-                                 int p_split, int64_t nbh)
+                                 int p_split, int64_t nbh, int premix = 0)
 {
     const int Q = chunk ? chunk : default_chunk(R, io);
     const m3::ScanVariant* best = nullptr;
@@ -64,8 +64,11 @@ const m3::ScanVariant* pick_scan(int io, int64_t N, int64_t R, int64_t P, int ch
         if (v.io != io || v.N != N || v.R != R || v.Q != Q) return;
         if (P % v.PS != 0) return;
         if (p_split != 0 && P / v.PS != p_split) return;
+        if (v.pm && !premix) return;                          // pre-mixer-only variant
         (void)nbh;
-        if (best == nullptr || v.PS > best->PS) best = &v;   // first of the widest
+        // first of the widest; with the pre-mixer a pre-mixer variant of
+        // the same width wins
+        if (best == nullptr || v.PS > best->PS || (v.PS == best->PS && v.pm && !best->pm)) best = &v;
     });
     return best;
 }
@@ -161,7 +164,7 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
     const int64_t nbh = Bt * H;
     if (nbh > (int64_t)1 << 28) return M3_ERR_UNSUPPORTED;
     const m3::ScanVariant* v = pick_scan(a->io_dtype, N, R, P, a->chunk, a->p_split,
-                                         nbh > 0 ? nbh : 1);
+                                         nbh > 0 ? nbh : 1, a->opt.premix == 1);
     if (v == nullptr) return M3_ERR_UNSUPPORTED;
     // In-chunk offsets are 32-bit: a chunk's span of every tensor must fit,
     // and a token's byte stride must fit the 24-bit multiplier.

@@ -179,6 +179,7 @@ struct ScanVariant {
     size_t lds_bytes;
     scan_launcher fn;
     scan_ws_fn ws_bytes;   // workspace bytes for a segmented call
+    int pm;                // 1: used only with the pre-mixer, and preferred then
 };
 
 // Tables defined by the instantiation units (host functions, so that the

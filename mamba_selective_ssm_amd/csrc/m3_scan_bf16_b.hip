@@ -10,6 +10,10 @@ const ScanVariant* scan_variants_bf16b(int* count)
     // headdim slice, the first listed is the one the library picks.
     static const ScanVariant table[] = {
     M3_SCAN_VARIANT(bf16, 1, 64, 1, 64, 64, 4, 4, 2),
+    // with the pre-mixer the two-per-unit variant spills: one workgroup per
+    // compute unit with 8 prep waves (54.3 -> 47.6 us on the single-layer
+    // prefill with the pre-mixer)
+    M3_SCAN_VARIANT_PM(bf16, 1, 64, 1, 64, 64, 4, 8, 1),
     // dstate 128 at one workgroup per compute unit: 4 matrix-core waves and 8
     // operand-prep waves (prep is the critical path; 13% faster on the MIMO
     // prefill and 7% on the long prefill than 4 + 4)
