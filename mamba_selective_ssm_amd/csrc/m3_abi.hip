@@ -136,6 +136,7 @@ void option_ranges(const m3_options& o, int64_t Bt, int64_t H, int64_t N, int64_
 struct ScanPlan {
     const m3::ScanVariant* v;
     int p_split, nseg, seg_chunks;
+    int nslots;                // packed sequences with per-sequence segments (0: uniform)
     int64_t phase_blocks;      // 64-token blocks per sequence (accumulated angle)
     size_t phase_off;          // workspace offset of the angle's partial sums
     bool rec_alias;            // the output state record is the input record
@@ -190,10 +191,34 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
     int64_t seg_chunks = nchunks > 0 ? (nchunks + nseg - 1) / nseg : 1;
     nseg = nchunks > 0 ? (nchunks + seg_chunks - 1) / seg_chunks : 1;
     if (nseg * ((nbh + 7) / 8 * 8) * p_split >= ((int64_t)1 << 31)) return M3_ERR_UNSUPPORTED;
+    int64_t nslots = 0;
+    if (a->opt.cu_seqlens != nullptr && a->segments == 0 && nbh > 0 && Bt <= 65536) {
+        // Packed sequences, library's segmentation: segments of a fixed
+        // number of chunks per sequence (a short sequence takes fewer), about
+        // `occ` workgroups per compute unit in all, at least three chunks per
+        // segment.  Each workgroup finds its (sequence, segment) on the device;
+        // the launch covers an upper bound of such slots.
+        const int64_t per_slot = (H + 7) / 8 * 8 * p_split;
+        int64_t tslots = 256 * (int64_t)v->occ / per_slot;
+        tslots = tslots < 1 ? 1 : tslots;
+        const int64_t tchunks = (L + v->Q - 1) / v->Q;
+        int64_t sc = (tchunks + tslots - 1) / tslots;
+        sc = sc < 3 ? 3 : sc;
+        const int64_t maxseg = nchunks > 0 ? (nchunks + sc - 1) / sc : 1;
+        if (maxseg > 1) {
+            // sum_b max(1, ceil(ceil(len_b / Q) / sc)) <= L / (Q sc) + 2 nseq
+            // when the offsets rise (others only give wrong results)
+            nslots = (tchunks + sc - 1) / sc + 2 * Bt + 1;
+            if (nslots * per_slot >= ((int64_t)1 << 31)) return M3_ERR_UNSUPPORTED;
+            nseg = maxseg;
+            seg_chunks = sc;
+        }
+    }
     out->v = v;
     out->p_split = p_split;
     out->nseg = (int)nseg;
     out->seg_chunks = (int)seg_chunks;
+    out->nslots = (int)nslots;
     out->ws = v->ws_bytes(nbh, P, (int)nseg);
     out->phase_blocks = 0;
     out->phase_off = 0;
@@ -830,6 +855,7 @@ m3_status scan_launch(const m3_scan_args* a, const ScanPlan& plan, const m3::Opt
     p.nbh = (int)nbh;
     p.nseg = plan.nseg;
     p.seg_chunks = plan.seg_chunks;
+    p.nslots = plan.nslots;
     const hipError_t e1 = plan.v->fn(p, static_cast<hipStream_t>(stream));
     if (e1 != hipSuccess || a->opt.phase_out == nullptr) return hip_status(e1);
     m3::PhaseParams q;

@@ -89,8 +89,11 @@ struct ScanParams {
     int64_t batch, L, H, P;
     int p_split;
     int nbh;
-    int nseg;           // sequence segments (1 = single pass)
+    int nseg;           // sequence segments (1 = single pass); per-sequence mode: the most
+                        // any sequence has (the record stride)
     int seg_chunks;     // chunks per segment
+    int nslots;         // packed sequences, per-sequence segments: (sequence, segment) slots
+                        // launched (an upper bound); 0: nseg segments of every sequence
 };
 
 // NBUF_ = 2: two chunk buffers in LDS (the prep waves fill one while the
@@ -256,6 +259,20 @@ __device__ __forceinline__ float group_inclusive_sum(float v)
     return v;
 }
 
+// Sum over aligned groups of G consecutive lanes (4, 8 or 16), every lane of a
+// group receiving its group's sum: a butterfly of DPP lane moves inside each
+// row of 16 lanes (no LDS round trip).
+template <int G>
+__device__ __forceinline__ float lane_group_sum(float v)
+{
+    static_assert(G == 4 || G == 8 || G == 16, "lane groups of 4, 8 or 16");
+    v += dpp_moved<0xB1, 0xf>(v);                            // quad_perm [1,0,3,2]
+    v += dpp_moved<0x4E, 0xf>(v);                            // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v += dpp_moved<0x141, 0xf>(v);     // row_half_mirror
+    if constexpr (G >= 16) v += dpp_moved<0x140, 0xf>(v);    // row_mirror
+    return v;
+}
+
 // Inclusive prefix sum over lanes l, l - S, l - 2S, ... (M lane groups of S
 // lanes: lanes with equal l % S form one sequence, ordered by l / S).
 template <int S, int M>
@@ -355,13 +372,49 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // go to different XCDs (round robin over 8), so the slices and segments
     // of one (b, h) are given ids that are multiples of 8 apart: they share an
     // XCD and its L2.
-    const int per_seg = (p.nbh + 7) / 8 * 8 * p.p_split;
-    const int seg = blockIdx.x / per_seg;
-    const int bid = blockIdx.x % per_seg;
-    const int bh = (bid >> 3) / p.p_split * 8 + (bid & 7);
-    const int ps = (bid >> 3) % p.p_split;
-    if (bh >= p.nbh) return;
     const int64_t H = p.H, P = p.P;
+    int seg, bh, ps, nseg_u = p.nseg;
+    if (p.nslots == 0) {
+        const int per_seg = (p.nbh + 7) / 8 * 8 * p.p_split;
+        seg = blockIdx.x / per_seg;
+        const int bid = blockIdx.x % per_seg;
+        bh = (bid >> 3) / p.p_split * 8 + (bid & 7);
+        ps = (bid >> 3) % p.p_split;
+        if (bh >= p.nbh) return;
+    } else {
+        // Packed sequences with segments sized per sequence: sequence b has
+        // max(1, ceil(chunks_b / seg_chunks)) segments, numbered in sequence
+        // order; a slot of heads x slices per (sequence, segment).  The slot
+        // is found by walking cu_seqlens (wave-uniform scalar loads); slots
+        // past the last sequence's last segment have no work.
+        const int per_slot = (int)((H + 7) / 8 * 8) * p.p_split;
+        const int slot = blockIdx.x / per_slot;
+        const int bid = blockIdx.x % per_slot;
+        const int hh = (bid >> 3) / p.p_split * 8 + (bid & 7);
+        ps = (bid >> 3) % p.p_split;
+        if (hh >= H) return;
+        int64_t first = 0, bsel = -1;
+        for (int64_t bb = 0; bb < p.batch; ++bb) {
+            int64_t lo = p.opt.cu[bb], hi = p.opt.cu[bb + 1];
+            lo = lo < 0 ? 0 : (lo > p.L ? p.L : lo);
+            hi = hi < lo ? lo : (hi > p.L ? p.L : hi);
+            const int64_t len = hi - lo < p.opt.max_len ? hi - lo : p.opt.max_len;
+            const int64_t nch = (len + Q - 1) / Q;
+            int64_t ns = (nch + p.seg_chunks - 1) / p.seg_chunks;
+            ns = ns < 1 ? 1 : ns;
+            if (slot < first + ns) {
+                bsel = bb;
+                nseg_u = (int)ns;
+                break;
+            }
+            first += ns;
+        }
+        if (bsel < 0) return;
+        seg = (int)(slot - first);
+        bh = (int)(bsel * H + hh);
+    }
+    // a state pass has no work in a sequence's last segment
+    if (!FULL && seg == nseg_u - 1) return;
     const int64_t b = bh / H, h = bh % H;
     const int p0 = ps * PS;
     // This unit's sequence: tokens base .. base+L-1 of the token arrays.  A
@@ -379,7 +432,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     const int64_t nchunks_all = (L + Q - 1) / Q;
     const int64_t c_begin = (int64_t)seg * p.seg_chunks;
     const int64_t c_end = c_begin + p.seg_chunks < nchunks_all ? c_begin + p.seg_chunks : nchunks_all;
-    const bool last_seg = seg == p.nseg - 1;
+    const bool last_seg = seg == nseg_u - 1;
 
     const int64_t G = p.opt.groups;                 // B/C head groups
     const int64_t hg = h / (H / G);                  // this head's group
@@ -775,11 +828,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                                 sc += vc * vc;
                             }
                         }
-#pragma unroll
-                        for (int o2 = 1; o2 < NPR4; o2 <<= 1) {
-                            sb += __shfl_xor(sb, o2, 64);
-                            if constexpr (FULL) sc += __shfl_xor(sc, o2, 64);
-                        }
+                        sb = lane_group_sum<NPR4>(sb);
+                        if constexpr (FULL) sc = lane_group_sum<NPR4>(sc);
                         scB[k] = rsqrtf(sb * rn + p.opt.eps);
                         scC[k] = FULL ? rsqrtf(sc * rn + p.opt.eps) : 0.f;
                     }
@@ -1682,6 +1732,11 @@ template <class Cf, bool PM>
 hipError_t launch_scan_t(const ScanParams& p, hipStream_t stream)
 {
     const int64_t per_seg = (int64_t)((p.nbh + 7) / 8) * 8 * p.p_split;
+    const int64_t per_slot = (p.H + 7) / 8 * 8 * p.p_split;
+    // grid of each pass: segments x (b, h, slice), or (sequence, segment)
+    // slots x (h, slice); a state pass's blocks in a last segment return
+    const int64_t grid_state = p.nslots ? per_slot * p.nslots : per_seg * (p.nseg - 1);
+    const int64_t grid_full = p.nslots ? per_slot * p.nslots : per_seg * p.nseg;
     constexpr size_t lds_state = Cf::template Lay<false, PM>::bytes;
     constexpr size_t lds_full = Cf::template Lay<true, PM>::bytes;
     auto* const k_state = &scan_kernel<Cf, false, PM>;
@@ -1691,14 +1746,13 @@ hipError_t launch_scan_t(const ScanParams& p, hipStream_t stream)
     if (p.nseg > 1) {
         e = scan_set_lds_limit<Cf, false, PM>();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_state, dim3((unsigned)(per_seg * (p.nseg - 1))), dim3(Cf::NT),
-                           lds_state, stream, p);
+        hipLaunchKernelGGL(k_state, dim3((unsigned)grid_state), dim3(Cf::NT), lds_state, stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     e = scan_set_lds_limit<Cf, true, PM>();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_full, dim3((unsigned)(per_seg * p.nseg)), dim3(Cf::NT), lds_full, stream, p);
+    hipLaunchKernelGGL(k_full, dim3((unsigned)grid_full), dim3(Cf::NT), lds_full, stream, p);
     return hipGetLastError();
 }
 

@@ -248,3 +248,30 @@ def test_packed_equal_lengths_match_dense_batch():
     torch.cuda.synchronize()
     assert torch.equal(yp.reshape(y.shape), y)
     assert torch.equal(sp.h, so.h)
+
+
+def test_packed_bench_lengths_per_sequence_segments():
+    """The benchmark's packed case: the single-layer prefill's 8192 tokens as
+    8 sequences of 1536, 256, 1024, 768, 2048, 512, 640 and 1408 tokens (16
+    heads, dstate 64, headdim 64, bf16), in the library's segmentation (a
+    fixed number of chunks per segment, so short sequences take fewer
+    segments), against the oracle per sequence, every head."""
+    lens = [1536, 256, 1024, 768, 2048, 512, 640, 1408]
+    T = sum(lens)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=DEV)
+    w = workload(1, T, 16, 1, 64, 64, io="bf16", dt_mu=-2.0)
+    say("case packed bench lengths %s" % (lens,))
+    inp = synth.make_scan_inputs(w, 460, DEV)
+    st = random_state(w.with_(batch=len(lens)), 461, DEV)
+    y, so = m3_scan_fwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
+                        inp["lam"], State(*st), cu_seqlens=cu, max_seqlen=max(lens))
+    torch.cuda.synchronize()
+    yr, hr, br, xr = oracle.scan_packed(f64(inp["x"]), f64(inp["B"]), f64(inp["C"]),
+                                        f64(inp["dt"]), f64(inp["A"]), f64(inp["theta"]),
+                                        f64(inp["lam"]), cu.cpu().numpy(), h0=f64(st[0]),
+                                        Bprev=f64(st[1]), xprev=f64(st[2]))
+    ey, eh = rel_err(f64(y), yr), rel_err(f64(so.h), hr)
+    say("   rel err y %.3e state %.3e" % (ey, eh))
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    np.testing.assert_array_equal(f64(so.B_prev), br)
+    np.testing.assert_array_equal(f64(so.x_prev), xr)
