@@ -235,9 +235,9 @@ def roofline(r, name, kernel="m3::scan_kernel", flops=True):
 
 
 def chunk_sweep(w, steps, warmup, torch, m3, synth, chunks=(32, 64, 128, 256), seed=1001):
-    """The long-context workload at each chunk length: time per call, HBM and
-    matrix-core fractions; chunk lengths outside the compiled set are listed
-    as unsupported."""
+    """A prefill workload at each chunk length (tokens): time per call, HBM
+    and matrix-core fractions (the dense-tile flops grow with the chunk);
+    chunk lengths outside the compiled set are listed as unsupported."""
     from mamba_selective_ssm_amd import M3_BF16
     inp = synth.make_scan_inputs(w, seed, "cuda")
     out = []
@@ -539,6 +539,12 @@ def main(argv=None):
                          "hbm_frac": round(ro["gbs"] / HBM_PEAK_GBS, 4)}
         sec.update(backward_lines(args.steps, torch, m3, synth))
         torch.cuda.empty_cache()
+        # the MIMO prefill at 32, 64 (the library's default) and 128 operand
+        # rows per chunk (chunks of 8, 16 and 32 tokens at rank 4)
+        wm = synth.WORKLOADS["mimo_prefill_bf16"]
+        progress("mimo_prefill_bf16 chunk sweep")
+        sec.setdefault("mimo_prefill_bf16", {})["chunk_sweep"] = chunk_sweep(
+            wm, nsec, 3, torch, m3, synth, chunks=(8, 16, 32))
 
     progress("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
     r = bench_prefill(w, args.steps, args.warmup, torch, m3, synth)
