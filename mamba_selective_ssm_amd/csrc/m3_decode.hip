@@ -36,6 +36,12 @@ namespace {
 
 constexpr int kDecWaves = 4;   // wavefronts (one (b, h) each) per workgroup, at most
 constexpr int kPB = 1;         // rotation pairs per batch and lane
+// The pre-mixer on row pieces (dstate 32, 64 or 128): each row's sum of
+// squares within an aligned lane group of N/8 lanes.
+__device__ constexpr bool decode_row_premix(bool pm, int N)
+{
+    return pm && (N == 32 || N == 64 || N == 128);
+}
 
 template <int R> struct RVec;
 template <> struct RVec<1> {
@@ -143,14 +149,42 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
     };
     if (npl > 0) load_batch(ha, 0);
 
+    // Pre-mixer, dstate 32, 64 or 128 (row pieces): each lane loads 8
+    // consecutive entries of one rank row of B and C below, so the N/8 lanes
+    // of an aligned lane group hold a whole row; the gains and biases of the
+    // lane's 8 entries are loaded now, in flight with the state.
+    const bool rowpm = decode_row_premix(PM, N);   // wave-uniform
+    f32x4 fw[4][2];   // B gain, C gain, B bias, C bias at the lane's entries
+    if constexpr (PM) {
+        if (rowpm && 8 * lane < R * N) {
+            const int r = 8 * lane / N, n = 8 * lane % N;
+            const int64_t bo = (h * R + r) * (int64_t)N + n;
+            const float* src[4] = {p.opt.Bw != nullptr ? p.opt.Bw + n : nullptr,
+                                   p.opt.Cw != nullptr ? p.opt.Cw + n : nullptr,
+                                   p.opt.Bb != nullptr ? p.opt.Bb + bo : nullptr,
+                                   p.opt.Cb != nullptr ? p.opt.Cb + bo : nullptr};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float dflt = m < 2 ? 1.f : 0.f;
+                if (src[m] != nullptr) {
+                    fw[m][0] = *reinterpret_cast<const f32x4*>(src[m]);
+                    fw[m][1] = *reinterpret_cast<const f32x4*>(src[m] + 4);
+                } else {
+                    fw[m][0] = f32x4{dflt, dflt, dflt, dflt};
+                    fw[m][1] = fw[m][0];
+                }
+            }
+        }
+    }
+
     // Pre-mixer gains and biases of this lane's first GPF entries n = lane +
-    // 64 k, loaded now so that they are in flight with the state (entries past
-    // 64 GPF, for N > 128, are read where they are used).
+    // 64 k (other dstates), loaded now so that they are in flight with the
+    // state (entries past 64 GPF, for N > 128, are read where they are used).
     constexpr int GPF = 2;
     float gwb[GPF], gwc[GPF], gbb[GPF][R], gbc[GPF][R];
     if constexpr (PM) {
 #pragma unroll
-        for (int k = 0; k < GPF; ++k) {
+        for (int k = 0; k < GPF && !rowpm; ++k) {
             const int n = lane + 64 * k;
             const bool ok = n < N;
             gwb[k] = (ok && p.opt.Bw != nullptr) ? p.opt.Bw[n] : 1.f;
@@ -174,11 +208,48 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
         gload8(vbp, Bp + idx);
         gload8_nt(vb, Bt + idx);
         gload8_nt(vc, Ct + idx);
+        if constexpr (PM) {
+            if (rowpm) {
+                // each row scaled by 1/rms over its N entries (the lane
+                // group's sum of squares), times the gain, plus the bias
+                float sb = 0.f, sc = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sb += vb[e] * vb[e];
+                    sc += vc[e] * vc[e];
+                }
+                if (N == 128) {
+                    sb = lane_group_sum<16>(sb);
+                    sc = lane_group_sum<16>(sc);
+                } else if (N == 64) {
+                    sb = lane_group_sum<8>(sb);
+                    sc = lane_group_sum<8>(sc);
+                } else {
+                    sb = lane_group_sum<4>(sb);
+                    sc = lane_group_sum<4>(sc);
+                }
+                const float kb = rsqrtf(sb / (float)N + p.opt.eps);
+                const float kc = rsqrtf(sc / (float)N + p.opt.eps);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    vb[e] = vb[e] * kb * fw[0][e / 4][e % 4] + fw[2][e / 4][e % 4];
+                    vc[e] = vc[e] * kc * fw[1][e / 4][e % 4] + fw[3][e / 4][e % 4];
+                }
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             sBp[(n + e) * R + r] = vbp[e];
             sB[(n + e) * R + r] = vb[e];
             sC[(n + e) * R + r] = vc[e];
+        }
+        if constexpr (PM) {
+            // the record's B: this step's pre-mixed row piece (the piece's
+            // old value, read above, is in LDS by now)
+            if (rowpm) {
+                gstore4(Bp + idx, f32x4{vb[0], vb[1], vb[2], vb[3]});
+                gstore4(Bp + idx + 4, f32x4{vb[4], vb[5], vb[6], vb[7]});
+            }
         }
     }
     for (int idx = n8 + lane; idx < R * N; idx += 64) {
@@ -233,50 +304,53 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
     // step's (every element is rewritten by an instruction of this wave that
     // follows the one that read it).
     if constexpr (PM) {
-        // Pre-mixer on the LDS copies of B and C: each (matrix, rank) row is
-        // scaled by 1/rms over its N entries, times the gain, plus the bias.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // Row sums of squares: the 2R rows' wavefront sums (DPP scans) are
-        // independent chains.
-        float sc[2][R];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float* row = m == 0 ? sB : sC;
-                float ss = 0.f;
-                for (int n = lane; n < N; n += 64) ss += row[n * R + r] * row[n * R + r];
-                ss = wave_read_lane(wave_inclusive_sum(ss), 63);
-                sc[m][r] = rsqrtf(ss / (float)N + p.opt.eps);
+        if (!rowpm) {
+            // Pre-mixer on the LDS copies of B and C (other dstates): each
+            // (matrix, rank) row is scaled by 1/rms over its N entries, times the
+            // gain, plus the bias.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // Row sums of squares: the 2R rows' wavefront sums (DPP scans) are
+            // independent chains.
+            float sc[2][R];
+    #pragma unroll
+            for (int m = 0; m < 2; ++m)
+    #pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float* row = m == 0 ? sB : sC;
+                    float ss = 0.f;
+                    for (int n = lane; n < N; n += 64) ss += row[n * R + r] * row[n * R + r];
+                    ss = wave_read_lane(wave_inclusive_sum(ss), 63);
+                    sc[m][r] = rsqrtf(ss / (float)N + p.opt.eps);
+                }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            auto premix_entry = [&](int n, float wb, float wc, const float (&bb)[R], const float (&bcv)[R]) {
+    #pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float vb = sB[n * R + r] * sc[0][r] * wb + bb[r];
+                    const float vc = sC[n * R + r] * sc[1][r] * wc + bcv[r];
+                    sB[n * R + r] = vb;
+                    sC[n * R + r] = vc;
+                    Bp[r * N + n] = from_f32<IO>(vb);
+                }
+            };
+    #pragma unroll
+            for (int k = 0; k < GPF; ++k)
+                if (lane + 64 * k < N) premix_entry(lane + 64 * k, gwb[k], gwc[k], gbb[k], gbc[k]);
+            for (int n = lane + 64 * GPF; n < N; n += 64) {
+                float bb[R], bcv[R];
+    #pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int64_t bi = (h * R + r) * (int64_t)N + n;
+                    bb[r] = p.opt.Bb != nullptr ? p.opt.Bb[bi] : 0.f;
+                    bcv[r] = p.opt.Cb != nullptr ? p.opt.Cb[bi] : 0.f;
+                }
+                premix_entry(n, p.opt.Bw != nullptr ? p.opt.Bw[n] : 1.f, p.opt.Cw != nullptr ? p.opt.Cw[n] : 1.f,
+                             bb, bcv);
             }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        auto premix_entry = [&](int n, float wb, float wc, const float (&bb)[R], const float (&bcv)[R]) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float vb = sB[n * R + r] * sc[0][r] * wb + bb[r];
-                const float vc = sC[n * R + r] * sc[1][r] * wc + bcv[r];
-                sB[n * R + r] = vb;
-                sC[n * R + r] = vc;
-                Bp[r * N + n] = from_f32<IO>(vb);
-            }
-        };
-#pragma unroll
-        for (int k = 0; k < GPF; ++k)
-            if (lane + 64 * k < N) premix_entry(lane + 64 * k, gwb[k], gwc[k], gbb[k], gbc[k]);
-        for (int n = lane + 64 * GPF; n < N; n += 64) {
-            float bb[R], bcv[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int64_t bi = (h * R + r) * (int64_t)N + n;
-                bb[r] = p.opt.Bb != nullptr ? p.opt.Bb[bi] : 0.f;
-                bcv[r] = p.opt.Cb != nullptr ? p.opt.Cb[bi] : 0.f;
-            }
-            premix_entry(n, p.opt.Bw != nullptr ? p.opt.Bw[n] : 1.f, p.opt.Cw != nullptr ? p.opt.Cw[n] : 1.f,
-                         bb, bcv);
         }
     } else {
         for (int idx = 8 * lane; idx < n8; idx += 512) copy8(Bp + idx, Bt + idx);

@@ -259,20 +259,6 @@ __device__ __forceinline__ float group_inclusive_sum(float v)
     return v;
 }
 
-// Sum over aligned groups of G consecutive lanes (4, 8 or 16), every lane of a
-// group receiving its group's sum: a butterfly of DPP lane moves inside each
-// row of 16 lanes (no LDS round trip).
-template <int G>
-__device__ __forceinline__ float lane_group_sum(float v)
-{
-    static_assert(G == 4 || G == 8 || G == 16, "lane groups of 4, 8 or 16");
-    v += dpp_moved<0xB1, 0xf>(v);                            // quad_perm [1,0,3,2]
-    v += dpp_moved<0x4E, 0xf>(v);                            // quad_perm [2,3,0,1]
-    if constexpr (G >= 8) v += dpp_moved<0x141, 0xf>(v);     // row_half_mirror
-    if constexpr (G >= 16) v += dpp_moved<0x140, 0xf>(v);    // row_mirror
-    return v;
-}
-
 // Inclusive prefix sum over lanes l, l - S, l - 2S, ... (M lane groups of S
 // lanes: lanes with equal l % S form one sequence, ordered by l / S).
 template <int S, int M>
