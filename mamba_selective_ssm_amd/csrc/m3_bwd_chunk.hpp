@@ -226,8 +226,11 @@ struct Held {
 __device__ __forceinline__ f32x4 v4f(const bf16x4& v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
 __device__ __forceinline__ f32x4 v4f(const f32x4& v) { return v; }
 
-// Issue every global load of chunk c of unit bh (zero past the sequence).
-template <class Cf, bool GRAD>
+// Issue the global loads of chunk c of unit bh (zero past the sequence), by
+// part: LR_STATE the boundary states (gradient only), LR_BC the B and C rows,
+// LR_XT the X and dY rows, theta and the token scalars.
+constexpr int LR_STATE = 1, LR_BC = 2, LR_XT = 4, LR_ALL = 7;
+template <class Cf, bool GRAD, int PARTS = LR_ALL>
 __device__ __forceinline__ void load_raw(const BcParams& p, int bh, int c, Raw<Cf>& rw, int tid)
 {
     using op_t = typename Cf::op_t;
@@ -240,7 +243,7 @@ __device__ __forceinline__ void load_raw(const BcParams& p, int bh, int c, Raw<C
     auto tok = [&](int64_t t) -> int64_t { return (b * L_ + t) * H + h; };
     const uint4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int it = 0; it < RW::IB; ++it) {
+    for (int it = 0; it < RW::IB && (PARTS & LR_BC); ++it) {
         const int v = tid + NTHR * it;
         rw.vb[it] = z; rw.vc[it] = z;
         if (v < T * VB) {
@@ -254,7 +257,7 @@ __device__ __forceinline__ void load_raw(const BcParams& p, int bh, int c, Raw<C
         }
     }
 #pragma unroll
-    for (int it = 0; it < RW::IX; ++it) {
+    for (int it = 0; it < RW::IX && (PARTS & LR_XT); ++it) {
         const int v = tid + NTHR * it;
         rw.vx[it] = z; rw.vy[it] = z;
         if (v < T * VX) {
@@ -268,7 +271,7 @@ __device__ __forceinline__ void load_raw(const BcParams& p, int bh, int c, Raw<C
         }
     }
 #pragma unroll
-    for (int it = 0; it < RW::IT; ++it) {
+    for (int it = 0; it < RW::IT && (PARTS & LR_XT); ++it) {
         const int v = tid + NTHR * it;
         rw.th[it] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (v < Q * (NPR / 4)) {
@@ -276,10 +279,12 @@ __device__ __forceinline__ void load_raw(const BcParams& p, int bh, int c, Raw<C
             if (t0 + j < L_) rw.th[it] = *reinterpret_cast<const f32x4*>(p.theta + tok(t0 + j) * NPR + 4 * q);
         }
     }
-    rw.dtv = 0.f; rw.lmv = 0.f; rw.av = 0.f;
-    if (tid <= Q && t0 + tid < L_) { rw.dtv = p.dt[tok(t0 + tid)]; rw.lmv = p.lam[tok(t0 + tid)]; }
-    if (p.a_tok && tid < Q && t0 + tid < L_) rw.av = p.A[tok(t0 + tid)];
-    if constexpr (GRAD) {
+    if constexpr ((PARTS & LR_XT) != 0) {
+        rw.dtv = 0.f; rw.lmv = 0.f; rw.av = 0.f;
+        if (tid <= Q && t0 + tid < L_) { rw.dtv = p.dt[tok(t0 + tid)]; rw.lmv = p.lam[tok(t0 + tid)]; }
+        if (p.a_tok && tid < Q && t0 + tid < L_) rw.av = p.A[tok(t0 + tid)];
+    }
+    if constexpr (GRAD && (PARTS & LR_STATE) != 0) {
         const op_t* gin = reinterpret_cast<const op_t*>(p.gst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
         const op_t* dgo = reinterpret_cast<const op_t*>(p.dgst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
         const float* cst = p.csum + ((size_t)bh * p.nc + c) * (1 + N);
@@ -693,10 +698,12 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
     auto tok = [&](int64_t t) -> int64_t { return (b * L_ + t) * H + h; };
     Held<Cf> hd;
     stage<Cf, true>(p, lds, bh, c, rw, hd, tid);
-    if (unit + (int)gridDim.x < nunits) {
-        const int un = unit + gridDim.x;
-        load_raw<Cf, true>(p, un / p.nc, un % p.nc, rw, tid);
-    }
+    // The next unit's loads go out in three parts, after staging and after
+    // the first two product phases, so that the waves' load issue does not
+    // all fall in one burst ahead of the first phase.
+    const bool more = unit + (int)gridDim.x < nunits;
+    const int un = unit + gridDim.x;
+    if (more) load_raw<Cf, true, LR_STATE>(p, un / p.nc, un % p.nc, rw, tid);
     const op_t* sBb = reinterpret_cast<const op_t*>(lds + L::oBb);
     const op_t* sCb = reinterpret_cast<const op_t*>(lds + L::oCb);
     const op_t* sX = reinterpret_cast<const op_t*>(lds + L::oX);
@@ -784,6 +791,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
         }
     }
     __syncthreads();
+    if (more) load_raw<Cf, true, LR_BC>(p, un / p.nc, un % p.nc, rw, tid);
 
     // ---- phase 2a: dX = (S o M)^T dY + diag(d) Bbar dGbar^T ------------------
     {
@@ -823,6 +831,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
         }
     }
     __syncthreads();                              // the S o M tile is free
+    if (more) load_raw<Cf, true, LR_XT>(p, un / p.nc, un % p.nc, rw, tid);
     put_gin<Cf>(sGi, hd, tid);
 
     // Back-rotation of dBbar / dCbar rows held in accumulators (lane: column
