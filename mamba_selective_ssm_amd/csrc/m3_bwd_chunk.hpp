@@ -842,9 +842,13 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
         for (int u = 0; u < NH; ++u) {
             const int n = 16 * (hf * NH + u) + l16, pr = n >> 1;
             const bool odd = (l16 & 1) != 0;
-            float dps[TPR];
+            float dps[TPR], snv[TPR], csv[TPR];
+            // the lane's 4 rows hold TPR tokens: one sine/cosine per token
 #pragma unroll
-            for (int v = 0; v < TPR; ++v) dps[v] = 0.f;
+            for (int v = 0; v < TPR; ++v) {
+                dps[v] = 0.f;
+                sincos_op<op_t>(sPhi[((r0w + 4 * g) / R + v) * LDH + pr], &snv[v], &csv[v]);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rk = r0w + 4 * g + i, tk = rk / R;
@@ -854,8 +858,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
                 const float bo = to_f32(sBar[rk * LDN + n]);
                 const float bx = pair_swap(bo);
                 const float b0 = odd ? bx : bo, b1 = odd ? bo : bx;
-                float sn, cs;
-                sincos_op<op_t>(sPhi[tk * LDH + pr], &sn, &cs);
+                const float sn = snv[i / R], cs = csv[i / R];
                 dps[i / R] += d0 * b1 - d1 * b0;
                 if (t0 + tk < L_)
                     gout[((size_t)tok(t0 + tk) * R + rk % R) * N + n] = odd ? sn * d0 + cs * d1 : cs * d0 - sn * d1;
