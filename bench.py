@@ -143,6 +143,103 @@ def traffic_summary(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     print(json.dumps(out))
 
 
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace_{n} -o t "
+             "-- python3 bench.py --steps 20 --warmup 3 --no-secondary --no-cpu-baseline --workload {n}",
+    "trace_decode": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace_decode "
+                    "-o t -- python3 bench.py --decode-only --decode-steps 256",
+    "pmc": "rocprofv3 --pmc {c} --kernel-include-regex scan_kernel --output-format csv "
+           "-d gpurun_out/prof/{f}_{n} -o {f} -- python3 bench.py --workload {n} --steps 3 --warmup 1 "
+           "--no-secondary --no-cpu-baseline",
+    "pmc_decode": "rocprofv3 --pmc {c} --kernel-include-regex decode_kernel --output-format csv "
+                  "-d gpurun_out/prof/{f}_decode -o {f} -- python3 bench.py --decode-only --decode-steps 64",
+    "copy": "rocprofv3 --pmc {c} --output-format csv -d gpurun_out/prof/c{f} -o {f} "
+            "-- python3 bench.py --copy-calibration 1024",
+}
+
+
+def trace_summary(name, trace_csv):
+    """profiles/<kernel>_<name>.md from a rocprofv3 kernel-trace csv of
+    `bench.py --workload name` (or --decode-only): per-kernel dispatch
+    statistics, the per-call sum, the algorithmic rate against 8 TB/s and 2.5
+    PFLOP/s, and the committed traffic summary of the same workload."""
+    import collections
+    import csv
+    import statistics
+    from mamba_selective_ssm_amd import synth
+    decode = name == "decode"
+    kre = "decode_kernel" if decode else "scan_kernel"
+    rows = [r for r in csv.DictReader(open(trace_csv)) if kre in r["Kernel_Name"]]
+    by = collections.OrderedDict()
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append(r)
+    w = synth.WORKLOADS[name]
+    lines = ["# %s on workload %s" % (kre, name), ""]
+    lines.append("Workload: batch %d, heads %d, seqlen %d, headdim %d, dstate %d, rank %d, %s I/O, "
+                 "chunk %d%s" % (w.batch, w.heads, w.seqlen, w.headdim, w.dstate, w.rank, w.io_dtype,
+                                 w.chunk, ", 256 decode steps" if decode else ""))
+    lines += ["", "## Kernel trace", "", "Command (repo root, `TMPDIR=/tmp`):", ""]
+    cmd = PROFILE_COMMANDS["trace_decode" if decode else "trace"].format(n=name)
+    lines += ["    " + cmd, "    python bench.py --trace-summary %s gpurun_out/prof/trace_%s/t_kernel_trace.csv"
+              % (name, name), ""]
+    lines += ["| kernel | pass | dispatches | avg us | median us | min us | max us | arch VGPR | "
+              "SGPR | grid | wg |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    call_avg = call_med = 0.0
+    durs_all = None
+    for k, rs in by.items():
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+        role = ("decode step" if decode else
+                "output (FULL)" if "EELb1E" in k else "state (no outputs)")
+        lines.append("| `%s` | %s | %d | %.1f | %.1f | %.1f | %.1f | %s | %s | %s | %s |" % (
+            k[:80], role, len(d), sum(d) / len(d), statistics.median(d), min(d), max(d),
+            rs[0]["VGPR_Count"], rs[0]["SGPR_Count"], rs[0]["Grid_Size_X"], rs[0]["Workgroup_Size_X"]))
+        call_avg += sum(d) / len(d)
+        call_med += statistics.median(d)
+        if durs_all is None or "EELb1E" in k:
+            durs_all = d
+    nbytes = decode_algorithmic_bytes(w) if decode else scan_algorithmic_bytes(w)
+    lines += ["", "Per entry-point call (sum of its passes): average %.1f us, median %.1f us." % (
+        call_avg, call_med)]
+    lines.append("Algorithmic bytes per call: %d -> %.0f GB/s on the average (%.1f%% of 8 TB/s), "
+                 "%.0f GB/s on the median." % (nbytes, nbytes / call_avg / 1e3,
+                                               nbytes / call_avg / 1e3 / HBM_PEAK_GBS * 100,
+                                               nbytes / call_med / 1e3))
+    if not decode:
+        fl = scan_dense_flops(w)
+        lines.append("Dense-tile flops per call (chunk %d): %d -> %.1f TFLOP/s on the average "
+                     "(%.1f%% of 2.5 PFLOP/s)." % (w.chunk, fl, fl / call_avg / 1e6,
+                                                   fl / call_avg / 1e6 / BF16_PEAK_TFLOPS * 100))
+    if durs_all and len(durs_all) <= 64:
+        lines.append("Dispatch durations in launch order (us): %s -- the spread is the device clock "
+                     "settling under sustained load, not the kernel." % [round(x) for x in durs_all])
+    tpath = os.path.join(PROFILE_DIR, "%s_traffic.json" % name)
+    if os.path.exists(tpath):
+        t = json.load(open(tpath))
+        pk = "pmc_decode" if decode else "pmc"
+        lines += ["", "## HBM traffic (FETCH_SIZE / WRITE_SIZE)", "",
+                  "Commands, each pass under `timeout -s KILL 120`:", ""]
+        lines += ["    " + PROFILE_COMMANDS[pk].format(c=c, f=f, n=name)
+                  for c, f in (("FETCH_SIZE", "f"), ("WRITE_SIZE", "w"))]
+        lines += ["    " + PROFILE_COMMANDS["copy"].format(c=c, f=f)
+                  for c, f in (("FETCH_SIZE", "f"), ("WRITE_SIZE", "w"))]
+        lines += ["    python bench.py --traffic-summary %s gpurun_out/prof/f_%s/f_counter_collection.csv "
+                  "gpurun_out/prof/w_%s/w_counter_collection.csv gpurun_out/prof/cf/f_counter_collection.csv "
+                  "gpurun_out/prof/cw/w_counter_collection.csv" % (name, name, name), ""]
+        lines += ["Copy calibration: a 1 GiB device-to-device copy reads FETCH_SIZE x %.4f and WRITE_SIZE x "
+                  "%.4f of its true bytes; both counters are scaled by that." % (1 / t["fetch_scale"],
+                                                                                  1 / t["write_scale"]), ""]
+        lines += ["| per call | bytes |", "|---|---|",
+                  "| fetched (scaled) | %d |" % t["fetch_bytes"], "| written (scaled) | %d |" % t["write_bytes"],
+                  "| total | %d |" % t["bytes_per_launch"], "| algorithmic | %d |" % nbytes,
+                  "| ratio | %.3f |" % (t["bytes_per_launch"] / nbytes), ""]
+        lines.append("Kernel sources hash at measurement: `%s` (bench.py reports traffic only while the "
+                     "sources match)." % t["source_hash"])
+    out = os.path.join(PROFILE_DIR, "%s_%s.md" % (kre, name))
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out)
+
+
 # Device sources each measured kernel is compiled from.
 KERNEL_SOURCES = {
     "scan": ["m3_device.hpp", "m3_scan_kernel.hpp", "m3_scan_inst.hpp", "m3_scan_f32.hip",
@@ -464,12 +561,21 @@ def main(argv=None):
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE csv files into "
                          "profiles/NAME_traffic.json (no GPU needed)")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--trace-summary", nargs=2, metavar=("NAME", "TRACE_CSV"),
+                    help="turn a rocprofv3 kernel-trace csv into profiles/<kernel>_NAME.md "
+                         "(no GPU needed)")
     args = ap.parse_args(argv)
+
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return 0
 
     if args.traffic_summary:
         name = args.traffic_summary[0]
+        # one dispatch per call: the output pass (the first template flag
+        # after the configuration, FULL, is true)
         regex, call = (("decode_kernel", "decode_kernel") if name == "decode"
-                       else ("scan_kernel", "scan_kernel.*Lb1E"))
+                       else ("scan_kernel", "scan_kernelI.*EELb1E"))
         traffic_summary(name, *args.traffic_summary[1:], args.copy_mib, regex, call)
         return 0
 
