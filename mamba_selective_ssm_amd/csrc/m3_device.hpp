@@ -211,6 +211,23 @@ __device__ __forceinline__ float wave_inclusive_sum(float v)
     return v;
 }
 
+// The same for 32-bit integers.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_moved_i(int x)
+{
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ int wave_inclusive_sum_i(int v)
+{
+    v += dpp_moved_i<0x111, 0xf>(v);
+    v += dpp_moved_i<0x112, 0xf>(v);
+    v += dpp_moved_i<0x114, 0xf>(v);
+    v += dpp_moved_i<0x118, 0xf>(v);
+    v += dpp_moved_i<0x142, 0xa>(v);
+    v += dpp_moved_i<0x143, 0xc>(v);
+    return v;
+}
+
 // Sum over aligned groups of G consecutive lanes (4, 8 or 16), every lane of a
 // group receiving its group's sum: a butterfly of DPP lane moves inside each
 // row of 16 lanes (no LDS round trip).

@@ -360,6 +360,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // XCD and its L2.
     const int64_t H = p.H, P = p.P;
     int seg, bh, ps, nseg_u = p.nseg;
+    int pk_lo = 0, pk_len = 0;   // per-sequence slots: the sequence's first token and length
     if (p.nslots == 0) {
         const int per_seg = (p.nbh + 7) / 8 * 8 * p.p_split;
         seg = blockIdx.x / per_seg;
@@ -370,30 +371,48 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     } else {
         // Packed sequences with segments sized per sequence: sequence b has
         // max(1, ceil(chunks_b / seg_chunks)) segments, numbered in sequence
-        // order; a slot of heads x slices per (sequence, segment).  The slot
-        // is found by walking cu_seqlens (wave-uniform scalar loads); slots
-        // past the last sequence's last segment have no work.
+        // order; a slot of heads x slices per (sequence, segment).  Slots
+        // past the last sequence's last segment have no work.  The slot is
+        // found without a walk: lane i loads sequence b0 + i's offsets and
+        // takes its segment count, a prefix sum over the lanes gives each
+        // sequence's first slot, and a ballot picks the sequence whose slots
+        // hold this one (64 sequences per round; one round trip to memory for
+        // up to 64 sequences instead of one per sequence).
         const int per_slot = (int)((H + 7) / 8 * 8) * p.p_split;
         const int slot = blockIdx.x / per_slot;
         const int bid = blockIdx.x % per_slot;
         const int hh = (bid >> 3) / p.p_split * 8 + (bid & 7);
         ps = (bid >> 3) % p.p_split;
         if (hh >= H) return;
-        int64_t first = 0, bsel = -1;
-        for (int64_t bb = 0; bb < p.batch; ++bb) {
-            int64_t lo = p.opt.cu[bb], hi = p.opt.cu[bb + 1];
-            lo = lo < 0 ? 0 : (lo > p.L ? p.L : lo);
-            hi = hi < lo ? lo : (hi > p.L ? p.L : hi);
-            const int64_t len = hi - lo < p.opt.max_len ? hi - lo : p.opt.max_len;
-            const int64_t nch = (len + Q - 1) / Q;
-            int64_t ns = (nch + p.seg_chunks - 1) / p.seg_chunks;
-            ns = ns < 1 ? 1 : ns;
-            if (slot < first + ns) {
-                bsel = bb;
-                nseg_u = (int)ns;
+        int first = 0;
+        int64_t bsel = -1;
+        for (int64_t b0 = 0; b0 < p.batch; b0 += 64) {
+            const int64_t bb = b0 + lane;
+            int ns = 0, lo_i = 0, len_i = 0;
+            if (bb < p.batch) {
+                int64_t lo = p.opt.cu[bb], hi = p.opt.cu[bb + 1];
+                lo = lo < 0 ? 0 : (lo > p.L ? p.L : lo);
+                hi = hi < lo ? lo : (hi > p.L ? p.L : hi);
+                const int64_t len = hi - lo < p.opt.max_len ? hi - lo : p.opt.max_len;
+                const int64_t nch = (len + Q - 1) / Q;
+                const int64_t n = (nch + p.seg_chunks - 1) / p.seg_chunks;
+                ns = n < 1 ? 1 : (int)n;
+                lo_i = (int)lo;       // offsets are int32 on input
+                len_i = (int)len;
+            }
+            const int incl = wave_inclusive_sum_i(ns);
+            const int start = first + incl - ns;            // this lane's sequence: its first slot
+            const unsigned long long hit = __ballot(bb < p.batch && slot >= start && slot < start + ns);
+            if (hit != 0) {
+                const int l = __builtin_ctzll(hit);
+                bsel = b0 + l;
+                first = __builtin_amdgcn_readlane(start, l);
+                nseg_u = __builtin_amdgcn_readlane(ns, l);
+                pk_lo = __builtin_amdgcn_readlane(lo_i, l);
+                pk_len = __builtin_amdgcn_readlane(len_i, l);
                 break;
             }
-            first += ns;
+            first += __builtin_amdgcn_readlane(incl, 63);
         }
         if (bsel < 0) return;
         seg = (int)(slot - first);
@@ -407,7 +426,10 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // dense batch has L = p.L and base = b * p.L; packed sequences take them
     // from cu_seqlens (clamped into the arrays and to max_seqlen).
     int64_t L = p.L, base = b * p.L;
-    if (p.opt.cu != nullptr) {
+    if (p.nslots != 0) {
+        base = pk_lo;
+        L = pk_len;
+    } else if (p.opt.cu != nullptr) {
         int64_t lo = p.opt.cu[b], hi = p.opt.cu[b + 1];
         lo = lo < 0 ? 0 : (lo > p.L ? p.L : lo);
         hi = hi < lo ? lo : (hi > p.L ? p.L : hi);

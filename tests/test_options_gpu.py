@@ -233,6 +233,36 @@ def test_packed_sequences(io, segments, opts):
     np.testing.assert_array_equal(f64(so.x_prev), xr)
 
 
+def test_packed_many_sequences_per_sequence_segments():
+    """100 packed sequences -- 99 short ones (0 to 40 tokens, some empty) and
+    one of 3000 tokens at index 70 -- in the library's segmentation: the long
+    sequence takes many segments, so each workgroup finds its (sequence,
+    segment) among more than 64 sequences (two rounds of the wave-wide
+    search).  Against the oracle per sequence."""
+    g = np.random.default_rng(470)
+    lens = [int(v) for v in g.integers(0, 41, size=100)]
+    lens[70] = 3000
+    lens[3] = 0
+    T = sum(lens)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=DEV)
+    w = workload(1, T, 2, 1, 32, 32, io="bf16", dt_mu=-1.0)
+    say("case packed many: %d sequences, %d tokens" % (len(lens), T))
+    inp = synth.make_scan_inputs(w, 471, DEV)
+    st = random_state(w.with_(batch=len(lens)), 472, DEV)
+    y, so = m3_scan_fwd(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["theta"],
+                        inp["lam"], State(*st), cu_seqlens=cu, max_seqlen=max(lens))
+    torch.cuda.synchronize()
+    yr, hr, br, xr = oracle.scan_packed(f64(inp["x"]), f64(inp["B"]), f64(inp["C"]),
+                                        f64(inp["dt"]), f64(inp["A"]), f64(inp["theta"]),
+                                        f64(inp["lam"]), cu.cpu().numpy(), h0=f64(st[0]),
+                                        Bprev=f64(st[1]), xprev=f64(st[2]))
+    ey, eh = rel_err(f64(y), yr), rel_err(f64(so.h), hr)
+    say("   rel err y %.3e state %.3e" % (ey, eh))
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    np.testing.assert_array_equal(f64(so.B_prev), br)
+    np.testing.assert_array_equal(f64(so.x_prev), xr)
+
+
 def test_packed_equal_lengths_match_dense_batch():
     """Packing equal-length sequences gives the dense batch's results bit for bit."""
     w = workload(3, 257, 4, 1, 64, 64, io="bf16")
