@@ -560,6 +560,12 @@ def main(argv=None):
                     metavar=("NAME", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE csv files into "
                          "profiles/NAME_traffic.json (no GPU needed)")
+    ap.add_argument("--row-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB as 128-byte rows gathered at a 4 KiB stride (the "
+                         "prefill's per-head row reads), for a second counter calibration")
+    ap.add_argument("--calibration-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "MIB"),
+                    help="FETCH_SIZE / WRITE_SIZE scale factors of a --copy-calibration or "
+                         "--row-calibration run of MIB MiB (no GPU needed)")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--trace-summary", nargs=2, metavar=("NAME", "TRACE_CSV"),
                     help="turn a rocprofv3 kernel-trace csv into profiles/<kernel>_NAME.md "
@@ -568,6 +574,21 @@ def main(argv=None):
 
     if args.trace_summary:
         trace_summary(*args.trace_summary)
+        return 0
+
+    if args.calibration_summary:
+        fcsv, wcsv, mib = args.calibration_summary
+        total = int(mib) * (1 << 20)
+        res = {}
+        for tag, path in (("fetch", fcsv), ("write", wcsv)):
+            # the copy dispatches of the run (3 rounds of one large copy, or of
+            # 32 row copies), not the fill that initialises the source
+            rows = [v for _, k, v in _counter_rows(path)
+                    if "copy" in k.lower() and "fill" not in k.lower()]
+            per_round = sum(rows) / 3 * 1024 if rows else 0.0
+            res[tag + "_kib_per_round"] = round(per_round / 1024, 1)
+            res[tag + "_scale"] = round(total / per_round, 4) if per_round else None
+        print(json.dumps(res))
         return 0
 
     if args.traffic_summary:
@@ -591,6 +612,20 @@ def main(argv=None):
     if args.backward_only:
         for k, v in backward_lines(args.steps, torch, m3, synth).items():
             print(json.dumps({"line": k, **v}), flush=True)
+        return 0
+
+    if args.row_calibration:
+        # src [L, 32, 64] bf16: head h's rows are 128 bytes, 4 KiB apart (the
+        # layout of x at 32 heads); each head's rows are copied to a
+        # contiguous destination, so every byte is read and written once.
+        L = args.row_calibration * (1 << 20) // (32 * 64 * 2)
+        src = torch.ones(L, 32, 64, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty(32, L, 64, dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            for h in range(32):
+                dst[h].copy_(src[:, h])
+        torch.cuda.synchronize()
+        print(json.dumps({"row_copy_bytes_each_way": L * 32 * 64 * 2, "launches": 3 * 32}))
         return 0
 
     if args.copy_calibration:
