@@ -238,7 +238,9 @@ __device__ __forceinline__ void load_raw(const BcParams& p, int bh, int c, Raw<C
     using V4 = typename RW::V4;
     constexpr int T = Cf::T, Q = Cf::Q, R = Cf::R, N = Cf::N, P = Cf::P, NPR = Cf::NPR;
     constexpr int VE = Cf::VE, NTHR = Cf::NTHR, VB = RW::VB, VX = RW::VX, G4 = RW::G4;
-    const int64_t L_ = p.L, H = p.H, b = bh / H, h = bh % H;
+    const int64_t L_ = p.L, H = p.H;
+    int64_t b, h;
+    split_bh(bh, H, b, h);
     const int64_t t0 = (int64_t)c * Q;
     auto tok = [&](int64_t t) -> int64_t { return (b * L_ + t) * H + h; };
     const uint4 z = {0u, 0u, 0u, 0u};
@@ -321,7 +323,7 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
     constexpr int LDN = Cf::LDN, LDP = Cf::LDP, LDH = Cf::LDH, VE = Cf::VE, TS = Cf::TS;
     constexpr int NTHR = Cf::NTHR, NW = Cf::NW, VB = RW::VB, VX = RW::VX, G4 = RW::G4;
     const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t H = p.H, h = bh % H;
+    const int64_t H = p.H, h = (int)bh % (int)H;
     op_t* sBb = reinterpret_cast<op_t*>(lds + L::oBb);
     op_t* sCb = reinterpret_cast<op_t*>(lds + L::oCb);
     op_t* sX = reinterpret_cast<op_t*>(lds + L::oX);
@@ -581,7 +583,9 @@ __global__ __launch_bounds__(256) void bc_scan_kernel(const BcParams p)
             g1 = *reinterpret_cast<const float2*>(p.h_in + bh * NP + o1);
         }
         if (p.Bp_in != nullptr && p.L > 0) {
-            const int64_t b = bh / p.H, h = bh % p.H, k0 = (b * p.L) * p.H + h;
+            int64_t b, h;
+            split_bh(bh, p.H, b, h);
+            const int64_t k0 = (b * p.L) * p.H + h;
             const float bhat = (1.f - p.lam[k0]) * p.dt[k0];
             const IO* Bp = reinterpret_cast<const IO*>(p.Bp_in) + (size_t)bh * R * N;
             const IO* xp = reinterpret_cast<const IO*>(p.xp_in) + (size_t)bh * R * P;
@@ -693,7 +697,8 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
     const int tid = tid_v, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), rt = wv & 3, hf = wv >> 2;
     const int bh = unit / p.nc, c = unit % p.nc;
-    const int64_t b = bh / H, h = bh % H;
+    int64_t b, h;
+    split_bh(bh, H, b, h);
     const int64_t t0 = (int64_t)c * Q;
     auto tok = [&](int64_t t) -> int64_t { return (b * L_ + t) * H + h; };
     Held<Cf> hd;
@@ -1094,7 +1099,9 @@ template <typename IO, typename ST>
 __global__ __launch_bounds__(256) void bc_final_kernel(const BcParams p)
 {
     const int bh = blockIdx.x, tid = threadIdx.x;
-    const int64_t H = p.H, b = bh / H, h = bh % H;
+    const int64_t H = p.H;
+    int64_t b, h;
+    split_bh(bh, H, b, h);
     const int N = p.N, P = p.P, R = p.R, nc = p.nc, Q = 64 / R;
     auto tok = [&](int64_t t) -> int64_t { return (b * p.L + t) * H + h; };
     __shared__ float red[256];

@@ -110,9 +110,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_kernel(const DecodePara
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t bh = (int64_t)blockIdx.x * (blockDim.x >> 6) + wv;
     if (bh >= p.nbh) return;   // whole wavefront
-    const int64_t h = bh % p.H;
+    int64_t bb, h;
+    split_bh(bh, p.H, bb, h);   // (batch x heads <= 2^30, checked on the host)
     const int64_t G = p.opt.groups;
-    const int64_t bg = (bh / p.H) * G + h / (p.H / G);   // B/C row of this head's group
+    const int64_t bg = bb * G + (int)h / ((int)p.H / (int)G);   // B/C row of this head's group
 
     float* sBp = dsm + (int64_t)wv * (3 * R * N + 2 * N);   // this wave's slice: [N][R]
     float* sB = sBp + R * N;                            // [N][R]

@@ -211,6 +211,16 @@ __device__ __forceinline__ float wave_inclusive_sum(float v)
     return v;
 }
 
+// (b, h) of a flattened (batch, head) index in 32-bit arithmetic: the callers
+// keep batch x heads below 2^31, and a 64-bit division is a long software
+// sequence at the start of every wave that needs it.
+__device__ __forceinline__ void split_bh(int64_t bh, int64_t H, int64_t& b, int64_t& h)
+{
+    const int q = (int)bh / (int)H;
+    b = q;
+    h = (int)bh - q * (int)H;
+}
+
 // The same for 32-bit integers.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ int dpp_moved_i(int x)

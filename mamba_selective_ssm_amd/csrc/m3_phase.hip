@@ -21,7 +21,8 @@ __global__ __launch_bounds__(64) void phase_block_kernel(const PhaseParams p)
 {
     const int64_t bh = blockIdx.x;            // row * H + head
     const int64_t blk = blockIdx.y;
-    const int64_t b = bh / p.H, h = bh % p.H;
+    int64_t b, h;
+    split_bh(bh, p.H, b, h);
     const int NPR = p.NPR;
     // this row's tokens: a dense batch row, or a packed sequence
     int64_t L = p.L, base = b * p.L;

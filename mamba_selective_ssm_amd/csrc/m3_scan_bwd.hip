@@ -91,7 +91,8 @@ __global__ __launch_bounds__(256) void bwd_kernel(const BwdParams p)
     constexpr int PP = 16 * KP;                   // pairs of one part
     const int part = blockIdx.x % p.parts;
     const int bh = blockIdx.x / p.parts;
-    const int64_t b = bh / H, h = bh % H;
+    int64_t b, h;
+    split_bh(bh, H, b, h);
     const int p_lo = part * PP;                   // first pair of this part
     const int NPRp = NPR - p_lo < PP ? NPR - p_lo : PP;
     const int cg = lane & 3, rg = lane >> 2;
@@ -593,7 +594,9 @@ template <int R>
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdParams p)
 {
     const int bh = blockIdx.x, tid = threadIdx.x;
-    const int64_t H = p.H, L = p.L, b = bh / H, h = bh % H;
+    const int64_t H = p.H, L = p.L;
+    int64_t b, h;
+    split_bh(bh, H, b, h);
     const int P = p.P, S = p.parts;
     const int64_t RP4 = (int64_t)R * P / 4;
     for (int64_t idx = tid; idx < L * RP4; idx += 256) {

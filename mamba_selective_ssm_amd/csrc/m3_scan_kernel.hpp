@@ -420,7 +420,11 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     }
     // a state pass has no work in a sequence's last segment
     if (!FULL && seg == nseg_u - 1) return;
-    const int64_t b = bh / H, h = bh % H;
+    // 32-bit division: batch x heads < 2^28 (checked on the host); a 64-bit
+    // one is a long software sequence ahead of every workgroup's first load
+    const int Hi = (int)H;
+    const int bi = bh / Hi;
+    const int64_t b = bi, h = bh - bi * Hi;
     const int p0 = ps * PS;
     // This unit's sequence: tokens base .. base+L-1 of the token arrays.  A
     // dense batch has L = p.L and base = b * p.L; packed sequences take them
@@ -443,7 +447,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     const bool last_seg = seg == nseg_u - 1;
 
     const int64_t G = p.opt.groups;                 // B/C head groups
-    const int64_t hg = h / (H / G);                  // this head's group
+    const int64_t hg = (int)h / (Hi / (int)G);       // this head's group
     const int sDT = (int)H, sTH = (int)(H * NPR), sBN = (int)(G * R * N), sXP = (int)(H * R * P);
     const int64_t tok0 = (base + c_begin * Q) * H + h;
     const int64_t tok0g = (base + c_begin * Q) * G + hg;   // B, C rows
@@ -1587,7 +1591,21 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     if (!is_math) {
         // prologue: chunk c_begin into buffer 0, chunk c_begin+1's loads out
         if (c_begin < c_end) {
-            issue_loads(c_begin);
+            if constexpr (CL) {
+                // Every workgroup starts at once, so the first chunk's loads
+                // arrive as one burst across the chip.  The angle and decay
+                // inputs go first and alone (a fifth of the bytes); the rows
+                // of X, B and C are issued once they have arrived, so that the
+                // angle prefix and A0 run while the larger burst is in flight.
+                issue_part(c_begin, ld_th{});
+                issue_part(c_begin, ld_a0{});
+                __builtin_amdgcn_s_waitcnt(0);
+                issue_part(c_begin, ld_x{});
+                issue_part(c_begin, ld_bc{});
+                advance();
+            } else {
+                issue_loads(c_begin);
+            }
             prep(c_begin, 0, EARLY && c_begin + 1 < c_end);
             if (!EARLY && !SBUF && c_begin + 1 < c_end) issue_loads(c_begin + 1);
             flush(c_begin, c_begin + 1 < c_end);
