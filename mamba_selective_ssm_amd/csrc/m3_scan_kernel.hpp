@@ -107,6 +107,10 @@ struct ScanCfg {
     using op_t = IO;
     static constexpr int N = N_, PS = PS_, R = R_, Q = Q_, NWM = NWM_, NWP = NWP_, OCC = OCC_;
     static constexpr int NBUF = NBUF_;
+    // raised issue priority for the younger half of the prep waves (the
+    // dstate-128, rank-1 variant with two chunk buffers, where it was measured
+    // to help)
+    static constexpr bool YOUNG_PRIO = NWP_ == 8 && R_ == 1 && N_ == 128 && NBUF_ == 2;
     static constexpr int NW = NWM + NWP;
     static constexpr int NT = 64 * NW;
     static constexpr int NP = N < 32 ? 32 : N;      // state rows padded to the K block
@@ -1611,7 +1615,16 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             flush(c_begin, c_begin + 1 < c_end);
         }
         __syncthreads();
+        // With 8 prep waves and one matrix-core wave per SIMD, the youngest
+        // prep waves lose instruction issue to the older waves of the
+        // workgroup and become the critical path (a per-wave timeline of the
+        // long prefill: their rotation and load issue run 30-50% longer and
+        // they reach the chunk barrier last); a raised priority for them
+        // balances the prep side: long prefill 754 -> 730 us.  (At rank 4 the
+        // matrix-core waves are as loaded and it costs 1%; with the pre-mixer
+        // at dstate 64, 3%.)
         __builtin_amdgcn_s_setprio(0);
+        if (Cf::YOUNG_PRIO && pw >= NWP / 2) __builtin_amdgcn_s_setprio(1);
         for (int64_t c = c_begin; c < c_end; ++c) {
             const int s = (int)((c - c_begin) & 1);
             if (c + 1 < c_end) {
