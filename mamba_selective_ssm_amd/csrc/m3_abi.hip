@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "m3_internal.hpp"
@@ -416,6 +417,23 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
+
+// Compute units of the current device (cached per device; 256 when unknown):
+// on a launch with two workgroups per CU, the second workgroup of each CU has
+// an id from here on.
+int cu_count()
+{
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 // Device address of the scratch array on the current device, which must be
 // the device of `stream` (NULL: the current device's default stream).
@@ -856,6 +874,7 @@ m3_status scan_launch(const m3_scan_args* a, const ScanPlan& plan, const m3::Opt
     p.nseg = plan.nseg;
     p.seg_chunks = plan.seg_chunks;
     p.nslots = plan.nslots;
+    p.young_from = cu_count();
     const hipError_t e1 = plan.v->fn(p, static_cast<hipStream_t>(stream));
     if (e1 != hipSuccess || a->opt.phase_out == nullptr) return hip_status(e1);
     m3::PhaseParams q;

@@ -94,6 +94,8 @@ struct ScanParams {
     int seg_chunks;     // chunks per segment
     int nslots;         // packed sequences, per-sequence segments: (sequence, segment) slots
                         // launched (an upper bound); 0: nseg segments of every sequence
+    int young_from;     // compute units of the device: with two workgroups per CU, the ids
+                        // from here on are the second workgroup on their CU
 };
 
 // NBUF_ = 2: two chunk buffers in LDS (the prep waves fill one while the
@@ -1584,6 +1586,13 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         }
     };
 
+    // Two workgroups per CU: the instruction arbiter favours the older
+    // workgroup's waves, so the younger one (dispatched in the second round)
+    // finishes 15-18% later and sets the pass's time (a per-wave timeline of
+    // prefill_bf16).  In the output pass its waves take a raised priority
+    // (prefill_bf16 37.8 -> 36.9 us; in the state pass it did not help).
+    const bool young_wg = FULL && Cf::OCC == 2 && (int)blockIdx.x >= p.young_from;
+
     // ========================= schedule =====================================
     // Each role runs its own loop with the same number of barriers: one after
     // the prologue and one per chunk.  (The role test is a scalar branch, so a
@@ -1625,6 +1634,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         // at dstate 64, 3%.)
         __builtin_amdgcn_s_setprio(0);
         if (Cf::YOUNG_PRIO && pw >= NWP / 2) __builtin_amdgcn_s_setprio(1);
+        if (young_wg) __builtin_amdgcn_s_setprio(1);
         for (int64_t c = c_begin; c < c_end; ++c) {
             const int s = (int)((c - c_begin) & 1);
             if (c + 1 < c_end) {
@@ -1663,6 +1673,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         if constexpr (FULL) stage_state(0);
         __syncthreads();
         __builtin_amdgcn_s_setprio(0);
+        if (young_wg) __builtin_amdgcn_s_setprio(1);
         for (int64_t c = c_begin; c < c_end; ++c) {
             const int s = (int)((c - c_begin) & 1);
             if constexpr (FULL) {
