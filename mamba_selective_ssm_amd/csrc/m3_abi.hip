@@ -174,6 +174,8 @@ m3_status plan_scan(const m3_scan_args* a, ScanPlan* out)
     if ((int64_t)v->Q * H * wide >= ((int64_t)1 << 31)) return M3_ERR_UNSUPPORTED;
     if (H * wide * 4 >= ((int64_t)1 << 24)) return M3_ERR_UNSUPPORTED;
     const int p_split = (int)(P / v->PS);
+    // the launch grid's x dimension, (b, h, slice) slots, counts work items in 32 bits
+    if (((nbh + 7) / 8 * 8 + 8) * p_split * (int64_t)v->NW * 64 >= ((int64_t)1 << 32)) return M3_ERR_UNSUPPORTED;
     // packed sequences: the launch is sized for the longest one
     const int64_t Lrun = a->opt.cu_seqlens != nullptr ? (a->opt.max_seqlen >= 0 ? a->opt.max_seqlen : 0) : L;
     const int64_t nchunks = (Lrun + v->Q - 1) / v->Q;

@@ -360,19 +360,26 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     const int l16 = lane & 15, g = lane >> 4;
     const bool is_math = wv < NWM;   // wave-uniform role
 
-    // Workgroup -> (segment, b, h, headdim slice).  Consecutive workgroup ids
-    // go to different XCDs (round robin over 8), so the slices and segments
-    // of one (b, h) are given ids that are multiples of 8 apart: they share an
-    // XCD and its L2.
+    // Workgroup -> (segment, b, h, headdim slice): the grid's y index is the
+    // segment (or packed slot), x the (b, h, slice) (no division by a runtime
+    // value: sixteen waves per CU computing the same scalar set-up share the
+    // CU's scalar unit ahead of their first loads).  Consecutive linear
+    // workgroup ids go to different XCDs (round robin over 8), so the slices
+    // and segments of one (b, h) are given ids that are multiples of 8 apart:
+    // they share an XCD and its L2.
     const int64_t H = p.H, P = p.P;
     int seg, bh, ps, nseg_u = p.nseg;
     int pk_lo = 0, pk_len = 0;   // per-sequence slots: the sequence's first token and length
     if (p.nslots == 0) {
-        const int per_seg = (p.nbh + 7) / 8 * 8 * p.p_split;
-        seg = blockIdx.x / per_seg;
-        const int bid = blockIdx.x % per_seg;
-        bh = (bid >> 3) / p.p_split * 8 + (bid & 7);
-        ps = (bid >> 3) % p.p_split;
+        seg = blockIdx.y;
+        const int bid = blockIdx.x;
+        if (p.p_split == 1) {
+            bh = bid;
+            ps = 0;
+        } else {
+            bh = (bid >> 3) / p.p_split * 8 + (bid & 7);
+            ps = (bid >> 3) % p.p_split;
+        }
         if (bh >= p.nbh) return;
     } else {
         // Packed sequences with segments sized per sequence: sequence b has
@@ -384,9 +391,8 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         // sequence's first slot, and a ballot picks the sequence whose slots
         // hold this one (64 sequences per round; one round trip to memory for
         // up to 64 sequences instead of one per sequence).
-        const int per_slot = (int)((H + 7) / 8 * 8) * p.p_split;
-        const int slot = blockIdx.x / per_slot;
-        const int bid = blockIdx.x % per_slot;
+        const int slot = blockIdx.y;
+        const int bid = blockIdx.x;
         const int hh = (bid >> 3) / p.p_split * 8 + (bid & 7);
         ps = (bid >> 3) % p.p_split;
         if (hh >= H) return;
@@ -1591,7 +1597,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // finishes 15-18% later and sets the pass's time (a per-wave timeline of
     // prefill_bf16).  In the output pass its waves take a raised priority
     // (prefill_bf16 37.8 -> 36.9 us; in the state pass it did not help).
-    const bool young_wg = FULL && Cf::OCC == 2 && (int)blockIdx.x >= p.young_from;
+    const bool young_wg = FULL && Cf::OCC == 2 && (int)(blockIdx.y * gridDim.x + blockIdx.x) >= p.young_from;
 
     // ========================= schedule =====================================
     // Each role runs its own loop with the same number of barriers: one after
@@ -1783,10 +1789,12 @@ hipError_t launch_scan_t(const ScanParams& p, hipStream_t stream)
 {
     const int64_t per_seg = (int64_t)((p.nbh + 7) / 8) * 8 * p.p_split;
     const int64_t per_slot = (p.H + 7) / 8 * 8 * p.p_split;
-    // grid of each pass: segments x (b, h, slice), or (sequence, segment)
-    // slots x (h, slice); a state pass's blocks in a last segment return
-    const int64_t grid_state = p.nslots ? per_slot * p.nslots : per_seg * (p.nseg - 1);
-    const int64_t grid_full = p.nslots ? per_slot * p.nslots : per_seg * p.nseg;
+    // grid of each pass: (b, h, slice) x segments, or (h, slice) x (sequence,
+    // segment) slots; a state pass's blocks in a last segment return
+    const dim3 grid_state(p.nslots ? (unsigned)per_slot : (unsigned)per_seg,
+                          p.nslots ? (unsigned)p.nslots : (unsigned)(p.nseg - 1));
+    const dim3 grid_full(p.nslots ? (unsigned)per_slot : (unsigned)per_seg,
+                         p.nslots ? (unsigned)p.nslots : (unsigned)p.nseg);
     constexpr size_t lds_state = Cf::template Lay<false, PM>::bytes;
     constexpr size_t lds_full = Cf::template Lay<true, PM>::bytes;
     auto* const k_state = &scan_kernel<Cf, false, PM>;
@@ -1796,13 +1804,13 @@ hipError_t launch_scan_t(const ScanParams& p, hipStream_t stream)
     if (p.nseg > 1) {
         e = scan_set_lds_limit<Cf, false, PM>();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_state, dim3((unsigned)grid_state), dim3(Cf::NT), lds_state, stream, p);
+        hipLaunchKernelGGL(k_state, grid_state, dim3(Cf::NT), lds_state, stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     e = scan_set_lds_limit<Cf, true, PM>();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_full, dim3((unsigned)grid_full), dim3(Cf::NT), lds_full, stream, p);
+    hipLaunchKernelGGL(k_full, grid_full, dim3(Cf::NT), lds_full, stream, p);
     return hipGetLastError();
 }
 
