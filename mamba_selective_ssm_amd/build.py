@@ -1,10 +1,13 @@
 """Build libm3scan.so (HIP, gfx950 only) in-tree.
 
-    python -m mamba_selective_ssm_amd.build        # compile every unit, link
+    python -m mamba_selective_ssm_amd.build             # compile every unit, link
+    python -m mamba_selective_ssm_amd.build --timeline  # the instrumented copy
 
 Each .hip unit under csrc/ is compiled by hipcc for --offload-arch=gfx950 in
 parallel into _build/, then linked into mamba_selective_ssm_amd/libm3scan.so.
-Packed fp32 instructions are disabled for all device code.
+Packed fp32 instructions are disabled for all device code.  --timeline builds
+a separate library, libm3scan_timeline.so, whose scan kernels stamp each
+wave's phase boundaries (M3_TIMELINE=1; read by the timeline module).
 """
 from __future__ import annotations
 
@@ -21,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libm3scan.so")
+LIB_TIMELINE = os.path.join(PKG, "libm3scan_timeline.so")
 ARCH = "gfx950"
 
 
@@ -36,33 +40,37 @@ def compile_flags():
             "-Wno-unused-result"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + compile_flags() + ["-c", src, "-o", obj]
+def _compile(src: str, bdir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(bdir, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + compile_flags() + list(extra) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stdout))
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile all units and link libm3scan.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = False, timeline: bool = False) -> str:
+    """Compile all units and link libm3scan.so (timeline: the instrumented
+    libm3scan_timeline.so); returns the library path."""
+    bdir = os.path.join(BUILD, "timeline") if timeline else BUILD
+    lib = LIB_TIMELINE if timeline else LIB
+    extra = ("-DM3_TIMELINE=1",) if timeline else ()
+    os.makedirs(bdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda f: _compile(f, bdir, extra), srcs))
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stdout)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, timeline="--timeline" in sys.argv[1:])
     sys.exit(0)

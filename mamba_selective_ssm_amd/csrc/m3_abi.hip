@@ -13,6 +13,14 @@
 
 namespace {
 
+#if M3_TIMELINE
+// Instrumented builds: the device buffer that scan kernels write their
+// per-wave phase stamps into (set by m3_timeline_buffer; null: no stamps).
+unsigned long long* g_timeline = nullptr;
+int64_t g_timeline_rows = 0;
+#endif
+
+
 thread_local int g_last_hip_error = 0;
 
 struct Range {
@@ -718,6 +726,18 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
 
 int m3_abi_version(void) { return M3_ABI_VERSION; }
 
+#if M3_TIMELINE
+// Instrumented builds only (not part of the ABI): the device buffer of
+// per-wave phase stamps for the following scan calls (rows of kTlSlots
+// 64-bit entries, one per wave of both passes' grids), or NULL.  A call whose
+// waves need more rows than `rows` runs without stamps.
+void m3_timeline_buffer(void* buf, int64_t rows)
+{
+    g_timeline = static_cast<unsigned long long*>(buf);
+    g_timeline_rows = buf != nullptr ? rows : 0;
+}
+#endif
+
 int m3_last_hip_error(void) { return g_last_hip_error; }
 
 const char* m3_status_string(m3_status s)
@@ -877,6 +897,10 @@ m3_status scan_launch(const m3_scan_args* a, const ScanPlan& plan, const m3::Opt
     p.seg_chunks = plan.seg_chunks;
     p.nslots = plan.nslots;
     p.young_from = cu_count();
+#if M3_TIMELINE
+    p.tl = g_timeline;
+    p.tl_rows = g_timeline_rows;
+#endif
     const hipError_t e1 = plan.v->fn(p, static_cast<hipStream_t>(stream));
     if (e1 != hipSuccess || a->opt.phase_out == nullptr) return hip_status(e1);
     m3::PhaseParams q;

@@ -96,6 +96,27 @@ struct ScanParams {
                         // launched (an upper bound); 0: nseg segments of every sequence
     int young_from;     // compute units of the device: with two workgroups per CU, the ids
                         // from here on are the second workgroup on their CU
+    unsigned long long* tl;   // per-wave phase stamps (instrumented builds only), else null
+    int64_t tl_rows;          // rows of kTlSlots entries that tl holds
+};
+
+// Per-wave phase timeline, compiled in only with M3_TIMELINE=1 (a separate,
+// instrumented build of the library): lane 0 of every wave writes, into its
+// own kTlSlots-entry row of p.tl, s_memrealtime, s_memtime and its pass, role,
+// wave, segment and unit at entry, then one 64-bit entry per phase boundary
+// (the event code in the top byte, s_memtime below it), and s_memtime and
+// s_memrealtime again in the row's last two entries at exit.
+// In the product build every stamp compiles to nothing.
+#ifndef M3_TIMELINE
+#define M3_TIMELINE 0
+#endif
+constexpr int kTlSlots = 256;
+enum TlEvent {
+    kTlFirstIssue = 1, kTlFirstArrived = 2, kTlProloguePrep = 3, kTlPrologueBarrier = 4, kTlSetup = 5,
+    kTlPrepStart = 10, kTlAngleScan = 11, kTlDecayScan = 12, kTlXRows = 13, kTlWaitTotals = 14,
+    kTlRotate = 15, kTlBarrier = 16,
+    kTlFold = 20, kTlStage0 = 21, kTlPhaseC = 22, kTlPhaseD = 23, kTlStage = 24,
+    kTlExit = 30
 };
 
 // NBUF_ = 2: two chunk buffers in LDS (the prep waves fill one while the
@@ -345,6 +366,18 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     constexpr int HSTAGE = PS * LDH;   // elements of one state stage
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    // One word of every 64-byte line of the kernel arguments, read at once:
+    // the set-up below reads the arguments in dependent steps, and each line
+    // it touches first would otherwise cost a round trip of its own.
+    {
+        const unsigned* kp = reinterpret_cast<const unsigned*>(&p);
+        constexpr int NLINE = (int)((sizeof(ScanParams) + 63) / 64);
+#pragma unroll
+        for (int i = 0; i < NLINE; ++i) {
+            const unsigned t = kp[16 * i];
+            asm volatile("" ::"s"(t));
+        }
+    }
     op_t* sH = reinterpret_cast<op_t*>(smem + Lay::oH);   // [1 or 2][PS][LDH] G^T
     constexpr bool SBUF = Lay::SB;
     auto buf_B = [&](int s) { return reinterpret_cast<op_t*>(smem + s * Lay::BSTR + Lay::oB); };
@@ -500,6 +533,47 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     float* const sXW = reinterpret_cast<float*>(smem + Lay::oXW);   // CL: [NWP][NPR] angle totals
     int* const sCnt = reinterpret_cast<int*>(smem + Lay::oCNT);
     int pcall = 0;                                                 // prep calls of this wave
+    unsigned long long* tlw = nullptr;   // this wave's timeline row (instrumented builds)
+    int tln = 0;
+    if constexpr (M3_TIMELINE) {
+        if (p.tl != nullptr) {
+            tlw = p.tl + ((size_t)(blockIdx.y * gridDim.x + blockIdx.x) * Cf::NW + wv) * kTlSlots;
+            const unsigned long long rt = __builtin_amdgcn_s_memrealtime();
+            const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+            if (lane == 0) {
+                tlw[0] = rt;
+                tlw[1] = t0;
+                // pass (bit 63: outputs), role (bit 62: matrix-core wave), wave
+                // index (bits 48-55), segment (bits 32-47), unit
+                tlw[2] = ((unsigned long long)FULL << 63) | ((unsigned long long)is_math << 62) |
+                         ((unsigned long long)(unsigned)wv << 48) |
+                         ((unsigned long long)((unsigned)seg & 0xffffu) << 32) | (unsigned)bh;
+            }
+            tln = 3;
+        }
+    }
+    auto stamp = [&](int code) {
+        if constexpr (M3_TIMELINE) {
+            if (tlw != nullptr && tln < kTlSlots - 2) {
+                const unsigned long long t = __builtin_amdgcn_s_memtime();
+                if (lane == 0) tlw[tln] = ((unsigned long long)code << 56) | (t & ((1ull << 56) - 1));
+                ++tln;
+            }
+        }
+    };
+    auto stamp_exit = [&]() {
+        if constexpr (M3_TIMELINE) {
+            if (tlw != nullptr) {
+                const unsigned long long t = __builtin_amdgcn_s_memtime();
+                const unsigned long long rt = __builtin_amdgcn_s_memrealtime();
+                if (lane == 0) {
+                    tlw[kTlSlots - 2] = t;
+                    tlw[kTlSlots - 1] = rt;
+                    if (tln < kTlSlots - 2) tlw[tln] = (unsigned long long)kTlExit << 56;
+                }
+            }
+        }
+    };
     if constexpr (PM && CL) {
         // every gain and bias (a prep lane reads its own pair quad's)
         for (int idx = tid; idx < 2 * (R + 1) * N; idx += NT) {
@@ -526,6 +600,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         if (tid == 0) *sCnt = 0;
         __syncthreads();
     }
+    stamp(kTlSetup);
     double l2seg = 0.0, phiseg[4] = {0.0, 0.0, 0.0, 0.0};   // segment totals (state pass)
     const int phase = p.opt.phase;
     const float dtb_h = (PM && p.opt.dtb != nullptr) ? p.opt.dtb[h] : 0.f;
@@ -696,6 +771,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // than issuing them all at the end).
     auto prep = [&](int64_t c, int s, bool nx) {
         ++pcall;
+        stamp(kTlPrepStart);
         op_t* sB = buf_B(s);
         op_t* sC = buf_C(s);
         op_t* sX = buf_X(s);
@@ -735,6 +811,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             // (one chunk buffer: issued after the rotation, so that these
             // registers are free while the rotated rows are held)
             if (nx && !SBUF) issue_part(c + 1, ld_th{});
+            stamp(kTlAngleScan);
         }
 
         // ---- A0: decay prefix scan and trapezoid weights (one wave) -------
@@ -786,6 +863,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             if constexpr (!FULL) l2seg += (double)l2tot;
         }
         if (CL && nx) issue_part(c + 1, ld_a0{});
+        stamp(kTlDecayScan);
 
         // ---- A2: X slice into LDS ------------------------------------------
         if (BF && jl == Q - 1) {
@@ -819,6 +897,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             }
         }
         if (CL && nx && !SBUF) issue_part(c + 1, ld_x{});
+        stamp(kTlXRows);
 
         // ---- A1: angle prefix per pair quad, rotate B and C ----------------
         if constexpr (CL) {
@@ -834,6 +913,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             // state of this unit come out NaN instead of silently wrong.
             if (!waited) off = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                                      __builtin_nanf("")};
+            stamp(kTlWaitTotals);
             auto rotate_cl = [&](auto fullc) {
                 constexpr bool FULLC = decltype(fullc)::value;
                 // Pre-mixer: each row's RMS scale from the NPR4 lanes that hold it.
@@ -924,6 +1004,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 issue_part(c + 1, ld_bc{});
                 advance();
             }
+            stamp(kTlRotate);
             // The last wave's last lane group holds the chunk's total angle.
             if (pw == NWP - 1) {
                 const f32x4 tot = off + cl_loc[KP - 1];
@@ -1618,7 +1699,9 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 // angle prefix and A0 run while the larger burst is in flight.
                 issue_part(c_begin, ld_th{});
                 issue_part(c_begin, ld_a0{});
+                stamp(kTlFirstIssue);
                 __builtin_amdgcn_s_waitcnt(0);
+                stamp(kTlFirstArrived);
                 issue_part(c_begin, ld_x{});
                 issue_part(c_begin, ld_bc{});
                 advance();
@@ -1628,8 +1711,10 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             prep(c_begin, 0, EARLY && c_begin + 1 < c_end);
             if (!EARLY && !SBUF && c_begin + 1 < c_end) issue_loads(c_begin + 1);
             flush(c_begin, c_begin + 1 < c_end);
+            stamp(kTlProloguePrep);
         }
         __syncthreads();
+        stamp(kTlPrologueBarrier);
         // With 8 prep waves and one matrix-core wave per SIMD, the youngest
         // prep waves lose instruction issue to the older waves of the
         // workgroup and become the critical path (a per-wave timeline of the
@@ -1654,7 +1739,9 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 if (c + 1 < c_end) flush(c + 1, c + 2 < c_end);
             }
             __syncthreads();
+            stamp(kTlBarrier);
         }
+        stamp_exit();
         if constexpr (!FULL) {
             // decay and angle totals of this segment
             float* rec = recs + (int64_t)seg * rec_sz;
@@ -1676,23 +1763,32 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     } else {
         int hs = 0;
         initial_state();
+        stamp(kTlFold);
         if constexpr (FULL) stage_state(0);
+        stamp(kTlStage0);
         __syncthreads();
+        stamp(kTlPrologueBarrier);
         __builtin_amdgcn_s_setprio(0);
         if (young_wg) __builtin_amdgcn_s_setprio(1);
         for (int64_t c = c_begin; c < c_end; ++c) {
             const int s = (int)((c - c_begin) & 1);
             if constexpr (FULL) {
                 phase_C(c, s, sH + hs * HSTAGE);
+                stamp(kTlPhaseC);
                 phase_D(s);
+                stamp(kTlPhaseD);
                 if constexpr (SBUF) __syncthreads();   // the operands may now be overwritten
                 if constexpr (!Cf::SH1) hs ^= 1;
                 stage_state(hs);
+                stamp(kTlStage);
             } else {
                 phase_D(s);
+                stamp(kTlPhaseD);
             }
             __syncthreads();
+            stamp(kTlBarrier);
         }
+        stamp_exit();
         if constexpr (!FULL) {
             // end state of this segment
             float* rec = recs + (int64_t)seg * rec_sz;
@@ -1801,6 +1897,14 @@ hipError_t launch_scan_t(const ScanParams& p, hipStream_t stream)
     auto* const k_full = &scan_kernel<Cf, true, PM>;
     hipError_t e;
     (void)hipGetLastError();
+    // instrumented builds: stamps only when the buffer holds a row for every
+    // wave of both passes
+    const int64_t state_rows = p.nseg > 1 ? (int64_t)grid_state.x * grid_state.y * Cf::NW : 0;
+    if (p.tl != nullptr && state_rows + (int64_t)grid_full.x * grid_full.y * Cf::NW > p.tl_rows) {
+        ScanParams q = p;
+        q.tl = nullptr;
+        return launch_scan_t<Cf, PM>(q, stream);
+    }
     if (p.nseg > 1) {
         e = scan_set_lds_limit<Cf, false, PM>();
         if (e != hipSuccess) return e;
@@ -1810,6 +1914,13 @@ hipError_t launch_scan_t(const ScanParams& p, hipStream_t stream)
     }
     e = scan_set_lds_limit<Cf, true, PM>();
     if (e != hipSuccess) return e;
+    if (p.tl != nullptr && p.nseg > 1) {
+        // instrumented builds: the output pass's rows follow the state pass's
+        ScanParams q = p;
+        q.tl += (size_t)state_rows * kTlSlots;
+        hipLaunchKernelGGL(k_full, grid_full, dim3(Cf::NT), lds_full, stream, q);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_full, grid_full, dim3(Cf::NT), lds_full, stream, p);
     return hipGetLastError();
 }
