@@ -114,7 +114,7 @@ constexpr int kTlSlots = 256;
 enum TlEvent {
     kTlFirstIssue = 1, kTlFirstArrived = 2, kTlProloguePrep = 3, kTlPrologueBarrier = 4, kTlSetup = 5,
     kTlPrepStart = 10, kTlAngleScan = 11, kTlDecayScan = 12, kTlXRows = 13, kTlWaitTotals = 14,
-    kTlRotate = 15, kTlBarrier = 16,
+    kTlRotate = 15, kTlBarrier = 16, kTlAngleIn = 17, kTlAngleScanned = 18,
     kTlFold = 20, kTlStage0 = 21, kTlPhaseC = 22, kTlPhaseD = 23, kTlStage = 24,
     kTlExit = 30
 };
@@ -286,17 +286,50 @@ __device__ __forceinline__ float group_inclusive_sum(float v)
     return v;
 }
 
+// The value of the lane 16 places below (the previous row of 16 lanes; 0 in
+// row 0) and 32 places below (0 in rows 0 and 1), by the row-swapping
+// permutes of gfx950: permlane16_swap(v, v) gives rows (v0, v0, v2, v2) and
+// (v1, v1, v3, v3), permlane32_swap(v, v) gives rows (v0, v1, v0, v1).  Every
+// lane of the wave must be active.
+__device__ __forceinline__ float lanes_up16(float v, int lane)
+{
+    const unsigned u = __float_as_uint(v);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const auto q = __builtin_amdgcn_permlane32_swap(p[1], p[1], false, false);
+    const int row = lane >> 4;
+    return row == 0 ? 0.f : __uint_as_float(row == 2 ? q[0] : p[0]);
+}
+__device__ __forceinline__ float lanes_up32(float v, int lane)
+{
+    const unsigned u = __float_as_uint(v);
+    const auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return lane < 32 ? 0.f : __uint_as_float(q[0]);
+}
 // Inclusive prefix sum over lanes l, l - S, l - 2S, ... (M lane groups of S
-// lanes: lanes with equal l % S form one sequence, ordered by l / S).
-template <int S, int M>
+// lanes: lanes with equal l % S form one sequence, ordered by l / S), as a
+// Hillis-Steele scan with lane shifts S, 2S, 4S, ...  With whole rows as the
+// groups (S = 16: dstate 128) the shifts run on the row permutes above (long
+// prefill 732 -> 712 us); otherwise through LDS (ds_bpermute), which measured
+// faster there than the permutes (dstate 64: 36.6 against 37.5 us per call
+// with them for the 16- and 32-lane shifts, 36.5 with DPP row shifts and
+// rotations for the 8-lane one as well).
+template <int S, int M, int D = 1>
 __device__ __forceinline__ float strided_inclusive_sum(float v, int lane)
 {
-#pragma unroll
-    for (int d = 1; d < M; d <<= 1) {
-        const float u = __shfl_up(v, (unsigned)(d * S), 64);
-        v += lane >= d * S ? u : 0.f;
+    constexpr int SH = D * S;
+    if constexpr (D >= M) {
+        return v;
+    } else {
+        if constexpr (S == 16 && SH == 16) {
+            v += lanes_up16(v, lane);
+        } else if constexpr (S == 16 && SH == 32) {
+            v += lanes_up32(v, lane);
+        } else {
+            const float u = __shfl_up(v, (unsigned)SH, 64);
+            v += lane >= SH ? u : 0.f;
+        }
+        return strided_inclusive_sum<S, M, 2 * D>(v, lane);
     }
-    return v;
 }
 
 // Wait until the workgroup-shared counter *cnt reaches target (the other
@@ -800,9 +833,13 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 for (int e = 0; e < 4; ++e) run[e] += ok ? dv * st.thv[k][e] : 0.f;
                 cl_loc[k] = run;
             }
+            if constexpr (M3_TIMELINE) asm volatile("" ::"v"(run[0]));   // (the stamp after the data)
+            stamp(kTlAngleIn);
             f32x4 inc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) inc[e] = strided_inclusive_sum<NPR4, MQ>(run[e], lane);
+            if constexpr (M3_TIMELINE) asm volatile("" ::"v"(inc[0]));
+            stamp(kTlAngleScanned);
             const f32x4 ex = inc - run;
 #pragma unroll
             for (int k = 0; k < KP; ++k) cl_loc[k] += ex;   // (cl_loc[KP-1] is now inc)

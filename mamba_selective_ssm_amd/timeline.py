@@ -28,12 +28,13 @@ SLOTS = 256            # 64-bit entries per wave (kTlSlots in the kernel)
 REALTIME_MHZ = 100.0   # s_memrealtime's constant clock
 
 EV = {5: "set-up done (workgroup barrier passed)", 1: "first loads issued", 2: "first angle/decay inputs in", 3: "first chunk prepared",
-      4: "prologue barrier passed", 10: "prep start", 11: "angle scan + publish",
+      4: "prologue barrier passed", 10: "prep start", 11: "angle totals published",
       12: "decay scan (A0)", 13: "X rows", 14: "wait for the other waves' totals",
       15: "rotation of B, C + next loads", 16: "chunk barrier", 20: "record fold / initial state",
+      17: "angle inputs in hand (the wait for this chunk's loads)", 18: "angle scan across the wave's lanes",
       21: "state staged", 22: "phase C (outputs)", 23: "phase D (state update)",
       24: "state staged for the next chunk", 30: "exit"}
-PREP_STEPS = [(10, 11), (11, 12), (12, 13), (13, 14), (14, 15), (15, 16)]
+PREP_STEPS = [(10, 17), (17, 18), (18, 11), (11, 12), (12, 13), (13, 14), (14, 15), (15, 16)]
 MATH_STEPS = [(16, 22), (22, 23), (23, 24), (24, 16)]      # output pass
 MATH_STEPS_STATE = [(16, 23), (23, 16)]                    # state pass: no outputs
 
