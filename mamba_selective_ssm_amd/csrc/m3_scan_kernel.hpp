@@ -678,6 +678,10 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     // lane's rows; LD_BC: B and C); `advance` then moves the pointers to the
     // next chunk.
     constexpr int LD_A0 = 1, LD_X = 2, LD_TH = 4, LD_BC = 8;
+    // State pass, bf16 row-coalesced prep: the matrix-core waves, which have
+    // only the state update to do there, load and store the X rows
+    // themselves (off the prep waves' critical path).
+    constexpr bool MX = !FULL && BF && CL && !SBUF;
     auto issue_part = [&](int64_t c, auto partc) {
         constexpr int part = decltype(partc)::value;
         const int64_t t0 = c * Q;
@@ -698,7 +702,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 st.a_ln[kk] = *at(llam, __umul24(jnc, bDT));
             }
         }
-        if constexpr ((part & LD_X) != 0) {
+        if constexpr ((part & LD_X) != 0 && !MX) {
 #pragma unroll
             for (int k = 0; k < XI; ++k) {
                 int it = ptid + k * 64 * NWP;
@@ -903,7 +907,9 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         stamp(kTlDecayScan);
 
         // ---- A2: X slice into LDS ------------------------------------------
-        if (BF && jl == Q - 1) {
+        if constexpr (MX) {
+            // (the matrix-core waves stage X in this pass)
+        } else if (BF && jl == Q - 1) {
             // full chunk: the raw bf16 rows go to LDS as loaded
 #pragma unroll
             for (int k = 0; k < XI; ++k) {
@@ -913,7 +919,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 xmap(it, rho, cg);
                 if constexpr (!SBUF) st.xq[k].store_raw(sX + rho * LDXR + 8 * cg);
             }
-        } else
+        } else {
 #pragma unroll
         for (int k = 0; k < XI; ++k) {
             int it = ptid + k * 64 * NWP;
@@ -932,6 +938,7 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sX[(8 * cg + e) * LDX + rho] = v[e];
             }
+        }
         }
         if (CL && nx && !SBUF) issue_part(c + 1, ld_x{});
         stamp(kTlXRows);
@@ -1274,6 +1281,53 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                     lX += Q * sXP;
                 } else {
                     issue_loads(c + 1);
+                }
+            }
+        }
+    };
+
+    // State pass (MX): the X rows of chunk c, loaded by the matrix-core waves
+    // into registers a chunk ahead and stored into a chunk buffer (rows past
+    // the sequence zeroed), with the same item map as the prep waves' A2.
+    constexpr int XIM = (XITEMS + 64 * NWM - 1) / (64 * NWM);
+    IoRow8<io_t> xm[MX ? XIM : 1];
+    const io_t* __restrict__ const lX0 = lX;
+    auto x_issue = [&](int64_t c) {
+        if constexpr (MX) {
+            const int64_t t0 = c * Q;
+            const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
+            const io_t* xb = lX0 + (c - c_begin) * Q * sXP;
+#pragma unroll
+            for (int k = 0; k < XIM; ++k) {
+                int it = tid + k * 64 * NWM;
+                if (XITEMS % (64 * NWM) != 0 && it >= XITEMS) it = XITEMS - 1;   // identical duplicate
+                int rho, cg;
+                xmap(it, rho, cg);
+                const unsigned j = (unsigned)(rho / R < jl ? rho / R : jl);
+                const unsigned lo = (unsigned)sizeof(io_t) * ((unsigned)(rho % R) * (unsigned)P + 8u * (unsigned)cg);
+                xm[k].load(at(xb, __umul24(j, bXP) + lo));
+            }
+        }
+    };
+    auto x_store = [&](int64_t c, int s) {
+        if constexpr (MX) {
+            const int64_t t0 = c * Q;
+            const int jl = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
+            op_t* sX = buf_X(s);
+#pragma unroll
+            for (int k = 0; k < XIM; ++k) {
+                int it = tid + k * 64 * NWM;
+                if (XITEMS % (64 * NWM) != 0 && it >= XITEMS) it = XITEMS - 1;
+                int rho, cg;
+                xmap(it, rho, cg);
+                if (jl == Q - 1) {
+                    xm[k].store_raw(sX + rho * LDXR + 8 * cg);
+                } else {
+                    const bool ok = rho / R <= jl;
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = ok ? xm[k].get(e) : 0.f;
+                    lds_store8(sX + rho * LDXR + 8 * cg, v);
                 }
             }
         }
@@ -1799,7 +1853,12 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
         }
     } else {
         int hs = 0;
+        if (MX && c_begin < c_end) x_issue(c_begin);
         initial_state();
+        if (MX && c_begin < c_end) {
+            x_store(c_begin, 0);
+            if (c_begin + 1 < c_end) x_issue(c_begin + 1);
+        }
         stamp(kTlFold);
         if constexpr (FULL) stage_state(0);
         stamp(kTlStage0);
@@ -1821,6 +1880,12 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
             } else {
                 phase_D(s);
                 stamp(kTlPhaseD);
+                if (MX && c + 1 < c_end) {
+                    // chunk c+1's X rows into the other buffer (last read by
+                    // phase D of chunk c-1, before the previous barrier)
+                    x_store(c + 1, s ^ 1);
+                    if (c + 2 < c_end) x_issue(c + 2);
+                }
             }
             __syncthreads();
             stamp(kTlBarrier);
