@@ -134,6 +134,26 @@ def summarize(waves, name):
                                                               statistics.mean(ds), len(ds)))
             out.append("| sum of means | | %.2f | |" % tot)
             out.append("")
+            # by wave index: the barrier wait and the work before it, per chunk
+            per = {}
+            for w in rw:
+                ev = w["ev"]
+                k0 = next((i for i, (c, _) in enumerate(ev) if c == 4), None)
+                if k0 is None:
+                    continue
+                marks = [t for (c, t) in ev[k0:] if c in (4, 16)]
+                last = [t for (c, t) in ev[k0:] if c == (15 if not math else (24 if full else 23))]
+                d = per.setdefault(w["wv"], [[], []])
+                for i in range(len(marks) - 1):
+                    ends = [t for t in last if marks[i] < t < marks[i + 1]]
+                    if ends:
+                        d[0].append((ends[-1] - marks[i]) / tpu)
+                        d[1].append((marks[i + 1] - ends[-1]) / tpu)
+            if per:
+                out.append("by wave index: work before the chunk barrier / wait at it (mean us per chunk): " +
+                           ", ".join("w%d %.2f/%.2f" % (k, statistics.mean(v[0]), statistics.mean(v[1]))
+                                     for k, v in sorted(per.items()) if v[0]))
+                out.append("")
     return "\n".join(out)
 
 
