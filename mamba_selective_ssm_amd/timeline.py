@@ -162,6 +162,7 @@ def main(argv=None):
     ap.add_argument("--workload", default="prefill_bf16")
     ap.add_argument("--calls", type=int, default=20)
     ap.add_argument("--seed", type=int, default=7)
+    ap.add_argument("--premix", action="store_true", help="with the fused pre-mixer")
     args = ap.parse_args(argv)
 
     import torch
@@ -175,11 +176,17 @@ def main(argv=None):
     lib.m3_timeline_buffer.argtypes = [ctypes.c_void_p, ctypes.c_int64]
 
     w = synth.WORKLOADS[args.workload]
-    inp = synth.make_scan_inputs(w, args.seed, "cuda")
     keys = ("x", "B", "C", "dt", "A", "theta", "lam")
+    pm = None
+    if args.premix:
+        inp, ex = synth.make_option_inputs(w, args.seed, "cuda", premix=True)
+        q = ex["premix"]
+        pm = binding.Premix(q["B_norm_w"], q["C_norm_w"], q["B_bias"], q["C_bias"], q["dt_bias"], q["eps"])
+    else:
+        inp = synth.make_scan_inputs(w, args.seed, "cuda")
     nrows = 32768                       # waves of both passes (a call needing more is not stamped)
     buf = torch.zeros(nrows * SLOTS, dtype=torch.int64, device="cuda")
-    call = binding.ScanCall(*[inp[k] for k in keys], chunk=w.chunk)
+    call = binding.ScanCall(*[inp[k] for k in keys], chunk=w.chunk, premix=pm)
     lib.m3_timeline_buffer(ctypes.c_void_p(buf.data_ptr()), nrows)
     for _ in range(args.calls - 1):
         call()
@@ -192,7 +199,7 @@ def main(argv=None):
     rows = buf.view(nrows, SLOTS).cpu().tolist()
     mask = (1 << 64) - 1
     rows = [[v & mask for v in r] for r in rows]
-    print(summarize(parse(rows), w.name))
+    print(summarize(parse(rows), w.name + (" with the pre-mixer" if pm is not None else "")))
     return 0
 
 
