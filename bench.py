@@ -242,7 +242,7 @@ def trace_summary(name, trace_csv):
 
 # Device sources each measured kernel is compiled from.
 KERNEL_SOURCES = {
-    "scan": ["m3_device.hpp", "m3_scan_kernel.hpp", "m3_scan_inst.hpp", "m3_scan_f32.hip",
+    "scan": ["m3_device.hpp", "m3_timeline.hpp", "m3_scan_kernel.hpp", "m3_scan_inst.hpp", "m3_scan_f32.hip",
              "m3_scan_bf16_a.hip", "m3_scan_bf16_b.hip"],
     "decode": ["m3_device.hpp", "m3_decode.hip"],
 }

@@ -677,6 +677,10 @@ m3_status m3_scan_bwd(const m3_scan_bwd_args* a, void* stream)
         q.L = Lc; q.H = H; q.N = (int)N; q.P = (int)P; q.R = (int)R;
         q.nbh = (int)nbh;
         q.nc = (int)plan.nc;
+#if M3_TIMELINE
+        q.tl = g_timeline;
+        q.tl_rows = g_timeline_rows;
+#endif
         err = m3::launch_bwd_chunked(q, a->io_dtype, st);
     } else {
         m3::BwdParams p;

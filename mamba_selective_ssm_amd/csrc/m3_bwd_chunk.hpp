@@ -45,6 +45,7 @@
 
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
+#include "m3_timeline.hpp"
 
 namespace m3 {
 namespace bc {
@@ -687,8 +688,12 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
     // Persistent: this workgroup takes units blockIdx.x, + gridDim.x, ...,
     // loading the next one's inputs while it works on the current one.
     Raw<Cf> rw;
+    TlRow tlr;   // per-wave phase stamps (instrumented builds)
+    tlr.open(p.tl, (size_t)blockIdx.x * NW + (threadIdx.x >> 6), threadIdx.x & 63,
+             kTlBackward | ((unsigned long long)(threadIdx.x >> 6) << 48) | blockIdx.x);
     if ((int)blockIdx.x < nunits) load_raw<Cf, true>(p, blockIdx.x / p.nc, blockIdx.x % p.nc, rw, threadIdx.x);
     for (int unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
+    tlr.stamp(kTlUnit, threadIdx.x & 63);
     // The lane's indices are made opaque per unit, so that the compiler
     // recomputes the (cheap) LDS addresses inside the loop instead of keeping
     // them all live across it.
@@ -721,6 +726,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
     float* sDPhi = reinterpret_cast<float*>(lds + L::oDPhi);
     float* sT = reinterpret_cast<float*>(lds + L::oTok);
     __syncthreads();
+    tlr.stamp(kTlStaged, lane);
 
     const int r0w = 16 * rt;                      // this wave's operand rows
     // ---- phase 1: S = Cbar Bbar^T, dSc = dY X^T on key tiles kt = hf (mod NS) --
@@ -796,6 +802,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
         }
     }
     __syncthreads();
+    tlr.stamp(kTlScores, lane);
     if (more) load_raw<Cf, true, LR_BC>(p, un / p.nc, un % p.nc, rw, tid);
 
     // ---- phase 2a: dX = (S o M)^T dY + diag(d) Bbar dGbar^T ------------------
@@ -836,6 +843,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
         }
     }
     __syncthreads();                              // the S o M tile is free
+    tlr.stamp(kTlGradX, lane);
     if (more) load_raw<Cf, true, LR_XT>(p, un / p.nc, un % p.nc, rw, tid);
     put_gin<Cf>(sGi, hd, tid);
 
@@ -906,6 +914,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
             }
         }
         __syncthreads();                          // X is free (angle gradients); G_in is staged
+        tlr.stamp(kTlGradB, lane);
         // dd_k = <Bbar_k, Zb_k> per row over this half's columns, and per pair
         // the sum over this wave's rows of d_k (Zb_0 Bbar_1 - Zb_1 Bbar_0)
         // (the state term's share of the angle gradient)
@@ -942,6 +951,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
             if (l16 == 0) sT[(kDD + hf) * TS + r0w + 4 * g + i] = sm;
         }
         back_rotate(ab, sBb, p.dB, false);
+        tlr.stamp(kTlGradBStored, lane);
     }
 
     // ---- phase 2c: dCbar = dS Bbar + diag(e^Lam) Zc, Zc = dY G_in^T -----------
@@ -970,6 +980,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
                 mma(a, bb, zc[u]);
             }
         }
+        tlr.stamp(kTlGradCProducts, lane);
         float ep[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -991,6 +1002,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
     }
     __syncthreads();
 
+    tlr.stamp(kTlGradC, lane);
     // ---- phase 3a: dphi = suffix sums of dPhi over the chunk's tokens ---------
     for (int i = wv; i < NPR; i += NW) {
         float v = 0.f;
@@ -1006,6 +1018,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
     }
     __syncthreads();
 
+    tlr.stamp(kTlAngleSuffix, lane);
     // ---- phase 3b: dtheta = dt dphi; sum_i theta_i dphi_i per token ------------
     {
         constexpr int G4 = NPR / 4;               // lanes per token (4, 8 or 16)
@@ -1035,6 +1048,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
     }
     __syncthreads();
 
+    tlr.stamp(kTlGradTheta, lane);
     // ---- phase 3c: decay and weight gradients per token (wave 0) --------------
     if (wv == 0) {
         const int t = lane;
@@ -1088,7 +1102,9 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
         if (lane == Q - 1) p.dw_last[(size_t)bh * p.nc + c] = dw;
     }
     __syncthreads();                              // LDS is reused by the next unit
+    tlr.stamp(kTlGradDecay, lane);
     }
+    tlr.close(threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------------------
@@ -1211,7 +1227,14 @@ hipError_t launch_cfg(const BcParams& p, hipStream_t stream)
             ncu = 256;
         (void)hipGetLastError();
         const unsigned ngrid = nunits < (unsigned)(occ * ncu) ? nunits : (unsigned)(occ * ncu);
-        hipLaunchKernelGGL(k3, dim3(ngrid), dim3(Cf::NTHR), grad_lds<Cf>(), stream, p);
+        if (p.tl != nullptr && (int64_t)ngrid * Cf::NW > p.tl_rows) {
+            // instrumented builds: no stamps unless every wave has a row
+            BcParams q = p;
+            q.tl = nullptr;
+            hipLaunchKernelGGL(k3, dim3(ngrid), dim3(Cf::NTHR), grad_lds<Cf>(), stream, q);
+        } else {
+            hipLaunchKernelGGL(k3, dim3(ngrid), dim3(Cf::NTHR), grad_lds<Cf>(), stream, p);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

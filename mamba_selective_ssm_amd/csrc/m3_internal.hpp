@@ -90,6 +90,8 @@ struct BcParams {
     int64_t L, H;
     int N, P, R;
     int nbh, nc;      // (b, h) units; chunks per unit
+    unsigned long long* tl;   // per-wave phase stamps (instrumented builds only), else null
+    int64_t tl_rows;          // rows that tl holds
 };
 
 bool bwd_chunked_supported(int64_t N, int64_t P, int64_t R, int io_dtype);

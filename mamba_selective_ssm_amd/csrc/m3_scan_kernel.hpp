@@ -73,6 +73,7 @@
 
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
+#include "m3_timeline.hpp"
 
 namespace m3 {
 
@@ -100,24 +101,7 @@ struct ScanParams {
     int64_t tl_rows;          // rows of kTlSlots entries that tl holds
 };
 
-// Per-wave phase timeline, compiled in only with M3_TIMELINE=1 (a separate,
-// instrumented build of the library): lane 0 of every wave writes, into its
-// own kTlSlots-entry row of p.tl, s_memrealtime, s_memtime and its pass, role,
-// wave, segment and unit at entry, then one 64-bit entry per phase boundary
-// (the event code in the top byte, s_memtime below it), and s_memtime and
-// s_memrealtime again in the row's last two entries at exit.
-// In the product build every stamp compiles to nothing.
-#ifndef M3_TIMELINE
-#define M3_TIMELINE 0
-#endif
-constexpr int kTlSlots = 256;
-enum TlEvent {
-    kTlFirstIssue = 1, kTlFirstArrived = 2, kTlProloguePrep = 3, kTlPrologueBarrier = 4, kTlSetup = 5,
-    kTlPrepStart = 10, kTlAngleScan = 11, kTlDecayScan = 12, kTlXRows = 13, kTlWaitTotals = 14,
-    kTlRotate = 15, kTlBarrier = 16, kTlAngleIn = 17, kTlAngleScanned = 18,
-    kTlFold = 20, kTlStage0 = 21, kTlPhaseC = 22, kTlPhaseD = 23, kTlStage = 24,
-    kTlExit = 30
-};
+// (The per-wave phase timeline of instrumented builds: m3_timeline.hpp.)
 
 // NBUF_ = 2: two chunk buffers in LDS (the prep waves fill one while the
 // math waves read the other); 1: one chunk buffer for chunks too long for two

@@ -1,7 +1,9 @@
-"""Per-wave phase timeline of the fused chunked prefill (instrumented library).
+"""Per-wave phase timeline of the fused chunked prefill and of the chunked
+gradient's main kernel (instrumented library).
 
     python -m mamba_selective_ssm_amd.build --timeline
-    python -m mamba_selective_ssm_amd.timeline [--workload prefill_bf16] [--calls 20]
+    python -m mamba_selective_ssm_amd.timeline [--workload prefill_bf16] [--calls 20] [--premix]
+    python -m mamba_selective_ssm_amd.timeline --backward [--workload prefill_bf16]
 
 Loads libm3scan_timeline.so -- the library built with M3_TIMELINE=1, whose
 scan kernels stamp every wave's phase boundaries with s_memtime -- in place of
@@ -37,6 +39,13 @@ EV = {5: "set-up done (workgroup barrier passed)", 1: "first loads issued", 2: "
 PREP_STEPS = [(10, 17), (17, 18), (18, 11), (11, 12), (12, 13), (13, 14), (14, 15), (15, 16)]
 MATH_STEPS = [(16, 22), (22, 23), (23, 24), (24, 16)]      # output pass
 MATH_STEPS_STATE = [(16, 23), (23, 16)]                    # state pass: no outputs
+BWD_STEPS = [(40, 41, "staging (inputs in, rotation into LDS)"), (41, 42, "phase 1: S, dS tiles"),
+             (42, 43, "phase 2a: dX"), (43, 44, "phase 2b: dBbar products"),
+             (44, 49, "phase 2b: angle terms, back-rotation and stores of dB"),
+             (49, 50, "phase 2c: dCbar products"),
+             (50, 45, "phase 2c: back-rotation and stores of dC, barrier"), (45, 46, "phase 3a: angle suffix sums"),
+             (46, 47, "phase 3b: dtheta"), (47, 48, "phase 3c: decay and weight gradients (wave 0)")]
+BACKWARD_BIT = 1 << 61
 
 
 def parse(rows):
@@ -59,6 +68,7 @@ def parse(rows):
         rt_span = r[SLOTS - 1] - r[0]
         tk_span = r[SLOTS - 2] - t0
         waves.append(dict(full=bool(hdr >> 63), math=bool((hdr >> 62) & 1), wv=(hdr >> 48) & 0xff,
+                          bwd=bool(hdr & BACKWARD_BIT),
                           seg=(hdr >> 32) & 0xffff, unit=hdr & 0xffffffff, rt0=r[0], ev=ev,
                           rt_span=rt_span, tk_span=tk_span))
     return waves
@@ -73,7 +83,7 @@ def summarize(waves, name):
                "100 MHz)." % tpu)
     out.append("")
     for full in (False, True):
-        pw = [w for w in waves if w["full"] == full]
+        pw = [w for w in waves if w["full"] == full and not w["bwd"]]
         if not pw:
             continue
         start = min(w["rt0"] for w in pw)
@@ -157,12 +167,48 @@ def summarize(waves, name):
     return "\n".join(out)
 
 
+def summarize_backward(waves, name):
+    """bc_grad_kernel rows: per unit (one chunk of one (b, h)), the phases
+    between its barriers, over all waves and the units they stamped."""
+    waves = [w for w in waves if w["bwd"]]
+    rates = [w["tk_span"] / (w["rt_span"] / REALTIME_MHZ) for w in waves if w["rt_span"] > 0]
+    tpu = statistics.median(rates)
+    start = min(w["rt0"] for w in waves)
+    end = max(w["rt0"] + w["rt_span"] for w in waves)
+    out = ["# Per-wave timeline of bc_grad_kernel (chunked gradient) on workload %s" % name, ""]
+    out.append("s_memtime runs at %.0f ticks per us here (median over waves, against s_memrealtime's "
+               "100 MHz)." % tpu)
+    out.append("")
+    out.append("%d waves of a persistent grid; kernel span %.1f us; wave lifetime median %.1f us." % (
+        len(waves), (end - start) / REALTIME_MHZ, statistics.median(w["rt_span"] / REALTIME_MHZ for w in waves)))
+    out.append("")
+    out.append("Per unit (one 64-row chunk), between the kernel's barriers:")
+    out.append("")
+    out.append("| phase | median us | mean us | samples |")
+    out.append("|---|---|---|---|")
+    tot = 0.0
+    for a, b, label in BWD_STEPS:
+        ds = []
+        for w in waves:
+            ev = w["ev"]
+            for i in range(len(ev) - 1):
+                if ev[i][0] == a and ev[i + 1][0] == b:
+                    ds.append((ev[i + 1][1] - ev[i][1]) / tpu)
+        if ds:
+            tot += statistics.mean(ds)
+            out.append("| %s | %.2f | %.2f | %d |" % (label, statistics.median(ds), statistics.mean(ds), len(ds)))
+    out.append("| sum of means (one unit) | | %.2f | |" % tot)
+    out.append("")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="prefill_bf16")
     ap.add_argument("--calls", type=int, default=20)
     ap.add_argument("--seed", type=int, default=7)
     ap.add_argument("--premix", action="store_true", help="with the fused pre-mixer")
+    ap.add_argument("--backward", action="store_true", help="the chunked gradient (m3_scan_bwd)")
     args = ap.parse_args(argv)
 
     import torch
@@ -186,7 +232,12 @@ def main(argv=None):
         inp = synth.make_scan_inputs(w, args.seed, "cuda")
     nrows = 32768                       # waves of both passes (a call needing more is not stamped)
     buf = torch.zeros(nrows * SLOTS, dtype=torch.int64, device="cuda")
-    call = binding.ScanCall(*[inp[k] for k in keys], chunk=w.chunk, premix=pm)
+    if args.backward:
+        gen = torch.Generator(device="cuda").manual_seed(args.seed + 1)
+        dy = torch.randn(inp["x"].shape, generator=gen, device="cuda").to(inp["x"].dtype)
+        call = binding.ScanBwdCall(*[inp[k] for k in keys], dy, method="chunked")
+    else:
+        call = binding.ScanCall(*[inp[k] for k in keys], chunk=w.chunk, premix=pm)
     lib.m3_timeline_buffer(ctypes.c_void_p(buf.data_ptr()), nrows)
     for _ in range(args.calls - 1):
         call()
@@ -199,7 +250,10 @@ def main(argv=None):
     rows = buf.view(nrows, SLOTS).cpu().tolist()
     mask = (1 << 64) - 1
     rows = [[v & mask for v in r] for r in rows]
-    print(summarize(parse(rows), w.name + (" with the pre-mixer" if pm is not None else "")))
+    if args.backward:
+        print(summarize_backward(parse(rows), w.name))
+    else:
+        print(summarize(parse(rows), w.name + (" with the pre-mixer" if pm is not None else "")))
     return 0
 
 
