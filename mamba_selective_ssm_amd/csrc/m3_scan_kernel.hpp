@@ -648,6 +648,22 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
     const unsigned bDT = 4u * (unsigned)sDT, bTH = 4u * (unsigned)sTH, bA = 4u * (unsigned)sA;
     const unsigned bBN = (unsigned)sizeof(io_t) * (unsigned)sBN, bXP = (unsigned)sizeof(io_t) * (unsigned)sXP;
     const unsigned bcq = (unsigned)sizeof(io_t) * 8u * (unsigned)qd;       // B/C quad
+    // Shuffled phases: the four source pairs of this lane's pair quad (fixed
+    // for the kernel), read once and packed one byte each (pair indices are
+    // below 128), so that no theta load waits on a load of the permutation
+    // (prefill_bf16 with shuffled phases 41.1 -> 39.0 us).  The pre-mixer
+    // variants read the permutation with each load instead: holding it cost
+    // them 2%.
+    unsigned shf = 0u;
+    if (!PM && p.opt.phase == 3 && !is_math) {
+        const int q = CL ? lane % NPR4 : qd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            int src = p.opt.perm[4 * q + e];
+            src = src < 0 ? 0 : (src >= NPR ? NPR - 1 : src);
+            shf |= (unsigned)src << (8 * e);
+        }
+    }
     auto at = [](const auto* base, unsigned off) {
         return reinterpret_cast<decltype(base)>(reinterpret_cast<const char*>(base) + off);
     };
@@ -707,7 +723,11 @@ __global__ __launch_bounds__(Cf::NT, Cf::OCC * Cf::NW / 4) void scan_kernel(cons
                 th = f32x4{0.f, 0.f, 0.f, 0.f};
             } else if (phase == 2) {        // reverse
                 th = -*reinterpret_cast<const f32x4*>(at(lth, __umul24(j, bTH) + tq16));
-            } else {                        // shuffle: pair i reads pair perm[i]
+            } else if constexpr (!PM) {     // shuffle: pair i reads pair perm[i] (of quad q, in shf)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    th[e] = *at(lth, __umul24(j, bTH) + 4u * ((shf >> (8 * e)) & 0xffu));
+            } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     int src = p.opt.perm[4 * q + e];
