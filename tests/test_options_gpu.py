@@ -97,6 +97,19 @@ def test_all_options_with_segments(io, segments):
              segments=segments, label="all+segments")
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("opts", [dict(ngroups=4, a_tok=True), dict(phase="zero"), dict(phase="shuffle"),
+                                  dict(premix=True)],
+                         ids=["groups4+A_t", "phase_zero", "phase_shuffle", "premix"])
+def test_option_workloads_full_every_unit(opts):
+    """The benchmark's option workloads at the single-layer prefill's full
+    shape (batch 4, 16 heads, 2048 tokens, P = N = 64, bf16, chunk 64) from
+    a random state record, in the launch the library picks (segments, the
+    pre-mixer's own variant): every (b, h) unit's y and final state against
+    the oracle."""
+    run_case(synth.WORKLOADS["prefill_bf16"], 470, label="option workload, full size", **opts)
+
+
 def test_premix_prefill_workload_sampled():
     """prefill_bf16 shapes with the pre-mixer and head groups (segmented
     launch as the library picks it): sampled (b, h) units against the oracle."""
