@@ -208,7 +208,7 @@ struct Raw {
     static constexpr int IG = (Cf::NPR * G4 + Cf::NTHR - 1) / Cf::NTHR;
     uint4 vb[IB], vc[IB], vx[IX], vy[IX];
     f32x4 th[IT];
-    float dtv, lmv, av;   // av: the token's decay rate when it is given per token
+    float dtv, lmv, av;   // av: the token's decay rate (per token, or the head's)
     V4 sd0[IG], sd1[IG], sg0[IG], sg1[IG];    // state pair items (rows 2i, 2i+1, columns 4q..4q+3)
     float scc[IG], sss[IG];
 };
@@ -222,6 +222,7 @@ struct Held {
     static constexpr int IT = Raw<Cf>::IT, IG = Raw<Cf>::IG;
     f32x4 th[IT];
     V4 g0[IG], g1[IG];
+    float av;             // the decay rate of token `lane` (wave 0)
 };
 
 __device__ __forceinline__ f32x4 v4f(const bf16x4& v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
@@ -285,7 +286,9 @@ __device__ __forceinline__ void load_raw(const BcParams& p, int bh, int c, Raw<C
     if constexpr ((PARTS & LR_XT) != 0) {
         rw.dtv = 0.f; rw.lmv = 0.f; rw.av = 0.f;
         if (tid <= Q && t0 + tid < L_) { rw.dtv = p.dt[tok(t0 + tid)]; rw.lmv = p.lam[tok(t0 + tid)]; }
-        if (p.a_tok && tid < Q && t0 + tid < L_) rw.av = p.A[tok(t0 + tid)];
+        // the decay rate, loaded with the chunk: per token, or the head's one
+        // (so that no later phase waits on a load of it)
+        if (tid < Q && t0 + tid < L_) rw.av = p.A[p.a_tok ? tok(t0 + tid) : h];
     }
     if constexpr (GRAD && (PARTS & LR_STATE) != 0) {
         const op_t* gin = reinterpret_cast<const op_t*>(p.gst) + ((size_t)bh * (p.nc + 1) + c) * N * P;
@@ -331,7 +334,6 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
     op_t* sDY = reinterpret_cast<op_t*>(lds + L::oDY);
     float* sPhi = reinterpret_cast<float*>(lds + L::oPhi);
     float* sT = reinterpret_cast<float*>(lds + L::oTok);
-    const float A = p.a_tok ? 0.f : p.A[h];
 
     // ---- S1: raw rows into LDS ----------------------------------------------
 #pragma unroll
@@ -370,7 +372,8 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
         const int j = lane;
         const float dtj = j < Q ? sT[kDt * TS + j] : 0.f;
         const float lmj = j < Q ? sT[kLm * TS + j] : 0.f;
-        const float lam_j = wave_inclusive_sum(dtj * (p.a_tok ? rw.av : A));
+        const float lam_j = wave_inclusive_sum(dtj * rw.av);
+        hd.av = rw.av;
         const float lam_tot = wave_read_lane(lam_j, 63);
         const float dtn = sT[kDt * TS + j + 1], lmn = sT[kLm * TS + j + 1];
         const float ga = lmj * dtj;
@@ -1091,7 +1094,7 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
             const float dtt = sT[kDt * TS + t], lm = sT[kLm * TS + t];
             const float dwp = t > 0 ? dw_prev : 0.f;
             const int64_t k = tok(t0 + t);
-            const float A = p.A[p.a_tok ? k : h];
+            const float A = hd.av;
             p.ddt[k] = A * da + sT[kTD * TS + t] + lm * dgt + (1.f - lm) * dwp;
             p.dlam[k] = dtt * (dgt - dwp);
             dAc = dtt * da;
