@@ -387,12 +387,19 @@ __device__ __forceinline__ void stage(const BcParams& p, unsigned char* lds, int
         }
     }
     {
+        // this wave's NPR / NW pairs as independent scans (their DPP chains
+        // interleave)
+        static_assert(NPR % NW == 0, "pairs split evenly over the waves");
+        constexpr int KW = NPR / NW;
         const float dtj = lane < Q ? sT[kDt * TS + lane] : 0.f;
-        for (int i = wv; i < NPR; i += NW) {
-            const float v = lane < Q ? dtj * sPhi[lane * LDH + i] : 0.f;
-            const float ph = wave_inclusive_sum(v);
-            if (lane < Q) sPhi[lane * LDH + i] = ph;
-        }
+        float v[KW];
+#pragma unroll
+        for (int k = 0; k < KW; ++k) v[k] = lane < Q ? dtj * sPhi[lane * LDH + wv + NW * k] : 0.f;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) v[k] = wave_inclusive_sum(v[k]);
+#pragma unroll
+        for (int k = 0; k < KW; ++k)
+            if (lane < Q) sPhi[lane * LDH + wv + NW * k] = v[k];
     }
     __syncthreads();
 
@@ -1007,17 +1014,29 @@ __global__ __launch_bounds__(Cf::NTHR) void bc_grad_kernel(const BcParams p)
 
     tlr.stamp(kTlGradC, lane);
     // ---- phase 3a: dphi = suffix sums of dPhi over the chunk's tokens ---------
-    for (int i = wv; i < NPR; i += NW) {
-        float v = 0.f;
-        if (lane < Q) {
-            v = sDPhi[lane * DPS + i];
-            if (lane == Q - 1)
-                v += sT[kCross * TS + i] - (sT[kZP * TS + i] + sT[(kZP + 1) * TS + i] +
-                                            sT[(kZP + 2) * TS + i] + sT[(kZP + 3) * TS + i]);
+    {
+        // this wave's NPR / NW pairs as independent scans (their DPP chains
+        // interleave)
+        constexpr int KW = NPR / NW;
+        float v[KW], inc[KW];
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+            const int i = wv + NW * k;
+            v[k] = 0.f;
+            if (lane < Q) {
+                v[k] = sDPhi[lane * DPS + i];
+                if (lane == Q - 1)
+                    v[k] += sT[kCross * TS + i] - (sT[kZP * TS + i] + sT[(kZP + 1) * TS + i] +
+                                                   sT[(kZP + 2) * TS + i] + sT[(kZP + 3) * TS + i]);
+            }
         }
-        const float inc = wave_inclusive_sum(v);
-        const float tot = wave_read_lane(inc, 63);
-        if (lane < Q) sDPhi[lane * DPS + i] = tot - inc + v;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) inc[k] = wave_inclusive_sum(v[k]);
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+            const float tot = wave_read_lane(inc[k], 63);
+            if (lane < Q) sDPhi[lane * DPS + wv + NW * k] = tot - inc[k] + v[k];
+        }
     }
     __syncthreads();
 
