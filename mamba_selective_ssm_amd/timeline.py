@@ -209,6 +209,7 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=7)
     ap.add_argument("--premix", action="store_true", help="with the fused pre-mixer")
     ap.add_argument("--backward", action="store_true", help="the chunked gradient (m3_scan_bwd)")
+    ap.add_argument("--raw", default=None, help="also save the stamped rows (uint64, one per wave) to this .npy file")
     args = ap.parse_args(argv)
 
     import torch
@@ -250,6 +251,9 @@ def main(argv=None):
     rows = buf.view(nrows, SLOTS).cpu().tolist()
     mask = (1 << 64) - 1
     rows = [[v & mask for v in r] for r in rows]
+    if args.raw:
+        import numpy as np
+        np.save(args.raw, np.array([r for r in rows if r[0] != 0], dtype=np.uint64))
     if args.backward:
         print(summarize_backward(parse(rows), w.name))
     else:
